@@ -1,0 +1,118 @@
+"""Group quantizers, written from the pages' definitions.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Affine (asymmetric) quantization -- page "KV缓存量化技术：提升大模型长文本生成效率"
+(rkmt.cn/news/1711363) §2.1: S = (max - min) / (2^n - 1), Z = round(-min / S),
+one (S, Z) per group of 64 elements, codes stored as n-bit integers.  The page
+prints the code as round(X/S) - Z; with Z = round(-min/S) that sends min to
+about -2Z, outside [0, 2^n - 1].  The reading adopted here is the one under which
+codes land in [0, 2^n - 1]:
+
+    q = clamp(round(x / S) + Z, 0, 2^n - 1),      x_hat = S * (q - Z)
+
+Readings of what the page leaves open (each listed in the design notes):
+  * "round" is round-half-to-even, applied to the exact quotient;
+  * S is rounded once from the exact (max - min) / (2^n - 1) to fp16;
+  * Z is the exact round(-min / S) using the stored fp16 S, stored as fp16
+    (exact for |Z| <= 2048, saturated to +-65504, zero stored as +0);
+  * codes use the stored S and stored Z;
+  * a group with max == min, or whose S rounds to 0, uses S = |min| (1 when
+    min is 0), which makes a constant group decode exactly.
+
+Float64 evaluation decides every rounding exactly here: mx - mn of two fp16
+values is exact in float64, and the float64 quotients x/S, -mn/S and
+(mx-mn)/(2^n-1) lie further from any rounding boundary of the target (an
+integer-plus-half, or an fp16 midpoint) than float64's relative error 2^-53;
+the tests pin this against exact rational arithmetic.
+
+NVFP4 -- page "NVFP4 KV缓存技术详解" (glsqs.com/news/814573) §2.1 (16 values share
+one FP8 scale) and §4.2 (clip range up to 6.0): per 16 contiguous head_dim
+values, s = E4M3_RNE(amax / 6) saturating at 448, code = sign bit * 8 +
+E2M1_RNE(min(|x| / s, 6)); decode x_hat = e2m1(code) * s.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .numerics import f16, f16_saturate, e4m3_encode, e4m3_decode, e2m1_encode, e2m1_decode
+
+GROUP = 64
+NV_BLOCK = 16
+
+
+def affine_quantize(x16: np.ndarray, nbits: int):
+    """Quantize groups of 64 along the last axis.
+
+    x16: fp16 [..., 64].  Returns (codes uint8 [..., 64], S fp16 [...], Z fp16 [...]).
+    """
+    if nbits not in (2, 4, 8):
+        raise ValueError(nbits)
+    x = np.asarray(x16, dtype=np.float16).astype(np.float64)
+    assert x.shape[-1] == GROUP
+    qmax = (1 << nbits) - 1
+    mn = x.min(axis=-1)
+    mx = x.max(axis=-1)
+    S = f16((mx - mn) / qmax)
+    degenerate = (mx == mn) | (S == 0)
+    S_deg = np.where(mn != 0, f16(np.abs(mn)), np.float16(1.0))
+    S = np.where(degenerate, S_deg, S).astype(np.float16)
+    S64 = S.astype(np.float64)
+    Z = np.rint(-mn / S64)
+    Zs = f16_saturate(Z)
+    q = np.rint(x / S64[..., None]) + Zs.astype(np.float64)[..., None]
+    q = np.clip(q, 0, qmax).astype(np.uint8)
+    return q, S, Zs
+
+
+def affine_dequantize(q: np.ndarray, S: np.ndarray, Z: np.ndarray) -> np.ndarray:
+    """x_hat = S * (q - Z) in float64 (exact: S and Z are fp16, q a small integer)."""
+    return S.astype(np.float64)[..., None] * (q.astype(np.float64) - Z.astype(np.float64)[..., None])
+
+
+def nvfp4_quantize(x16: np.ndarray):
+    """Quantize blocks of 16 along the last axis.
+
+    x16: fp16 [..., 16].  Returns (codes uint8 [..., 16] in 0..15, scale byte uint8 [...]).
+    """
+    x = np.asarray(x16, dtype=np.float16)
+    assert x.shape[-1] == NV_BLOCK
+    amax = np.abs(x.astype(np.float64)).max(axis=-1)
+    sbyte = e4m3_encode(amax / 6.0)
+    s = e4m3_decode(sbyte)
+    codes = e2m1_encode(x, s[..., None])
+    return codes, sbyte
+
+
+def nvfp4_dequantize(codes: np.ndarray, sbyte: np.ndarray) -> np.ndarray:
+    return e2m1_decode(codes) * e4m3_decode(sbyte)[..., None]
+
+
+def quantize_tokens(x16: np.ndarray, fmt: str):
+    """Quantize token rows of head_dim 128: x16 fp16 [N, 128].
+
+    Returns a dict with the stored fields:
+      affine: codes [N,128], S [N,2], Z [N,2]
+      nvfp4 : codes [N,128], scale [N,8]
+    """
+    x16 = np.asarray(x16, dtype=np.float16)
+    N, D = x16.shape
+    if fmt in ("int2", "int4", "int8"):
+        nb = int(fmt[3:])
+        q, S, Z = affine_quantize(x16.reshape(N, D // GROUP, GROUP), nb)
+        return {"codes": q.reshape(N, D), "S": S, "Z": Z}
+    if fmt == "nvfp4":
+        c, s = nvfp4_quantize(x16.reshape(N, D // NV_BLOCK, NV_BLOCK))
+        return {"codes": c.reshape(N, D), "scale": s}
+    raise ValueError(fmt)
+
+
+def dequantize_tokens(qt: dict, fmt: str) -> np.ndarray:
+    """float64 [N, 128] decoded values of quantize_tokens()' output."""
+    codes = qt["codes"]
+    N, D = codes.shape
+    if fmt in ("int2", "int4", "int8"):
+        return affine_dequantize(codes.reshape(N, D // GROUP, GROUP), qt["S"], qt["Z"]).reshape(N, D)
+    if fmt == "nvfp4":
+        return nvfp4_dequantize(codes.reshape(N, D // NV_BLOCK, NV_BLOCK), qt["scale"]).reshape(N, D)
+    raise ValueError(fmt)

@@ -1,0 +1,101 @@
+"""Pins of the oracle's block packer against hand-derived byte positions and structural properties."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import layout
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "layout_cases.json")))
+
+
+def _empty(fmt):
+    if fmt == "nvfp4":
+        return {"codes": np.zeros((128, 128), np.uint8), "scale": np.zeros((128, 8), np.uint8)}
+    return {"codes": np.zeros((128, 128), np.uint8), "S": np.zeros((128, 2), np.float16),
+            "Z": np.zeros((128, 2), np.float16)}
+
+
+def _pack(fmt, kq, vq):
+    if fmt == "nvfp4":
+        return layout.pack_nvfp4_block(kq, vq, 128)
+    return layout.pack_affine_block(int(fmt[3:]), kq, vq, 128)
+
+
+@pytest.mark.parametrize("case", GOLDEN["cases"], ids=lambda c: f"{c['fmt']}-{c['part']}-{c['slot']}-{c['dim']}")
+def test_code_positions(case):
+    kq, vq = _empty(case["fmt"]), _empty(case["fmt"])
+    (kq if case["part"] == "Kc" else vq)["codes"][case["slot"], case["dim"]] = case["code"]
+    blk = _pack(case["fmt"], kq, vq)
+    nz = np.flatnonzero(blk)
+    assert list(nz) == [case["byte"]]
+    assert blk[case["byte"]] == (case["code"] << case["shift"]) & 0xFF
+
+
+@pytest.mark.parametrize("case", GOLDEN["meta_cases"], ids=lambda c: f"{c['fmt']}-{c['part']}-{c['slot']}-{c['field']}")
+def test_meta_positions(case):
+    kq, vq = _empty(case["fmt"]), _empty(case["fmt"])
+    (kq if case["part"] == "Km" else vq)[case["field"]][case["slot"], case["group"]] = 1.5   # 0x3E00
+    blk = _pack(case["fmt"], kq, vq)
+    assert list(np.flatnonzero(blk)) == [case["byte"] + 1]
+    assert blk[case["byte"] + 1] == 0x3E
+
+
+@pytest.mark.parametrize("case", GOLDEN["scale_cases"], ids=lambda c: f"{c['part']}-{c['slot']}")
+def test_scale_positions(case):
+    kq, vq = _empty("nvfp4"), _empty("nvfp4")
+    (kq if case["part"] == "Ks" else vq)["scale"][case["slot"], case["dim"] // 16] = 0x38
+    blk = _pack("nvfp4", kq, vq)
+    assert list(np.flatnonzero(blk)) == [case["byte"]]
+
+
+@pytest.mark.parametrize("case", GOLDEN["residual_cases"], ids=lambda c: c["part"])
+def test_residual_positions(case):
+    R = case["R"]
+    k = np.zeros((R, 128), np.float16); v = np.zeros((R, 128), np.float16)
+    (k if case["part"] == "K" else v)[case["slot"], case["dim"]] = 1.5
+    data, mask = layout.pack_residual(k, v, R)
+    assert list(np.flatnonzero(data)) == [case["byte"] + 1]
+
+
+@pytest.mark.parametrize("n", [2, 4, 8])
+def test_sigma_is_a_permutation_grouping_lane_quarters(n):
+    s = layout.sigma(n)
+    assert sorted(s) == list(range(128))
+    q = np.arange(128) // 32
+    assert np.all(((s % 16) // 4) == q)          # quarter q holds the slots of lane group q
+    # inside every 32-bit word the slots are whole 4-slot runs (one 16x16 MFMA operand column)
+    F = 32 // n
+    for w in range(128 // F):
+        slots = s[w * F:(w + 1) * F]
+        assert set(slots // 4 * 4) == set(slots - slots % 4)
+        assert np.all(np.bincount(slots // 4, minlength=32)[np.unique(slots // 4)] == 4)
+
+
+def test_every_bit_of_a_block_is_reachable_once():
+    """Setting all codes/meta to all-ones fills every byte of the block with 0xFF
+    (no gaps, and codes of different elements never share bits)."""
+    for fmt in ("int2", "int4", "int8"):
+        n = int(fmt[3:])
+        full = {"codes": np.full((128, 128), (1 << n) - 1, np.uint8),
+                "S": np.full((128, 2), np.uint16(0xFFFF).view(np.float16)),
+                "Z": np.full((128, 2), np.uint16(0xFFFF).view(np.float16))}
+        blk = layout.pack_affine_block(n, full, full, 128)
+        assert np.all(blk == 0xFF) and blk.size == layout.affine_block_bytes(n)
+    full = {"codes": np.full((128, 128), 15, np.uint8), "scale": np.full((128, 8), 0xFF, np.uint8)}
+    blk = layout.pack_nvfp4_block(full, full, 128)
+    assert np.all(blk == 0xFF) and blk.size == layout.NVFP4_BLOCK_BYTES
+
+
+def test_partial_block_tail_is_zero():
+    full = {"codes": np.full((128, 128), 3, np.uint8), "S": np.ones((128, 2), np.float16),
+            "Z": np.ones((128, 2), np.float16)}
+    used = 37
+    part = {k: v[:used] for k, v in full.items()}
+    blk = layout.pack_affine_block(2, part, part, used)
+    ref = layout.pack_affine_block(2, {k: np.where(np.arange(128)[:, None] < used, v, 0).astype(v.dtype)
+                                       for k, v in full.items()},
+                                   {k: np.where(np.arange(128)[:, None] < used, v, 0).astype(v.dtype)
+                                    for k, v in full.items()}, 128)
+    assert np.array_equal(blk, ref)

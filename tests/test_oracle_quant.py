@@ -1,0 +1,144 @@
+"""Pins of the oracle's affine and NVFP4 quantizers: brute-force nearest codes, exact
+rational S and Z, and the invariants the method implies."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import quant, numerics as nm
+
+
+def _groups(seed, n=400):
+    """Random and adversarial fp16 groups of 64."""
+    r = np.random.default_rng(seed)
+    gs = [r.standard_normal((n, 64)),
+          r.standard_normal((n // 4, 64)) * 15.0,
+          r.standard_t(4, (n // 4, 64)),
+          r.uniform(3.0, 3.01, (n // 8, 64)),            # narrow, not straddling 0
+          -r.uniform(100, 101, (n // 8, 64)),
+          r.standard_normal((n // 8, 64)) * 1e-6,       # subnormal territory
+          np.clip(r.standard_normal((n // 8, 64)) * 40000, -65504, 65504)]
+    two = np.where(r.random((n // 8, 64)) < 0.5, -1.25, 2.5); two[:, 0] = -1.25; two[:, 1] = 2.5
+    gs.append(two)
+    ties = np.round(r.standard_normal((n // 8, 64)) * 8) / 2   # many half-integers
+    gs.append(ties)
+    return np.concatenate(gs).astype(np.float16)
+
+
+@pytest.mark.parametrize("nbits", [2, 4, 8])
+def test_codes_are_brute_force_nearest(nbits):
+    """Each code is the nearest valid code: argmin over q in [0, 2^n-1] of |x - S(q - Z)|,
+    ties broken towards even q - Z (round half to even of x/S)."""
+    g = _groups(nbits)
+    q, S, Z = quant.affine_quantize(g, nbits)
+    qmax = (1 << nbits) - 1
+    cand = np.arange(qmax + 1, dtype=np.float64)
+    dec = S.astype(np.float64)[:, None] * (cand[None, :] - Z.astype(np.float64)[:, None])   # [G, 2^n]
+    x = g.astype(np.float64)
+    dist = np.abs(x[:, :, None] - dec[:, None, :])                   # exact in float64
+    best = dist.min(axis=2, keepdims=True)
+    tied = dist == best
+    even = tied & (((cand[None, None, :] - Z.astype(np.float64)[:, None, None]) % 2) == 0)
+    expect = np.where(tied.sum(axis=2) > 1, np.argmax(even, axis=2), np.argmax(tied, axis=2))
+    assert np.array_equal(q.astype(np.int64), expect)
+
+
+@pytest.mark.parametrize("nbits", [2, 4, 8])
+def test_scale_and_zero_exact_rational(nbits):
+    g = _groups(10 + nbits, 200)
+    q, S, Z = quant.affine_quantize(g, nbits)
+    qmax = (1 << nbits) - 1
+    for row, s, z in zip(g, S, Z):
+        mn, mx = Fraction(float(row.min())), Fraction(float(row.max()))
+        t = (mx - mn) / qmax
+        s_exact_nearest = None
+        if mx > mn:
+            lo = np.float16(float(t))
+            cands = [c for c in {lo, np.nextafter(lo, np.float16(np.inf)), np.nextafter(lo, np.float16(0))}]
+            best = min(abs(Fraction(float(c)) - t) for c in cands)
+            tied = [c for c in cands if abs(Fraction(float(c)) - t) == best]
+            if len(tied) > 1:
+                tied = [c for c in tied if (np.array(c, np.float16).view(np.uint16) & 1) == 0]
+            s_exact_nearest = float(tied[0])
+        if s_exact_nearest:
+            assert float(s) == s_exact_nearest
+        else:                                   # degenerate: S = |min|, or 1 when min is 0
+            assert float(s) == (abs(float(mn)) if mn != 0 else 1.0)
+        zq = -mn / Fraction(float(s))
+        zi = int(zq.__round__())                # Fraction.__round__ rounds half to even
+        zi = max(-65504, min(65504, zi))
+        assert float(z) == float(np.float16(zi)), (float(mn), float(s), zi)
+
+
+@pytest.mark.parametrize("nbits", [2, 4, 8])
+def test_invariants(nbits):
+    g = _groups(20 + nbits)
+    q, S, Z = quant.affine_quantize(g, nbits)
+    qmax = (1 << nbits) - 1
+    x = g.astype(np.float64)
+    xh = quant.affine_dequantize(q, S, Z)
+    S64 = S.astype(np.float64)[:, None]
+    small_z = np.abs(Z.astype(np.float64)) <= 2048
+    # (i) the minimum of a group always gets code 0 (when Z is stored exactly)
+    amin = np.argmin(x, axis=1)
+    assert np.all(q[np.arange(len(q)), amin][small_z] == 0)
+    # (ii) round-trip error <= S/2 for values whose code is not clamped
+    raw = np.rint(x / S64) + Z.astype(np.float64)[:, None]
+    unclamped = (raw >= 0) & (raw <= qmax)
+    assert np.all(np.abs(x - xh)[unclamped] <= 0.5 * np.broadcast_to(S64, x.shape)[unclamped])
+    # (iii) projection: quantizing the decoded values with the same (S, Z) gives q back
+    q2 = np.clip(np.rint(xh / S64) + Z.astype(np.float64)[:, None], 0, qmax)
+    assert np.array_equal(q2, q.astype(np.float64))
+    # (iv) idempotence: re-quantizing the decoded group from scratch reproduces (S, Z, q)
+    #      when the group's codes span [0, 2^n - 1] and x_hat is representable in fp16
+    span = (q.min(axis=1) == 0) & (q.max(axis=1) == qmax)
+    with np.errstate(over="ignore"):
+        rep = np.all(xh.astype(np.float16).astype(np.float64) == xh, axis=1)
+    sel = span & rep & small_z
+    # int8 decoded values rarely fit fp16 (11 significant bits), so few groups qualify
+    assert sel.sum() > (100 if nbits <= 4 else 0)
+    q3, S3, Z3 = quant.affine_quantize(xh[sel].astype(np.float16), nbits)
+    assert np.array_equal(q3, q[sel]) and np.array_equal(S3, S[sel]) and np.array_equal(Z3, Z[sel])
+
+
+def test_constant_and_two_valued_groups():
+    for c in [0.0, -0.0, 1.5, -7.25, 65504.0, 2.0 ** -24]:
+        g = np.full((1, 64), c, np.float16)
+        for nb in (2, 4, 8):
+            q, S, Z = quant.affine_quantize(g, nb)
+            assert np.array_equal(quant.affine_dequantize(q, S, Z), g.astype(np.float64))
+            assert np.all(q == 0)
+    g = np.where(np.arange(64) % 3 == 0, -2.0, 5.0).astype(np.float16)[None]
+    for nb in (2, 4, 8):
+        q, S, Z = quant.affine_quantize(g, nb)
+        assert set(np.unique(q)) == {0, (1 << nb) - 1}
+
+
+def test_zero_is_stored_as_positive_zero():
+    g = np.zeros((2, 64), np.float16); g[1, :] = -0.0
+    g[0, 5] = 1.0
+    _, _, Z = quant.affine_quantize(g, 4)
+    assert np.all(Z.view(np.uint16) == 0)
+
+
+def test_nvfp4_block_quantizer():
+    r = np.random.default_rng(3)
+    x = (r.standard_normal((500, 16)) * np.exp2(r.integers(-12, 10, (500, 1)))).astype(np.float16)
+    codes, sb = quant.nvfp4_quantize(x)
+    amax = np.abs(x.astype(np.float64)).max(axis=1)
+    assert np.array_equal(sb, nm.e4m3_encode(amax / 6))
+    s = nm.e4m3_decode(sb)
+    xh = quant.nvfp4_dequantize(codes, sb)
+    # decoded magnitudes never exceed 6 * s, and each element is the nearest grid value
+    assert np.all(np.abs(xh) <= 6 * s[:, None])
+    grid = np.asarray(nm.E2M1_MAGNITUDES)[None, None, :] * s[:, None, None]
+    d_best = np.abs(np.abs(x.astype(np.float64))[:, :, None] - grid).min(axis=2)
+    assert np.array_equal(np.abs(np.abs(x.astype(np.float64)) - np.abs(xh)), d_best)
+    # an all-zero block has scale 0 and signed-zero codes
+    z = np.array([[0.0] * 8 + [-0.0] * 8], np.float16)
+    c0, s0 = quant.nvfp4_quantize(z)
+    assert s0[0] == 0 and list(c0[0]) == [0] * 8 + [8] * 8
+    # a block whose amax/6 exceeds 448 saturates the scale
+    big = np.full((1, 16), 60000.0, np.float16)
+    _, sbig = quant.nvfp4_quantize(big)
+    assert sbig[0] == 0x7E
