@@ -1,0 +1,172 @@
+"""Python binding of libkvq (quantized KV cache + fused dequant decode attention on MI355X).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of libkvq.so.
+PyTorch provides device memory and the stream.  The functions below carry the C ABI's
+names (include/kvq.h); `Cache` bundles the device buffer and the handle.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkvq.so")
+
+KVQ_OK, KVQ_EINVAL, KVQ_ECAPACITY, KVQ_ENOSPACE, KVQ_EHIP, KVQ_ESTATE = 0, -1, -2, -3, -4, -5
+FMT = {"fp16": 0, "int2": 2, "int4": 4, "int8": 8, "nvfp4": 16}
+REGION_RESIDUAL, REGION_YOUNG, REGION_OLD = 0, 1, 2
+
+# every symbol include/kvq.h declares
+EXPORTS = ("kvq_cache_bytes", "kvq_cache_create", "kvq_cache_destroy", "kvq_cache_reset", "kvq_append",
+           "kvq_flush_residual", "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_seq_len", "kvq_layout",
+           "kvq_set_plan_only", "kvq_last_error")
+
+
+class KvqError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"kvq error {code}: {msg}")
+        self.code = code
+
+
+class kvq_config(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("max_tokens", ctypes.c_int64), ("format", ctypes.c_int32),
+                ("group_size", ctypes.c_int32), ("residual_len", ctypes.c_int32), ("old_format", ctypes.c_int32),
+                ("old_after", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkvq.so; raises if it has not been built (there is no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "or python bit_quantized_kv_kvq_amd/_build.py")
+    # torch must load its HIP runtime first: libkvq then binds to that same instance
+    # (libamdhip64.so.7), so device memory, streams and kernels share one runtime.
+    import torch  # noqa: F401
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    P = ctypes.POINTER
+    L.kvq_cache_bytes.argtypes = [P(kvq_config)]; L.kvq_cache_bytes.restype = sz
+    L.kvq_cache_create.argtypes = [P(kvq_config), vp, sz, P(vp)]; L.kvq_cache_create.restype = ctypes.c_int
+    L.kvq_cache_destroy.argtypes = [vp]; L.kvq_cache_destroy.restype = ctypes.c_int
+    L.kvq_cache_reset.argtypes = [vp]; L.kvq_cache_reset.restype = ctypes.c_int
+    L.kvq_append.argtypes = [vp, i32, vp, vp, i64, vp]; L.kvq_append.restype = ctypes.c_int
+    L.kvq_flush_residual.argtypes = [vp, i32, vp]; L.kvq_flush_residual.restype = ctypes.c_int
+    L.kvq_decode_workspace_bytes.argtypes = [vp, i32]; L.kvq_decode_workspace_bytes.restype = sz
+    L.kvq_decode_attn.argtypes = [vp, i32, vp, i32, ctypes.c_float, vp, i32, vp, sz, vp]
+    L.kvq_decode_attn.restype = ctypes.c_int
+    L.kvq_seq_len.argtypes = [vp, i32, P(i64), P(i64)]; L.kvq_seq_len.restype = ctypes.c_int
+    L.kvq_layout.argtypes = [vp, i32, i32, P(sz), P(sz), P(i64)]; L.kvq_layout.restype = ctypes.c_int
+    L.kvq_set_plan_only.argtypes = [vp, i32]; L.kvq_set_plan_only.restype = ctypes.c_int
+    L.kvq_last_error.argtypes = []; L.kvq_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(code: int):
+    if code != KVQ_OK:
+        raise KvqError(code, lib().kvq_last_error().decode())
+
+
+def make_config(num_layers, batch, num_kv_heads, max_tokens, fmt="int4", residual_len=128,
+                old_fmt=None, old_after=0, head_dim=128) -> kvq_config:
+    return kvq_config(num_layers, batch, num_kv_heads, head_dim, max_tokens, FMT[fmt],
+                      16 if fmt == "nvfp4" else 64, residual_len, FMT[old_fmt or fmt], old_after)
+
+
+def kvq_cache_bytes(cfg: kvq_config) -> int:
+    return lib().kvq_cache_bytes(ctypes.byref(cfg))
+
+
+def _stream_ptr(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+class Cache:
+    """A kvq cache over a torch uint8 device buffer.
+
+    `plan_only=True` creates the handle without a GPU over a fake (never touched)
+    address, for bookkeeping checks on machines without a device."""
+
+    def __init__(self, cfg: kvq_config, device="cuda", plan_only=False):
+        import torch
+        self.cfg = cfg
+        self.nbytes = kvq_cache_bytes(cfg)
+        if self.nbytes == 0:
+            raise KvqError(KVQ_EINVAL, lib().kvq_last_error().decode())
+        self.plan_only = plan_only
+        if plan_only:
+            self.buf = None
+            ptr = 1 << 40                     # 256-aligned placeholder, never dereferenced
+        else:
+            self.buf = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=device)
+            ptr = (self.buf.data_ptr() + 255) // 256 * 256
+        self.base_ptr = ptr
+        self.base_off = ptr - (self.buf.data_ptr() if self.buf is not None else ptr)
+        h = ctypes.c_void_p()
+        _check(lib().kvq_cache_create(ctypes.byref(cfg), ctypes.c_void_p(ptr), self.nbytes, ctypes.byref(h)))
+        self.h = h
+        if plan_only:
+            _check(lib().kvq_set_plan_only(self.h, 1))
+
+    def __del__(self):
+        h = getattr(self, "h", None)
+        if h is not None and _lib is not None:
+            _lib.kvq_cache_destroy(h)
+            self.h = None
+
+    # -- calls
+    def append(self, layer: int, k, v, stream=None):
+        n = k.shape[2] if k is not None else 0
+        kp = k.data_ptr() if k is not None else None
+        vp_ = v.data_ptr() if v is not None else None
+        s = None if self.plan_only else _stream_ptr(stream)
+        _check(lib().kvq_append(self.h, layer, kp, vp_, n, s))
+
+    def append_plan(self, layer: int, n: int):
+        """Bookkeeping-only append of n tokens (plan-only caches)."""
+        assert self.plan_only
+        _check(lib().kvq_append(self.h, layer, 1 << 40, 1 << 40, n, None))
+
+    def flush(self, layer: int, stream=None):
+        _check(lib().kvq_flush_residual(self.h, layer, None if self.plan_only else _stream_ptr(stream)))
+
+    def reset(self):
+        _check(lib().kvq_cache_reset(self.h))
+
+    def workspace_bytes(self, num_q_heads: int) -> int:
+        return lib().kvq_decode_workspace_bytes(self.h, num_q_heads)
+
+    def decode(self, layer: int, q, softmax_scale: float, out, workspace, stream=None):
+        import torch
+        out_fp32 = 1 if out.dtype == torch.float32 else 0
+        _check(lib().kvq_decode_attn(self.h, layer, q.data_ptr(), q.shape[1], float(softmax_scale), out.data_ptr(),
+                                     out_fp32, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                     _stream_ptr(stream)))
+
+    def seq_len(self, layer: int) -> tuple[int, int]:
+        t, r = ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().kvq_seq_len(self.h, layer, ctypes.byref(t), ctypes.byref(r)))
+        return t.value, r.value
+
+    def layout(self, layer: int, region: int) -> tuple[int, int, int]:
+        """(byte offset in the cache buffer, bytes, slots used per (batch, kv_head))."""
+        off, nb, tok = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int64()
+        _check(lib().kvq_layout(self.h, layer, region, ctypes.byref(off), ctypes.byref(nb), ctypes.byref(tok)))
+        return off.value, nb.value, tok.value
+
+    def region_tensor(self, layer: int, region: int):
+        """uint8 device view [batch, kv_heads, bytes per (b, h)] of a region."""
+        off, nb, _ = self.layout(layer, region)
+        B, H = self.cfg.batch, self.cfg.num_kv_heads
+        t = self.buf[self.base_off + off:self.base_off + off + nb]
+        return t.view(B, H, nb // (B * H)) if nb else t.view(B, H, 0)

@@ -1,0 +1,412 @@
+// Host side of libkvq: configuration checks, arena planning, the residual / tier schedule
+// and kernel launches.  Implements include/kvq.h.
+//
+// Schedule (page "KV缓存量化技术：提升大模型长文本生成效率" §2.2, residual cache): tokens
+// arrive in order; a token that finds the residual full (R tokens) first flushes those R
+// tokens into the quantized tier as one chunk.  With R = 0 each token is its own chunk
+// (page "NVFP4 KV缓存技术详解" §2.1, update phase).  A chunk goes to the old tier (page
+// "KV缓存量化技术…" §4.2, stronger quantization for early blocks) when every token in it is
+// at least old_after positions behind the length reached at the end of the append call.
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+using namespace kvq;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool is_quant_fmt(int f) { return f == kFmtInt2 || f == kFmtInt4 || f == kFmtInt8 || f == kFmtNvfp4; }
+
+// Items per (b, h) and segment never exceed this, so the workspace has a fixed bound.
+constexpr int kMaxItemsPerSeg = 64;
+
+struct LayerState {
+  int64_t length = 0;  // tokens cached
+  int64_t res = 0;     // tokens in the residual
+  int64_t young = 0;   // slots used in the young arena
+  int64_t old = 0;     // slots used in the old arena
+};
+
+struct Geometry {
+  int64_t young_cap_blocks = 0, old_cap_blocks = 0;
+  size_t res_bh = 0, young_bh = 0, old_bh = 0;   // bytes per (b, h)
+  size_t off_res = 0, off_young = 0, off_old = 0; // offsets inside a layer
+  size_t layer_bytes = 0;
+};
+
+const char *check_config(const kvq_config *c) {
+  if (!c) return "cfg is NULL";
+  if (c->num_layers < 1 || c->batch < 1 || c->num_kv_heads < 1) return "num_layers, batch and num_kv_heads must be >= 1";
+  if (c->head_dim != kHeadDim) return "head_dim must be 128";
+  if (c->max_tokens < 1) return "max_tokens must be >= 1";
+  if (!is_quant_fmt(c->format)) return "format must be KVQ_FMT_INT2/INT4/INT8/NVFP4";
+  if (c->format == kFmtNvfp4 ? c->group_size != kNvBlock : c->group_size != kGroup)
+    return "group_size must be 64 for affine formats and 16 for NVFP4";
+  if (c->residual_len < 0 || c->residual_len > 1024 || c->residual_len % 16 != 0)
+    return "residual_len must be 0 or a multiple of 16 up to 1024";
+  if (c->old_after < 0) return "old_after must be >= 0";
+  if (c->old_after > 0) {
+    if (!is_quant_fmt(c->old_format)) return "old_format must be a quantized format when old_after > 0";
+  }
+  return nullptr;
+}
+
+Geometry geometry(const kvq_config *c) {
+  Geometry g;
+  const size_t bh = (size_t)c->batch * (size_t)c->num_kv_heads;
+  g.young_cap_blocks = ceil_div(c->max_tokens, kBlock);
+  g.old_cap_blocks = c->old_after > 0 && c->max_tokens > c->old_after ? ceil_div(c->max_tokens - c->old_after, kBlock) : 0;
+  g.res_bh = (size_t)512 * (size_t)c->residual_len;
+  g.young_bh = (size_t)g.young_cap_blocks * block_bytes(c->format);
+  g.old_bh = g.old_cap_blocks ? (size_t)g.old_cap_blocks * block_bytes(c->old_format) : 0;
+  g.off_res = 0;
+  g.off_young = align_up(bh * g.res_bh);
+  g.off_old = g.off_young + align_up(bh * g.young_bh);
+  g.layer_bytes = g.off_old + align_up(bh * g.old_bh);
+  return g;
+}
+
+}  // namespace
+
+struct kvq_cache {
+  kvq_config cfg;
+  Geometry geo;
+  uint8_t *base = nullptr;
+  size_t bytes = 0;
+  std::vector<LayerState> layers;
+  int plan_only = 0;
+  int num_cus = 0;
+
+  uint8_t *layer_base(int l) const { return base + (size_t)l * geo.layer_bytes; }
+  uint8_t *res(int l) const { return layer_base(l) + geo.off_res; }
+  uint8_t *young(int l) const { return layer_base(l) + geo.off_young; }
+  uint8_t *old(int l) const { return layer_base(l) + geo.off_old; }
+};
+
+namespace {
+
+int check_cache(const kvq_cache *c, int32_t layer) {
+  if (!c) return fail(KVQ_EINVAL, "cache handle is NULL");
+  if (layer < 0 || layer >= c->cfg.num_layers) return fail(KVQ_EINVAL, "layer %d out of range [0, %d)", layer, c->cfg.num_layers);
+  return KVQ_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int hip_check(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(KVQ_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return KVQ_OK;
+}
+
+// ---------------------------------------------------------------------------- append plan
+
+struct Op {
+  enum Kind { kResCopy, kQuantInput, kQuantResidual } kind;
+  int64_t src_tok0, count, dst_slot0;
+  int tier;  // 0 young, 1 old (quantize ops)
+};
+
+struct Plan {
+  std::vector<Op> ops;
+  LayerState after;
+};
+
+// Tier of a chunk ending at stream position `end` (exclusive) in an append ending at L1.
+int chunk_tier(const kvq_config &cfg, int64_t end, int64_t L1) {
+  return (cfg.old_after > 0 && end <= L1 - cfg.old_after) ? 1 : 0;
+}
+
+void add_quant(Plan &p, Op::Kind kind, int64_t src0, int64_t count, int tier) {
+  if (count <= 0) return;
+  Op op{kind, src0, count, tier ? p.after.old : p.after.young, tier};
+  (tier ? p.after.old : p.after.young) += count;
+  // merge with the previous op when it continues the same tier from the same source
+  if (!p.ops.empty()) {
+    Op &b = p.ops.back();
+    if (b.kind == kind && kind == Op::kQuantInput && b.tier == tier && b.src_tok0 + b.count == src0 &&
+        b.dst_slot0 + b.count == op.dst_slot0) {
+      b.count += count;
+      return;
+    }
+  }
+  p.ops.push_back(op);
+}
+
+Plan plan_append(const kvq_config &cfg, const LayerState &st, int64_t n) {
+  Plan p;
+  p.after = st;
+  const int64_t R = cfg.residual_len, L = st.length, L1 = L + n, r = st.res;
+  p.after.length = L1;
+  if (R == 0) {
+    int64_t n_old = 0;
+    if (cfg.old_after > 0) n_old = std::min<int64_t>(n, std::max<int64_t>(0, L1 - cfg.old_after - L));
+    add_quant(p, Op::kQuantInput, 0, n_old, 1);
+    add_quant(p, Op::kQuantInput, n_old, n - n_old, 0);
+    return p;
+  }
+  const int64_t total = r + n;
+  if (total <= R) {
+    p.ops.push_back(Op{Op::kResCopy, 0, n, r, 0});
+    p.after.res = total;
+    return p;
+  }
+  const int64_t r_final = (total - 1) % R + 1;
+  const int64_t n_chunks = (total - r_final) / R;
+  int64_t c0 = 0;
+  if (r > 0) {
+    p.ops.push_back(Op{Op::kResCopy, 0, R - r, r, 0});            // top the residual up to R
+    add_quant(p, Op::kQuantResidual, 0, R, chunk_tier(cfg, L - r + R, L1));
+    c0 = 1;
+  }
+  for (int64_t c = c0; c < n_chunks; ++c)                        // chunk c = input [cR - r, cR - r + R)
+    add_quant(p, Op::kQuantInput, c * R - r, R, chunk_tier(cfg, L - r + (c + 1) * R, L1));
+  p.ops.push_back(Op{Op::kResCopy, n - r_final, r_final, 0, 0});
+  p.after.res = r_final;
+  return p;
+}
+
+int run_plan(kvq_cache *c, int layer, const Plan &p, const void *k, const void *v, int64_t n, hipStream_t s) {
+  const auto &cfg = c->cfg;
+  // capacity of the tier arenas follows from max_tokens; checked again here
+  if (p.after.young > c->geo.young_cap_blocks * kBlock || p.after.old > c->geo.old_cap_blocks * kBlock)
+    return fail(KVQ_ECAPACITY, "tier arena full (young %lld/%lld, old %lld/%lld slots)", (long long)p.after.young,
+                (long long)(c->geo.young_cap_blocks * kBlock), (long long)p.after.old, (long long)(c->geo.old_cap_blocks * kBlock));
+  if (c->plan_only) return KVQ_OK;
+  for (const Op &op : p.ops) {
+    if (op.kind == Op::kResCopy) {
+      ResCopyArgs a{};
+      a.k_src = (const uint16_t *)k; a.v_src = (const uint16_t *)v; a.src_ntok = n;
+      a.src_tok0 = op.src_tok0; a.count = op.count;
+      a.res_base = c->res(layer); a.res_bh_stride = (int64_t)c->geo.res_bh; a.res_len = cfg.residual_len;
+      a.dst_slot0 = op.dst_slot0; a.B = cfg.batch; a.H = cfg.num_kv_heads;
+      if (int e = hip_check(launch_residual_copy(a, s), "residual copy")) return e;
+    } else {
+      QuantArgs a{};
+      a.src_kind = op.kind == Op::kQuantInput ? 0 : 1;
+      a.k_src = (const uint16_t *)k; a.v_src = (const uint16_t *)v; a.src_ntok = n;
+      a.res_base = c->res(layer); a.res_bh_stride = (int64_t)c->geo.res_bh; a.res_len = cfg.residual_len;
+      a.src_tok0 = op.src_tok0; a.count = op.count;
+      a.arena = op.tier ? c->old(layer) : c->young(layer);
+      a.arena_bh_stride = (int64_t)(op.tier ? c->geo.old_bh : c->geo.young_bh);
+      a.dst_slot0 = op.dst_slot0;
+      a.fmt = op.tier ? cfg.old_format : cfg.format;
+      a.B = cfg.batch; a.H = cfg.num_kv_heads;
+      if (int e = hip_check(launch_quantize(a, s), "quantize")) return e;
+    }
+  }
+  return KVQ_OK;
+}
+
+// ---------------------------------------------------------------------------- decode plan
+
+struct DecodePlan {
+  DecodeSeg seg[3];  // old tier, young tier, residual
+  int nseg = 0;
+  int n_items = 0;
+};
+
+DecodePlan plan_decode(const kvq_cache *c, int layer) {
+  const auto &cfg = c->cfg;
+  const LayerState &st = c->layers[layer];
+  DecodePlan p;
+  const int64_t bh = (int64_t)cfg.batch * cfg.num_kv_heads;
+  const int64_t nb_old = ceil_div(st.old, kBlock), nb_young = ceil_div(st.young, kBlock);
+  const int cus = c->num_cus > 0 ? c->num_cus : 256;
+  const int64_t target_items = 8LL * cus;  // one-wave work items across the whole grid
+  int64_t bpi = std::max<int64_t>(1, ceil_div((nb_old + nb_young) * bh, target_items));
+  auto add_tier = [&](const uint8_t *base, int64_t bh_stride, int64_t ntok, int64_t nb, int fmt) {
+    if (nb == 0) return;
+    int64_t u = std::max<int64_t>(bpi, ceil_div(nb, kMaxItemsPerSeg));
+    DecodeSeg &s = p.seg[p.nseg++];
+    s.base = base; s.bh_stride = bh_stride; s.ntok = ntok; s.fmt = fmt;
+    s.units_per_item = (int)u; s.n_items = (int)ceil_div(nb, u); s.item0 = p.n_items; s.res_len = 0;
+    p.n_items += s.n_items;
+  };
+  add_tier(c->old(layer), (int64_t)c->geo.old_bh, st.old, nb_old, cfg.old_format);
+  add_tier(c->young(layer), (int64_t)c->geo.young_bh, st.young, nb_young, cfg.format);
+  if (st.res > 0) {
+    DecodeSeg &s = p.seg[p.nseg++];
+    s.base = c->res(layer); s.bh_stride = (int64_t)c->geo.res_bh; s.ntok = st.res; s.fmt = kFmtFp16;
+    s.units_per_item = (int)ceil_div(st.res, 32); s.n_items = 1; s.item0 = p.n_items; s.res_len = cfg.residual_len;
+    p.n_items += 1;
+  }
+  return p;
+}
+
+size_t workspace_bound(const kvq_cache *c, int32_t num_q_heads) {
+  const size_t items = 2 * kMaxItemsPerSeg + 1;
+  return items * (size_t)c->cfg.batch * (size_t)num_q_heads * kPartialStride * sizeof(float);
+}
+
+}  // namespace
+
+// ============================================================================== C ABI
+
+extern "C" {
+
+size_t kvq_cache_bytes(const kvq_config *cfg) {
+  if (const char *e = check_config(cfg)) {
+    fail(KVQ_EINVAL, "%s", e);
+    return 0;
+  }
+  return geometry(cfg).layer_bytes * (size_t)cfg->num_layers;
+}
+
+int kvq_cache_create(const kvq_config *cfg, void *dev_buf, size_t dev_bytes, kvq_cache **out) {
+  if (!out) return fail(KVQ_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (const char *e = check_config(cfg)) return fail(KVQ_EINVAL, "%s", e);
+  if (!dev_buf) return fail(KVQ_EINVAL, "dev_buf is NULL");
+  if (((uintptr_t)dev_buf % kAlign) != 0) return fail(KVQ_EINVAL, "dev_buf must be 256-byte aligned");
+  const size_t need = kvq_cache_bytes(cfg);
+  if (dev_bytes < need) return fail(KVQ_ENOSPACE, "dev_bytes %zu < required %zu", dev_bytes, need);
+  kvq_cache *c = new (std::nothrow) kvq_cache();
+  if (!c) return fail(KVQ_EINVAL, "out of host memory");
+  c->cfg = *cfg;
+  if (c->cfg.old_after == 0) c->cfg.old_format = c->cfg.format;
+  c->geo = geometry(cfg);
+  c->base = (uint8_t *)dev_buf;
+  c->bytes = dev_bytes;
+  c->layers.assign(cfg->num_layers, LayerState{});
+  *out = c;
+  g_err.clear();
+  return KVQ_OK;
+}
+
+int kvq_cache_destroy(kvq_cache *c) {
+  delete c;
+  return KVQ_OK;
+}
+
+int kvq_cache_reset(kvq_cache *c) {
+  if (!c) return fail(KVQ_EINVAL, "cache handle is NULL");
+  for (auto &l : c->layers) l = LayerState{};
+  return KVQ_OK;
+}
+
+int kvq_set_plan_only(kvq_cache *c, int32_t plan_only) {
+  if (!c) return fail(KVQ_EINVAL, "cache handle is NULL");
+  c->plan_only = plan_only ? 1 : 0;
+  return KVQ_OK;
+}
+
+int kvq_append(kvq_cache *c, int32_t layer, const void *k, const void *v, int64_t n_tokens, void *stream) {
+  if (int e = check_cache(c, layer)) return e;
+  if (n_tokens < 0) return fail(KVQ_EINVAL, "n_tokens < 0");
+  if (n_tokens == 0) return KVQ_OK;
+  if (!k || !v) return fail(KVQ_EINVAL, "k or v is NULL");
+  if (!aligned16(k) || !aligned16(v)) return fail(KVQ_EINVAL, "k and v must be 16-byte aligned");
+  LayerState &st = c->layers[layer];
+  if (st.length + n_tokens > c->cfg.max_tokens)
+    return fail(KVQ_ECAPACITY, "layer %d: %lld + %lld tokens exceeds max_tokens %lld", layer, (long long)st.length,
+                (long long)n_tokens, (long long)c->cfg.max_tokens);
+  Plan p = plan_append(c->cfg, st, n_tokens);
+  int e = run_plan(c, layer, p, k, v, n_tokens, (hipStream_t)stream);
+  if (e == KVQ_OK || e == KVQ_EHIP) st = p.after;
+  return e;
+}
+
+int kvq_flush_residual(kvq_cache *c, int32_t layer, void *stream) {
+  if (int e = check_cache(c, layer)) return e;
+  LayerState &st = c->layers[layer];
+  if (st.res == 0) return KVQ_OK;
+  Plan p;
+  p.after = st;
+  add_quant(p, Op::kQuantResidual, 0, st.res, chunk_tier(c->cfg, st.length, st.length));
+  p.after.res = 0;
+  int e = run_plan(c, layer, p, nullptr, nullptr, 0, (hipStream_t)stream);
+  if (e == KVQ_OK || e == KVQ_EHIP) st = p.after;
+  return e;
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t num_q_heads) {
+  if (!c || num_q_heads < 1 || num_q_heads % c->cfg.num_kv_heads != 0) return 0;
+  return workspace_bound(c, num_q_heads);
+}
+
+int kvq_decode_attn(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_heads, float softmax_scale, void *out,
+                    int32_t out_fp32, void *workspace, size_t ws_bytes, void *stream) {
+  if (int e = check_cache(c, layer)) return e;
+  const auto &cfg = c->cfg;
+  if (num_q_heads < 1 || num_q_heads % cfg.num_kv_heads != 0)
+    return fail(KVQ_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads, cfg.num_kv_heads);
+  const int G = num_q_heads / cfg.num_kv_heads;
+  if (G > 16) return fail(KVQ_EINVAL, "query heads per kv head (%d) must be <= 16", G);
+  if (!q || !out || !workspace) return fail(KVQ_EINVAL, "q, out and workspace must be non-NULL");
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return fail(KVQ_EINVAL, "q, out and workspace must be 16-byte aligned");
+  if (!(softmax_scale == softmax_scale)) return fail(KVQ_EINVAL, "softmax_scale is NaN");
+  if (ws_bytes < workspace_bound(c, num_q_heads))
+    return fail(KVQ_ENOSPACE, "workspace %zu < required %zu", ws_bytes, workspace_bound(c, num_q_heads));
+  if (c->layers[layer].length == 0) return fail(KVQ_ESTATE, "layer %d is empty", layer);
+  if (c->plan_only) return KVQ_OK;
+  if (c->num_cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      c->num_cus = n;
+    else
+      c->num_cus = 256;
+  }
+  DecodePlan p = plan_decode(c, layer);
+  DecodeArgs a{};
+  a.q = (const uint16_t *)q;
+  a.partials = (float *)workspace;
+  a.n_items_total = p.n_items;
+  a.B = cfg.batch; a.H = cfg.num_kv_heads; a.G = G;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipStream_t s = (hipStream_t)stream;
+  for (int i = 0; i < p.nseg; ++i) {
+    if (int e = hip_check(launch_decode_segment(a, p.seg[i], s), "decode partial")) return e;
+  }
+  return hip_check(launch_merge(a, out, out_fp32, s), "decode merge");
+}
+
+int kvq_seq_len(const kvq_cache *c, int32_t layer, int64_t *total, int64_t *in_residual) {
+  if (int e = check_cache(c, layer)) return e;
+  if (total) *total = c->layers[layer].length;
+  if (in_residual) *in_residual = c->layers[layer].res;
+  return KVQ_OK;
+}
+
+int kvq_layout(const kvq_cache *c, int32_t layer, int32_t region, size_t *offset, size_t *bytes, int64_t *tokens) {
+  if (int e = check_cache(c, layer)) return e;
+  const size_t bh = (size_t)c->cfg.batch * c->cfg.num_kv_heads;
+  const size_t lb = (size_t)layer * c->geo.layer_bytes;
+  size_t off, nb;
+  int64_t t;
+  switch (region) {
+    case 0: off = lb + c->geo.off_res; nb = bh * c->geo.res_bh; t = c->layers[layer].res; break;
+    case 1: off = lb + c->geo.off_young; nb = bh * c->geo.young_bh; t = c->layers[layer].young; break;
+    case 2: off = lb + c->geo.off_old; nb = bh * c->geo.old_bh; t = c->layers[layer].old; break;
+    default: return fail(KVQ_EINVAL, "region %d is not 0, 1 or 2", region);
+  }
+  if (offset) *offset = off;
+  if (bytes) *bytes = nb;
+  if (tokens) *tokens = t;
+  return KVQ_OK;
+}
+
+const char *kvq_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,320 @@
+// Quantize-and-pack kernels of libkvq (gfx950): affine INT2/INT4/INT8 groups of 64 and
+// NVFP4 blocks of 16, written into 128-slot cache blocks, plus the fp16 residual copy.
+//
+// Affine: page "KV缓存量化技术：提升大模型长文本生成效率" §2.1 (S = (max-min)/(2^n-1),
+// Z = round(-min/S), groups of 64); codes q = clamp(round(x/S) + Z, 0, 2^n-1).
+// NVFP4: page "NVFP4 KV缓存技术详解" §2.1 (16 values share an FP8 scale) and §4.2
+// (clip to 6): s = E4M3_RNE(amax/6), code = sign*8 + E2M1_RNE(min(|x|/s, 6)).
+//
+// Every rounding is decided exactly:
+//  * S: fp64 (max - min) is exact for fp16 inputs; the fp64 quotient by 2^n-1 is never
+//    closer to an fp16 rounding midpoint than its own error, so one fp64 -> fp16 RNE of
+//    it equals the exact rounding.
+//  * Z: fp64 -min/S, then round-half-even (same argument with half-integers).
+//  * codes: k = rint(x * (1/S)) is within one of round(x/S); the remainder x - k*S is exact
+//    in fp32 (one fma), and comparing it with S/2 fixes k, ties to even.
+//  * E4M3: fp32 amax/6 (correctly rounded) is never closer to an E4M3 midpoint than its
+//    error unless it lies on it exactly; it is then rounded to 3 mantissa bits, ties even.
+//  * E2M1: |x| is compared with midpoint*s, both exact in fp32.
+#include "kvq_internal.h"
+
+#include <cmath>
+
+namespace kvq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowHalves = 136;  // LDS row stride (halves) of the staged fp16 tokens
+
+__device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// Round a double to the nearest binary16, ties to even; zero becomes +0.
+__device__ uint16_t f64_to_f16_rne(double v) {
+  if (v == 0.0) return 0;
+  uint16_t sign = v < 0 ? 0x8000 : 0;
+  double a = fabs(v);
+  if (a >= 65520.0) return sign | 0x7C00;
+  if (a < 6.103515625e-05) {                        // below 2^-14: multiples of 2^-24
+    double k = rint(a * 16777216.0);                // exact scaling, round half even
+    return sign | (uint16_t)k;                      // k = 1024 is the smallest normal
+  }
+  uint64_t bits = (uint64_t)__double_as_longlong(a);
+  int e = (int)((bits >> 52) & 0x7FF) - 1023;       // -14..15
+  uint64_t m = bits & ((1ull << 52) - 1);
+  uint32_t keep = (uint32_t)(m >> 42);
+  uint64_t rem = m & ((1ull << 42) - 1), half = 1ull << 41;
+  if (rem > half || (rem == half && (keep & 1))) ++keep;
+  if (keep == 1024) { keep = 0; ++e; }
+  if (e > 15) return sign | 0x7C00;
+  return sign | (uint16_t)((e + 15) << 10) | (uint16_t)keep;
+}
+
+// Non-negative float -> OCP E4M3 byte, round to nearest even, saturating at 448 (0x7E).
+__device__ uint8_t f32_to_e4m3(float v) {
+  if (v >= 448.0f) return 0x7E;
+  if (v < 0.015625f) return (uint8_t)rintf(v * 512.0f);   // below 2^-6: multiples of 2^-9 (8 -> 0x08)
+  uint32_t bits = __float_as_uint(v);
+  int e = (int)((bits >> 23) & 0xFF) - 127;                // -6..8
+  uint32_t m = bits & 0x7FFFFF;
+  uint32_t keep = m >> 20, rem = m & 0xFFFFF, half = 0x80000;
+  if (rem > half || (rem == half && (keep & 1))) ++keep;
+  if (keep == 8) { keep = 0; ++e; }
+  uint32_t code = ((uint32_t)(e + 7) << 3) | keep;
+  return (uint8_t)(code > 0x7E ? 0x7E : code);
+}
+
+__device__ float e4m3_to_f32(uint32_t b) {
+  uint32_t e = (b >> 3) & 0xF, m = b & 7;
+  float mag = e == 0 ? (float)m * 0.001953125f : ldexpf(1.0f + (float)m * 0.125f, (int)e - 7);
+  return (b & 0x80) ? -mag : mag;
+}
+
+// round-half-even of x/S for fp16-valued x and S > 0 with |x/S| < 2^20; inv ~ 1/S.
+__device__ __forceinline__ float div_rne(float x, float S, float inv) {
+  float k = rintf(x * inv);
+  float r = fmaf(-k, S, x);       // exact
+  float h = 0.5f * S;             // exact
+  bool odd = ((int)k & 1) != 0;
+  if (r > h || (r == h && odd)) k += 1.0f;
+  else if (r < -h || (r == -h && odd)) k -= 1.0f;
+  return k;
+}
+
+__device__ __forceinline__ uint32_t affine_code(float x, float S, float inv, float Z, int qmax) {
+  float q = div_rne(x, S, inv) + Z;
+  q = fminf(fmaxf(q, 0.0f), (float)qmax);
+  return (uint32_t)q;
+}
+
+__device__ __forceinline__ uint32_t e2m1_code(float x, float s) {
+  float a = fabsf(x);
+  uint32_t idx = 0;
+  if (s > 0.0f) {
+    const float t0 = 0.25f * s, t1 = 0.75f * s, t2 = 1.25f * s, t3 = 1.75f * s, t4 = 2.5f * s, t5 = 3.5f * s, t6 = 5.0f * s;
+    idx = (a > t0) + (a > t1) + (a > t2) + (a > t3) + (a > t4) + (a > t5) + (a > t6);
+    bool tie = a == t0 || a == t1 || a == t2 || a == t3 || a == t4 || a == t5 || a == t6;
+    if (tie && (idx & 1)) ++idx;   // on midpoint idx: pick the even neighbour
+  }
+  return idx | (signbit(x) ? 8u : 0u);
+}
+
+// V-row field order: slot held by field k' of 32-bit word j in quarter q (n-bit fields).
+__device__ __forceinline__ int v_field_slot(int nbits, int q, int j, int kp) {
+  const int F = 32 / nbits, halfF = F / 2;
+  const int s = kp % halfF, hi = kp / halfF;
+  const int tau = (F / 4) * j + 2 * (s / 4) + ((s % 4) / 2);
+  const int i = 2 * (s % 2) + hi;
+  return 16 * tau + 4 * q + i;
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t blk0, int64_t nblk) {
+  constexpr bool kNv = FMT == kFmtNvfp4;
+  constexpr int kBits = kNv ? 4 : FMT;
+  constexpr int kRowBytes = 16 * kBits;           // bytes per code row (128 fields)
+  constexpr int kWordsPerRow = kRowBytes / 4;
+  constexpr int kQmax = (1 << kBits) - 1;
+  constexpr size_t kBlockBytes = kNv ? kNvfp4BlockBytes : affine_block_bytes(kBits);
+
+  __shared__ __align__(16) uint16_t xs[kBlock * kRowHalves];
+  __shared__ float mS[kBlock][8];     // affine: S per group (2 used); NVFP4: scale per 16-block
+  __shared__ float mInv[kBlock][2];
+  __shared__ float mZ[kBlock][2];
+
+  const int tid = threadIdx.x;
+  const int64_t blk = blk0 + blockIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z >> 1, kv = blockIdx.z & 1;
+  const int64_t bstart = blk * kBlock;
+  const int lo = (int)(max(a.dst_slot0, bstart) - bstart);
+  const int hi = (int)(min(a.dst_slot0 + a.count, bstart + kBlock) - bstart);
+  const bool last = blockIdx.x == nblk - 1;
+  const int zhi = last ? kBlock : hi;             // slots [hi, zhi) are cleared
+  uint8_t *blkp = a.arena + (int64_t)(b * a.H + h) * a.arena_bh_stride + blk * (int64_t)kBlockBytes;
+  const int64_t tok_off = a.src_tok0 + bstart - a.dst_slot0;   // source index of slot 0
+
+  // ---- stage the source tokens of slots [lo, hi) in LDS as fp16 rows
+  if (a.src_kind == 0 || kv == 0) {
+    const uint8_t *src;
+    int64_t row_stride;
+    if (a.src_kind == 0) {
+      src = (const uint8_t *)(kv ? a.v_src : a.k_src) + (int64_t)(b * a.H + h) * a.src_ntok * 256;
+      row_stride = 256;
+    } else {
+      src = a.res_base + (int64_t)(b * a.H + h) * a.res_bh_stride;   // residual K [R][128]
+      row_stride = 256;
+    }
+    const int nchunks = (hi - lo) * 16;
+    for (int c = tid; c < nchunks; c += kThreads) {
+      const int row = lo + c / 16, col = c % 16;
+      uint4 v = *(const uint4 *)(src + (tok_off + row) * row_stride + col * 16);
+      *(uint4 *)&xs[row * kRowHalves + col * 8] = v;
+    }
+  } else {
+    // residual V: [R/16][128][16] fp16
+    const uint16_t *src = (const uint16_t *)(a.res_base + (int64_t)(b * a.H + h) * a.res_bh_stride + (int64_t)a.res_len * 256);
+    const int nel = (hi - lo) * kHeadDim;
+    for (int e = tid; e < nel; e += kThreads) {
+      const int row = lo + e / kHeadDim, d = e % kHeadDim;
+      const int64_t t = tok_off + row;
+      xs[row * kRowHalves + d] = src[((t / 16) * kHeadDim + d) * 16 + t % 16];
+    }
+  }
+  __syncthreads();
+
+  // ---- per-group metadata
+  if constexpr (!kNv) {
+    const int slot = tid >> 1, g = tid & 1;
+    uint32_t Sb = 0, Zb = 0;
+    bool write = false;
+    if (slot >= lo && slot < hi) {
+      float mn = INFINITY, mx = -INFINITY;
+      for (int d = 0; d < kGroup; ++d) {
+        float x = h2f(xs[slot * kRowHalves + g * kGroup + d]);
+        mn = fminf(mn, x);
+        mx = fmaxf(mx, x);
+      }
+      float S = 0.0f;
+      if (mx > mn) {
+        Sb = f64_to_f16_rne(((double)mx - (double)mn) / (double)kQmax);
+        S = h2f((uint16_t)Sb);
+      }
+      if (!(mx > mn) || S == 0.0f) {          // degenerate group: S = |min|, or 1 when min is 0
+        S = mn != 0.0f ? fabsf(mn) : 1.0f;
+        Sb = __builtin_bit_cast(uint16_t, (_Float16)S);
+      }
+      double z = rint(-(double)mn / (double)S);
+      z = fmin(fmax(z, -65504.0), 65504.0);
+      Zb = f64_to_f16_rne(z);
+      mS[slot][g] = S;
+      mInv[slot][g] = 1.0f / S;
+      mZ[slot][g] = h2f((uint16_t)Zb);
+      write = true;
+    } else if (slot >= hi && slot < zhi) {
+      write = true;                            // cleared slot: S = Z = +0
+    }
+    if (write) {
+      if (kv == 0) {
+        *(uint32_t *)(blkp + aff_km(kBits) + slot * 8 + g * 4) = Sb | (Zb << 16);
+      } else {
+        const int q = (slot % 16) / 4, tau = slot / 16, i = slot % 4;
+        uint8_t *e = blkp + aff_vm(kBits) + ((g * 4 + q) * 8 + tau) * 16;
+        *(uint16_t *)(e + 2 * i) = (uint16_t)Sb;
+        *(uint16_t *)(e + 8 + 2 * i) = (uint16_t)Zb;
+      }
+    }
+  } else {
+    for (int idx = tid; idx < kBlock * 8; idx += kThreads) {
+      const int slot = idx >> 3, nb = idx & 7;
+      uint8_t sb = 0;
+      bool write = false;
+      if (slot >= lo && slot < hi) {
+        float amax = 0.0f;
+        for (int d = 0; d < kNvBlock; ++d) amax = fmaxf(amax, fabsf(h2f(xs[slot * kRowHalves + nb * kNvBlock + d])));
+        sb = f32_to_e4m3(amax / 6.0f);
+        mS[slot][nb] = e4m3_to_f32(sb);
+        write = true;
+      } else if (slot >= hi && slot < zhi) {
+        write = true;
+      }
+      if (write) {
+        if (kv == 0) {
+          blkp[kNvKs + slot * 8 + nb] = sb;
+        } else {
+          const int q = (slot % 16) / 4, tau = slot / 16, i = slot % 4;
+          blkp[kNvVs + nb * 128 + 32 * q + 4 * tau + i] = sb;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- codes, one 32-bit word per thread iteration
+  constexpr int F = 32 / kBits;                     // fields per word
+  constexpr int kWords = kBlock * kWordsPerRow;
+  if (kv == 0) {
+    // K: row = slot, field = dim
+    for (int w = tid; w < kWords; w += kThreads) {
+      const int slot = w / kWordsPerRow, wi = w % kWordsPerRow;
+      if (slot < lo || slot >= zhi) continue;
+      uint32_t word = 0;
+      if (slot < hi) {
+        for (int k = 0; k < F; ++k) {
+          const int d = wi * F + k;
+          const float x = h2f(xs[slot * kRowHalves + d]);
+          uint32_t c;
+          if constexpr (kNv) c = e2m1_code(x, mS[slot][d / kNvBlock]);
+          else c = affine_code(x, mS[slot][d / kGroup], mInv[slot][d / kGroup], mZ[slot][d / kGroup], kQmax);
+          word |= c << (k * kBits);
+        }
+      }
+      *(uint32_t *)(blkp + slot * kRowBytes + wi * 4) = word;
+    }
+  } else {
+    // V: row = dim, fields in the lane-quarter slot order
+    const size_t vc = kNv ? kNvVc : aff_vc(kBits);
+    for (int w = tid; w < kWords; w += kThreads) {
+      const int d = w / kWordsPerRow, wi = w % kWordsPerRow;
+      const int q = wi / kBits, j = wi % kBits;       // kBits words per quarter
+      uint32_t *dst = (uint32_t *)(blkp + vc + d * kRowBytes + wi * 4);
+      bool any = false, keep_any = false;
+      for (int k = 0; k < F; ++k) {
+        const int slot = v_field_slot(kBits, q, j, k);
+        any |= slot >= lo && slot < zhi;
+        keep_any |= slot < lo;
+      }
+      if (!any) continue;
+      uint32_t word = keep_any ? *dst : 0u;
+      for (int k = 0; k < F; ++k) {
+        const int slot = v_field_slot(kBits, q, j, k);
+        if (slot < lo || slot >= zhi) continue;
+        uint32_t c = 0;
+        if (slot < hi) {
+          const float x = h2f(xs[slot * kRowHalves + d]);
+          if constexpr (kNv) c = e2m1_code(x, mS[slot][d / kNvBlock]);
+          else c = affine_code(x, mS[slot][d / kGroup], mInv[slot][d / kGroup], mZ[slot][d / kGroup], kQmax);
+        }
+        const uint32_t mask = (uint32_t)kQmax << (k * kBits);
+        word = (word & ~mask) | (c << (k * kBits));
+      }
+      *dst = word;
+    }
+  }
+}
+
+__global__ __launch_bounds__(128) void residual_copy_kernel(ResCopyArgs a) {
+  const int64_t i = blockIdx.x;                 // token of this copy
+  const int h = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
+  const int64_t tok = a.src_tok0 + i, slot = a.dst_slot0 + i;
+  const int64_t src = ((int64_t)(b * a.H + h) * a.src_ntok + tok) * kHeadDim + d;
+  uint8_t *res = a.res_base + (int64_t)(b * a.H + h) * a.res_bh_stride;
+  ((uint16_t *)res)[slot * kHeadDim + d] = a.k_src[src];
+  uint16_t *rv = (uint16_t *)(res + (int64_t)a.res_len * 256);
+  rv[((slot / 16) * kHeadDim + d) * 16 + slot % 16] = a.v_src[src];
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantArgs &a, hipStream_t s) {
+  if (a.count <= 0) return hipSuccess;
+  const int64_t blk0 = a.dst_slot0 / kBlock;
+  const int64_t blk1 = (a.dst_slot0 + a.count - 1) / kBlock;
+  const int64_t nblk = blk1 - blk0 + 1;
+  dim3 grid((unsigned)nblk, (unsigned)a.H, (unsigned)(a.B * 2));
+  switch (a.fmt) {
+    case kFmtInt2: quantize_kernel<kFmtInt2><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
+    case kFmtInt4: quantize_kernel<kFmtInt4><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
+    case kFmtInt8: quantize_kernel<kFmtInt8><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
+    case kFmtNvfp4: quantize_kernel<kFmtNvfp4><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_residual_copy(const ResCopyArgs &a, hipStream_t s) {
+  if (a.count <= 0) return hipSuccess;
+  dim3 grid((unsigned)a.count, (unsigned)a.H, (unsigned)a.B);
+  residual_copy_kernel<<<grid, kHeadDim, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,143 @@
+/* kvq.h — quantized KV cache for single-token decode on AMD MI355X (gfx950).
+ *
+ * C ABI of libkvq.so.  Two operations make up the path:
+ *   kvq_append / kvq_flush_residual  quantize and pack new K/V into the cache;
+ *   kvq_decode_attn                  attention of one query token over the whole cache,
+ *                                    dequantizing the packed bytes in registers.
+ *
+ * Method (cited by page title and section):
+ *  - affine group quantization: page "KV缓存量化技术：提升大模型长文本生成效率"
+ *    (rkmt.cn) §2.1 — per group of 64 values S = (max-min)/(2^n-1), Z = round(-min/S),
+ *    codes stored as n-bit integers; stored here as q = clamp(round(x/S)+Z, 0, 2^n-1),
+ *    decoded x_hat = S*(q-Z);
+ *  - fp16 residual of the most recent R tokens, quantized and merged when full: same page §2.2;
+ *    configuration names nbits / group_size / residual_length: same page §3.2;
+ *  - stronger quantization (INT2) for early blocks: same page §4.2;
+ *  - NVFP4: page "NVFP4 KV缓存技术详解" (glsqs.com) §2.1 — 16 values share one FP8 (E4M3)
+ *    scale; the new token is quantized and appended at each decode step;
+ *  - every decode step reads the whole history: page "KV Cache量化实战：Model Optimizer为大模型
+ *    长上下文省下50%显存" (m.nxbn.cn), section on why long context runs out of memory first.
+ *
+ * Conventions for every call:
+ *  - Device pointers are HIP device addresses owned by the caller.  The library never
+ *    allocates or frees device memory and never synchronizes the host with the device.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is
+ *    enqueued on it in call order; calls on one cache must be serialized on one stream.
+ *  - Host bookkeeping (lengths) advances when a call enqueues its work.
+ *  - Return value: KVQ_OK (0) or a negative kvq_status.  Every argument and capacity check
+ *    happens before anything is enqueued; on any error except KVQ_EHIP nothing is enqueued
+ *    and the cache state is unchanged.  KVQ_EHIP means a kernel launch failed; the
+ *    contents of that layer are then undefined.  kvq_last_error() describes the failure.
+ *  - head_dim is 128.  K/V/Q must hold finite fp16 values.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct kvq_cache kvq_cache; /* opaque host handle */
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_EINVAL = -1,    /* bad argument or configuration */
+  KVQ_ECAPACITY = -2, /* appending would exceed max_tokens */
+  KVQ_ENOSPACE = -3,  /* device buffer or workspace too small */
+  KVQ_EHIP = -4,      /* a HIP launch failed */
+  KVQ_ESTATE = -5     /* operation not valid in the current state (e.g. decode on an empty cache) */
+} kvq_status;
+
+typedef enum {
+  KVQ_FMT_FP16 = 0,  /* only as residual storage */
+  KVQ_FMT_INT2 = 2,  /* affine, 2-bit codes, group 64, fp16 S and Z */
+  KVQ_FMT_INT4 = 4,  /* affine, 4-bit codes */
+  KVQ_FMT_INT8 = 8,  /* affine, 8-bit codes */
+  KVQ_FMT_NVFP4 = 16 /* E2M1 codes, one E4M3 scale per 16 values */
+} kvq_format;
+
+typedef struct {
+  int32_t num_layers;   /* >= 1 */
+  int32_t batch;        /* >= 1 */
+  int32_t num_kv_heads; /* >= 1 */
+  int32_t head_dim;     /* must be 128 */
+  int64_t max_tokens;   /* per-sequence capacity, >= 1 */
+  int32_t format;       /* kvq_format of the (young) quantized tier ("nbits") */
+  int32_t group_size;   /* 64 for affine formats, 16 for NVFP4 ("group_size") */
+  int32_t residual_len; /* fp16 residual length R: 0 (quantize on append) or a multiple of
+                           16 up to 1024 ("residual_length"; 128 in the pages) */
+  int32_t old_format;   /* kvq_format of the old tier; ignored when old_after == 0 */
+  int64_t old_after;    /* a chunk of tokens quantized together goes to the old tier when
+                           all of them are at least old_after positions behind the length
+                           at the end of the append call; 0 disables the old tier */
+} kvq_config;
+
+/* Bytes of device memory a cache with this configuration needs (0 if cfg is invalid).
+   Host-only. */
+size_t kvq_cache_bytes(const kvq_config *cfg);
+
+/* Create a cache over caller-owned device memory dev_buf of dev_bytes bytes (256-byte
+   aligned, at least kvq_cache_bytes(cfg)).  All lengths start at 0.  Host-only: nothing
+   is enqueued and dev_buf is not touched.  *out receives the handle.
+   Errors: KVQ_EINVAL (cfg, pointers), KVQ_ENOSPACE (dev_bytes too small). */
+int kvq_cache_create(const kvq_config *cfg, void *dev_buf, size_t dev_bytes, kvq_cache **out);
+
+/* Free the host handle (not dev_buf).  NULL is accepted. */
+int kvq_cache_destroy(kvq_cache *c);
+
+/* Set every layer's length to 0 (host-only; stored bytes are overwritten by later appends). */
+int kvq_cache_reset(kvq_cache *c);
+
+/* Append n_tokens new tokens to layer `layer`.
+   k, v: fp16 [batch][num_kv_heads][n_tokens][128], contiguous, 16-byte aligned, read on the
+   stream.  Tokens are processed in order: with R > 0 a token that arrives while the
+   residual holds R tokens first flushes those R tokens into the quantized tier (one chunk),
+   then goes to the residual; with R = 0 every token is quantized at once.  Appending n
+   tokens stores exactly the bytes of n single-token appends when the old tier is off.
+   n_tokens = 0 is a no-op.  Errors: KVQ_EINVAL, KVQ_ECAPACITY, KVQ_EHIP. */
+int kvq_append(kvq_cache *c, int32_t layer, const void *k, const void *v, int64_t n_tokens, void *stream);
+
+/* Quantize the r tokens currently in the residual of `layer` (one chunk) and empty it.
+   No-op when r = 0.  Errors: KVQ_EINVAL, KVQ_EHIP. */
+int kvq_flush_residual(kvq_cache *c, int32_t layer, void *stream);
+
+/* Workspace bytes kvq_decode_attn needs for num_q_heads query heads at the current lengths
+   (the maximum over layers).  0 if the arguments are invalid. */
+size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t num_q_heads);
+
+/* Attention of one query token per (batch, query head) over every token cached in `layer`:
+   out[b][h] = softmax(softmax_scale * q[b][h] . K_hat^T) . V_hat with query head h reading kv
+   head h / (num_q_heads / num_kv_heads).
+   q: fp16 [batch][num_q_heads][128]; out: [batch][num_q_heads][128] fp32 if out_fp32 else
+   fp16; workspace: at least kvq_decode_workspace_bytes() bytes, 16-byte aligned, scratch
+   owned by the caller (its contents on entry do not matter).  The cache is not modified.
+   num_q_heads must be a multiple of num_kv_heads with a group of at most 16.
+   Errors: KVQ_EINVAL, KVQ_ENOSPACE (workspace), KVQ_ESTATE (layer empty), KVQ_EHIP. */
+int kvq_decode_attn(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_heads, float softmax_scale,
+                    void *out, int32_t out_fp32, void *workspace, size_t ws_bytes, void *stream);
+
+/* Host counters of a layer: total cached tokens and tokens currently in the residual. */
+int kvq_seq_len(const kvq_cache *c, int32_t layer, int64_t *total, int64_t *in_residual);
+
+/* Where a region of a layer lives: region 0 = fp16 residual, 1 = young tier, 2 = old tier.
+   *offset: byte offset of the region in dev_buf; *bytes: bytes of the region (all batch
+   entries and kv heads, [batch][kv_head][...]); *tokens: slots in use per (batch, kv_head).
+   Any output pointer may be NULL. */
+int kvq_layout(const kvq_cache *c, int32_t layer, int32_t region, size_t *offset, size_t *bytes, int64_t *tokens);
+
+/* Plan-only mode (1) updates the host counters exactly as the real calls do but enqueues
+   no device work; it lets the bookkeeping run on machines without a GPU.  0 restores
+   normal operation. */
+int kvq_set_plan_only(kvq_cache *c, int32_t plan_only);
+
+/* Text describing the last failure on the calling thread ("" if none). */
+const char *kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

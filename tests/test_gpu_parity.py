@@ -1,0 +1,130 @@
+"""GPU parity: packed bytes bit-exact and decode attention within 1e-3 * max|out| of the oracle.
+
+Small shapes that span several blocks and a ragged tail; every case names itself in the
+test id.  Marked gpu: run on an MI355X."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import Pair, adversarial_tokens, assert_attention_close
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = ["int2", "int4", "int8", "nvfp4"]
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("R", [0, 16, 128])
+def test_append_bytes_exact(fmt, R):
+    rng = np.random.default_rng(hash((fmt, R)) % 2 ** 32)
+    B, H = 2, 2
+    p = Pair(1, B, H, 2000, fmt, R)
+    for n in [300, 1, 1, 127, 5, "flush", 129, 1, 250]:
+        if n == "flush":
+            p.flush(0)
+            continue
+        p.append(0, adversarial_tokens(rng, B, H, n), adversarial_tokens(rng, B, H, n))
+        p.check_bytes(0)
+
+
+def test_tiers_bytes_exact():
+    rng = np.random.default_rng(77)
+    B, H = 1, 2
+    p = Pair(1, B, H, 3000, "int4", 128, "int2", 700)
+    for n in [1800, 1, 1, 300, "flush", 200]:
+        if n == "flush":
+            p.flush(0)
+            continue
+        p.append(0, adversarial_tokens(rng, B, H, n), adversarial_tokens(rng, B, H, n))
+        p.check_bytes(0)
+    assert p.gpu.layout(0, 2)[2] > 0
+
+
+def test_nvfp4_every_amax():
+    """Every positive finite fp16 value as a block maximum (so every E4M3 scale and every
+    rounding tie), with the other 15 values drawn below it, plus signed zeros."""
+    rng = np.random.default_rng(5)
+    bits = np.arange(1, 0x7C00, dtype=np.uint16)
+    amax = bits.view(np.float16).astype(np.float64)                      # 31743 values
+    n_blocks = amax.size
+    frac = rng.uniform(-1, 1, (n_blocks, 16))
+    x = (frac * amax[:, None]).astype(np.float16)
+    x[:, 0] = amax * np.where(rng.random(n_blocks) < 0.5, 1, -1)
+    x[::7, 5] = -0.0
+    ntok = -(-n_blocks // 8)
+    flat = np.zeros((ntok * 8, 16), np.float16)
+    flat[:n_blocks] = x
+    toks = flat.reshape(1, 1, ntok, 128)
+    p = Pair(1, 1, 1, ntok + 8, "nvfp4", 0)
+    p.append(0, toks, toks[..., ::-1].copy())
+    p.check_bytes(0)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("G", [1, 4, 8])
+@pytest.mark.parametrize("L", [1, 2, 127, 128, 129, 1000])
+def test_decode_matches_oracle(fmt, G, L):
+    R = 0 if fmt == "nvfp4" else 128
+    rng = np.random.default_rng(L * 31 + G)
+    B, H = 2, 2
+    p = Pair(1, B, H, 1200, fmt, R)
+    k = rng.standard_normal((B, H, L, 128)).astype(np.float16)
+    k[..., :4] *= 15
+    v = rng.standard_normal((B, H, L, 128)).astype(np.float16)
+    p.append(0, k, v)
+    q = (rng.standard_normal((B, H * G, 128)) / np.sqrt(128)).astype(np.float16)
+    for sigma in (1 / np.sqrt(128), 1.0):
+        got, want = p.decode(0, q, sigma)
+        assert_attention_close(got, want)
+
+
+@pytest.mark.parametrize("R", [16, 32, 128])
+def test_decode_residual_only_and_mixed(R):
+    rng = np.random.default_rng(R)
+    B, H, G = 1, 3, 4
+    p = Pair(1, B, H, 3000, "int4", R)
+    q = (rng.standard_normal((B, H * G, 128)) / np.sqrt(128)).astype(np.float16)
+    for n in [R // 2, R // 2, 1, 3 * R + 5, "flush", 7]:
+        if n == "flush":
+            p.flush(0)
+        else:
+            p.append(0, rng.standard_normal((B, H, n, 128)).astype(np.float16),
+                     rng.standard_normal((B, H, n, 128)).astype(np.float16))
+        got, want = p.decode(0, q, 1.0)
+        assert_attention_close(got, want)
+
+
+def test_decode_tiers_and_fp16_output():
+    rng = np.random.default_rng(3)
+    B, H, G = 1, 2, 4
+    p = Pair(1, B, H, 4000, "int4", 128, "int2", 1000)
+    p.append(0, rng.standard_normal((B, H, 3000, 128)).astype(np.float16),
+             rng.standard_normal((B, H, 3000, 128)).astype(np.float16))
+    p.append(0, rng.standard_normal((B, H, 1, 128)).astype(np.float16),
+             rng.standard_normal((B, H, 1, 128)).astype(np.float16))
+    q = (rng.standard_normal((B, H * G, 128)) / np.sqrt(128)).astype(np.float16)
+    got, want = p.decode(0, q, 1 / np.sqrt(128))
+    assert_attention_close(got, want)
+    got16, _ = p.decode(0, q, 1 / np.sqrt(128), out_dtype=torch.float16)
+    assert_attention_close(got16, want)
+
+
+def test_decode_adversarial_values():
+    rng = np.random.default_rng(11)
+    B, H, G = 1, 2, 8
+    for fmt in FORMATS:
+        p = Pair(1, B, H, 800, fmt, 0 if fmt == "nvfp4" else 128)
+        p.append(0, adversarial_tokens(rng, B, H, 700, 0.5), adversarial_tokens(rng, B, H, 700, 0.5))
+        q = (rng.standard_normal((B, H * G, 128)) / np.sqrt(128)).astype(np.float16)
+        got, want = p.decode(0, q, 1 / np.sqrt(128))
+        assert_attention_close(got, want)
+
+
+def test_decode_is_deterministic():
+    rng = np.random.default_rng(2)
+    p = Pair(1, 2, 2, 5000, "int4", 128)
+    p.append(0, rng.standard_normal((2, 2, 4500, 128)).astype(np.float16),
+             rng.standard_normal((2, 2, 4500, 128)).astype(np.float16))
+    q = (rng.standard_normal((2, 8, 128)) / np.sqrt(128)).astype(np.float16)
+    outs = [p.decode(0, q, 1.0)[0] for _ in range(3)]
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
