@@ -1,0 +1,302 @@
+"""Decode-step benchmark of the quantized KV cache on one MI355X.
+
+A step is, for every layer: append one new token (quantize + pack when the fp16 residual is
+full, else an fp16 copy into the residual) and one fused dequant + decode-attention call over
+the whole cache.  Inputs are seeded synthetic K/V/Q drawn on the GPU before the timed region.
+
+Default workload: 32 layers, batch 8, 32 query / 8 KV heads, head_dim 128, 131072 cached
+tokens per sequence in INT4 affine (group 64, fp16 S/Z, 128-token fp16 residual), Student-t
+(nu = 4) K and Gaussian V, consecutive decode steps with append and residual flushes.
+
+Output: one JSON line.  `value` is the effective HBM GB/s of the cache read (codes + scales +
+zero points + fp16 residual) summed over the timed steps, divided by their wall time.
+`roofline` gives the decode-attention call alone, timed with HIP events on the stream it is
+launched on.  `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+DECODE_SRC = os.path.join(ROOT, "bit_quantized_kv_kvq_amd", "csrc", "kvq_decode.hip")
+
+# workload name -> (config id in kvq_synth.WORKLOADS, young format override)
+WORKLOADS = {
+    "c1": (1, None), "c2": (2, None), "c3": (3, None),
+    "c4-int4": (4, "int4"), "c4-int2": (4, "int2"), "c5": (5, None),
+}
+
+
+def bytes_per_token(fmt: str) -> float:
+    """Stored bytes of one token of one (batch, kv_head), K and V together."""
+    return {"int2": 10240 / 128, "int4": 18432 / 128, "int8": 34816 / 128, "nvfp4": 18432 / 128,
+            "fp16": 512.0}[fmt]
+
+
+def decode_bytes(cache, layer: int, fmt: str, old_fmt: str) -> float:
+    """Algorithmic cache bytes one decode call reads: every cached token once."""
+    import bit_quantized_kv_kvq_amd as kvq
+    B, H = cache.cfg.batch, cache.cfg.num_kv_heads
+    n_res = cache.layout(layer, kvq.REGION_RESIDUAL)[2]
+    n_young = cache.layout(layer, kvq.REGION_YOUNG)[2]
+    n_old = cache.layout(layer, kvq.REGION_OLD)[2]
+    return B * H * (n_old * bytes_per_token(old_fmt) + n_young * bytes_per_token(fmt) + n_res * 512.0)
+
+
+def kernel_src_sha() -> str:
+    return hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per decode launch from the committed PMC summary, when it was taken on the
+    current decode kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    sha = re.search(r"kernel_src_sha:\s*([0-9a-f]+)", txt)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not sha or not val or sha.group(1) != kernel_src_sha():
+        return None
+    return float(val.group(1))
+
+
+def cpu_baseline(samples, wl, sigma, budget_s: float):
+    """Time the CPU oracle on (layer 0, b, kv_head) samples of the final cache state.
+
+    samples: list of (b, h, k chunks, v chunks, q16 [G,128], gpu_out [G,128] fp32); the chunks
+    (fp16 [n_i, 128]) are appended in order, as the GPU cache received them.
+    Returns (baseline dict, max relative error of the GPU output on the samples)."""
+    from threadpoolctl import threadpool_limits
+    from oracle.cache import LayerCache
+    from oracle.attention import decode_layer
+    used = 0
+    t_total = 0.0
+    bytes_total = 0.0
+    worst = 0.0
+    with threadpool_limits(limits=1):
+        for (b, h, kch, vch, q16, got) in samples:
+            t0 = time.perf_counter()
+            lc = LayerCache(wl["fmt"], wl["R"], wl["old_fmt"], wl["old_after"])
+            for kc, vc in zip(kch, vch):
+                lc.append(kc[None, None], vc[None, None])
+            want = decode_layer(lc, q16[None], sigma)[0]
+            dt = time.perf_counter() - t0
+            t_total += dt
+            n_tok = lc.sched.length
+            nq_y, nq_o, nr = len(lc.sched.young), len(lc.sched.old), len(lc.sched.residual)
+            bytes_total += nq_o * bytes_per_token(lc.old_fmt) + nq_y * bytes_per_token(lc.fmt) + nr * 512.0
+            worst = max(worst, float(np.abs(got - want).max() / np.abs(want).max()))
+            used += 1
+            if t_total >= budget_s:
+                break
+    return {"value": bytes_total / t_total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"layer 0, {used} (batch, kv_head) pair(s) x {n_tok} tokens at the final state: "
+                      f"quantize every token + fp64 attention of the {samples[0][4].shape[0]} query heads; "
+                      f"{t_total:.1f} s on 1 host thread"}, worst
+
+
+def copy_probe():
+    """A plain copy of a known size (1 GiB), for scaling the HBM byte counters."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": "copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n, "launches": 5}))
+
+
+def read_probe_gbs() -> float:
+    """Achievable HBM read rate: a 4 GiB sum (read-bound), best of 5."""
+    import torch
+    x = torch.ones(1 << 31, dtype=torch.float16, device="cuda")
+    best = 0.0
+    for _ in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        x.sum(dtype=torch.float32)
+        e1.record()
+        e1.synchronize()
+        best = max(best, x.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del x
+    torch.cuda.empty_cache()
+    return best
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c4-int4", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--cpu-pairs", type=int, default=48, help="(batch, kv_head) pairs of layer 0 kept for the oracle")
+    ap.add_argument("--probe", choices=["copy"], default=None)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this path runs on one GPU; (batch, kv_head) pairs, layers and token splits shard "
+              "without exchange except a final LSE merge, which is not built here. Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.probe == "copy":
+        copy_probe()
+        return
+
+    import bit_quantized_kv_kvq_amd as kvq
+    import kvq_synth as syn
+
+    cid, fmt_over = WORKLOADS[args.workload]
+    W = syn.WORKLOADS[cid]
+    fmt = fmt_over or W.fmt
+    old_fmt = W.old_fmt or fmt
+    L, B, Hq, H, T, R = W.num_layers, W.batch, W.num_q_heads, W.num_kv_heads, W.prefill, W.residual_len
+    G = Hq // H
+    sigma = 1.0 / np.sqrt(128.0)
+    per_step = max(1, W.append_per_step)
+    n_steps = args.warmup + args.steps
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    probe = read_probe_gbs()
+
+    cfg = kvq.make_config(L, B, H, T + n_steps * per_step + 1, fmt, R, W.old_fmt, W.old_after)
+    cache = kvq.Cache(cfg)
+    samples_bh = [(b, h) for b in range(B) for h in range(H)][:args.cpu_pairs]
+    host_hist = {bh: ([], []) for bh in samples_bh}
+
+    # ---- untimed state: bulk prefill of every layer (one append of T tokens)
+    t_prefill = time.perf_counter()
+    for l in range(L):
+        k = syn.draw_k_dev(cid, l, B, H, T, W.kdist)
+        v = syn.draw_v_dev(cid, l, B, H, T)
+        if l == 0:
+            for (b, h) in samples_bh:
+                host_hist[(b, h)][0].append(k[b, h].cpu().numpy())
+                host_hist[(b, h)][1].append(v[b, h].cpu().numpy())
+        cache.append(l, k, v)
+        del k, v
+        if l % 8 == 7 or l == L - 1:
+            torch.cuda.synchronize()
+            log(f"prefill: {l + 1}/{L} layers, {time.perf_counter() - t_prefill:.1f} s")
+    torch.cuda.synchronize()
+    t_prefill = time.perf_counter() - t_prefill
+
+    # ---- step inputs, resident in HBM before the timed region
+    knew = [[syn.draw_k_dev(cid, l, B, H, per_step, W.kdist, syn.STREAM_K_APPEND, s) for l in range(L)]
+            for s in range(n_steps)]
+    vnew = [[syn.draw_v_dev(cid, l, B, H, per_step, syn.STREAM_V_APPEND, s) for l in range(L)]
+            for s in range(n_steps)]
+    qs = [[syn.draw_q_dev(cid, l, B, Hq, s) for l in range(L)] for s in range(n_steps)]
+    for s in range(n_steps):
+        for (b, h) in samples_bh:
+            host_hist[(b, h)][0].append(knew[s][0][b, h].cpu().numpy())
+            host_hist[(b, h)][1].append(vnew[s][0][b, h].cpu().numpy())
+    ws = torch.empty(cache.workspace_bytes(Hq), dtype=torch.uint8, device=dev)
+    outs = [torch.empty((B, Hq, 128), dtype=torch.float16, device=dev) for _ in range(L)]
+    torch.cuda.synchronize()
+
+    def step(s, events=None, nbytes=None):
+        for l in range(L):
+            cache.append(l, knew[s][l], vnew[s][l])
+            if nbytes is not None:
+                nbytes.append(decode_bytes(cache, l, fmt, old_fmt))
+            if events is not None:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                cache.decode(l, qs[s][l], sigma, outs[l], ws)
+                e1.record(stream)
+                events.append((e0, e1))
+            else:
+                cache.decode(l, qs[s][l], sigma, outs[l], ws)
+
+    log("step inputs ready; warmup")
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+
+    events, nbytes = [], []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.warmup, n_steps):
+        step(s, events, nbytes)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"timed {args.steps} steps in {wall:.3f} s")
+
+    dec_ms = np.array([a.elapsed_time(b) for a, b in events])
+    nbytes = np.array(nbytes)
+    total_bytes = float(nbytes.sum())
+    value = total_bytes / wall / 1e9
+    achieved = float(nbytes.mean() / (dec_ms.mean() * 1e-3) / 1e9)
+
+    # ---- parity on sampled outputs at full size: one more fp32 decode of layer 0
+    out32 = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+    cache.decode(0, qs[n_steps - 1][0], sigma, out32, ws)
+    torch.cuda.synchronize()
+    out_h = out32.cpu().numpy().astype(np.float64)
+    q_h = qs[n_steps - 1][0].cpu().numpy()
+    samples = []
+    for (b, h) in samples_bh:
+        samples.append((b, h, host_hist[(b, h)][0], host_hist[(b, h)][1], q_h[b, h * G:(h + 1) * G],
+                        out_h[b, h * G:(h + 1) * G]))
+
+    line = {
+        "metric": "fused dequant+decode-attn effective GB/s (% HBM peak); decode steps/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"{fmt}-codes/fp16-operands/fp32-accum",
+        "data": "synthetic (seeded, drawn on the GPU)",
+        "config": {"workload": W.name if fmt_over is None else W.name.replace("int4", fmt),
+                   "layers": L, "batch": B, "q_heads": Hq, "kv_heads": H, "head_dim": 128,
+                   "cached_tokens": T, "format": fmt, "old_format": W.old_fmt, "residual": R,
+                   "append_per_step": per_step, "parallelism": "none (1 GPU)"},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "decode_steps_per_s": round(args.steps / wall, 2),
+        "read_probe_gbs": round(probe, 1),
+        "prefill_s": round(t_prefill, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(args.workload),
+                     "kernel": "kvq_decode_attn (all launches of one call)",
+                     "launch_us": round(float(dec_ms.mean()) * 1e3, 2),
+                     "bytes_per_launch": round(float(nbytes.mean()))},
+    }
+    if not args.no_cpu_baseline:
+        wl = {"fmt": fmt, "R": R, "old_fmt": W.old_fmt, "old_after": W.old_after}
+        log("cpu baseline (oracle)")
+        base, err = cpu_baseline(samples, wl, sigma, args.cpu_budget)
+        line["cpu_baseline"] = base
+        line["sample_parity_max_rel_err"] = float(f"{err:.3e}")
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -104,3 +104,78 @@ WORKLOADS = {
                 KDist("normal", 4, 10.0), old_fmt="int2", old_after=65536,
                 decode_steps=16, append_per_step=1),
 }
+
+
+# ----------------------------------------------------------------------------- device-side draws
+# The full-size workloads hold up to 4.3 GB of fp16 K/V per layer; drawing them on the host
+# would take minutes, so the bench and the full-size tests draw them on the GPU with torch's
+# seeded generator.  Same recipe (one seed per (config, layer, stream, step), outlier channels
+# from the host generator above), a different random stream: these arrays are not equal to
+# the host draws, and a test that checks them copies the slices it needs to the host.
+
+DEV_CHUNK_TOKENS = 8192
+
+
+def torch_seed(config_id: int, layer: int, stream: int, step: int = 0) -> int:
+    s = np.random.SeedSequence([1000 + config_id, layer, stream, step]).generate_state(1, dtype=np.uint64)[0]
+    return int(s) & ((1 << 63) - 1)
+
+
+def _dev_gen(config_id, layer, stream, step, device):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(torch_seed(config_id, layer, stream, step))
+    return g
+
+
+def _dev_fill(out, g, dist: "KDist | None", mult=None):
+    """Fill fp16 out [B, H, n, 128] chunk by chunk along tokens from generator g; `mult`
+    ([1, H, 1, 128] fp32, outlier channel factors) is applied before the single fp16 rounding."""
+    import torch
+    B, H, n, D = out.shape
+    for t0 in range(0, n, DEV_CHUNK_TOKENS):
+        t1 = min(n, t0 + DEV_CHUNK_TOKENS)
+        shape = (B, H, t1 - t0, D)
+        x = torch.randn(shape, generator=g, device=out.device, dtype=torch.float32)
+        if dist is not None and dist.kind == "student_t":
+            # Student-t with integer nu: N(0,1) / sqrt(chi2_nu / nu), chi2_nu a sum of nu squared normals
+            nu = int(dist.nu)
+            assert nu == dist.nu and nu >= 1
+            chi = torch.zeros(shape, device=out.device, dtype=torch.float32)
+            for _ in range(nu):
+                chi.addcmul_(y := torch.randn(shape, generator=g, device=out.device, dtype=torch.float32), y)
+            x.div_(torch.sqrt(chi.div_(nu)))
+        if mult is not None:
+            x.mul_(mult)
+        out[:, :, t0:t1] = x.to(torch.float16)
+
+
+def draw_k_dev(config_id: int, layer: int, batch: int, num_kv_heads: int, n: int, dist: KDist,
+               stream: int = STREAM_K, step: int = 0, device="cuda"):
+    """fp16 device tensor [batch, num_kv_heads, n, HEAD_DIM] (K, outlier channels scaled)."""
+    import torch
+    out = torch.empty((batch, num_kv_heads, n, HEAD_DIM), dtype=torch.float16, device=device)
+    m = None
+    if dist.outlier_channels:
+        ch = outlier_channels(config_id, layer, num_kv_heads, dist.outlier_channels)
+        mult = np.ones((num_kv_heads, HEAD_DIM), np.float32)
+        for h in range(num_kv_heads):
+            mult[h, ch[h]] = dist.outlier_scale
+        m = torch.from_numpy(mult).to(device)[None, :, None, :]
+    _dev_fill(out, _dev_gen(config_id, layer, stream, step, device), dist, m)
+    return out
+
+
+def draw_v_dev(config_id: int, layer: int, batch: int, num_kv_heads: int, n: int,
+               stream: int = STREAM_V, step: int = 0, device="cuda"):
+    import torch
+    out = torch.empty((batch, num_kv_heads, n, HEAD_DIM), dtype=torch.float16, device=device)
+    _dev_fill(out, _dev_gen(config_id, layer, stream, step, device), None)
+    return out
+
+
+def draw_q_dev(config_id: int, layer: int, batch: int, num_q_heads: int, step: int = 0, device="cuda"):
+    import torch
+    g = _dev_gen(config_id, layer, STREAM_Q, step, device)
+    x = torch.randn((batch, num_q_heads, HEAD_DIM), generator=g, device=device, dtype=torch.float32)
+    return (x / np.sqrt(HEAD_DIM)).to(torch.float16)
