@@ -10,6 +10,8 @@
 #include "../../include/kvq.h"
 #include "kvq_internal.h"
 
+#include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -38,9 +40,6 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool is_quant_fmt(int f) { return f == kFmtInt2 || f == kFmtInt4 || f == kFmtInt8 || f == kFmtNvfp4; }
-
-// Items per (b, h) and segment never exceed this, so the workspace has a fixed bound.
-constexpr int kMaxItemsPerSeg = 64;
 
 struct LayerState {
   int64_t length = 0;  // tokens cached
@@ -221,43 +220,53 @@ int run_plan(kvq_cache *c, int layer, const Plan &p, const void *k, const void *
 
 // ---------------------------------------------------------------------------- decode plan
 
-struct DecodePlan {
-  DecodeSeg seg[3];  // old tier, young tier, residual
-  int nseg = 0;
-  int n_items = 0;
-};
+std::atomic<uint32_t> g_epoch{0};
 
-DecodePlan plan_decode(const kvq_cache *c, int layer) {
-  const auto &cfg = c->cfg;
-  const LayerState &st = c->layers[layer];
-  DecodePlan p;
-  const int64_t bh = (int64_t)cfg.batch * cfg.num_kv_heads;
-  const int64_t nb_old = ceil_div(st.old, kBlock), nb_young = ceil_div(st.young, kBlock);
-  const int cus = c->num_cus > 0 ? c->num_cus : 256;
-  const int64_t target_items = 8LL * cus;  // one-wave work items across the whole grid
-  int64_t bpi = std::max<int64_t>(1, ceil_div((nb_old + nb_young) * bh, target_items));
-  auto add_tier = [&](const uint8_t *base, int64_t bh_stride, int64_t ntok, int64_t nb, int fmt) {
-    if (nb == 0) return;
-    int64_t u = std::max<int64_t>(bpi, ceil_div(nb, kMaxItemsPerSeg));
-    DecodeSeg &s = p.seg[p.nseg++];
-    s.base = base; s.bh_stride = bh_stride; s.ntok = ntok; s.fmt = fmt;
-    s.units_per_item = (int)u; s.n_items = (int)ceil_div(nb, u); s.item0 = p.n_items; s.res_len = 0;
-    p.n_items += s.n_items;
-  };
-  add_tier(c->old(layer), (int64_t)c->geo.old_bh, st.old, nb_old, cfg.old_format);
-  add_tier(c->young(layer), (int64_t)c->geo.young_bh, st.young, nb_young, cfg.format);
-  if (st.res > 0) {
-    DecodeSeg &s = p.seg[p.nseg++];
-    s.base = c->res(layer); s.bh_stride = (int64_t)c->geo.res_bh; s.ntok = st.res; s.fmt = kFmtFp16;
-    s.units_per_item = (int)ceil_div(st.res, 32); s.n_items = 1; s.item0 = p.n_items; s.res_len = cfg.residual_len;
-    p.n_items += 1;
-  }
-  return p;
-}
+size_t counters_bytes(const kvq_cache *c) { return align_up((size_t)c->cfg.batch * c->cfg.num_kv_heads * sizeof(uint64_t)); }
 
 size_t workspace_bound(const kvq_cache *c, int32_t num_q_heads) {
-  const size_t items = 2 * kMaxItemsPerSeg + 1;
-  return items * (size_t)c->cfg.batch * (size_t)num_q_heads * kPartialStride * sizeof(float);
+  const size_t bh = (size_t)c->cfg.batch * c->cfg.num_kv_heads;
+  const size_t G = (size_t)(num_q_heads / c->cfg.num_kv_heads);
+  return counters_bytes(c) + bh * kMaxParts * G * kPartialStride * sizeof(float);
+}
+
+// Split every tier of the layer into work items of whole blocks, sized so that all work
+// items of the call fill the GPU about once (two workgroups per CU), in proportion to bytes.
+int plan_decode(const kvq_cache *c, int layer, DecodeArgs &a) {
+  const auto &cfg = c->cfg;
+  const LayerState &st = c->layers[layer];
+  const int64_t nbh = (int64_t)cfg.batch * cfg.num_kv_heads;
+  struct T { const uint8_t *base; int64_t stride, ntok, nblk; int fmt; };
+  T tiers[2];
+  int nt = 0;
+  if (st.old > 0) tiers[nt++] = {c->old(layer), (int64_t)c->geo.old_bh, st.old, ceil_div(st.old, kBlock), cfg.old_format};
+  if (st.young > 0) tiers[nt++] = {c->young(layer), (int64_t)c->geo.young_bh, st.young, ceil_div(st.young, kBlock), cfg.format};
+  const int cus = c->num_cus > 0 ? c->num_cus : 256;
+  const int64_t slots = 2LL * cus;
+  const int64_t target = std::max<int64_t>(1, slots / nbh);       // work items per (b, h)
+  double bytes = 0;
+  for (int i = 0; i < nt; ++i) bytes += (double)tiers[i].nblk * (double)block_bytes(tiers[i].fmt);
+  a.nseg = 0;
+  int parts = 0;
+  for (int i = 0; i < nt; ++i) {
+    const T &t = tiers[i];
+    int64_t items = std::max<int64_t>(1, (int64_t)((double)target * t.nblk * block_bytes(t.fmt) / bytes + 0.5));
+    items = std::min<int64_t>(items, t.nblk);
+    int64_t bpi = ceil_div(t.nblk, items);
+    const int64_t cap = kMaxParts / std::max(1, nt);
+    if (ceil_div(t.nblk, bpi) > cap) bpi = ceil_div(t.nblk, cap);
+    items = ceil_div(t.nblk, bpi);
+    DecodeSeg &s = a.seg[a.nseg++];
+    s.base = t.base; s.bh_stride = t.stride; s.ntok = t.ntok; s.fmt = t.fmt;
+    s.blocks_per_item = (int)bpi; s.items = (int)items; s.part0 = parts;
+    parts += (int)items;
+  }
+  a.items_total = std::max(1, parts);
+  a.res_base = c->res(layer);
+  a.res_bh_stride = (int64_t)c->geo.res_bh;
+  a.res_len = cfg.residual_len;
+  a.res_ntok = (int)st.res;
+  return (int)(nbh * a.items_total);
 }
 
 }  // namespace
@@ -368,18 +377,19 @@ int kvq_decode_attn(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_he
     else
       c->num_cus = 256;
   }
-  DecodePlan p = plan_decode(c, layer);
   DecodeArgs a{};
+  const int num_wg = plan_decode(c, layer, a);
   a.q = (const uint16_t *)q;
-  a.partials = (float *)workspace;
-  a.n_items_total = p.n_items;
+  a.out = out;
+  a.out_fp32 = out_fp32 ? 1 : 0;
+  a.counters = (uint64_t *)workspace;
+  a.partials = (float *)((uint8_t *)workspace + counters_bytes(c));
   a.B = cfg.batch; a.H = cfg.num_kv_heads; a.G = G;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  hipStream_t s = (hipStream_t)stream;
-  for (int i = 0; i < p.nseg; ++i) {
-    if (int e = hip_check(launch_decode_segment(a, p.seg[i], s), "decode partial")) return e;
-  }
-  return hip_check(launch_merge(a, out, out_fp32, s), "decode merge");
+  uint32_t ep = ++g_epoch;
+  if (ep == 0) ep = ++g_epoch;
+  a.epoch = ep;
+  return hip_check(launch_decode(a, num_wg, (hipStream_t)stream), "decode");
 }
 
 int kvq_seq_len(const kvq_cache *c, int32_t layer, int64_t *total, int64_t *in_residual) {

@@ -61,31 +61,44 @@ struct ResCopyArgs {
   int B, H;
 };
 
-// One stretch of the cache that the decode kernel streams: a tier arena or the residual.
+// One stretch of the cache that the decode kernel streams: a tier arena of one format.
 struct DecodeSeg {
-  const uint8_t *base;     // arena (or residual region) of the layer
+  const uint8_t *base;     // arena of the layer
   int64_t bh_stride;       // bytes per (b, h)
   int64_t ntok;            // valid slots per (b, h)
-  int fmt;                 // kFmt*; kFmtFp16 for the residual
-  int units_per_item;      // blocks (quantized) or 32-slot steps (residual) per work item
-  int n_items;             // work items per (b, h)
-  int item0;               // index of this segment's first item among all items
-  int res_len;             // residual: R
+  int fmt;                 // kFmtInt2 / Int4 / Int8 / Nvfp4
+  int blocks_per_item;     // 128-slot blocks per work item
+  int items;               // work items per (b, h)
+  int part0;               // index of this segment's first partial among a (b, h)'s partials
 };
+
+constexpr int kMaxSegs = 2;        // old tier, young tier
+constexpr int kMaxParts = 128;     // partial results per (b, h) and call
+constexpr int kPartialStride = 132;  // floats per (part, head): m, l, -, -, o[128]
 
 struct DecodeArgs {
   const uint16_t *q;       // [B][Hq][128] fp16
-  float *partials;         // [n_items_total][B][Hq][132] fp32: m, l, -, -, o[128]
-  int n_items_total;
+  void *out;               // [B][Hq][128] fp32 or fp16
+  int out_fp32;
+  uint64_t *counters;      // [B*H] arrival counters (epoch << 32 | count)
+  float *partials;         // [B*H][kMaxParts][G][kPartialStride]
+  DecodeSeg seg[kMaxSegs];
+  int nseg;
+  int items_total;         // work items per (b, h), all segments (at least 1)
+  // fp16 residual, handled by the last work item of each (b, h)
+  const uint8_t *res_base;
+  int64_t res_bh_stride;
+  int res_len;             // R (slots allocated)
+  int res_ntok;            // r (slots in use)
   int B, H, G;             // Hq = H * G
   float scale_log2;        // softmax_scale * log2(e)
+  uint32_t epoch;          // distinct per call, tags the arrival counters
 };
 
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t s);
 hipError_t launch_residual_copy(const ResCopyArgs &a, hipStream_t s);
-hipError_t launch_decode_segment(const DecodeArgs &a, const DecodeSeg &seg, hipStream_t s);
-hipError_t launch_merge(const DecodeArgs &a, void *out, int out_fp32, hipStream_t s);
-
-constexpr int kPartialStride = 132;  // floats per (item, b, hq) partial
+// LDS bytes one decode workgroup needs for the segments in `a`.
+size_t decode_lds_bytes(const DecodeArgs &a);
+hipError_t launch_decode(const DecodeArgs &a, int num_wg, hipStream_t s);
 
 }  // namespace kvq

@@ -98,13 +98,29 @@ __device__ __forceinline__ uint32_t e2m1_code(float x, float s) {
   return idx | (signbit(x) ? 8u : 0u);
 }
 
-// V-row field order: slot held by field k' of 32-bit word j in quarter q (n-bit fields).
-__device__ __forceinline__ int v_field_slot(int nbits, int q, int j, int kp) {
-  const int F = 32 / nbits, halfF = F / 2;
-  const int s = kp % halfF, hi = kp / halfF;
-  const int tau = (F / 4) * j + 2 * (s / 4) + ((s % 4) / 2);
-  const int i = 2 * (s % 2) + hi;
-  return 16 * tau + 4 * q + i;
+// Block layout (128 slots, head_dim 128).  K rows: affine field f holds dim
+// 64*((f >> 4) & 1) + 16*(f >> 5) + (f & 15) (each 16-field half of a lane quarter stays in
+// one 64-dim group); NVFP4 field f holds dim f.  V codes: 4 parts w x 64 lanes (g = lane >> 4,
+// c = lane & 15) x 8n bytes in 16-byte chunks; lane field phi holds dim 16k + c and slot
+// 32w + 16(e >> 2) + 4g + (e & 3), (k, e) per format below.
+__device__ __forceinline__ int k_field_dim(int fmt, int f) {
+  return fmt == kFmtNvfp4 ? f : 64 * ((f >> 4) & 1) + 16 * (f >> 5) + (f & 15);
+}
+
+__device__ __forceinline__ void v_field(int fmt, int phi, int &k, int &e) {
+  if (fmt == kFmtInt2) {
+    const int u = phi >> 4, m = phi & 15;
+    k = 2 * u + ((m >> 2) & 1);
+    e = 2 * (m & 3) + (m >> 3);
+  } else if (fmt == kFmtInt8) {
+    const int u = phi >> 2, b = phi & 3;
+    k = u >> 1;
+    e = 4 * (u & 1) + 2 * (b & 1) + (b >> 1);
+  } else {
+    const int v = phi & 7;
+    k = phi >> 3;
+    e = fmt == kFmtNvfp4 ? v : 2 * (v & 3) + (v >> 2);
+  }
 }
 
 template <int FMT>
@@ -193,13 +209,16 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
       write = true;                            // cleared slot: S = Z = +0
     }
     if (write) {
+      const int tau = slot >> 4, r = slot & 15;
       if (kv == 0) {
-        *(uint32_t *)(blkp + aff_km(kBits) + slot * 8 + g * 4) = Sb | (Zb << 16);
+        uint8_t *m = blkp + aff_km(kBits) + tau * 128;
+        *(uint16_t *)(m + 4 * r + 2 * g) = (uint16_t)Sb;
+        *(uint16_t *)(m + 64 + 4 * r + 2 * g) = (uint16_t)Zb;
       } else {
-        const int q = (slot % 16) / 4, tau = slot / 16, i = slot % 4;
-        uint8_t *e = blkp + aff_vm(kBits) + ((g * 4 + q) * 8 + tau) * 16;
-        *(uint16_t *)(e + 2 * i) = (uint16_t)Sb;
-        *(uint16_t *)(e + 8 + 2 * i) = (uint16_t)Zb;
+        const int q = r >> 2, i = r & 3;
+        uint8_t *m = blkp + aff_vm(kBits) + (tau * 4 + q) * 32;
+        *(uint16_t *)(m + 8 * g + 2 * i) = (uint16_t)Sb;
+        *(uint16_t *)(m + 16 + 8 * g + 2 * i) = (uint16_t)Zb;
       }
     }
   } else {
@@ -220,8 +239,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
         if (kv == 0) {
           blkp[kNvKs + slot * 8 + nb] = sb;
         } else {
-          const int q = (slot % 16) / 4, tau = slot / 16, i = slot % 4;
-          blkp[kNvVs + nb * 128 + 32 * q + 4 * tau + i] = sb;
+          const int w = slot >> 5, tt = (slot >> 4) & 1, q = (slot >> 2) & 3, i = slot & 3;
+          blkp[kNvVs + ((4 * w + q) * 8 + nb) * 8 + 4 * tt + i] = sb;
         }
       }
     }
@@ -232,14 +251,14 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
   constexpr int F = 32 / kBits;                     // fields per word
   constexpr int kWords = kBlock * kWordsPerRow;
   if (kv == 0) {
-    // K: row = slot, field = dim
+    // K: row = slot
     for (int w = tid; w < kWords; w += kThreads) {
       const int slot = w / kWordsPerRow, wi = w % kWordsPerRow;
       if (slot < lo || slot >= zhi) continue;
       uint32_t word = 0;
       if (slot < hi) {
         for (int k = 0; k < F; ++k) {
-          const int d = wi * F + k;
+          const int d = k_field_dim(FMT, wi * F + k);
           const float x = h2f(xs[slot * kRowHalves + d]);
           uint32_t c;
           if constexpr (kNv) c = e2m1_code(x, mS[slot][d / kNvBlock]);
@@ -250,31 +269,40 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
       *(uint32_t *)(blkp + slot * kRowBytes + wi * 4) = word;
     }
   } else {
-    // V: row = dim, fields in the lane-quarter slot order
+    // V: [part w][chunk r][lane][16 bytes]; lane word omega = 4r + (word in chunk)
     const size_t vc = kNv ? kNvVc : aff_vc(kBits);
+    constexpr int kChunks = kBits / 2;              // 16-byte chunks per lane
     for (int w = tid; w < kWords; w += kThreads) {
-      const int d = w / kWordsPerRow, wi = w % kWordsPerRow;
-      const int q = wi / kBits, j = wi % kBits;       // kBits words per quarter
-      uint32_t *dst = (uint32_t *)(blkp + vc + d * kRowBytes + wi * 4);
+      const int chunk = w >> 2, wc = w & 3;
+      const int lane = chunk & 63, wr = chunk >> 6;
+      const int part = wr / kChunks, r = wr % kChunks;
+      const int g = lane >> 4, c = lane & 15;
+      const int omega = 4 * r + wc;
+      uint32_t *dst = (uint32_t *)(blkp + vc + (size_t)w * 4);
       bool any = false, keep_any = false;
-      for (int k = 0; k < F; ++k) {
-        const int slot = v_field_slot(kBits, q, j, k);
+      for (int j = 0; j < F; ++j) {
+        int k, e;
+        v_field(FMT, omega * F + j, k, e);
+        const int slot = 32 * part + 16 * (e >> 2) + 4 * g + (e & 3);
         any |= slot >= lo && slot < zhi;
         keep_any |= slot < lo;
       }
       if (!any) continue;
       uint32_t word = keep_any ? *dst : 0u;
-      for (int k = 0; k < F; ++k) {
-        const int slot = v_field_slot(kBits, q, j, k);
+      for (int j = 0; j < F; ++j) {
+        int k, e;
+        v_field(FMT, omega * F + j, k, e);
+        const int slot = 32 * part + 16 * (e >> 2) + 4 * g + (e & 3);
         if (slot < lo || slot >= zhi) continue;
-        uint32_t c = 0;
+        const int d = 16 * k + c;
+        uint32_t code = 0;
         if (slot < hi) {
           const float x = h2f(xs[slot * kRowHalves + d]);
-          if constexpr (kNv) c = e2m1_code(x, mS[slot][d / kNvBlock]);
-          else c = affine_code(x, mS[slot][d / kGroup], mInv[slot][d / kGroup], mZ[slot][d / kGroup], kQmax);
+          if constexpr (kNv) code = e2m1_code(x, mS[slot][d / kNvBlock]);
+          else code = affine_code(x, mS[slot][d / kGroup], mInv[slot][d / kGroup], mZ[slot][d / kGroup], kQmax);
         }
-        const uint32_t mask = (uint32_t)kQmax << (k * kBits);
-        word = (word & ~mask) | (c << (k * kBits));
+        const uint32_t mask = (uint32_t)kQmax << (j * kBits);
+        word = (word & ~mask) | (code << (j * kBits));
       }
       *dst = word;
     }

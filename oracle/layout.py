@@ -4,33 +4,40 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 This module packs stored fields into bytes following the written layout
 specification, independently of the HIP code that implements the same spec.
+The pages fix no byte layout (only that codes are stored as n-bit integers with
+S and Z per group, page "KV缓存量化技术：提升大模型长文本生成效率" §2.1, and that NVFP4
+stores E2M1 codes with one FP8 scale per 16 values, page "NVFP4 KV缓存技术详解" §2.1);
+the layout below is this cache's own.
 
-Notation: a block holds 128 token slots t = 0..127; D = 128 dims; n = code bits.
-"n-bit little-endian field string": field f occupies bits [f*n, f*n + n) of the
-byte string, bit b of the string being bit (b mod 8) of byte b // 8.
+Notation: a block holds 128 token slots t = 0..127; D = 128 dims; n = code bits
+(NVFP4 codes are 4-bit fields).  "n-bit little-endian field string": field f
+occupies bits [f*n, f*n + n) of the byte string, bit b of the string being bit
+(b mod 8) of byte b // 8.  A block is [Kc][Km][Vc][Vm].
 
-Affine block (n in {2, 4, 8}), 4096*n + 2048 bytes:
-  Kc  @ 0          128 rows (slot t) x 16n bytes; row t = field string of the 128
-                   codes of token t, field d = dim d.
-  Km  @ 2048n      128 x 8 bytes; slot t: fp16 S0, Z0, S1, Z1 (group 0 = dims 0..63).
-  Vc  @ 2048n+1024 128 rows (dim d) x 16n bytes; row d = field string of 128
-                   codes, field f holding slot sigma_n(f) (below).
-  Vm  @ 4096n+1024 64 entries of 16 bytes, entry (g, q, tau) at ((g*4+q)*8+tau)*16:
-                   fp16 S of slots 16tau+4q+i for i = 0..3, then fp16 Z of the same.
-NVFP4 block, 18432 bytes:
-  Kc  @ 0      128 rows x 64 bytes; 4-bit field d = E2M1 code of dim d.
-  Ks  @ 8192   128 rows x 8 bytes; byte b = E4M3 scale of dims 16b..16b+15.
-  Vc  @ 9216   128 rows (dim d) x 64 bytes; 4-bit field f holds slot sigma_4(f).
-  Vs  @ 17408  8 rows (16-dim block b) x 128 bytes; byte p of row b holds the scale
-               of slot rho(p) = 16*((p mod 32) div 4) + 4*(p div 32) + (p mod 4).
-
-sigma_n(f): quarter q = f div 32, k = f mod 32; with F = 32/n fields per 32-bit
-word, (j, k') = divmod(k, F), s = k' mod (F/2), hi = k' div (F/2):
-    tau = (F/4)*j + 2*(s div 4) + ((s mod 4) div 2),   i = 2*(s mod 2) + hi,
-    slot = 16*tau + 4*q + i.
-(Each quarter q holds the 32 slots with (slot mod 16) div 4 == q, i.e. the
-slots one lane group consumes; inside a 32-bit word the order matches a
-two-at-a-time integer-to-fp16 unpack.)
+Kc, affine (2048n bytes): 128 rows (slot t) of 16n bytes.  A row is the field
+    string of 128 fields; field f = 32q + 16G + m (quarter q = 0..3, group G = 0, 1,
+    m = 0..15) holds the code of dim 64G + 16q + m.
+Kc, NVFP4 (8192 bytes): 128 rows of 64 bytes; field d holds the code of dim d.
+Km, affine (1024 bytes): 8 tiles tau of 128 bytes (slots 16tau + r, r = 0..15):
+    fp16 S at tau*128 + 4r + 2G, fp16 Z at tau*128 + 64 + 4r + 2G.
+Km, NVFP4 (1024 bytes): 128 rows of 8 bytes; byte b of row t = E4M3 scale of
+    dims 16b..16b+15 of slot t.
+Vc (2048n bytes; NVFP4 8192): 4 parts w, each 64 lanes L (g = L div 16,
+    c = L mod 16) of 8n bytes, stored as n/2 chunks of 16 bytes: chunk r of lane
+    L of part w at ((w*(n/2) + r)*64 + L)*16.  The lane's 8n bytes are the field
+    string of 64 fields phi; field phi holds the code of dim 16k + c and slot
+    32w + 16(e div 4) + 4g + (e mod 4), with (k, e) given by:
+      INT4:  k = phi div 8, v = phi mod 8, e = 2(v mod 4) + v div 4
+      NVFP4: k = phi div 8, e = phi mod 8
+      INT2:  u = phi div 16, m = phi mod 16, k = 2u + (m div 4) mod 2,
+             e = 2(m mod 4) + m div 8
+      INT8:  u = phi div 4, b = phi mod 4, k = u div 2,
+             e = 4(u mod 2) + 2(b mod 2) + b div 2
+Vm, affine (1024 bytes): 8 tiles tau x 4 quarters g of 32 bytes at (4tau + g)*32:
+    fp16 S of group 0 for slots 16tau + 4g + i (i = 0..3), then S of group 1,
+    then Z of group 0, then Z of group 1.
+Vm, NVFP4 (1024 bytes): byte ((4w + g)*8 + k)*8 + e = E4M3 scale of dims
+    16k..16k+15 of slot 32w + 16(e div 4) + 4g + (e mod 4).
 
 Residual (fp16, per layer and (batch, kv_head)), R slots (R a multiple of 16):
   K @ 0        [R][128] fp16, slot-major.
@@ -57,23 +64,40 @@ def block_bytes(fmt: str) -> int:
     return affine_block_bytes(int(fmt[3:]))
 
 
-def sigma(n: int) -> np.ndarray:
-    """sigma_n as an array: field index f (0..127) -> slot."""
-    F = 32 // n
-    out = np.empty(128, dtype=np.int64)
-    for f in range(128):
-        q, k = divmod(f, 32)
-        j, kp = divmod(k, F)
-        s, hi = kp % (F // 2), kp // (F // 2)
-        tau = (F // 4) * j + 2 * (s // 4) + ((s % 4) // 2)
-        i = 2 * (s % 2) + hi
-        out[f] = 16 * tau + 4 * q + i
-    return out
+def k_field_dims() -> np.ndarray:
+    """Affine Kc row: field f -> dim (f = 32q + 16G + m holds dim 64G + 16q + m)."""
+    f = np.arange(128)
+    q, G, m = f // 32, (f // 16) % 2, f % 16
+    return 64 * G + 16 * q + m
 
 
-def rho() -> np.ndarray:
-    p = np.arange(128)
-    return 16 * ((p % 32) // 4) + 4 * (p // 32) + (p % 4)
+def v_lane_fields(fmt: str) -> tuple[np.ndarray, np.ndarray]:
+    """Vc lane field string: field phi (0..63) -> (dim tile k, operand position e)."""
+    phi = np.arange(64)
+    if fmt in ("int4", "nvfp4"):
+        k, v = phi // 8, phi % 8
+        e = v if fmt == "nvfp4" else 2 * (v % 4) + v // 4
+    elif fmt == "int2":
+        u, m = phi // 16, phi % 16
+        k = 2 * u + (m // 4) % 2
+        e = 2 * (m % 4) + m // 8
+    elif fmt == "int8":
+        u, b = phi // 4, phi % 4
+        k = u // 2
+        e = 4 * (u % 2) + 2 * (b % 2) + b // 2
+    else:
+        raise ValueError(fmt)
+    return k, e
+
+
+def lane_slot(w: int, g: int, e) -> np.ndarray:
+    """Slot of operand position e of a lane in quarter g of part w."""
+    e = np.asarray(e)
+    return 32 * w + 16 * (e // 4) + 4 * g + (e % 4)
+
+
+def code_bits(fmt: str) -> int:
+    return 4 if fmt == "nvfp4" else int(fmt[3:])
 
 
 def pack_fields(fields: np.ndarray, n: int) -> np.ndarray:
@@ -94,9 +118,24 @@ def f16_bytes(a: np.ndarray) -> np.ndarray:
     return a.view(np.uint8).reshape(a.shape[:-1] + (a.shape[-1] * 2,))
 
 
+def _pack_vc(fmt: str, codes_v: np.ndarray) -> np.ndarray:
+    """Vc region from the [slot, dim] code array."""
+    n = code_bits(fmt)
+    k, e = v_lane_fields(fmt)
+    nchunk = n // 2
+    out = np.zeros((4, nchunk, 64, 16), np.uint8)
+    for w in range(4):
+        for L in range(64):
+            g, c = L // 16, L % 16
+            fields = codes_v[lane_slot(w, g, e), 16 * k + c]
+            out[w, :, L, :] = pack_fields(fields, n).reshape(nchunk, 16)
+    return out.ravel()
+
+
 def pack_affine_block(n: int, kq: dict, vq: dict, used: int) -> np.ndarray:
     """One affine block.  kq/vq: quantize_tokens() output for the block's slots
     (arrays of length `used` <= 128); slots >= used are all-zero bytes."""
+    fmt = f"int{n}"
     codes_k = np.zeros((BLOCK, D), np.uint8); codes_k[:used] = kq["codes"]
     codes_v = np.zeros((BLOCK, D), np.uint8); codes_v[:used] = vq["codes"]
     Sk = np.zeros((BLOCK, 2), np.float16); Sk[:used] = kq["S"]
@@ -104,17 +143,19 @@ def pack_affine_block(n: int, kq: dict, vq: dict, used: int) -> np.ndarray:
     Sv = np.zeros((BLOCK, 2), np.float16); Sv[:used] = vq["S"]
     Zv = np.zeros((BLOCK, 2), np.float16); Zv[:used] = vq["Z"]
 
-    kc = pack_fields(codes_k, n).ravel()                                   # 128 x 16n
-    km = f16_bytes(np.stack([Sk[:, 0], Zk[:, 0], Sk[:, 1], Zk[:, 1]], axis=1)).ravel()
-    vc = pack_fields(codes_v.T[:, sigma(n)], n).ravel()                    # row d: fields in sigma order
+    kc = pack_fields(codes_k[:, k_field_dims()], n).ravel()                # 128 rows x 16n
+    km = np.concatenate([np.concatenate([f16_bytes(Sk[16 * t:16 * t + 16].ravel()),
+                                         f16_bytes(Zk[16 * t:16 * t + 16].ravel())]) for t in range(8)])
+    vc = _pack_vc(fmt, codes_v)
     vm = np.zeros(1024, np.uint8)
-    for g in range(2):
-        for q in range(4):
-            for tau in range(8):
-                slots = 16 * tau + 4 * q + np.arange(4)
-                e = ((g * 4 + q) * 8 + tau) * 16
-                vm[e:e + 8] = f16_bytes(Sv[slots, g])
-                vm[e + 8:e + 16] = f16_bytes(Zv[slots, g])
+    for t in range(8):
+        for g in range(4):
+            slots = 16 * t + 4 * g + np.arange(4)
+            e = (4 * t + g) * 32
+            vm[e:e + 8] = f16_bytes(Sv[slots, 0])
+            vm[e + 8:e + 16] = f16_bytes(Sv[slots, 1])
+            vm[e + 16:e + 24] = f16_bytes(Zv[slots, 0])
+            vm[e + 24:e + 32] = f16_bytes(Zv[slots, 1])
     out = np.concatenate([kc, km, vc, vm])
     assert out.size == affine_block_bytes(n)
     return out
@@ -127,9 +168,13 @@ def pack_nvfp4_block(kq: dict, vq: dict, used: int) -> np.ndarray:
     sv = np.zeros((BLOCK, 8), np.uint8); sv[:used] = vq["scale"]
     kc = pack_fields(codes_k, 4).ravel()
     ks = sk.ravel()
-    vc = pack_fields(codes_v.T[:, sigma(4)], 4).ravel()
-    vs = sv.T[:, rho()].ravel()
-    out = np.concatenate([kc, ks, vc, vs])
+    vc = _pack_vc("nvfp4", codes_v)
+    vs = np.zeros((4, 4, 8, 8), np.uint8)                                   # [w][g][k][e]
+    e = np.arange(8)
+    for w in range(4):
+        for g in range(4):
+            vs[w, g] = sv[lane_slot(w, g, e)].T                             # [k][e]
+    out = np.concatenate([kc, ks, vc, vs.ravel()])
     assert out.size == NVFP4_BLOCK_BYTES
     return out
 

@@ -59,18 +59,27 @@ def test_residual_positions(case):
     assert list(np.flatnonzero(data)) == [case["byte"] + 1]
 
 
-@pytest.mark.parametrize("n", [2, 4, 8])
-def test_sigma_is_a_permutation_grouping_lane_quarters(n):
-    s = layout.sigma(n)
-    assert sorted(s) == list(range(128))
-    q = np.arange(128) // 32
-    assert np.all(((s % 16) // 4) == q)          # quarter q holds the slots of lane group q
-    # inside every 32-bit word the slots are whole 4-slot runs (one 16x16 MFMA operand column)
-    F = 32 // n
-    for w in range(128 // F):
-        slots = s[w * F:(w + 1) * F]
-        assert set(slots // 4 * 4) == set(slots - slots % 4)
-        assert np.all(np.bincount(slots // 4, minlength=32)[np.unique(slots // 4)] == 4)
+@pytest.mark.parametrize("fmt", ["int2", "int4", "int8", "nvfp4"])
+def test_v_lane_fields_cover_every_slot_and_dim_once(fmt):
+    """Every (slot, dim) of the block is held by exactly one (part, lane, field), and each
+    lane's 8 operand positions e are the slots 16(e div 4) + 4g + (e mod 4) of its part."""
+    k, e = layout.v_lane_fields(fmt)
+    seen = np.zeros((128, 128), np.int64)
+    for w in range(4):
+        for L in range(64):
+            g, c = L // 16, L % 16
+            seen[layout.lane_slot(w, g, e), 16 * k + c] += 1
+    assert np.all(seen == 1)
+    # each dim tile k gets all 8 positions once
+    for kk in range(8):
+        assert sorted(e[k == kk]) == list(range(8))
+
+
+def test_k_field_dims_is_a_permutation_keeping_quarters_in_one_group_each_half():
+    d = layout.k_field_dims()
+    assert sorted(d) == list(range(128))
+    f = np.arange(128)
+    assert np.all(d // 64 == (f // 16) % 2)          # each 16-field half lies in one 64-dim group
 
 
 def test_every_bit_of_a_block_is_reachable_once():
