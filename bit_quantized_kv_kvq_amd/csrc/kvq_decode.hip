@@ -15,7 +15,8 @@
 // byte is read once per group).  At the end of an item the four waves merge their running
 // softmax states in LDS, the workgroup writes one partial (m, l, o) and bumps an arrival
 // counter; the last workgroup of a (batch, kv_head) merges all partials with a log-sum-exp
-// reduction and writes the output.
+// reduction and writes the output.  The partials and the counter use agent-scope atomics
+// only: no device-wide fence (which would write back and invalidate the L2 of the XCD).
 //
 // Matrix cores, per 32 slots of a wave (v_mfma_f32_16x16x32_f16):
 //  QK^T  A = K codes (16 slots x 32 dims), B = Q^T (32 dims x 16 heads; heads >= G are zero);
@@ -624,18 +625,26 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int v = 0; v < kWaves; ++v) {
       const float mv = wm[v * 16 + hc];
-      const float wt = mv == kNegInf ? 0.0f : exp2f(mv - M);
+      const float wt = mv == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
       O += wt * wo[(v * 16 + hc) * kHeadDim + d];
       L += wt * wl[v * 16 + hc];
     }
+    // Partials are written with agent-scope stores, which go past this XCD's L2, so the
+    // merging workgroup (possibly on another XCD) reads them without any L2 write-back.
     float *pp = part + hc * kPartialStride;
-    pp[4 + d] = O;
-    if (d == 0) { pp[0] = M; pp[1] = L; }
+    __hip_atomic_store(pp + 4 + d, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == 0) {
+      __hip_atomic_store(pp, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(pp + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 
-  // ---- arrival; the last workgroup of this (batch, kv_head) merges every partial
+  // ---- arrival; the last workgroup of this (batch, kv_head) merges every partial.
+  // Every thread waits for its own partial stores to complete before the barrier; thread 0
+  // then counts the arrival with an agent-scope atomic.  The merging workgroup reads the
+  // partials with agent-scope loads issued after it has seen the final count.
   __shared__ int s_last;
-  __threadfence();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
     uint64_t *cnt = a.counters + it.bh;
@@ -643,30 +652,49 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     uint64_t next;
     for (;;) {
       next = ((uint32_t)(cur >> 32) == a.epoch) ? cur + 1 : (((uint64_t)a.epoch << 32) | 1u);
-      if (__hip_atomic_compare_exchange_strong(cnt, &cur, next, __ATOMIC_ACQ_REL, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      if (__hip_atomic_compare_exchange_strong(cnt, &cur, next, __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
         break;
     }
     s_last = (int)(uint32_t)next == a.items_total;
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
 
+  const int P = a.items_total;
   const float *parts = a.partials + (int64_t)it.bh * kMaxParts * G * kPartialStride;
+  float *sm_m = (float *)smem;            // [P][G]
+  float *sm_w = sm_m + P * G;             // [P][G] weights, after the max is known
+  float *sm_l = sm_w + P * G;             // [P][G]
+  float *sm_inv = sm_l + P * G;           // [G]
+  for (int idx = threadIdx.x; idx < P * G; idx += kThreads) {
+    const float *pp = parts + (int64_t)idx * kPartialStride;       // part idx / G, head idx % G
+    sm_m[idx] = __hip_atomic_load(pp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm_l[idx] = __hip_atomic_load(pp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int hc = threadIdx.x;
+    float M = kNegInf;
+    for (int p = 0; p < P; ++p) M = fmaxf(M, sm_m[p * G + hc]);
+    float L = 0.0f;
+    for (int p = 0; p < P; ++p) {
+      const float mv = sm_m[p * G + hc];
+      const float wt = mv == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
+      sm_w[p * G + hc] = wt;
+      L += wt * sm_l[p * G + hc];
+    }
+    sm_inv[hc] = 1.0f / L;
+  }
+  __syncthreads();
   const int b = it.bh / a.H, h = it.bh % a.H;
   for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kThreads) {
     const int hc = idx >> 7, d = idx & 127;
-    float M = kNegInf;
-    for (int p = 0; p < a.items_total; ++p) M = fmaxf(M, parts[(p * G + hc) * kPartialStride]);
-    float O = 0.0f, L = 0.0f;
-    for (int p = 0; p < a.items_total; ++p) {
-      const float *pp = parts + (p * G + hc) * kPartialStride;
-      const float mv = pp[0];
-      const float wt = mv == kNegInf ? 0.0f : exp2f(mv - M);
-      O += wt * pp[4 + d];
-      L += wt * pp[1];
-    }
-    const float r = O / L;
+    float O = 0.0f;
+#pragma unroll 8
+    for (int p = 0; p < P; ++p)
+      O += sm_w[p * G + hc] * __hip_atomic_load(parts + (int64_t)(p * G + hc) * kPartialStride + 4 + d, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    const float r = O * sm_inv[hc];
     const int64_t o = ((int64_t)b * a.H * G + (int64_t)h * G + hc) * kHeadDim + d;
     if (a.out_fp32) ((float *)a.out)[o] = r;
     else ((_Float16 *)a.out)[o] = (_Float16)r;
