@@ -365,7 +365,7 @@ int kvq_decode_attn(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_he
   if (G > 16) return fail(KVQ_EINVAL, "query heads per kv head (%d) must be <= 16", G);
   if (!q || !out || !workspace) return fail(KVQ_EINVAL, "q, out and workspace must be non-NULL");
   if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return fail(KVQ_EINVAL, "q, out and workspace must be 16-byte aligned");
-  if (!(softmax_scale == softmax_scale)) return fail(KVQ_EINVAL, "softmax_scale is NaN");
+  if (!(softmax_scale > 0.0f) || softmax_scale > 3.0e38f) return fail(KVQ_EINVAL, "softmax_scale must be positive and finite");
   if (ws_bytes < workspace_bound(c, num_q_heads))
     return fail(KVQ_ENOSPACE, "workspace %zu < required %zu", ws_bytes, workspace_bound(c, num_q_heads));
   if (c->layers[layer].length == 0) return fail(KVQ_ESTATE, "layer %d is empty", layer);

@@ -60,6 +60,12 @@ __device__ __forceinline__ uint32_t pk(float a, float b) { return as_u(half2_t{(
 __device__ __forceinline__ float4_t mfma(half8_t a, half8_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ half4_t h4(uint32_t a, uint32_t b) { return __builtin_bit_cast(half4_t, u32x2{a, b}); }
+__device__ __forceinline__ float4_t mfma16(half4_t a, half4_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
 
 // fp16 pair (1024 + f_lo, 1024 + f_hi) of the two fields selected by mask, minus 1024 + off:
 // exact (f - off, or 16 f - off for a mask shifted by 4 bits).
@@ -77,33 +83,36 @@ __device__ __forceinline__ uint32_t field_pair(uint32_t x, uint32_t mask) {
 }
 
 // ---------------------------------------------------------------- operand unpack per format
-// The K operand takes the codes c as they are; the V operand takes c - C (C = 2^(n-1)), so
-// that the PV sums stay centred and the zero-point term sum P'(Z - C) stays small over long
-// contexts (no cancellation between two large sums).
-// INT4 word -> [n0, n4, 16n1, 16n5, n2, n6, 16n3, 16n7] - C (n_v = nibble v; 16 C on the
-// scaled positions)
+// The K operand takes the codes c (16c on scaled positions) as exact fp16 integers; the V
+// operand takes c - C (C = 2^(n-1)), so that the PV sums stay centred and the zero-point term
+// sum P'(Z - C) stays small over long contexts (no cancellation between two large sums).
+// (Leaving the 1024 bias of the magic constant in the K operand and starting the MFMA
+// accumulator at -1024 sum(B) would save the subtraction, but the accumulation error against
+// the bias exceeds the attention tolerance for INT2 codes.)
+template <bool CENTER, int C1>
+__device__ __forceinline__ uint32_t code_pair(uint32_t x, uint32_t mask) {
+  return field_pair<CENTER ? C1 : 0>(x, mask);
+}
+// INT4 word -> [n0, n4, 16n1, 16n5, n2, n6, 16n3, 16n7] (n_v = nibble v; minus 8 / 128 if CENTER)
 template <bool CENTER>
 __device__ __forceinline__ half8_t unpack_int4(uint32_t x) {
   const uint32_t y = x >> 8;
-  constexpr int C1 = CENTER ? 8 : 0, C16 = CENTER ? 128 : 0;
-  return h8(field_pair<C1>(x, 0x000F000Fu), field_pair<C16>(x, 0x00F000F0u), field_pair<C1>(y, 0x000F000Fu),
-            field_pair<C16>(y, 0x00F000F0u));
+  return h8(code_pair<CENTER, 8>(x, 0x000F000Fu), code_pair<CENTER, 128>(x, 0x00F000F0u), code_pair<CENTER, 8>(y, 0x000F000Fu),
+            code_pair<CENTER, 128>(y, 0x00F000F0u));
 }
-// INT2 word -> lo = crumbs [0,8,1,9,2,10,3,11], hi = [4,12,5,13,6,14,7,15] (minus C)
+// INT2 word -> lo = crumbs [0,8,1,9,2,10,3,11], hi = [4,12,5,13,6,14,7,15] (minus 2 if CENTER)
 template <bool CENTER>
 __device__ __forceinline__ void unpack_int2(uint32_t x, half8_t &lo, half8_t &hi) {
-  constexpr int C = CENTER ? 2 : 0;
-  lo = h8(field_pair<C>(x, 0x00030003u), field_pair<C>(x >> 2, 0x00030003u), field_pair<C>(x >> 4, 0x00030003u),
-          field_pair<C>(x >> 6, 0x00030003u));
-  hi = h8(field_pair<C>(x >> 8, 0x00030003u), field_pair<C>(x >> 10, 0x00030003u), field_pair<C>(x >> 12, 0x00030003u),
-          field_pair<C>(x >> 14, 0x00030003u));
+  lo = h8(code_pair<CENTER, 2>(x, 0x00030003u), code_pair<CENTER, 2>(x >> 2, 0x00030003u),
+          code_pair<CENTER, 2>(x >> 4, 0x00030003u), code_pair<CENTER, 2>(x >> 6, 0x00030003u));
+  hi = h8(code_pair<CENTER, 2>(x >> 8, 0x00030003u), code_pair<CENTER, 2>(x >> 10, 0x00030003u),
+          code_pair<CENTER, 2>(x >> 12, 0x00030003u), code_pair<CENTER, 2>(x >> 14, 0x00030003u));
 }
-// INT8 word pair -> [w0.b0, w0.b2, w0.b1, w0.b3, w1.b0, w1.b2, w1.b1, w1.b3] (minus C)
+// INT8 word pair -> [w0.b0, w0.b2, w0.b1, w0.b3, w1.b0, w1.b2, w1.b1, w1.b3] (minus 128 if CENTER)
 template <bool CENTER>
 __device__ __forceinline__ half8_t unpack_int8(uint32_t w0, uint32_t w1) {
-  constexpr int C = CENTER ? 128 : 0;
-  return h8(field_pair<C>(w0, 0x00FF00FFu), field_pair<C>(w0 >> 8, 0x00FF00FFu), field_pair<C>(w1, 0x00FF00FFu),
-            field_pair<C>(w1 >> 8, 0x00FF00FFu));
+  return h8(code_pair<CENTER, 128>(w0, 0x00FF00FFu), code_pair<CENTER, 128>(w0 >> 8, 0x00FF00FFu),
+            code_pair<CENTER, 128>(w1, 0x00FF00FFu), code_pair<CENTER, 128>(w1 >> 8, 0x00FF00FFu));
 }
 // NVFP4 word (8 E2M1 codes, nibble order) times per-pair fp16 scales
 __device__ __forceinline__ half8_t unpack_fp4(uint32_t x, uint32_t s01, uint32_t s23, uint32_t s45, uint32_t s67) {
@@ -118,6 +127,20 @@ __device__ __forceinline__ uint32_t e4m3_pair(uint32_t x, bool sel) {
   return as_u(sel ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true)
                   : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false));
 }
+
+// ---------------------------------------------------------------- cross-quarter reductions
+// Reduce over lanes {c, c+16, c+32, c+48} (the four lane quarters holding one head).
+__device__ __forceinline__ float quad_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+// Over the eight lanes {c, c^8} x quarters that hold one head in the paired-subtile layout.
+__device__ __forceinline__ float head_max2(float x) { return quad_max(fmaxf(x, __shfl_xor(x, 8))); }
+__device__ __forceinline__ float head_sum2(float x) { return quad_sum(x + __shfl_xor(x, 8)); }
 
 // ---------------------------------------------------------------- Q operand per format
 // Dim fed by B element e of k-step j in lane quarter g, and whether the A element it meets
@@ -160,8 +183,7 @@ __device__ __forceinline__ void load_q(const uint16_t *qrow, bool valid, int g, 
 #pragma unroll
     for (int e = 0; e < 8; ++e) loc[8 * i + e] = valid ? v[e] : (_Float16)0.0f;
   }
-  qs0 = 0.0f;
-  qs1 = 0.0f;
+  qs0 = qs1 = 0.0f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -177,10 +199,8 @@ __device__ __forceinline__ void load_q(const uint16_t *qrow, bool valid, int g, 
     }
   }
   // group sums over the four lane quarters (lanes c, c+16, c+32, c+48 hold one head)
-  qs0 += __shfl_xor(qs0, 16);
-  qs0 += __shfl_xor(qs0, 32);
-  qs1 += __shfl_xor(qs1, 16);
-  qs1 += __shfl_xor(qs1, 32);
+  qs0 = quad_sum(qs0);
+  qs1 = quad_sum(qs1);
 }
 
 // ---------------------------------------------------------------- LDS DMA
@@ -236,37 +256,39 @@ __device__ __forceinline__ void barrier() {
 
 // ---------------------------------------------------------------- running softmax state
 struct State {
-  float m = kNegInf;   // running max (log2 domain) of head c, same on the 4 lane quarters
+  float m = kNegInf;   // running max of the unscaled logits of head c, same on the 4 lane quarters
   float l = 0.0f;      // this lane's share of sum p
   float z1 = 0.0f, z16 = 0.0f;   // affine V: this lane's share of sum P' Z (group 0 / 1 folded below)
   float z1b = 0.0f, z16b = 0.0f;
   float4_t o[8];       // O^T[dims 16k + 4g + i][head c]
 };
 
-// Update the running max with 8 logits (slots (tt, i) = (e >> 2, e & 3)) and return the
-// probabilities; positions whose A element is scaled by 16 (mask bit e) get p / 16.
+// Update the running max with 8 unscaled logits (slots (tt, i) = (e >> 2, e & 3)) and return
+// p = exp2(sl2 (s - m)), sl2 = softmax_scale * log2(e) > 0; positions whose A element is scaled
+// by 16 (mask bit e) get p / 16.
 __device__ __forceinline__ void softmax_step(State &st, const float (&s)[8], float (&p)[8], bool valid_head,
-                                             unsigned scaled_mask) {
-  float mt = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-  mt = fmaxf(mt, __shfl_xor(mt, 16));
-  mt = fmaxf(mt, __shfl_xor(mt, 32));
-  const bool grow = valid_head && mt > st.m;
-  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                                             unsigned scaled_mask, float sl2) {
+  // Fast path: no logit of a valid head exceeds the running max, so the max and every
+  // accumulator stay as they are and no cross-lane reduction is needed.  Otherwise the new
+  // max of each head is reduced over its four lane quarters and the state is rescaled.
+  const float ml = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+  if (__builtin_amdgcn_ballot_w64(valid_head && ml > st.m) != 0) {
+    const float mt = quad_max(ml);
     const float m_new = fmaxf(st.m, mt);
-    const float alpha = (m_new == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f(st.m - m_new);
+    const float alpha = (m_new == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f((st.m - m_new) * sl2);
     st.l *= alpha;
     st.z1 *= alpha; st.z16 *= alpha; st.z1b *= alpha; st.z16b *= alpha;
 #pragma unroll
     for (int k = 0; k < 8; ++k) st.o[k] *= alpha;
     st.m = m_new;
   }
-  const float m0 = st.m == kNegInf ? 0.0f : st.m;
-  const float m4 = m0 + 4.0f;
+  const float nm = st.m == kNegInf ? 0.0f : -st.m * sl2;
+  const float nm4 = nm - 4.0f;
   float ls = 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const bool sc = (scaled_mask >> e) & 1;
-    p[e] = __builtin_amdgcn_exp2f(s[e] - (sc ? m4 : m0));   // v_exp_f32; results below 2^-126 flush to 0
+    p[e] = __builtin_amdgcn_exp2f(fmaf(s[e], sl2, sc ? nm4 : nm));   // v_exp_f32; results below 2^-126 flush to 0
     ls = sc ? fmaf(16.0f, p[e], ls) : ls + p[e];
   }
   st.l += ls;
@@ -275,17 +297,57 @@ __device__ __forceinline__ void softmax_step(State &st, const float (&s)[8], flo
 // ---------------------------------------------------------------- one 32-slot step per format
 // blk: LDS copy of the block; w: wave; TAIL: only the first nvalid slots of the block hold
 // tokens (the last block of a tier).
+struct QOp {
+  half8_t qb[4];
+  float qs0, qs1;          // per-group sums of the effective q (zero-point terms)
+};
+
 template <int NB, bool TAIL>
-__device__ __forceinline__ void affine_step(const uint8_t *blk, int w, int g, int c, const half8_t (&qb)[4], float qs0,
-                                            float qs1, float sl2, bool valid_head, int nvalid, State &st) {
-  constexpr int kRow = 16 * NB;                      // K row bytes
+__device__ __forceinline__ void affine_step(const uint8_t *blk, int w, int g, int c, const QOp &q, float sl2,
+                                            bool valid_head, int nvalid, State &st) {
   constexpr int kKm = 2048 * NB, kVc = 2048 * NB + 1024, kVm = 4096 * NB + 1024;
   const int lane = 16 * g + c;
+  const half8_t (&qb)[4] = q.qb;
+  const float qs0 = q.qs0, qs1 = q.qs1;
+
+  // Everything that does not depend on the softmax state first (LDS reads, the V operands),
+  // so that it overlaps the K -> logits -> max chain.
+  // V codes of this lane: [part w][chunk r][lane][16 B]
+  constexpr int kChunks = NB / 2;
+  const uint8_t *vc = blk + kVc + (w * kChunks * 64 + lane) * 16;
+  half8_t va[8];
+  if constexpr (NB == 4) {
+    const uint4 x0 = *(const uint4 *)vc, x1 = *(const uint4 *)(vc + 1024);
+    va[0] = unpack_int4<true>(x0.x); va[1] = unpack_int4<true>(x0.y);
+    va[2] = unpack_int4<true>(x0.z); va[3] = unpack_int4<true>(x0.w);
+    va[4] = unpack_int4<true>(x1.x); va[5] = unpack_int4<true>(x1.y);
+    va[6] = unpack_int4<true>(x1.z); va[7] = unpack_int4<true>(x1.w);
+  } else if constexpr (NB == 2) {
+    const uint4 x = *(const uint4 *)vc;
+    const uint32_t ws[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) unpack_int2<true>(ws[u], va[2 * u], va[2 * u + 1]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint4 x = *(const uint4 *)(vc + r * 1024);
+      va[2 * r] = unpack_int8<true>(x.x, x.y);
+      va[2 * r + 1] = unpack_int8<true>(x.z, x.w);
+    }
+  }
+  uint4 vm0[2], vz[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    vm0[tt] = *(const uint4 *)(blk + kVm + ((2 * w + tt) * 4 + g) * 32);        // S_G0[0..3], S_G1[0..3]
+    vz[tt] = *(const uint4 *)(blk + kVm + ((2 * w + tt) * 4 + g) * 32 + 16);    // Z_G0[0..3], Z_G1[0..3]
+  }
+
   float s[8];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
     const int tau = 2 * w + tt;
-    const uint8_t *row = blk + (32 * w + 16 * tt + c) * kRow + g * (4 * NB);
+    // K codes: [part w][tile tt][chunk][lane][min(16, 4n) bytes]
+    const uint8_t *row = blk + (tau * (NB == 8 ? 2 : 1) * 64 + lane) * (NB == 2 ? 8 : 16);
     float4_t a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0;
     if constexpr (NB == 4) {
       const uint4 x = *(const uint4 *)row;
@@ -303,7 +365,7 @@ __device__ __forceinline__ void affine_step(const uint8_t *blk, int w, int g, in
       a1 = mfma(l1, qb[2], a1);
       a1 = mfma(h1, qb[3], a1);
     } else {
-      const uint4 x = *(const uint4 *)row, y = *(const uint4 *)(row + 16);
+      const uint4 x = *(const uint4 *)row, y = *(const uint4 *)(row + 1024);
       a0 = mfma(unpack_int8<false>(x.x, x.y), qb[0], a0);
       a0 = mfma(unpack_int8<false>(x.z, x.w), qb[1], a0);
       a1 = mfma(unpack_int8<false>(y.x, y.y), qb[2], a1);
@@ -316,91 +378,60 @@ __device__ __forceinline__ void affine_step(const uint8_t *blk, int w, int g, in
     for (int i = 0; i < 4; ++i) {
       const float u0 = fmaf(-lo_f(zw[i]), qs0, a0[i]);
       const float u1 = fmaf(-hi_f(zw[i]), qs1, a1[i]);
-      float v = fmaf(hi_f(sw[i]), u1, lo_f(sw[i]) * u0) * sl2;
+      float v = fmaf(hi_f(sw[i]), u1, lo_f(sw[i]) * u0);
       if (TAIL && 16 * tau + 4 * g + i >= nvalid) v = kNegInf;
       s[4 * tt + i] = v;
     }
   }
   float p[8];
   constexpr unsigned kScaled = NB == 4 ? 0xCCu : 0u;   // INT4: positions i = 2, 3 of both tiles
-  softmax_step(st, s, p, valid_head, kScaled);
+  softmax_step(st, s, p, valid_head, kScaled, sl2);
 
-  // P' = p * S per group, and the zero-point sums sum P' (Z - C)
+  // P' = p * S per group (one fp16 rounding), and the zero-point sums sum P' (Z - C)
   half8_t pb[2];
   {
+    constexpr _Float16 kC = (_Float16)(1 << (NB - 1));
+    const half2_t cc = {kC, kC};
     uint32_t pw[2][4];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const uint4 vm0 = *(const uint4 *)(blk + kVm + ((2 * w + tt) * 4 + g) * 32);        // S_G0[0..3], S_G1[0..3]
-      const uint4 vz = *(const uint4 *)(blk + kVm + ((2 * w + tt) * 4 + g) * 32 + 16);    // Z_G0[0..3], Z_G1[0..3]
-      constexpr _Float16 kC = (_Float16)(1 << (NB - 1));
-      const half2_t cc = {kC, kC};
-      const uint4 vm1 = {as_u(as_h2(vz.x) - cc), as_u(as_h2(vz.y) - cc), as_u(as_h2(vz.z) - cc), as_u(as_h2(vz.w) - cc)};
-      // p * S in fp32, rounded once to fp16
       const float *pp = p + 4 * tt;
-      const uint32_t a01 = pk(pp[0] * lo_f(vm0.x), pp[1] * hi_f(vm0.x)), a23 = pk(pp[2] * lo_f(vm0.y), pp[3] * hi_f(vm0.y));
-      const uint32_t b01 = pk(pp[0] * lo_f(vm0.z), pp[1] * hi_f(vm0.z)), b23 = pk(pp[2] * lo_f(vm0.w), pp[3] * hi_f(vm0.w));
+      const uint4 sm = vm0[tt], zz = vz[tt];
+      const uint32_t a01 = pk(pp[0] * lo_f(sm.x), pp[1] * hi_f(sm.x)), a23 = pk(pp[2] * lo_f(sm.y), pp[3] * hi_f(sm.y));
+      const uint32_t b01 = pk(pp[0] * lo_f(sm.z), pp[1] * hi_f(sm.z)), b23 = pk(pp[2] * lo_f(sm.w), pp[3] * hi_f(sm.w));
       pw[0][2 * tt + 0] = a01; pw[0][2 * tt + 1] = a23;
       pw[1][2 * tt + 0] = b01; pw[1][2 * tt + 1] = b23;
+      const half2_t z0 = as_h2(zz.x) - cc, z1 = as_h2(zz.y) - cc, z2 = as_h2(zz.z) - cc, z3 = as_h2(zz.w) - cc;
       if constexpr (NB == 4) {
-        st.z1 = __builtin_amdgcn_fdot2(as_h2(a01), as_h2(vm1.x), st.z1, false);
-        st.z16 = __builtin_amdgcn_fdot2(as_h2(a23), as_h2(vm1.y), st.z16, false);
-        st.z1b = __builtin_amdgcn_fdot2(as_h2(b01), as_h2(vm1.z), st.z1b, false);
-        st.z16b = __builtin_amdgcn_fdot2(as_h2(b23), as_h2(vm1.w), st.z16b, false);
+        st.z1 = __builtin_amdgcn_fdot2(as_h2(a01), z0, st.z1, false);
+        st.z16 = __builtin_amdgcn_fdot2(as_h2(a23), z1, st.z16, false);
+        st.z1b = __builtin_amdgcn_fdot2(as_h2(b01), z2, st.z1b, false);
+        st.z16b = __builtin_amdgcn_fdot2(as_h2(b23), z3, st.z16b, false);
       } else {
-        st.z1 = __builtin_amdgcn_fdot2(as_h2(a01), as_h2(vm1.x), st.z1, false);
-        st.z1 = __builtin_amdgcn_fdot2(as_h2(a23), as_h2(vm1.y), st.z1, false);
-        st.z1b = __builtin_amdgcn_fdot2(as_h2(b01), as_h2(vm1.z), st.z1b, false);
-        st.z1b = __builtin_amdgcn_fdot2(as_h2(b23), as_h2(vm1.w), st.z1b, false);
+        st.z1 = __builtin_amdgcn_fdot2(as_h2(a01), z0, st.z1, false);
+        st.z1 = __builtin_amdgcn_fdot2(as_h2(a23), z1, st.z1, false);
+        st.z1b = __builtin_amdgcn_fdot2(as_h2(b01), z2, st.z1b, false);
+        st.z1b = __builtin_amdgcn_fdot2(as_h2(b23), z3, st.z1b, false);
       }
     }
     pb[0] = h8(pw[0][0], pw[0][1], pw[0][2], pw[0][3]);
     pb[1] = h8(pw[1][0], pw[1][1], pw[1][2], pw[1][3]);
   }
-
-  // V codes of this lane: [part w][chunk r][lane][16 B]
-  constexpr int kChunks = NB / 2;
-  const uint8_t *vc = blk + kVc + (w * kChunks * 64 + lane) * 16;
-  if constexpr (NB == 4) {
-    const uint4 x0 = *(const uint4 *)vc, x1 = *(const uint4 *)(vc + 1024);
-    st.o[0] = mfma(unpack_int4<true>(x0.x), pb[0], st.o[0]);
-    st.o[1] = mfma(unpack_int4<true>(x0.y), pb[0], st.o[1]);
-    st.o[2] = mfma(unpack_int4<true>(x0.z), pb[0], st.o[2]);
-    st.o[3] = mfma(unpack_int4<true>(x0.w), pb[0], st.o[3]);
-    st.o[4] = mfma(unpack_int4<true>(x1.x), pb[1], st.o[4]);
-    st.o[5] = mfma(unpack_int4<true>(x1.y), pb[1], st.o[5]);
-    st.o[6] = mfma(unpack_int4<true>(x1.z), pb[1], st.o[6]);
-    st.o[7] = mfma(unpack_int4<true>(x1.w), pb[1], st.o[7]);
-  } else if constexpr (NB == 2) {
-    const uint4 x = *(const uint4 *)vc;
-    const uint32_t ws[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      half8_t lo, hi;
-      unpack_int2<true>(ws[u], lo, hi);
-      st.o[2 * u] = mfma(lo, pb[u >> 1], st.o[2 * u]);
-      st.o[2 * u + 1] = mfma(hi, pb[u >> 1], st.o[2 * u + 1]);
-    }
-  } else {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint4 x = *(const uint4 *)(vc + r * 1024);
-      st.o[2 * r] = mfma(unpack_int8<true>(x.x, x.y), pb[r >> 1], st.o[2 * r]);
-      st.o[2 * r + 1] = mfma(unpack_int8<true>(x.z, x.w), pb[r >> 1], st.o[2 * r + 1]);
-    }
-  }
+  for (int k = 0; k < 8; ++k) st.o[k] = mfma(va[k], pb[k >> 2], st.o[k]);
 }
 
 template <bool TAIL>
-__device__ __forceinline__ void nvfp4_step(const uint8_t *blk, int w, int g, int c, const half8_t (&qb)[4], float sl2,
+__device__ __forceinline__ void nvfp4_step(const uint8_t *blk, int w, int g, int c, const QOp &q, float sl2,
                                            bool valid_head, int nvalid, State &st) {
   const int lane = 16 * g + c;
+  const half8_t (&qb)[4] = q.qb;
   float s[8];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    const int t = 32 * w + 16 * tt + c;
-    const uint4 x = *(const uint4 *)(blk + t * 64 + 16 * g);                  // dims 32g .. 32g+31
-    const uint32_t sb = *(const uint16_t *)(blk + kNvKs + t * 8 + 2 * g);     // scales of blocks 2g, 2g+1
+    const int tl = (2 * w + tt) * 64 + lane;
+    const uint4 x = *(const uint4 *)(blk + tl * 16);                          // dims 32g .. 32g+31 of slot c
+    const uint32_t sb = *(const uint16_t *)(blk + kNvKs + tl * 2);            // scales of blocks 2g, 2g+1
     const uint32_t s0 = e4m3_pair((sb & 0xFFu) * 0x0101u, false);             // (s_2g, s_2g)
     const uint32_t s1 = e4m3_pair((sb >> 8) * 0x0101u, false);                // (s_2g+1, s_2g+1)
     float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -410,13 +441,13 @@ __device__ __forceinline__ void nvfp4_step(const uint8_t *blk, int w, int g, int
     acc = mfma(unpack_fp4(x.w, s1, s1, s1, s1), qb[3], acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float v = acc[i] * sl2;
+      float v = acc[i];
       if (TAIL && 16 * (2 * w + tt) + 4 * g + i >= nvalid) v = kNegInf;
       s[4 * tt + i] = v;
     }
   }
   float p[8];
-  softmax_step(st, s, p, valid_head, 0u);
+  softmax_step(st, s, p, valid_head, 0u, sl2);
   const half8_t pb = h8(pk(p[0], p[1]), pk(p[2], p[3]), pk(p[4], p[5]), pk(p[6], p[7]));
   const uint8_t *vc = blk + kNvVc + (w * 2 * 64 + lane) * 16;
   const uint8_t *vs = blk + kNvVs + (4 * w + g) * 64;                          // [k][e] scale bytes
@@ -432,8 +463,9 @@ __device__ __forceinline__ void nvfp4_step(const uint8_t *blk, int w, int g, int
 }
 
 // fp16 residual, 32 slots u*32 .. u*32+31 (direct global loads; R slots allocated, r used).
-__device__ __forceinline__ void residual_step(const uint8_t *res, int R, int r, int u, int g, int c, const half8_t (&qb)[4],
+__device__ __forceinline__ void residual_step(const uint8_t *res, int R, int r, int u, int g, int c, const QOp &q,
                                               float sl2, bool valid_head, State &st) {
+  const half8_t (&qb)[4] = q.qb;
   const int ntiles = R / 16;
   float s[8];
 #pragma unroll
@@ -449,11 +481,11 @@ __device__ __forceinline__ void residual_step(const uint8_t *res, int R, int r, 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int slot = 16 * tau + 4 * g + i;
-      s[4 * tt + i] = (tau < ntiles && slot < r) ? acc[i] * sl2 : kNegInf;
+      s[4 * tt + i] = (tau < ntiles && slot < r) ? acc[i] : kNegInf;
     }
   }
   float p[8];
-  softmax_step(st, s, p, valid_head, 0u);
+  softmax_step(st, s, p, valid_head, 0u, sl2);
   const half8_t pb = h8(pk(p[0], p[1]), pk(p[2], p[3]), pk(p[4], p[5]), pk(p[6], p[7]));
   const uint8_t *vres = res + (int64_t)R * 256;
 #pragma unroll
@@ -476,6 +508,341 @@ __device__ __forceinline__ void residual_step(const uint8_t *res, int R, int r, 
       }
     }
     st.o[k] = mfma(h8(v[0], v[1], v[2], v[3]), pb, st.o[k]);
+  }
+}
+
+// ================================================================ paired subtiles (G <= 8)
+// A wave's 32 slots are two 16-slot subtiles s = 0, 1.  The QK^T MFMA puts (subtile, head)
+// in its 16 columns, c = 8s + h, and splits its 32-wide k range by lane quarter: quarters
+// 2s and 2s+1 feed the tokens of subtile s (each quarter 8 of the 16 dims of a k-step), and
+// the Q operand is block diagonal (zero where the quarter's subtile is not the column's).
+// So every column carries a real head when G = 8 (half of them when G = 4) and each lane
+// holds 4 logits, not 8.  PV uses v_mfma_f32_16x16x16_f16 once per subtile s0 computing
+// O^T: A = the V codes of subtile s0, B = P' of the lanes whose column subtile is s0 (zero
+// elsewhere); each lane accumulates its own column (subtile, head), and the two subtile
+// columns of a head are summed at the end.
+struct QOp2 {
+  half8_t qb[8];
+  float qs0, qs1;
+};
+
+// Dim (index into the lane's 64 loaded dims) fed by B element e of k-step j, and whether it
+// meets an A element scaled by 16.  Affine formats: the lane holds dims 64G + 16(2q + gi) + m
+// at local index 32G + 16gi + m (G, gi in {0,1}); natural formats dims 64q + i at index i.
+template <int FMT>
+__device__ __forceinline__ int q_loc2(int j, int e, bool &scaled) {
+  const int G = j >> 2, gi = (j >> 1) & 1, hh = j & 1;
+  scaled = false;
+  if constexpr (FMT == kFmtInt4) {
+    scaled = ((e >> 1) & 1) != 0;
+    return 32 * G + 16 * gi + 8 * hh + (e >> 1) + 4 * (e & 1);
+  } else if constexpr (FMT == kFmtInt2) {
+    return 32 * G + 16 * gi + 4 * hh + (e >> 1) + 8 * (e & 1);
+  } else if constexpr (FMT == kFmtInt8) {
+    return 32 * G + 16 * gi + 4 * (2 * hh + (e >> 2)) + ((e >> 1) & 1) + 2 * (e & 1);
+  } else {
+    return 8 * j + e;
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void load_q2(const uint16_t *qrow, bool valid, int g, int c, QOp2 &q) {
+  constexpr bool kAff = FMT == kFmtInt2 || FMT == kFmtInt4 || FMT == kFmtInt8;
+  const int qq = g & 1;
+  const bool active = valid && (c >> 3) == (g >> 1);
+  uint4 raw[8];
+  if constexpr (kAff) {
+#pragma unroll
+    for (int G = 0; G < 2; ++G)
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        const uint16_t *r = qrow + 64 * G + 16 * (2 * qq + gi);
+        raw[4 * G + 2 * gi] = *(const uint4 *)r;
+        raw[4 * G + 2 * gi + 1] = *(const uint4 *)(r + 8);
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) raw[i] = *(const uint4 *)(qrow + 64 * qq + 8 * i);
+  }
+  _Float16 loc[64];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const half8_t v = __builtin_bit_cast(half8_t, raw[i]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) loc[8 * i + e] = active ? v[e] : (_Float16)0.0f;
+  }
+  float qs0 = 0.0f, qs1 = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      bool scaled;
+      _Float16 v = loc[q_loc2<FMT>(j, e, scaled)];
+      if (scaled) v = v * (_Float16)0.0625f;
+      q.qb[j][e] = v;
+      const float eff = scaled ? 16.0f * (float)v : (float)v;
+      if (j < 4) qs0 += eff; else qs1 += eff;
+    }
+  }
+  q.qs0 = quad_sum(qs0);
+  q.qs1 = quad_sum(qs1);
+}
+
+// Running max / probabilities for 4 logits (slots i of the lane's subtile); scaled_mask bit i
+// marks positions whose V operand carries a factor 16 (p / 16 there).
+__device__ __forceinline__ void softmax_step2(State &st, const float (&s)[4], float (&p)[4], bool valid_head,
+                                              unsigned scaled_mask, float sl2) {
+  const float ml = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  if (__builtin_amdgcn_ballot_w64(valid_head && ml > st.m) != 0) {
+    const float m_new = fmaxf(st.m, head_max2(ml));
+    const float alpha = (m_new == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f((st.m - m_new) * sl2);
+    st.l *= alpha;
+    st.z1 *= alpha; st.z16 *= alpha; st.z1b *= alpha; st.z16b *= alpha;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) st.o[k] *= alpha;
+    st.m = m_new;
+  }
+  const float nm = st.m == kNegInf ? 0.0f : -st.m * sl2;
+  const float nm4 = nm - 4.0f;
+  float ls = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool sc = (scaled_mask >> i) & 1;
+    p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, sc ? nm4 : nm));
+    ls = sc ? fmaf(16.0f, p[i], ls) : ls + p[i];
+  }
+  st.l += ls;
+}
+
+// INT4 V operand of subtile s0 from word k: tokens i = 0..3 as [c0, c1, 16 c2, 16 c3] - centre
+template <int NB>
+__device__ __forceinline__ half4_t v_operand2(const uint32_t *vw, int k, int s0);
+
+template <>
+__device__ __forceinline__ half4_t v_operand2<4>(const uint32_t *vw, int k, int s0) {
+  const uint32_t x = s0 ? vw[k] >> 8 : vw[k];
+  return h4(field_pair<8>(x, 0x000F000Fu), field_pair<128>(x, 0x00F000F0u));
+}
+template <>
+__device__ __forceinline__ half4_t v_operand2<2>(const uint32_t *vw, int k, int s0) {
+  // word k >> 1 holds tiles 2(k>>1) + a; pairs (crumb s, crumb s+8), s = 4a + 2 s0 + {0, 1}
+  const uint32_t x = vw[k >> 1] >> (2 * (4 * (k & 1) + 2 * s0));
+  return h4(field_pair<2>(x, 0x00030003u), field_pair<2>(x >> 2, 0x00030003u));
+}
+template <>
+__device__ __forceinline__ half4_t v_operand2<8>(const uint32_t *vw, int k, int s0) {
+  const uint32_t x = vw[2 * k + s0];
+  return h4(field_pair<128>(x, 0x00FF00FFu), field_pair<128>(x >> 8, 0x00FF00FFu));
+}
+
+template <int NB, bool TAIL>
+__device__ __forceinline__ void affine_step2(const uint8_t *blk, int w, int g, int c, const QOp2 &q, float sl2,
+                                             bool valid_head, int nvalid, State &st) {
+  constexpr int kKm = 2048 * NB, kVc = 2048 * NB + 1024, kVm = 4096 * NB + 1024;
+  const int lane = 16 * g + c;
+  const int qq = g & 1, sa = g >> 1;           // A operand: this lane feeds subtile sa, dim half qq
+  const int sc = c >> 3;                       // output column subtile
+
+  // V codes of this lane ([part w][chunk][lane][16 B]) and V meta of the column's slots
+  constexpr int kChunks = NB / 2;
+  uint32_t vw[2 * NB];
+  {
+    const uint8_t *vc = blk + kVc + (w * kChunks * 64 + lane) * 16;
+#pragma unroll
+    for (int r = 0; r < kChunks; ++r) {
+      const uint4 x = *(const uint4 *)(vc + r * 1024);
+      vw[4 * r] = x.x; vw[4 * r + 1] = x.y; vw[4 * r + 2] = x.z; vw[4 * r + 3] = x.w;
+    }
+  }
+  const int tau_c = 2 * w + sc;
+  const uint4 vm = *(const uint4 *)(blk + kVm + (tau_c * 4 + g) * 32);          // S_G0[0..3], S_G1[0..3]
+  const uint4 vz = *(const uint4 *)(blk + kVm + (tau_c * 4 + g) * 32 + 16);     // Z_G0[0..3], Z_G1[0..3]
+  const uint4 ks = *(const uint4 *)(blk + kKm + tau_c * 128 + 16 * g);          // (S0, S1) of slots 4g+i
+  const uint4 kz = *(const uint4 *)(blk + kKm + tau_c * 128 + 64 + 16 * g);     // (Z0, Z1)
+
+  // QK^T: lane feeds token (subtile sa, row c), dims of layout chunks 2qq and 2qq+1
+  const int tau_a = 2 * w + sa;
+  float4_t a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0;
+  if constexpr (NB == 4) {
+    const uint4 x0 = *(const uint4 *)(blk + (tau_a * 64 + 16 * (2 * qq) + c) * 16);
+    const uint4 x1 = *(const uint4 *)(blk + (tau_a * 64 + 16 * (2 * qq + 1) + c) * 16);
+    a0 = mfma(unpack_int4<false>(x0.x), q.qb[0], a0);
+    a0 = mfma(unpack_int4<false>(x0.y), q.qb[1], a0);
+    a0 = mfma(unpack_int4<false>(x1.x), q.qb[2], a0);
+    a0 = mfma(unpack_int4<false>(x1.y), q.qb[3], a0);
+    a1 = mfma(unpack_int4<false>(x0.z), q.qb[4], a1);
+    a1 = mfma(unpack_int4<false>(x0.w), q.qb[5], a1);
+    a1 = mfma(unpack_int4<false>(x1.z), q.qb[6], a1);
+    a1 = mfma(unpack_int4<false>(x1.w), q.qb[7], a1);
+  } else if constexpr (NB == 2) {
+    const uint2 x0 = *(const uint2 *)(blk + (tau_a * 64 + 16 * (2 * qq) + c) * 8);
+    const uint2 x1 = *(const uint2 *)(blk + (tau_a * 64 + 16 * (2 * qq + 1) + c) * 8);
+    half8_t l0, h0, l1, h1;
+    unpack_int2<false>(x0.x, l0, h0);
+    unpack_int2<false>(x1.x, l1, h1);
+    a0 = mfma(l0, q.qb[0], a0);
+    a0 = mfma(h0, q.qb[1], a0);
+    a0 = mfma(l1, q.qb[2], a0);
+    a0 = mfma(h1, q.qb[3], a0);
+    unpack_int2<false>(x0.y, l0, h0);
+    unpack_int2<false>(x1.y, l1, h1);
+    a1 = mfma(l0, q.qb[4], a1);
+    a1 = mfma(h0, q.qb[5], a1);
+    a1 = mfma(l1, q.qb[6], a1);
+    a1 = mfma(h1, q.qb[7], a1);
+  } else {
+    // chunk r of (tile, lane') at ((tile * 2 + r) * 64 + lane') * 16, r = group G
+    const uint8_t *k0 = blk + ((tau_a * 2) * 64 + 16 * (2 * qq) + c) * 16;
+    const uint8_t *k1 = blk + ((tau_a * 2) * 64 + 16 * (2 * qq + 1) + c) * 16;
+    const uint4 x0 = *(const uint4 *)k0, y0 = *(const uint4 *)(k0 + 1024);
+    const uint4 x1 = *(const uint4 *)k1, y1 = *(const uint4 *)(k1 + 1024);
+    a0 = mfma(unpack_int8<false>(x0.x, x0.y), q.qb[0], a0);
+    a0 = mfma(unpack_int8<false>(x0.z, x0.w), q.qb[1], a0);
+    a0 = mfma(unpack_int8<false>(x1.x, x1.y), q.qb[2], a0);
+    a0 = mfma(unpack_int8<false>(x1.z, x1.w), q.qb[3], a0);
+    a1 = mfma(unpack_int8<false>(y0.x, y0.y), q.qb[4], a1);
+    a1 = mfma(unpack_int8<false>(y0.z, y0.w), q.qb[5], a1);
+    a1 = mfma(unpack_int8<false>(y1.x, y1.y), q.qb[6], a1);
+    a1 = mfma(unpack_int8<false>(y1.z, y1.w), q.qb[7], a1);
+  }
+  float s[4];
+  const uint32_t sw[4] = {ks.x, ks.y, ks.z, ks.w}, zw[4] = {kz.x, kz.y, kz.z, kz.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float u0 = fmaf(-lo_f(zw[i]), q.qs0, a0[i]);
+    const float u1 = fmaf(-hi_f(zw[i]), q.qs1, a1[i]);
+    float v = fmaf(hi_f(sw[i]), u1, lo_f(sw[i]) * u0);
+    if (TAIL && 16 * tau_c + 4 * g + i >= nvalid) v = kNegInf;
+    s[i] = v;
+  }
+  float p[4];
+  constexpr unsigned kScaled = NB == 4 ? 0xCu : 0u;   // INT4: positions i = 2, 3
+  softmax_step2(st, s, p, valid_head, kScaled, sl2);
+
+  // P' = p * S per group (one fp16 rounding) and the zero-point sums sum P' (Z - C)
+  constexpr _Float16 kC = (_Float16)(1 << (NB - 1));
+  const half2_t cc = {kC, kC};
+  const uint32_t a01 = pk(p[0] * lo_f(vm.x), p[1] * hi_f(vm.x)), a23 = pk(p[2] * lo_f(vm.y), p[3] * hi_f(vm.y));
+  const uint32_t b01 = pk(p[0] * lo_f(vm.z), p[1] * hi_f(vm.z)), b23 = pk(p[2] * lo_f(vm.w), p[3] * hi_f(vm.w));
+  if constexpr (NB == 4) {
+    st.z1 = __builtin_amdgcn_fdot2(as_h2(a01), as_h2(vz.x) - cc, st.z1, false);
+    st.z16 = __builtin_amdgcn_fdot2(as_h2(a23), as_h2(vz.y) - cc, st.z16, false);
+    st.z1b = __builtin_amdgcn_fdot2(as_h2(b01), as_h2(vz.z) - cc, st.z1b, false);
+    st.z16b = __builtin_amdgcn_fdot2(as_h2(b23), as_h2(vz.w) - cc, st.z16b, false);
+  } else {
+    st.z1 = __builtin_amdgcn_fdot2(as_h2(a01), as_h2(vz.x) - cc, st.z1, false);
+    st.z1 = __builtin_amdgcn_fdot2(as_h2(a23), as_h2(vz.y) - cc, st.z1, false);
+    st.z1b = __builtin_amdgcn_fdot2(as_h2(b01), as_h2(vz.z) - cc, st.z1b, false);
+    st.z1b = __builtin_amdgcn_fdot2(as_h2(b23), as_h2(vz.w) - cc, st.z1b, false);
+  }
+  // PV as O^T += V^T P per subtile s0: A = V codes of s0, B = this lane's P' where its column
+  // subtile is s0 (else zero); the accumulator rows are dims, its column the lane's head.
+  const half4_t pa0 = sc == 0 ? h4(a01, a23) : h4(0u, 0u), pb0 = sc == 0 ? h4(b01, b23) : h4(0u, 0u);
+  const half4_t pa1 = sc == 1 ? h4(a01, a23) : h4(0u, 0u), pb1 = sc == 1 ? h4(b01, b23) : h4(0u, 0u);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    st.o[k] = mfma16(v_operand2<NB>(vw, k, 0), k < 4 ? pa0 : pb0, st.o[k]);
+    st.o[k] = mfma16(v_operand2<NB>(vw, k, 1), k < 4 ? pa1 : pb1, st.o[k]);
+  }
+}
+
+template <bool TAIL>
+__device__ __forceinline__ void nvfp4_step2(const uint8_t *blk, int w, int g, int c, const QOp2 &q, float sl2,
+                                            bool valid_head, int nvalid, State &st) {
+  const int lane = 16 * g + c;
+  const int qq = g & 1, sa = g >> 1, sc = c >> 3;
+  const int tau_a = 2 * w + sa, tau_c = 2 * w + sc;
+  const int l0 = tau_a * 64 + 16 * (2 * qq) + c, l1 = l0 + 16;
+  const uint4 x0 = *(const uint4 *)(blk + l0 * 16), x1 = *(const uint4 *)(blk + l1 * 16);
+  const uint32_t sb0 = *(const uint16_t *)(blk + kNvKs + l0 * 2), sb1 = *(const uint16_t *)(blk + kNvKs + l1 * 2);
+  const uint32_t s00 = e4m3_pair((sb0 & 0xFFu) * 0x0101u, false), s01 = e4m3_pair((sb0 >> 8) * 0x0101u, false);
+  const uint32_t s10 = e4m3_pair((sb1 & 0xFFu) * 0x0101u, false), s11 = e4m3_pair((sb1 >> 8) * 0x0101u, false);
+  const uint4 vx0 = *(const uint4 *)(blk + kNvVc + (w * 2 * 64 + lane) * 16);
+  const uint4 vx1 = *(const uint4 *)(blk + kNvVc + (w * 2 * 64 + lane) * 16 + 1024);
+  const uint32_t vw[8] = {vx0.x, vx0.y, vx0.z, vx0.w, vx1.x, vx1.y, vx1.z, vx1.w};
+  const uint8_t *vs = blk + kNvVs + (4 * w + g) * 64;                          // [k][e] scale bytes
+
+  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  acc = mfma(unpack_fp4(x0.x, s00, s00, s00, s00), q.qb[0], acc);
+  acc = mfma(unpack_fp4(x0.y, s00, s00, s00, s00), q.qb[1], acc);
+  acc = mfma(unpack_fp4(x0.z, s01, s01, s01, s01), q.qb[2], acc);
+  acc = mfma(unpack_fp4(x0.w, s01, s01, s01, s01), q.qb[3], acc);
+  acc = mfma(unpack_fp4(x1.x, s10, s10, s10, s10), q.qb[4], acc);
+  acc = mfma(unpack_fp4(x1.y, s10, s10, s10, s10), q.qb[5], acc);
+  acc = mfma(unpack_fp4(x1.z, s11, s11, s11, s11), q.qb[6], acc);
+  acc = mfma(unpack_fp4(x1.w, s11, s11, s11, s11), q.qb[7], acc);
+  float s[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v = acc[i];
+    if (TAIL && 16 * tau_c + 4 * g + i >= nvalid) v = kNegInf;
+    s[i] = v;
+  }
+  float p[4];
+  softmax_step2(st, s, p, valid_head, 0u, sl2);
+  const uint32_t p01 = pk(p[0], p[1]), p23 = pk(p[2], p[3]);
+  const half4_t pa0 = sc == 0 ? h4(p01, p23) : h4(0u, 0u), pa1 = sc == 1 ? h4(p01, p23) : h4(0u, 0u);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint2 scb = *(const uint2 *)(vs + 8 * k);      // scales of e = 0..3 (subtile 0), 4..7 (subtile 1)
+    const uint32_t f0 = as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vw[k], 1.0f, 0));
+    const uint32_t f1 = as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vw[k], 1.0f, 1));
+    const uint32_t f2 = as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vw[k], 1.0f, 2));
+    const uint32_t f3 = as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vw[k], 1.0f, 3));
+    const half4_t b0 = h4(as_u(as_h2(f0) * as_h2(e4m3_pair(scb.x, false))), as_u(as_h2(f1) * as_h2(e4m3_pair(scb.x, true))));
+    const half4_t b1 = h4(as_u(as_h2(f2) * as_h2(e4m3_pair(scb.y, false))), as_u(as_h2(f3) * as_h2(e4m3_pair(scb.y, true))));
+    st.o[k] = mfma16(b0, pa0, st.o[k]);
+    st.o[k] = mfma16(b1, pa1, st.o[k]);
+  }
+}
+
+// fp16 residual, slots 32u .. 32u+31, paired subtiles (direct global loads).
+__device__ __forceinline__ void residual_step2(const uint8_t *res, int R, int r, int u, int g, int c, const QOp2 &q,
+                                               float sl2, bool valid_head, State &st) {
+  const int ntiles = R / 16;
+  const int qq = g & 1, sa = g >> 1, sc = c >> 3;
+  const int tau_a = 2 * u + sa, tau_c = 2 * u + sc;
+  // Rows past r may hold stale bits (even NaN); with the block-diagonal Q a NaN row would reach
+  // the other subtile's columns through 0 * NaN, so such rows are fed as zeros.
+  const bool arow = tau_a < ntiles && 16 * tau_a + c < r;
+  const uint4 *row = (const uint4 *)(res + (arow ? 16 * tau_a + c : 0) * 256 + 128 * qq);   // dims 64qq .. 64qq+63
+  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint4 x = row[j];
+    acc = mfma(arow ? __builtin_bit_cast(half8_t, x) : h8(0u, 0u, 0u, 0u), q.qb[j], acc);
+  }
+  float s[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int slot = 16 * tau_c + 4 * g + i;
+    s[i] = (tau_c < ntiles && slot < r) ? acc[i] : kNegInf;
+  }
+  float p[4];
+  softmax_step2(st, s, p, valid_head, 0u, sl2);
+  const uint32_t p01 = pk(p[0], p[1]), p23 = pk(p[2], p[3]);
+  const half4_t pa0 = sc == 0 ? h4(p01, p23) : h4(0u, 0u), pa1 = sc == 1 ? h4(p01, p23) : h4(0u, 0u);
+  const uint8_t *vres = res + (int64_t)R * 256;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int d = 16 * k + c;
+#pragma unroll
+    for (int s0 = 0; s0 < 2; ++s0) {
+      const int tau = 2 * u + s0;
+      uint32_t v0 = 0u, v1 = 0u;
+      if (tau < ntiles) {
+        const uint2 x = *(const uint2 *)(vres + ((tau * kHeadDim + d) * 16 + 4 * g) * 2);
+        v0 = x.x;
+        v1 = x.y;
+        // slots past r may hold stale bits (even NaN): zero them
+        const int t0 = 16 * tau + 4 * g;
+        if (t0 + 0 >= r) v0 &= 0xFFFF0000u;
+        if (t0 + 1 >= r) v0 &= 0x0000FFFFu;
+        if (t0 + 2 >= r) v1 &= 0xFFFF0000u;
+        if (t0 + 3 >= r) v1 &= 0x0000FFFFu;
+      }
+      st.o[k] = mfma16(h4(v0, v1), s0 ? pa1 : pa0, st.o[k]);
+    }
   }
 }
 
@@ -511,18 +878,26 @@ __device__ __forceinline__ int block_bytes_of(int fmt) { return (int)block_bytes
 // LDS ring depth: four blocks (three in flight) when two workgroups still fit in a CU.
 __host__ __device__ __forceinline__ int ring_depth(int bb) { return bb <= 18432 ? 4 : 3; }
 
-template <int FMT>
+// Query row of the head a lane's column belongs to (a valid row even for padding columns).
+template <int NSUB>
+__device__ __forceinline__ const uint16_t *q_row(const DecodeArgs &a, int bh, int c, bool valid_head) {
+  const int b = bh / a.H, h = bh % a.H;
+  const int hc = valid_head ? (NSUB == 2 ? (c & 7) : c) : 0;
+  return a.q + ((int64_t)b * a.H * a.G + (int64_t)h * a.G + hc) * kHeadDim;
+}
+
+template <int FMT, int NSUB>
 __device__ void stream_segment(const DecodeArgs &a, const DecodeSeg &sg, const Item &it, uint8_t *smem, int w, int g, int c,
                                bool valid_head, State &st) {
   const int lane = 16 * g + c;
   const int bb = block_bytes_of(FMT);
   const int ndma = bb / 1024;                                 // 1 KB per wave instruction
   const int mine = (ndma - w + kWaves - 1) / kWaves;          // instructions this wave issues per block
-  const int b = it.bh / a.H, h = it.bh % a.H;
-  const uint16_t *qrow = a.q + ((int64_t)b * a.H * a.G + (int64_t)h * a.G + (valid_head ? c : 0)) * kHeadDim;
-  half8_t qb[4];
-  float qs0, qs1;
-  load_q<FMT>(qrow, valid_head, g, qb, qs0, qs1);
+  const uint16_t *qrow = q_row<NSUB>(a, it.bh, c, valid_head);
+  QOp q;
+  QOp2 q2;
+  if constexpr (NSUB == 2) load_q2<FMT>(qrow, valid_head, g, c, q2);
+  else load_q<FMT>(qrow, valid_head, g, q.qb, q.qs0, q.qs1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   const uint8_t *gbase = sg.base + (int64_t)it.bh * sg.bh_stride + it.blk_lo * (int64_t)bb + lane * 16;
@@ -548,32 +923,68 @@ __device__ void stream_segment(const DecodeArgs &a, const DecodeSeg &sg, const I
     if (i + nbuf - 1 < n) issue(i + nbuf - 1);
     const uint8_t *blk = smem + buf * bb;
     buf = buf + 1 == nbuf ? 0 : buf + 1;
-    if (i < nfull) {
-      if constexpr (FMT == kFmtNvfp4) nvfp4_step<false>(blk, w, g, c, qb, a.scale_log2, valid_head, kBlock, st);
-      else affine_step<FMT, false>(blk, w, g, c, qb, qs0, qs1, a.scale_log2, valid_head, kBlock, st);
+    const bool full = i < nfull;
+    const int nv = full ? kBlock : tail_valid;
+    if constexpr (NSUB == 2) {
+      if constexpr (FMT == kFmtNvfp4) {
+        if (full) nvfp4_step2<false>(blk, w, g, c, q2, a.scale_log2, valid_head, nv, st);
+        else nvfp4_step2<true>(blk, w, g, c, q2, a.scale_log2, valid_head, nv, st);
+      } else {
+        if (full) affine_step2<FMT, false>(blk, w, g, c, q2, a.scale_log2, valid_head, nv, st);
+        else affine_step2<FMT, true>(blk, w, g, c, q2, a.scale_log2, valid_head, nv, st);
+      }
     } else {
-      if constexpr (FMT == kFmtNvfp4) nvfp4_step<true>(blk, w, g, c, qb, a.scale_log2, valid_head, tail_valid, st);
-      else affine_step<FMT, true>(blk, w, g, c, qb, qs0, qs1, a.scale_log2, valid_head, tail_valid, st);
+      if constexpr (FMT == kFmtNvfp4) {
+        if (full) nvfp4_step<false>(blk, w, g, c, q, a.scale_log2, valid_head, nv, st);
+        else nvfp4_step<true>(blk, w, g, c, q, a.scale_log2, valid_head, nv, st);
+      } else {
+        if (full) affine_step<FMT, false>(blk, w, g, c, q, a.scale_log2, valid_head, nv, st);
+        else affine_step<FMT, true>(blk, w, g, c, q, a.scale_log2, valid_head, nv, st);
+      }
     }
   }
   barrier();   // every wave is done with the ring before it is reused
-  if constexpr (FMT != kFmtNvfp4) {
-    // fold the zero points into o: o[d] -= sum_t P'_t (Z_t - C) of the group of d
-    float zg0 = st.z1 + 16.0f * st.z16, zg1 = st.z1b + 16.0f * st.z16b;
-    zg0 += __shfl_xor(zg0, 16);
-    zg0 += __shfl_xor(zg0, 32);
-    zg1 += __shfl_xor(zg1, 16);
-    zg1 += __shfl_xor(zg1, 32);
+}
+
+// Per-wave state -> LDS rows for the workgroup merge: m[16], l[16] (log2 units) and
+// o[16][128], heads in natural order.  Folds the zero-point sums sum P'(Z - C) into o.
+template <int NSUB>
+__device__ __forceinline__ void state_to_lds(State &st, int w, int g, int c, float sl2, float *wm, float *wl, float *wo) {
+  if constexpr (NSUB == 1) {
+    const float zg0 = quad_sum(st.z1 + 16.0f * st.z16), zg1 = quad_sum(st.z1b + 16.0f * st.z16b);
+    const float l = quad_sum(st.l);
+    if (g == 0) {
+      wm[w * 16 + c] = st.m * sl2;
+      wl[w * 16 + c] = l;
+    }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) st.o[k] -= (k < 4 ? zg0 : zg1);
-    st.z1 = st.z16 = st.z1b = st.z16b = 0.0f;
+    for (int k = 0; k < 8; ++k) *(float4_t *)(wo + ((w * 16 + c) * kHeadDim + 16 * k + 4 * g)) = st.o[k] - (k < 4 ? zg0 : zg1);
+  } else {
+    // lane (c, g): column (subtile c >> 3, head c & 7), accumulator rows dims 16k + 4g + i;
+    // the subtile-1 column of a head is lane c ^ 8
+    const float zg0 = head_sum2(st.z1 + 16.0f * st.z16), zg1 = head_sum2(st.z1b + 16.0f * st.z16b);
+    const float l = head_sum2(st.l);
+    if (g == 0 && c < 8) {
+      wm[w * 16 + c] = st.m * sl2;
+      wl[w * 16 + c] = l;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      float4_t o = st.o[k];
+      o[0] += __shfl_xor(o[0], 8);
+      o[1] += __shfl_xor(o[1], 8);
+      o[2] += __shfl_xor(o[2], 8);
+      o[3] += __shfl_xor(o[3], 8);
+      if (c < 8) *(float4_t *)(wo + ((w * 16 + c) * kHeadDim + 16 * k + 4 * g)) = o - (k < 4 ? zg0 : zg1);
+    }
   }
 }
 
+template <int NSUB>
 __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-  const bool valid_head = c < a.G;
+  const bool valid_head = (NSUB == 2 ? (c & 7) : c) < a.G;
   const Item it = decode_item(a, blockIdx.x);
   State st;
 #pragma unroll
@@ -582,36 +993,32 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   if (it.seg >= 0) {
     const DecodeSeg &sg = a.seg[it.seg];
     switch (sg.fmt) {
-      case kFmtInt2: stream_segment<kFmtInt2>(a, sg, it, smem, w, g, c, valid_head, st); break;
-      case kFmtInt4: stream_segment<kFmtInt4>(a, sg, it, smem, w, g, c, valid_head, st); break;
-      case kFmtInt8: stream_segment<kFmtInt8>(a, sg, it, smem, w, g, c, valid_head, st); break;
-      default: stream_segment<kFmtNvfp4>(a, sg, it, smem, w, g, c, valid_head, st); break;
+      case kFmtInt2: stream_segment<kFmtInt2, NSUB>(a, sg, it, smem, w, g, c, valid_head, st); break;
+      case kFmtInt4: stream_segment<kFmtInt4, NSUB>(a, sg, it, smem, w, g, c, valid_head, st); break;
+      case kFmtInt8: stream_segment<kFmtInt8, NSUB>(a, sg, it, smem, w, g, c, valid_head, st); break;
+      default: stream_segment<kFmtNvfp4, NSUB>(a, sg, it, smem, w, g, c, valid_head, st); break;
     }
   }
   if (it.has_res) {
-    const int b = it.bh / a.H, h = it.bh % a.H;
-    const uint16_t *qrow = a.q + ((int64_t)b * a.H * a.G + (int64_t)h * a.G + (valid_head ? c : 0)) * kHeadDim;
-    half8_t qb[4];
-    float qs0, qs1;
-    load_q<kFmtFp16>(qrow, valid_head, g, qb, qs0, qs1);
+    const uint16_t *qrow = q_row<NSUB>(a, it.bh, c, valid_head);
     const uint8_t *res = a.res_base + (int64_t)it.bh * a.res_bh_stride;
     const int nsteps = (a.res_ntok + 31) / 32;
-    for (int u = w; u < nsteps; u += kWaves) residual_step(res, a.res_len, a.res_ntok, u, g, c, qb, a.scale_log2, valid_head, st);
+    if constexpr (NSUB == 2) {
+      QOp2 q;
+      load_q2<kFmtFp16>(qrow, valid_head, g, c, q);
+      for (int u = w; u < nsteps; u += kWaves) residual_step2(res, a.res_len, a.res_ntok, u, g, c, q, a.scale_log2, valid_head, st);
+    } else {
+      QOp q;
+      load_q<kFmtFp16>(qrow, valid_head, g, q.qb, q.qs0, q.qs1);
+      for (int u = w; u < nsteps; u += kWaves) residual_step(res, a.res_len, a.res_ntok, u, g, c, q, a.scale_log2, valid_head, st);
+    }
   }
 
-  // ---- merge the four waves in LDS: per wave m[16], l[16], o[16][128]
-  float l = st.l;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  // ---- merge the four waves in LDS: per wave m[16], l[16], o[16][128] (m in log2 units)
   float *wm = (float *)smem;                       // [4][16]
   float *wl = wm + kWaves * 16;                    // [4][16]
   float *wo = wl + kWaves * 16;                    // [4][16][128]
-  if (g == 0) {
-    wm[w * 16 + c] = st.m;
-    wl[w * 16 + c] = l;
-  }
-#pragma unroll
-  for (int k = 0; k < 8; ++k) *(float4_t *)(wo + ((w * 16 + c) * kHeadDim + 16 * k + 4 * g)) = st.o[k];
+  state_to_lds<NSUB>(st, w, g, c, a.scale_log2, wm, wl, wo);
   __syncthreads();
 
   const int G = a.G;
@@ -716,12 +1123,16 @@ size_t decode_lds_bytes(const DecodeArgs &a) {
 hipError_t launch_decode(const DecodeArgs &a, int num_wg, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)decode_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+    hipError_t e = hipFuncSetAttribute((const void *)decode_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void *)decode_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const size_t lds = decode_lds_bytes(a);
-  decode_kernel<<<(unsigned)num_wg, kThreads, lds, s>>>(a);
+  // two 16-slot subtiles share the MFMA columns when at most 8 query heads share a kv head
+  if (a.G <= 8) decode_kernel<2><<<(unsigned)num_wg, kThreads, lds, s>>>(a);
+  else decode_kernel<1><<<(unsigned)num_wg, kThreads, lds, s>>>(a);
   return hipGetLastError();
 }
 

@@ -98,13 +98,14 @@ __device__ __forceinline__ uint32_t e2m1_code(float x, float s) {
   return idx | (signbit(x) ? 8u : 0u);
 }
 
-// Block layout (128 slots, head_dim 128).  K rows: affine field f holds dim
-// 64*((f >> 4) & 1) + 16*(f >> 5) + (f & 15) (each 16-field half of a lane quarter stays in
-// one 64-dim group); NVFP4 field f holds dim f.  V codes: 4 parts w x 64 lanes (g = lane >> 4,
-// c = lane & 15) x 8n bytes in 16-byte chunks; lane field phi holds dim 16k + c and slot
-// 32w + 16(e >> 2) + 4g + (e & 3), (k, e) per format below.
-__device__ __forceinline__ int k_field_dim(int fmt, int f) {
-  return fmt == kFmtNvfp4 ? f : 64 * ((f >> 4) & 1) + 16 * (f >> 5) + (f & 15);
+// Block layout (128 slots, head_dim 128).  K codes: 4 parts w x 2 tiles u x 64 lanes
+// (g = lane >> 4, c = lane & 15) x 4n bytes (NVFP4 16) of slot 32w + 16u + c, stored in
+// chunks of min(16, 4n) bytes; lane field f holds dim 64(f >> 4) + 16g + (f & 15) (affine)
+// or 32g + f (NVFP4).  V codes: 4 parts w x 64 lanes x 8n bytes in 16-byte chunks; lane
+// field phi holds dim 16k + c and slot 32w + 16(e >> 2) + 4g + (e & 3), (k, e) per format
+// below.
+__device__ __forceinline__ int k_lane_dim(int fmt, int g, int f) {
+  return fmt == kFmtNvfp4 ? 32 * g + f : 64 * (f >> 4) + 16 * g + (f & 15);
 }
 
 __device__ __forceinline__ void v_field(int fmt, int phi, int &k, int &e) {
@@ -237,7 +238,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
       }
       if (write) {
         if (kv == 0) {
-          blkp[kNvKs + slot * 8 + nb] = sb;
+          const int lane = 16 * (nb >> 1) + (slot & 15);
+          blkp[kNvKs + ((slot >> 4) * 64 + lane) * 2 + (nb & 1)] = sb;
         } else {
           const int w = slot >> 5, tt = (slot >> 4) & 1, q = (slot >> 2) & 3, i = slot & 3;
           blkp[kNvVs + ((4 * w + q) * 8 + nb) * 8 + 4 * tt + i] = sb;
@@ -251,22 +253,30 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
   constexpr int F = 32 / kBits;                     // fields per word
   constexpr int kWords = kBlock * kWordsPerRow;
   if (kv == 0) {
-    // K: row = slot
+    // K: [part w][tile u][chunk r][lane][cb bytes]; every word holds fields of one slot
+    constexpr int kLaneBytes = 4 * kBits;
+    constexpr int kCb = kLaneBytes < 16 ? kLaneBytes : 16;
+    constexpr int kK = kLaneBytes / kCb;
     for (int w = tid; w < kWords; w += kThreads) {
-      const int slot = w / kWordsPerRow, wi = w % kWordsPerRow;
+      const int ci = (4 * w) / kCb, in_chunk = (4 * w) % kCb;
+      const int lane = ci & 63, t2 = ci >> 6;
+      const int r = t2 % kK, wu = t2 / kK;
+      const int g = lane >> 4, c = lane & 15;
+      const int slot = 16 * wu + c;                  // 32 * part + 16 * tile + c
       if (slot < lo || slot >= zhi) continue;
+      const int omega = (r * kCb + in_chunk) / 4;    // word of the lane string
       uint32_t word = 0;
       if (slot < hi) {
         for (int k = 0; k < F; ++k) {
-          const int d = k_field_dim(FMT, wi * F + k);
+          const int d = k_lane_dim(FMT, g, omega * F + k);
           const float x = h2f(xs[slot * kRowHalves + d]);
-          uint32_t c;
-          if constexpr (kNv) c = e2m1_code(x, mS[slot][d / kNvBlock]);
-          else c = affine_code(x, mS[slot][d / kGroup], mInv[slot][d / kGroup], mZ[slot][d / kGroup], kQmax);
-          word |= c << (k * kBits);
+          uint32_t cd;
+          if constexpr (kNv) cd = e2m1_code(x, mS[slot][d / kNvBlock]);
+          else cd = affine_code(x, mS[slot][d / kGroup], mInv[slot][d / kGroup], mZ[slot][d / kGroup], kQmax);
+          word |= cd << (k * kBits);
         }
       }
-      *(uint32_t *)(blkp + slot * kRowBytes + wi * 4) = word;
+      *(uint32_t *)(blkp + (size_t)w * 4) = word;
     }
   } else {
     // V: [part w][chunk r][lane][16 bytes]; lane word omega = 4r + (word in chunk)

@@ -114,7 +114,8 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t num_q_heads);
    q: fp16 [batch][num_q_heads][128]; out: [batch][num_q_heads][128] fp32 if out_fp32 else
    fp16; workspace: at least kvq_decode_workspace_bytes() bytes, 16-byte aligned, scratch
    owned by the caller (its contents on entry do not matter).  The cache is not modified.
-   num_q_heads must be a multiple of num_kv_heads with a group of at most 16.
+   num_q_heads must be a multiple of num_kv_heads with a group of at most 16; softmax_scale
+   must be positive and finite.
    Errors: KVQ_EINVAL, KVQ_ENOSPACE (workspace), KVQ_ESTATE (layer empty), KVQ_EHIP. */
 int kvq_decode_attn(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_heads, float softmax_scale,
                     void *out, int32_t out_fp32, void *workspace, size_t ws_bytes, void *stream);

@@ -14,14 +14,17 @@ Notation: a block holds 128 token slots t = 0..127; D = 128 dims; n = code bits
 occupies bits [f*n, f*n + n) of the byte string, bit b of the string being bit
 (b mod 8) of byte b // 8.  A block is [Kc][Km][Vc][Vm].
 
-Kc, affine (2048n bytes): 128 rows (slot t) of 16n bytes.  A row is the field
-    string of 128 fields; field f = 32q + 16G + m (quarter q = 0..3, group G = 0, 1,
-    m = 0..15) holds the code of dim 64G + 16q + m.
-Kc, NVFP4 (8192 bytes): 128 rows of 64 bytes; field d holds the code of dim d.
+Kc (2048n bytes; NVFP4 8192): 4 parts w x 2 tiles u x 64 lanes L (g = L div 16,
+    c = L mod 16), each lane holding 4n bytes (NVFP4 16) of slot t = 32w + 16u + c:
+    the field string of 32 fields, field f holding the code of dim
+    64(f div 16) + 16g + (f mod 16) (affine) or of dim 32g + f (NVFP4).  Lane data
+    is stored in chunks of min(16, 4n) bytes: chunk r of lane L of (w, u) at
+    (((2w + u)*K + r)*64 + L)*min(16, 4n), K = 4n / min(16, 4n) (INT2 8-byte
+    chunks, INT4 and NVFP4 one 16-byte chunk, INT8 two 16-byte chunks).
 Km, affine (1024 bytes): 8 tiles tau of 128 bytes (slots 16tau + r, r = 0..15):
     fp16 S at tau*128 + 4r + 2G, fp16 Z at tau*128 + 64 + 4r + 2G.
-Km, NVFP4 (1024 bytes): 128 rows of 8 bytes; byte b of row t = E4M3 scale of
-    dims 16b..16b+15 of slot t.
+Km, NVFP4 (1024 bytes): 2 bytes per (w, u, L) at ((2w + u)*64 + L)*2: the E4M3
+    scales of dims 32g..32g+15 and 32g+16..32g+31 of slot 32w + 16u + c.
 Vc (2048n bytes; NVFP4 8192): 4 parts w, each 64 lanes L (g = L div 16,
     c = L mod 16) of 8n bytes, stored as n/2 chunks of 16 bytes: chunk r of lane
     L of part w at ((w*(n/2) + r)*64 + L)*16.  The lane's 8n bytes are the field
@@ -64,11 +67,28 @@ def block_bytes(fmt: str) -> int:
     return affine_block_bytes(int(fmt[3:]))
 
 
-def k_field_dims() -> np.ndarray:
-    """Affine Kc row: field f -> dim (f = 32q + 16G + m holds dim 64G + 16q + m)."""
-    f = np.arange(128)
-    q, G, m = f // 32, (f // 16) % 2, f % 16
-    return 64 * G + 16 * q + m
+def k_lane_dims(fmt: str, g: int) -> np.ndarray:
+    """Kc lane field string of lane quarter g: field f (0..31) -> dim."""
+    f = np.arange(32)
+    if fmt == "nvfp4":
+        return 32 * g + f
+    return 64 * (f // 16) + 16 * g + f % 16
+
+
+def _pack_kc(fmt: str, codes_k: np.ndarray) -> np.ndarray:
+    """Kc region from the [slot, dim] code array."""
+    n = code_bits(fmt)
+    lane_bytes = 4 * n
+    cb = min(16, lane_bytes)
+    K = lane_bytes // cb
+    out = np.zeros((4, 2, K, 64, cb), np.uint8)
+    for w in range(4):
+        for u in range(2):
+            for L in range(64):
+                g, c = L // 16, L % 16
+                t = 32 * w + 16 * u + c
+                out[w, u, :, L, :] = pack_fields(codes_k[t, k_lane_dims(fmt, g)], n).reshape(K, cb)
+    return out.ravel()
 
 
 def v_lane_fields(fmt: str) -> tuple[np.ndarray, np.ndarray]:
@@ -143,7 +163,7 @@ def pack_affine_block(n: int, kq: dict, vq: dict, used: int) -> np.ndarray:
     Sv = np.zeros((BLOCK, 2), np.float16); Sv[:used] = vq["S"]
     Zv = np.zeros((BLOCK, 2), np.float16); Zv[:used] = vq["Z"]
 
-    kc = pack_fields(codes_k[:, k_field_dims()], n).ravel()                # 128 rows x 16n
+    kc = _pack_kc(fmt, codes_k)
     km = np.concatenate([np.concatenate([f16_bytes(Sk[16 * t:16 * t + 16].ravel()),
                                          f16_bytes(Zk[16 * t:16 * t + 16].ravel())]) for t in range(8)])
     vc = _pack_vc(fmt, codes_v)
@@ -166,8 +186,14 @@ def pack_nvfp4_block(kq: dict, vq: dict, used: int) -> np.ndarray:
     codes_v = np.zeros((BLOCK, D), np.uint8); codes_v[:used] = vq["codes"]
     sk = np.zeros((BLOCK, 8), np.uint8); sk[:used] = kq["scale"]
     sv = np.zeros((BLOCK, 8), np.uint8); sv[:used] = vq["scale"]
-    kc = pack_fields(codes_k, 4).ravel()
-    ks = sk.ravel()
+    kc = _pack_kc("nvfp4", codes_k)
+    ks = np.zeros((4, 2, 64, 2), np.uint8)
+    for w in range(4):
+        for u in range(2):
+            for L in range(64):
+                g, c = L // 16, L % 16
+                ks[w, u, L] = sk[32 * w + 16 * u + c, 2 * g:2 * g + 2]
+    ks = ks.ravel()
     vc = _pack_vc("nvfp4", codes_v)
     vs = np.zeros((4, 4, 8, 8), np.uint8)                                   # [w][g][k][e]
     e = np.arange(8)

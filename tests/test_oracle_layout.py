@@ -75,11 +75,16 @@ def test_v_lane_fields_cover_every_slot_and_dim_once(fmt):
         assert sorted(e[k == kk]) == list(range(8))
 
 
-def test_k_field_dims_is_a_permutation_keeping_quarters_in_one_group_each_half():
-    d = layout.k_field_dims()
+@pytest.mark.parametrize("fmt", ["int2", "int4", "int8", "nvfp4"])
+def test_k_lane_dims_cover_every_dim_once_per_slot(fmt):
+    """The four lane quarters of a slot hold all 128 dims once; in affine formats each
+    16-field half of a lane lies in one 64-dim group."""
+    d = np.concatenate([layout.k_lane_dims(fmt, g) for g in range(4)])
     assert sorted(d) == list(range(128))
-    f = np.arange(128)
-    assert np.all(d // 64 == (f // 16) % 2)          # each 16-field half lies in one 64-dim group
+    if fmt != "nvfp4":
+        f = np.arange(32)
+        for g in range(4):
+            assert np.all(layout.k_lane_dims(fmt, g) // 64 == f // 16)
 
 
 def test_every_bit_of_a_block_is_reachable_once():
