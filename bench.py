@@ -285,7 +285,7 @@ def main():
         "prefill_s": round(t_prefill, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(args.workload),
-                     "kernel": "kvq_decode_attn (all launches of one call)",
+                     "kernel": "decode_kernel (one launch per kvq_decode_attn call)",
                      "launch_us": round(float(dec_ms.mean()) * 1e3, 2),
                      "bytes_per_launch": round(float(nbytes.mean()))},
     }
