@@ -25,10 +25,10 @@
 //  PV    O^T += V^T P: A = V codes (16 dims x 32 slots), B = P (32 slots x 16 heads); lane
 //        (c, g) feeds dim c of the tile and the 8 slots whose logits it holds, and accumulates
 //        O^T[dims 4g..4g+3][head c].
-// Affine: the MFMA takes exact code integers as fp16 (some scaled by 16).  K: codes c,
-// logit = S0 (dot0 - Z0 qsum0) + S1 (dot1 - Z1 qsum1) per 64-dim group.  V: codes c - C with
-// C = 2^(n-1); the scale S of each (slot, group) is folded into P and the zero point enters as
-// o -= sum_t P'_t (Z_t - C).
+// Affine: the MFMA takes the raw codes as fp16 subnormals (c * 2^-24, some scaled by 16).  K:
+// logit = S0 (dot0 - Z0 qsum0) + S1 (dot1 - Z1 qsum1) per 64-dim group, in units of 2^-24.  V:
+// the scale S of each (slot, group) is folded into P and the zero point enters as
+// o = 2^24 o - sum_t P'_t Z_t at the end of the work item.
 // NVFP4: E2M1 codes and E4M3 scales are converted by the hardware to fp16 and multiplied
 // (exact: at most 6 significant bits, magnitude in [2^-10, 2688]).
 #include "kvq_internal.h"
@@ -83,37 +83,26 @@ __device__ __forceinline__ uint32_t field_pair(uint32_t x, uint32_t mask) {
 }
 
 // ---------------------------------------------------------------- operand unpack per format
-// The K operand takes the codes c (16c on scaled positions) as exact fp16 integers; the V
-// operand takes c - C (C = 2^(n-1)), so that the PV sums stay centred and the zero-point term
-// sum P'(Z - C) stays small over long contexts (no cancellation between two large sums).
-// (Leaving the 1024 bias of the magic constant in the K operand and starting the MFMA
-// accumulator at -1024 sum(B) would save the subtraction, but the accumulation error against
-// the bias exceeds the attention tolerance for INT2 codes.)
-template <bool CENTER, int C1>
-__device__ __forceinline__ uint32_t code_pair(uint32_t x, uint32_t mask) {
-  return field_pair<CENTER ? C1 : 0>(x, mask);
-}
-// INT4 word -> [n0, n4, 16n1, 16n5, n2, n6, 16n3, 16n7] (n_v = nibble v; minus 8 / 128 if CENTER)
-template <bool CENTER>
+// Affine codes enter the MFMA as fp16 subnormals: the 16-bit halves of (x & mask) are the raw
+// codes c, i.e. the values c * 2^-24 (16 c * 2^-24 for a mask shifted by 4 bits), which the
+// matrix core multiplies exactly.  One v_and per pair; the factor 2^24 is carried by the
+// softmax scale and removed from the PV sums once per work item.
+// INT4 word -> [n0, n4, 16n1, 16n5, n2, n6, 16n3, 16n7] * 2^-24 (n_v = nibble v)
 __device__ __forceinline__ half8_t unpack_int4(uint32_t x) {
   const uint32_t y = x >> 8;
-  return h8(code_pair<CENTER, 8>(x, 0x000F000Fu), code_pair<CENTER, 128>(x, 0x00F000F0u), code_pair<CENTER, 8>(y, 0x000F000Fu),
-            code_pair<CENTER, 128>(y, 0x00F000F0u));
+  return h8(x & 0x000F000Fu, x & 0x00F000F0u, y & 0x000F000Fu, y & 0x00F000F0u);
 }
-// INT2 word -> lo = crumbs [0,8,1,9,2,10,3,11], hi = [4,12,5,13,6,14,7,15] (minus 2 if CENTER)
-template <bool CENTER>
+// INT2 word -> lo = crumbs [0,8,1,9,2,10,3,11], hi = [4,12,5,13,6,14,7,15]
 __device__ __forceinline__ void unpack_int2(uint32_t x, half8_t &lo, half8_t &hi) {
-  lo = h8(code_pair<CENTER, 2>(x, 0x00030003u), code_pair<CENTER, 2>(x >> 2, 0x00030003u),
-          code_pair<CENTER, 2>(x >> 4, 0x00030003u), code_pair<CENTER, 2>(x >> 6, 0x00030003u));
-  hi = h8(code_pair<CENTER, 2>(x >> 8, 0x00030003u), code_pair<CENTER, 2>(x >> 10, 0x00030003u),
-          code_pair<CENTER, 2>(x >> 12, 0x00030003u), code_pair<CENTER, 2>(x >> 14, 0x00030003u));
+  lo = h8(x & 0x00030003u, (x >> 2) & 0x00030003u, (x >> 4) & 0x00030003u, (x >> 6) & 0x00030003u);
+  hi = h8((x >> 8) & 0x00030003u, (x >> 10) & 0x00030003u, (x >> 12) & 0x00030003u, (x >> 14) & 0x00030003u);
 }
-// INT8 word pair -> [w0.b0, w0.b2, w0.b1, w0.b3, w1.b0, w1.b2, w1.b1, w1.b3] (minus 128 if CENTER)
-template <bool CENTER>
+// INT8 word pair -> [w0.b0, w0.b2, w0.b1, w0.b3, w1.b0, w1.b2, w1.b1, w1.b3]
 __device__ __forceinline__ half8_t unpack_int8(uint32_t w0, uint32_t w1) {
-  return h8(code_pair<CENTER, 128>(w0, 0x00FF00FFu), code_pair<CENTER, 128>(w0 >> 8, 0x00FF00FFu),
-            code_pair<CENTER, 128>(w1, 0x00FF00FFu), code_pair<CENTER, 128>(w1 >> 8, 0x00FF00FFu));
+  return h8(w0 & 0x00FF00FFu, (w0 >> 8) & 0x00FF00FFu, w1 & 0x00FF00FFu, (w1 >> 8) & 0x00FF00FFu);
 }
+constexpr float kSub = 5.9604644775390625e-08f;   // 2^-24, the value of fp16 bit pattern 1
+constexpr float kInvSub = 16777216.0f;            // 2^24
 // NVFP4 word (8 E2M1 codes, nibble order) times per-pair fp16 scales
 __device__ __forceinline__ half8_t unpack_fp4(uint32_t x, uint32_t s01, uint32_t s23, uint32_t s45, uint32_t s67) {
   const uint32_t a = as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 0));
@@ -198,9 +187,10 @@ __device__ __forceinline__ void load_q(const uint16_t *qrow, bool valid, int g, 
       if (j < 2) qs0 += eff; else qs1 += eff;
     }
   }
-  // group sums over the four lane quarters (lanes c, c+16, c+32, c+48 hold one head)
-  qs0 = quad_sum(qs0);
-  qs1 = quad_sum(qs1);
+  // group sums over the four lane quarters (lanes c, c+16, c+32, c+48 hold one head), in the
+  // 2^-24 units of the subnormal code operands
+  qs0 = quad_sum(qs0) * kSub;
+  qs1 = quad_sum(qs1) * kSub;
 }
 
 // ---------------------------------------------------------------- LDS DMA
@@ -318,21 +308,21 @@ __device__ __forceinline__ void affine_step(const uint8_t *blk, int w, int g, in
   half8_t va[8];
   if constexpr (NB == 4) {
     const uint4 x0 = *(const uint4 *)vc, x1 = *(const uint4 *)(vc + 1024);
-    va[0] = unpack_int4<true>(x0.x); va[1] = unpack_int4<true>(x0.y);
-    va[2] = unpack_int4<true>(x0.z); va[3] = unpack_int4<true>(x0.w);
-    va[4] = unpack_int4<true>(x1.x); va[5] = unpack_int4<true>(x1.y);
-    va[6] = unpack_int4<true>(x1.z); va[7] = unpack_int4<true>(x1.w);
+    va[0] = unpack_int4(x0.x); va[1] = unpack_int4(x0.y);
+    va[2] = unpack_int4(x0.z); va[3] = unpack_int4(x0.w);
+    va[4] = unpack_int4(x1.x); va[5] = unpack_int4(x1.y);
+    va[6] = unpack_int4(x1.z); va[7] = unpack_int4(x1.w);
   } else if constexpr (NB == 2) {
     const uint4 x = *(const uint4 *)vc;
     const uint32_t ws[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) unpack_int2<true>(ws[u], va[2 * u], va[2 * u + 1]);
+    for (int u = 0; u < 4; ++u) unpack_int2(ws[u], va[2 * u], va[2 * u + 1]);
   } else {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const uint4 x = *(const uint4 *)(vc + r * 1024);
-      va[2 * r] = unpack_int8<true>(x.x, x.y);
-      va[2 * r + 1] = unpack_int8<true>(x.z, x.w);
+      va[2 * r] = unpack_int8(x.x, x.y);
+      va[2 * r + 1] = unpack_int8(x.z, x.w);
     }
   }
   uint4 vm0[2], vz[2];
@@ -351,25 +341,25 @@ __device__ __forceinline__ void affine_step(const uint8_t *blk, int w, int g, in
     float4_t a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0;
     if constexpr (NB == 4) {
       const uint4 x = *(const uint4 *)row;
-      a0 = mfma(unpack_int4<false>(x.x), qb[0], a0);
-      a0 = mfma(unpack_int4<false>(x.y), qb[1], a0);
-      a1 = mfma(unpack_int4<false>(x.z), qb[2], a1);
-      a1 = mfma(unpack_int4<false>(x.w), qb[3], a1);
+      a0 = mfma(unpack_int4(x.x), qb[0], a0);
+      a0 = mfma(unpack_int4(x.y), qb[1], a0);
+      a1 = mfma(unpack_int4(x.z), qb[2], a1);
+      a1 = mfma(unpack_int4(x.w), qb[3], a1);
     } else if constexpr (NB == 2) {
       const uint2 x = *(const uint2 *)row;
       half8_t l0, h0, l1, h1;
-      unpack_int2<false>(x.x, l0, h0);
-      unpack_int2<false>(x.y, l1, h1);
+      unpack_int2(x.x, l0, h0);
+      unpack_int2(x.y, l1, h1);
       a0 = mfma(l0, qb[0], a0);
       a0 = mfma(h0, qb[1], a0);
       a1 = mfma(l1, qb[2], a1);
       a1 = mfma(h1, qb[3], a1);
     } else {
       const uint4 x = *(const uint4 *)row, y = *(const uint4 *)(row + 1024);
-      a0 = mfma(unpack_int8<false>(x.x, x.y), qb[0], a0);
-      a0 = mfma(unpack_int8<false>(x.z, x.w), qb[1], a0);
-      a1 = mfma(unpack_int8<false>(y.x, y.y), qb[2], a1);
-      a1 = mfma(unpack_int8<false>(y.z, y.w), qb[3], a1);
+      a0 = mfma(unpack_int8(x.x, x.y), qb[0], a0);
+      a0 = mfma(unpack_int8(x.z, x.w), qb[1], a0);
+      a1 = mfma(unpack_int8(y.x, y.y), qb[2], a1);
+      a1 = mfma(unpack_int8(y.z, y.w), qb[3], a1);
     }
     const uint4 ks = *(const uint4 *)(blk + kKm + tau * 128 + 16 * g);        // (S0, S1) of slots 4g+i
     const uint4 kz = *(const uint4 *)(blk + kKm + tau * 128 + 64 + 16 * g);   // (Z0, Z1)
@@ -387,11 +377,9 @@ __device__ __forceinline__ void affine_step(const uint8_t *blk, int w, int g, in
   constexpr unsigned kScaled = NB == 4 ? 0xCCu : 0u;   // INT4: positions i = 2, 3 of both tiles
   softmax_step(st, s, p, valid_head, kScaled, sl2);
 
-  // P' = p * S per group (one fp16 rounding), and the zero-point sums sum P' (Z - C)
+  // P' = p * S per group (one fp16 rounding), and the zero-point sums sum P' Z
   half8_t pb[2];
   {
-    constexpr _Float16 kC = (_Float16)(1 << (NB - 1));
-    const half2_t cc = {kC, kC};
     uint32_t pw[2][4];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -401,7 +389,7 @@ __device__ __forceinline__ void affine_step(const uint8_t *blk, int w, int g, in
       const uint32_t b01 = pk(pp[0] * lo_f(sm.z), pp[1] * hi_f(sm.z)), b23 = pk(pp[2] * lo_f(sm.w), pp[3] * hi_f(sm.w));
       pw[0][2 * tt + 0] = a01; pw[0][2 * tt + 1] = a23;
       pw[1][2 * tt + 0] = b01; pw[1][2 * tt + 1] = b23;
-      const half2_t z0 = as_h2(zz.x) - cc, z1 = as_h2(zz.y) - cc, z2 = as_h2(zz.z) - cc, z3 = as_h2(zz.w) - cc;
+      const half2_t z0 = as_h2(zz.x), z1 = as_h2(zz.y), z2 = as_h2(zz.z), z3 = as_h2(zz.w);
       if constexpr (NB == 4) {
         st.z1 = __builtin_amdgcn_fdot2(as_h2(a01), z0, st.z1, false);
         st.z16 = __builtin_amdgcn_fdot2(as_h2(a23), z1, st.z16, false);
@@ -584,8 +572,8 @@ __device__ __forceinline__ void load_q2(const uint16_t *qrow, bool valid, int g,
       if (j < 4) qs0 += eff; else qs1 += eff;
     }
   }
-  q.qs0 = quad_sum(qs0);
-  q.qs1 = quad_sum(qs1);
+  q.qs0 = quad_sum(qs0) * kSub;
+  q.qs1 = quad_sum(qs1) * kSub;
 }
 
 // Running max / probabilities for 4 logits (slots i of the lane's subtile); scaled_mask bit i
@@ -614,25 +602,26 @@ __device__ __forceinline__ void softmax_step2(State &st, const float (&s)[4], fl
   st.l += ls;
 }
 
-// INT4 V operand of subtile s0 from word k: tokens i = 0..3 as [c0, c1, 16 c2, 16 c3] - centre
+// V operand of subtile s0 from the lane's words (tokens i = 0..3), raw codes as subnormals
+// (INT4: [c0, c1, 16 c2, 16 c3])
 template <int NB>
 __device__ __forceinline__ half4_t v_operand2(const uint32_t *vw, int k, int s0);
 
 template <>
 __device__ __forceinline__ half4_t v_operand2<4>(const uint32_t *vw, int k, int s0) {
   const uint32_t x = s0 ? vw[k] >> 8 : vw[k];
-  return h4(field_pair<8>(x, 0x000F000Fu), field_pair<128>(x, 0x00F000F0u));
+  return h4(x & 0x000F000Fu, x & 0x00F000F0u);
 }
 template <>
 __device__ __forceinline__ half4_t v_operand2<2>(const uint32_t *vw, int k, int s0) {
   // word k >> 1 holds tiles 2(k>>1) + a; pairs (crumb s, crumb s+8), s = 4a + 2 s0 + {0, 1}
   const uint32_t x = vw[k >> 1] >> (2 * (4 * (k & 1) + 2 * s0));
-  return h4(field_pair<2>(x, 0x00030003u), field_pair<2>(x >> 2, 0x00030003u));
+  return h4(x & 0x00030003u, (x >> 2) & 0x00030003u);
 }
 template <>
 __device__ __forceinline__ half4_t v_operand2<8>(const uint32_t *vw, int k, int s0) {
   const uint32_t x = vw[2 * k + s0];
-  return h4(field_pair<128>(x, 0x00FF00FFu), field_pair<128>(x >> 8, 0x00FF00FFu));
+  return h4(x & 0x00FF00FFu, (x >> 8) & 0x00FF00FFu);
 }
 
 template <int NB, bool TAIL>
@@ -666,26 +655,26 @@ __device__ __forceinline__ void affine_step2(const uint8_t *blk, int w, int g, i
   if constexpr (NB == 4) {
     const uint4 x0 = *(const uint4 *)(blk + (tau_a * 64 + 16 * (2 * qq) + c) * 16);
     const uint4 x1 = *(const uint4 *)(blk + (tau_a * 64 + 16 * (2 * qq + 1) + c) * 16);
-    a0 = mfma(unpack_int4<false>(x0.x), q.qb[0], a0);
-    a0 = mfma(unpack_int4<false>(x0.y), q.qb[1], a0);
-    a0 = mfma(unpack_int4<false>(x1.x), q.qb[2], a0);
-    a0 = mfma(unpack_int4<false>(x1.y), q.qb[3], a0);
-    a1 = mfma(unpack_int4<false>(x0.z), q.qb[4], a1);
-    a1 = mfma(unpack_int4<false>(x0.w), q.qb[5], a1);
-    a1 = mfma(unpack_int4<false>(x1.z), q.qb[6], a1);
-    a1 = mfma(unpack_int4<false>(x1.w), q.qb[7], a1);
+    a0 = mfma(unpack_int4(x0.x), q.qb[0], a0);
+    a0 = mfma(unpack_int4(x0.y), q.qb[1], a0);
+    a0 = mfma(unpack_int4(x1.x), q.qb[2], a0);
+    a0 = mfma(unpack_int4(x1.y), q.qb[3], a0);
+    a1 = mfma(unpack_int4(x0.z), q.qb[4], a1);
+    a1 = mfma(unpack_int4(x0.w), q.qb[5], a1);
+    a1 = mfma(unpack_int4(x1.z), q.qb[6], a1);
+    a1 = mfma(unpack_int4(x1.w), q.qb[7], a1);
   } else if constexpr (NB == 2) {
     const uint2 x0 = *(const uint2 *)(blk + (tau_a * 64 + 16 * (2 * qq) + c) * 8);
     const uint2 x1 = *(const uint2 *)(blk + (tau_a * 64 + 16 * (2 * qq + 1) + c) * 8);
     half8_t l0, h0, l1, h1;
-    unpack_int2<false>(x0.x, l0, h0);
-    unpack_int2<false>(x1.x, l1, h1);
+    unpack_int2(x0.x, l0, h0);
+    unpack_int2(x1.x, l1, h1);
     a0 = mfma(l0, q.qb[0], a0);
     a0 = mfma(h0, q.qb[1], a0);
     a0 = mfma(l1, q.qb[2], a0);
     a0 = mfma(h1, q.qb[3], a0);
-    unpack_int2<false>(x0.y, l0, h0);
-    unpack_int2<false>(x1.y, l1, h1);
+    unpack_int2(x0.y, l0, h0);
+    unpack_int2(x1.y, l1, h1);
     a1 = mfma(l0, q.qb[4], a1);
     a1 = mfma(h0, q.qb[5], a1);
     a1 = mfma(l1, q.qb[6], a1);
@@ -696,14 +685,14 @@ __device__ __forceinline__ void affine_step2(const uint8_t *blk, int w, int g, i
     const uint8_t *k1 = blk + ((tau_a * 2) * 64 + 16 * (2 * qq + 1) + c) * 16;
     const uint4 x0 = *(const uint4 *)k0, y0 = *(const uint4 *)(k0 + 1024);
     const uint4 x1 = *(const uint4 *)k1, y1 = *(const uint4 *)(k1 + 1024);
-    a0 = mfma(unpack_int8<false>(x0.x, x0.y), q.qb[0], a0);
-    a0 = mfma(unpack_int8<false>(x0.z, x0.w), q.qb[1], a0);
-    a0 = mfma(unpack_int8<false>(x1.x, x1.y), q.qb[2], a0);
-    a0 = mfma(unpack_int8<false>(x1.z, x1.w), q.qb[3], a0);
-    a1 = mfma(unpack_int8<false>(y0.x, y0.y), q.qb[4], a1);
-    a1 = mfma(unpack_int8<false>(y0.z, y0.w), q.qb[5], a1);
-    a1 = mfma(unpack_int8<false>(y1.x, y1.y), q.qb[6], a1);
-    a1 = mfma(unpack_int8<false>(y1.z, y1.w), q.qb[7], a1);
+    a0 = mfma(unpack_int8(x0.x, x0.y), q.qb[0], a0);
+    a0 = mfma(unpack_int8(x0.z, x0.w), q.qb[1], a0);
+    a0 = mfma(unpack_int8(x1.x, x1.y), q.qb[2], a0);
+    a0 = mfma(unpack_int8(x1.z, x1.w), q.qb[3], a0);
+    a1 = mfma(unpack_int8(y0.x, y0.y), q.qb[4], a1);
+    a1 = mfma(unpack_int8(y0.z, y0.w), q.qb[5], a1);
+    a1 = mfma(unpack_int8(y1.x, y1.y), q.qb[6], a1);
+    a1 = mfma(unpack_int8(y1.z, y1.w), q.qb[7], a1);
   }
   float s[4];
   const uint32_t sw[4] = {ks.x, ks.y, ks.z, ks.w}, zw[4] = {kz.x, kz.y, kz.z, kz.w};
@@ -719,21 +708,19 @@ __device__ __forceinline__ void affine_step2(const uint8_t *blk, int w, int g, i
   constexpr unsigned kScaled = NB == 4 ? 0xCu : 0u;   // INT4: positions i = 2, 3
   softmax_step2(st, s, p, valid_head, kScaled, sl2);
 
-  // P' = p * S per group (one fp16 rounding) and the zero-point sums sum P' (Z - C)
-  constexpr _Float16 kC = (_Float16)(1 << (NB - 1));
-  const half2_t cc = {kC, kC};
+  // P' = p * S per group (one fp16 rounding) and the zero-point sums sum P' Z
   const uint32_t a01 = pk(p[0] * lo_f(vm.x), p[1] * hi_f(vm.x)), a23 = pk(p[2] * lo_f(vm.y), p[3] * hi_f(vm.y));
   const uint32_t b01 = pk(p[0] * lo_f(vm.z), p[1] * hi_f(vm.z)), b23 = pk(p[2] * lo_f(vm.w), p[3] * hi_f(vm.w));
   if constexpr (NB == 4) {
-    st.z1 = __builtin_amdgcn_fdot2(as_h2(a01), as_h2(vz.x) - cc, st.z1, false);
-    st.z16 = __builtin_amdgcn_fdot2(as_h2(a23), as_h2(vz.y) - cc, st.z16, false);
-    st.z1b = __builtin_amdgcn_fdot2(as_h2(b01), as_h2(vz.z) - cc, st.z1b, false);
-    st.z16b = __builtin_amdgcn_fdot2(as_h2(b23), as_h2(vz.w) - cc, st.z16b, false);
+    st.z1 = __builtin_amdgcn_fdot2(as_h2(a01), as_h2(vz.x), st.z1, false);
+    st.z16 = __builtin_amdgcn_fdot2(as_h2(a23), as_h2(vz.y), st.z16, false);
+    st.z1b = __builtin_amdgcn_fdot2(as_h2(b01), as_h2(vz.z), st.z1b, false);
+    st.z16b = __builtin_amdgcn_fdot2(as_h2(b23), as_h2(vz.w), st.z16b, false);
   } else {
-    st.z1 = __builtin_amdgcn_fdot2(as_h2(a01), as_h2(vz.x) - cc, st.z1, false);
-    st.z1 = __builtin_amdgcn_fdot2(as_h2(a23), as_h2(vz.y) - cc, st.z1, false);
-    st.z1b = __builtin_amdgcn_fdot2(as_h2(b01), as_h2(vz.z) - cc, st.z1b, false);
-    st.z1b = __builtin_amdgcn_fdot2(as_h2(b23), as_h2(vz.w) - cc, st.z1b, false);
+    st.z1 = __builtin_amdgcn_fdot2(as_h2(a01), as_h2(vz.x), st.z1, false);
+    st.z1 = __builtin_amdgcn_fdot2(as_h2(a23), as_h2(vz.y), st.z1, false);
+    st.z1b = __builtin_amdgcn_fdot2(as_h2(b01), as_h2(vz.z), st.z1b, false);
+    st.z1b = __builtin_amdgcn_fdot2(as_h2(b23), as_h2(vz.w), st.z1b, false);
   }
   // PV as O^T += V^T P per subtile s0: A = V codes of s0, B = this lane's P' where its column
   // subtile is s0 (else zero); the accumulator rows are dims, its column the lane's head.
@@ -910,6 +897,9 @@ __device__ void stream_segment(const DecodeArgs &a, const DecodeSeg &sg, const I
     for (int j = w; j < ndma; j += kWaves) dma16(src + j * 1024, __builtin_amdgcn_readfirstlane(dst + j * 1024));
   };
   for (int i = 0; i < nbuf - 1 && i < n; ++i) issue(i);
+  // affine logits come out in units of 2^-24 (subnormal code operands)
+  constexpr bool kAff = FMT != kFmtNvfp4;
+  const float sl2 = kAff ? a.scale_log2 * kInvSub : a.scale_log2;
   // valid slots in the last block of the segment (128 when it is full)
   const int64_t nblk_seg = (sg.ntok + kBlock - 1) / kBlock;
   const int tail_valid = (int)(sg.ntok - (nblk_seg - 1) * kBlock);
@@ -927,42 +917,60 @@ __device__ void stream_segment(const DecodeArgs &a, const DecodeSeg &sg, const I
     const int nv = full ? kBlock : tail_valid;
     if constexpr (NSUB == 2) {
       if constexpr (FMT == kFmtNvfp4) {
-        if (full) nvfp4_step2<false>(blk, w, g, c, q2, a.scale_log2, valid_head, nv, st);
-        else nvfp4_step2<true>(blk, w, g, c, q2, a.scale_log2, valid_head, nv, st);
+        if (full) nvfp4_step2<false>(blk, w, g, c, q2, sl2, valid_head, nv, st);
+        else nvfp4_step2<true>(blk, w, g, c, q2, sl2, valid_head, nv, st);
       } else {
-        if (full) affine_step2<FMT, false>(blk, w, g, c, q2, a.scale_log2, valid_head, nv, st);
-        else affine_step2<FMT, true>(blk, w, g, c, q2, a.scale_log2, valid_head, nv, st);
+        if (full) affine_step2<FMT, false>(blk, w, g, c, q2, sl2, valid_head, nv, st);
+        else affine_step2<FMT, true>(blk, w, g, c, q2, sl2, valid_head, nv, st);
       }
     } else {
       if constexpr (FMT == kFmtNvfp4) {
-        if (full) nvfp4_step<false>(blk, w, g, c, q, a.scale_log2, valid_head, nv, st);
-        else nvfp4_step<true>(blk, w, g, c, q, a.scale_log2, valid_head, nv, st);
+        if (full) nvfp4_step<false>(blk, w, g, c, q, sl2, valid_head, nv, st);
+        else nvfp4_step<true>(blk, w, g, c, q, sl2, valid_head, nv, st);
       } else {
-        if (full) affine_step<FMT, false>(blk, w, g, c, q, a.scale_log2, valid_head, nv, st);
-        else affine_step<FMT, true>(blk, w, g, c, q, a.scale_log2, valid_head, nv, st);
+        if (full) affine_step<FMT, false>(blk, w, g, c, q, sl2, valid_head, nv, st);
+        else affine_step<FMT, true>(blk, w, g, c, q, sl2, valid_head, nv, st);
       }
     }
   }
   barrier();   // every wave is done with the ring before it is reused
+  if constexpr (kAff) {
+    // Back to natural units: m * 2^24, and o = 2^24 o - sum P' Z of the group of each dim (for
+    // paired subtiles the head's total goes to its subtile-0 column only; the two columns are
+    // summed later).
+    if (st.m != kNegInf) st.m *= kInvSub;
+    float zg0, zg1;
+    bool take = true;
+    if constexpr (NSUB == 2) {
+      zg0 = head_sum2(st.z1 + 16.0f * st.z16);
+      zg1 = head_sum2(st.z1b + 16.0f * st.z16b);
+      take = (c >> 3) == 0;
+    } else {
+      zg0 = quad_sum(st.z1 + 16.0f * st.z16);
+      zg1 = quad_sum(st.z1b + 16.0f * st.z16b);
+    }
+    if (!take) zg0 = zg1 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) st.o[k] = st.o[k] * kInvSub - (k < 4 ? zg0 : zg1);
+    st.z1 = st.z16 = st.z1b = st.z16b = 0.0f;
+  }
 }
 
 // Per-wave state -> LDS rows for the workgroup merge: m[16], l[16] (log2 units) and
-// o[16][128], heads in natural order.  Folds the zero-point sums sum P'(Z - C) into o.
+// o[16][128], heads in natural order.
 template <int NSUB>
 __device__ __forceinline__ void state_to_lds(State &st, int w, int g, int c, float sl2, float *wm, float *wl, float *wo) {
   if constexpr (NSUB == 1) {
-    const float zg0 = quad_sum(st.z1 + 16.0f * st.z16), zg1 = quad_sum(st.z1b + 16.0f * st.z16b);
     const float l = quad_sum(st.l);
     if (g == 0) {
       wm[w * 16 + c] = st.m * sl2;
       wl[w * 16 + c] = l;
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) *(float4_t *)(wo + ((w * 16 + c) * kHeadDim + 16 * k + 4 * g)) = st.o[k] - (k < 4 ? zg0 : zg1);
+    for (int k = 0; k < 8; ++k) *(float4_t *)(wo + ((w * 16 + c) * kHeadDim + 16 * k + 4 * g)) = st.o[k];
   } else {
     // lane (c, g): column (subtile c >> 3, head c & 7), accumulator rows dims 16k + 4g + i;
     // the subtile-1 column of a head is lane c ^ 8
-    const float zg0 = head_sum2(st.z1 + 16.0f * st.z16), zg1 = head_sum2(st.z1b + 16.0f * st.z16b);
     const float l = head_sum2(st.l);
     if (g == 0 && c < 8) {
       wm[w * 16 + c] = st.m * sl2;
@@ -975,7 +983,7 @@ __device__ __forceinline__ void state_to_lds(State &st, int w, int g, int c, flo
       o[1] += __shfl_xor(o[1], 8);
       o[2] += __shfl_xor(o[2], 8);
       o[3] += __shfl_xor(o[3], 8);
-      if (c < 8) *(float4_t *)(wo + ((w * 16 + c) * kHeadDim + 16 * k + 4 * g)) = o - (k < 4 ? zg0 : zg1);
+      if (c < 8) *(float4_t *)(wo + ((w * 16 + c) * kHeadDim + 16 * k + 4 * g)) = o;
     }
   }
 }
