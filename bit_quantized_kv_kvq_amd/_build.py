@@ -14,6 +14,9 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # a fetch-add whose result is read much later must not be rewritten into a wave-wide
+    # add whose result is broadcast (and so waited for) right away
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wno-unused-result",
 ]
 

@@ -222,7 +222,10 @@ int run_plan(kvq_cache *c, int layer, const Plan &p, const void *k, const void *
 
 std::atomic<uint32_t> g_epoch{0};
 
-size_t counters_bytes(const kvq_cache *c) { return align_up((size_t)c->cfg.batch * c->cfg.num_kv_heads * sizeof(uint64_t)); }
+// Per (b, h): one arrival counter and one chunk cursor per tier.
+size_t counters_bytes(const kvq_cache *c) {
+  return align_up((size_t)c->cfg.batch * c->cfg.num_kv_heads * (1 + kMaxSegs) * sizeof(uint64_t));
+}
 
 size_t workspace_bound(const kvq_cache *c, int32_t num_q_heads) {
   const size_t bh = (size_t)c->cfg.batch * c->cfg.num_kv_heads;
@@ -230,9 +233,10 @@ size_t workspace_bound(const kvq_cache *c, int32_t num_q_heads) {
   return counters_bytes(c) + bh * kMaxParts * G * kPartialStride * sizeof(float);
 }
 
-// Split every tier of the layer into work items of whole blocks, sized so that all work
-// items of the call fill the GPU about once (two workgroups per CU), in proportion to bytes.
-int plan_decode(const kvq_cache *c, int layer, DecodeArgs &a) {
+// Give every tier of the layer work items in proportion to its bytes, so that all work items
+// of the call fill the GPU about once (two workgroups per CU), and cut it into chunks small
+// enough (about 32 per item) that the items of a (b, h) even out their finishing times.
+int plan_decode(const kvq_cache *c, int layer, DecodeArgs &a, uint64_t *cursors) {
   const auto &cfg = c->cfg;
   const LayerState &st = c->layers[layer];
   const int64_t nbh = (int64_t)cfg.batch * cfg.num_kv_heads;
@@ -251,14 +255,22 @@ int plan_decode(const kvq_cache *c, int layer, DecodeArgs &a) {
   for (int i = 0; i < nt; ++i) {
     const T &t = tiers[i];
     int64_t items = std::max<int64_t>(1, (int64_t)((double)target * t.nblk * block_bytes(t.fmt) / bytes + 0.5));
-    items = std::min<int64_t>(items, t.nblk);
-    int64_t bpi = ceil_div(t.nblk, items);
-    const int64_t cap = kMaxParts / std::max(1, nt);
-    if (ceil_div(t.nblk, bpi) > cap) bpi = ceil_div(t.nblk, cap);
-    items = ceil_div(t.nblk, bpi);
+    items = std::min<int64_t>(items, kMaxParts / std::max(1, nt));
+    const int64_t depth = decode_ring_depth(block_bytes(t.fmt));
+    int64_t chunk = std::max<int64_t>(depth, ceil_div(t.nblk, items * 32));
+    int64_t nch = ceil_div(t.nblk, chunk);
+    int64_t fixed = 2;
+    if (nch < 4 * items) {
+      // too little to share out: single blocks, dealt round-robin
+      chunk = 1;
+      nch = t.nblk;
+      items = std::min<int64_t>(items, nch);
+      fixed = ceil_div(nch, items);
+    }
     DecodeSeg &s = a.seg[a.nseg++];
     s.base = t.base; s.bh_stride = t.stride; s.ntok = t.ntok; s.fmt = t.fmt;
-    s.blocks_per_item = (int)bpi; s.items = (int)items; s.part0 = parts;
+    s.chunk = (int)chunk; s.nchunks = (int)nch; s.items = (int)items; s.fixed = (int)fixed; s.part0 = parts;
+    s.cursors = cursors + (size_t)i * nbh;
     parts += (int)items;
   }
   a.items_total = std::max(1, parts);
@@ -378,7 +390,7 @@ int kvq_decode_attn(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_he
       c->num_cus = 256;
   }
   DecodeArgs a{};
-  const int num_wg = plan_decode(c, layer, a);
+  const int num_wg = plan_decode(c, layer, a, (uint64_t *)workspace + (size_t)cfg.batch * cfg.num_kv_heads);
   a.q = (const uint16_t *)q;
   a.out = out;
   a.out_fp32 = out_fp32 ? 1 : 0;

@@ -231,7 +231,11 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
     case 17: asm volatile("s_waitcnt vmcnt(17)" ::: "memory"); break;
     case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
     case 19: asm volatile("s_waitcnt vmcnt(19)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
+    case 20: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
+    case 21: asm volatile("s_waitcnt vmcnt(21)" ::: "memory"); break;
+    case 22: asm volatile("s_waitcnt vmcnt(22)" ::: "memory"); break;
+    case 23: asm volatile("s_waitcnt vmcnt(23)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;   // never weaker than asked
   }
 }
 
@@ -833,37 +837,75 @@ __device__ __forceinline__ void residual_step2(const uint8_t *res, int R, int r,
   }
 }
 
+// ---------------------------------------------------------------- call-tagged counters
+// A counter in the caller's workspace is a 64-bit word (epoch << 32 | count).  A call works
+// only with words tagged with its own epoch; a word still tagged with an older one is
+// replaced, by compare-and-swap, with a fresh count of this call.  Adds that land on an old
+// word are void (their issuer sees the old tag) and are made again.  All accesses are
+// agent-scope atomics, so workgroups on different XCDs see one order of them.
+__device__ __forceinline__ uint32_t tag_of(uint64_t v) { return (uint32_t)(v >> 32); }
+
+// Tag the word with this call's epoch and a zero count, unless this call has done so already.
+__device__ __forceinline__ void counter_open(uint64_t *w, uint32_t epoch) {
+  uint64_t cur = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  while (tag_of(cur) != epoch)
+    if (__hip_atomic_compare_exchange_strong(w, &cur, (uint64_t)epoch << 32, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      break;
+}
+
+// The count before this call's add, after an add that came back with an older tag: open the
+// word with this add counted (count 0 before it), or add again once another opener has.
+// Each pass either succeeds or finds the word changed by one of the finitely many other
+// accesses of the call.
+__device__ __forceinline__ uint32_t counter_add_slow(uint64_t *w, uint32_t epoch) {
+  uint64_t cur = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {
+    if (tag_of(cur) == epoch)
+      return (uint32_t)__hip_atomic_fetch_add(w, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__hip_atomic_compare_exchange_strong(w, &cur, ((uint64_t)epoch << 32) | 1u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return 0;
+  }
+}
+
+// The count before an add whose returned word is `old`.
+__device__ __forceinline__ uint32_t counter_result(uint64_t *w, uint32_t epoch, uint64_t old) {
+  return tag_of(old) == epoch ? (uint32_t)old : counter_add_slow(w, epoch);
+}
+
 // ---------------------------------------------------------------- the kernel
 struct Item {
   int bh, part, seg;          // seg = -1: residual only
-  int64_t blk_lo, blk_hi;     // blocks of the segment
+  int j;                      // index of the item among its segment's items
   bool has_res;
 };
 
+// Part p of every (b, h) comes in the p-th run of B*H workgroups, so that each (b, h) has
+// items among the first and among the later residents of the CUs (the older wave has the
+// issue priority), and the (b, h) order turns by one per run, so that round-robin dispatch
+// puts the items of a (b, h) on different XCDs.  The items of a (b, h) share its chunks and
+// so even out these speed differences.
 __device__ __forceinline__ Item decode_item(const DecodeArgs &a, int wg) {
   const int nbh = a.B * a.H;
   Item it;
-  it.bh = wg % nbh;
-  it.part = a.items_total - 1 - wg / nbh;      // the residual-carrying last part starts first
+  it.part = wg / nbh;
+  it.bh = (wg + it.part) % nbh;
   it.seg = -1;
-  it.blk_lo = it.blk_hi = 0;
+  it.j = 0;
   for (int s = 0; s < a.nseg; ++s) {
     const DecodeSeg &sg = a.seg[s];
     if (it.part >= sg.part0 && it.part < sg.part0 + sg.items) {
       it.seg = s;
-      const int64_t nblk = (sg.ntok + kBlock - 1) / kBlock;
-      it.blk_lo = (int64_t)(it.part - sg.part0) * sg.blocks_per_item;
-      it.blk_hi = min(nblk, it.blk_lo + sg.blocks_per_item);
+      it.j = it.part - sg.part0;
     }
   }
-  it.has_res = a.res_ntok > 0 && it.part == a.items_total - 1;
+  it.has_res = a.res_ntok > 0 && it.part == it.bh % a.items_total;
   return it;
 }
 
 __device__ __forceinline__ int block_bytes_of(int fmt) { return (int)block_bytes(fmt); }
 
-// LDS ring depth: four blocks (three in flight) when two workgroups still fit in a CU.
-__host__ __device__ __forceinline__ int ring_depth(int bb) { return bb <= 18432 ? 4 : 3; }
 
 // Query row of the head a lane's column belongs to (a valid row even for padding columns).
 template <int NSUB>
@@ -873,47 +915,116 @@ __device__ __forceinline__ const uint16_t *q_row(const DecodeArgs &a, int bh, in
   return a.q + ((int64_t)b * a.H * a.G + (int64_t)h * a.G + hc) * kHeadDim;
 }
 
+// The fp16 residual of the item's (b, h), in natural units.
+template <int NSUB>
+__device__ __forceinline__ void residual_part(const DecodeArgs &a, const Item &it, int w, int g, int c, bool valid_head,
+                                              State &st) {
+  const uint16_t *qrow = q_row<NSUB>(a, it.bh, c, valid_head);
+  const uint8_t *res = a.res_base + (int64_t)it.bh * a.res_bh_stride;
+  const int nsteps = (a.res_ntok + 31) / 32;
+  if constexpr (NSUB == 2) {
+    QOp2 q;
+    load_q2<kFmtFp16>(qrow, valid_head, g, c, q);
+    for (int u = w; u < nsteps; u += kWaves) residual_step2(res, a.res_len, a.res_ntok, u, g, c, q, a.scale_log2, valid_head, st);
+  } else {
+    QOp q;
+    load_q<kFmtFp16>(qrow, valid_head, g, q.qb, q.qs0, q.qs1);
+    for (int u = w; u < nsteps; u += kWaves) residual_step(res, a.res_len, a.res_ntok, u, g, c, q, a.scale_log2, valid_head, st);
+  }
+}
+
 template <int FMT, int NSUB>
-__device__ void stream_segment(const DecodeArgs &a, const DecodeSeg &sg, const Item &it, uint8_t *smem, int w, int g, int c,
-                               bool valid_head, State &st) {
+__device__ void stream_segment(const DecodeArgs &a, const DecodeSeg &sg, const Item &it, uint8_t *smem, int *s_chunk, int w,
+                               int g, int c, bool valid_head, State &st) {
   const int lane = 16 * g + c;
   const int bb = block_bytes_of(FMT);
   const int ndma = bb / 1024;                                 // 1 KB per wave instruction
-  const int mine = (ndma - w + kWaves - 1) / kWaves;          // instructions this wave issues per block
+  // Waves 0..2 load the blocks; wave 3 loads none and hands out the chunks, so that waiting
+  // for its cursor atomic never waits for block loads (vmcnt counts both).
+  constexpr int kDmaWaves = kWaves - 1;
+  const bool dispatcher = w == kDmaWaves;
+  const int mine = dispatcher ? 0 : (ndma - w + kDmaWaves - 1) / kDmaWaves;
+  uint64_t *cursor = sg.cursors + it.bh;
+  const int K = sg.chunk, nch = sg.nchunks, items = sg.items, fixed = sg.fixed, j = it.j;
+  const bool dyn = fixed * items < nch;                      // a cursor hands out the rest
+  const int64_t nblk = (sg.ntok + kBlock - 1) / kBlock;
+  const int r = (int)((int64_t)nch * K - nblk);               // chunk 0 is short by r blocks
+  // item 0 opens the cursor early, so that the other items' first fetch-adds find it open
+  if (dyn && j == 0 && dispatcher && lane == 0) counter_open(cursor, a.epoch);
+  const uint8_t *gbh = sg.base + (int64_t)it.bh * sg.bh_stride + lane * 16;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  const int nbuf = decode_ring_depth(bb);
+  const int tail_valid = (int)(sg.ntok - (nblk - 1) * kBlock);   // slots in the last block
+  // Positions p = 0, 1, ... of the item's block sequence: slot p / K holds chunk
+  // slot * items + j (fixed slots), then the chunks the cursor hands out; the block is
+  // chunk * K + p % K - r.  Item 0 starts at p = r, inside the short chunk 0.
+  const int p0 = j == 0 ? r : 0;
+  int iss_ch = j;            // chunk of the slot being issued
+  int cons_ch = j;           // chunk of the slot being consumed
+  int iss_end = p0;          // next position to issue
+  bool iss_done = false;
+  uint64_t grab = 0;         // dispatcher lane 0: cursor value before its last fetch-add
+  auto issue_next = [&]() {
+    const int qp = iss_end;
+    const int o = qp % K;
+    if (o == 0 && qp > 0) {
+      const int slot = qp / K;
+      iss_ch = (!dyn || slot < fixed) ? slot * items + j : __builtin_amdgcn_readfirstlane(*s_chunk);
+      if (iss_ch >= nch) {
+        iss_done = true;
+        return;
+      }
+      // ask for the chunk of the next slot when the cursor hands it out
+      if (dyn && slot + 1 >= fixed && dispatcher && lane == 0)
+        grab = __hip_atomic_fetch_add(cursor, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (!dispatcher) {
+      const uint8_t *src = gbh + ((int64_t)iss_ch * K + o - r) * bb;
+      const uint32_t dst = lds0 + (uint32_t)(((qp - p0) % nbuf) * bb);
+      for (int jj = w; jj < ndma; jj += kDmaWaves) dma16(src + jj * 1024, __builtin_amdgcn_readfirstlane(dst + jj * 1024));
+    }
+    iss_end = __builtin_amdgcn_readfirstlane(qp + 1);   // uniform: keeps the waits scalar
+  };
+  for (int t = 0; t < nbuf - 1 && !iss_done; ++t) issue_next();
+
+  // while the first blocks load: the residual (natural units), then the query operand
+  if (it.has_res) residual_part<NSUB>(a, it, w, g, c, valid_head, st);
   const uint16_t *qrow = q_row<NSUB>(a, it.bh, c, valid_head);
   QOp q;
   QOp2 q2;
   if constexpr (NSUB == 2) load_q2<FMT>(qrow, valid_head, g, c, q2);
   else load_q<FMT>(qrow, valid_head, g, q.qb, q.qs0, q.qs1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-  const uint8_t *gbase = sg.base + (int64_t)it.bh * sg.bh_stride + it.blk_lo * (int64_t)bb + lane * 16;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  const int nbuf = ring_depth(bb);
-  const int n = (int)(it.blk_hi - it.blk_lo);
-  auto issue = [&](int i) {
-    const uint8_t *src = gbase + (int64_t)i * bb;
-    const uint32_t dst = lds0 + (uint32_t)((i % nbuf) * bb);
-    for (int j = w; j < ndma; j += kWaves) dma16(src + j * 1024, __builtin_amdgcn_readfirstlane(dst + j * 1024));
-  };
-  for (int i = 0; i < nbuf - 1 && i < n; ++i) issue(i);
   // affine logits come out in units of 2^-24 (subnormal code operands)
   constexpr bool kAff = FMT != kFmtNvfp4;
   const float sl2 = kAff ? a.scale_log2 * kInvSub : a.scale_log2;
-  // valid slots in the last block of the segment (128 when it is full)
-  const int64_t nblk_seg = (sg.ntok + kBlock - 1) / kBlock;
-  const int tail_valid = (int)(sg.ntok - (nblk_seg - 1) * kBlock);
-  const bool has_tail = it.blk_hi == nblk_seg && tail_valid < kBlock;
-  const int nfull = has_tail ? n - 1 : n;
+  if constexpr (kAff) {
+    if (st.m != kNegInf) st.m *= kSub;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) st.o[k] = st.o[k] * kSub;
+  }
   int buf = 0;
-  for (int i = 0; i < n; ++i) {
-    // blocks i+1 .. i+nbuf-2 may still be in flight
-    wait_vmcnt(mine * min(nbuf - 2, n - 1 - i));
+  for (int p = p0; p < iss_end; ++p) {
+    const int o = p % K;
+    if (!dyn) cons_ch = (p / K) * items + j;
+    else if (o == 0) cons_ch = iss_ch;      // the issue side is in this slot too (nbuf <= K)
+    const int64_t blk_idx = (int64_t)cons_ch * K + o - r;
+    if (!dispatcher) {
+      // blocks issued after this one may stay in flight
+      wait_vmcnt(__builtin_amdgcn_readfirstlane(mine * (iss_end - p - 1)));
+    } else if (dyn && !iss_done && iss_end % K == 0 && iss_end >= fixed * K) {
+      // the issue side enters a cursor slot now: publish the chunk fetched one slot ago
+      if (lane == 0) {
+        const uint32_t idx = counter_result(cursor, a.epoch, grab);
+        *s_chunk = idx < (uint32_t)nch ? fixed * items + (int)idx : nch;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
     barrier();
-    if (i + nbuf - 1 < n) issue(i + nbuf - 1);
+    if (!iss_done) issue_next();
     const uint8_t *blk = smem + buf * bb;
     buf = buf + 1 == nbuf ? 0 : buf + 1;
-    const bool full = i < nfull;
+    const bool full = blk_idx != nblk - 1 || tail_valid == kBlock;
     const int nv = full ? kBlock : tail_valid;
     if constexpr (NSUB == 2) {
       if constexpr (FMT == kFmtNvfp4) {
@@ -994,34 +1105,24 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
   const bool valid_head = (NSUB == 2 ? (c & 7) : c) < a.G;
   const Item it = decode_item(a, blockIdx.x);
+  __shared__ int s_chunk;
   State st;
 #pragma unroll
   for (int k = 0; k < 8; ++k) st.o[k] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // part 0 opens the arrival counter early, so that the arrivals find it open (wave 3 issues
+  // no block loads, so its wait here holds up nothing else)
+  if (it.part == 0 && w == kWaves - 1 && lane == 0) counter_open(a.counters + it.bh, a.epoch);
+  if (it.seg < 0 && it.has_res) residual_part<NSUB>(a, it, w, g, c, valid_head, st);
   if (it.seg >= 0) {
     const DecodeSeg &sg = a.seg[it.seg];
     switch (sg.fmt) {
-      case kFmtInt2: stream_segment<kFmtInt2, NSUB>(a, sg, it, smem, w, g, c, valid_head, st); break;
-      case kFmtInt4: stream_segment<kFmtInt4, NSUB>(a, sg, it, smem, w, g, c, valid_head, st); break;
-      case kFmtInt8: stream_segment<kFmtInt8, NSUB>(a, sg, it, smem, w, g, c, valid_head, st); break;
-      default: stream_segment<kFmtNvfp4, NSUB>(a, sg, it, smem, w, g, c, valid_head, st); break;
+      case kFmtInt2: stream_segment<kFmtInt2, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
+      case kFmtInt4: stream_segment<kFmtInt4, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
+      case kFmtInt8: stream_segment<kFmtInt8, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
+      default: stream_segment<kFmtNvfp4, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
     }
   }
-  if (it.has_res) {
-    const uint16_t *qrow = q_row<NSUB>(a, it.bh, c, valid_head);
-    const uint8_t *res = a.res_base + (int64_t)it.bh * a.res_bh_stride;
-    const int nsteps = (a.res_ntok + 31) / 32;
-    if constexpr (NSUB == 2) {
-      QOp2 q;
-      load_q2<kFmtFp16>(qrow, valid_head, g, c, q);
-      for (int u = w; u < nsteps; u += kWaves) residual_step2(res, a.res_len, a.res_ntok, u, g, c, q, a.scale_log2, valid_head, st);
-    } else {
-      QOp q;
-      load_q<kFmtFp16>(qrow, valid_head, g, q.qb, q.qs0, q.qs1);
-      for (int u = w; u < nsteps; u += kWaves) residual_step(res, a.res_len, a.res_ntok, u, g, c, q, a.scale_log2, valid_head, st);
-    }
-  }
-
   // ---- merge the four waves in LDS: per wave m[16], l[16], o[16][128] (m in log2 units)
   float *wm = (float *)smem;                       // [4][16]
   float *wl = wm + kWaves * 16;                    // [4][16]
@@ -1063,14 +1164,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   __syncthreads();
   if (threadIdx.x == 0) {
     uint64_t *cnt = a.counters + it.bh;
-    uint64_t cur = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    uint64_t next;
-    for (;;) {
-      next = ((uint32_t)(cur >> 32) == a.epoch) ? cur + 1 : (((uint64_t)a.epoch << 32) | 1u);
-      if (__hip_atomic_compare_exchange_strong(cnt, &cur, next, __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-        break;
-    }
-    s_last = (int)(uint32_t)next == a.items_total;
+    const uint64_t old = __hip_atomic_fetch_add(cnt, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (int)counter_result(cnt, a.epoch, old) + 1 == a.items_total;
   }
   __syncthreads();
   if (!s_last) return;
@@ -1122,7 +1217,7 @@ size_t decode_lds_bytes(const DecodeArgs &a) {
   size_t ring = 0;
   for (int s = 0; s < a.nseg; ++s) {
     const int bb = (int)block_bytes(a.seg[s].fmt);
-    ring = std::max(ring, (size_t)ring_depth(bb) * bb);
+    ring = std::max(ring, (size_t)decode_ring_depth(bb) * bb);
   }
   const size_t merge = (size_t)kWaves * (16 + 16 + 16 * kHeadDim) * sizeof(float);
   return std::max(ring, merge);

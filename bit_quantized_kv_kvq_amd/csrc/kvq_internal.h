@@ -20,6 +20,9 @@ constexpr int kFmtFp16 = 0, kFmtInt2 = 2, kFmtInt4 = 4, kFmtInt8 = 8, kFmtNvfp4 
 __host__ __device__ constexpr size_t affine_block_bytes(int nbits) { return 4096u * (size_t)nbits + 2048u; }
 constexpr size_t kNvfp4BlockBytes = 18432;
 __host__ __device__ constexpr size_t block_bytes(int fmt) { return fmt == kFmtNvfp4 ? kNvfp4BlockBytes : affine_block_bytes(fmt); }
+// Blocks in the decode kernel's LDS ring: four (three in flight) while two workgroups still
+// fit in a CU, else three.
+__host__ __device__ constexpr int decode_ring_depth(size_t bb) { return bb <= 18432 ? 4 : 3; }
 
 // Offsets inside an affine block.
 constexpr size_t aff_km(int n) { return 2048u * (size_t)n; }
@@ -62,14 +65,22 @@ struct ResCopyArgs {
 };
 
 // One stretch of the cache that the decode kernel streams: a tier arena of one format.
+// A tier of a layer as the decode kernel streams it.  Its blocks are cut into chunks of
+// `chunk` consecutive blocks (chunk 0 is the short one when the count does not divide), and
+// the work items of a (b, h) share them.  Item j takes chunks j, items + j, 2 items + j, ...:
+// all of them when `fixed` covers every chunk, else the first `fixed` (2) of them and then
+// the chunks 2 items, 2 items + 1, ... that the (b, h)'s cursor hands out, until they run out.
 struct DecodeSeg {
   const uint8_t *base;     // arena of the layer
   int64_t bh_stride;       // bytes per (b, h)
   int64_t ntok;            // valid slots per (b, h)
   int fmt;                 // kFmtInt2 / Int4 / Int8 / Nvfp4
-  int blocks_per_item;     // 128-slot blocks per work item
+  int chunk;               // blocks per chunk (with a cursor: at least the LDS ring depth)
+  int nchunks;             // chunks per (b, h)
   int items;               // work items per (b, h)
+  int fixed;               // chunks per item assigned up front
   int part0;               // index of this segment's first partial among a (b, h)'s partials
+  uint64_t *cursors;       // [B*H] chunk cursors (epoch << 32 | chunks handed out)
 };
 
 constexpr int kMaxSegs = 2;        // old tier, young tier
