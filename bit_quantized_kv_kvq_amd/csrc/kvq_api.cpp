@@ -256,20 +256,22 @@ int plan_decode(const kvq_cache *c, int layer, DecodeArgs &a, uint64_t *cursors)
     const T &t = tiers[i];
     int64_t items = std::max<int64_t>(1, (int64_t)((double)target * t.nblk * block_bytes(t.fmt) / bytes + 0.5));
     items = std::min<int64_t>(items, kMaxParts / std::max(1, nt));
-    const int64_t depth = decode_ring_depth(block_bytes(t.fmt));
-    int64_t chunk = std::max<int64_t>(depth, ceil_div(t.nblk, items * 32));
-    int64_t nch = ceil_div(t.nblk, chunk);
-    int64_t fixed = 2;
-    if (nch < 4 * items) {
+    // units of about 1/32 of an item's share, at least four blocks (a unit's cursor fetch
+    // has four block times to come back); two fixed units per item, then the cursor's big
+    // units, then two single blocks per item for the finish
+    int64_t chunk = std::max<int64_t>(4, ceil_div(t.nblk, items * 32));
+    int64_t fixed = 2, nbig = 0;
+    if (t.nblk >= (fixed + 2) * items * chunk) {
+      nbig = std::max<int64_t>(0, (t.nblk - fixed * items * chunk - 2 * items) / chunk);
+    } else {
       // too little to share out: single blocks, dealt round-robin
       chunk = 1;
-      nch = t.nblk;
-      items = std::min<int64_t>(items, nch);
-      fixed = ceil_div(nch, items);
+      items = std::min<int64_t>(items, t.nblk);
+      fixed = ceil_div(t.nblk, items);
     }
     DecodeSeg &s = a.seg[a.nseg++];
     s.base = t.base; s.bh_stride = t.stride; s.ntok = t.ntok; s.fmt = t.fmt;
-    s.chunk = (int)chunk; s.nchunks = (int)nch; s.items = (int)items; s.fixed = (int)fixed; s.part0 = parts;
+    s.chunk = (int)chunk; s.items = (int)items; s.fixed = (int)fixed; s.nbig = (int)nbig; s.part0 = parts;
     s.cursors = cursors + (size_t)i * nbh;
     parts += (int)items;
   }

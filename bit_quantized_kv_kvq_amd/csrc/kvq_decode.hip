@@ -945,45 +945,59 @@ __device__ void stream_segment(const DecodeArgs &a, const DecodeSeg &sg, const I
   const bool dispatcher = w == kDmaWaves;
   const int mine = dispatcher ? 0 : (ndma - w + kDmaWaves - 1) / kDmaWaves;
   uint64_t *cursor = sg.cursors + it.bh;
-  const int K = sg.chunk, nch = sg.nchunks, items = sg.items, fixed = sg.fixed, j = it.j;
-  const bool dyn = fixed * items < nch;                      // a cursor hands out the rest
-  const int64_t nblk = (sg.ntok + kBlock - 1) / kBlock;
-  const int r = (int)((int64_t)nch * K - nblk);               // chunk 0 is short by r blocks
+  const int K = sg.chunk, items = sg.items, F = sg.fixed, nbig = sg.nbig, j = it.j;
+  const int nblk = (int)((sg.ntok + kBlock - 1) / kBlock);
+  const int fixed_end = min(F * items * K, nblk);            // blocks of the fixed units
+  const bool dyn = fixed_end < nblk;                          // a cursor hands out the rest
   // item 0 opens the cursor early, so that the other items' first fetch-adds find it open
   if (dyn && j == 0 && dispatcher && lane == 0) counter_open(cursor, a.epoch);
   const uint8_t *gbh = sg.base + (int64_t)it.bh * sg.bh_stride + lane * 16;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   const int nbuf = decode_ring_depth(bb);
-  const int tail_valid = (int)(sg.ntok - (nblk - 1) * kBlock);   // slots in the last block
-  // Positions p = 0, 1, ... of the item's block sequence: slot p / K holds chunk
-  // slot * items + j (fixed slots), then the chunks the cursor hands out; the block is
-  // chunk * K + p % K - r.  Item 0 starts at p = r, inside the short chunk 0.
-  const int p0 = j == 0 ? r : 0;
-  int iss_ch = j;            // chunk of the slot being issued
-  int cons_ch = j;           // chunk of the slot being consumed
-  int iss_end = p0;          // next position to issue
-  bool iss_done = false;
-  uint64_t grab = 0;         // dispatcher lane 0: cursor value before its last fetch-add
+  const int tail_valid = (int)(sg.ntok - (int64_t)(nblk - 1) * kBlock);   // slots in the last block
+  // The item's blocks come in units: fixed unit s (s < F) is blocks [(s items + j) K, +K);
+  // the cursor's unit u is K blocks at fixed_end + u K for u < nbig, else the single block
+  // fixed_end + nbig K + (u - nbig).  A unit starting at or past nblk ends the sequence.
+  int u_idx = 0;               // units entered so far - 1
+  int u_start = j * K;         // current unit: first block, length, blocks issued from it
+  int u_len = min(K, nblk - u_start);
+  int u_off = 0;
+  int iss_end = 0;             // blocks issued
+  bool iss_done = u_start >= nblk;
+  uint32_t tailmask = 0;       // ring slots that hold the partial last block
+  uint64_t grab = 0;           // dispatcher lane 0: cursor value before its last fetch-add
   auto issue_next = [&]() {
-    const int qp = iss_end;
-    const int o = qp % K;
-    if (o == 0 && qp > 0) {
-      const int slot = qp / K;
-      iss_ch = (!dyn || slot < fixed) ? slot * items + j : __builtin_amdgcn_readfirstlane(*s_chunk);
-      if (iss_ch >= nch) {
+    if (u_off == u_len) {
+      ++u_idx;
+      if (u_idx < F) {
+        u_start = (u_idx * items + j) * K;
+      } else if (dyn) {
+        const int u = __builtin_amdgcn_readfirstlane(*s_chunk);
+        u_start = u < nbig ? fixed_end + u * K : fixed_end + nbig * K + (u - nbig);
+      } else {
+        u_start = nblk;
+      }
+      if (u_start >= nblk) {
         iss_done = true;
         return;
       }
-      // ask for the chunk of the next slot when the cursor hands it out
-      if (dyn && slot + 1 >= fixed && dispatcher && lane == 0)
+      u_len = min(u_idx < F || u_start < fixed_end + nbig * K ? K : 1, nblk - u_start);
+      u_off = 0;
+      // ask for the unit after this one when the cursor hands it out
+      if (dyn && u_idx + 1 >= F && dispatcher && lane == 0)
         grab = __hip_atomic_fetch_add(cursor, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    const int blk_idx = u_start + u_off;
+    const int slot = iss_end % nbuf;
     if (!dispatcher) {
-      const uint8_t *src = gbh + ((int64_t)iss_ch * K + o - r) * bb;
-      const uint32_t dst = lds0 + (uint32_t)(((qp - p0) % nbuf) * bb);
+      const uint8_t *src = gbh + (int64_t)blk_idx * bb;
+      const uint32_t dst = lds0 + (uint32_t)(slot * bb);
       for (int jj = w; jj < ndma; jj += kDmaWaves) dma16(src + jj * 1024, __builtin_amdgcn_readfirstlane(dst + jj * 1024));
     }
-    iss_end = __builtin_amdgcn_readfirstlane(qp + 1);   // uniform: keeps the waits scalar
+    const bool part = blk_idx == nblk - 1 && tail_valid < kBlock;
+    tailmask = (tailmask & ~(1u << slot)) | ((uint32_t)part << slot);
+    u_off = __builtin_amdgcn_readfirstlane(u_off + 1);
+    iss_end = __builtin_amdgcn_readfirstlane(iss_end + 1);   // uniform: keeps the waits scalar
   };
   for (int t = 0; t < nbuf - 1 && !iss_done; ++t) issue_next();
 
@@ -1004,27 +1018,23 @@ __device__ void stream_segment(const DecodeArgs &a, const DecodeSeg &sg, const I
     for (int k = 0; k < 8; ++k) st.o[k] = st.o[k] * kSub;
   }
   int buf = 0;
-  for (int p = p0; p < iss_end; ++p) {
-    const int o = p % K;
-    if (!dyn) cons_ch = (p / K) * items + j;
-    else if (o == 0) cons_ch = iss_ch;      // the issue side is in this slot too (nbuf <= K)
-    const int64_t blk_idx = (int64_t)cons_ch * K + o - r;
+  for (int p = 0; p < iss_end; ++p) {
     if (!dispatcher) {
       // blocks issued after this one may stay in flight
       wait_vmcnt(__builtin_amdgcn_readfirstlane(mine * (iss_end - p - 1)));
-    } else if (dyn && !iss_done && iss_end % K == 0 && iss_end >= fixed * K) {
-      // the issue side enters a cursor slot now: publish the chunk fetched one slot ago
+    } else if (dyn && !iss_done && u_off == u_len && u_idx + 1 >= F) {
+      // the issue side enters a cursor unit now: publish the one fetched a unit ago
       if (lane == 0) {
-        const uint32_t idx = counter_result(cursor, a.epoch, grab);
-        *s_chunk = idx < (uint32_t)nch ? fixed * items + (int)idx : nch;
+        const uint32_t u = counter_result(cursor, a.epoch, grab);
+        *s_chunk = u < (uint32_t)nblk ? (int)u : nblk;
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
     barrier();
+    const bool full = !((tailmask >> buf) & 1u);
     if (!iss_done) issue_next();
     const uint8_t *blk = smem + buf * bb;
     buf = buf + 1 == nbuf ? 0 : buf + 1;
-    const bool full = blk_idx != nblk - 1 || tail_valid == kBlock;
     const int nv = full ? kBlock : tail_valid;
     if constexpr (NSUB == 2) {
       if constexpr (FMT == kFmtNvfp4) {

@@ -65,22 +65,22 @@ struct ResCopyArgs {
 };
 
 // One stretch of the cache that the decode kernel streams: a tier arena of one format.
-// A tier of a layer as the decode kernel streams it.  Its blocks are cut into chunks of
-// `chunk` consecutive blocks (chunk 0 is the short one when the count does not divide), and
-// the work items of a (b, h) share them.  Item j takes chunks j, items + j, 2 items + j, ...:
-// all of them when `fixed` covers every chunk, else the first `fixed` (2) of them and then
-// the chunks 2 items, 2 items + 1, ... that the (b, h)'s cursor hands out, until they run out.
+// A tier of a layer as the decode kernel streams it.  The work items of a (b, h) share its
+// blocks in units.  Item j first takes the `fixed` units of `chunk` blocks starting at blocks
+// (s items + j) chunk, s < fixed; when these do not cover the tier, the (b, h)'s cursor hands
+// out the rest: `nbig` units of `chunk` blocks, then single blocks, so that the items of a
+// (b, h) finish within about one block of each other.
 struct DecodeSeg {
   const uint8_t *base;     // arena of the layer
   int64_t bh_stride;       // bytes per (b, h)
   int64_t ntok;            // valid slots per (b, h)
   int fmt;                 // kFmtInt2 / Int4 / Int8 / Nvfp4
-  int chunk;               // blocks per chunk (with a cursor: at least the LDS ring depth)
-  int nchunks;             // chunks per (b, h)
+  int chunk;               // blocks per unit (fixed units and the cursor's big units)
   int items;               // work items per (b, h)
-  int fixed;               // chunks per item assigned up front
+  int fixed;               // units per item assigned up front
+  int nbig;                // big units the cursor hands out before the single blocks
   int part0;               // index of this segment's first partial among a (b, h)'s partials
-  uint64_t *cursors;       // [B*H] chunk cursors (epoch << 32 | chunks handed out)
+  uint64_t *cursors;       // [B*H] chunk cursors (epoch << 32 | units handed out)
 };
 
 constexpr int kMaxSegs = 2;        // old tier, young tier
