@@ -907,19 +907,25 @@ __device__ __forceinline__ Item decode_item(const DecodeArgs &a, int wg) {
 __device__ __forceinline__ int block_bytes_of(int fmt) { return (int)block_bytes(fmt); }
 
 
-// Query row of the head a lane's column belongs to (a valid row even for padding columns).
-template <int NSUB>
-__device__ __forceinline__ const uint16_t *q_row(const DecodeArgs &a, int bh, int c, bool valid_head) {
+// The G query rows of a (b, h) in global memory (consecutive heads).
+__device__ __forceinline__ const uint16_t *q_group(const DecodeArgs &a, int bh) {
   const int b = bh / a.H, h = bh % a.H;
+  return a.q + ((int64_t)b * a.H * a.G + (int64_t)h * a.G) * kHeadDim;
+}
+
+// Row of the head a lane's column belongs to within a group's rows (global or LDS; a valid
+// row even for padding columns).
+template <int NSUB>
+__device__ __forceinline__ const uint16_t *q_row(const uint16_t *group, int c, bool valid_head) {
   const int hc = valid_head ? (NSUB == 2 ? (c & 7) : c) : 0;
-  return a.q + ((int64_t)b * a.H * a.G + (int64_t)h * a.G + hc) * kHeadDim;
+  return group + hc * kHeadDim;
 }
 
 // The fp16 residual of the item's (b, h), in natural units.
 template <int NSUB>
-__device__ __forceinline__ void residual_part(const DecodeArgs &a, const Item &it, int w, int g, int c, bool valid_head,
-                                              State &st) {
-  const uint16_t *qrow = q_row<NSUB>(a, it.bh, c, valid_head);
+__device__ __forceinline__ void residual_part(const DecodeArgs &a, const Item &it, const uint16_t *qgroup, int w, int g,
+                                              int c, bool valid_head, State &st) {
+  const uint16_t *qrow = q_row<NSUB>(qgroup, c, valid_head);
   const uint8_t *res = a.res_base + (int64_t)it.bh * a.res_bh_stride;
   const int nsteps = (a.res_ntok + 31) / 32;
   if constexpr (NSUB == 2) {
@@ -954,6 +960,8 @@ __device__ void stream_segment(const DecodeArgs &a, const DecodeSeg &sg, const I
   const uint8_t *gbh = sg.base + (int64_t)it.bh * sg.bh_stride + lane * 16;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   const int nbuf = decode_ring_depth(bb);
+  const uint16_t *qlds = (const uint16_t *)(smem + a.q_lds_off);   // the group's query rows
+
   const int tail_valid = (int)(sg.ntok - (int64_t)(nblk - 1) * kBlock);   // slots in the last block
   // The item's blocks come in units: fixed unit s (s < F) is blocks [(s items + j) K, +K);
   // the cursor's unit u is K blocks at fixed_end + u K for u < nbig, else the single block
@@ -1001,14 +1009,15 @@ __device__ void stream_segment(const DecodeArgs &a, const DecodeSeg &sg, const I
   };
   for (int t = 0; t < nbuf - 1 && !iss_done; ++t) issue_next();
 
-  // while the first blocks load: the residual (natural units), then the query operand
-  if (it.has_res) residual_part<NSUB>(a, it, w, g, c, valid_head, st);
-  const uint16_t *qrow = q_row<NSUB>(a, it.bh, c, valid_head);
+  // while the first blocks load: the residual (natural units), the operands
+  barrier();
+  if (it.has_res) residual_part<NSUB>(a, it, qlds, w, g, c, valid_head, st);
+  asm volatile("" ::: "memory");   // the operands below are not read before the residual is done
+  const uint16_t *qrow = q_row<NSUB>(qlds, c, valid_head);
   QOp q;
   QOp2 q2;
   if constexpr (NSUB == 2) load_q2<FMT>(qrow, valid_head, g, c, q2);
   else load_q<FMT>(qrow, valid_head, g, q.qb, q.qs0, q.qs1);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   // affine logits come out in units of 2^-24 (subnormal code operands)
   constexpr bool kAff = FMT != kFmtNvfp4;
   const float sl2 = kAff ? a.scale_log2 * kInvSub : a.scale_log2;
@@ -1120,10 +1129,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) st.o[k] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // part 0 opens the arrival counter early, so that the arrivals find it open (wave 3 issues
-  // no block loads, so its wait here holds up nothing else)
+  // part 0 opens the arrival counter early, so that the arrivals find it open (wave 3 loads no
+  // blocks, so its wait here holds up nothing else)
   if (it.part == 0 && w == kWaves - 1 && lane == 0) counter_open(a.counters + it.bh, a.epoch);
-  if (it.seg < 0 && it.has_res) residual_part<NSUB>(a, it, w, g, c, valid_head, st);
+  // residual only (no quantized tier yet)
+  if (it.seg < 0 && it.has_res) residual_part<NSUB>(a, it, q_group(a, it.bh), w, g, c, valid_head, st);
+  if (it.seg >= 0 && w == kWaves - 1) {
+    // wave 3 copies the group's query rows into LDS past the ring: it loads no blocks, so its
+    // wait for these loads waits for nothing else, and the other waves read the rows from LDS
+    // (after the segment's first barrier) instead of waiting for global loads while their
+    // first blocks are in flight
+    const int qbytes = a.G * kHeadDim * 2;
+    const uint8_t *qsrc = (const uint8_t *)q_group(a, it.bh);
+    for (int off = lane * 16; off < qbytes; off += 1024)
+      *(uint4 *)(smem + a.q_lds_off + off) = *(const uint4 *)(qsrc + off);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
   if (it.seg >= 0) {
     const DecodeSeg &sg = a.seg[it.seg];
     switch (sg.fmt) {
@@ -1223,14 +1244,20 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
 
 }  // namespace
 
-size_t decode_lds_bytes(const DecodeArgs &a) {
+// LDS of the largest block ring among the call's tiers; the query rows follow it.
+static size_t decode_ring_bytes(const DecodeArgs &a) {
   size_t ring = 0;
   for (int s = 0; s < a.nseg; ++s) {
     const int bb = (int)block_bytes(a.seg[s].fmt);
     ring = std::max(ring, (size_t)decode_ring_depth(bb) * bb);
   }
+  return ring;
+}
+
+size_t decode_lds_bytes(const DecodeArgs &a) {
+  const size_t stream = decode_ring_bytes(a) + (size_t)a.G * kHeadDim * 2;
   const size_t merge = (size_t)kWaves * (16 + 16 + 16 * kHeadDim) * sizeof(float);
-  return std::max(ring, merge);
+  return std::max(stream, merge);
 }
 
 hipError_t launch_decode(const DecodeArgs &a, int num_wg, hipStream_t s) {
@@ -1242,10 +1269,12 @@ hipError_t launch_decode(const DecodeArgs &a, int num_wg, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
+  DecodeArgs b = a;
+  b.q_lds_off = (int)decode_ring_bytes(a);
   const size_t lds = decode_lds_bytes(a);
   // two 16-slot subtiles share the MFMA columns when at most 8 query heads share a kv head
-  if (a.G <= 8) decode_kernel<2><<<(unsigned)num_wg, kThreads, lds, s>>>(a);
-  else decode_kernel<1><<<(unsigned)num_wg, kThreads, lds, s>>>(a);
+  if (a.G <= 8) decode_kernel<2><<<(unsigned)num_wg, kThreads, lds, s>>>(b);
+  else decode_kernel<1><<<(unsigned)num_wg, kThreads, lds, s>>>(b);
   return hipGetLastError();
 }
 

@@ -104,6 +104,7 @@ struct DecodeArgs {
   int B, H, G;             // Hq = H * G
   float scale_log2;        // softmax_scale * log2(e)
   uint32_t epoch;          // distinct per call, tags the arrival counters
+  int q_lds_off;           // LDS byte offset of the query rows (past the largest block ring)
 };
 
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t s);
