@@ -19,7 +19,7 @@ REGION_RESIDUAL, REGION_YOUNG, REGION_OLD = 0, 1, 2
 # every symbol include/kvq.h declares
 EXPORTS = ("kvq_cache_bytes", "kvq_cache_create", "kvq_cache_destroy", "kvq_cache_reset", "kvq_append",
            "kvq_flush_residual", "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_seq_len", "kvq_layout",
-           "kvq_set_plan_only", "kvq_last_error")
+           "kvq_set_plan_only", "kvq_set_deterministic", "kvq_last_error")
 
 
 class KvqError(RuntimeError):
@@ -64,6 +64,7 @@ def lib() -> ctypes.CDLL:
     L.kvq_seq_len.argtypes = [vp, i32, P(i64), P(i64)]; L.kvq_seq_len.restype = ctypes.c_int
     L.kvq_layout.argtypes = [vp, i32, i32, P(sz), P(sz), P(i64)]; L.kvq_layout.restype = ctypes.c_int
     L.kvq_set_plan_only.argtypes = [vp, i32]; L.kvq_set_plan_only.restype = ctypes.c_int
+    L.kvq_set_deterministic.argtypes = [vp, i32]; L.kvq_set_deterministic.restype = ctypes.c_int
     L.kvq_last_error.argtypes = []; L.kvq_last_error.restype = ctypes.c_char_p
     _lib = L
     return L
@@ -142,6 +143,11 @@ class Cache:
 
     def reset(self):
         _check(lib().kvq_cache_reset(self.h))
+
+    def set_deterministic(self, on: bool = True):
+        """Decode with chunks assigned up front (bitwise reproducible output) instead of
+        shared through the workspace cursor (the default)."""
+        _check(lib().kvq_set_deterministic(self.h, 1 if on else 0))
 
     def workspace_bytes(self, num_q_heads: int) -> int:
         return lib().kvq_decode_workspace_bytes(self.h, num_q_heads)

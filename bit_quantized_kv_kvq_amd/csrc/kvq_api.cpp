@@ -96,6 +96,7 @@ struct kvq_cache {
   size_t bytes = 0;
   std::vector<LayerState> layers;
   int plan_only = 0;
+  int deterministic = 0;   // decode: chunks assigned up front instead of through the cursor
   int num_cus = 0;
 
   uint8_t *layer_base(int l) const { return base + (size_t)l * geo.layer_bytes; }
@@ -262,7 +263,10 @@ int plan_decode(const kvq_cache *c, int layer, DecodeArgs &a, uint64_t *cursors)
     int64_t chunk = std::max<int64_t>(4, ceil_div(t.nblk, items * 32));
     int64_t fixed = 2, nbig = 0;
     if (t.nblk >= (fixed + 2) * items * chunk) {
-      nbig = std::max<int64_t>(0, (t.nblk - fixed * items * chunk - 2 * items) / chunk);
+      if (c->deterministic)
+        fixed = ceil_div(ceil_div(t.nblk, chunk), items);   // every chunk dealt round-robin up front
+      else
+        nbig = std::max<int64_t>(0, (t.nblk - fixed * items * chunk - 2 * items) / chunk);
     } else {
       // too little to share out: single blocks, dealt round-robin
       chunk = 1;
@@ -332,6 +336,12 @@ int kvq_cache_reset(kvq_cache *c) {
 int kvq_set_plan_only(kvq_cache *c, int32_t plan_only) {
   if (!c) return fail(KVQ_EINVAL, "cache handle is NULL");
   c->plan_only = plan_only ? 1 : 0;
+  return KVQ_OK;
+}
+
+int kvq_set_deterministic(kvq_cache *c, int32_t on) {
+  if (!c) return fail(KVQ_EINVAL, "cache handle is NULL");
+  c->deterministic = on ? 1 : 0;
   return KVQ_OK;
 }
 

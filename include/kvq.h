@@ -134,6 +134,15 @@ int kvq_layout(const kvq_cache *c, int32_t layer, int32_t region, size_t *offset
    normal operation. */
 int kvq_set_plan_only(kvq_cache *c, int32_t plan_only);
 
+/* Decode work split of this cache.  Default (0): the work items of a (batch, kv_head) share
+   its blocks through a cursor in the workspace, which evens out their finishing times; which
+   item sums which blocks then varies from call to call, and so may the last bits of the
+   output (always within the attention tolerance).  1: every block is assigned to a work item
+   up front (chunks dealt round-robin), so that for fixed lengths every call sums in the same
+   order and the output is bitwise reproducible.  Host-only; takes effect from the next
+   kvq_decode_attn call.  Errors: KVQ_EINVAL (NULL handle). */
+int kvq_set_deterministic(kvq_cache *c, int32_t on);
+
 /* Text describing the last failure on the calling thread ("" if none). */
 const char *kvq_last_error(void);
 

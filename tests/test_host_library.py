@@ -135,3 +135,11 @@ def test_create_checks_buffer():
     assert L.kvq_cache_create(ctypes.byref(cfg), None, need, ctypes.byref(h)) == kvq.KVQ_EINVAL
     assert L.kvq_cache_create(ctypes.byref(cfg), ctypes.c_void_p(1 << 40), need, ctypes.byref(h)) == kvq.KVQ_OK
     assert L.kvq_cache_destroy(h) == kvq.KVQ_OK
+
+
+def test_deterministic_switch():
+    L = kvq.lib()
+    assert L.kvq_set_deterministic(None, 1) == kvq.KVQ_EINVAL
+    c = kvq.Cache(kvq.make_config(1, 1, 1, 1000), plan_only=True)
+    c.set_deterministic(True)
+    c.set_deterministic(False)
