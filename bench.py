@@ -16,6 +16,7 @@ launched on.  `cpu_baseline` times the CPU oracle on a bounded sample of the sam
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -186,8 +187,10 @@ def main():
     samples_bh = [(b, h) for b in range(B) for h in range(H)][:args.cpu_pairs]
     host_hist = {bh: ([], []) for bh in samples_bh}
 
-    # ---- untimed state: bulk prefill of every layer (one append of T tokens)
+    # ---- untimed state: bulk prefill of every layer (one append of T tokens); HIP events
+    # around each append give the bulk quantize rate (fp16 read + packed bytes written)
     t_prefill = time.perf_counter()
+    pre_events = []
     for l in range(L):
         k = syn.draw_k_dev(cid, l, B, H, T, W.kdist)
         v = syn.draw_v_dev(cid, l, B, H, T)
@@ -195,13 +198,19 @@ def main():
             for (b, h) in samples_bh:
                 host_hist[(b, h)][0].append(k[b, h].cpu().numpy())
                 host_hist[(b, h)][1].append(v[b, h].cpu().numpy())
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
         cache.append(l, k, v)
+        e1.record(stream)
+        pre_events.append((e0, e1))
         del k, v
         if l % 8 == 7 or l == L - 1:
             torch.cuda.synchronize()
             log(f"prefill: {l + 1}/{L} layers, {time.perf_counter() - t_prefill:.1f} s")
     torch.cuda.synchronize()
     t_prefill = time.perf_counter() - t_prefill
+    pre_ms = float(sum(a.elapsed_time(b) for a, b in pre_events))
+    pre_bytes = float(L * B * H * T * 2 * 128 * 2) + sum(decode_bytes(cache, l, fmt, old_fmt) for l in range(L))
 
     # ---- step inputs, resident in HBM before the timed region
     knew = [[syn.draw_k_dev(cid, l, B, H, per_step, W.kdist, syn.STREAM_K_APPEND, s) for l in range(L)]
@@ -217,17 +226,24 @@ def main():
     outs = [torch.empty((B, Hq, 128), dtype=torch.float16, device=dev) for _ in range(L)]
     torch.cuda.synchronize()
 
-    def step(s, events=None, nbytes=None):
+    # HIP events around every decode launch of the timed steps, created (and each recorded
+    # once) before the timed region so that no event set-up falls inside it
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps * L)]
+    for e0, e1 in events:
+        e0.record(stream)
+        e1.record(stream)
+
+    def step(s, ev=None, nbytes=None):
         for l in range(L):
             cache.append(l, knew[s][l], vnew[s][l])
             if nbytes is not None:
                 nbytes.append(decode_bytes(cache, l, fmt, old_fmt))
-            if events is not None:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            if ev is not None:
+                e0, e1 = ev[l]
                 e0.record(stream)
                 cache.decode(l, qs[s][l], sigma, outs[l], ws)
                 e1.record(stream)
-                events.append((e0, e1))
             else:
                 cache.decode(l, qs[s][l], sigma, outs[l], ws)
 
@@ -236,13 +252,16 @@ def main():
         step(s)
     torch.cuda.synchronize()
 
-    events, nbytes = [], []
+    nbytes = []
+    gc.collect()
+    gc.disable()            # no collector pause inside the timed region
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.warmup, n_steps):
-        step(s, events, nbytes)
+    for i, s in enumerate(range(args.warmup, n_steps)):
+        step(s, events[i * L:(i + 1) * L], nbytes)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gc.enable()
     log(f"timed {args.steps} steps in {wall:.3f} s")
 
     dec_ms = np.array([a.elapsed_time(b) for a, b in events])
@@ -283,6 +302,8 @@ def main():
         "decode_steps_per_s": round(args.steps / wall, 2),
         "read_probe_gbs": round(probe, 1),
         "prefill_s": round(t_prefill, 2),
+        "prefill_quantize_ms": round(pre_ms, 2),
+        "prefill_quantize_gbs": round(pre_bytes / (pre_ms * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(args.workload),
                      "kernel": "decode_kernel (one launch per kvq_decode_attn call)",
