@@ -28,6 +28,19 @@ constexpr int kRowHalves = 136;  // LDS row stride (halves) of the staged fp16 t
 
 __device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// the 8 fp16 values of a 16-byte LDS read, as floats
+__device__ __forceinline__ void unpack8(const uint4 &v, float (&x)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = h2f((uint16_t)(w[i] & 0xFFFFu));
+    x[2 * i + 1] = h2f((uint16_t)(w[i] >> 16));
+  }
+}
+
 // Round a double to the nearest binary16, ties to even; zero becomes +0.
 __device__ uint16_t f64_to_f16_rne(double v) {
   if (v == 0.0) return 0;
@@ -133,10 +146,13 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
   constexpr int kQmax = (1 << kBits) - 1;
   constexpr size_t kBlockBytes = kNv ? kNvfp4BlockBytes : affine_block_bytes(kBits);
 
+  // 34.8 KB of staged tokens and 1-3 KB of metadata: four workgroups fit in a CU
+  constexpr int kMeta = kNv ? 8 : 2;  // affine: S per 64-group; NVFP4: scale per 16-block
+  constexpr int kAffMeta = kNv ? 1 : 2;
   __shared__ __align__(16) uint16_t xs[kBlock * kRowHalves];
-  __shared__ float mS[kBlock][8];     // affine: S per group (2 used); NVFP4: scale per 16-block
-  __shared__ float mInv[kBlock][2];
-  __shared__ float mZ[kBlock][2];
+  __shared__ float mS[kBlock][kMeta];
+  __shared__ float mInv[kBlock][kAffMeta];
+  __shared__ float mZ[kBlock][kAffMeta];
 
   const int tid = threadIdx.x;
   const int64_t blk = blk0 + blockIdx.x;
@@ -160,11 +176,23 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
       src = a.res_base + (int64_t)(b * a.H + h) * a.res_bh_stride;   // residual K [R][128]
       row_stride = 256;
     }
+    // all of a thread's loads (up to 8 x 16 bytes) are issued before the first LDS write, so
+    // that their latencies overlap
     const int nchunks = (hi - lo) * 16;
-    for (int c = tid; c < nchunks; c += kThreads) {
-      const int row = lo + c / 16, col = c % 16;
-      uint4 v = *(const uint4 *)(src + (tok_off + row) * row_stride + col * 16);
-      *(uint4 *)&xs[row * kRowHalves + col * 8] = v;
+    constexpr int kPer = kBlock * 16 / kThreads;
+    uint4 v[kPer];
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) {
+      // unconditional (a branch around each load makes the compiler wait for it at the join);
+      // past the staged rows the index repeats the last chunk
+      const int c = min(tid + t * kThreads, nchunks - 1);
+      v[t] = *(const uint4 *)(src + (tok_off + lo + c / 16) * row_stride + (c % 16) * 16);
+    }
+    asm volatile("" ::: "memory");   // keeps the loads here (not sunk into the stores' branches)
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) {
+      const int c = tid + t * kThreads;
+      if (c < nchunks) *(uint4 *)&xs[(lo + c / 16) * kRowHalves + (c % 16) * 8] = v[t];
     }
   } else {
     // residual V: [R/16][128][16] fp16
@@ -184,12 +212,21 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
     uint32_t Sb = 0, Zb = 0;
     bool write = false;
     if (slot >= lo && slot < hi) {
-      float mn = INFINITY, mx = -INFINITY;
-      for (int d = 0; d < kGroup; ++d) {
-        float x = h2f(xs[slot * kRowHalves + g * kGroup + d]);
-        mn = fminf(mn, x);
-        mx = fmaxf(mx, x);
+      // min / max of the 64 values with packed fp16 compares (exact: they only select)
+      const uint4 *row = (const uint4 *)&xs[slot * kRowHalves + g * kGroup];
+      half2v mn2 = {(_Float16)INFINITY, (_Float16)INFINITY}, mx2 = {-(_Float16)INFINITY, -(_Float16)INFINITY};
+#pragma unroll
+      for (int i = 0; i < kGroup / 8; ++i) {
+        const uint4 v = row[i];
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const half2v x2 = __builtin_bit_cast(half2v, w4[k]);
+          mn2 = __builtin_elementwise_min(mn2, x2);
+          mx2 = __builtin_elementwise_max(mx2, x2);
+        }
       }
+      const float mn = fminf((float)mn2.x, (float)mn2.y), mx = fmaxf((float)mx2.x, (float)mx2.y);
       float S = 0.0f;
       if (mx > mn) {
         Sb = f64_to_f16_rne(((double)mx - (double)mn) / (double)kQmax);
@@ -228,8 +265,17 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
       uint8_t sb = 0;
       bool write = false;
       if (slot >= lo && slot < hi) {
-        float amax = 0.0f;
-        for (int d = 0; d < kNvBlock; ++d) amax = fmaxf(amax, fabsf(h2f(xs[slot * kRowHalves + nb * kNvBlock + d])));
+        // |x| of finite fp16 values orders like its bit pattern: integer max of the magnitudes
+        const uint4 *row = (const uint4 *)&xs[slot * kRowHalves + nb * kNvBlock];
+        u16x2 m2 = {0, 0};
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint4 v = row[i];
+          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, w4[k] & 0x7FFF7FFFu));
+        }
+        const float amax = h2f(m2.x > m2.y ? m2.x : m2.y);
         sb = f32_to_e4m3(amax / 6.0f);
         mS[slot][nb] = e4m3_to_f32(sb);
         write = true;
@@ -249,11 +295,16 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
   }
   __syncthreads();
 
-  // ---- codes, one 32-bit word per thread iteration
+  // ---- codes
   constexpr int F = 32 / kBits;                     // fields per word
-  constexpr int kWords = kBlock * kWordsPerRow;
+  auto code_of = [&](float x, int slot, int grp) -> uint32_t {
+    if constexpr (kNv) return e2m1_code(x, mS[slot][grp]);
+    else return affine_code(x, mS[slot][grp], mInv[slot][grp], mZ[slot][grp], kQmax);
+  };
   if (kv == 0) {
-    // K: [part w][tile u][chunk r][lane][cb bytes]; every word holds fields of one slot
+    // K: [part w][tile u][chunk r][lane][cb bytes]; a word holds F fields of one slot at F
+    // consecutive dims, read from LDS 8 values at a time
+    constexpr int kWords = kBlock * kWordsPerRow;
     constexpr int kLaneBytes = 4 * kBits;
     constexpr int kCb = kLaneBytes < 16 ? kLaneBytes : 16;
     constexpr int kK = kLaneBytes / kCb;
@@ -267,54 +318,68 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
       const int omega = (r * kCb + in_chunk) / 4;    // word of the lane string
       uint32_t word = 0;
       if (slot < hi) {
-        for (int k = 0; k < F; ++k) {
-          const int d = k_lane_dim(FMT, g, omega * F + k);
-          const float x = h2f(xs[slot * kRowHalves + d]);
-          uint32_t cd;
-          if constexpr (kNv) cd = e2m1_code(x, mS[slot][d / kNvBlock]);
-          else cd = affine_code(x, mS[slot][d / kGroup], mInv[slot][d / kGroup], mZ[slot][d / kGroup], kQmax);
-          word |= cd << (k * kBits);
+        const int d0 = k_lane_dim(FMT, g, omega * F);   // first of F consecutive dims
+        const int grp = d0 / (kNv ? kNvBlock : kGroup);
+        const uint16_t *xr = &xs[slot * kRowHalves + d0];
+        if constexpr (F >= 8) {
+#pragma unroll
+          for (int h8 = 0; h8 < F / 8; ++h8) {
+            float x[8];
+            unpack8(*(const uint4 *)(xr + 8 * h8), x);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) word |= code_of(x[k], slot, grp) << ((8 * h8 + k) * kBits);
+          }
+        } else {
+          const uint2 v = *(const uint2 *)xr;
+          const float x[4] = {h2f((uint16_t)(v.x & 0xFFFFu)), h2f((uint16_t)(v.x >> 16)), h2f((uint16_t)(v.y & 0xFFFFu)),
+                              h2f((uint16_t)(v.y >> 16))};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) word |= code_of(x[k], slot, grp) << (k * kBits);
         }
       }
       *(uint32_t *)(blkp + (size_t)w * 4) = word;
     }
   } else {
-    // V: [part w][chunk r][lane][16 bytes]; lane word omega = 4r + (word in chunk)
+    // V: [part w][chunk r][lane][16 bytes]; lane (g, c) word omega holds fields phi = omega F + j
+    // of dim 16 k + c and slot 32 w + 16 (e >> 2) + 4 g + (e & 3).  A task is (part, g, omega,
+    // c0 in {0, 8}): the words of lanes 16 g + c0 .. +7, whose field j reads the same slot at
+    // the 8 consecutive dims 16 k + c0 .. +7 (one 16-byte LDS read and one metadata lookup).
     const size_t vc = kNv ? kNvVc : aff_vc(kBits);
     constexpr int kChunks = kBits / 2;              // 16-byte chunks per lane
-    for (int w = tid; w < kWords; w += kThreads) {
-      const int chunk = w >> 2, wc = w & 3;
-      const int lane = chunk & 63, wr = chunk >> 6;
-      const int part = wr / kChunks, r = wr % kChunks;
-      const int g = lane >> 4, c = lane & 15;
-      const int omega = 4 * r + wc;
-      uint32_t *dst = (uint32_t *)(blkp + vc + (size_t)w * 4);
-      bool any = false, keep_any = false;
+    constexpr int kLaneWords = 4 * kChunks;
+    constexpr int kTasks = 4 * 4 * kLaneWords * 2;
+    for (int task = tid; task < kTasks; task += kThreads) {
+      const int c0 = 8 * (task & 1), omega = (task >> 1) % kLaneWords, g = ((task >> 1) / kLaneWords) & 3;
+      const int part = (task >> 1) / kLaneWords >> 2;
+      uint32_t words[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      uint32_t keep = 0;                            // field bits of slots before lo (kept as stored)
+      bool any = false;
+#pragma unroll
       for (int j = 0; j < F; ++j) {
         int k, e;
         v_field(FMT, omega * F + j, k, e);
         const int slot = 32 * part + 16 * (e >> 2) + 4 * g + (e & 3);
-        any |= slot >= lo && slot < zhi;
-        keep_any |= slot < lo;
+        if (slot < lo) {
+          keep |= (uint32_t)kQmax << (j * kBits);
+          continue;
+        }
+        if (slot >= zhi) continue;
+        any = true;
+        if (slot >= hi) continue;                    // cleared: code 0
+        const int d0 = 16 * k + c0;
+        const int grp = d0 / (kNv ? kNvBlock : kGroup);
+        float x[8];
+        unpack8(*(const uint4 *)&xs[slot * kRowHalves + d0], x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) words[i] |= code_of(x[i], slot, grp) << (j * kBits);
       }
       if (!any) continue;
-      uint32_t word = keep_any ? *dst : 0u;
-      for (int j = 0; j < F; ++j) {
-        int k, e;
-        v_field(FMT, omega * F + j, k, e);
-        const int slot = 32 * part + 16 * (e >> 2) + 4 * g + (e & 3);
-        if (slot < lo || slot >= zhi) continue;
-        const int d = 16 * k + c;
-        uint32_t code = 0;
-        if (slot < hi) {
-          const float x = h2f(xs[slot * kRowHalves + d]);
-          if constexpr (kNv) code = e2m1_code(x, mS[slot][d / kNvBlock]);
-          else code = affine_code(x, mS[slot][d / kGroup], mInv[slot][d / kGroup], mZ[slot][d / kGroup], kQmax);
-        }
-        const uint32_t mask = (uint32_t)kQmax << (j * kBits);
-        word = (word & ~mask) | (code << (j * kBits));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int lane = 16 * g + c0 + i;
+        uint32_t *dst = (uint32_t *)(blkp + vc + ((size_t)(part * kChunks + omega / 4) * 64 + lane) * 16 + (omega % 4) * 4);
+        *dst = keep ? (*dst & keep) | words[i] : words[i];
       }
-      *dst = word;
     }
   }
 }
