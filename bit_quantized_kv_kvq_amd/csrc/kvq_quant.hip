@@ -82,15 +82,16 @@ __device__ float e4m3_to_f32(uint32_t b) {
   return (b & 0x80) ? -mag : mag;
 }
 
-// round-half-even of x/S for fp16-valued x and S > 0 with |x/S| < 2^20; inv ~ 1/S.
+// round-half-even of x/S for fp16-valued x and S > 0 with |x/S| < 2^20; inv ~ 1/S.  k is
+// within one of the answer; the exact remainder r = x - k S decides: |r| > S/2, or |r| = S/2
+// with k odd, moves k one step towards r.
 __device__ __forceinline__ float div_rne(float x, float S, float inv) {
-  float k = rintf(x * inv);
-  float r = fmaf(-k, S, x);       // exact
-  float h = 0.5f * S;             // exact
-  bool odd = ((int)k & 1) != 0;
-  if (r > h || (r == h && odd)) k += 1.0f;
-  else if (r < -h || (r == -h && odd)) k -= 1.0f;
-  return k;
+  const float k = rintf(x * inv);
+  const float r = fmaf(-k, S, x);   // exact
+  const float h = 0.5f * S;         // exact
+  const float ar = fabsf(r);
+  const bool odd = ((int)k & 1) != 0;
+  return (ar > h || (ar == h && odd)) ? k + copysignf(1.0f, r) : k;
 }
 
 __device__ __forceinline__ uint32_t affine_code(float x, float S, float inv, float Z, int qmax) {
