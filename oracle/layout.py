@@ -42,6 +42,9 @@ Vm, affine (1024 bytes): 8 tiles tau x 4 quarters g of 32 bytes at (4tau + g)*32
 Vm, NVFP4 (1024 bytes): byte ((4w + g)*8 + k)*8 + e = E4M3 scale of dims
     16k..16k+15 of slot 32w + 16(e div 4) + 4g + (e mod 4).
 
+FP8 block (32768 bytes): [Kc][Vc], the Kc and Vc regions of INT8 (n = 8) with E4M3 bytes as
+the codes, Vc at 16384; no metadata (the scale is fixed).
+
 Residual (fp16, per layer and (batch, kv_head)), R slots (R a multiple of 16):
   K @ 0        [R][128] fp16, slot-major.
   V @ 256*R    [R/16][128][16] fp16: slot t, dim d at ((t div 16)*128 + d)*16 + t mod 16.
@@ -59,11 +62,14 @@ def affine_block_bytes(n: int) -> int:
 
 
 NVFP4_BLOCK_BYTES = 18432
+FP8_BLOCK_BYTES = 32768
 
 
 def block_bytes(fmt: str) -> int:
     if fmt == "nvfp4":
         return NVFP4_BLOCK_BYTES
+    if fmt == "fp8":
+        return FP8_BLOCK_BYTES
     return affine_block_bytes(int(fmt[3:]))
 
 
@@ -101,7 +107,7 @@ def v_lane_fields(fmt: str) -> tuple[np.ndarray, np.ndarray]:
         u, m = phi // 16, phi % 16
         k = 2 * u + (m // 4) % 2
         e = 2 * (m % 4) + m // 8
-    elif fmt == "int8":
+    elif fmt in ("int8", "fp8"):
         u, b = phi // 4, phi % 4
         k = u // 2
         e = 4 * (u % 2) + 2 * (b % 2) + b // 2
@@ -117,7 +123,7 @@ def lane_slot(w: int, g: int, e) -> np.ndarray:
 
 
 def code_bits(fmt: str) -> int:
-    return 4 if fmt == "nvfp4" else int(fmt[3:])
+    return {"nvfp4": 4, "fp8": 8}.get(fmt) or int(fmt[3:])
 
 
 def pack_fields(fields: np.ndarray, n: int) -> np.ndarray:
@@ -205,6 +211,14 @@ def pack_nvfp4_block(kq: dict, vq: dict, used: int) -> np.ndarray:
     return out
 
 
+def pack_fp8_block(kq: dict, vq: dict, used: int) -> np.ndarray:
+    codes_k = np.zeros((BLOCK, D), np.uint8); codes_k[:used] = kq["codes"]
+    codes_v = np.zeros((BLOCK, D), np.uint8); codes_v[:used] = vq["codes"]
+    out = np.concatenate([_pack_kc("fp8", codes_k), _pack_vc("fp8", codes_v)])
+    assert out.size == FP8_BLOCK_BYTES
+    return out
+
+
 def pack_arena(fmt: str, kq: dict, vq: dict) -> np.ndarray:
     """Pack N quantized token slots into ceil(N/128) blocks -> uint8 [nblocks, block_bytes]."""
     N = kq["codes"].shape[0]
@@ -216,6 +230,8 @@ def pack_arena(fmt: str, kq: dict, vq: dict) -> np.ndarray:
         sv = {k: v[lo:hi] for k, v in vq.items()}
         if fmt == "nvfp4":
             blocks.append(pack_nvfp4_block(sl, sv, hi - lo))
+        elif fmt == "fp8":
+            blocks.append(pack_fp8_block(sl, sv, hi - lo))
         else:
             blocks.append(pack_affine_block(int(fmt[3:]), sl, sv, hi - lo))
     if not blocks:

@@ -8,7 +8,10 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 * E4M3: the OCP 8-bit float with 4 exponent bits (bias 7) and 3 mantissa bits,
   no infinities, 0x7F/0xFF = NaN, largest finite 448.  Page
   "NVFP4 KV缓存技术详解" (glsqs.com/news/814573) §2.1 says that each group of 16
-  values shares one FP8 scale; the scale format is read as E4M3.
+  values shares one FP8 scale; the scale format is read as E4M3.  The same format
+  stores whole FP8 caches (page "KV Cache量化实战：Model Optimizer为大模型长上下文省下50%显存",
+  section on the KV cache formats: an FP8 cast with a fixed scale), read as a cast of each
+  value with scale 1, saturating at 448.
 * E2M1: the 4-bit float of NVFP4 (1 sign, 2 exponent, 1 mantissa bit), with
   magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
 """
@@ -82,6 +85,30 @@ def e4m3_encode(v) -> np.ndarray:
     v = np.asarray(v, dtype=np.float64)
     out = np.fromiter((e4m3_encode_scalar(float(x)) for x in v.ravel()), dtype=np.uint8, count=v.size)
     return out.reshape(v.shape)
+
+
+_E4M3_CAST_TABLE = None
+
+
+def _e4m3_cast_table() -> np.ndarray:
+    """Signed E4M3 byte of every fp16 bit pattern (finite ones; inf/NaN patterns map to the
+    saturated code of their sign), from e4m3_encode_scalar on the magnitude."""
+    global _E4M3_CAST_TABLE
+    if _E4M3_CAST_TABLE is None:
+        bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+        mag = np.abs(bits.view(np.float16).astype(np.float64))
+        mag = np.where(np.isfinite(mag), mag, E4M3_MAX)
+        table = np.array([e4m3_encode_scalar(float(m)) for m in mag], dtype=np.uint8)
+        table |= np.where(bits & 0x8000, 0x80, 0).astype(np.uint8)
+        _E4M3_CAST_TABLE = table
+    return _E4M3_CAST_TABLE
+
+
+def e4m3_cast(x16) -> np.ndarray:
+    """fp16 values -> E4M3 bytes: magnitude rounded to nearest, ties to even mantissa,
+    saturating at 448; the sign bit is kept (so -0 and negatives that round to 0 give 0x80)."""
+    x = np.ascontiguousarray(np.asarray(x16, dtype=np.float16))
+    return _e4m3_cast_table()[x.view(np.uint16)]
 
 
 # ----------------------------------------------------------------------------- E2M1

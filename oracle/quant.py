@@ -26,6 +26,11 @@ values is exact in float64, and the float64 quotients x/S, -mn/S and
 integer-plus-half, or an fp16 midpoint) than float64's relative error 2^-53;
 the tests pin this against exact rational arithmetic.
 
+FP8 -- page "KV Cache量化实战：Model Optimizer为大模型长上下文省下50%显存", section on the KV
+cache formats (an FP8 cast with a fixed scale is the default format): every value is
+cast to E4M3 with scale 1, round to nearest even, saturating at 448, sign kept;
+decode x_hat = e4m3(code).
+
 NVFP4 -- page "NVFP4 KV缓存技术详解" (glsqs.com/news/814573) §2.1 (16 values share
 one FP8 scale) and §4.2 (clip range up to 6.0): per 16 contiguous head_dim
 values, s = E4M3_RNE(amax / 6) saturating at 448, code = sign bit * 8 +
@@ -35,7 +40,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .numerics import f16, f16_saturate, e4m3_encode, e4m3_decode, e2m1_encode, e2m1_decode
+from .numerics import f16, f16_saturate, e4m3_encode, e4m3_decode, e2m1_encode, e2m1_decode, e4m3_cast
 
 GROUP = 64
 NV_BLOCK = 16
@@ -94,6 +99,7 @@ def quantize_tokens(x16: np.ndarray, fmt: str):
     Returns a dict with the stored fields:
       affine: codes [N,128], S [N,2], Z [N,2]
       nvfp4 : codes [N,128], scale [N,8]
+      fp8   : codes [N,128] (E4M3 bytes)
     """
     x16 = np.asarray(x16, dtype=np.float16)
     N, D = x16.shape
@@ -104,6 +110,8 @@ def quantize_tokens(x16: np.ndarray, fmt: str):
     if fmt == "nvfp4":
         c, s = nvfp4_quantize(x16.reshape(N, D // NV_BLOCK, NV_BLOCK))
         return {"codes": c.reshape(N, D), "scale": s}
+    if fmt == "fp8":
+        return {"codes": e4m3_cast(x16)}
     raise ValueError(fmt)
 
 
@@ -115,4 +123,6 @@ def dequantize_tokens(qt: dict, fmt: str) -> np.ndarray:
         return affine_dequantize(codes.reshape(N, D // GROUP, GROUP), qt["S"], qt["Z"]).reshape(N, D)
     if fmt == "nvfp4":
         return nvfp4_dequantize(codes.reshape(N, D // NV_BLOCK, NV_BLOCK), qt["scale"]).reshape(N, D)
+    if fmt == "fp8":
+        return e4m3_decode(codes)
     raise ValueError(fmt)

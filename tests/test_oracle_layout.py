@@ -11,6 +11,8 @@ GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "layou
 
 
 def _empty(fmt):
+    if fmt == "fp8":
+        return {"codes": np.zeros((128, 128), np.uint8)}
     if fmt == "nvfp4":
         return {"codes": np.zeros((128, 128), np.uint8), "scale": np.zeros((128, 8), np.uint8)}
     return {"codes": np.zeros((128, 128), np.uint8), "S": np.zeros((128, 2), np.float16),
@@ -18,6 +20,8 @@ def _empty(fmt):
 
 
 def _pack(fmt, kq, vq):
+    if fmt == "fp8":
+        return layout.pack_fp8_block(kq, vq, 128)
     if fmt == "nvfp4":
         return layout.pack_nvfp4_block(kq, vq, 128)
     return layout.pack_affine_block(int(fmt[3:]), kq, vq, 128)
@@ -59,7 +63,7 @@ def test_residual_positions(case):
     assert list(np.flatnonzero(data)) == [case["byte"] + 1]
 
 
-@pytest.mark.parametrize("fmt", ["int2", "int4", "int8", "nvfp4"])
+@pytest.mark.parametrize("fmt", ["int2", "int4", "int8", "nvfp4", "fp8"])
 def test_v_lane_fields_cover_every_slot_and_dim_once(fmt):
     """Every (slot, dim) of the block is held by exactly one (part, lane, field), and each
     lane's 8 operand positions e are the slots 16(e div 4) + 4g + (e mod 4) of its part."""
@@ -75,7 +79,7 @@ def test_v_lane_fields_cover_every_slot_and_dim_once(fmt):
         assert sorted(e[k == kk]) == list(range(8))
 
 
-@pytest.mark.parametrize("fmt", ["int2", "int4", "int8", "nvfp4"])
+@pytest.mark.parametrize("fmt", ["int2", "int4", "int8", "nvfp4", "fp8"])
 def test_k_lane_dims_cover_every_dim_once_per_slot(fmt):
     """The four lane quarters of a slot hold all 128 dims once; in affine formats each
     16-field half of a lane lies in one 64-dim group."""
@@ -100,6 +104,9 @@ def test_every_bit_of_a_block_is_reachable_once():
     full = {"codes": np.full((128, 128), 15, np.uint8), "scale": np.full((128, 8), 0xFF, np.uint8)}
     blk = layout.pack_nvfp4_block(full, full, 128)
     assert np.all(blk == 0xFF) and blk.size == layout.NVFP4_BLOCK_BYTES
+    full = {"codes": np.full((128, 128), 0xFF, np.uint8)}
+    blk = layout.pack_fp8_block(full, full, 128)
+    assert np.all(blk == 0xFF) and blk.size == layout.FP8_BLOCK_BYTES
 
 
 def test_partial_block_tail_is_zero():

@@ -81,6 +81,40 @@ def test_e4m3_encode_exhaustive_over_fp16_amax():
     assert ties > 0                        # the exhaustive sweep does contain exact ties
 
 
+def test_e4m3_cast_exhaustive_over_fp16():
+    """Every finite fp16 value cast to E4M3 (the FP8 cache format): the magnitude byte is the
+    exact nearest E4M3 value (ties to the even code), saturating at 448; the sign bit is
+    the sign bit of x, -0 included."""
+    import bisect
+    grid = [Fraction(float(v)) for v in nm.e4m3_decode(np.arange(0, 0x7F))]
+    x = _all_finite_f16()
+    codes = nm.e4m3_cast(x)
+    ties = 0
+    for xv, c in zip(x, codes):
+        assert (c >> 7) == int(np.signbit(xv))
+        t = abs(Fraction(float(xv)))
+        mag = c & 0x7F
+        if t >= 448:
+            assert mag == 0x7E
+            continue
+        k = bisect.bisect_left(grid, t)
+        cands = [i for i in (k - 1, k, k + 1) if 0 <= i < len(grid)]
+        best = min(abs(grid[i] - t) for i in cands)
+        tied = [i for i in cands if abs(grid[i] - t) == best]
+        if len(tied) > 1:
+            ties += 1
+            tied = [i for i in tied if i % 2 == 0]
+        assert mag == tied[0], (float(xv), hex(c), tied)
+    assert ties > 0
+
+
+def test_e4m3_cast_round_trips_every_e4m3_value():
+    """Casting the fp16 form of each finite E4M3 value returns its code (0x80 = -0 included)."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = nm.e4m3_decode(codes).astype(np.float16)
+    np.testing.assert_array_equal(nm.e4m3_cast(vals), codes)
+
+
 def test_e2m1_encode_exhaustive_brute_force():
     """All finite fp16 x against all 126 positive finite E4M3 scales: the oracle's
     midpoint comparison equals a brute-force nearest-magnitude search (exact float64

@@ -44,5 +44,8 @@ def test_stored_bytes_include_metadata():
     assert sizes.stored_bytes_per_token("int2") == 2 * 128 * 2.5 / 8
     assert sizes.stored_bytes_per_token("int8") == 2 * 128 * 8.5 / 8
     assert sizes.stored_bytes_per_token("fp16") == 512
+    assert sizes.stored_bytes_per_token("fp8") == 256            # fixed scale: no metadata
+    # the page's FP8 row: 32 layers / 8 kv heads / 32K tokens at one byte per value = 2 GiB
+    assert sizes.packed_cache_bytes("fp8", 32, 8, 32768) == 2 * GiB
     # 4 GiB fp16 at 32 layers / 8 kv heads / 32K tokens is 1 GiB at 4 bits before metadata
     assert sizes.packed_cache_bytes("int4", 32, 8, 32768) == 1 * GiB * 4.5 / 4
