@@ -36,13 +36,14 @@ DECODE_SRC = os.path.join(ROOT, "bit_quantized_kv_kvq_amd", "csrc", "kvq_decode.
 WORKLOADS = {
     "c1": (1, None), "c2": (2, None), "c3": (3, None),
     "c4-int4": (4, "int4"), "c4-int2": (4, "int2"), "c5": (5, None),
+    "c3-fp8": (3, "fp8"), "c4-fp8": (4, "fp8"),
 }
 
 
 def bytes_per_token(fmt: str) -> float:
     """Stored bytes of one token of one (batch, kv_head), K and V together."""
     return {"int2": 10240 / 128, "int4": 18432 / 128, "int8": 34816 / 128, "nvfp4": 18432 / 128,
-            "fp16": 512.0}[fmt]
+            "fp8": 32768 / 128, "fp16": 512.0}[fmt]
 
 
 def decode_bytes(cache, layer: int, fmt: str, old_fmt: str) -> float:
@@ -294,7 +295,7 @@ def main():
         "vs_baseline": None,
         "dtype": f"{fmt}-codes/fp16-operands/fp32-accum",
         "data": "synthetic (seeded, drawn on the GPU)",
-        "config": {"workload": W.name if fmt_over is None else W.name.replace("int4", fmt),
+        "config": {"workload": W.name if fmt_over is None else W.name.replace(W.fmt, fmt),
                    "layers": L, "batch": B, "q_heads": Hq, "kv_heads": H, "head_dim": 128,
                    "cached_tokens": T, "format": fmt, "old_format": W.old_fmt, "residual": R,
                    "append_per_step": per_step, "parallelism": "none (1 GPU)"},

@@ -13,7 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libkvq.so")
 
 KVQ_OK, KVQ_EINVAL, KVQ_ECAPACITY, KVQ_ENOSPACE, KVQ_EHIP, KVQ_ESTATE = 0, -1, -2, -3, -4, -5
-FMT = {"fp16": 0, "int2": 2, "int4": 4, "int8": 8, "nvfp4": 16}
+FMT = {"fp16": 0, "int2": 2, "int4": 4, "int8": 8, "nvfp4": 16, "fp8": 32}
+GROUP_SIZE = {"int2": 64, "int4": 64, "int8": 64, "nvfp4": 16, "fp8": 0}
 REGION_RESIDUAL, REGION_YOUNG, REGION_OLD = 0, 1, 2
 
 # every symbol include/kvq.h declares
@@ -78,7 +79,7 @@ def _check(code: int):
 def make_config(num_layers, batch, num_kv_heads, max_tokens, fmt="int4", residual_len=128,
                 old_fmt=None, old_after=0, head_dim=128) -> kvq_config:
     return kvq_config(num_layers, batch, num_kv_heads, head_dim, max_tokens, FMT[fmt],
-                      16 if fmt == "nvfp4" else 64, residual_len, FMT[old_fmt or fmt], old_after)
+                      GROUP_SIZE[fmt], residual_len, FMT[old_fmt or fmt], old_after)
 
 
 def kvq_cache_bytes(cfg: kvq_config) -> int:

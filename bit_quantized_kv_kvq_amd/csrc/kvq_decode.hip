@@ -117,6 +117,11 @@ __device__ __forceinline__ uint32_t e4m3_pair(uint32_t x, bool sel) {
                   : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false));
 }
 
+// FP8 word pair -> the 8 values in byte order [w0.b0, w0.b1, w0.b2, w0.b3, w1.b0, ..., w1.b3]
+__device__ __forceinline__ half8_t unpack_fp8(uint32_t w0, uint32_t w1) {
+  return h8(e4m3_pair(w0, false), e4m3_pair(w0, true), e4m3_pair(w1, false), e4m3_pair(w1, true));
+}
+
 // ---------------------------------------------------------------- cross-quarter reductions
 // Reduce over lanes {c, c+16, c+32, c+48} (the four lane quarters holding one head).
 __device__ __forceinline__ float quad_max(float x) {
@@ -145,16 +150,19 @@ __device__ __forceinline__ int q_dim(int g, int j, int e, bool &scaled) {
     return 64 * G + 16 * g + 4 * h + (e >> 1) + 8 * (e & 1);
   } else if constexpr (FMT == kFmtInt8) {
     return 64 * G + 16 * g + 4 * (2 * h + (e >> 2)) + ((e >> 1) & 1) + 2 * (e & 1);
+  } else if constexpr (FMT == kFmtFp8) {
+    return 64 * G + 16 * g + 8 * h + e;   // INT8 lane fields, converted in byte order
   } else {
     return 32 * g + 8 * j + e;   // NVFP4 and the fp16 residual: natural order
   }
 }
 
-// The 32 dims a lane quarter g feeds: affine formats dims 16g..16g+15 and 64+16g..64+16g+15
-// (local index 16G + m); NVFP4 and fp16 dims 32g..32g+31 (local index dim - 32g).
+// The 32 dims a lane quarter g feeds: affine formats and FP8 dims 16g..16g+15 and
+// 64+16g..64+16g+15 (local index 16G + m); NVFP4 and fp16 dims 32g..32g+31 (local index
+// dim - 32g).
 template <int FMT>
 __device__ __forceinline__ void load_q(const uint16_t *qrow, bool valid, int g, half8_t (&qb)[4], float &qs0, float &qs1) {
-  constexpr bool kAff = FMT == kFmtInt2 || FMT == kFmtInt4 || FMT == kFmtInt8;
+  constexpr bool kAff = FMT == kFmtInt2 || FMT == kFmtInt4 || FMT == kFmtInt8 || FMT == kFmtFp8;
   uint4 raw[4];
   if constexpr (kAff) {
     raw[0] = *(const uint4 *)(qrow + 16 * g);
@@ -454,6 +462,48 @@ __device__ __forceinline__ void nvfp4_step(const uint8_t *blk, int w, int g, int
   }
 }
 
+// FP8 (E4M3 codes with scale 1, INT8's byte positions): the values are exact fp16, so the
+// logits are the plain dot products and P multiplies the converted codes directly.  The
+// convert yields a word's bytes in order (b0, b1, b2, b3) where INT8's unpack yields operand
+// positions (b0, b2, b1, b3), so the Q dims and the P operand follow that order.
+template <bool TAIL>
+__device__ __forceinline__ void fp8_step(const uint8_t *blk, int w, int g, int c, const QOp &q, float sl2,
+                                         bool valid_head, int nvalid, State &st) {
+  const int lane = 16 * g + c;
+  const half8_t (&qb)[4] = q.qb;
+  const uint8_t *vc = blk + kF8Vc + (w * 4 * 64 + lane) * 16;
+  half8_t va[8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint4 x = *(const uint4 *)(vc + r * 1024);
+    va[2 * r] = unpack_fp8(x.x, x.y);
+    va[2 * r + 1] = unpack_fp8(x.z, x.w);
+  }
+  float s[8];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int tau = 2 * w + tt;
+    const uint8_t *row = blk + (tau * 2 * 64 + lane) * 16;
+    const uint4 x = *(const uint4 *)row, y = *(const uint4 *)(row + 1024);
+    float4_t a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0;
+    a0 = mfma(unpack_fp8(x.x, x.y), qb[0], a0);
+    a0 = mfma(unpack_fp8(x.z, x.w), qb[1], a0);
+    a1 = mfma(unpack_fp8(y.x, y.y), qb[2], a1);
+    a1 = mfma(unpack_fp8(y.z, y.w), qb[3], a1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = a0[i] + a1[i];
+      if (TAIL && 16 * tau + 4 * g + i >= nvalid) v = kNegInf;
+      s[4 * tt + i] = v;
+    }
+  }
+  float p[8];
+  softmax_step(st, s, p, valid_head, 0u, sl2);
+  const half8_t pb = h8(pk(p[0], p[2]), pk(p[1], p[3]), pk(p[4], p[6]), pk(p[5], p[7]));
+#pragma unroll
+  for (int k = 0; k < 8; ++k) st.o[k] = mfma(va[k], pb, st.o[k]);
+}
+
 // fp16 residual, 32 slots u*32 .. u*32+31 (direct global loads; R slots allocated, r used).
 __device__ __forceinline__ void residual_step(const uint8_t *res, int R, int r, int u, int g, int c, const QOp &q,
                                               float sl2, bool valid_head, State &st) {
@@ -519,7 +569,7 @@ struct QOp2 {
 };
 
 // Dim (index into the lane's 64 loaded dims) fed by B element e of k-step j, and whether it
-// meets an A element scaled by 16.  Affine formats: the lane holds dims 64G + 16(2q + gi) + m
+// meets an A element scaled by 16.  Affine formats and FP8: the lane holds dims 64G + 16(2q + gi) + m
 // at local index 32G + 16gi + m (G, gi in {0,1}); natural formats dims 64q + i at index i.
 template <int FMT>
 __device__ __forceinline__ int q_loc2(int j, int e, bool &scaled) {
@@ -532,6 +582,8 @@ __device__ __forceinline__ int q_loc2(int j, int e, bool &scaled) {
     return 32 * G + 16 * gi + 4 * hh + (e >> 1) + 8 * (e & 1);
   } else if constexpr (FMT == kFmtInt8) {
     return 32 * G + 16 * gi + 4 * (2 * hh + (e >> 2)) + ((e >> 1) & 1) + 2 * (e & 1);
+  } else if constexpr (FMT == kFmtFp8) {
+    return 32 * G + 16 * gi + 8 * hh + e;
   } else {
     return 8 * j + e;
   }
@@ -539,7 +591,7 @@ __device__ __forceinline__ int q_loc2(int j, int e, bool &scaled) {
 
 template <int FMT>
 __device__ __forceinline__ void load_q2(const uint16_t *qrow, bool valid, int g, int c, QOp2 &q) {
-  constexpr bool kAff = FMT == kFmtInt2 || FMT == kFmtInt4 || FMT == kFmtInt8;
+  constexpr bool kAff = FMT == kFmtInt2 || FMT == kFmtInt4 || FMT == kFmtInt8 || FMT == kFmtFp8;
   const int qq = g & 1;
   const bool active = valid && (c >> 3) == (g >> 1);
   uint4 raw[8];
@@ -787,6 +839,54 @@ __device__ __forceinline__ void nvfp4_step2(const uint8_t *blk, int w, int g, in
   }
 }
 
+template <bool TAIL>
+__device__ __forceinline__ void fp8_step2(const uint8_t *blk, int w, int g, int c, const QOp2 &q, float sl2,
+                                          bool valid_head, int nvalid, State &st) {
+  const int lane = 16 * g + c;
+  const int qq = g & 1, sa = g >> 1, sc = c >> 3;
+  const int tau_a = 2 * w + sa, tau_c = 2 * w + sc;
+  uint32_t vw[16];
+  {
+    const uint8_t *vc = blk + kF8Vc + (w * 4 * 64 + lane) * 16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint4 x = *(const uint4 *)(vc + r * 1024);
+      vw[4 * r] = x.x; vw[4 * r + 1] = x.y; vw[4 * r + 2] = x.z; vw[4 * r + 3] = x.w;
+    }
+  }
+  // K: chunk G of (tile, lane') at ((tile * 2 + G) * 64 + lane') * 16, lane quarters 2qq, 2qq+1
+  const uint8_t *k0 = blk + ((tau_a * 2) * 64 + 16 * (2 * qq) + c) * 16;
+  const uint8_t *k1 = blk + ((tau_a * 2) * 64 + 16 * (2 * qq + 1) + c) * 16;
+  const uint4 x0 = *(const uint4 *)k0, y0 = *(const uint4 *)(k0 + 1024);
+  const uint4 x1 = *(const uint4 *)k1, y1 = *(const uint4 *)(k1 + 1024);
+  float4_t a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0;
+  a0 = mfma(unpack_fp8(x0.x, x0.y), q.qb[0], a0);
+  a0 = mfma(unpack_fp8(x0.z, x0.w), q.qb[1], a0);
+  a0 = mfma(unpack_fp8(x1.x, x1.y), q.qb[2], a0);
+  a0 = mfma(unpack_fp8(x1.z, x1.w), q.qb[3], a0);
+  a1 = mfma(unpack_fp8(y0.x, y0.y), q.qb[4], a1);
+  a1 = mfma(unpack_fp8(y0.z, y0.w), q.qb[5], a1);
+  a1 = mfma(unpack_fp8(y1.x, y1.y), q.qb[6], a1);
+  a1 = mfma(unpack_fp8(y1.z, y1.w), q.qb[7], a1);
+  float s[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v = a0[i] + a1[i];
+    if (TAIL && 16 * tau_c + 4 * g + i >= nvalid) v = kNegInf;
+    s[i] = v;
+  }
+  float p[4];
+  softmax_step2(st, s, p, valid_head, 0u, sl2);
+  // word 2k + s0 holds slots 4 s0 + (0, 2, 1, 3) of dim 16k + c in byte order
+  const uint32_t p02 = pk(p[0], p[2]), p13 = pk(p[1], p[3]);
+  const half4_t pa0 = sc == 0 ? h4(p02, p13) : h4(0u, 0u), pa1 = sc == 1 ? h4(p02, p13) : h4(0u, 0u);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    st.o[k] = mfma16(h4(e4m3_pair(vw[2 * k], false), e4m3_pair(vw[2 * k], true)), pa0, st.o[k]);
+    st.o[k] = mfma16(h4(e4m3_pair(vw[2 * k + 1], false), e4m3_pair(vw[2 * k + 1], true)), pa1, st.o[k]);
+  }
+}
+
 // fp16 residual, slots 32u .. 32u+31, paired subtiles (direct global loads).
 __device__ __forceinline__ void residual_step2(const uint8_t *res, int R, int r, int u, int g, int c, const QOp2 &q,
                                                float sl2, bool valid_head, State &st) {
@@ -1019,7 +1119,7 @@ __device__ void stream_segment(const DecodeArgs &a, const DecodeSeg &sg, const I
   if constexpr (NSUB == 2) load_q2<FMT>(qrow, valid_head, g, c, q2);
   else load_q<FMT>(qrow, valid_head, g, q.qb, q.qs0, q.qs1);
   // affine logits come out in units of 2^-24 (subnormal code operands)
-  constexpr bool kAff = FMT != kFmtNvfp4;
+  constexpr bool kAff = FMT == kFmtInt2 || FMT == kFmtInt4 || FMT == kFmtInt8;
   const float sl2 = kAff ? a.scale_log2 * kInvSub : a.scale_log2;
   if constexpr (kAff) {
     if (st.m != kNegInf) st.m *= kSub;
@@ -1049,6 +1149,9 @@ __device__ void stream_segment(const DecodeArgs &a, const DecodeSeg &sg, const I
       if constexpr (FMT == kFmtNvfp4) {
         if (full) nvfp4_step2<false>(blk, w, g, c, q2, sl2, valid_head, nv, st);
         else nvfp4_step2<true>(blk, w, g, c, q2, sl2, valid_head, nv, st);
+      } else if constexpr (FMT == kFmtFp8) {
+        if (full) fp8_step2<false>(blk, w, g, c, q2, sl2, valid_head, nv, st);
+        else fp8_step2<true>(blk, w, g, c, q2, sl2, valid_head, nv, st);
       } else {
         if (full) affine_step2<FMT, false>(blk, w, g, c, q2, sl2, valid_head, nv, st);
         else affine_step2<FMT, true>(blk, w, g, c, q2, sl2, valid_head, nv, st);
@@ -1057,6 +1160,9 @@ __device__ void stream_segment(const DecodeArgs &a, const DecodeSeg &sg, const I
       if constexpr (FMT == kFmtNvfp4) {
         if (full) nvfp4_step<false>(blk, w, g, c, q, sl2, valid_head, nv, st);
         else nvfp4_step<true>(blk, w, g, c, q, sl2, valid_head, nv, st);
+      } else if constexpr (FMT == kFmtFp8) {
+        if (full) fp8_step<false>(blk, w, g, c, q, sl2, valid_head, nv, st);
+        else fp8_step<true>(blk, w, g, c, q, sl2, valid_head, nv, st);
       } else {
         if (full) affine_step<FMT, false>(blk, w, g, c, q, sl2, valid_head, nv, st);
         else affine_step<FMT, true>(blk, w, g, c, q, sl2, valid_head, nv, st);
@@ -1151,6 +1257,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
       case kFmtInt2: stream_segment<kFmtInt2, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
       case kFmtInt4: stream_segment<kFmtInt4, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
       case kFmtInt8: stream_segment<kFmtInt8, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
+      case kFmtFp8: stream_segment<kFmtFp8, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
       default: stream_segment<kFmtNvfp4, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
     }
   }

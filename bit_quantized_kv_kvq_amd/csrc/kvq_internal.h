@@ -14,12 +14,15 @@ constexpr int kGroup = 64;      // affine group (values of one token sharing S, 
 constexpr int kNvBlock = 16;    // NVFP4 values sharing one E4M3 scale
 
 // Format codes (values of kvq_format).
-constexpr int kFmtFp16 = 0, kFmtInt2 = 2, kFmtInt4 = 4, kFmtInt8 = 8, kFmtNvfp4 = 16;
+constexpr int kFmtFp16 = 0, kFmtInt2 = 2, kFmtInt4 = 4, kFmtInt8 = 8, kFmtNvfp4 = 16, kFmtFp8 = 32;
 
 // Bytes of one 128-slot block (K and V parts together).
 __host__ __device__ constexpr size_t affine_block_bytes(int nbits) { return 4096u * (size_t)nbits + 2048u; }
 constexpr size_t kNvfp4BlockBytes = 18432;
-__host__ __device__ constexpr size_t block_bytes(int fmt) { return fmt == kFmtNvfp4 ? kNvfp4BlockBytes : affine_block_bytes(fmt); }
+constexpr size_t kFp8BlockBytes = 32768;
+__host__ __device__ constexpr size_t block_bytes(int fmt) {
+  return fmt == kFmtNvfp4 ? kNvfp4BlockBytes : fmt == kFmtFp8 ? kFp8BlockBytes : affine_block_bytes(fmt);
+}
 // Blocks in the decode kernel's LDS ring: four (three in flight) while two workgroups still
 // fit in a CU, else three.
 __host__ __device__ constexpr int decode_ring_depth(size_t bb) { return bb <= 18432 ? 4 : 3; }
@@ -30,6 +33,8 @@ constexpr size_t aff_vc(int n) { return 2048u * (size_t)n + 1024u; }
 constexpr size_t aff_vm(int n) { return 4096u * (size_t)n + 1024u; }
 // Offsets inside an NVFP4 block.
 constexpr size_t kNvKs = 8192, kNvVc = 9216, kNvVs = 17408;
+// FP8 block: the INT8 code regions (E4M3 bytes), no metadata.
+constexpr size_t kF8Vc = 16384;
 
 // One quantize launch: tokens [src_tok0, src_tok0 + count) of a source are quantized into
 // slots [dst_slot0, dst_slot0 + count) of a tier arena, for every (batch, kv_head), K and V.

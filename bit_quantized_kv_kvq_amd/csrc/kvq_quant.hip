@@ -76,6 +76,12 @@ __device__ uint8_t f32_to_e4m3(float v) {
   return (uint8_t)(code > 0x7E ? 0x7E : code);
 }
 
+// FP8 cache code of an fp16 value: E4M3 of |x| (round to nearest even, saturating at 448)
+// with the sign bit of x.
+__device__ __forceinline__ uint32_t e4m3_cast(float x) {
+  return (uint32_t)f32_to_e4m3(fabsf(x)) | (signbit(x) ? 0x80u : 0u);
+}
+
 __device__ float e4m3_to_f32(uint32_t b) {
   uint32_t e = (b >> 3) & 0xF, m = b & 7;
   float mag = e == 0 ? (float)m * 0.001953125f : ldexpf(1.0f + (float)m * 0.125f, (int)e - 7);
@@ -127,7 +133,7 @@ __device__ __forceinline__ void v_field(int fmt, int phi, int &k, int &e) {
     const int u = phi >> 4, m = phi & 15;
     k = 2 * u + ((m >> 2) & 1);
     e = 2 * (m & 3) + (m >> 3);
-  } else if (fmt == kFmtInt8) {
+  } else if (fmt == kFmtInt8 || fmt == kFmtFp8) {   // FP8 codes sit where INT8 codes do
     const int u = phi >> 2, b = phi & 3;
     k = u >> 1;
     e = 4 * (u & 1) + 2 * (b & 1) + (b >> 1);
@@ -141,11 +147,12 @@ __device__ __forceinline__ void v_field(int fmt, int phi, int &k, int &e) {
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t blk0, int64_t nblk) {
   constexpr bool kNv = FMT == kFmtNvfp4;
-  constexpr int kBits = kNv ? 4 : FMT;
+  constexpr bool kF8 = FMT == kFmtFp8;                   // fixed scale: codes only
+  constexpr int kBits = kNv ? 4 : kF8 ? 8 : FMT;
   constexpr int kRowBytes = 16 * kBits;           // bytes per code row (128 fields)
   constexpr int kWordsPerRow = kRowBytes / 4;
   constexpr int kQmax = (1 << kBits) - 1;
-  constexpr size_t kBlockBytes = kNv ? kNvfp4BlockBytes : affine_block_bytes(kBits);
+  constexpr size_t kBlockBytes = block_bytes(FMT);
 
   // 34.8 KB of staged tokens and 1-3 KB of metadata: four workgroups fit in a CU
   constexpr int kMeta = kNv ? 8 : 2;  // affine: S per 64-group; NVFP4: scale per 16-block
@@ -207,8 +214,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
   }
   __syncthreads();
 
-  // ---- per-group metadata
-  if constexpr (!kNv) {
+  // ---- per-group metadata (none for FP8)
+  if constexpr (kF8) {
+  } else if constexpr (!kNv) {
     const int slot = tid >> 1, g = tid & 1;
     uint32_t Sb = 0, Zb = 0;
     bool write = false;
@@ -299,7 +307,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
   // ---- codes
   constexpr int F = 32 / kBits;                     // fields per word
   auto code_of = [&](float x, int slot, int grp) -> uint32_t {
-    if constexpr (kNv) return e2m1_code(x, mS[slot][grp]);
+    if constexpr (kF8) return e4m3_cast(x);
+    else if constexpr (kNv) return e2m1_code(x, mS[slot][grp]);
     else return affine_code(x, mS[slot][grp], mInv[slot][grp], mZ[slot][grp], kQmax);
   };
   if (kv == 0) {
@@ -345,7 +354,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
     // of dim 16 k + c and slot 32 w + 16 (e >> 2) + 4 g + (e & 3).  A task is (part, g, omega,
     // c0 in {0, 8}): the words of lanes 16 g + c0 .. +7, whose field j reads the same slot at
     // the 8 consecutive dims 16 k + c0 .. +7 (one 16-byte LDS read and one metadata lookup).
-    const size_t vc = kNv ? kNvVc : aff_vc(kBits);
+    const size_t vc = kNv ? kNvVc : kF8 ? kF8Vc : aff_vc(kBits);
     constexpr int kChunks = kBits / 2;              // 16-byte chunks per lane
     constexpr int kLaneWords = 4 * kChunks;
     constexpr int kTasks = 4 * 4 * kLaneWords * 2;
@@ -409,6 +418,7 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t s) {
     case kFmtInt4: quantize_kernel<kFmtInt4><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
     case kFmtInt8: quantize_kernel<kFmtInt8><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
     case kFmtNvfp4: quantize_kernel<kFmtNvfp4><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
+    case kFmtFp8: quantize_kernel<kFmtFp8><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

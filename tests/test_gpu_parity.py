@@ -10,7 +10,7 @@ from gpu_helpers import Pair, adversarial_tokens, assert_attention_close
 
 pytestmark = pytest.mark.gpu
 
-FORMATS = ["int2", "int4", "int8", "nvfp4"]
+FORMATS = ["int2", "int4", "int8", "nvfp4", "fp8"]
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
@@ -58,6 +58,38 @@ def test_nvfp4_every_amax():
     p = Pair(1, 1, 1, ntok + 8, "nvfp4", 0)
     p.append(0, toks, toks[..., ::-1].copy())
     p.check_bytes(0)
+
+
+def test_fp8_every_fp16_value():
+    """Every finite fp16 value (both zeros, subnormals, the rounding ties between E4M3 values,
+    the saturating range above 448) through the FP8 cast, as K and (reversed) as V."""
+    bits = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16)
+    x = bits.view(np.float16)
+    x = x[np.isfinite(x)]                                                 # 63488 values
+    rng = np.random.default_rng(8)
+    x = x[rng.permutation(x.size)]
+    ntok = x.size // 128
+    toks = x.reshape(1, 1, ntok, 128)
+    p = Pair(1, 1, 1, ntok + 8, "fp8", 0)
+    p.append(0, toks, toks[..., ::-1].copy())
+    p.check_bytes(0)
+
+
+def test_fp8_tier_under_int4():
+    """FP8 as the older tier below an INT4 young tier: bytes of both tiers and the decode."""
+    rng = np.random.default_rng(21)
+    B, H, G = 1, 2, 4
+    p = Pair(1, B, H, 3000, "int4", 128, "fp8", 900)
+    for n in [1500, 1, 300, "flush", 77]:
+        if n == "flush":
+            p.flush(0)
+            continue
+        p.append(0, adversarial_tokens(rng, B, H, n), adversarial_tokens(rng, B, H, n))
+        p.check_bytes(0)
+    assert p.gpu.layout(0, 2)[2] > 0
+    q = (rng.standard_normal((B, H * G, 128)) / np.sqrt(128)).astype(np.float16)
+    got, want = p.decode(0, q, 1 / np.sqrt(128))
+    assert_attention_close(got, want)
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
