@@ -45,6 +45,11 @@ Vm, NVFP4 (1024 bytes): byte ((4w + g)*8 + k)*8 + e = E4M3 scale of dims
 FP8 block (32768 bytes): [Kc][Vc], the Kc and Vc regions of INT8 (n = 8) with E4M3 bytes as
 the codes, Vc at 16384; no metadata (the scale is fixed).
 
+FP16 block (65536 bytes): [Kc][Vc] with n = 16 (every field an fp16 value, little-endian) and
+the fields in NVFP4's order: Kc lane field f of quarter g holds dim 32g + f (4 chunks of 16
+bytes per lane); Vc field phi has k = phi div 8, e = phi mod 8 (8 chunks per lane), Vc at
+32768; no metadata.
+
 Residual (fp16, per layer and (batch, kv_head)), R slots (R a multiple of 16):
   K @ 0        [R][128] fp16, slot-major.
   V @ 256*R    [R/16][128][16] fp16: slot t, dim d at ((t div 16)*128 + d)*16 + t mod 16.
@@ -63,6 +68,7 @@ def affine_block_bytes(n: int) -> int:
 
 NVFP4_BLOCK_BYTES = 18432
 FP8_BLOCK_BYTES = 32768
+FP16_BLOCK_BYTES = 65536
 
 
 def block_bytes(fmt: str) -> int:
@@ -70,13 +76,15 @@ def block_bytes(fmt: str) -> int:
         return NVFP4_BLOCK_BYTES
     if fmt == "fp8":
         return FP8_BLOCK_BYTES
+    if fmt == "fp16":
+        return FP16_BLOCK_BYTES
     return affine_block_bytes(int(fmt[3:]))
 
 
 def k_lane_dims(fmt: str, g: int) -> np.ndarray:
     """Kc lane field string of lane quarter g: field f (0..31) -> dim."""
     f = np.arange(32)
-    if fmt == "nvfp4":
+    if fmt in ("nvfp4", "fp16"):
         return 32 * g + f
     return 64 * (f // 16) + 16 * g + f % 16
 
@@ -100,9 +108,9 @@ def _pack_kc(fmt: str, codes_k: np.ndarray) -> np.ndarray:
 def v_lane_fields(fmt: str) -> tuple[np.ndarray, np.ndarray]:
     """Vc lane field string: field phi (0..63) -> (dim tile k, operand position e)."""
     phi = np.arange(64)
-    if fmt in ("int4", "nvfp4"):
+    if fmt in ("int4", "nvfp4", "fp16"):
         k, v = phi // 8, phi % 8
-        e = v if fmt == "nvfp4" else 2 * (v % 4) + v // 4
+        e = 2 * (v % 4) + v // 4 if fmt == "int4" else v
     elif fmt == "int2":
         u, m = phi // 16, phi % 16
         k = 2 * u + (m // 4) % 2
@@ -123,11 +131,14 @@ def lane_slot(w: int, g: int, e) -> np.ndarray:
 
 
 def code_bits(fmt: str) -> int:
-    return {"nvfp4": 4, "fp8": 8}.get(fmt) or int(fmt[3:])
+    return {"nvfp4": 4, "fp8": 8, "fp16": 16}.get(fmt) or int(fmt[3:])
 
 
 def pack_fields(fields: np.ndarray, n: int) -> np.ndarray:
     """n-bit little-endian field string: fields uint [..., m] -> bytes uint8 [..., m*n/8]."""
+    if n == 16:
+        return np.ascontiguousarray(np.asarray(fields).astype("<u2")).view(np.uint8).reshape(
+            np.shape(fields)[:-1] + (2 * np.shape(fields)[-1],))
     fields = np.asarray(fields, dtype=np.uint64)
     m = fields.shape[-1]
     per = 8 // n
@@ -219,6 +230,14 @@ def pack_fp8_block(kq: dict, vq: dict, used: int) -> np.ndarray:
     return out
 
 
+def pack_fp16_block(kq: dict, vq: dict, used: int) -> np.ndarray:
+    codes_k = np.zeros((BLOCK, D), np.uint16); codes_k[:used] = kq["codes"]
+    codes_v = np.zeros((BLOCK, D), np.uint16); codes_v[:used] = vq["codes"]
+    out = np.concatenate([_pack_kc("fp16", codes_k), _pack_vc("fp16", codes_v)])
+    assert out.size == FP16_BLOCK_BYTES
+    return out
+
+
 def pack_arena(fmt: str, kq: dict, vq: dict) -> np.ndarray:
     """Pack N quantized token slots into ceil(N/128) blocks -> uint8 [nblocks, block_bytes]."""
     N = kq["codes"].shape[0]
@@ -232,6 +251,8 @@ def pack_arena(fmt: str, kq: dict, vq: dict) -> np.ndarray:
             blocks.append(pack_nvfp4_block(sl, sv, hi - lo))
         elif fmt == "fp8":
             blocks.append(pack_fp8_block(sl, sv, hi - lo))
+        elif fmt == "fp16":
+            blocks.append(pack_fp16_block(sl, sv, hi - lo))
         else:
             blocks.append(pack_affine_block(int(fmt[3:]), sl, sv, hi - lo))
     if not blocks:

@@ -31,6 +31,11 @@ cache formats (an FP8 cast with a fixed scale is the default format): every valu
 cast to E4M3 with scale 1, round to nearest even, saturating at 448, sign kept;
 decode x_hat = e4m3(code).
 
+FP16 -- the unquantized reference: the pages' comparisons take the fp16 cache as the baseline
+(page "KV缓存量化技术：提升大模型长文本生成效率" §3.1, first row of the quality/memory table;
+page "KV Cache量化实战：Model Optimizer为大模型长上下文省下50%显存", formats section, keeping
+the 16-bit cache).  The stored fields are the fp16 bit patterns themselves; x_hat = x.
+
 NVFP4 -- page "NVFP4 KV缓存技术详解" (glsqs.com/news/814573) §2.1 (16 values share
 one FP8 scale) and §4.2 (clip range up to 6.0): per 16 contiguous head_dim
 values, s = E4M3_RNE(amax / 6) saturating at 448, code = sign bit * 8 +
@@ -100,6 +105,7 @@ def quantize_tokens(x16: np.ndarray, fmt: str):
       affine: codes [N,128], S [N,2], Z [N,2]
       nvfp4 : codes [N,128], scale [N,8]
       fp8   : codes [N,128] (E4M3 bytes)
+      fp16  : codes [N,128] (uint16 fp16 bit patterns)
     """
     x16 = np.asarray(x16, dtype=np.float16)
     N, D = x16.shape
@@ -112,6 +118,8 @@ def quantize_tokens(x16: np.ndarray, fmt: str):
         return {"codes": c.reshape(N, D), "scale": s}
     if fmt == "fp8":
         return {"codes": e4m3_cast(x16)}
+    if fmt == "fp16":
+        return {"codes": x16.view(np.uint16).copy()}
     raise ValueError(fmt)
 
 
@@ -125,4 +133,6 @@ def dequantize_tokens(qt: dict, fmt: str) -> np.ndarray:
         return nvfp4_dequantize(codes.reshape(N, D // NV_BLOCK, NV_BLOCK), qt["scale"]).reshape(N, D)
     if fmt == "fp8":
         return e4m3_decode(codes)
+    if fmt == "fp16":
+        return np.asarray(codes, np.uint16).view(np.float16).astype(np.float64)
     raise ValueError(fmt)

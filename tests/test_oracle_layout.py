@@ -11,6 +11,8 @@ GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "layou
 
 
 def _empty(fmt):
+    if fmt == "fp16":
+        return {"codes": np.zeros((128, 128), np.uint16)}
     if fmt == "fp8":
         return {"codes": np.zeros((128, 128), np.uint8)}
     if fmt == "nvfp4":
@@ -20,6 +22,8 @@ def _empty(fmt):
 
 
 def _pack(fmt, kq, vq):
+    if fmt == "fp16":
+        return layout.pack_fp16_block(kq, vq, 128)
     if fmt == "fp8":
         return layout.pack_fp8_block(kq, vq, 128)
     if fmt == "nvfp4":
@@ -63,7 +67,7 @@ def test_residual_positions(case):
     assert list(np.flatnonzero(data)) == [case["byte"] + 1]
 
 
-@pytest.mark.parametrize("fmt", ["int2", "int4", "int8", "nvfp4", "fp8"])
+@pytest.mark.parametrize("fmt", ["int2", "int4", "int8", "nvfp4", "fp8", "fp16"])
 def test_v_lane_fields_cover_every_slot_and_dim_once(fmt):
     """Every (slot, dim) of the block is held by exactly one (part, lane, field), and each
     lane's 8 operand positions e are the slots 16(e div 4) + 4g + (e mod 4) of its part."""
@@ -79,13 +83,13 @@ def test_v_lane_fields_cover_every_slot_and_dim_once(fmt):
         assert sorted(e[k == kk]) == list(range(8))
 
 
-@pytest.mark.parametrize("fmt", ["int2", "int4", "int8", "nvfp4", "fp8"])
+@pytest.mark.parametrize("fmt", ["int2", "int4", "int8", "nvfp4", "fp8", "fp16"])
 def test_k_lane_dims_cover_every_dim_once_per_slot(fmt):
     """The four lane quarters of a slot hold all 128 dims once; in affine formats each
     16-field half of a lane lies in one 64-dim group."""
     d = np.concatenate([layout.k_lane_dims(fmt, g) for g in range(4)])
     assert sorted(d) == list(range(128))
-    if fmt != "nvfp4":
+    if fmt not in ("nvfp4", "fp16"):
         f = np.arange(32)
         for g in range(4):
             assert np.all(layout.k_lane_dims(fmt, g) // 64 == f // 16)
@@ -107,6 +111,20 @@ def test_every_bit_of_a_block_is_reachable_once():
     full = {"codes": np.full((128, 128), 0xFF, np.uint8)}
     blk = layout.pack_fp8_block(full, full, 128)
     assert np.all(blk == 0xFF) and blk.size == layout.FP8_BLOCK_BYTES
+    full = {"codes": np.full((128, 128), 0xFFFF, np.uint16)}
+    blk = layout.pack_fp16_block(full, full, 128)
+    assert np.all(blk == 0xFF) and blk.size == layout.FP16_BLOCK_BYTES
+
+
+def test_fp16_block_holds_every_value_once():
+    """Distinct bit patterns in every (slot, dim) of K and V: the block is a permutation of
+    the 2 x 16384 values (each at an even byte offset, low byte first)."""
+    k = (np.arange(128 * 128, dtype=np.uint32).reshape(128, 128) * 2 + 1).astype(np.uint16)
+    v = (np.arange(128 * 128, dtype=np.uint32).reshape(128, 128) * 2).astype(np.uint16)
+    blk = layout.pack_fp16_block({"codes": k}, {"codes": v}, 128)
+    vals = blk.view("<u2")
+    assert sorted(vals[:16384]) == sorted(k.ravel())
+    assert sorted(vals[16384:]) == sorted(v.ravel())
 
 
 def test_partial_block_tail_is_zero():

@@ -142,3 +142,17 @@ def test_nvfp4_block_quantizer():
     big = np.full((1, 16), 60000.0, np.float16)
     _, sbig = quant.nvfp4_quantize(big)
     assert sbig[0] == 0x7E
+
+
+def test_fp16_format_stores_the_values_themselves():
+    """The unquantized format keeps every finite fp16 value bit for bit (signed zeros and
+    subnormals included) and decodes it exactly."""
+    from oracle.quant import quantize_tokens, dequantize_tokens
+    bits = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16)
+    x = bits.view(np.float16)
+    x = x[np.isfinite(x)][:63488 // 128 * 128].reshape(-1, 128)
+    q = quantize_tokens(x, "fp16")
+    assert np.array_equal(q["codes"], x.view(np.uint16))
+    xh = dequantize_tokens(q, "fp16")
+    assert np.array_equal(xh, x.astype(np.float64))
+    assert np.array_equal(np.signbit(xh), np.signbit(x))

@@ -47,5 +47,9 @@ def test_stored_bytes_include_metadata():
     assert sizes.stored_bytes_per_token("fp8") == 256            # fixed scale: no metadata
     # the page's FP8 row: 32 layers / 8 kv heads / 32K tokens at one byte per value = 2 GiB
     assert sizes.packed_cache_bytes("fp8", 32, 8, 32768) == 2 * GiB
+    # and its FP16 column (4 / 16 / 32 GiB at 32K / 128K / 256K): the fp16 block holds exactly
+    # the raw values
+    for T, gib in ((32768, 4), (131072, 16), (262144, 32)):
+        assert sizes.packed_cache_bytes("fp16", 32, 8, T) == gib * GiB
     # 4 GiB fp16 at 32 layers / 8 kv heads / 32K tokens is 1 GiB at 4 bits before metadata
     assert sizes.packed_cache_bytes("int4", 32, 8, 32768) == 1 * GiB * 4.5 / 4
