@@ -36,7 +36,7 @@ DECODE_SRC = os.path.join(ROOT, "bit_quantized_kv_kvq_amd", "csrc", "kvq_decode.
 WORKLOADS = {
     "c1": (1, None), "c2": (2, None), "c3": (3, None),
     "c4-int4": (4, "int4"), "c4-int2": (4, "int2"), "c5": (5, None),
-    "c3-fp8": (3, "fp8"), "c4-fp8": (4, "fp8"),
+    "c3-fp8": (3, "fp8"), "c4-fp8": (4, "fp8"), "c3-fp16": (3, "fp16"), "c4-fp16": (4, "fp16"),
 }
 
 

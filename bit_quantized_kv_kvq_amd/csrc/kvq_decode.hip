@@ -504,6 +504,39 @@ __device__ __forceinline__ void fp8_step(const uint8_t *blk, int w, int g, int c
   for (int k = 0; k < 8; ++k) st.o[k] = mfma(va[k], pb, st.o[k]);
 }
 
+// FP16 blocks: the operands are the stored values (K lane chunks of dims 32g + 8i .. +7 in
+// natural order, V chunks of 8 slots at one dim), so a step is two MFMA chains and the softmax.
+template <bool TAIL>
+__device__ __forceinline__ void fp16_step(const uint8_t *blk, int w, int g, int c, const QOp &q, float sl2,
+                                          bool valid_head, int nvalid, State &st) {
+  const int lane = 16 * g + c;
+  const half8_t (&qb)[4] = q.qb;
+  const uint8_t *vc = blk + kF16Vc + (w * 8 * 64 + lane) * 16;
+  half8_t va[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) va[k] = *(const half8_t *)(vc + k * 1024);
+  float s[8];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int tau = 2 * w + tt;
+    const uint8_t *row = blk + (tau * 4 * 64 + lane) * 16;
+    float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = mfma(*(const half8_t *)(row + i * 1024), qb[i], acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = acc[i];
+      if (TAIL && 16 * tau + 4 * g + i >= nvalid) v = kNegInf;
+      s[4 * tt + i] = v;
+    }
+  }
+  float p[8];
+  softmax_step(st, s, p, valid_head, 0u, sl2);
+  const half8_t pb = h8(pk(p[0], p[1]), pk(p[2], p[3]), pk(p[4], p[5]), pk(p[6], p[7]));
+#pragma unroll
+  for (int k = 0; k < 8; ++k) st.o[k] = mfma(va[k], pb, st.o[k]);
+}
+
 // fp16 residual, 32 slots u*32 .. u*32+31 (direct global loads; R slots allocated, r used).
 __device__ __forceinline__ void residual_step(const uint8_t *res, int R, int r, int u, int g, int c, const QOp &q,
                                               float sl2, bool valid_head, State &st) {
@@ -887,6 +920,43 @@ __device__ __forceinline__ void fp8_step2(const uint8_t *blk, int w, int g, int 
   }
 }
 
+template <bool TAIL>
+__device__ __forceinline__ void fp16_step2(const uint8_t *blk, int w, int g, int c, const QOp2 &q, float sl2,
+                                           bool valid_head, int nvalid, State &st) {
+  const int lane = 16 * g + c;
+  const int qq = g & 1, sa = g >> 1, sc = c >> 3;
+  const int tau_a = 2 * w + sa, tau_c = 2 * w + sc;
+  // V chunk k of this lane: halves 0..3 are subtile 0's slots, 4..7 subtile 1's
+  const uint8_t *vc = blk + kF16Vc + (w * 8 * 64 + lane) * 16;
+  uint4 vx[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) vx[k] = *(const uint4 *)(vc + k * 1024);
+  // K: the lane strings of quarters 2qq and 2qq+1 (dims 64qq .. 64qq+63) of row c of tile tau_a
+  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const uint8_t *row = blk + (tau_a * 4 * 64 + 16 * (2 * qq + gi) + c) * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = mfma(*(const half8_t *)(row + i * 1024), q.qb[4 * gi + i], acc);
+  }
+  float s[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v = acc[i];
+    if (TAIL && 16 * tau_c + 4 * g + i >= nvalid) v = kNegInf;
+    s[i] = v;
+  }
+  float p[4];
+  softmax_step2(st, s, p, valid_head, 0u, sl2);
+  const uint32_t p01 = pk(p[0], p[1]), p23 = pk(p[2], p[3]);
+  const half4_t pa0 = sc == 0 ? h4(p01, p23) : h4(0u, 0u), pa1 = sc == 1 ? h4(p01, p23) : h4(0u, 0u);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    st.o[k] = mfma16(h4(vx[k].x, vx[k].y), pa0, st.o[k]);
+    st.o[k] = mfma16(h4(vx[k].z, vx[k].w), pa1, st.o[k]);
+  }
+}
+
 // fp16 residual, slots 32u .. 32u+31, paired subtiles (direct global loads).
 __device__ __forceinline__ void residual_step2(const uint8_t *res, int R, int r, int u, int g, int c, const QOp2 &q,
                                                float sl2, bool valid_head, State &st) {
@@ -1152,6 +1222,9 @@ __device__ void stream_segment(const DecodeArgs &a, const DecodeSeg &sg, const I
       } else if constexpr (FMT == kFmtFp8) {
         if (full) fp8_step2<false>(blk, w, g, c, q2, sl2, valid_head, nv, st);
         else fp8_step2<true>(blk, w, g, c, q2, sl2, valid_head, nv, st);
+      } else if constexpr (FMT == kFmtFp16) {
+        if (full) fp16_step2<false>(blk, w, g, c, q2, sl2, valid_head, nv, st);
+        else fp16_step2<true>(blk, w, g, c, q2, sl2, valid_head, nv, st);
       } else {
         if (full) affine_step2<FMT, false>(blk, w, g, c, q2, sl2, valid_head, nv, st);
         else affine_step2<FMT, true>(blk, w, g, c, q2, sl2, valid_head, nv, st);
@@ -1163,6 +1236,9 @@ __device__ void stream_segment(const DecodeArgs &a, const DecodeSeg &sg, const I
       } else if constexpr (FMT == kFmtFp8) {
         if (full) fp8_step<false>(blk, w, g, c, q, sl2, valid_head, nv, st);
         else fp8_step<true>(blk, w, g, c, q, sl2, valid_head, nv, st);
+      } else if constexpr (FMT == kFmtFp16) {
+        if (full) fp16_step<false>(blk, w, g, c, q, sl2, valid_head, nv, st);
+        else fp16_step<true>(blk, w, g, c, q, sl2, valid_head, nv, st);
       } else {
         if (full) affine_step<FMT, false>(blk, w, g, c, q, sl2, valid_head, nv, st);
         else affine_step<FMT, true>(blk, w, g, c, q, sl2, valid_head, nv, st);
@@ -1258,6 +1334,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
       case kFmtInt4: stream_segment<kFmtInt4, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
       case kFmtInt8: stream_segment<kFmtInt8, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
       case kFmtFp8: stream_segment<kFmtFp8, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
+      case kFmtFp16: stream_segment<kFmtFp16, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
       default: stream_segment<kFmtNvfp4, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
     }
   }
@@ -1370,15 +1447,16 @@ size_t decode_lds_bytes(const DecodeArgs &a) {
 hipError_t launch_decode(const DecodeArgs &a, int num_wg, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)decode_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+    hipError_t e = hipFuncSetAttribute((const void *)decode_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxDecodeLds);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void *)decode_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+      e = hipFuncSetAttribute((const void *)decode_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxDecodeLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   DecodeArgs b = a;
   b.q_lds_off = (int)decode_ring_bytes(a);
   const size_t lds = decode_lds_bytes(a);
+  if (lds > (size_t)kMaxDecodeLds) return hipErrorInvalidValue;
   // two 16-slot subtiles share the MFMA columns when at most 8 query heads share a kv head
   if (a.G <= 8) decode_kernel<2><<<(unsigned)num_wg, kThreads, lds, s>>>(b);
   else decode_kernel<1><<<(unsigned)num_wg, kThreads, lds, s>>>(b);

@@ -20,12 +20,16 @@ constexpr int kFmtFp16 = 0, kFmtInt2 = 2, kFmtInt4 = 4, kFmtInt8 = 8, kFmtNvfp4 
 __host__ __device__ constexpr size_t affine_block_bytes(int nbits) { return 4096u * (size_t)nbits + 2048u; }
 constexpr size_t kNvfp4BlockBytes = 18432;
 constexpr size_t kFp8BlockBytes = 32768;
+constexpr size_t kFp16BlockBytes = 65536;
 __host__ __device__ constexpr size_t block_bytes(int fmt) {
-  return fmt == kFmtNvfp4 ? kNvfp4BlockBytes : fmt == kFmtFp8 ? kFp8BlockBytes : affine_block_bytes(fmt);
+  return fmt == kFmtNvfp4 ? kNvfp4BlockBytes
+         : fmt == kFmtFp8 ? kFp8BlockBytes
+         : fmt == kFmtFp16 ? kFp16BlockBytes
+                           : affine_block_bytes(fmt);
 }
 // Blocks in the decode kernel's LDS ring: four (three in flight) while two workgroups still
-// fit in a CU, else three.
-__host__ __device__ constexpr int decode_ring_depth(size_t bb) { return bb <= 18432 ? 4 : 3; }
+// fit in a CU, else three, and two for the 64 KB fp16 blocks.
+__host__ __device__ constexpr int decode_ring_depth(size_t bb) { return bb <= 18432 ? 4 : bb <= 40960 ? 3 : 2; }
 
 // Offsets inside an affine block.
 constexpr size_t aff_km(int n) { return 2048u * (size_t)n; }
@@ -35,6 +39,8 @@ constexpr size_t aff_vm(int n) { return 4096u * (size_t)n + 1024u; }
 constexpr size_t kNvKs = 8192, kNvVc = 9216, kNvVs = 17408;
 // FP8 block: the INT8 code regions (E4M3 bytes), no metadata.
 constexpr size_t kF8Vc = 16384;
+// FP16 block: K lane strings [tile][chunk][lane][16 B], then V at 32768 [part][k][lane][16 B].
+constexpr size_t kF16Vc = 32768;
 
 // One quantize launch: tokens [src_tok0, src_tok0 + count) of a source are quantized into
 // slots [dst_slot0, dst_slot0 + count) of a tier arena, for every (batch, kv_head), K and V.
@@ -116,6 +122,8 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t s);
 hipError_t launch_residual_copy(const ResCopyArgs &a, hipStream_t s);
 // LDS bytes one decode workgroup needs for the segments in `a`.
 size_t decode_lds_bytes(const DecodeArgs &a);
+// Dynamic LDS limit of the decode kernel: the fp16 ring (2 x 64 KB) plus 16 query rows
+constexpr int kMaxDecodeLds = 144 * 1024;
 hipError_t launch_decode(const DecodeArgs &a, int num_wg, hipStream_t s);
 
 }  // namespace kvq

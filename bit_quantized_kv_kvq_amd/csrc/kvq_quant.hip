@@ -144,11 +144,61 @@ __device__ __forceinline__ void v_field(int fmt, int phi, int &k, int &e) {
   }
 }
 
+// FP16 block: the staged values themselves.  K chunk ((tile*4 + i)*64 + lane) holds dims
+// 32g + 8i .. +7 of slot 16 tile + c; V chunk ((w*8 + k)*64 + lane) at kF16Vc holds dim 16k + c
+// of slots 32w + 16(e >> 2) + 4g + (e & 3), e = 0..7.  Slots before lo keep their stored
+// values; slots [hi, zhi) are cleared.
+__device__ void store_fp16_block(const uint16_t *xs, uint8_t *blkp, int kv, int lo, int hi, int zhi, int tid) {
+  constexpr int kChunks = kBlock * kHeadDim * 2 / 16;   // 16-byte chunks of K (or V)
+  if (kv == 0) {
+    for (int id = tid; id < kChunks; id += kThreads) {
+      const int lane = id & 63, i = (id >> 6) & 3, tile = id >> 8;
+      const int slot = 16 * tile + (lane & 15);
+      if (slot < lo || slot >= zhi) continue;
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (slot < hi) v = *(const uint4 *)&xs[slot * kRowHalves + 32 * (lane >> 4) + 8 * i];
+      *(uint4 *)(blkp + (size_t)id * 16) = v;
+    }
+  } else {
+    for (int id = tid; id < kChunks; id += kThreads) {
+      const int lane = id & 63, k = (id >> 6) & 7, w = id >> 9;
+      const int s0 = 32 * w + 4 * (lane >> 4), d = 16 * k + (lane & 15);
+      uint32_t word[4], keep[4];
+      bool any = false;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        word[m] = keep[m] = 0u;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int e = 2 * m + hh;
+          const int slot = s0 + 16 * (e >> 2) + (e & 3);
+          if (slot < lo) {
+            keep[m] |= 0xFFFFu << (16 * hh);
+          } else if (slot < zhi) {
+            any = true;
+            if (slot < hi) word[m] |= (uint32_t)xs[slot * kRowHalves + d] << (16 * hh);
+          }
+        }
+      }
+      if (!any) continue;
+      uint4 *dst = (uint4 *)(blkp + kF16Vc + (size_t)id * 16);
+      uint4 out = {word[0], word[1], word[2], word[3]};
+      if (keep[0] | keep[1] | keep[2] | keep[3]) {
+        const uint4 old = *dst;
+        out.x |= old.x & keep[0]; out.y |= old.y & keep[1];
+        out.z |= old.z & keep[2]; out.w |= old.w & keep[3];
+      }
+      *dst = out;
+    }
+  }
+}
+
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t blk0, int64_t nblk) {
   constexpr bool kNv = FMT == kFmtNvfp4;
   constexpr bool kF8 = FMT == kFmtFp8;                   // fixed scale: codes only
-  constexpr int kBits = kNv ? 4 : kF8 ? 8 : FMT;
+  constexpr bool kF16 = FMT == kFmtFp16;                 // the values themselves
+  constexpr int kBits = kNv ? 4 : kF8 ? 8 : kF16 ? 16 : FMT;
   constexpr int kRowBytes = 16 * kBits;           // bytes per code row (128 fields)
   constexpr int kWordsPerRow = kRowBytes / 4;
   constexpr int kQmax = (1 << kBits) - 1;
@@ -196,7 +246,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
       const int c = min(tid + t * kThreads, nchunks - 1);
       v[t] = *(const uint4 *)(src + (tok_off + lo + c / 16) * row_stride + (c % 16) * 16);
     }
-    asm volatile("" ::: "memory");   // keeps the loads here (not sunk into the stores' branches)
+    // the loaded registers pass through empty asm statements: the loads stay here, all issued
+    // before the first store, rather than being sunk into the stores' branches (a "memory"
+    // clobber would do the same but sends the array through scratch)
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) asm volatile("" : "+v"(v[t].x), "+v"(v[t].y), "+v"(v[t].z), "+v"(v[t].w));
 #pragma unroll
     for (int t = 0; t < kPer; ++t) {
       const int c = tid + t * kThreads;
@@ -213,9 +267,13 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
     }
   }
   __syncthreads();
+  if constexpr (kF16) {
+    store_fp16_block(xs, blkp, kv, lo, hi, zhi, tid);
+    return;
+  }
 
   // ---- per-group metadata (none for FP8)
-  if constexpr (kF8) {
+  if constexpr (kF8 || kF16) {
   } else if constexpr (!kNv) {
     const int slot = tid >> 1, g = tid & 1;
     uint32_t Sb = 0, Zb = 0;
@@ -419,6 +477,7 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t s) {
     case kFmtInt8: quantize_kernel<kFmtInt8><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
     case kFmtNvfp4: quantize_kernel<kFmtNvfp4><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
     case kFmtFp8: quantize_kernel<kFmtFp8><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
+    case kFmtFp16: quantize_kernel<kFmtFp16><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -52,7 +52,9 @@ typedef enum {
 } kvq_status;
 
 typedef enum {
-  KVQ_FMT_FP16 = 0,  /* only as residual storage */
+  KVQ_FMT_FP16 = 0,  /* the values themselves: the residual's storage, and as a tier format the
+                        unquantized baseline (page "KV缓存量化技术：提升大模型长文本生成效率" §3.1,
+                        the FP16 row of the quality/memory table) */
   KVQ_FMT_INT2 = 2,  /* affine, 2-bit codes, group 64, fp16 S and Z */
   KVQ_FMT_INT4 = 4,  /* affine, 4-bit codes */
   KVQ_FMT_INT8 = 8,  /* affine, 8-bit codes */
@@ -68,8 +70,8 @@ typedef struct {
   int32_t num_kv_heads; /* >= 1 */
   int32_t head_dim;     /* must be 128 */
   int64_t max_tokens;   /* per-sequence capacity, >= 1 */
-  int32_t format;       /* kvq_format of the (young) quantized tier ("nbits") */
-  int32_t group_size;   /* 64 for affine formats, 16 for NVFP4, 0 for FP8 ("group_size") */
+  int32_t format;       /* kvq_format of the (young) tier ("nbits") */
+  int32_t group_size;   /* 64 for affine formats, 16 for NVFP4, 0 for FP8 and FP16 ("group_size") */
   int32_t residual_len; /* fp16 residual length R: 0 (quantize on append) or a multiple of
                            16 up to 1024 ("residual_length"; 128 in the pages) */
   int32_t old_format;   /* kvq_format of the old tier; ignored when old_after == 0 */

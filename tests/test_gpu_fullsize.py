@@ -45,6 +45,8 @@ def _check_blocks(cache, ora: LayerCache, b, h, tier, region):
             want = olayout.pack_nvfp4_block(kq, vq, sl.size)
         elif fmt == "fp8":
             want = olayout.pack_fp8_block(kq, vq, sl.size)
+        elif fmt == "fp16":
+            want = olayout.pack_fp16_block(kq, vq, sl.size)
         else:
             want = olayout.pack_affine_block(int(fmt[3:]), kq, vq, sl.size)
         got = dev[b, h, blk * bb:(blk + 1) * bb].cpu().numpy()
@@ -122,6 +124,14 @@ def test_fullsize_long_context_128k_fp8():
 
 def test_fullsize_llama3_70b_gqa8_32k_fp8():
     _run(3, "fp8", n_pairs=2)
+
+
+def test_fullsize_long_context_128k_fp16():
+    _run(4, "fp16", steps=1, n_pairs=2)
+
+
+def test_fullsize_llama3_70b_gqa8_32k_fp16():
+    _run(3, "fp16", n_pairs=2)
 
 
 def test_fullsize_256k_prefill_int2_int4_tiers():

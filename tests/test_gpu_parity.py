@@ -10,7 +10,7 @@ from gpu_helpers import Pair, adversarial_tokens, assert_attention_close
 
 pytestmark = pytest.mark.gpu
 
-FORMATS = ["int2", "int4", "int8", "nvfp4", "fp8"]
+FORMATS = ["int2", "int4", "int8", "nvfp4", "fp8", "fp16"]
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
@@ -75,11 +75,13 @@ def test_fp8_every_fp16_value():
     p.check_bytes(0)
 
 
-def test_fp8_tier_under_int4():
-    """FP8 as the older tier below an INT4 young tier: bytes of both tiers and the decode."""
+@pytest.mark.parametrize("old", ["fp8", "fp16"])
+def test_tier_under_int4(old):
+    """FP8 or FP16 as the older tier below an INT4 young tier: bytes of both tiers and the
+    decode (one call streams two block formats)."""
     rng = np.random.default_rng(21)
     B, H, G = 1, 2, 4
-    p = Pair(1, B, H, 3000, "int4", 128, "fp8", 900)
+    p = Pair(1, B, H, 3000, "int4", 128, old, 900)
     for n in [1500, 1, 300, "flush", 77]:
         if n == "flush":
             p.flush(0)
@@ -90,6 +92,18 @@ def test_fp8_tier_under_int4():
     q = (rng.standard_normal((B, H * G, 128)) / np.sqrt(128)).astype(np.float16)
     got, want = p.decode(0, q, 1 / np.sqrt(128))
     assert_attention_close(got, want)
+
+
+def test_fp16_every_fp16_value():
+    """Every finite fp16 value stored bit for bit (signed zeros, subnormals, +-65504)."""
+    bits = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16)
+    x = bits.view(np.float16)
+    x = x[np.isfinite(x)]
+    x = x[np.random.default_rng(9).permutation(x.size)]
+    toks = x.reshape(1, 1, x.size // 128, 128)
+    p = Pair(1, 1, 1, x.size // 128 + 8, "fp16", 0)
+    p.append(0, toks, toks[..., ::-1].copy())
+    p.check_bytes(0)
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
