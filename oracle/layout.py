@@ -42,6 +42,16 @@ Vm, affine (1024 bytes): 8 tiles tau x 4 quarters g of 32 bytes at (4tau + g)*32
 Vm, NVFP4 (1024 bytes): byte ((4w + g)*8 + k)*8 + e = E4M3 scale of dims
     16k..16k+15 of slot 32w + 16(e div 4) + 4g + (e mod 4).
 
+MXFP4 block (17408 bytes): [Kc][Ks][Vc][Vs].
+Kc (8192 bytes): as NVFP4's (lane quarter g of a slot holds dims 32g .. 32g+31: one MX block).
+Ks (512 bytes): byte ((2w + u)*64 + L) = E8M0 scale of that lane's block (slot 32w + 16u + c,
+    dims 32g .. 32g+31).
+Vc (8192 bytes): the chunk scheme of NVFP4's Vc with field phi holding k = 2(phi div 16) +
+    (phi mod 2), e = (phi div 2) mod 8: byte 8m + e of a lane string holds slot e's values at
+    dims 16(2m) + c (low nibble) and 16(2m+1) + c (high nibble), two dims of one MX block.
+Vs (512 bytes): byte ((4w + g)*4 + m)*8 + e = E8M0 scale of dims 32m .. 32m+31 of slot
+    32w + 16(e div 4) + 4g + (e mod 4).
+
 FP8 block (32768 bytes): [Kc][Vc], the Kc and Vc regions of INT8 (n = 8) with E4M3 bytes as
 the codes, Vc at 16384; no metadata (the scale is fixed).
 
@@ -67,6 +77,7 @@ def affine_block_bytes(n: int) -> int:
 
 
 NVFP4_BLOCK_BYTES = 18432
+MXFP4_BLOCK_BYTES = 17408
 FP8_BLOCK_BYTES = 32768
 FP16_BLOCK_BYTES = 65536
 
@@ -74,6 +85,8 @@ FP16_BLOCK_BYTES = 65536
 def block_bytes(fmt: str) -> int:
     if fmt == "nvfp4":
         return NVFP4_BLOCK_BYTES
+    if fmt == "mxfp4":
+        return MXFP4_BLOCK_BYTES
     if fmt == "fp8":
         return FP8_BLOCK_BYTES
     if fmt == "fp16":
@@ -84,7 +97,7 @@ def block_bytes(fmt: str) -> int:
 def k_lane_dims(fmt: str, g: int) -> np.ndarray:
     """Kc lane field string of lane quarter g: field f (0..31) -> dim."""
     f = np.arange(32)
-    if fmt in ("nvfp4", "fp16"):
+    if fmt in ("nvfp4", "mxfp4", "fp16"):
         return 32 * g + f
     return 64 * (f // 16) + 16 * g + f % 16
 
@@ -111,6 +124,9 @@ def v_lane_fields(fmt: str) -> tuple[np.ndarray, np.ndarray]:
     if fmt in ("int4", "nvfp4", "fp16"):
         k, v = phi // 8, phi % 8
         e = 2 * (v % 4) + v // 4 if fmt == "int4" else v
+    elif fmt == "mxfp4":
+        k = 2 * (phi // 16) + phi % 2
+        e = (phi // 2) % 8
     elif fmt == "int2":
         u, m = phi // 16, phi % 16
         k = 2 * u + (m // 4) % 2
@@ -131,7 +147,7 @@ def lane_slot(w: int, g: int, e) -> np.ndarray:
 
 
 def code_bits(fmt: str) -> int:
-    return {"nvfp4": 4, "fp8": 8, "fp16": 16}.get(fmt) or int(fmt[3:])
+    return {"nvfp4": 4, "mxfp4": 4, "fp8": 8, "fp16": 16}.get(fmt) or int(fmt[3:])
 
 
 def pack_fields(fields: np.ndarray, n: int) -> np.ndarray:
@@ -222,6 +238,28 @@ def pack_nvfp4_block(kq: dict, vq: dict, used: int) -> np.ndarray:
     return out
 
 
+def pack_mxfp4_block(kq: dict, vq: dict, used: int) -> np.ndarray:
+    codes_k = np.zeros((BLOCK, D), np.uint8); codes_k[:used] = kq["codes"]
+    codes_v = np.zeros((BLOCK, D), np.uint8); codes_v[:used] = vq["codes"]
+    sk = np.zeros((BLOCK, 4), np.uint8); sk[:used] = kq["scale"]
+    sv = np.zeros((BLOCK, 4), np.uint8); sv[:used] = vq["scale"]
+    kc = _pack_kc("mxfp4", codes_k)
+    ks = np.zeros((4, 2, 64), np.uint8)
+    for w in range(4):
+        for u in range(2):
+            for L in range(64):
+                ks[w, u, L] = sk[32 * w + 16 * u + L % 16, L // 16]
+    vc = _pack_vc("mxfp4", codes_v)
+    vs = np.zeros((4, 4, 4, 8), np.uint8)                                   # [w][g][m][e]
+    e = np.arange(8)
+    for w in range(4):
+        for g in range(4):
+            vs[w, g] = sv[lane_slot(w, g, e)].T                             # [m][e]
+    out = np.concatenate([kc, ks.ravel(), vc, vs.ravel()])
+    assert out.size == MXFP4_BLOCK_BYTES
+    return out
+
+
 def pack_fp8_block(kq: dict, vq: dict, used: int) -> np.ndarray:
     codes_k = np.zeros((BLOCK, D), np.uint8); codes_k[:used] = kq["codes"]
     codes_v = np.zeros((BLOCK, D), np.uint8); codes_v[:used] = vq["codes"]
@@ -249,6 +287,8 @@ def pack_arena(fmt: str, kq: dict, vq: dict) -> np.ndarray:
         sv = {k: v[lo:hi] for k, v in vq.items()}
         if fmt == "nvfp4":
             blocks.append(pack_nvfp4_block(sl, sv, hi - lo))
+        elif fmt == "mxfp4":
+            blocks.append(pack_mxfp4_block(sl, sv, hi - lo))
         elif fmt == "fp8":
             blocks.append(pack_fp8_block(sl, sv, hi - lo))
         elif fmt == "fp16":

@@ -14,6 +14,9 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
   value with scale 1, saturating at 448.
 * E2M1: the 4-bit float of NVFP4 (1 sign, 2 exponent, 1 mantissa bit), with
   magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+* E8M0: the power-of-two scale of the microscaling (MX) formats, byte b = 2^(b - 127),
+  0xFF = NaN; page "NVFP4 KV缓存技术详解" §3.2 compares NVFP4 with MXFP4 (E2M1 elements
+  sharing one such scale per 32 values).
 """
 from __future__ import annotations
 
@@ -142,3 +145,14 @@ def e2m1_decode(code) -> np.ndarray:
     c = np.asarray(code, dtype=np.int64)
     mag = np.asarray(E2M1_MAGNITUDES)[c & 7]
     return np.where(c & 8, -mag, mag)
+
+
+def e8m0_decode(byte) -> np.ndarray:
+    b = np.asarray(byte, dtype=np.int64)
+    return np.where(b == 0xFF, np.nan, np.ldexp(1.0, b - 127))
+
+
+def floor_log2(a: float) -> int:
+    """floor(log2(a)) of a positive finite float, exactly (frexp: a = m 2^e, 0.5 <= m < 1)."""
+    m, e = math.frexp(a)
+    return e - 1

@@ -36,6 +36,13 @@ FP16 -- the unquantized reference: the pages' comparisons take the fp16 cache as
 page "KV Cache量化实战：Model Optimizer为大模型长上下文省下50%显存", formats section, keeping
 the 16-bit cache).  The stored fields are the fp16 bit patterns themselves; x_hat = x.
 
+MXFP4 -- page "NVFP4 KV缓存技术详解" §3.2 compares NVFP4 with MXFP4 without defining it; the
+definition taken is the open microscaling (MX) format's: 32 contiguous head_dim values share a
+power-of-two scale X = 2^(floor(log2 amax) - 2) stored as an E8M0 byte (2 is the exponent of
+E2M1's largest magnitude, 6 = 1.5 * 2^2), code = sign bit * 8 + E2M1_RNE(min(|x| / X, 6))
+(amax / X lies in [4, 8), so values above 6X saturate), decode x_hat = e2m1(code) * X.  A block
+of zeros stores byte 0 (the smallest scale) and signed-zero codes.
+
 NVFP4 -- page "NVFP4 KV缓存技术详解" (glsqs.com/news/814573) §2.1 (16 values share
 one FP8 scale) and §4.2 (clip range up to 6.0): per 16 contiguous head_dim
 values, s = E4M3_RNE(amax / 6) saturating at 448, code = sign bit * 8 +
@@ -45,10 +52,13 @@ from __future__ import annotations
 
 import numpy as np
 
-from .numerics import f16, f16_saturate, e4m3_encode, e4m3_decode, e2m1_encode, e2m1_decode, e4m3_cast
+from .numerics import (f16, f16_saturate, e4m3_encode, e4m3_decode, e2m1_encode, e2m1_decode, e4m3_cast,
+                       e8m0_decode, floor_log2)
 
 GROUP = 64
 NV_BLOCK = 16
+MX_BLOCK = 32
+E2M1_EMAX = 2            # exponent of E2M1's largest magnitude, 6 = 1.5 * 2^2
 
 
 def affine_quantize(x16: np.ndarray, nbits: int):
@@ -98,12 +108,33 @@ def nvfp4_dequantize(codes: np.ndarray, sbyte: np.ndarray) -> np.ndarray:
     return e2m1_decode(codes) * e4m3_decode(sbyte)[..., None]
 
 
+def mxfp4_quantize(x16: np.ndarray):
+    """Quantize blocks of 32 along the last axis.
+
+    x16: fp16 [..., 32].  Returns (codes uint8 [..., 32] in 0..15, E8M0 scale byte uint8 [...]).
+    """
+    x = np.asarray(x16, dtype=np.float16)
+    assert x.shape[-1] == MX_BLOCK
+    amax = np.abs(x.astype(np.float64)).max(axis=-1)
+    flat = amax.ravel()
+    e = np.array([floor_log2(a) - E2M1_EMAX if a > 0 else -127 for a in flat], dtype=np.int64).reshape(amax.shape)
+    sbyte = (e + 127).astype(np.uint8)
+    X = np.where(amax > 0, np.ldexp(1.0, e), 0.0)
+    codes = e2m1_encode(x, X[..., None])
+    return codes, sbyte
+
+
+def mxfp4_dequantize(codes: np.ndarray, sbyte: np.ndarray) -> np.ndarray:
+    return e2m1_decode(codes) * e8m0_decode(sbyte)[..., None]
+
+
 def quantize_tokens(x16: np.ndarray, fmt: str):
     """Quantize token rows of head_dim 128: x16 fp16 [N, 128].
 
     Returns a dict with the stored fields:
       affine: codes [N,128], S [N,2], Z [N,2]
       nvfp4 : codes [N,128], scale [N,8]
+      mxfp4 : codes [N,128], scale [N,4] (E8M0 bytes)
       fp8   : codes [N,128] (E4M3 bytes)
       fp16  : codes [N,128] (uint16 fp16 bit patterns)
     """
@@ -115,6 +146,9 @@ def quantize_tokens(x16: np.ndarray, fmt: str):
         return {"codes": q.reshape(N, D), "S": S, "Z": Z}
     if fmt == "nvfp4":
         c, s = nvfp4_quantize(x16.reshape(N, D // NV_BLOCK, NV_BLOCK))
+        return {"codes": c.reshape(N, D), "scale": s}
+    if fmt == "mxfp4":
+        c, s = mxfp4_quantize(x16.reshape(N, D // MX_BLOCK, MX_BLOCK))
         return {"codes": c.reshape(N, D), "scale": s}
     if fmt == "fp8":
         return {"codes": e4m3_cast(x16)}
@@ -131,6 +165,8 @@ def dequantize_tokens(qt: dict, fmt: str) -> np.ndarray:
         return affine_dequantize(codes.reshape(N, D // GROUP, GROUP), qt["S"], qt["Z"]).reshape(N, D)
     if fmt == "nvfp4":
         return nvfp4_dequantize(codes.reshape(N, D // NV_BLOCK, NV_BLOCK), qt["scale"]).reshape(N, D)
+    if fmt == "mxfp4":
+        return mxfp4_dequantize(codes.reshape(N, D // MX_BLOCK, MX_BLOCK), qt["scale"]).reshape(N, D)
     if fmt == "fp8":
         return e4m3_decode(codes)
     if fmt == "fp16":

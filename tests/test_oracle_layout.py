@@ -17,6 +17,8 @@ def _empty(fmt):
         return {"codes": np.zeros((128, 128), np.uint8)}
     if fmt == "nvfp4":
         return {"codes": np.zeros((128, 128), np.uint8), "scale": np.zeros((128, 8), np.uint8)}
+    if fmt == "mxfp4":
+        return {"codes": np.zeros((128, 128), np.uint8), "scale": np.zeros((128, 4), np.uint8)}
     return {"codes": np.zeros((128, 128), np.uint8), "S": np.zeros((128, 2), np.float16),
             "Z": np.zeros((128, 2), np.float16)}
 
@@ -28,6 +30,8 @@ def _pack(fmt, kq, vq):
         return layout.pack_fp8_block(kq, vq, 128)
     if fmt == "nvfp4":
         return layout.pack_nvfp4_block(kq, vq, 128)
+    if fmt == "mxfp4":
+        return layout.pack_mxfp4_block(kq, vq, 128)
     return layout.pack_affine_block(int(fmt[3:]), kq, vq, 128)
 
 
@@ -58,6 +62,14 @@ def test_scale_positions(case):
     assert list(np.flatnonzero(blk)) == [case["byte"]]
 
 
+@pytest.mark.parametrize("case", GOLDEN["mx_scale_cases"], ids=lambda c: f"{c['part']}-{c['slot']}")
+def test_mx_scale_positions(case):
+    kq, vq = _empty("mxfp4"), _empty("mxfp4")
+    (kq if case["part"] == "Ks" else vq)["scale"][case["slot"], case["dim"] // 32] = 0x7F
+    blk = _pack("mxfp4", kq, vq)
+    assert list(np.flatnonzero(blk)) == [case["byte"]]
+
+
 @pytest.mark.parametrize("case", GOLDEN["residual_cases"], ids=lambda c: c["part"])
 def test_residual_positions(case):
     R = case["R"]
@@ -67,7 +79,7 @@ def test_residual_positions(case):
     assert list(np.flatnonzero(data)) == [case["byte"] + 1]
 
 
-@pytest.mark.parametrize("fmt", ["int2", "int4", "int8", "nvfp4", "fp8", "fp16"])
+@pytest.mark.parametrize("fmt", ["int2", "int4", "int8", "nvfp4", "mxfp4", "fp8", "fp16"])
 def test_v_lane_fields_cover_every_slot_and_dim_once(fmt):
     """Every (slot, dim) of the block is held by exactly one (part, lane, field), and each
     lane's 8 operand positions e are the slots 16(e div 4) + 4g + (e mod 4) of its part."""
@@ -83,13 +95,13 @@ def test_v_lane_fields_cover_every_slot_and_dim_once(fmt):
         assert sorted(e[k == kk]) == list(range(8))
 
 
-@pytest.mark.parametrize("fmt", ["int2", "int4", "int8", "nvfp4", "fp8", "fp16"])
+@pytest.mark.parametrize("fmt", ["int2", "int4", "int8", "nvfp4", "mxfp4", "fp8", "fp16"])
 def test_k_lane_dims_cover_every_dim_once_per_slot(fmt):
     """The four lane quarters of a slot hold all 128 dims once; in affine formats each
     16-field half of a lane lies in one 64-dim group."""
     d = np.concatenate([layout.k_lane_dims(fmt, g) for g in range(4)])
     assert sorted(d) == list(range(128))
-    if fmt not in ("nvfp4", "fp16"):
+    if fmt not in ("nvfp4", "mxfp4", "fp16"):
         f = np.arange(32)
         for g in range(4):
             assert np.all(layout.k_lane_dims(fmt, g) // 64 == f // 16)
@@ -108,6 +120,9 @@ def test_every_bit_of_a_block_is_reachable_once():
     full = {"codes": np.full((128, 128), 15, np.uint8), "scale": np.full((128, 8), 0xFF, np.uint8)}
     blk = layout.pack_nvfp4_block(full, full, 128)
     assert np.all(blk == 0xFF) and blk.size == layout.NVFP4_BLOCK_BYTES
+    full = {"codes": np.full((128, 128), 15, np.uint8), "scale": np.full((128, 4), 0xFF, np.uint8)}
+    blk = layout.pack_mxfp4_block(full, full, 128)
+    assert np.all(blk == 0xFF) and blk.size == layout.MXFP4_BLOCK_BYTES
     full = {"codes": np.full((128, 128), 0xFF, np.uint8)}
     blk = layout.pack_fp8_block(full, full, 128)
     assert np.all(blk == 0xFF) and blk.size == layout.FP8_BLOCK_BYTES

@@ -156,3 +156,56 @@ def test_fp16_format_stores_the_values_themselves():
     xh = dequantize_tokens(q, "fp16")
     assert np.array_equal(xh, x.astype(np.float64))
     assert np.array_equal(np.signbit(xh), np.signbit(x))
+
+
+def test_mx_scale_exhaustive_over_fp16_amax():
+    """For every positive finite fp16 block maximum the E8M0 scale X is the power of two with
+    4 <= amax / X < 8 (the largest magnitude then lands in E2M1's top binade [4, 8))."""
+    from oracle.quant import mxfp4_quantize
+    bits = np.arange(1, 0x7C00, dtype=np.uint16)
+    amax = bits.view(np.float16)
+    x = np.zeros((amax.size, 32), np.float16)
+    x[:, 7] = amax
+    x[::2, 7] *= -1                                  # the sign does not matter
+    _, sb = mxfp4_quantize(x)
+    X = np.ldexp(1.0, sb.astype(np.int64) - 127)
+    r = amax.astype(np.float64) / X
+    assert np.all((r >= 4) & (r < 8))
+    assert sb.min() == 127 - 26 and sb.max() == 127 + 13    # 2^-24 and 65504
+
+
+def test_mxfp4_codes_brute_force():
+    """Each code is the E2M1 magnitude nearest to min(|x| / X, 6) (ties to the even code), with
+    x's sign bit; decoding multiplies by X exactly."""
+    from oracle.quant import mxfp4_quantize, mxfp4_dequantize
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal((4000, 32)) * np.exp2(rng.integers(-20, 12, (4000, 1)))).astype(np.float16)
+    x[::5] = np.round(x[::5].astype(np.float64) * 4) / 4            # many exact grid points and ties
+    x[3::7, 2] = -0.0
+    codes, sb = mxfp4_quantize(x)
+    X = np.ldexp(1.0, sb.astype(np.int64) - 127)[:, None]
+    t = np.minimum(np.abs(x.astype(np.float64)) / X, 6.0)
+    d = np.abs(t[..., None] - mags)                                  # [n, 32, 8]
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best
+    # nearest; on a tie the even index
+    want = np.where(cand.sum(-1) > 1, np.argmax(cand & (np.arange(8) % 2 == 0), axis=-1), np.argmax(cand, axis=-1))
+    assert np.array_equal(codes & 7, want)
+    assert np.array_equal(codes >> 3, np.signbit(x).astype(np.uint8))
+    xh = mxfp4_dequantize(codes, sb)
+    assert np.array_equal(xh, np.where(codes & 8, -1, 1) * mags[codes & 7] * X)
+
+
+def test_mxfp4_saturation_and_zero_block():
+    """Values between 6X and 8X saturate to 6X (amax = 7 * 2^k gives X = 2^(k+0), since
+    floor(log2 7) = 2); an all-zero block stores the smallest scale and signed zeros."""
+    from oracle.quant import mxfp4_quantize, mxfp4_dequantize
+    x = np.zeros((2, 32), np.float16)
+    x[0, 0] = 7.0
+    x[0, 1] = -3.0
+    x[1, 5] = -0.0
+    codes, sb = mxfp4_quantize(x)
+    assert sb[0] == 127 and codes[0, 0] == 7 and codes[0, 1] == 8 + 5
+    assert mxfp4_dequantize(codes, sb)[0, 0] == 6.0
+    assert sb[1] == 0 and codes[1, 5] == 8 and not codes[1, :5].any()

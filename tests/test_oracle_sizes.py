@@ -45,6 +45,8 @@ def test_stored_bytes_include_metadata():
     assert sizes.stored_bytes_per_token("int8") == 2 * 128 * 8.5 / 8
     assert sizes.stored_bytes_per_token("fp16") == 512
     assert sizes.stored_bytes_per_token("fp8") == 256            # fixed scale: no metadata
+    # MXFP4: 4-bit codes + one byte per 32 values = 4.25 bits
+    assert sizes.stored_bytes_per_token("mxfp4") == 2 * 128 * 4.25 / 8
     # the page's FP8 row: 32 layers / 8 kv heads / 32K tokens at one byte per value = 2 GiB
     assert sizes.packed_cache_bytes("fp8", 32, 8, 32768) == 2 * GiB
     # and its FP16 column (4 / 16 / 32 GiB at 32K / 128K / 256K): the fp16 block holds exactly
