@@ -13,8 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libkvq.so")
 
 KVQ_OK, KVQ_EINVAL, KVQ_ECAPACITY, KVQ_ENOSPACE, KVQ_EHIP, KVQ_ESTATE = 0, -1, -2, -3, -4, -5
-FMT = {"fp16": 0, "int2": 2, "int4": 4, "int8": 8, "nvfp4": 16, "fp8": 32}
-GROUP_SIZE = {"int2": 64, "int4": 64, "int8": 64, "nvfp4": 16, "fp8": 0, "fp16": 0}
+FMT = {"fp16": 0, "int2": 2, "int4": 4, "int8": 8, "nvfp4": 16, "fp8": 32, "mxfp4": 64}
+GROUP_SIZE = {"int2": 64, "int4": 64, "int8": 64, "nvfp4": 16, "fp8": 0, "fp16": 0, "mxfp4": 32}
 REGION_RESIDUAL, REGION_YOUNG, REGION_OLD = 0, 1, 2
 
 # every symbol include/kvq.h declares

@@ -41,9 +41,12 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // formats a tier's blocks can hold (fp16: the values themselves, the unquantized baseline)
 bool is_block_fmt(int f) {
-  return f == kFmtInt2 || f == kFmtInt4 || f == kFmtInt8 || f == kFmtNvfp4 || f == kFmtFp8 || f == kFmtFp16;
+  return f == kFmtInt2 || f == kFmtInt4 || f == kFmtInt8 || f == kFmtNvfp4 || f == kFmtMxfp4 || f == kFmtFp8 ||
+         f == kFmtFp16;
 }
-int group_of(int f) { return f == kFmtNvfp4 ? kNvBlock : (f == kFmtFp8 || f == kFmtFp16) ? 0 : kGroup; }
+int group_of(int f) {
+  return f == kFmtNvfp4 ? kNvBlock : f == kFmtMxfp4 ? kMxBlock : (f == kFmtFp8 || f == kFmtFp16) ? 0 : kGroup;
+}
 
 struct LayerState {
   int64_t length = 0;  // tokens cached
@@ -64,9 +67,9 @@ const char *check_config(const kvq_config *c) {
   if (c->num_layers < 1 || c->batch < 1 || c->num_kv_heads < 1) return "num_layers, batch and num_kv_heads must be >= 1";
   if (c->head_dim != kHeadDim) return "head_dim must be 128";
   if (c->max_tokens < 1) return "max_tokens must be >= 1";
-  if (!is_block_fmt(c->format)) return "format must be KVQ_FMT_FP16/INT2/INT4/INT8/NVFP4/FP8";
+  if (!is_block_fmt(c->format)) return "format must be KVQ_FMT_FP16/INT2/INT4/INT8/NVFP4/MXFP4/FP8";
   if (c->group_size != group_of(c->format))
-    return "group_size must be 64 for affine formats, 16 for NVFP4 and 0 for FP8 and FP16";
+    return "group_size must be 64 for affine formats, 16 for NVFP4, 32 for MXFP4 and 0 for FP8 and FP16";
   if (c->residual_len < 0 || c->residual_len > 1024 || c->residual_len % 16 != 0)
     return "residual_len must be 0 or a multiple of 16 up to 1024";
   if (c->old_after < 0) return "old_after must be >= 0";

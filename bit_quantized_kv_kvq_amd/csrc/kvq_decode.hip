@@ -117,6 +117,41 @@ __device__ __forceinline__ uint32_t e4m3_pair(uint32_t x, bool sel) {
                   : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false));
 }
 
+// MXFP4 scales.  The scaled conversion multiplies by 2^(e - 127), e the exponent field of its
+// f32 scale, and reads no other bit of it (measured over every exponent 101..140, the range of
+// fp16 data, with sign and mantissa bits set and clear); the products are exact, subnormal fp16
+// results included.  So an E8M0 byte only has to be moved into bits 23..30: one shift, whatever
+// lands in the other bits.
+__device__ __forceinline__ float e8m0_f32(uint32_t d, int k) {
+  return __uint_as_float(k == 3 ? d >> 1 : d << (23 - 8 * k));
+}
+// 8 E2M1 codes of one word (nibble order) times the power-of-two scale X
+__device__ __forceinline__ half8_t unpack_mx(uint32_t x, float X) {
+  return h8(as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, X, 0)), as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, X, 1)),
+            as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, X, 2)), as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, X, 3)));
+}
+// MXFP4 V of dim block m: byte 8m + e of the lane string holds slot e at dims 16(2m) + c (low
+// nibble) and 16(2m+1) + c (high nibble), under the slot's own scale.  Each byte converts under
+// its scale into (tile 2m, tile 2m+1) of slot e; byte permutes regroup the halves into the
+// operands of tile 2m (lo[0..3]: slots (0,1), (2,3), (4,5), (6,7)) and tile 2m+1 (hi[0..3]).
+__device__ __forceinline__ void mx_v_tiles(uint32_t x0, uint32_t x1, uint32_t s0, uint32_t s1, uint32_t (&lo)[4],
+                                           uint32_t (&hi)[4]) {
+  uint32_t r[8];
+  r[0] = as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x0, e8m0_f32(s0, 0), 0));
+  r[1] = as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x0, e8m0_f32(s0, 1), 1));
+  r[2] = as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x0, e8m0_f32(s0, 2), 2));
+  r[3] = as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x0, e8m0_f32(s0, 3), 3));
+  r[4] = as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x1, e8m0_f32(s1, 0), 0));
+  r[5] = as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x1, e8m0_f32(s1, 1), 1));
+  r[6] = as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x1, e8m0_f32(s1, 2), 2));
+  r[7] = as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x1, e8m0_f32(s1, 3), 3));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo[i] = __builtin_amdgcn_perm(r[2 * i + 1], r[2 * i], 0x05040100u);
+    hi[i] = __builtin_amdgcn_perm(r[2 * i + 1], r[2 * i], 0x07060302u);
+  }
+}
+
 // FP8 word pair -> the 8 values in byte order [w0.b0, w0.b1, w0.b2, w0.b3, w1.b0, ..., w1.b3]
 __device__ __forceinline__ half8_t unpack_fp8(uint32_t w0, uint32_t w1) {
   return h8(e4m3_pair(w0, false), e4m3_pair(w0, true), e4m3_pair(w1, false), e4m3_pair(w1, true));
@@ -500,6 +535,54 @@ __device__ __forceinline__ void fp8_step(const uint8_t *blk, int w, int g, int c
   float p[8];
   softmax_step(st, s, p, valid_head, 0u, sl2);
   const half8_t pb = h8(pk(p[0], p[2]), pk(p[1], p[3]), pk(p[4], p[6]), pk(p[5], p[7]));
+#pragma unroll
+  for (int k = 0; k < 8; ++k) st.o[k] = mfma(va[k], pb, st.o[k]);
+}
+
+// MXFP4: K lanes hold one 32-dim block of one slot, so its codes convert under a single scale
+// (no multiply); V as in mx_v_tiles.
+template <bool TAIL>
+__device__ __forceinline__ void mxfp4_step(const uint8_t *blk, int w, int g, int c, const QOp &q, float sl2,
+                                           bool valid_head, int nvalid, State &st) {
+  const int lane = 16 * g + c;
+  const half8_t (&qb)[4] = q.qb;
+  half8_t va[8];
+  {
+    const uint8_t *vc = blk + kMxVc + (w * 2 * 64 + lane) * 16;
+    const uint4 x0 = *(const uint4 *)vc, x1 = *(const uint4 *)(vc + 1024);
+    const uint4 s01 = *(const uint4 *)(blk + kMxVs + (4 * w + g) * 32);        // [m][e], m = 0, 1
+    const uint4 s23 = *(const uint4 *)(blk + kMxVs + (4 * w + g) * 32 + 16);   // m = 2, 3
+    const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    const uint32_t sw[8] = {s01.x, s01.y, s01.z, s01.w, s23.x, s23.y, s23.z, s23.w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      uint32_t lo[4], hi[4];
+      mx_v_tiles(xw[2 * m], xw[2 * m + 1], sw[2 * m], sw[2 * m + 1], lo, hi);
+      va[2 * m] = h8(lo[0], lo[1], lo[2], lo[3]);
+      va[2 * m + 1] = h8(hi[0], hi[1], hi[2], hi[3]);
+    }
+  }
+  float s[8];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int tl = (2 * w + tt) * 64 + lane;
+    const uint4 x = *(const uint4 *)(blk + tl * 16);                          // dims 32g .. 32g+31 of slot c
+    const float X = e8m0_f32((uint32_t)blk[kMxKs + tl], 0);
+    float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    acc = mfma(unpack_mx(x.x, X), qb[0], acc);
+    acc = mfma(unpack_mx(x.y, X), qb[1], acc);
+    acc = mfma(unpack_mx(x.z, X), qb[2], acc);
+    acc = mfma(unpack_mx(x.w, X), qb[3], acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = acc[i];
+      if (TAIL && 16 * (2 * w + tt) + 4 * g + i >= nvalid) v = kNegInf;
+      s[4 * tt + i] = v;
+    }
+  }
+  float p[8];
+  softmax_step(st, s, p, valid_head, 0u, sl2);
+  const half8_t pb = h8(pk(p[0], p[1]), pk(p[2], p[3]), pk(p[4], p[5]), pk(p[6], p[7]));
 #pragma unroll
   for (int k = 0; k < 8; ++k) st.o[k] = mfma(va[k], pb, st.o[k]);
 }
@@ -921,6 +1004,53 @@ __device__ __forceinline__ void fp8_step2(const uint8_t *blk, int w, int g, int 
 }
 
 template <bool TAIL>
+__device__ __forceinline__ void mxfp4_step2(const uint8_t *blk, int w, int g, int c, const QOp2 &q, float sl2,
+                                            bool valid_head, int nvalid, State &st) {
+  const int lane = 16 * g + c;
+  const int qq = g & 1, sa = g >> 1, sc = c >> 3;
+  const int tau_a = 2 * w + sa, tau_c = 2 * w + sc;
+  const int l0 = tau_a * 64 + 16 * (2 * qq) + c, l1 = l0 + 16;
+  const uint4 x0 = *(const uint4 *)(blk + l0 * 16), x1 = *(const uint4 *)(blk + l1 * 16);
+  const float X0 = e8m0_f32((uint32_t)blk[kMxKs + l0], 0), X1 = e8m0_f32((uint32_t)blk[kMxKs + l1], 0);
+  const uint8_t *vc = blk + kMxVc + (w * 2 * 64 + lane) * 16;
+  const uint4 vx0 = *(const uint4 *)vc, vx1 = *(const uint4 *)(vc + 1024);
+  const uint4 s01 = *(const uint4 *)(blk + kMxVs + (4 * w + g) * 32);
+  const uint4 s23 = *(const uint4 *)(blk + kMxVs + (4 * w + g) * 32 + 16);
+
+  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  acc = mfma(unpack_mx(x0.x, X0), q.qb[0], acc);
+  acc = mfma(unpack_mx(x0.y, X0), q.qb[1], acc);
+  acc = mfma(unpack_mx(x0.z, X0), q.qb[2], acc);
+  acc = mfma(unpack_mx(x0.w, X0), q.qb[3], acc);
+  acc = mfma(unpack_mx(x1.x, X1), q.qb[4], acc);
+  acc = mfma(unpack_mx(x1.y, X1), q.qb[5], acc);
+  acc = mfma(unpack_mx(x1.z, X1), q.qb[6], acc);
+  acc = mfma(unpack_mx(x1.w, X1), q.qb[7], acc);
+  float s[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v = acc[i];
+    if (TAIL && 16 * tau_c + 4 * g + i >= nvalid) v = kNegInf;
+    s[i] = v;
+  }
+  float p[4];
+  softmax_step2(st, s, p, valid_head, 0u, sl2);
+  const uint32_t p01 = pk(p[0], p[1]), p23 = pk(p[2], p[3]);
+  const half4_t pa0 = sc == 0 ? h4(p01, p23) : h4(0u, 0u), pa1 = sc == 1 ? h4(p01, p23) : h4(0u, 0u);
+  const uint32_t xw[8] = {vx0.x, vx0.y, vx0.z, vx0.w, vx1.x, vx1.y, vx1.z, vx1.w};
+  const uint32_t sw[8] = {s01.x, s01.y, s01.z, s01.w, s23.x, s23.y, s23.z, s23.w};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    uint32_t lo[4], hi[4];
+    mx_v_tiles(xw[2 * m], xw[2 * m + 1], sw[2 * m], sw[2 * m + 1], lo, hi);
+    st.o[2 * m] = mfma16(h4(lo[0], lo[1]), pa0, st.o[2 * m]);
+    st.o[2 * m] = mfma16(h4(lo[2], lo[3]), pa1, st.o[2 * m]);
+    st.o[2 * m + 1] = mfma16(h4(hi[0], hi[1]), pa0, st.o[2 * m + 1]);
+    st.o[2 * m + 1] = mfma16(h4(hi[2], hi[3]), pa1, st.o[2 * m + 1]);
+  }
+}
+
+template <bool TAIL>
 __device__ __forceinline__ void fp16_step2(const uint8_t *blk, int w, int g, int c, const QOp2 &q, float sl2,
                                            bool valid_head, int nvalid, State &st) {
   const int lane = 16 * g + c;
@@ -1110,7 +1240,7 @@ __device__ __forceinline__ void residual_part(const DecodeArgs &a, const Item &i
 }
 
 template <int FMT, int NSUB>
-__device__ void stream_segment(const DecodeArgs &a, const DecodeSeg &sg, const Item &it, uint8_t *smem, int *s_chunk, int w,
+__device__ __forceinline__ void stream_segment(const DecodeArgs &a, const DecodeSeg &sg, const Item &it, uint8_t *smem, int *s_chunk, int w,
                                int g, int c, bool valid_head, State &st) {
   const int lane = 16 * g + c;
   const int bb = block_bytes_of(FMT);
@@ -1225,6 +1355,9 @@ __device__ void stream_segment(const DecodeArgs &a, const DecodeSeg &sg, const I
       } else if constexpr (FMT == kFmtFp16) {
         if (full) fp16_step2<false>(blk, w, g, c, q2, sl2, valid_head, nv, st);
         else fp16_step2<true>(blk, w, g, c, q2, sl2, valid_head, nv, st);
+      } else if constexpr (FMT == kFmtMxfp4) {
+        if (full) mxfp4_step2<false>(blk, w, g, c, q2, sl2, valid_head, nv, st);
+        else mxfp4_step2<true>(blk, w, g, c, q2, sl2, valid_head, nv, st);
       } else {
         if (full) affine_step2<FMT, false>(blk, w, g, c, q2, sl2, valid_head, nv, st);
         else affine_step2<FMT, true>(blk, w, g, c, q2, sl2, valid_head, nv, st);
@@ -1239,6 +1372,9 @@ __device__ void stream_segment(const DecodeArgs &a, const DecodeSeg &sg, const I
       } else if constexpr (FMT == kFmtFp16) {
         if (full) fp16_step<false>(blk, w, g, c, q, sl2, valid_head, nv, st);
         else fp16_step<true>(blk, w, g, c, q, sl2, valid_head, nv, st);
+      } else if constexpr (FMT == kFmtMxfp4) {
+        if (full) mxfp4_step<false>(blk, w, g, c, q, sl2, valid_head, nv, st);
+        else mxfp4_step<true>(blk, w, g, c, q, sl2, valid_head, nv, st);
       } else {
         if (full) affine_step<FMT, false>(blk, w, g, c, q, sl2, valid_head, nv, st);
         else affine_step<FMT, true>(blk, w, g, c, q, sl2, valid_head, nv, st);
@@ -1335,6 +1471,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
       case kFmtInt8: stream_segment<kFmtInt8, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
       case kFmtFp8: stream_segment<kFmtFp8, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
       case kFmtFp16: stream_segment<kFmtFp16, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
+      case kFmtMxfp4: stream_segment<kFmtMxfp4, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
       default: stream_segment<kFmtNvfp4, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
     }
   }

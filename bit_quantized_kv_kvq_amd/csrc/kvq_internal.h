@@ -12,17 +12,20 @@ constexpr int kHeadDim = 128;   // head_dim supported by the kernels
 constexpr int kBlock = 128;     // token slots per cache block
 constexpr int kGroup = 64;      // affine group (values of one token sharing S, Z)
 constexpr int kNvBlock = 16;    // NVFP4 values sharing one E4M3 scale
+constexpr int kMxBlock = 32;    // MXFP4 values sharing one E8M0 scale
 
 // Format codes (values of kvq_format).
-constexpr int kFmtFp16 = 0, kFmtInt2 = 2, kFmtInt4 = 4, kFmtInt8 = 8, kFmtNvfp4 = 16, kFmtFp8 = 32;
+constexpr int kFmtFp16 = 0, kFmtInt2 = 2, kFmtInt4 = 4, kFmtInt8 = 8, kFmtNvfp4 = 16, kFmtFp8 = 32, kFmtMxfp4 = 64;
 
 // Bytes of one 128-slot block (K and V parts together).
 __host__ __device__ constexpr size_t affine_block_bytes(int nbits) { return 4096u * (size_t)nbits + 2048u; }
 constexpr size_t kNvfp4BlockBytes = 18432;
+constexpr size_t kMxfp4BlockBytes = 17408;
 constexpr size_t kFp8BlockBytes = 32768;
 constexpr size_t kFp16BlockBytes = 65536;
 __host__ __device__ constexpr size_t block_bytes(int fmt) {
   return fmt == kFmtNvfp4 ? kNvfp4BlockBytes
+         : fmt == kFmtMxfp4 ? kMxfp4BlockBytes
          : fmt == kFmtFp8 ? kFp8BlockBytes
          : fmt == kFmtFp16 ? kFp16BlockBytes
                            : affine_block_bytes(fmt);
@@ -37,6 +40,9 @@ constexpr size_t aff_vc(int n) { return 2048u * (size_t)n + 1024u; }
 constexpr size_t aff_vm(int n) { return 4096u * (size_t)n + 1024u; }
 // Offsets inside an NVFP4 block.
 constexpr size_t kNvKs = 8192, kNvVc = 9216, kNvVs = 17408;
+// Offsets inside an MXFP4 block: Kc as NVFP4's, one E8M0 byte per K lane, V bytes pairing
+// dims 16(2m) + c and 16(2m+1) + c of one slot, E8M0 bytes [w][g][m][e].
+constexpr size_t kMxKs = 8192, kMxVc = 8704, kMxVs = 16896;
 // FP8 block: the INT8 code regions (E4M3 bytes), no metadata.
 constexpr size_t kF8Vc = 16384;
 // FP16 block: K lane strings [tile][chunk][lane][16 B], then V at 32768 [part][k][lane][16 B].

@@ -121,11 +121,11 @@ __device__ __forceinline__ uint32_t e2m1_code(float x, float s) {
 // Block layout (128 slots, head_dim 128).  K codes: 4 parts w x 2 tiles u x 64 lanes
 // (g = lane >> 4, c = lane & 15) x 4n bytes (NVFP4 16) of slot 32w + 16u + c, stored in
 // chunks of min(16, 4n) bytes; lane field f holds dim 64(f >> 4) + 16g + (f & 15) (affine)
-// or 32g + f (NVFP4).  V codes: 4 parts w x 64 lanes x 8n bytes in 16-byte chunks; lane
-// field phi holds dim 16k + c and slot 32w + 16(e >> 2) + 4g + (e & 3), (k, e) per format
-// below.
+// or 32g + f (NVFP4, MXFP4).  V codes: 4 parts w x 64 lanes x 8n bytes in 16-byte chunks;
+// lane field phi holds dim 16k + c and slot 32w + 16(e >> 2) + 4g + (e & 3), (k, e) per
+// format below.
 __device__ __forceinline__ int k_lane_dim(int fmt, int g, int f) {
-  return fmt == kFmtNvfp4 ? 32 * g + f : 64 * (f >> 4) + 16 * g + (f & 15);
+  return (fmt == kFmtNvfp4 || fmt == kFmtMxfp4) ? 32 * g + f : 64 * (f >> 4) + 16 * g + (f & 15);
 }
 
 __device__ __forceinline__ void v_field(int fmt, int phi, int &k, int &e) {
@@ -137,6 +137,9 @@ __device__ __forceinline__ void v_field(int fmt, int phi, int &k, int &e) {
     const int u = phi >> 2, b = phi & 3;
     k = u >> 1;
     e = 4 * (u & 1) + 2 * (b & 1) + (b >> 1);
+  } else if (fmt == kFmtMxfp4) {                       // a byte: one slot, dims 16(2m) + c, 16(2m+1) + c
+    k = 2 * (phi >> 4) + (phi & 1);
+    e = (phi >> 1) & 7;
   } else {
     const int v = phi & 7;
     k = phi >> 3;
@@ -195,7 +198,8 @@ __device__ void store_fp16_block(const uint16_t *xs, uint8_t *blkp, int kv, int 
 
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t blk0, int64_t nblk) {
-  constexpr bool kNv = FMT == kFmtNvfp4;
+  constexpr bool kMx = FMT == kFmtMxfp4;
+  constexpr bool kNv = FMT == kFmtNvfp4 || kMx;          // E2M1 codes (NVFP4 or MXFP4 scales)
   constexpr bool kF8 = FMT == kFmtFp8;                   // fixed scale: codes only
   constexpr bool kF16 = FMT == kFmtFp16;                 // the values themselves
   constexpr int kBits = kNv ? 4 : kF8 ? 8 : kF16 ? 16 : FMT;
@@ -205,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
   constexpr size_t kBlockBytes = block_bytes(FMT);
 
   // 34.8 KB of staged tokens and 1-3 KB of metadata: four workgroups fit in a CU
-  constexpr int kMeta = kNv ? 8 : 2;  // affine: S per 64-group; NVFP4: scale per 16-block
+  constexpr int kMeta = kMx ? 4 : kNv ? 8 : 2;  // affine: S per 64-group; NVFP4: per 16; MXFP4: per 32
   constexpr int kAffMeta = kNv ? 1 : 2;
   __shared__ __align__(16) uint16_t xs[kBlock * kRowHalves];
   __shared__ float mS[kBlock][kMeta];
@@ -326,6 +330,45 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
         *(uint16_t *)(m + 16 + 8 * g + 2 * i) = (uint16_t)Zb;
       }
     }
+  } else if constexpr (kMx) {
+    for (int idx = tid; idx < kBlock * 4; idx += kThreads) {
+      const int slot = idx >> 2, m = idx & 3;
+      uint32_t sb = 0;
+      bool write = false;
+      if (slot >= lo && slot < hi) {
+        // amax by an integer max of the magnitude bits; X = 2^(floor(log2 amax) - 2) read off
+        // the fp16 exponent (or the leading mantissa bit of a subnormal)
+        const uint4 *row = (const uint4 *)&xs[slot * kRowHalves + m * kMxBlock];
+        u16x2 m2 = {0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 v = row[i];
+          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, w4[k] & 0x7FFF7FFFu));
+        }
+        const uint32_t amax = m2.x > m2.y ? m2.x : m2.y;
+        float X = 0.0f;
+        if (amax != 0) {
+          const int ebits = (int)(amax >> 10);
+          const int fl = ebits > 0 ? ebits - 15 : (31 - __builtin_clz(amax)) - 24;
+          sb = (uint32_t)(fl - 2 + 127);
+          X = __uint_as_float(sb << 23);
+        }
+        mS[slot][m] = X;
+        write = true;
+      } else if (slot >= hi && slot < zhi) {
+        write = true;
+      }
+      if (write) {
+        if (kv == 0) {
+          blkp[kMxKs + (slot >> 4) * 64 + 16 * m + (slot & 15)] = (uint8_t)sb;
+        } else {
+          const int w = slot >> 5, g = (slot >> 2) & 3, e = 4 * ((slot >> 4) & 1) + (slot & 3);
+          blkp[kMxVs + ((4 * w + g) * 4 + m) * 8 + e] = (uint8_t)sb;
+        }
+      }
+    }
   } else {
     for (int idx = tid; idx < kBlock * 8; idx += kThreads) {
       const int slot = idx >> 3, nb = idx & 7;
@@ -387,7 +430,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
       uint32_t word = 0;
       if (slot < hi) {
         const int d0 = k_lane_dim(FMT, g, omega * F);   // first of F consecutive dims
-        const int grp = d0 / (kNv ? kNvBlock : kGroup);
+        const int grp = d0 / (kMx ? kMxBlock : kNv ? kNvBlock : kGroup);
         const uint16_t *xr = &xs[slot * kRowHalves + d0];
         if constexpr (F >= 8) {
 #pragma unroll
@@ -412,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
     // of dim 16 k + c and slot 32 w + 16 (e >> 2) + 4 g + (e & 3).  A task is (part, g, omega,
     // c0 in {0, 8}): the words of lanes 16 g + c0 .. +7, whose field j reads the same slot at
     // the 8 consecutive dims 16 k + c0 .. +7 (one 16-byte LDS read and one metadata lookup).
-    const size_t vc = kNv ? kNvVc : kF8 ? kF8Vc : aff_vc(kBits);
+    const size_t vc = kMx ? kMxVc : kNv ? kNvVc : kF8 ? kF8Vc : aff_vc(kBits);
     constexpr int kChunks = kBits / 2;              // 16-byte chunks per lane
     constexpr int kLaneWords = 4 * kChunks;
     constexpr int kTasks = 4 * 4 * kLaneWords * 2;
@@ -435,7 +478,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
         any = true;
         if (slot >= hi) continue;                    // cleared: code 0
         const int d0 = 16 * k + c0;
-        const int grp = d0 / (kNv ? kNvBlock : kGroup);
+        const int grp = d0 / (kMx ? kMxBlock : kNv ? kNvBlock : kGroup);
         float x[8];
         unpack8(*(const uint4 *)&xs[slot * kRowHalves + d0], x);
 #pragma unroll
@@ -477,6 +520,7 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t s) {
     case kFmtInt8: quantize_kernel<kFmtInt8><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
     case kFmtNvfp4: quantize_kernel<kFmtNvfp4><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
     case kFmtFp8: quantize_kernel<kFmtFp8><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
+    case kFmtMxfp4: quantize_kernel<kFmtMxfp4><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
     case kFmtFp16: quantize_kernel<kFmtFp16><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
     default: return hipErrorInvalidValue;
   }

@@ -59,6 +59,8 @@ typedef enum {
   KVQ_FMT_INT4 = 4,  /* affine, 4-bit codes */
   KVQ_FMT_INT8 = 8,  /* affine, 8-bit codes */
   KVQ_FMT_NVFP4 = 16, /* E2M1 codes, one E4M3 scale per 16 values */
+  KVQ_FMT_MXFP4 = 64, /* E2M1 codes, one E8M0 power-of-two scale per 32 values (the microscaling
+                         FP4 that page "NVFP4 KV缓存技术详解" §3.2 compares NVFP4 with) */
   KVQ_FMT_FP8 = 32    /* every value cast to E4M3 (scale 1, round to nearest even, saturating
                          at +-448, sign kept): page "KV Cache量化实战：Model Optimizer为大模型长上下文
                          省下50%显存", section on the KV cache formats (FP8 cast with a fixed scale) */
@@ -71,7 +73,8 @@ typedef struct {
   int32_t head_dim;     /* must be 128 */
   int64_t max_tokens;   /* per-sequence capacity, >= 1 */
   int32_t format;       /* kvq_format of the (young) tier ("nbits") */
-  int32_t group_size;   /* 64 for affine formats, 16 for NVFP4, 0 for FP8 and FP16 ("group_size") */
+  int32_t group_size;   /* 64 for affine formats, 16 for NVFP4, 32 for MXFP4, 0 for FP8 and FP16
+                           ("group_size") */
   int32_t residual_len; /* fp16 residual length R: 0 (quantize on append) or a multiple of
                            16 up to 1024 ("residual_length"; 128 in the pages) */
   int32_t old_format;   /* kvq_format of the old tier; ignored when old_after == 0 */

@@ -43,6 +43,8 @@ def _check_blocks(cache, ora: LayerCache, b, h, tier, region):
         kq, vq = quantize_tokens(K[sl], fmt), quantize_tokens(V[sl], fmt)
         if fmt == "nvfp4":
             want = olayout.pack_nvfp4_block(kq, vq, sl.size)
+        elif fmt == "mxfp4":
+            want = olayout.pack_mxfp4_block(kq, vq, sl.size)
         elif fmt == "fp8":
             want = olayout.pack_fp8_block(kq, vq, sl.size)
         elif fmt == "fp16":
@@ -124,6 +126,14 @@ def test_fullsize_long_context_128k_fp8():
 
 def test_fullsize_llama3_70b_gqa8_32k_fp8():
     _run(3, "fp8", n_pairs=2)
+
+
+def test_fullsize_long_context_128k_mxfp4():
+    _run(4, "mxfp4", steps=1, n_pairs=2)
+
+
+def test_fullsize_llama3_70b_gqa8_32k_mxfp4():
+    _run(3, "mxfp4", n_pairs=2)
 
 
 def test_fullsize_long_context_128k_fp16():

@@ -10,7 +10,7 @@ from gpu_helpers import Pair, adversarial_tokens, assert_attention_close
 
 pytestmark = pytest.mark.gpu
 
-FORMATS = ["int2", "int4", "int8", "nvfp4", "fp8", "fp16"]
+FORMATS = ["int2", "int4", "int8", "nvfp4", "mxfp4", "fp8", "fp16"]
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
@@ -60,6 +60,30 @@ def test_nvfp4_every_amax():
     p.check_bytes(0)
 
 
+def test_mxfp4_every_amax():
+    """Every positive finite fp16 value as the maximum of a 32-value block (so every E8M0 scale
+    an fp16 block can have, and the saturating range above 6X), the other 31 values drawn
+    below it, plus signed zeros and all-zero blocks."""
+    rng = np.random.default_rng(6)
+    bits = np.arange(1, 0x7C00, dtype=np.uint16)
+    amax = bits.view(np.float16).astype(np.float64)
+    n_blocks = amax.size + 5
+    frac = rng.uniform(-1, 1, (n_blocks, 32))
+    frac[:amax.size] *= amax[:, None]
+    x = frac.astype(np.float16)
+    x[:amax.size, 0] = amax * np.where(rng.random(amax.size) < 0.5, 1, -1)
+    x[amax.size:] = 0.0
+    x[-1, 3] = -0.0
+    x[::7, 5] = -0.0
+    ntok = -(-n_blocks // 4)
+    flat = np.zeros((ntok * 4, 32), np.float16)
+    flat[:n_blocks] = x
+    toks = flat.reshape(1, 1, ntok, 128)
+    p = Pair(1, 1, 1, ntok + 8, "mxfp4", 0)
+    p.append(0, toks, toks[..., ::-1].copy())
+    p.check_bytes(0)
+
+
 def test_fp8_every_fp16_value():
     """Every finite fp16 value (both zeros, subnormals, the rounding ties between E4M3 values,
     the saturating range above 448) through the FP8 cast, as K and (reversed) as V."""
@@ -75,7 +99,7 @@ def test_fp8_every_fp16_value():
     p.check_bytes(0)
 
 
-@pytest.mark.parametrize("old", ["fp8", "fp16"])
+@pytest.mark.parametrize("old", ["fp8", "fp16", "mxfp4"])
 def test_tier_under_int4(old):
     """FP8 or FP16 as the older tier below an INT4 young tier: bytes of both tiers and the
     decode (one call streams two block formats)."""
