@@ -138,6 +138,57 @@ def read_probe_gbs() -> float:
     return best
 
 
+NOISE_FORMATS = ("int8", "fp8", "nvfp4", "mxfp4", "int4", "int2")
+
+
+def noise_study(lengths, n_queries: int):
+    """Quantization noise of each cache format against sequence length (the comparison of
+    page "NVFP4 KV缓存技术详解" §3.2, NVFP4 against MXFP4 over long sequences, on synthetic data).
+
+    For the K distributions of the 128K workload (Student-t, nu = 4) and of the 32K NVFP4 workload
+    (Gaussian, 3 outlier channels x20), V Gaussian: one sequence of 8 kv heads grows through the
+    given lengths; at each length every format's cache (residual 0: every token quantized)
+    answers the same n_queries decode calls of 32 query heads (GQA 4), and the error is
+    ||o_fmt - o_fp16|| / ||o_fp16|| over heads and queries, o_fp16 being the same kernel on the
+    fp16 cache (itself within the parity tolerance of exact attention).  One JSON line per K
+    distribution."""
+    import torch
+    import bit_quantized_kv_kvq_amd as kvq
+    import kvq_synth as syn
+    sigma = 1.0 / np.sqrt(128.0)
+    H, G = 8, 4
+    Lmax = max(lengths)
+    for cid in (4, 3):
+        W = syn.WORKLOADS[cid]
+        k = syn.draw_k_dev(cid, 0, 1, H, Lmax, W.kdist)
+        v = syn.draw_v_dev(cid, 0, 1, H, Lmax)
+        qs = [syn.draw_q_dev(cid, 0, 1, H * G, s) for s in range(n_queries)]
+        outs = {}
+        for fmt in ("fp16",) + NOISE_FORMATS:
+            cache = kvq.Cache(kvq.make_config(1, 1, H, Lmax, fmt, 0))
+            ws = torch.empty(cache.workspace_bytes(H * G), dtype=torch.uint8, device="cuda")
+            done = 0
+            for L in sorted(lengths):
+                cache.append(0, k[:, :, done:L].contiguous(), v[:, :, done:L].contiguous())
+                done = L
+                o = torch.empty((n_queries, H * G, 128), dtype=torch.float32, device="cuda")
+                for i, q in enumerate(qs):
+                    cache.decode(0, q, sigma, o[i:i + 1], ws)
+                outs[(fmt, L)] = o.double()
+            torch.cuda.synchronize()
+            del cache, ws
+        errs = {fmt: {str(L): float((outs[(fmt, L)] - outs[("fp16", L)]).norm() / outs[("fp16", L)].norm())
+                      for L in lengths} for fmt in NOISE_FORMATS}
+        kd = W.kdist
+        desc = (f"student-t nu={kd.nu:g}" if kd.kind == "student_t" else "normal") + \
+            (f", {kd.outlier_channels} outlier channels x{kd.outlier_scale:g}" if kd.outlier_channels else "")
+        print(json.dumps({"study": "decode output error vs fp16 cache", "k_distribution": desc,
+                          "lengths": list(lengths), "queries": n_queries, "kv_heads": H, "gqa": G,
+                          "relative_error": errs}), flush=True)
+        del k, v, qs, outs
+        torch.cuda.empty_cache()
+
+
 def log(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -152,6 +203,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--cpu-pairs", type=int, default=48, help="(batch, kv_head) pairs of layer 0 kept for the oracle")
     ap.add_argument("--probe", choices=["copy"], default=None)
+    ap.add_argument("--study", choices=["noise"], default=None,
+                    help="noise: decode error of every format against the fp16 cache vs cached length")
+    ap.add_argument("--study-lengths", default="1024,4096,16384,65536,131072")
+    ap.add_argument("--study-queries", type=int, default=8)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -163,6 +218,9 @@ def main():
     import torch
     if args.probe == "copy":
         copy_probe()
+        return
+    if args.study == "noise":
+        noise_study([int(x) for x in args.study_lengths.split(",")], args.study_queries)
         return
 
     import bit_quantized_kv_kvq_amd as kvq
