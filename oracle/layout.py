@@ -17,12 +17,18 @@ occupies bits [f*n, f*n + n) of the byte string, bit b of the string being bit
 Kc (2048n bytes; NVFP4 8192): 4 parts w x 2 tiles u x 64 lanes L (g = L div 16,
     c = L mod 16), each lane holding 4n bytes (NVFP4 16) of slot t = 32w + 16u + c:
     the field string of 32 fields, field f holding the code of dim
-    64(f div 16) + 16g + (f mod 16) (affine) or of dim 32g + f (NVFP4).  Lane data
+    64(f div 16) + 16g + (f mod 16) (affine, groups of 64 or 128) or of dim 32g + f (NVFP4).
+    Affine groups of 32: field f holds dim 32j + 8g + e, where (j, e) is f's place among the
+    decode kernel's MFMA operands (step j, element e; every step then covers one group):
+      INT4: j = f div 8, r = f mod 8, e = 2(r mod 4) + r div 4
+      INT8: j = f div 8, r = f mod 8, e = 4(r div 4) + 2(r mod 2) + (r div 2) mod 2
+      INT2: j = 2(f div 16) + (f div 4) mod 2, r = f mod 16, e = 2(r mod 4) + r div 8  Lane data
     is stored in chunks of min(16, 4n) bytes: chunk r of lane L of (w, u) at
     (((2w + u)*K + r)*64 + L)*min(16, 4n), K = 4n / min(16, 4n) (INT2 8-byte
     chunks, INT4 and NVFP4 one 16-byte chunk, INT8 two 16-byte chunks).
-Km, affine (1024 bytes): 8 tiles tau of 128 bytes (slots 16tau + r, r = 0..15):
-    fp16 S at tau*128 + 4r + 2G, fp16 Z at tau*128 + 64 + 4r + 2G.
+Km, affine (512 NG bytes, NG = 128/g groups per token): 8 tiles tau of 64 NG bytes (slots
+    16tau + r, r = 0..15): fp16 S of group G at tau*64NG + 2(NG r + G), fp16 Z at
+    tau*64NG + 32NG + 2(NG r + G) (NG = 2: S at tau*128 + 4r + 2G, Z 64 bytes later).
 Km, NVFP4 (1024 bytes): 2 bytes per (w, u, L) at ((2w + u)*64 + L)*2: the E4M3
     scales of dims 32g..32g+15 and 32g+16..32g+31 of slot 32w + 16u + c.
 Vc (2048n bytes; NVFP4 8192): 4 parts w, each 64 lanes L (g = L div 16,
@@ -36,9 +42,9 @@ Vc (2048n bytes; NVFP4 8192): 4 parts w, each 64 lanes L (g = L div 16,
              e = 2(m mod 4) + m div 8
       INT8:  u = phi div 4, b = phi mod 4, k = u div 2,
              e = 4(u mod 2) + 2(b mod 2) + b div 2
-Vm, affine (1024 bytes): 8 tiles tau x 4 quarters g of 32 bytes at (4tau + g)*32:
-    fp16 S of group 0 for slots 16tau + 4g + i (i = 0..3), then S of group 1,
-    then Z of group 0, then Z of group 1.
+Vm, affine (512 NG bytes): 8 tiles tau x 4 quarters g of 16 NG bytes at (4tau + g)*16NG:
+    fp16 S of group G for slots 16tau + 4g + i (i = 0..3) at 8G + 2i, then the Z likewise
+    from 8NG (NG = 2: S of group 0, S of group 1, Z of group 0, Z of group 1).
 Vm, NVFP4 (1024 bytes): byte ((4w + g)*8 + k)*8 + e = E4M3 scale of dims
     16k..16k+15 of slot 32w + 16(e div 4) + 4g + (e mod 4).
 
@@ -68,12 +74,14 @@ from __future__ import annotations
 
 import numpy as np
 
+from .quant import affine_params
+
 D = 128
 BLOCK = 128
 
 
-def affine_block_bytes(n: int) -> int:
-    return 4096 * n + 2048
+def affine_block_bytes(n: int, gs: int = 64) -> int:
+    return 4096 * n + 1024 * (128 // gs)
 
 
 NVFP4_BLOCK_BYTES = 18432
@@ -91,7 +99,8 @@ def block_bytes(fmt: str) -> int:
         return FP8_BLOCK_BYTES
     if fmt == "fp16":
         return FP16_BLOCK_BYTES
-    return affine_block_bytes(int(fmt[3:]))
+    n, gs = affine_params(fmt)
+    return affine_block_bytes(n, gs)
 
 
 def k_lane_dims(fmt: str, g: int) -> np.ndarray:
@@ -99,6 +108,19 @@ def k_lane_dims(fmt: str, g: int) -> np.ndarray:
     f = np.arange(32)
     if fmt in ("nvfp4", "mxfp4", "fp16"):
         return 32 * g + f
+    ap = affine_params(fmt)
+    if ap and ap[1] == 32:
+        n = ap[0]
+        if n == 2:
+            j, r = 2 * (f // 16) + (f // 4) % 2, f % 16
+            e = 2 * (r % 4) + r // 8
+        elif n == 4:
+            j, r = f // 8, f % 8
+            e = 2 * (r % 4) + r // 4
+        else:
+            j, r = f // 8, f % 8
+            e = 4 * (r // 4) + 2 * (r % 2) + (r // 2) % 2
+        return 32 * j + 8 * g + e
     return 64 * (f // 16) + 16 * g + f % 16
 
 
@@ -121,17 +143,17 @@ def _pack_kc(fmt: str, codes_k: np.ndarray) -> np.ndarray:
 def v_lane_fields(fmt: str) -> tuple[np.ndarray, np.ndarray]:
     """Vc lane field string: field phi (0..63) -> (dim tile k, operand position e)."""
     phi = np.arange(64)
-    if fmt in ("int4", "nvfp4", "fp16"):
+    if fmt in ("nvfp4", "fp16") or (affine_params(fmt) or (0,))[0] == 4:
         k, v = phi // 8, phi % 8
-        e = 2 * (v % 4) + v // 4 if fmt == "int4" else v
+        e = v if fmt in ("nvfp4", "fp16") else 2 * (v % 4) + v // 4
     elif fmt == "mxfp4":
         k = 2 * (phi // 16) + phi % 2
         e = (phi // 2) % 8
-    elif fmt == "int2":
+    elif (affine_params(fmt) or (0,))[0] == 2:
         u, m = phi // 16, phi % 16
         k = 2 * u + (m // 4) % 2
         e = 2 * (m % 4) + m // 8
-    elif fmt in ("int8", "fp8"):
+    elif fmt == "fp8" or (affine_params(fmt) or (0,))[0] == 8:
         u, b = phi // 4, phi % 4
         k = u // 2
         e = 4 * (u % 2) + 2 * (b % 2) + b // 2
@@ -147,7 +169,7 @@ def lane_slot(w: int, g: int, e) -> np.ndarray:
 
 
 def code_bits(fmt: str) -> int:
-    return {"nvfp4": 4, "mxfp4": 4, "fp8": 8, "fp16": 16}.get(fmt) or int(fmt[3:])
+    return {"nvfp4": 4, "mxfp4": 4, "fp8": 8, "fp16": 16}.get(fmt) or affine_params(fmt)[0]
 
 
 def pack_fields(fields: np.ndarray, n: int) -> np.ndarray:
@@ -185,32 +207,33 @@ def _pack_vc(fmt: str, codes_v: np.ndarray) -> np.ndarray:
     return out.ravel()
 
 
-def pack_affine_block(n: int, kq: dict, vq: dict, used: int) -> np.ndarray:
-    """One affine block.  kq/vq: quantize_tokens() output for the block's slots
-    (arrays of length `used` <= 128); slots >= used are all-zero bytes."""
-    fmt = f"int{n}"
+def pack_affine_block(n: int, kq: dict, vq: dict, used: int, gs: int = 64) -> np.ndarray:
+    """One affine block with groups of gs values.  kq/vq: quantize_tokens() output for the
+    block's slots (arrays of length `used` <= 128); slots >= used are all-zero bytes."""
+    fmt = f"int{n}" if gs == 64 else f"int{n}g{gs}"
+    ng = D // gs
     codes_k = np.zeros((BLOCK, D), np.uint8); codes_k[:used] = kq["codes"]
     codes_v = np.zeros((BLOCK, D), np.uint8); codes_v[:used] = vq["codes"]
-    Sk = np.zeros((BLOCK, 2), np.float16); Sk[:used] = kq["S"]
-    Zk = np.zeros((BLOCK, 2), np.float16); Zk[:used] = kq["Z"]
-    Sv = np.zeros((BLOCK, 2), np.float16); Sv[:used] = vq["S"]
-    Zv = np.zeros((BLOCK, 2), np.float16); Zv[:used] = vq["Z"]
+    Sk = np.zeros((BLOCK, ng), np.float16); Sk[:used] = kq["S"]
+    Zk = np.zeros((BLOCK, ng), np.float16); Zk[:used] = kq["Z"]
+    Sv = np.zeros((BLOCK, ng), np.float16); Sv[:used] = vq["S"]
+    Zv = np.zeros((BLOCK, ng), np.float16); Zv[:used] = vq["Z"]
 
     kc = _pack_kc(fmt, codes_k)
+    # per tile: S of (slot r, group G) in order NG r + G, then the Z likewise
     km = np.concatenate([np.concatenate([f16_bytes(Sk[16 * t:16 * t + 16].ravel()),
                                          f16_bytes(Zk[16 * t:16 * t + 16].ravel())]) for t in range(8)])
     vc = _pack_vc(fmt, codes_v)
-    vm = np.zeros(1024, np.uint8)
+    vm = np.zeros(512 * ng, np.uint8)
     for t in range(8):
         for g in range(4):
             slots = 16 * t + 4 * g + np.arange(4)
-            e = (4 * t + g) * 32
-            vm[e:e + 8] = f16_bytes(Sv[slots, 0])
-            vm[e + 8:e + 16] = f16_bytes(Sv[slots, 1])
-            vm[e + 16:e + 24] = f16_bytes(Zv[slots, 0])
-            vm[e + 24:e + 32] = f16_bytes(Zv[slots, 1])
+            base = (4 * t + g) * 16 * ng
+            for G in range(ng):
+                vm[base + 8 * G:base + 8 * G + 8] = f16_bytes(Sv[slots, G])
+                vm[base + 8 * ng + 8 * G:base + 8 * ng + 8 * G + 8] = f16_bytes(Zv[slots, G])
     out = np.concatenate([kc, km, vc, vm])
-    assert out.size == affine_block_bytes(n)
+    assert out.size == affine_block_bytes(n, gs)
     return out
 
 
@@ -294,7 +317,8 @@ def pack_arena(fmt: str, kq: dict, vq: dict) -> np.ndarray:
         elif fmt == "fp16":
             blocks.append(pack_fp16_block(sl, sv, hi - lo))
         else:
-            blocks.append(pack_affine_block(int(fmt[3:]), sl, sv, hi - lo))
+            n, gs = affine_params(fmt)
+            blocks.append(pack_affine_block(n, sl, sv, hi - lo, gs))
     if not blocks:
         return np.zeros((0, block_bytes(fmt)), np.uint8)
     return np.stack(blocks)

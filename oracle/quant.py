@@ -4,7 +4,9 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Affine (asymmetric) quantization -- page "KV缓存量化技术：提升大模型长文本生成效率"
 (rkmt.cn/news/1711363) §2.1: S = (max - min) / (2^n - 1), Z = round(-min / S),
-one (S, Z) per group of 64 elements, codes stored as n-bit integers.  The page
+one (S, Z) per group of 64 elements, codes stored as n-bit integers.  The same page's §4.3
+debugging configuration uses groups of 32 (and a 256-token residual); groups of 32, 64 and 128
+contiguous head_dim values are supported, named "int4g32", "int4" (64) and "int4g128".  The page
 prints the code as round(X/S) - Z; with Z = round(-min/S) that sends min to
 about -2Z, outside [0, 2^n - 1].  The reading adopted here is the one under which
 codes land in [0, 2^n - 1]:
@@ -50,6 +52,8 @@ E2M1_RNE(min(|x| / s, 6)); decode x_hat = e2m1(code) * s.
 """
 from __future__ import annotations
 
+import re
+
 import numpy as np
 
 from .numerics import (f16, f16_saturate, e4m3_encode, e4m3_decode, e2m1_encode, e2m1_decode, e4m3_cast,
@@ -61,15 +65,23 @@ MX_BLOCK = 32
 E2M1_EMAX = 2            # exponent of E2M1's largest magnitude, 6 = 1.5 * 2^2
 
 
-def affine_quantize(x16: np.ndarray, nbits: int):
-    """Quantize groups of 64 along the last axis.
+def affine_params(fmt: str):
+    """(code bits, group size) of an affine format name ("int4", "int2g32", "int8g128"), else None."""
+    m = re.fullmatch(r"int([248])(?:g(32|64|128))?", fmt)
+    if not m:
+        return None
+    return int(m.group(1)), int(m.group(2) or GROUP)
 
-    x16: fp16 [..., 64].  Returns (codes uint8 [..., 64], S fp16 [...], Z fp16 [...]).
+
+def affine_quantize(x16: np.ndarray, nbits: int):
+    """Quantize groups along the last axis (one group per row of the last axis).
+
+    x16: fp16 [..., g].  Returns (codes uint8 [..., g], S fp16 [...], Z fp16 [...]).
     """
     if nbits not in (2, 4, 8):
         raise ValueError(nbits)
     x = np.asarray(x16, dtype=np.float16).astype(np.float64)
-    assert x.shape[-1] == GROUP
+    assert x.shape[-1] in (32, 64, 128)
     qmax = (1 << nbits) - 1
     mn = x.min(axis=-1)
     mx = x.max(axis=-1)
@@ -132,7 +144,7 @@ def quantize_tokens(x16: np.ndarray, fmt: str):
     """Quantize token rows of head_dim 128: x16 fp16 [N, 128].
 
     Returns a dict with the stored fields:
-      affine: codes [N,128], S [N,2], Z [N,2]
+      affine: codes [N,128], S [N,128/g], Z [N,128/g] (g the group size)
       nvfp4 : codes [N,128], scale [N,8]
       mxfp4 : codes [N,128], scale [N,4] (E8M0 bytes)
       fp8   : codes [N,128] (E4M3 bytes)
@@ -140,9 +152,10 @@ def quantize_tokens(x16: np.ndarray, fmt: str):
     """
     x16 = np.asarray(x16, dtype=np.float16)
     N, D = x16.shape
-    if fmt in ("int2", "int4", "int8"):
-        nb = int(fmt[3:])
-        q, S, Z = affine_quantize(x16.reshape(N, D // GROUP, GROUP), nb)
+    ap = affine_params(fmt)
+    if ap:
+        nb, gs = ap
+        q, S, Z = affine_quantize(x16.reshape(N, D // gs, gs), nb)
         return {"codes": q.reshape(N, D), "S": S, "Z": Z}
     if fmt == "nvfp4":
         c, s = nvfp4_quantize(x16.reshape(N, D // NV_BLOCK, NV_BLOCK))
@@ -161,8 +174,10 @@ def dequantize_tokens(qt: dict, fmt: str) -> np.ndarray:
     """float64 [N, 128] decoded values of quantize_tokens()' output."""
     codes = qt["codes"]
     N, D = codes.shape
-    if fmt in ("int2", "int4", "int8"):
-        return affine_dequantize(codes.reshape(N, D // GROUP, GROUP), qt["S"], qt["Z"]).reshape(N, D)
+    ap = affine_params(fmt)
+    if ap:
+        gs = ap[1]
+        return affine_dequantize(codes.reshape(N, D // gs, gs), qt["S"], qt["Z"]).reshape(N, D)
     if fmt == "nvfp4":
         return nvfp4_dequantize(codes.reshape(N, D // NV_BLOCK, NV_BLOCK), qt["scale"]).reshape(N, D)
     if fmt == "mxfp4":

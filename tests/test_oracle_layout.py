@@ -5,9 +5,14 @@ import os
 import numpy as np
 import pytest
 
-from oracle import layout
+from oracle import layout, quant
 
 GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "layout_cases.json")))
+
+
+def _ng(fmt):
+    ap = quant.affine_params(fmt)
+    return 128 // ap[1] if ap else 0
 
 
 def _empty(fmt):
@@ -19,8 +24,8 @@ def _empty(fmt):
         return {"codes": np.zeros((128, 128), np.uint8), "scale": np.zeros((128, 8), np.uint8)}
     if fmt == "mxfp4":
         return {"codes": np.zeros((128, 128), np.uint8), "scale": np.zeros((128, 4), np.uint8)}
-    return {"codes": np.zeros((128, 128), np.uint8), "S": np.zeros((128, 2), np.float16),
-            "Z": np.zeros((128, 2), np.float16)}
+    return {"codes": np.zeros((128, 128), np.uint8), "S": np.zeros((128, _ng(fmt)), np.float16),
+            "Z": np.zeros((128, _ng(fmt)), np.float16)}
 
 
 def _pack(fmt, kq, vq):
@@ -32,7 +37,8 @@ def _pack(fmt, kq, vq):
         return layout.pack_nvfp4_block(kq, vq, 128)
     if fmt == "mxfp4":
         return layout.pack_mxfp4_block(kq, vq, 128)
-    return layout.pack_affine_block(int(fmt[3:]), kq, vq, 128)
+    n, gs = quant.affine_params(fmt)
+    return layout.pack_affine_block(n, kq, vq, 128, gs)
 
 
 @pytest.mark.parametrize("case", GOLDEN["cases"], ids=lambda c: f"{c['fmt']}-{c['part']}-{c['slot']}-{c['dim']}")
@@ -79,7 +85,8 @@ def test_residual_positions(case):
     assert list(np.flatnonzero(data)) == [case["byte"] + 1]
 
 
-@pytest.mark.parametrize("fmt", ["int2", "int4", "int8", "nvfp4", "mxfp4", "fp8", "fp16"])
+@pytest.mark.parametrize("fmt", ["int2", "int4", "int8", "int2g32", "int4g32", "int8g32", "int4g128",
+                                 "nvfp4", "mxfp4", "fp8", "fp16"])
 def test_v_lane_fields_cover_every_slot_and_dim_once(fmt):
     """Every (slot, dim) of the block is held by exactly one (part, lane, field), and each
     lane's 8 operand positions e are the slots 16(e div 4) + 4g + (e mod 4) of its part."""
@@ -95,28 +102,34 @@ def test_v_lane_fields_cover_every_slot_and_dim_once(fmt):
         assert sorted(e[k == kk]) == list(range(8))
 
 
-@pytest.mark.parametrize("fmt", ["int2", "int4", "int8", "nvfp4", "mxfp4", "fp8", "fp16"])
+@pytest.mark.parametrize("fmt", ["int2", "int4", "int8", "int2g32", "int4g32", "int8g32", "int4g128",
+                                 "nvfp4", "mxfp4", "fp8", "fp16"])
 def test_k_lane_dims_cover_every_dim_once_per_slot(fmt):
     """The four lane quarters of a slot hold all 128 dims once; in affine formats each
     16-field half of a lane lies in one 64-dim group."""
     d = np.concatenate([layout.k_lane_dims(fmt, g) for g in range(4)])
     assert sorted(d) == list(range(128))
-    if fmt not in ("nvfp4", "mxfp4", "fp16"):
+    ap = quant.affine_params(fmt)
+    if ap and ap[1] != 32:
         f = np.arange(32)
         for g in range(4):
             assert np.all(layout.k_lane_dims(fmt, g) // 64 == f // 16)
+    if ap and ap[1] == 32:
+        # quarter g holds the dims 32j + 8g .. 32j + 8g + 7 of every 32-dim group j
+        for g in range(4):
+            assert np.all((layout.k_lane_dims(fmt, g) % 32) // 8 == g)
 
 
 def test_every_bit_of_a_block_is_reachable_once():
     """Setting all codes/meta to all-ones fills every byte of the block with 0xFF
     (no gaps, and codes of different elements never share bits)."""
-    for fmt in ("int2", "int4", "int8"):
-        n = int(fmt[3:])
+    for fmt in ("int2", "int4", "int8", "int2g32", "int4g32", "int8g32", "int2g128", "int4g128", "int8g128"):
+        n, gs = quant.affine_params(fmt)
         full = {"codes": np.full((128, 128), (1 << n) - 1, np.uint8),
-                "S": np.full((128, 2), np.uint16(0xFFFF).view(np.float16)),
-                "Z": np.full((128, 2), np.uint16(0xFFFF).view(np.float16))}
-        blk = layout.pack_affine_block(n, full, full, 128)
-        assert np.all(blk == 0xFF) and blk.size == layout.affine_block_bytes(n)
+                "S": np.full((128, 128 // gs), np.uint16(0xFFFF).view(np.float16)),
+                "Z": np.full((128, 128 // gs), np.uint16(0xFFFF).view(np.float16))}
+        blk = layout.pack_affine_block(n, full, full, 128, gs)
+        assert np.all(blk == 0xFF) and blk.size == layout.affine_block_bytes(n, gs)
     full = {"codes": np.full((128, 128), 15, np.uint8), "scale": np.full((128, 8), 0xFF, np.uint8)}
     blk = layout.pack_nvfp4_block(full, full, 128)
     assert np.all(blk == 0xFF) and blk.size == layout.NVFP4_BLOCK_BYTES

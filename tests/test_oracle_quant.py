@@ -8,28 +8,29 @@ import pytest
 from oracle import quant, numerics as nm
 
 
-def _groups(seed, n=400):
-    """Random and adversarial fp16 groups of 64."""
+def _groups(seed, n=400, w=64):
+    """Random and adversarial fp16 groups of w values."""
     r = np.random.default_rng(seed)
-    gs = [r.standard_normal((n, 64)),
-          r.standard_normal((n // 4, 64)) * 15.0,
-          r.standard_t(4, (n // 4, 64)),
-          r.uniform(3.0, 3.01, (n // 8, 64)),            # narrow, not straddling 0
-          -r.uniform(100, 101, (n // 8, 64)),
-          r.standard_normal((n // 8, 64)) * 1e-6,       # subnormal territory
-          np.clip(r.standard_normal((n // 8, 64)) * 40000, -65504, 65504)]
-    two = np.where(r.random((n // 8, 64)) < 0.5, -1.25, 2.5); two[:, 0] = -1.25; two[:, 1] = 2.5
+    gs = [r.standard_normal((n, w)),
+          r.standard_normal((n // 4, w)) * 15.0,
+          r.standard_t(4, (n // 4, w)),
+          r.uniform(3.0, 3.01, (n // 8, w)),            # narrow, not straddling 0
+          -r.uniform(100, 101, (n // 8, w)),
+          r.standard_normal((n // 8, w)) * 1e-6,       # subnormal territory
+          np.clip(r.standard_normal((n // 8, w)) * 40000, -65504, 65504)]
+    two = np.where(r.random((n // 8, w)) < 0.5, -1.25, 2.5); two[:, 0] = -1.25; two[:, 1] = 2.5
     gs.append(two)
-    ties = np.round(r.standard_normal((n // 8, 64)) * 8) / 2   # many half-integers
+    ties = np.round(r.standard_normal((n // 8, w)) * 8) / 2   # many half-integers
     gs.append(ties)
     return np.concatenate(gs).astype(np.float16)
 
 
+@pytest.mark.parametrize("w", [32, 64, 128])
 @pytest.mark.parametrize("nbits", [2, 4, 8])
-def test_codes_are_brute_force_nearest(nbits):
+def test_codes_are_brute_force_nearest(nbits, w):
     """Each code is the nearest valid code: argmin over q in [0, 2^n-1] of |x - S(q - Z)|,
     ties broken towards even q - Z (round half to even of x/S)."""
-    g = _groups(nbits)
+    g = _groups(nbits, w=w)
     q, S, Z = quant.affine_quantize(g, nbits)
     qmax = (1 << nbits) - 1
     cand = np.arange(qmax + 1, dtype=np.float64)
@@ -43,9 +44,10 @@ def test_codes_are_brute_force_nearest(nbits):
     assert np.array_equal(q.astype(np.int64), expect)
 
 
+@pytest.mark.parametrize("w", [32, 64, 128])
 @pytest.mark.parametrize("nbits", [2, 4, 8])
-def test_scale_and_zero_exact_rational(nbits):
-    g = _groups(10 + nbits, 200)
+def test_scale_and_zero_exact_rational(nbits, w):
+    g = _groups(10 + nbits, 200, w)
     q, S, Z = quant.affine_quantize(g, nbits)
     qmax = (1 << nbits) - 1
     for row, s, z in zip(g, S, Z):
@@ -70,9 +72,10 @@ def test_scale_and_zero_exact_rational(nbits):
         assert float(z) == float(np.float16(zi)), (float(mn), float(s), zi)
 
 
+@pytest.mark.parametrize("w", [32, 64, 128])
 @pytest.mark.parametrize("nbits", [2, 4, 8])
-def test_invariants(nbits):
-    g = _groups(20 + nbits)
+def test_invariants(nbits, w):
+    g = _groups(20 + nbits, w=w)
     q, S, Z = quant.affine_quantize(g, nbits)
     qmax = (1 << nbits) - 1
     x = g.astype(np.float64)
@@ -209,3 +212,24 @@ def test_mxfp4_saturation_and_zero_block():
     assert sb[0] == 127 and codes[0, 0] == 7 and codes[0, 1] == 8 + 5
     assert mxfp4_dequantize(codes, sb)[0, 0] == 6.0
     assert sb[1] == 0 and codes[1, 5] == 8 and not codes[1, :5].any()
+
+
+@pytest.mark.parametrize("fmt", ["int4g32", "int2g32", "int8g128", "int4"])
+def test_token_groups_are_contiguous_head_dim_runs(fmt):
+    """quantize_tokens splits each token's 128 values into 128/g runs of g contiguous dims."""
+    n, gs = quant.affine_params(fmt)
+    x = _groups(5, 64, 128)
+    qt = quant.quantize_tokens(x, fmt)
+    assert qt["S"].shape == (x.shape[0], 128 // gs)
+    for G in range(128 // gs):
+        q, S, Z = quant.affine_quantize(x[:, gs * G:gs * (G + 1)], n)
+        assert np.array_equal(qt["codes"][:, gs * G:gs * (G + 1)], q)
+        assert np.array_equal(qt["S"][:, G], S) and np.array_equal(qt["Z"][:, G], Z)
+
+
+def test_affine_format_names():
+    assert quant.affine_params("int4") == (4, 64)
+    assert quant.affine_params("int2g32") == (2, 32)
+    assert quant.affine_params("int8g128") == (8, 128)
+    for bad in ("int3", "int4g16", "nvfp4", "fp8", "int4g"):
+        assert quant.affine_params(bad) is None

@@ -45,6 +45,10 @@ def test_stored_bytes_include_metadata():
     assert sizes.stored_bytes_per_token("int8") == 2 * 128 * 8.5 / 8
     assert sizes.stored_bytes_per_token("fp16") == 512
     assert sizes.stored_bytes_per_token("fp8") == 256            # fixed scale: no metadata
+    # groups of 32 / 128: one fp16 (S, Z) pair per 32 / 128 values = 5 / 4.25 bits for INT4
+    assert sizes.stored_bytes_per_token("int4g32") == 2 * 128 * 5 / 8
+    assert sizes.stored_bytes_per_token("int4g128") == 2 * 128 * 4.25 / 8
+    assert sizes.stored_bytes_per_token("int2g32") == 2 * 128 * 3 / 8
     # MXFP4: 4-bit codes + one byte per 32 values = 4.25 bits
     assert sizes.stored_bytes_per_token("mxfp4") == 2 * 128 * 4.25 / 8
     # the page's FP8 row: 32 layers / 8 kv heads / 32K tokens at one byte per value = 2 GiB
