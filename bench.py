@@ -36,14 +36,18 @@ DECODE_SRC = os.path.join(ROOT, "bit_quantized_kv_kvq_amd", "csrc", "kvq_decode.
 WORKLOADS = {
     "c1": (1, None), "c2": (2, None), "c3": (3, None),
     "c4-int4": (4, "int4"), "c4-int2": (4, "int2"), "c5": (5, None),
+    "c4-int4g32": (4, "int4g32"), "c4-int4g128": (4, "int4g128"),
     "c3-mxfp4": (3, "mxfp4"), "c4-mxfp4": (4, "mxfp4"), "c3-fp8": (3, "fp8"), "c4-fp8": (4, "fp8"), "c3-fp16": (3, "fp16"), "c4-fp16": (4, "fp16"),
 }
 
 
 def bytes_per_token(fmt: str) -> float:
     """Stored bytes of one token of one (batch, kv_head), K and V together."""
-    return {"int2": 10240 / 128, "int4": 18432 / 128, "int8": 34816 / 128, "nvfp4": 18432 / 128, "mxfp4": 17408 / 128,
-            "fp8": 32768 / 128, "fp16": 512.0}[fmt]
+    m = re.fullmatch(r"int([248])(?:g(32|64|128))?", fmt)
+    if m:   # n-bit codes + one fp16 (S, Z) pair per group of K and of V
+        n, gs = int(m.group(1)), int(m.group(2) or 64)
+        return (4096 * n + 1024 * (128 // gs)) / 128
+    return {"nvfp4": 18432 / 128, "mxfp4": 17408 / 128, "fp8": 32768 / 128, "fp16": 512.0}[fmt]
 
 
 def decode_bytes(cache, layer: int, fmt: str, old_fmt: str) -> float:

@@ -7,6 +7,7 @@ names (include/kvq.h); `Cache` bundles the device buffer and the handle.
 from __future__ import annotations
 
 import ctypes
+import re
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -76,10 +77,27 @@ def _check(code: int):
         raise KvqError(code, lib().kvq_last_error().decode())
 
 
+def parse_format(name: str):
+    """(format code, group size) of a format name: "int4" (groups of 64), "int4g32", "int2g128",
+    "nvfp4", "mxfp4", "fp8", "fp16"."""
+    m = re.fullmatch(r"(int[248])g(32|64|128)", name)
+    if m:
+        return FMT[m.group(1)], int(m.group(2))
+    if name not in FMT:
+        raise ValueError(f"unknown cache format {name!r}")
+    return FMT[name], GROUP_SIZE[name]
+
+
 def make_config(num_layers, batch, num_kv_heads, max_tokens, fmt="int4", residual_len=128,
                 old_fmt=None, old_after=0, head_dim=128) -> kvq_config:
-    return kvq_config(num_layers, batch, num_kv_heads, head_dim, max_tokens, FMT[fmt],
-                      GROUP_SIZE[fmt], residual_len, FMT[old_fmt or fmt], old_after)
+    """An affine old tier shares the young tier's group size when the young format is affine
+    (64 otherwise): old_fmt must name that group size."""
+    code, gs = parse_format(fmt)
+    old_code, old_gs = parse_format(old_fmt or fmt)
+    if old_fmt and old_code in (2, 4, 8) and old_gs != (gs if code in (2, 4, 8) else 64):
+        raise ValueError(f"old tier {old_fmt!r} must use the group size of the young tier ({fmt!r})")
+    return kvq_config(num_layers, batch, num_kv_heads, head_dim, max_tokens, code, gs, residual_len,
+                      old_code, old_after)
 
 
 def kvq_cache_bytes(cfg: kvq_config) -> int:

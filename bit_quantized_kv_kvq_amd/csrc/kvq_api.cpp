@@ -47,6 +47,12 @@ bool is_block_fmt(int f) {
 int group_of(int f) {
   return f == kFmtNvfp4 ? kNvBlock : f == kFmtMxfp4 ? kMxBlock : (f == kFmtFp8 || f == kFmtFp16) ? 0 : kGroup;
 }
+// Group size of a tier: an affine tier takes the configured group size when the young format
+// is affine too, else 64; the other formats have their own fixed grouping (64 passed along).
+int tier_gs(const kvq_config *c, int fmt) {
+  if (!is_affine(fmt)) return kGroup;
+  return is_affine(c->format) ? c->group_size : kGroup;
+}
 
 struct LayerState {
   int64_t length = 0;  // tokens cached
@@ -68,8 +74,9 @@ const char *check_config(const kvq_config *c) {
   if (c->head_dim != kHeadDim) return "head_dim must be 128";
   if (c->max_tokens < 1) return "max_tokens must be >= 1";
   if (!is_block_fmt(c->format)) return "format must be KVQ_FMT_FP16/INT2/INT4/INT8/NVFP4/MXFP4/FP8";
-  if (c->group_size != group_of(c->format))
-    return "group_size must be 64 for affine formats, 16 for NVFP4, 32 for MXFP4 and 0 for FP8 and FP16";
+  if (is_affine(c->format) ? (c->group_size != 32 && c->group_size != 64 && c->group_size != 128)
+                           : c->group_size != group_of(c->format))
+    return "group_size must be 32, 64 or 128 for affine formats, 16 for NVFP4, 32 for MXFP4 and 0 for FP8 and FP16";
   if (c->residual_len < 0 || c->residual_len > 1024 || c->residual_len % 16 != 0)
     return "residual_len must be 0 or a multiple of 16 up to 1024";
   if (c->old_after < 0) return "old_after must be >= 0";
@@ -85,8 +92,8 @@ Geometry geometry(const kvq_config *c) {
   g.young_cap_blocks = ceil_div(c->max_tokens, kBlock);
   g.old_cap_blocks = c->old_after > 0 && c->max_tokens > c->old_after ? ceil_div(c->max_tokens - c->old_after, kBlock) : 0;
   g.res_bh = (size_t)512 * (size_t)c->residual_len;
-  g.young_bh = (size_t)g.young_cap_blocks * block_bytes(c->format);
-  g.old_bh = g.old_cap_blocks ? (size_t)g.old_cap_blocks * block_bytes(c->old_format) : 0;
+  g.young_bh = (size_t)g.young_cap_blocks * block_bytes(c->format, tier_gs(c, c->format));
+  g.old_bh = g.old_cap_blocks ? (size_t)g.old_cap_blocks * block_bytes(c->old_format, tier_gs(c, c->old_format)) : 0;
   g.off_res = 0;
   g.off_young = align_up(bh * g.res_bh);
   g.off_old = g.off_young + align_up(bh * g.young_bh);
@@ -219,6 +226,7 @@ int run_plan(kvq_cache *c, int layer, const Plan &p, const void *k, const void *
       a.arena_bh_stride = (int64_t)(op.tier ? c->geo.old_bh : c->geo.young_bh);
       a.dst_slot0 = op.dst_slot0;
       a.fmt = op.tier ? cfg.old_format : cfg.format;
+      a.gs = tier_gs(&cfg, a.fmt);
       a.B = cfg.batch; a.H = cfg.num_kv_heads;
       if (int e = hip_check(launch_quantize(a, s), "quantize")) return e;
     }
@@ -248,21 +256,25 @@ int plan_decode(const kvq_cache *c, int layer, DecodeArgs &a, uint64_t *cursors)
   const auto &cfg = c->cfg;
   const LayerState &st = c->layers[layer];
   const int64_t nbh = (int64_t)cfg.batch * cfg.num_kv_heads;
-  struct T { const uint8_t *base; int64_t stride, ntok, nblk; int fmt; };
+  struct T { const uint8_t *base; int64_t stride, ntok, nblk; int fmt, gs; };
   T tiers[2];
   int nt = 0;
-  if (st.old > 0) tiers[nt++] = {c->old(layer), (int64_t)c->geo.old_bh, st.old, ceil_div(st.old, kBlock), cfg.old_format};
-  if (st.young > 0) tiers[nt++] = {c->young(layer), (int64_t)c->geo.young_bh, st.young, ceil_div(st.young, kBlock), cfg.format};
+  if (st.old > 0)
+    tiers[nt++] = {c->old(layer), (int64_t)c->geo.old_bh, st.old, ceil_div(st.old, kBlock), cfg.old_format,
+                   tier_gs(&cfg, cfg.old_format)};
+  if (st.young > 0)
+    tiers[nt++] = {c->young(layer), (int64_t)c->geo.young_bh, st.young, ceil_div(st.young, kBlock), cfg.format,
+                   tier_gs(&cfg, cfg.format)};
   const int cus = c->num_cus > 0 ? c->num_cus : 256;
   const int64_t slots = 2LL * cus;
   const int64_t target = std::max<int64_t>(1, slots / nbh);       // work items per (b, h)
   double bytes = 0;
-  for (int i = 0; i < nt; ++i) bytes += (double)tiers[i].nblk * (double)block_bytes(tiers[i].fmt);
+  for (int i = 0; i < nt; ++i) bytes += (double)tiers[i].nblk * (double)block_bytes(tiers[i].fmt, tiers[i].gs);
   a.nseg = 0;
   int parts = 0;
   for (int i = 0; i < nt; ++i) {
     const T &t = tiers[i];
-    int64_t items = std::max<int64_t>(1, (int64_t)((double)target * t.nblk * block_bytes(t.fmt) / bytes + 0.5));
+    int64_t items = std::max<int64_t>(1, (int64_t)((double)target * t.nblk * block_bytes(t.fmt, t.gs) / bytes + 0.5));
     items = std::min<int64_t>(items, kMaxParts / std::max(1, nt));
     // units of about 1/32 of an item's share, at least four blocks (a unit's cursor fetch
     // has four block times to come back); two fixed units per item, then the cursor's big
@@ -281,7 +293,7 @@ int plan_decode(const kvq_cache *c, int layer, DecodeArgs &a, uint64_t *cursors)
       fixed = ceil_div(t.nblk, items);
     }
     DecodeSeg &s = a.seg[a.nseg++];
-    s.base = t.base; s.bh_stride = t.stride; s.ntok = t.ntok; s.fmt = t.fmt;
+    s.base = t.base; s.bh_stride = t.stride; s.ntok = t.ntok; s.fmt = t.fmt; s.gs = t.gs;
     s.chunk = (int)chunk; s.items = (int)items; s.fixed = (int)fixed; s.nbig = (int)nbig; s.part0 = parts;
     s.cursors = cursors + (size_t)i * nbh;
     parts += (int)items;

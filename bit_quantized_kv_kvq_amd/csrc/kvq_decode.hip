@@ -174,12 +174,13 @@ __device__ __forceinline__ float head_sum2(float x) { return quad_sum(x + __shfl
 // ---------------------------------------------------------------- Q operand per format
 // Dim fed by B element e of k-step j in lane quarter g, and whether the A element it meets
 // carries a factor 16 (then B holds q / 16).
-template <int FMT>
+template <int FMT, int GS>
 __device__ __forceinline__ int q_dim(int g, int j, int e, bool &scaled) {
   const int G = j >> 1, h = j & 1;
-  scaled = false;
-  if constexpr (FMT == kFmtInt4) {
-    scaled = ((e >> 1) & 1) != 0;
+  scaled = FMT == kFmtInt4 && ((e >> 1) & 1) != 0;
+  if constexpr (is_affine(FMT) && GS == 32) {
+    return 32 * j + 8 * g + e;   // groups of 32: k-step j feeds dims 32j + 8g .. +7 (group j)
+  } else if constexpr (FMT == kFmtInt4) {
     return 64 * G + 16 * g + 8 * h + (e >> 1) + 4 * (e & 1);
   } else if constexpr (FMT == kFmtInt2) {
     return 64 * G + 16 * g + 4 * h + (e >> 1) + 8 * (e & 1);
@@ -192,14 +193,25 @@ __device__ __forceinline__ int q_dim(int g, int j, int e, bool &scaled) {
   }
 }
 
-// The 32 dims a lane quarter g feeds: affine formats and FP8 dims 16g..16g+15 and
-// 64+16g..64+16g+15 (local index 16G + m); NVFP4 and fp16 dims 32g..32g+31 (local index
-// dim - 32g).
-template <int FMT>
-__device__ __forceinline__ void load_q(const uint16_t *qrow, bool valid, int g, half8_t (&qb)[4], float &qs0, float &qs1) {
-  constexpr bool kAff = FMT == kFmtInt2 || FMT == kFmtInt4 || FMT == kFmtInt8 || FMT == kFmtFp8;
+// Affine group of MFMA k-step j (groups of 32: one per step; 64: steps 2G, 2G + 1; 128: all)
+// and of V dim tile k (dims 16k .. 16k + 15).
+template <int GS>
+__device__ __forceinline__ constexpr int k_group(int j) { return GS == 32 ? j : GS == 64 ? j >> 1 : 0; }
+template <int GS>
+__device__ __forceinline__ constexpr int v_group(int k) { return GS == 32 ? k >> 1 : GS == 64 ? k >> 2 : 0; }
+
+// The 32 dims a lane quarter g feeds: affine formats (groups of 64 or 128) and FP8 dims
+// 16g..16g+15 and 64+16g..64+16g+15 (local index 16G + m); affine groups of 32 dims 32j + 8g
+// .. +7 (local index 8j + m); NVFP4 and fp16 dims 32g..32g+31 (local index dim - 32g).
+template <int FMT, int GS>
+__device__ __forceinline__ void load_q(const uint16_t *qrow, bool valid, int g, half8_t (&qb)[4], float (&qs)[4]) {
+  constexpr bool kLay32 = is_affine(FMT) && GS == 32;
+  constexpr bool kLay64 = !kLay32 && (is_affine(FMT) || FMT == kFmtFp8);
   uint4 raw[4];
-  if constexpr (kAff) {
+  if constexpr (kLay32) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) raw[j] = *(const uint4 *)(qrow + 32 * j + 8 * g);
+  } else if constexpr (kLay64) {
     raw[0] = *(const uint4 *)(qrow + 16 * g);
     raw[1] = *(const uint4 *)(qrow + 16 * g + 8);
     raw[2] = *(const uint4 *)(qrow + 64 + 16 * g);
@@ -215,25 +227,26 @@ __device__ __forceinline__ void load_q(const uint16_t *qrow, bool valid, int g, 
 #pragma unroll
     for (int e = 0; e < 8; ++e) loc[8 * i + e] = valid ? v[e] : (_Float16)0.0f;
   }
-  qs0 = qs1 = 0.0f;
+#pragma unroll
+  for (int G = 0; G < 4; ++G) qs[G] = 0.0f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       bool scaled;
-      const int d = q_dim<FMT>(g, j, e, scaled);
-      const int li = kAff ? 16 * (d >> 6) + (d & 15) : d - 32 * g;
+      const int d = q_dim<FMT, GS>(g, j, e, scaled);
+      const int li = kLay32 ? 8 * (d >> 5) + (d & 7) : kLay64 ? 16 * (d >> 6) + (d & 15) : d - 32 * g;
       _Float16 v = loc[li];
       if (scaled) v = v * (_Float16)0.0625f;
       qb[j][e] = v;
       const float eff = scaled ? 16.0f * (float)v : (float)v;    // the q the MFMA effectively uses
-      if (j < 2) qs0 += eff; else qs1 += eff;
+      qs[k_group<GS>(j)] += eff;
     }
   }
   // group sums over the four lane quarters (lanes c, c+16, c+32, c+48 hold one head), in the
   // 2^-24 units of the subnormal code operands
-  qs0 = quad_sum(qs0) * kSub;
-  qs1 = quad_sum(qs1) * kSub;
+#pragma unroll
+  for (int G = 0; G < kHeadDim / GS; ++G) qs[G] = quad_sum(qs[G]) * kSub;
 }
 
 // ---------------------------------------------------------------- LDS DMA
@@ -295,8 +308,8 @@ __device__ __forceinline__ void barrier() {
 struct State {
   float m = kNegInf;   // running max of the unscaled logits of head c, same on the 4 lane quarters
   float l = 0.0f;      // this lane's share of sum p
-  float z1 = 0.0f, z16 = 0.0f;   // affine V: this lane's share of sum P' Z (group 0 / 1 folded below)
-  float z1b = 0.0f, z16b = 0.0f;
+  float z[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};   // affine V: this lane's share of
+                       // sum P' Z of group G (z[2G]; INT4's x16 positions in z[2G + 1])
   float4_t o[8];       // O^T[dims 16k + 4g + i][head c]
 };
 
@@ -314,7 +327,8 @@ __device__ __forceinline__ void softmax_step(State &st, const float (&s)[8], flo
     const float m_new = fmaxf(st.m, mt);
     const float alpha = (m_new == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f((st.m - m_new) * sl2);
     st.l *= alpha;
-    st.z1 *= alpha; st.z16 *= alpha; st.z1b *= alpha; st.z16b *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.z[i] *= alpha;
 #pragma unroll
     for (int k = 0; k < 8; ++k) st.o[k] *= alpha;
     st.m = m_new;
@@ -336,16 +350,32 @@ __device__ __forceinline__ void softmax_step(State &st, const float (&s)[8], flo
 // tokens (the last block of a tier).
 struct QOp {
   half8_t qb[4];
-  float qs0, qs1;          // per-group sums of the effective q (zero-point terms)
+  float qs[4];             // per-group sums of the effective q (zero-point terms)
 };
 
-template <int NB, bool TAIL>
+// N consecutive 32-bit words from LDS (N = 2, 4 or 8)
+template <int N>
+__device__ __forceinline__ void lds_words(const uint8_t *p, uint32_t (&w)[N]) {
+  if constexpr (N == 2) {
+    const uint2 x = *(const uint2 *)p;
+    w[0] = x.x; w[1] = x.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const uint4 x = *(const uint4 *)(p + 16 * i);
+      w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z; w[4 * i + 3] = x.w;
+    }
+  }
+}
+__device__ __forceinline__ float half_of(uint32_t word, int h) { return h ? hi_f(word) : lo_f(word); }
+
+template <int NB, int GS, bool TAIL>
 __device__ __forceinline__ void affine_step(const uint8_t *blk, int w, int g, int c, const QOp &q, float sl2,
                                             bool valid_head, int nvalid, State &st) {
-  constexpr int kKm = 2048 * NB, kVc = 2048 * NB + 1024, kVm = 4096 * NB + 1024;
+  constexpr int NG = kHeadDim / GS;   // groups per token
+  constexpr int kKm = 2048 * NB, kVc = 2048 * NB + 512 * NG, kVm = 4096 * NB + 512 * NG;
   const int lane = 16 * g + c;
   const half8_t (&qb)[4] = q.qb;
-  const float qs0 = q.qs0, qs1 = q.qs1;
 
   // Everything that does not depend on the softmax state first (LDS reads, the V operands),
   // so that it overlaps the K -> logits -> max chain.
@@ -372,50 +402,52 @@ __device__ __forceinline__ void affine_step(const uint8_t *blk, int w, int g, in
       va[2 * r + 1] = unpack_int8(x.z, x.w);
     }
   }
-  uint4 vm0[2], vz[2];
+  // V metadata of slots 4g + i (i = 0..3) of each tile: S of group G at half 4G + i, then the Z
+  uint32_t vsw[2][2 * NG], vzw[2][2 * NG];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    vm0[tt] = *(const uint4 *)(blk + kVm + ((2 * w + tt) * 4 + g) * 32);        // S_G0[0..3], S_G1[0..3]
-    vz[tt] = *(const uint4 *)(blk + kVm + ((2 * w + tt) * 4 + g) * 32 + 16);    // Z_G0[0..3], Z_G1[0..3]
+    const uint8_t *m = blk + kVm + ((2 * w + tt) * 4 + g) * 16 * NG;
+    lds_words<2 * NG>(m, vsw[tt]);
+    lds_words<2 * NG>(m + 8 * NG, vzw[tt]);
   }
 
   float s[8];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
     const int tau = 2 * w + tt;
-    // K codes: [part w][tile tt][chunk][lane][min(16, 4n) bytes]
+    // K codes: [part w][tile tt][chunk][lane][min(16, 4n) bytes]; op[j] feeds k-step j
     const uint8_t *row = blk + (tau * (NB == 8 ? 2 : 1) * 64 + lane) * (NB == 2 ? 8 : 16);
-    float4_t a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0;
+    half8_t op[4];
     if constexpr (NB == 4) {
       const uint4 x = *(const uint4 *)row;
-      a0 = mfma(unpack_int4(x.x), qb[0], a0);
-      a0 = mfma(unpack_int4(x.y), qb[1], a0);
-      a1 = mfma(unpack_int4(x.z), qb[2], a1);
-      a1 = mfma(unpack_int4(x.w), qb[3], a1);
+      op[0] = unpack_int4(x.x); op[1] = unpack_int4(x.y); op[2] = unpack_int4(x.z); op[3] = unpack_int4(x.w);
     } else if constexpr (NB == 2) {
       const uint2 x = *(const uint2 *)row;
-      half8_t l0, h0, l1, h1;
-      unpack_int2(x.x, l0, h0);
-      unpack_int2(x.y, l1, h1);
-      a0 = mfma(l0, qb[0], a0);
-      a0 = mfma(h0, qb[1], a0);
-      a1 = mfma(l1, qb[2], a1);
-      a1 = mfma(h1, qb[3], a1);
+      unpack_int2(x.x, op[0], op[1]);
+      unpack_int2(x.y, op[2], op[3]);
     } else {
       const uint4 x = *(const uint4 *)row, y = *(const uint4 *)(row + 1024);
-      a0 = mfma(unpack_int8(x.x, x.y), qb[0], a0);
-      a0 = mfma(unpack_int8(x.z, x.w), qb[1], a0);
-      a1 = mfma(unpack_int8(y.x, y.y), qb[2], a1);
-      a1 = mfma(unpack_int8(y.z, y.w), qb[3], a1);
+      op[0] = unpack_int8(x.x, x.y); op[1] = unpack_int8(x.z, x.w);
+      op[2] = unpack_int8(y.x, y.y); op[3] = unpack_int8(y.z, y.w);
     }
-    const uint4 ks = *(const uint4 *)(blk + kKm + tau * 128 + 16 * g);        // (S0, S1) of slots 4g+i
-    const uint4 kz = *(const uint4 *)(blk + kKm + tau * 128 + 64 + 16 * g);   // (Z0, Z1)
-    const uint32_t sw[4] = {ks.x, ks.y, ks.z, ks.w}, zw[4] = {kz.x, kz.y, kz.z, kz.w};
+    float4_t acc[NG];
+#pragma unroll
+    for (int G = 0; G < NG; ++G) acc[G] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[k_group<GS>(j)] = mfma(op[j], qb[j], acc[k_group<GS>(j)]);
+    // (S, Z) of slots 16 tau + 4g + i, group G at half NG i + G
+    uint32_t ksw[2 * NG], kzw[2 * NG];
+    lds_words<2 * NG>(blk + kKm + tau * 64 * NG + 8 * NG * g, ksw);
+    lds_words<2 * NG>(blk + kKm + tau * 64 * NG + 32 * NG + 8 * NG * g, kzw);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float u0 = fmaf(-lo_f(zw[i]), qs0, a0[i]);
-      const float u1 = fmaf(-hi_f(zw[i]), qs1, a1[i]);
-      float v = fmaf(hi_f(sw[i]), u1, lo_f(sw[i]) * u0);
+      float v = 0.0f;
+#pragma unroll
+      for (int G = 0; G < NG; ++G) {
+        const int hx = NG * i + G;
+        const float u = fmaf(-half_of(kzw[hx >> 1], hx & 1), q.qs[G], acc[G][i]);
+        v = G == 0 ? half_of(ksw[hx >> 1], hx & 1) * u : fmaf(half_of(ksw[hx >> 1], hx & 1), u, v);
+      }
       if (TAIL && 16 * tau + 4 * g + i >= nvalid) v = kNegInf;
       s[4 * tt + i] = v;
     }
@@ -425,35 +457,30 @@ __device__ __forceinline__ void affine_step(const uint8_t *blk, int w, int g, in
   softmax_step(st, s, p, valid_head, kScaled, sl2);
 
   // P' = p * S per group (one fp16 rounding), and the zero-point sums sum P' Z
-  half8_t pb[2];
-  {
-    uint32_t pw[2][4];
+  half8_t pb[NG];
+#pragma unroll
+  for (int G = 0; G < NG; ++G) {
+    uint32_t pw[4];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const float *pp = p + 4 * tt;
-      const uint4 sm = vm0[tt], zz = vz[tt];
-      const uint32_t a01 = pk(pp[0] * lo_f(sm.x), pp[1] * hi_f(sm.x)), a23 = pk(pp[2] * lo_f(sm.y), pp[3] * hi_f(sm.y));
-      const uint32_t b01 = pk(pp[0] * lo_f(sm.z), pp[1] * hi_f(sm.z)), b23 = pk(pp[2] * lo_f(sm.w), pp[3] * hi_f(sm.w));
-      pw[0][2 * tt + 0] = a01; pw[0][2 * tt + 1] = a23;
-      pw[1][2 * tt + 0] = b01; pw[1][2 * tt + 1] = b23;
-      const half2_t z0 = as_h2(zz.x), z1 = as_h2(zz.y), z2 = as_h2(zz.z), z3 = as_h2(zz.w);
+      const uint32_t s01 = vsw[tt][2 * G], s23 = vsw[tt][2 * G + 1];
+      const uint32_t a01 = pk(pp[0] * lo_f(s01), pp[1] * hi_f(s01)), a23 = pk(pp[2] * lo_f(s23), pp[3] * hi_f(s23));
+      pw[2 * tt] = a01;
+      pw[2 * tt + 1] = a23;
+      const half2_t z01 = as_h2(vzw[tt][2 * G]), z23 = as_h2(vzw[tt][2 * G + 1]);
       if constexpr (NB == 4) {
-        st.z1 = __builtin_amdgcn_fdot2(as_h2(a01), z0, st.z1, false);
-        st.z16 = __builtin_amdgcn_fdot2(as_h2(a23), z1, st.z16, false);
-        st.z1b = __builtin_amdgcn_fdot2(as_h2(b01), z2, st.z1b, false);
-        st.z16b = __builtin_amdgcn_fdot2(as_h2(b23), z3, st.z16b, false);
+        st.z[2 * G] = __builtin_amdgcn_fdot2(as_h2(a01), z01, st.z[2 * G], false);
+        st.z[2 * G + 1] = __builtin_amdgcn_fdot2(as_h2(a23), z23, st.z[2 * G + 1], false);
       } else {
-        st.z1 = __builtin_amdgcn_fdot2(as_h2(a01), z0, st.z1, false);
-        st.z1 = __builtin_amdgcn_fdot2(as_h2(a23), z1, st.z1, false);
-        st.z1b = __builtin_amdgcn_fdot2(as_h2(b01), z2, st.z1b, false);
-        st.z1b = __builtin_amdgcn_fdot2(as_h2(b23), z3, st.z1b, false);
+        st.z[2 * G] = __builtin_amdgcn_fdot2(as_h2(a01), z01, st.z[2 * G], false);
+        st.z[2 * G] = __builtin_amdgcn_fdot2(as_h2(a23), z23, st.z[2 * G], false);
       }
     }
-    pb[0] = h8(pw[0][0], pw[0][1], pw[0][2], pw[0][3]);
-    pb[1] = h8(pw[1][0], pw[1][1], pw[1][2], pw[1][3]);
+    pb[G] = h8(pw[0], pw[1], pw[2], pw[3]);
   }
 #pragma unroll
-  for (int k = 0; k < 8; ++k) st.o[k] = mfma(va[k], pb[k >> 2], st.o[k]);
+  for (int k = 0; k < 8; ++k) st.o[k] = mfma(va[k], pb[v_group<GS>(k)], st.o[k]);
 }
 
 template <bool TAIL>
@@ -681,18 +708,20 @@ __device__ __forceinline__ void residual_step(const uint8_t *res, int R, int r, 
 // columns of a head are summed at the end.
 struct QOp2 {
   half8_t qb[8];
-  float qs0, qs1;
+  float qs[4];
 };
 
 // Dim (index into the lane's 64 loaded dims) fed by B element e of k-step j, and whether it
 // meets an A element scaled by 16.  Affine formats and FP8: the lane holds dims 64G + 16(2q + gi) + m
 // at local index 32G + 16gi + m (G, gi in {0,1}); natural formats dims 64q + i at index i.
-template <int FMT>
+// B operand idx feeds k-step j = 2(idx >> 2) + (idx & 1) of lane quarter 2q + gi, gi = (idx >> 1) & 1.
+template <int FMT, int GS>
 __device__ __forceinline__ int q_loc2(int j, int e, bool &scaled) {
   const int G = j >> 2, gi = (j >> 1) & 1, hh = j & 1;
-  scaled = false;
-  if constexpr (FMT == kFmtInt4) {
-    scaled = ((e >> 1) & 1) != 0;
+  scaled = FMT == kFmtInt4 && ((e >> 1) & 1) != 0;
+  if constexpr (is_affine(FMT) && GS == 32) {
+    return 8 * (2 * (2 * G + hh) + gi) + e;   // groups of 32: dims 32 step + 8(2q + gi) + e
+  } else if constexpr (FMT == kFmtInt4) {
     return 32 * G + 16 * gi + 8 * hh + (e >> 1) + 4 * (e & 1);
   } else if constexpr (FMT == kFmtInt2) {
     return 32 * G + 16 * gi + 4 * hh + (e >> 1) + 8 * (e & 1);
@@ -705,13 +734,19 @@ __device__ __forceinline__ int q_loc2(int j, int e, bool &scaled) {
   }
 }
 
-template <int FMT>
+template <int FMT, int GS>
 __device__ __forceinline__ void load_q2(const uint16_t *qrow, bool valid, int g, int c, QOp2 &q) {
-  constexpr bool kAff = FMT == kFmtInt2 || FMT == kFmtInt4 || FMT == kFmtInt8 || FMT == kFmtFp8;
+  constexpr bool kLay32 = is_affine(FMT) && GS == 32;
+  constexpr bool kLay64 = !kLay32 && (is_affine(FMT) || FMT == kFmtFp8);
   const int qq = g & 1;
   const bool active = valid && (c >> 3) == (g >> 1);
   uint4 raw[8];
-  if constexpr (kAff) {
+  if constexpr (kLay32) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) raw[2 * j + gi] = *(const uint4 *)(qrow + 32 * j + 8 * (2 * qq + gi));
+  } else if constexpr (kLay64) {
 #pragma unroll
     for (int G = 0; G < 2; ++G)
 #pragma unroll
@@ -731,21 +766,21 @@ __device__ __forceinline__ void load_q2(const uint16_t *qrow, bool valid, int g,
 #pragma unroll
     for (int e = 0; e < 8; ++e) loc[8 * i + e] = active ? v[e] : (_Float16)0.0f;
   }
-  float qs0 = 0.0f, qs1 = 0.0f;
+  float qs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       bool scaled;
-      _Float16 v = loc[q_loc2<FMT>(j, e, scaled)];
+      _Float16 v = loc[q_loc2<FMT, GS>(j, e, scaled)];
       if (scaled) v = v * (_Float16)0.0625f;
       q.qb[j][e] = v;
       const float eff = scaled ? 16.0f * (float)v : (float)v;
-      if (j < 4) qs0 += eff; else qs1 += eff;
+      qs[k_group<GS>(2 * (j >> 2) + (j & 1))] += eff;
     }
   }
-  q.qs0 = quad_sum(qs0) * kSub;
-  q.qs1 = quad_sum(qs1) * kSub;
+#pragma unroll
+  for (int G = 0; G < 4; ++G) q.qs[G] = G < kHeadDim / GS ? quad_sum(qs[G]) * kSub : 0.0f;
 }
 
 // Running max / probabilities for 4 logits (slots i of the lane's subtile); scaled_mask bit i
@@ -757,7 +792,8 @@ __device__ __forceinline__ void softmax_step2(State &st, const float (&s)[4], fl
     const float m_new = fmaxf(st.m, head_max2(ml));
     const float alpha = (m_new == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f((st.m - m_new) * sl2);
     st.l *= alpha;
-    st.z1 *= alpha; st.z16 *= alpha; st.z1b *= alpha; st.z16b *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.z[i] *= alpha;
 #pragma unroll
     for (int k = 0; k < 8; ++k) st.o[k] *= alpha;
     st.m = m_new;
@@ -796,15 +832,16 @@ __device__ __forceinline__ half4_t v_operand2<8>(const uint32_t *vw, int k, int 
   return h4(x & 0x00FF00FFu, (x >> 8) & 0x00FF00FFu);
 }
 
-template <int NB, bool TAIL>
+template <int NB, int GS, bool TAIL>
 __device__ __forceinline__ void affine_step2(const uint8_t *blk, int w, int g, int c, const QOp2 &q, float sl2,
                                              bool valid_head, int nvalid, State &st) {
-  constexpr int kKm = 2048 * NB, kVc = 2048 * NB + 1024, kVm = 4096 * NB + 1024;
+  constexpr int NG = kHeadDim / GS;
+  constexpr int kKm = 2048 * NB, kVc = 2048 * NB + 512 * NG, kVm = 4096 * NB + 512 * NG;
   const int lane = 16 * g + c;
   const int qq = g & 1, sa = g >> 1;           // A operand: this lane feeds subtile sa, dim half qq
   const int sc = c >> 3;                       // output column subtile
 
-  // V codes of this lane ([part w][chunk][lane][16 B]) and V meta of the column's slots
+  // V codes of this lane ([part w][chunk][lane][16 B]) and the metadata of the column's slots
   constexpr int kChunks = NB / 2;
   uint32_t vw[2 * NB];
   {
@@ -816,63 +853,58 @@ __device__ __forceinline__ void affine_step2(const uint8_t *blk, int w, int g, i
     }
   }
   const int tau_c = 2 * w + sc;
-  const uint4 vm = *(const uint4 *)(blk + kVm + (tau_c * 4 + g) * 32);          // S_G0[0..3], S_G1[0..3]
-  const uint4 vz = *(const uint4 *)(blk + kVm + (tau_c * 4 + g) * 32 + 16);     // Z_G0[0..3], Z_G1[0..3]
-  const uint4 ks = *(const uint4 *)(blk + kKm + tau_c * 128 + 16 * g);          // (S0, S1) of slots 4g+i
-  const uint4 kz = *(const uint4 *)(blk + kKm + tau_c * 128 + 64 + 16 * g);     // (Z0, Z1)
+  uint32_t vsw[2 * NG], vzw[2 * NG], ksw[2 * NG], kzw[2 * NG];
+  lds_words<2 * NG>(blk + kVm + (tau_c * 4 + g) * 16 * NG, vsw);            // S of group G, slot 4g + i: half 4G + i
+  lds_words<2 * NG>(blk + kVm + (tau_c * 4 + g) * 16 * NG + 8 * NG, vzw);   // the Z likewise
+  lds_words<2 * NG>(blk + kKm + tau_c * 64 * NG + 8 * NG * g, ksw);         // (S, Z) of slots 4g + i: half NG i + G
+  lds_words<2 * NG>(blk + kKm + tau_c * 64 * NG + 32 * NG + 8 * NG * g, kzw);
 
-  // QK^T: lane feeds token (subtile sa, row c), dims of layout chunks 2qq and 2qq+1
+  // QK^T: lane feeds token (subtile sa, row c) from the lane strings of quarters 2qq + gi:
+  // op[gi][j] feeds k-step j
   const int tau_a = 2 * w + sa;
-  float4_t a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0;
+  half8_t op[2][4];
   if constexpr (NB == 4) {
-    const uint4 x0 = *(const uint4 *)(blk + (tau_a * 64 + 16 * (2 * qq) + c) * 16);
-    const uint4 x1 = *(const uint4 *)(blk + (tau_a * 64 + 16 * (2 * qq + 1) + c) * 16);
-    a0 = mfma(unpack_int4(x0.x), q.qb[0], a0);
-    a0 = mfma(unpack_int4(x0.y), q.qb[1], a0);
-    a0 = mfma(unpack_int4(x1.x), q.qb[2], a0);
-    a0 = mfma(unpack_int4(x1.y), q.qb[3], a0);
-    a1 = mfma(unpack_int4(x0.z), q.qb[4], a1);
-    a1 = mfma(unpack_int4(x0.w), q.qb[5], a1);
-    a1 = mfma(unpack_int4(x1.z), q.qb[6], a1);
-    a1 = mfma(unpack_int4(x1.w), q.qb[7], a1);
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const uint4 x = *(const uint4 *)(blk + (tau_a * 64 + 16 * (2 * qq + gi) + c) * 16);
+      op[gi][0] = unpack_int4(x.x); op[gi][1] = unpack_int4(x.y);
+      op[gi][2] = unpack_int4(x.z); op[gi][3] = unpack_int4(x.w);
+    }
   } else if constexpr (NB == 2) {
-    const uint2 x0 = *(const uint2 *)(blk + (tau_a * 64 + 16 * (2 * qq) + c) * 8);
-    const uint2 x1 = *(const uint2 *)(blk + (tau_a * 64 + 16 * (2 * qq + 1) + c) * 8);
-    half8_t l0, h0, l1, h1;
-    unpack_int2(x0.x, l0, h0);
-    unpack_int2(x1.x, l1, h1);
-    a0 = mfma(l0, q.qb[0], a0);
-    a0 = mfma(h0, q.qb[1], a0);
-    a0 = mfma(l1, q.qb[2], a0);
-    a0 = mfma(h1, q.qb[3], a0);
-    unpack_int2(x0.y, l0, h0);
-    unpack_int2(x1.y, l1, h1);
-    a1 = mfma(l0, q.qb[4], a1);
-    a1 = mfma(h0, q.qb[5], a1);
-    a1 = mfma(l1, q.qb[6], a1);
-    a1 = mfma(h1, q.qb[7], a1);
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const uint2 x = *(const uint2 *)(blk + (tau_a * 64 + 16 * (2 * qq + gi) + c) * 8);
+      unpack_int2(x.x, op[gi][0], op[gi][1]);
+      unpack_int2(x.y, op[gi][2], op[gi][3]);
+    }
   } else {
-    // chunk r of (tile, lane') at ((tile * 2 + r) * 64 + lane') * 16, r = group G
-    const uint8_t *k0 = blk + ((tau_a * 2) * 64 + 16 * (2 * qq) + c) * 16;
-    const uint8_t *k1 = blk + ((tau_a * 2) * 64 + 16 * (2 * qq + 1) + c) * 16;
-    const uint4 x0 = *(const uint4 *)k0, y0 = *(const uint4 *)(k0 + 1024);
-    const uint4 x1 = *(const uint4 *)k1, y1 = *(const uint4 *)(k1 + 1024);
-    a0 = mfma(unpack_int8(x0.x, x0.y), q.qb[0], a0);
-    a0 = mfma(unpack_int8(x0.z, x0.w), q.qb[1], a0);
-    a0 = mfma(unpack_int8(x1.x, x1.y), q.qb[2], a0);
-    a0 = mfma(unpack_int8(x1.z, x1.w), q.qb[3], a0);
-    a1 = mfma(unpack_int8(y0.x, y0.y), q.qb[4], a1);
-    a1 = mfma(unpack_int8(y0.z, y0.w), q.qb[5], a1);
-    a1 = mfma(unpack_int8(y1.x, y1.y), q.qb[6], a1);
-    a1 = mfma(unpack_int8(y1.z, y1.w), q.qb[7], a1);
+    // chunk r of (tile, lane') at ((tile * 2 + r) * 64 + lane') * 16
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const uint8_t *k = blk + ((tau_a * 2) * 64 + 16 * (2 * qq + gi) + c) * 16;
+      const uint4 x = *(const uint4 *)k, y = *(const uint4 *)(k + 1024);
+      op[gi][0] = unpack_int8(x.x, x.y); op[gi][1] = unpack_int8(x.z, x.w);
+      op[gi][2] = unpack_int8(y.x, y.y); op[gi][3] = unpack_int8(y.z, y.w);
+    }
+  }
+  float4_t acc[NG];
+#pragma unroll
+  for (int G = 0; G < NG; ++G) acc[G] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int idx = 0; idx < 8; ++idx) {
+    const int j = 2 * (idx >> 2) + (idx & 1), gi = (idx >> 1) & 1;
+    acc[k_group<GS>(j)] = mfma(op[gi][j], q.qb[idx], acc[k_group<GS>(j)]);
   }
   float s[4];
-  const uint32_t sw[4] = {ks.x, ks.y, ks.z, ks.w}, zw[4] = {kz.x, kz.y, kz.z, kz.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float u0 = fmaf(-lo_f(zw[i]), q.qs0, a0[i]);
-    const float u1 = fmaf(-hi_f(zw[i]), q.qs1, a1[i]);
-    float v = fmaf(hi_f(sw[i]), u1, lo_f(sw[i]) * u0);
+    float v = 0.0f;
+#pragma unroll
+    for (int G = 0; G < NG; ++G) {
+      const int hx = NG * i + G;
+      const float u = fmaf(-half_of(kzw[hx >> 1], hx & 1), q.qs[G], acc[G][i]);
+      v = G == 0 ? half_of(ksw[hx >> 1], hx & 1) * u : fmaf(half_of(ksw[hx >> 1], hx & 1), u, v);
+    }
     if (TAIL && 16 * tau_c + 4 * g + i >= nvalid) v = kNegInf;
     s[i] = v;
   }
@@ -880,28 +912,28 @@ __device__ __forceinline__ void affine_step2(const uint8_t *blk, int w, int g, i
   constexpr unsigned kScaled = NB == 4 ? 0xCu : 0u;   // INT4: positions i = 2, 3
   softmax_step2(st, s, p, valid_head, kScaled, sl2);
 
-  // P' = p * S per group (one fp16 rounding) and the zero-point sums sum P' Z
-  const uint32_t a01 = pk(p[0] * lo_f(vm.x), p[1] * hi_f(vm.x)), a23 = pk(p[2] * lo_f(vm.y), p[3] * hi_f(vm.y));
-  const uint32_t b01 = pk(p[0] * lo_f(vm.z), p[1] * hi_f(vm.z)), b23 = pk(p[2] * lo_f(vm.w), p[3] * hi_f(vm.w));
-  if constexpr (NB == 4) {
-    st.z1 = __builtin_amdgcn_fdot2(as_h2(a01), as_h2(vz.x), st.z1, false);
-    st.z16 = __builtin_amdgcn_fdot2(as_h2(a23), as_h2(vz.y), st.z16, false);
-    st.z1b = __builtin_amdgcn_fdot2(as_h2(b01), as_h2(vz.z), st.z1b, false);
-    st.z16b = __builtin_amdgcn_fdot2(as_h2(b23), as_h2(vz.w), st.z16b, false);
-  } else {
-    st.z1 = __builtin_amdgcn_fdot2(as_h2(a01), as_h2(vz.x), st.z1, false);
-    st.z1 = __builtin_amdgcn_fdot2(as_h2(a23), as_h2(vz.y), st.z1, false);
-    st.z1b = __builtin_amdgcn_fdot2(as_h2(b01), as_h2(vz.z), st.z1b, false);
-    st.z1b = __builtin_amdgcn_fdot2(as_h2(b23), as_h2(vz.w), st.z1b, false);
-  }
-  // PV as O^T += V^T P per subtile s0: A = V codes of s0, B = this lane's P' where its column
+  // P' = p * S per group (one fp16 rounding) and the zero-point sums sum P' Z; PV as
+  // O^T += V^T P per subtile s0: A = V codes of s0, B = this lane's P' where its column
   // subtile is s0 (else zero); the accumulator rows are dims, its column the lane's head.
-  const half4_t pa0 = sc == 0 ? h4(a01, a23) : h4(0u, 0u), pb0 = sc == 0 ? h4(b01, b23) : h4(0u, 0u);
-  const half4_t pa1 = sc == 1 ? h4(a01, a23) : h4(0u, 0u), pb1 = sc == 1 ? h4(b01, b23) : h4(0u, 0u);
+  half4_t pa[NG][2];
+#pragma unroll
+  for (int G = 0; G < NG; ++G) {
+    const uint32_t a01 = pk(p[0] * lo_f(vsw[2 * G]), p[1] * hi_f(vsw[2 * G]));
+    const uint32_t a23 = pk(p[2] * lo_f(vsw[2 * G + 1]), p[3] * hi_f(vsw[2 * G + 1]));
+    if constexpr (NB == 4) {
+      st.z[2 * G] = __builtin_amdgcn_fdot2(as_h2(a01), as_h2(vzw[2 * G]), st.z[2 * G], false);
+      st.z[2 * G + 1] = __builtin_amdgcn_fdot2(as_h2(a23), as_h2(vzw[2 * G + 1]), st.z[2 * G + 1], false);
+    } else {
+      st.z[2 * G] = __builtin_amdgcn_fdot2(as_h2(a01), as_h2(vzw[2 * G]), st.z[2 * G], false);
+      st.z[2 * G] = __builtin_amdgcn_fdot2(as_h2(a23), as_h2(vzw[2 * G + 1]), st.z[2 * G], false);
+    }
+    pa[G][0] = sc == 0 ? h4(a01, a23) : h4(0u, 0u);
+    pa[G][1] = sc == 1 ? h4(a01, a23) : h4(0u, 0u);
+  }
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    st.o[k] = mfma16(v_operand2<NB>(vw, k, 0), k < 4 ? pa0 : pb0, st.o[k]);
-    st.o[k] = mfma16(v_operand2<NB>(vw, k, 1), k < 4 ? pa1 : pb1, st.o[k]);
+    st.o[k] = mfma16(v_operand2<NB>(vw, k, 0), pa[v_group<GS>(k)][0], st.o[k]);
+    st.o[k] = mfma16(v_operand2<NB>(vw, k, 1), pa[v_group<GS>(k)][1], st.o[k]);
   }
 }
 
@@ -1204,7 +1236,6 @@ __device__ __forceinline__ Item decode_item(const DecodeArgs &a, int wg) {
   return it;
 }
 
-__device__ __forceinline__ int block_bytes_of(int fmt) { return (int)block_bytes(fmt); }
 
 
 // The G query rows of a (b, h) in global memory (consecutive heads).
@@ -1230,20 +1261,20 @@ __device__ __forceinline__ void residual_part(const DecodeArgs &a, const Item &i
   const int nsteps = (a.res_ntok + 31) / 32;
   if constexpr (NSUB == 2) {
     QOp2 q;
-    load_q2<kFmtFp16>(qrow, valid_head, g, c, q);
+    load_q2<kFmtFp16, kGroup>(qrow, valid_head, g, c, q);
     for (int u = w; u < nsteps; u += kWaves) residual_step2(res, a.res_len, a.res_ntok, u, g, c, q, a.scale_log2, valid_head, st);
   } else {
     QOp q;
-    load_q<kFmtFp16>(qrow, valid_head, g, q.qb, q.qs0, q.qs1);
+    load_q<kFmtFp16, kGroup>(qrow, valid_head, g, q.qb, q.qs);
     for (int u = w; u < nsteps; u += kWaves) residual_step(res, a.res_len, a.res_ntok, u, g, c, q, a.scale_log2, valid_head, st);
   }
 }
 
-template <int FMT, int NSUB>
+template <int FMT, int GS, int NSUB>
 __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const DecodeSeg &sg, const Item &it, uint8_t *smem, int *s_chunk, int w,
                                int g, int c, bool valid_head, State &st) {
   const int lane = 16 * g + c;
-  const int bb = block_bytes_of(FMT);
+  const int bb = (int)block_bytes(FMT, GS);
   const int ndma = bb / 1024;                                 // 1 KB per wave instruction
   // Waves 0..2 load the blocks; wave 3 loads none and hands out the chunks, so that waiting
   // for its cursor atomic never waits for block loads (vmcnt counts both).
@@ -1316,8 +1347,8 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
   const uint16_t *qrow = q_row<NSUB>(qlds, c, valid_head);
   QOp q;
   QOp2 q2;
-  if constexpr (NSUB == 2) load_q2<FMT>(qrow, valid_head, g, c, q2);
-  else load_q<FMT>(qrow, valid_head, g, q.qb, q.qs0, q.qs1);
+  if constexpr (NSUB == 2) load_q2<FMT, GS>(qrow, valid_head, g, c, q2);
+  else load_q<FMT, GS>(qrow, valid_head, g, q.qb, q.qs);
   // affine logits come out in units of 2^-24 (subnormal code operands)
   constexpr bool kAff = FMT == kFmtInt2 || FMT == kFmtInt4 || FMT == kFmtInt8;
   const float sl2 = kAff ? a.scale_log2 * kInvSub : a.scale_log2;
@@ -1359,8 +1390,8 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
         if (full) mxfp4_step2<false>(blk, w, g, c, q2, sl2, valid_head, nv, st);
         else mxfp4_step2<true>(blk, w, g, c, q2, sl2, valid_head, nv, st);
       } else {
-        if (full) affine_step2<FMT, false>(blk, w, g, c, q2, sl2, valid_head, nv, st);
-        else affine_step2<FMT, true>(blk, w, g, c, q2, sl2, valid_head, nv, st);
+        if (full) affine_step2<FMT, GS, false>(blk, w, g, c, q2, sl2, valid_head, nv, st);
+        else affine_step2<FMT, GS, true>(blk, w, g, c, q2, sl2, valid_head, nv, st);
       }
     } else {
       if constexpr (FMT == kFmtNvfp4) {
@@ -1376,8 +1407,8 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
         if (full) mxfp4_step<false>(blk, w, g, c, q, sl2, valid_head, nv, st);
         else mxfp4_step<true>(blk, w, g, c, q, sl2, valid_head, nv, st);
       } else {
-        if (full) affine_step<FMT, false>(blk, w, g, c, q, sl2, valid_head, nv, st);
-        else affine_step<FMT, true>(blk, w, g, c, q, sl2, valid_head, nv, st);
+        if (full) affine_step<FMT, GS, false>(blk, w, g, c, q, sl2, valid_head, nv, st);
+        else affine_step<FMT, GS, true>(blk, w, g, c, q, sl2, valid_head, nv, st);
       }
     }
   }
@@ -1387,20 +1418,19 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
     // paired subtiles the head's total goes to its subtile-0 column only; the two columns are
     // summed later).
     if (st.m != kNegInf) st.m *= kInvSub;
-    float zg0, zg1;
-    bool take = true;
-    if constexpr (NSUB == 2) {
-      zg0 = head_sum2(st.z1 + 16.0f * st.z16);
-      zg1 = head_sum2(st.z1b + 16.0f * st.z16b);
-      take = (c >> 3) == 0;
-    } else {
-      zg0 = quad_sum(st.z1 + 16.0f * st.z16);
-      zg1 = quad_sum(st.z1b + 16.0f * st.z16b);
-    }
-    if (!take) zg0 = zg1 = 0.0f;
+    constexpr int NG = kHeadDim / GS;
+    const bool take = NSUB == 2 ? (c >> 3) == 0 : true;
+    float zg[NG];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) st.o[k] = st.o[k] * kInvSub - (k < 4 ? zg0 : zg1);
-    st.z1 = st.z16 = st.z1b = st.z16b = 0.0f;
+    for (int G = 0; G < NG; ++G) {
+      const float zl = st.z[2 * G] + 16.0f * st.z[2 * G + 1];
+      zg[G] = NSUB == 2 ? head_sum2(zl) : quad_sum(zl);
+      if (!take) zg[G] = 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) st.o[k] = st.o[k] * kInvSub - zg[v_group<GS>(k)];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.z[i] = 0.0f;
   }
 }
 
@@ -1465,15 +1495,24 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   }
   if (it.seg >= 0) {
     const DecodeSeg &sg = a.seg[it.seg];
+#define KVQ_SEG(F, GS) stream_segment<F, GS, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st)
+#define KVQ_AFFINE_SEG(F)                  \
+  case F:                                  \
+    if (sg.gs == 32) KVQ_SEG(F, 32);       \
+    else if (sg.gs == 128) KVQ_SEG(F, 128); \
+    else KVQ_SEG(F, 64);                   \
+    break;
     switch (sg.fmt) {
-      case kFmtInt2: stream_segment<kFmtInt2, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
-      case kFmtInt4: stream_segment<kFmtInt4, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
-      case kFmtInt8: stream_segment<kFmtInt8, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
-      case kFmtFp8: stream_segment<kFmtFp8, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
-      case kFmtFp16: stream_segment<kFmtFp16, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
-      case kFmtMxfp4: stream_segment<kFmtMxfp4, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
-      default: stream_segment<kFmtNvfp4, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st); break;
+      KVQ_AFFINE_SEG(kFmtInt2)
+      KVQ_AFFINE_SEG(kFmtInt4)
+      KVQ_AFFINE_SEG(kFmtInt8)
+      case kFmtFp8: KVQ_SEG(kFmtFp8, kGroup); break;
+      case kFmtFp16: KVQ_SEG(kFmtFp16, kGroup); break;
+      case kFmtMxfp4: KVQ_SEG(kFmtMxfp4, kGroup); break;
+      default: KVQ_SEG(kFmtNvfp4, kGroup); break;
     }
+#undef KVQ_AFFINE_SEG
+#undef KVQ_SEG
   }
   // ---- merge the four waves in LDS: per wave m[16], l[16], o[16][128] (m in log2 units)
   float *wm = (float *)smem;                       // [4][16]
@@ -1569,7 +1608,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
 static size_t decode_ring_bytes(const DecodeArgs &a) {
   size_t ring = 0;
   for (int s = 0; s < a.nseg; ++s) {
-    const int bb = (int)block_bytes(a.seg[s].fmt);
+    const int bb = (int)block_bytes(a.seg[s].fmt, a.seg[s].gs);
     ring = std::max(ring, (size_t)decode_ring_depth(bb) * bb);
   }
   return ring;

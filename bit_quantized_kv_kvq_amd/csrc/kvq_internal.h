@@ -17,27 +17,32 @@ constexpr int kMxBlock = 32;    // MXFP4 values sharing one E8M0 scale
 // Format codes (values of kvq_format).
 constexpr int kFmtFp16 = 0, kFmtInt2 = 2, kFmtInt4 = 4, kFmtInt8 = 8, kFmtNvfp4 = 16, kFmtFp8 = 32, kFmtMxfp4 = 64;
 
-// Bytes of one 128-slot block (K and V parts together).
-__host__ __device__ constexpr size_t affine_block_bytes(int nbits) { return 4096u * (size_t)nbits + 2048u; }
+// Bytes of one 128-slot block (K and V parts together); affine blocks hold one (S, Z) pair per
+// group of gs values (32, 64 or 128) of each token.
+__host__ __device__ constexpr size_t affine_block_bytes(int nbits, int gs = kGroup) {
+  return 4096u * (size_t)nbits + 1024u * (size_t)(kHeadDim / gs);
+}
 constexpr size_t kNvfp4BlockBytes = 18432;
 constexpr size_t kMxfp4BlockBytes = 17408;
 constexpr size_t kFp8BlockBytes = 32768;
 constexpr size_t kFp16BlockBytes = 65536;
-__host__ __device__ constexpr size_t block_bytes(int fmt) {
+__host__ __device__ constexpr bool is_affine(int fmt) { return fmt == kFmtInt2 || fmt == kFmtInt4 || fmt == kFmtInt8; }
+__host__ __device__ constexpr size_t block_bytes(int fmt, int gs = kGroup) {
   return fmt == kFmtNvfp4 ? kNvfp4BlockBytes
          : fmt == kFmtMxfp4 ? kMxfp4BlockBytes
          : fmt == kFmtFp8 ? kFp8BlockBytes
          : fmt == kFmtFp16 ? kFp16BlockBytes
-                           : affine_block_bytes(fmt);
+                           : affine_block_bytes(fmt, gs);
 }
 // Blocks in the decode kernel's LDS ring: four (three in flight) while two workgroups still
 // fit in a CU, else three, and two for the 64 KB fp16 blocks.
 __host__ __device__ constexpr int decode_ring_depth(size_t bb) { return bb <= 18432 ? 4 : bb <= 40960 ? 3 : 2; }
 
-// Offsets inside an affine block.
+// Offsets inside an affine block with ng groups per token: [Kc][Km][Vc][Vm], Km and Vm of
+// 512 ng bytes.
 constexpr size_t aff_km(int n) { return 2048u * (size_t)n; }
-constexpr size_t aff_vc(int n) { return 2048u * (size_t)n + 1024u; }
-constexpr size_t aff_vm(int n) { return 4096u * (size_t)n + 1024u; }
+constexpr size_t aff_vc(int n, int ng) { return 2048u * (size_t)n + 512u * (size_t)ng; }
+constexpr size_t aff_vm(int n, int ng) { return 4096u * (size_t)n + 512u * (size_t)ng; }
 // Offsets inside an NVFP4 block.
 constexpr size_t kNvKs = 8192, kNvVc = 9216, kNvVs = 17408;
 // Offsets inside an MXFP4 block: Kc as NVFP4's, one E8M0 byte per K lane, V bytes pairing
@@ -65,6 +70,7 @@ struct QuantArgs {
   int64_t arena_bh_stride;        // bytes per (b, h)
   int64_t dst_slot0;
   int fmt;
+  int gs;                         // affine group size (32, 64, 128)
   int B, H;
 };
 
@@ -91,7 +97,8 @@ struct DecodeSeg {
   const uint8_t *base;     // arena of the layer
   int64_t bh_stride;       // bytes per (b, h)
   int64_t ntok;            // valid slots per (b, h)
-  int fmt;                 // kFmtInt2 / Int4 / Int8 / Nvfp4
+  int fmt;                 // block format (kFmt*)
+  int gs;                  // affine group size (32, 64, 128; 64 for the other formats)
   int chunk;               // blocks per unit (fixed units and the cursor's big units)
   int items;               // work items per (b, h)
   int fixed;               // units per item assigned up front

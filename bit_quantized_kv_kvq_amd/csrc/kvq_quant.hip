@@ -127,6 +127,25 @@ __device__ __forceinline__ uint32_t e2m1_code(float x, float s) {
 __device__ __forceinline__ int k_lane_dim(int fmt, int g, int f) {
   return (fmt == kFmtNvfp4 || fmt == kFmtMxfp4) ? 32 * g + f : 64 * (f >> 4) + 16 * g + (f & 15);
 }
+// Affine groups of 32: field f of quarter g holds dim 32j + 8g + e, (j, e) being f's place among
+// the decode kernel's MFMA operands (k-step j, element e), so that every step covers one group.
+__device__ __forceinline__ int k_lane_dim32(int fmt, int g, int f) {
+  int j, e;
+  if (fmt == kFmtInt2) {
+    const int r = f & 15;
+    j = 2 * (f >> 4) + ((f >> 2) & 1);
+    e = 2 * (r & 3) + (r >> 3);
+  } else if (fmt == kFmtInt4) {
+    const int r = f & 7;
+    j = f >> 3;
+    e = 2 * (r & 3) + (r >> 2);
+  } else {
+    const int r = f & 7;
+    j = f >> 3;
+    e = 4 * (r >> 2) + 2 * (r & 1) + ((r >> 1) & 1);
+  }
+  return 32 * j + 8 * g + e;
+}
 
 __device__ __forceinline__ void v_field(int fmt, int phi, int &k, int &e) {
   if (fmt == kFmtInt2) {
@@ -196,21 +215,23 @@ __device__ void store_fp16_block(const uint16_t *xs, uint8_t *blkp, int kv, int 
   }
 }
 
-template <int FMT>
+template <int FMT, int GS>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t blk0, int64_t nblk) {
   constexpr bool kMx = FMT == kFmtMxfp4;
   constexpr bool kNv = FMT == kFmtNvfp4 || kMx;          // E2M1 codes (NVFP4 or MXFP4 scales)
   constexpr bool kF8 = FMT == kFmtFp8;                   // fixed scale: codes only
   constexpr bool kF16 = FMT == kFmtFp16;                 // the values themselves
+  constexpr bool kAffine = is_affine(FMT);
   constexpr int kBits = kNv ? 4 : kF8 ? 8 : kF16 ? 16 : FMT;
   constexpr int kRowBytes = 16 * kBits;           // bytes per code row (128 fields)
   constexpr int kWordsPerRow = kRowBytes / 4;
   constexpr int kQmax = (1 << kBits) - 1;
-  constexpr size_t kBlockBytes = block_bytes(FMT);
+  constexpr size_t kBlockBytes = block_bytes(FMT, GS);
+  constexpr int NG = kHeadDim / GS;                      // affine groups per token
 
   // 34.8 KB of staged tokens and 1-3 KB of metadata: four workgroups fit in a CU
-  constexpr int kMeta = kMx ? 4 : kNv ? 8 : 2;  // affine: S per 64-group; NVFP4: per 16; MXFP4: per 32
-  constexpr int kAffMeta = kNv ? 1 : 2;
+  constexpr int kMeta = kMx ? 4 : kNv ? 8 : NG;  // affine: S per group; NVFP4: per 16; MXFP4: per 32
+  constexpr int kAffMeta = kNv ? 1 : NG;
   __shared__ __align__(16) uint16_t xs[kBlock * kRowHalves];
   __shared__ float mS[kBlock][kMeta];
   __shared__ float mInv[kBlock][kAffMeta];
@@ -279,15 +300,16 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
   // ---- per-group metadata (none for FP8)
   if constexpr (kF8 || kF16) {
   } else if constexpr (!kNv) {
-    const int slot = tid >> 1, g = tid & 1;
+   for (int idx = tid; idx < kBlock * NG; idx += kThreads) {
+    const int slot = idx / NG, g = idx % NG;
     uint32_t Sb = 0, Zb = 0;
     bool write = false;
     if (slot >= lo && slot < hi) {
-      // min / max of the 64 values with packed fp16 compares (exact: they only select)
-      const uint4 *row = (const uint4 *)&xs[slot * kRowHalves + g * kGroup];
+      // min / max of the GS values with packed fp16 compares (exact: they only select)
+      const uint4 *row = (const uint4 *)&xs[slot * kRowHalves + g * GS];
       half2v mn2 = {(_Float16)INFINITY, (_Float16)INFINITY}, mx2 = {-(_Float16)INFINITY, -(_Float16)INFINITY};
 #pragma unroll
-      for (int i = 0; i < kGroup / 8; ++i) {
+      for (int i = 0; i < GS / 8; ++i) {
         const uint4 v = row[i];
         const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -318,18 +340,21 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
       write = true;                            // cleared slot: S = Z = +0
     }
     if (write) {
+      // Km: per tile, S of (slot r, group g) at 2(NG r + g), the Z 32 NG bytes later; Vm: per
+      // (tile, quarter q), S of group g for slot 4q + i at 8g + 2i, the Z 8 NG bytes later
       const int tau = slot >> 4, r = slot & 15;
       if (kv == 0) {
-        uint8_t *m = blkp + aff_km(kBits) + tau * 128;
-        *(uint16_t *)(m + 4 * r + 2 * g) = (uint16_t)Sb;
-        *(uint16_t *)(m + 64 + 4 * r + 2 * g) = (uint16_t)Zb;
+        uint8_t *m = blkp + aff_km(kBits) + tau * 64 * NG;
+        *(uint16_t *)(m + 2 * (NG * r + g)) = (uint16_t)Sb;
+        *(uint16_t *)(m + 32 * NG + 2 * (NG * r + g)) = (uint16_t)Zb;
       } else {
         const int q = r >> 2, i = r & 3;
-        uint8_t *m = blkp + aff_vm(kBits) + (tau * 4 + q) * 32;
+        uint8_t *m = blkp + aff_vm(kBits, NG) + (tau * 4 + q) * 16 * NG;
         *(uint16_t *)(m + 8 * g + 2 * i) = (uint16_t)Sb;
-        *(uint16_t *)(m + 16 + 8 * g + 2 * i) = (uint16_t)Zb;
+        *(uint16_t *)(m + 8 * NG + 8 * g + 2 * i) = (uint16_t)Zb;
       }
     }
+   }
   } else if constexpr (kMx) {
     for (int idx = tid; idx < kBlock * 4; idx += kThreads) {
       const int slot = idx >> 2, m = idx & 3;
@@ -428,9 +453,16 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
       if (slot < lo || slot >= zhi) continue;
       const int omega = (r * kCb + in_chunk) / 4;    // word of the lane string
       uint32_t word = 0;
-      if (slot < hi) {
+      if (kAffine && GS == 32 && slot < hi) {
+        // groups of 32: the word's fields are permuted within runs of 8 dims; one at a time
+#pragma unroll
+        for (int k = 0; k < F; ++k) {
+          const int d = k_lane_dim32(FMT, g, omega * F + k);
+          word |= code_of(h2f(xs[slot * kRowHalves + d]), slot, d >> 5) << (k * kBits);
+        }
+      } else if (slot < hi) {
         const int d0 = k_lane_dim(FMT, g, omega * F);   // first of F consecutive dims
-        const int grp = d0 / (kMx ? kMxBlock : kNv ? kNvBlock : kGroup);
+        const int grp = d0 / (kMx ? kMxBlock : kNv ? kNvBlock : GS);
         const uint16_t *xr = &xs[slot * kRowHalves + d0];
         if constexpr (F >= 8) {
 #pragma unroll
@@ -455,7 +487,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
     // of dim 16 k + c and slot 32 w + 16 (e >> 2) + 4 g + (e & 3).  A task is (part, g, omega,
     // c0 in {0, 8}): the words of lanes 16 g + c0 .. +7, whose field j reads the same slot at
     // the 8 consecutive dims 16 k + c0 .. +7 (one 16-byte LDS read and one metadata lookup).
-    const size_t vc = kMx ? kMxVc : kNv ? kNvVc : kF8 ? kF8Vc : aff_vc(kBits);
+    const size_t vc = kMx ? kMxVc : kNv ? kNvVc : kF8 ? kF8Vc : aff_vc(kBits, NG);
     constexpr int kChunks = kBits / 2;              // 16-byte chunks per lane
     constexpr int kLaneWords = 4 * kChunks;
     constexpr int kTasks = 4 * 4 * kLaneWords * 2;
@@ -478,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
         any = true;
         if (slot >= hi) continue;                    // cleared: code 0
         const int d0 = 16 * k + c0;
-        const int grp = d0 / (kMx ? kMxBlock : kNv ? kNvBlock : kGroup);
+        const int grp = d0 / (kMx ? kMxBlock : kNv ? kNvBlock : GS);
         float x[8];
         unpack8(*(const uint4 *)&xs[slot * kRowHalves + d0], x);
 #pragma unroll
@@ -514,16 +546,24 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t s) {
   const int64_t blk1 = (a.dst_slot0 + a.count - 1) / kBlock;
   const int64_t nblk = blk1 - blk0 + 1;
   dim3 grid((unsigned)nblk, (unsigned)a.H, (unsigned)(a.B * 2));
+#define KVQ_AFFINE_CASE(F)                                                                             \
+  case F:                                                                                              \
+    if (a.gs == 32) quantize_kernel<F, 32><<<grid, kThreads, 0, s>>>(a, blk0, nblk);                   \
+    else if (a.gs == 128) quantize_kernel<F, 128><<<grid, kThreads, 0, s>>>(a, blk0, nblk);            \
+    else if (a.gs == 64) quantize_kernel<F, 64><<<grid, kThreads, 0, s>>>(a, blk0, nblk);              \
+    else return hipErrorInvalidValue;                                                                  \
+    break;
   switch (a.fmt) {
-    case kFmtInt2: quantize_kernel<kFmtInt2><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
-    case kFmtInt4: quantize_kernel<kFmtInt4><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
-    case kFmtInt8: quantize_kernel<kFmtInt8><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
-    case kFmtNvfp4: quantize_kernel<kFmtNvfp4><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
-    case kFmtFp8: quantize_kernel<kFmtFp8><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
-    case kFmtMxfp4: quantize_kernel<kFmtMxfp4><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
-    case kFmtFp16: quantize_kernel<kFmtFp16><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
+    KVQ_AFFINE_CASE(kFmtInt2)
+    KVQ_AFFINE_CASE(kFmtInt4)
+    KVQ_AFFINE_CASE(kFmtInt8)
+    case kFmtNvfp4: quantize_kernel<kFmtNvfp4, 64><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
+    case kFmtFp8: quantize_kernel<kFmtFp8, 64><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
+    case kFmtMxfp4: quantize_kernel<kFmtMxfp4, 64><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
+    case kFmtFp16: quantize_kernel<kFmtFp16, 64><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
     default: return hipErrorInvalidValue;
   }
+#undef KVQ_AFFINE_CASE
   return hipGetLastError();
 }
 

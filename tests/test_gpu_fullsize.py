@@ -15,7 +15,7 @@ import kvq_synth as syn
 from oracle.cache import LayerCache
 from oracle.attention import decode_layer
 from oracle import layout as olayout
-from oracle.quant import quantize_tokens
+from oracle.quant import quantize_tokens, affine_params
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +50,8 @@ def _check_blocks(cache, ora: LayerCache, b, h, tier, region):
         elif fmt == "fp16":
             want = olayout.pack_fp16_block(kq, vq, sl.size)
         else:
-            want = olayout.pack_affine_block(int(fmt[3:]), kq, vq, sl.size)
+            n, gs = affine_params(fmt)
+            want = olayout.pack_affine_block(n, kq, vq, sl.size, gs)
         got = dev[b, h, blk * bb:(blk + 1) * bb].cpu().numpy()
         assert np.array_equal(got, want), f"{tier} block {blk} of (b={b}, h={h}) differs"
     return 1
@@ -126,6 +127,14 @@ def test_fullsize_long_context_128k_fp8():
 
 def test_fullsize_llama3_70b_gqa8_32k_fp8():
     _run(3, "fp8", n_pairs=2)
+
+
+def test_fullsize_long_context_128k_int4_groups_of_32():
+    _run(4, "int4g32", steps=1, n_pairs=2)
+
+
+def test_fullsize_long_context_128k_int4_groups_of_128():
+    _run(4, "int4g128", steps=1, n_pairs=2)
 
 
 def test_fullsize_long_context_128k_mxfp4():

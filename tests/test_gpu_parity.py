@@ -130,6 +130,55 @@ def test_fp16_every_fp16_value():
     p.check_bytes(0)
 
 
+GROUP_FORMATS = ["int2g32", "int4g32", "int8g32", "int2g128", "int4g128", "int8g128"]
+
+
+@pytest.mark.parametrize("fmt", GROUP_FORMATS)
+def test_group_sizes_bytes_exact(fmt):
+    rng = np.random.default_rng(sum(map(ord, fmt)))
+    B, H = 2, 2
+    p = Pair(1, B, H, 2000, fmt, 128)
+    for n in [300, 1, 127, "flush", 129, 250]:
+        if n == "flush":
+            p.flush(0)
+            continue
+        p.append(0, adversarial_tokens(rng, B, H, n), adversarial_tokens(rng, B, H, n))
+        p.check_bytes(0)
+
+
+@pytest.mark.parametrize("fmt", GROUP_FORMATS)
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_group_sizes_decode(fmt, G):
+    rng = np.random.default_rng(G + sum(map(ord, fmt)))
+    B, H = 2, 2
+    p = Pair(1, B, H, 1400, fmt, 128)
+    for L in (129, 1000):
+        k = rng.standard_normal((B, H, L, 128)).astype(np.float16)
+        k[..., :4] *= 15
+        p.append(0, k, rng.standard_normal((B, H, L, 128)).astype(np.float16))
+        q = (rng.standard_normal((B, H * G, 128)) / np.sqrt(128)).astype(np.float16)
+        for sigma in (1 / np.sqrt(128), 1.0):
+            got, want = p.decode(0, q, sigma)
+            assert_attention_close(got, want)
+
+
+def test_group_size_tiers():
+    """Young INT4 and old INT2 tiers sharing groups of 32; adversarial values; decode."""
+    rng = np.random.default_rng(31)
+    B, H, G = 1, 2, 8
+    p = Pair(1, B, H, 3000, "int4g32", 128, "int2g32", 700)
+    for n in [1800, 1, 300, "flush", 200]:
+        if n == "flush":
+            p.flush(0)
+            continue
+        p.append(0, adversarial_tokens(rng, B, H, n), adversarial_tokens(rng, B, H, n))
+        p.check_bytes(0)
+    assert p.gpu.layout(0, 2)[2] > 0
+    q = (rng.standard_normal((B, H * G, 128)) / np.sqrt(128)).astype(np.float16)
+    got, want = p.decode(0, q, 1 / np.sqrt(128))
+    assert_attention_close(got, want)
+
+
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("G", [1, 4, 8])
 @pytest.mark.parametrize("L", [1, 2, 127, 128, 129, 1000])
