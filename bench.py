@@ -142,7 +142,7 @@ def read_probe_gbs() -> float:
     return best
 
 
-NOISE_FORMATS = ("int8", "fp8", "nvfp4", "mxfp4", "int4", "int2")
+NOISE_FORMATS = ("int8", "fp8", "int4g32", "int4", "int4g128", "nvfp4", "mxfp4", "int2g32", "int2")
 
 
 def noise_study(lengths, n_queries: int):

@@ -162,6 +162,23 @@ def test_group_sizes_decode(fmt, G):
             assert_attention_close(got, want)
 
 
+def test_debugging_configuration_group32_residual256():
+    """The page's debugging configuration: 4 bits, groups of 32, a 256-token residual; flushes
+    by filling the residual and explicitly, decode after each."""
+    rng = np.random.default_rng(256)
+    B, H, G = 2, 2, 4
+    p = Pair(1, B, H, 3000, "int4g32", 256)
+    q = (rng.standard_normal((B, H * G, 128)) / np.sqrt(128)).astype(np.float16)
+    for n in [255, 1, 1, 600, "flush", 3, 300]:
+        if n == "flush":
+            p.flush(0)
+        else:
+            p.append(0, adversarial_tokens(rng, B, H, n), adversarial_tokens(rng, B, H, n))
+        p.check_bytes(0)
+        got, want = p.decode(0, q, 1 / np.sqrt(128))
+        assert_attention_close(got, want)
+
+
 def test_group_size_tiers():
     """Young INT4 and old INT2 tiers sharing groups of 32; adversarial values; decode."""
     rng = np.random.default_rng(31)
