@@ -105,7 +105,7 @@ class LayerCache:
         K, V = self.history(b, h)
         pos = np.asarray(self.tier_tokens(tier), dtype=np.int64)
         fmt = self.tier_format(tier)
-        return pack_arena(fmt, quantize_tokens(K[pos], fmt), quantize_tokens(V[pos], fmt))
+        return pack_arena(fmt, quantize_tokens(K[pos], fmt, "k"), quantize_tokens(V[pos], fmt, "v"))
 
     def residual(self, b: int, h: int) -> tuple[np.ndarray, np.ndarray]:
         K, V = self.history(b, h)
@@ -120,8 +120,8 @@ class LayerCache:
             pos = np.asarray(self.tier_tokens(tier), dtype=np.int64)
             if pos.size:
                 fmt = self.tier_format(tier)
-                ks.append(dequantize_tokens(quantize_tokens(K[pos], fmt), fmt))
-                vs.append(dequantize_tokens(quantize_tokens(V[pos], fmt), fmt))
+                ks.append(dequantize_tokens(quantize_tokens(K[pos], fmt, "k"), fmt, "k"))
+                vs.append(dequantize_tokens(quantize_tokens(V[pos], fmt, "v"), fmt, "v"))
         pos = np.asarray(self.sched.residual, dtype=np.int64)
         if pos.size:
             ks.append(K[pos].astype(np.float64))

@@ -42,6 +42,10 @@ Vc (2048n bytes; NVFP4 8192): 4 parts w, each 64 lanes L (g = L div 16,
              e = 2(m mod 4) + m div 8
       INT8:  u = phi div 4, b = phi mod 4, k = u div 2,
              e = 4(u mod 2) + 2(b mod 2) + b div 2
+Per-channel K ("int{n}kc"): Kc as groups of 64; Km (512 bytes) holds the block's per-dim S
+    (256 bytes) then Z: fp16 at 2(32g + 8j + e) for the dim fed by element e of MFMA k-step j
+    in lane quarter g (the dim of the field f whose (j, e) is that pair, in the table above);
+    Vc and Vm as groups of 64.
 Vm, affine (512 NG bytes): 8 tiles tau x 4 quarters g of 16 NG bytes at (4tau + g)*16NG:
     fp16 S of group G for slots 16tau + 4g + i (i = 0..3) at 8G + 2i, then the Z likewise
     from 8NG (NG = 2: S of group 0, S of group 1, Z of group 0, Z of group 1).
@@ -74,13 +78,15 @@ from __future__ import annotations
 
 import numpy as np
 
-from .quant import affine_params
+from .quant import affine_params, k_per_channel
 
 D = 128
 BLOCK = 128
 
 
-def affine_block_bytes(n: int, gs: int = 64) -> int:
+def affine_block_bytes(n: int, gs: int = 64, kc: bool = False) -> int:
+    if kc:
+        return 4096 * n + 512 + 1024
     return 4096 * n + 1024 * (128 // gs)
 
 
@@ -100,7 +106,7 @@ def block_bytes(fmt: str) -> int:
     if fmt == "fp16":
         return FP16_BLOCK_BYTES
     n, gs = affine_params(fmt)
-    return affine_block_bytes(n, gs)
+    return affine_block_bytes(n, gs, k_per_channel(fmt))
 
 
 def k_lane_dims(fmt: str, g: int) -> np.ndarray:
@@ -110,18 +116,33 @@ def k_lane_dims(fmt: str, g: int) -> np.ndarray:
         return 32 * g + f
     ap = affine_params(fmt)
     if ap and ap[1] == 32:
-        n = ap[0]
-        if n == 2:
-            j, r = 2 * (f // 16) + (f // 4) % 2, f % 16
-            e = 2 * (r % 4) + r // 8
-        elif n == 4:
-            j, r = f // 8, f % 8
-            e = 2 * (r % 4) + r // 4
-        else:
-            j, r = f // 8, f % 8
-            e = 4 * (r // 4) + 2 * (r % 2) + (r // 2) % 2
+        j, e = step_elem(ap[0], f)
         return 32 * j + 8 * g + e
     return 64 * (f // 16) + 16 * g + f % 16
+
+
+def step_elem(n: int, f):
+    """(k-step j, element e) of the decode kernel's MFMA operand that K lane field f feeds."""
+    f = np.asarray(f)
+    if n == 2:
+        j, r = 2 * (f // 16) + (f // 4) % 2, f % 16
+        e = 2 * (r % 4) + r // 8
+    elif n == 4:
+        j, r = f // 8, f % 8
+        e = 2 * (r % 4) + r // 4
+    else:
+        j, r = f // 8, f % 8
+        e = 4 * (r // 4) + 2 * (r % 2) + (r // 2) % 2
+    return j, e
+
+
+def k_operand_dims(n: int, g: int) -> np.ndarray:
+    """[4, 8]: dim fed by element e of k-step j in lane quarter g (K lanes of groups of 64)."""
+    f = np.arange(32)
+    j, e = step_elem(n, f)
+    out = np.full((4, 8), -1, np.int64)
+    out[j, e] = k_lane_dims(f"int{n}", g)
+    return out
 
 
 def _pack_kc(fmt: str, codes_k: np.ndarray) -> np.ndarray:
@@ -237,6 +258,22 @@ def pack_affine_block(n: int, kq: dict, vq: dict, used: int, gs: int = 64) -> np
     return out
 
 
+def pack_affine_kc_block(n: int, kq: dict, vq: dict) -> np.ndarray:
+    """One block of per-channel K (kq: codes [128, 128], S and Z [128] of the block's window)
+    and per-token V in groups of 64 (vq as quantize_tokens() gives it for the 128 slots)."""
+    fmt = f"int{n}"
+    kc = _pack_kc(fmt, np.asarray(kq["codes"], np.uint8))
+    order = np.concatenate([k_operand_dims(n, g).ravel() for g in range(4)])    # position -> dim
+    km = np.concatenate([f16_bytes(np.asarray(kq["S"], np.float16)[order]),
+                         f16_bytes(np.asarray(kq["Z"], np.float16)[order])])
+    full = pack_affine_block(n, {"codes": np.zeros((BLOCK, D), np.uint8), "S": np.zeros((BLOCK, 2), np.float16),
+                                 "Z": np.zeros((BLOCK, 2), np.float16)}, vq, BLOCK, 64)
+    vpart = full[2048 * n + 1024:]                                              # Vc and Vm of groups of 64
+    out = np.concatenate([kc, km, vpart])
+    assert out.size == affine_block_bytes(n, 64, True)
+    return out
+
+
 def pack_nvfp4_block(kq: dict, vq: dict, used: int) -> np.ndarray:
     codes_k = np.zeros((BLOCK, D), np.uint8); codes_k[:used] = kq["codes"]
     codes_v = np.zeros((BLOCK, D), np.uint8); codes_v[:used] = vq["codes"]
@@ -304,6 +341,13 @@ def pack_arena(fmt: str, kq: dict, vq: dict) -> np.ndarray:
     N = kq["codes"].shape[0]
     nblk = (N + BLOCK - 1) // BLOCK
     blocks = []
+    if k_per_channel(fmt):
+        n = affine_params(fmt)[0]
+        for b in range(nblk):
+            sl = slice(b * BLOCK, (b + 1) * BLOCK)
+            blocks.append(pack_affine_kc_block(n, {"codes": kq["codes"][sl], "S": kq["S"][b], "Z": kq["Z"][b]},
+                                               {k: v[sl] for k, v in vq.items()}))
+        return np.stack(blocks) if blocks else np.zeros((0, block_bytes(fmt)), np.uint8)
     for b in range(nblk):
         lo, hi = b * BLOCK, min(N, (b + 1) * BLOCK)
         sl = {k: v[lo:hi] for k, v in kq.items()}

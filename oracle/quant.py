@@ -6,7 +6,10 @@ Affine (asymmetric) quantization -- page "KV缓存量化技术：提升大模型
 (rkmt.cn/news/1711363) §2.1: S = (max - min) / (2^n - 1), Z = round(-min / S),
 one (S, Z) per group of 64 elements, codes stored as n-bit integers.  The same page's §4.3
 debugging configuration uses groups of 32 (and a 256-token residual); groups of 32, 64 and 128
-contiguous head_dim values are supported, named "int4g32", "int4" (64) and "int4g128".  The page
+contiguous head_dim values are supported, named "int4g32", "int4" (64) and "int4g128".  The
+same §2.1 lists per-channel quantization among the scheme's options: "int4kc" quantizes K per
+channel -- each dim's values over a window of 128 consecutive tokens form one group (the
+residual fills and flushes in whole windows) -- and V per token in groups of 64.  The page
 prints the code as round(X/S) - Z; with Z = round(-min/S) that sends min to
 about -2Z, outside [0, 2^n - 1].  The reading adopted here is the one under which
 codes land in [0, 2^n - 1]:
@@ -65,12 +68,20 @@ MX_BLOCK = 32
 E2M1_EMAX = 2            # exponent of E2M1's largest magnitude, 6 = 1.5 * 2^2
 
 
+KC_WINDOW = 128         # tokens per per-channel K group
+
+
 def affine_params(fmt: str):
-    """(code bits, group size) of an affine format name ("int4", "int2g32", "int8g128"), else None."""
-    m = re.fullmatch(r"int([248])(?:g(32|64|128))?", fmt)
+    """(code bits, group size along head_dim) of an affine format name ("int4", "int2g32",
+    "int8g128", "int4kc": V in groups of 64), else None."""
+    m = re.fullmatch(r"int([248])(?:g(32|64|128)|kc)?", fmt)
     if not m:
         return None
     return int(m.group(1)), int(m.group(2) or GROUP)
+
+
+def k_per_channel(fmt: str) -> bool:
+    return fmt.endswith("kc") and affine_params(fmt) is not None
 
 
 def affine_quantize(x16: np.ndarray, nbits: int):
@@ -140,11 +151,13 @@ def mxfp4_dequantize(codes: np.ndarray, sbyte: np.ndarray) -> np.ndarray:
     return e2m1_decode(codes) * e8m0_decode(sbyte)[..., None]
 
 
-def quantize_tokens(x16: np.ndarray, fmt: str):
-    """Quantize token rows of head_dim 128: x16 fp16 [N, 128].
+def quantize_tokens(x16: np.ndarray, fmt: str, tensor: str = "v"):
+    """Quantize token rows of head_dim 128: x16 fp16 [N, 128] (tensor "k" or "v": only the
+    per-channel formats treat K differently).
 
     Returns a dict with the stored fields:
       affine: codes [N,128], S [N,128/g], Z [N,128/g] (g the group size)
+      per-channel K: codes [N,128], S [N/128, 128], Z [N/128, 128] (one pair per dim and window)
       nvfp4 : codes [N,128], scale [N,8]
       mxfp4 : codes [N,128], scale [N,4] (E8M0 bytes)
       fp8   : codes [N,128] (E4M3 bytes)
@@ -153,6 +166,11 @@ def quantize_tokens(x16: np.ndarray, fmt: str):
     x16 = np.asarray(x16, dtype=np.float16)
     N, D = x16.shape
     ap = affine_params(fmt)
+    if ap and k_per_channel(fmt) and tensor == "k":
+        assert N % KC_WINDOW == 0, "per-channel K is quantized in whole windows"
+        w = x16.reshape(N // KC_WINDOW, KC_WINDOW, D).transpose(0, 2, 1)          # [window, dim, token]
+        q, S, Z = affine_quantize(w, ap[0])
+        return {"codes": np.ascontiguousarray(q.transpose(0, 2, 1)).reshape(N, D), "S": S, "Z": Z}
     if ap:
         nb, gs = ap
         q, S, Z = affine_quantize(x16.reshape(N, D // gs, gs), nb)
@@ -170,10 +188,13 @@ def quantize_tokens(x16: np.ndarray, fmt: str):
     raise ValueError(fmt)
 
 
-def dequantize_tokens(qt: dict, fmt: str) -> np.ndarray:
+def dequantize_tokens(qt: dict, fmt: str, tensor: str = "v") -> np.ndarray:
     """float64 [N, 128] decoded values of quantize_tokens()' output."""
     codes = qt["codes"]
     N, D = codes.shape
+    if k_per_channel(fmt) and tensor == "k":
+        c = codes.reshape(N // KC_WINDOW, KC_WINDOW, D).transpose(0, 2, 1)
+        return affine_dequantize(c, qt["S"], qt["Z"]).transpose(0, 2, 1).reshape(N, D)
     ap = affine_params(fmt)
     if ap:
         gs = ap[1]

@@ -76,6 +76,30 @@ def test_mx_scale_positions(case):
     assert list(np.flatnonzero(blk)) == [case["byte"]]
 
 
+@pytest.mark.parametrize("case", GOLDEN["kc_meta_cases"], ids=lambda c: f"{c['fmt']}-{c['field']}-{c['dim']}")
+def test_per_channel_k_meta_positions(case):
+    n = quant.affine_params(case["fmt"])[0]
+    kq = {"codes": np.zeros((128, 128), np.uint8), "S": np.zeros(128, np.float16), "Z": np.zeros(128, np.float16)}
+    kq[case["field"]][case["dim"]] = 1.5                                   # 0x3E00
+    blk = layout.pack_affine_kc_block(n, kq, _empty("int4"))
+    assert list(np.flatnonzero(blk)) == [case["byte"] + 1] and blk[case["byte"] + 1] == 0x3E
+
+
+@pytest.mark.parametrize("n", [2, 4, 8])
+def test_per_channel_k_block_coverage(n):
+    """All-ones codes, S, Z and V fields fill the whole block; the operand order lists every
+    dim once per block and each quarter's 32 dims are the quarter's K lane dims."""
+    ones = np.uint16(0xFFFF).view(np.float16)
+    kq = {"codes": np.full((128, 128), (1 << n) - 1, np.uint8), "S": np.full(128, ones), "Z": np.full(128, ones)}
+    vq = {"codes": np.full((128, 128), (1 << n) - 1, np.uint8), "S": np.full((128, 2), ones), "Z": np.full((128, 2), ones)}
+    blk = layout.pack_affine_kc_block(n, kq, vq)
+    assert np.all(blk == 0xFF) and blk.size == layout.block_bytes(f"int{n}kc") == 4096 * n + 1536
+    order = [layout.k_operand_dims(n, g) for g in range(4)]
+    assert sorted(np.concatenate([o.ravel() for o in order])) == list(range(128))
+    for g in range(4):
+        assert sorted(order[g].ravel()) == sorted(layout.k_lane_dims(f"int{n}", g))
+
+
 @pytest.mark.parametrize("case", GOLDEN["residual_cases"], ids=lambda c: c["part"])
 def test_residual_positions(case):
     R = case["R"]

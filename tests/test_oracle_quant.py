@@ -233,3 +233,25 @@ def test_affine_format_names():
     assert quant.affine_params("int8g128") == (8, 128)
     for bad in ("int3", "int4g16", "nvfp4", "fp8", "int4g"):
         assert quant.affine_params(bad) is None
+
+
+@pytest.mark.parametrize("fmt", ["int4kc", "int2kc", "int8kc"])
+def test_per_channel_k_groups_are_dims_of_a_window(fmt):
+    """K: each dim's values over a window of 128 consecutive tokens are one affine group; V
+    is quantized per token exactly as the groups-of-64 format."""
+    n = quant.affine_params(fmt)[0]
+    x = _groups(7, 128, 128)[:256]                      # two windows of 128 tokens
+    x[:, 9] = np.clip(x[:, 9].astype(np.float64) * 40, -65504, 65504).astype(np.float16)   # an outlier channel
+    qk = quant.quantize_tokens(x, fmt, "k")
+    assert qk["S"].shape == (2, 128)
+    for w in range(2):
+        win = x[128 * w:128 * (w + 1)]
+        q, S, Z = quant.affine_quantize(np.ascontiguousarray(win.T), n)      # rows = dims
+        assert np.array_equal(qk["codes"][128 * w:128 * (w + 1)], q.T)
+        assert np.array_equal(qk["S"][w], S) and np.array_equal(qk["Z"][w], Z)
+    xh = quant.dequantize_tokens(qk, fmt, "k")
+    assert np.array_equal(xh[:128, 9], quant.affine_dequantize(qk["codes"][:128, 9][None], qk["S"][0, 9:10], qk["Z"][0, 9:10])[0])
+    qv, qv64 = quant.quantize_tokens(x, fmt, "v"), quant.quantize_tokens(x, f"int{n}")
+    assert all(np.array_equal(qv[k], qv64[k]) for k in qv64)
+    with pytest.raises(AssertionError):
+        quant.quantize_tokens(x[:100], fmt, "k")

@@ -49,6 +49,8 @@ def test_stored_bytes_include_metadata():
     assert sizes.stored_bytes_per_token("int4g32") == 2 * 128 * 5 / 8
     assert sizes.stored_bytes_per_token("int4g128") == 2 * 128 * 4.25 / 8
     assert sizes.stored_bytes_per_token("int2g32") == 2 * 128 * 3 / 8
+    # per-channel K: one (S, Z) pair per dim per 128 tokens (4 bytes per 128 values) + V in groups of 64
+    assert sizes.stored_bytes_per_token("int4kc") == 128 * (4 + 32 / 128) / 8 + 128 * 4.5 / 8
     # MXFP4: 4-bit codes + one byte per 32 values = 4.25 bits
     assert sizes.stored_bytes_per_token("mxfp4") == 2 * 128 * 4.25 / 8
     # the page's FP8 row: 32 layers / 8 kv heads / 32K tokens at one byte per value = 2 GiB
