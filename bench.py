@@ -36,16 +36,18 @@ DECODE_SRC = os.path.join(ROOT, "bit_quantized_kv_kvq_amd", "csrc", "kvq_decode.
 WORKLOADS = {
     "c1": (1, None), "c2": (2, None), "c3": (3, None),
     "c4-int4": (4, "int4"), "c4-int2": (4, "int2"), "c5": (5, None),
-    "c4-int4g32": (4, "int4g32"), "c4-int4g128": (4, "int4g128"),
+    "c4-int4g32": (4, "int4g32"), "c4-int4g128": (4, "int4g128"), "c4-int4kc": (4, "int4kc"),
     "c3-mxfp4": (3, "mxfp4"), "c4-mxfp4": (4, "mxfp4"), "c3-fp8": (3, "fp8"), "c4-fp8": (4, "fp8"), "c3-fp16": (3, "fp16"), "c4-fp16": (4, "fp16"),
 }
 
 
 def bytes_per_token(fmt: str) -> float:
     """Stored bytes of one token of one (batch, kv_head), K and V together."""
-    m = re.fullmatch(r"int([248])(?:g(32|64|128))?", fmt)
+    m = re.fullmatch(r"int([248])(?:g(32|64|128)|(kc))?", fmt)
     if m:   # n-bit codes + one fp16 (S, Z) pair per group of K and of V
         n, gs = int(m.group(1)), int(m.group(2) or 64)
+        if m.group(3):   # K per channel: one pair per dim per 128-token block
+            return (4096 * n + 1536) / 128
         return (4096 * n + 1024 * (128 // gs)) / 128
     return {"nvfp4": 18432 / 128, "mxfp4": 17408 / 128, "fp8": 32768 / 128, "fp16": 512.0}[fmt]
 
@@ -142,7 +144,7 @@ def read_probe_gbs() -> float:
     return best
 
 
-NOISE_FORMATS = ("int8", "fp8", "int4g32", "int4", "int4g128", "nvfp4", "mxfp4", "int2g32", "int2")
+NOISE_FORMATS = ("int8", "fp8", "int4g32", "int4", "int4kc", "int4g128", "nvfp4", "mxfp4", "int2g32", "int2kc", "int2")
 
 
 def noise_study(lengths, n_queries: int):
@@ -169,11 +171,16 @@ def noise_study(lengths, n_queries: int):
         qs = [syn.draw_q_dev(cid, 0, 1, H * G, s) for s in range(n_queries)]
         outs = {}
         for fmt in ("fp16",) + NOISE_FORMATS:
-            cache = kvq.Cache(kvq.make_config(1, 1, H, Lmax, fmt, 0))
+            # per-channel K fills 128-token windows through the residual; a flush after each
+            # append (the lengths are whole windows) leaves every token quantized, as R = 0 does
+            R = 128 if fmt.endswith("kc") else 0
+            cache = kvq.Cache(kvq.make_config(1, 1, H, Lmax, fmt, R))
             ws = torch.empty(cache.workspace_bytes(H * G), dtype=torch.uint8, device="cuda")
             done = 0
             for L in sorted(lengths):
                 cache.append(0, k[:, :, done:L].contiguous(), v[:, :, done:L].contiguous())
+                if R:
+                    cache.flush(0)
                 done = L
                 o = torch.empty((n_queries, H * G, 128), dtype=torch.float32, device="cuda")
                 for i, q in enumerate(qs):

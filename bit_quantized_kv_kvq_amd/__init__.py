@@ -34,7 +34,7 @@ class kvq_config(ctypes.Structure):
     _fields_ = [("num_layers", ctypes.c_int32), ("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("max_tokens", ctypes.c_int64), ("format", ctypes.c_int32),
                 ("group_size", ctypes.c_int32), ("residual_len", ctypes.c_int32), ("old_format", ctypes.c_int32),
-                ("old_after", ctypes.c_int64)]
+                ("old_after", ctypes.c_int64), ("k_per_channel", ctypes.c_int32)]
 
 
 _lib = None
@@ -83,6 +83,9 @@ def parse_format(name: str):
     m = re.fullmatch(r"(int[248])g(32|64|128)", name)
     if m:
         return FMT[m.group(1)], int(m.group(2))
+    m = re.fullmatch(r"(int[248])kc", name)      # K per channel over 128-token windows, V in groups of 64
+    if m:
+        return FMT[m.group(1)], 64
     if name not in FMT:
         raise ValueError(f"unknown cache format {name!r}")
     return FMT[name], GROUP_SIZE[name]
@@ -96,8 +99,11 @@ def make_config(num_layers, batch, num_kv_heads, max_tokens, fmt="int4", residua
     old_code, old_gs = parse_format(old_fmt or fmt)
     if old_fmt and old_code in (2, 4, 8) and old_gs != (gs if code in (2, 4, 8) else 64):
         raise ValueError(f"old tier {old_fmt!r} must use the group size of the young tier ({fmt!r})")
+    kc = fmt.endswith("kc")
+    if old_fmt and old_code in (2, 4, 8) and old_fmt.endswith("kc") != kc:
+        raise ValueError(f"old tier {old_fmt!r} must quantize K like the young tier ({fmt!r})")
     return kvq_config(num_layers, batch, num_kv_heads, head_dim, max_tokens, code, gs, residual_len,
-                      old_code, old_after)
+                      old_code, old_after, int(kc))
 
 
 def kvq_cache_bytes(cfg: kvq_config) -> int:

@@ -51,6 +51,7 @@ int group_of(int f) {
 // is affine too, else 64; the other formats have their own fixed grouping (64 passed along).
 int tier_gs(const kvq_config *c, int fmt) {
   if (!is_affine(fmt)) return kGroup;
+  if (c->k_per_channel) return kKc;
   return is_affine(c->format) ? c->group_size : kGroup;
 }
 
@@ -80,6 +81,13 @@ const char *check_config(const kvq_config *c) {
   if (c->residual_len < 0 || c->residual_len > 1024 || c->residual_len % 16 != 0)
     return "residual_len must be 0 or a multiple of 16 up to 1024";
   if (c->old_after < 0) return "old_after must be >= 0";
+  if (c->k_per_channel != 0 && c->k_per_channel != 1) return "k_per_channel must be 0 or 1";
+  if (c->k_per_channel) {
+    if (!is_affine(c->format) || c->group_size != kGroup) return "k_per_channel needs an affine format with group_size 64";
+    if (c->residual_len == 0 || c->residual_len % kBlock != 0)
+      return "k_per_channel needs residual_len a positive multiple of 128 (whole windows)";
+    if (c->old_after > 0 && !is_affine(c->old_format)) return "k_per_channel needs an affine old_format";
+  }
   if (c->old_after > 0) {
     if (!is_block_fmt(c->old_format)) return "old_format must be a block format when old_after > 0";
   }
@@ -227,6 +235,9 @@ int run_plan(kvq_cache *c, int layer, const Plan &p, const void *k, const void *
       a.dst_slot0 = op.dst_slot0;
       a.fmt = op.tier ? cfg.old_format : cfg.format;
       a.gs = tier_gs(&cfg, a.fmt);
+      if (a.gs == kKc && (op.dst_slot0 % kBlock != 0 || op.count % kBlock != 0))
+        return fail(KVQ_ESTATE, "per-channel K: a quantize of %lld slots at %lld is not whole windows",
+                    (long long)op.count, (long long)op.dst_slot0);
       a.B = cfg.batch; a.H = cfg.num_kv_heads;
       if (int e = hip_check(launch_quantize(a, s), "quantize")) return e;
     }
@@ -384,6 +395,9 @@ int kvq_flush_residual(kvq_cache *c, int32_t layer, void *stream) {
   if (int e = check_cache(c, layer)) return e;
   LayerState &st = c->layers[layer];
   if (st.res == 0) return KVQ_OK;
+  if (c->cfg.k_per_channel && st.res % kBlock != 0)
+    return fail(KVQ_ESTATE, "per-channel K quantizes whole windows of 128 tokens; the residual holds %lld",
+                (long long)st.res);
   Plan p;
   p.after = st;
   add_quant(p, Op::kQuantResidual, 0, st.res, chunk_tier(c->cfg, st.length, st.length));

@@ -195,10 +195,13 @@ __device__ __forceinline__ int q_dim(int g, int j, int e, bool &scaled) {
 
 // Affine group of MFMA k-step j (groups of 32: one per step; 64: steps 2G, 2G + 1; 128: all)
 // and of V dim tile k (dims 16k .. 16k + 15).
+// (kKc, per-channel K, has V groups of 64 and no K groups along head_dim.)
 template <int GS>
-__device__ __forceinline__ constexpr int k_group(int j) { return GS == 32 ? j : GS == 64 ? j >> 1 : 0; }
+__device__ __forceinline__ constexpr int k_group(int j) { return GS == 32 ? j : (GS == 64 || GS == kKc) ? j >> 1 : 0; }
 template <int GS>
-__device__ __forceinline__ constexpr int v_group(int k) { return GS == 32 ? k >> 1 : GS == 64 ? k >> 2 : 0; }
+__device__ __forceinline__ constexpr int v_group(int k) { return GS == 32 ? k >> 1 : (GS == 64 || GS == kKc) ? k >> 2 : 0; }
+template <int GS>
+constexpr int kGroups = GS == kKc ? 2 : kHeadDim / GS;   // per-token groups along head_dim
 
 // The 32 dims a lane quarter g feeds: affine formats (groups of 64 or 128) and FP8 dims
 // 16g..16g+15 and 64+16g..64+16g+15 (local index 16G + m); affine groups of 32 dims 32j + 8g
@@ -246,7 +249,7 @@ __device__ __forceinline__ void load_q(const uint16_t *qrow, bool valid, int g, 
   // group sums over the four lane quarters (lanes c, c+16, c+32, c+48 hold one head), in the
   // 2^-24 units of the subnormal code operands
 #pragma unroll
-  for (int G = 0; G < kHeadDim / GS; ++G) qs[G] = quad_sum(qs[G]) * kSub;
+  for (int G = 0; G < kGroups<GS>; ++G) qs[G] = quad_sum(qs[G]) * kSub;
 }
 
 // ---------------------------------------------------------------- LDS DMA
@@ -369,11 +372,28 @@ __device__ __forceinline__ void lds_words(const uint8_t *p, uint32_t (&w)[N]) {
 }
 __device__ __forceinline__ float half_of(uint32_t word, int h) { return h ? hi_f(word) : lo_f(word); }
 
+// Per-channel K: add a Q operand's sum of (qh + ql) Z over its 8 elements into b1 (or b16 for
+// the INT4 elements 2, 3, 6, 7, which meet codes times 16)
+template <bool kInt4>
+__device__ __forceinline__ void kc_zero_point(half8_t qh, half8_t ql, uint4 zv, float &b1, float &b16) {
+  const uint4 hw = __builtin_bit_cast(uint4, qh), lw = __builtin_bit_cast(uint4, ql);
+  const uint32_t h[4] = {hw.x, hw.y, hw.z, hw.w}, l[4] = {lw.x, lw.y, lw.z, lw.w}, z[4] = {zv.x, zv.y, zv.z, zv.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float &b = (kInt4 && (k & 1)) ? b16 : b1;
+    b = __builtin_amdgcn_fdot2(as_h2(h[k]), as_h2(z[k]), b, false);
+    b = __builtin_amdgcn_fdot2(as_h2(l[k]), as_h2(z[k]), b, false);
+  }
+}
+
 template <int NB, int GS, bool TAIL>
 __device__ __forceinline__ void affine_step(const uint8_t *blk, int w, int g, int c, const QOp &q, float sl2,
                                             bool valid_head, int nvalid, State &st) {
-  constexpr int NG = kHeadDim / GS;   // groups per token
-  constexpr int kKm = 2048 * NB, kVc = 2048 * NB + 512 * NG, kVm = 4096 * NB + 512 * NG;
+  constexpr bool kKcK = GS == kKc;          // K per channel: one (S, Z) per dim for the whole block
+  constexpr int NG = kGroups<GS>;           // per-token groups (of V; also of K unless per channel)
+  constexpr int kKm = 2048 * NB;
+  constexpr int kVc = kKcK ? 2048 * NB + 512 : 2048 * NB + 512 * NG;
+  constexpr int kVm = kKcK ? 4096 * NB + 512 : 4096 * NB + 512 * NG;
   const int lane = 16 * g + c;
   const half8_t (&qb)[4] = q.qb;
 
@@ -411,6 +431,26 @@ __device__ __forceinline__ void affine_step(const uint8_t *blk, int w, int g, in
     lds_words<2 * NG>(m + 8 * NG, vzw[tt]);
   }
 
+  // Per-channel K: the block's per-dim S is folded into Q as two fp16 terms, qh = RN(q S) and
+  // ql = q S - qh (exact through a fused multiply-add: an fp16 product has at most 22
+  // significant bits), so the logits keep the accuracy of an fp32 product; the head's
+  // sum_d q_d S_d Z_d, the same for every token of the block, leaves each logit.
+  half8_t qkh[4], qkl[4];
+  float bq = 0.0f;
+  if constexpr (kKcK) {
+    const uint8_t *km = blk + kKm + 64 * g;            // (S, Z) in operand order: 32g + 8j + e
+    float b1 = 0.0f, b16 = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 sv = *(const uint4 *)(km + 16 * j), zv = *(const uint4 *)(km + 256 + 16 * j);
+      const half8_t s8 = __builtin_bit_cast(half8_t, sv);
+      qkh[j] = qb[j] * s8;
+      qkl[j] = __builtin_elementwise_fma(qb[j], s8, -qkh[j]);
+      kc_zero_point<NB == 4>(qkh[j], qkl[j], zv, b1, b16);
+    }
+    bq = quad_sum(fmaf(16.0f, b16, b1)) * kSub;        // in the 2^-24 units of the logits
+  }
+
   float s[8];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
@@ -429,6 +469,21 @@ __device__ __forceinline__ void affine_step(const uint8_t *blk, int w, int g, in
       const uint4 x = *(const uint4 *)row, y = *(const uint4 *)(row + 1024);
       op[0] = unpack_int8(x.x, x.y); op[1] = unpack_int8(x.z, x.w);
       op[2] = unpack_int8(y.x, y.y); op[3] = unpack_int8(y.z, y.w);
+    }
+    if constexpr (kKcK) {
+      float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f}, accl = acc;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc = mfma(op[j], qkh[j], acc);
+        accl = mfma(op[j], qkl[j], accl);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = (acc[i] + accl[i]) - bq;
+        if (TAIL && 16 * tau + 4 * g + i >= nvalid) v = kNegInf;
+        s[4 * tt + i] = v;
+      }
+      continue;
     }
     float4_t acc[NG];
 #pragma unroll
@@ -780,7 +835,7 @@ __device__ __forceinline__ void load_q2(const uint16_t *qrow, bool valid, int g,
     }
   }
 #pragma unroll
-  for (int G = 0; G < 4; ++G) q.qs[G] = G < kHeadDim / GS ? quad_sum(qs[G]) * kSub : 0.0f;
+  for (int G = 0; G < 4; ++G) q.qs[G] = G < kGroups<GS> ? quad_sum(qs[G]) * kSub : 0.0f;
 }
 
 // Running max / probabilities for 4 logits (slots i of the lane's subtile); scaled_mask bit i
@@ -835,8 +890,11 @@ __device__ __forceinline__ half4_t v_operand2<8>(const uint32_t *vw, int k, int 
 template <int NB, int GS, bool TAIL>
 __device__ __forceinline__ void affine_step2(const uint8_t *blk, int w, int g, int c, const QOp2 &q, float sl2,
                                              bool valid_head, int nvalid, State &st) {
-  constexpr int NG = kHeadDim / GS;
-  constexpr int kKm = 2048 * NB, kVc = 2048 * NB + 512 * NG, kVm = 4096 * NB + 512 * NG;
+  constexpr bool kKcK = GS == kKc;
+  constexpr int NG = kGroups<GS>;
+  constexpr int kKm = 2048 * NB;
+  constexpr int kVc = kKcK ? 2048 * NB + 512 : 2048 * NB + 512 * NG;
+  constexpr int kVm = kKcK ? 4096 * NB + 512 : 4096 * NB + 512 * NG;
   const int lane = 16 * g + c;
   const int qq = g & 1, sa = g >> 1;           // A operand: this lane feeds subtile sa, dim half qq
   const int sc = c >> 3;                       // output column subtile
@@ -856,8 +914,28 @@ __device__ __forceinline__ void affine_step2(const uint8_t *blk, int w, int g, i
   uint32_t vsw[2 * NG], vzw[2 * NG], ksw[2 * NG], kzw[2 * NG];
   lds_words<2 * NG>(blk + kVm + (tau_c * 4 + g) * 16 * NG, vsw);            // S of group G, slot 4g + i: half 4G + i
   lds_words<2 * NG>(blk + kVm + (tau_c * 4 + g) * 16 * NG + 8 * NG, vzw);   // the Z likewise
-  lds_words<2 * NG>(blk + kKm + tau_c * 64 * NG + 8 * NG * g, ksw);         // (S, Z) of slots 4g + i: half NG i + G
-  lds_words<2 * NG>(blk + kKm + tau_c * 64 * NG + 32 * NG + 8 * NG * g, kzw);
+  if constexpr (!kKcK) {
+    lds_words<2 * NG>(blk + kKm + tau_c * 64 * NG + 8 * NG * g, ksw);       // (S, Z) of slots 4g + i: half NG i + G
+    lds_words<2 * NG>(blk + kKm + tau_c * 64 * NG + 32 * NG + 8 * NG * g, kzw);
+  }
+  // Per-channel K: the block's per-dim S folded into this lane's Q elements (quarters 2qq + gi)
+  // and the head's sum_d q_d S_d Z_d
+  half8_t qkh[8], qkl[8];
+  float bq = 0.0f;
+  if constexpr (kKcK) {
+    float b1 = 0.0f, b16 = 0.0f;
+#pragma unroll
+    for (int idx = 0; idx < 8; ++idx) {
+      const int j = 2 * (idx >> 2) + (idx & 1), gq = 2 * qq + ((idx >> 1) & 1);
+      const uint8_t *km = blk + kKm + 64 * gq + 16 * j;
+      const uint4 sv = *(const uint4 *)km, zv = *(const uint4 *)(km + 256);
+      const half8_t s8 = __builtin_bit_cast(half8_t, sv);
+      qkh[idx] = q.qb[idx] * s8;
+      qkl[idx] = __builtin_elementwise_fma(q.qb[idx], s8, -qkh[idx]);
+      kc_zero_point<NB == 4>(qkh[idx], qkl[idx], zv, b1, b16);
+    }
+    bq = quad_sum(fmaf(16.0f, b16, b1)) * kSub;
+  }
 
   // QK^T: lane feeds token (subtile sa, row c) from the lane strings of quarters 2qq + gi:
   // op[gi][j] feeds k-step j
@@ -893,12 +971,23 @@ __device__ __forceinline__ void affine_step2(const uint8_t *blk, int w, int g, i
 #pragma unroll
   for (int idx = 0; idx < 8; ++idx) {
     const int j = 2 * (idx >> 2) + (idx & 1), gi = (idx >> 1) & 1;
-    acc[k_group<GS>(j)] = mfma(op[gi][j], q.qb[idx], acc[k_group<GS>(j)]);
+    if constexpr (kKcK) {
+      acc[0] = mfma(op[gi][j], qkh[idx], acc[0]);        // the two terms of q S (acc[1] is free)
+      acc[1] = mfma(op[gi][j], qkl[idx], acc[1]);
+    } else {
+      acc[k_group<GS>(j)] = mfma(op[gi][j], q.qb[idx], acc[k_group<GS>(j)]);
+    }
   }
   float s[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float v = 0.0f;
+    if constexpr (kKcK) {
+      v = (acc[0][i] + acc[1][i]) - bq;
+      if (TAIL && 16 * tau_c + 4 * g + i >= nvalid) v = kNegInf;
+      s[i] = v;
+      continue;
+    }
 #pragma unroll
     for (int G = 0; G < NG; ++G) {
       const int hx = NG * i + G;
@@ -1275,7 +1364,10 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
                                int g, int c, bool valid_head, State &st) {
   const int lane = 16 * g + c;
   const int bb = (int)block_bytes(FMT, GS);
-  const int ndma = bb / 1024;                                 // 1 KB per wave instruction
+  // 1 KB per wave instruction; a block that ends on a partial KB (per-channel K blocks end on
+  // half a KB) gets a last instruction with only the lanes of its remaining bytes active
+  constexpr int kTailLanes = (int)(block_bytes(FMT, GS) % 1024) / 16;
+  const int ndma = (bb + 1023) / 1024;
   // Waves 0..2 load the blocks; wave 3 loads none and hands out the chunks, so that waiting
   // for its cursor atomic never waits for block loads (vmcnt counts both).
   constexpr int kDmaWaves = kWaves - 1;
@@ -1331,7 +1423,13 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
     if (!dispatcher) {
       const uint8_t *src = gbh + (int64_t)blk_idx * bb;
       const uint32_t dst = lds0 + (uint32_t)(slot * bb);
-      for (int jj = w; jj < ndma; jj += kDmaWaves) dma16(src + jj * 1024, __builtin_amdgcn_readfirstlane(dst + jj * 1024));
+      for (int jj = w; jj < ndma; jj += kDmaWaves) {
+        if (kTailLanes != 0 && jj == ndma - 1) {
+          if (lane < kTailLanes) dma16(src + jj * 1024, __builtin_amdgcn_readfirstlane(dst + jj * 1024));
+        } else {
+          dma16(src + jj * 1024, __builtin_amdgcn_readfirstlane(dst + jj * 1024));
+        }
+      }
     }
     const bool part = blk_idx == nblk - 1 && tail_valid < kBlock;
     tailmask = (tailmask & ~(1u << slot)) | ((uint32_t)part << slot);
@@ -1418,7 +1516,7 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
     // paired subtiles the head's total goes to its subtile-0 column only; the two columns are
     // summed later).
     if (st.m != kNegInf) st.m *= kInvSub;
-    constexpr int NG = kHeadDim / GS;
+    constexpr int NG = kGroups<GS>;
     const bool take = NSUB == 2 ? (c >> 3) == 0 : true;
     float zg[NG];
 #pragma unroll
@@ -1498,7 +1596,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
 #define KVQ_SEG(F, GS) stream_segment<F, GS, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st)
 #define KVQ_AFFINE_SEG(F)                  \
   case F:                                  \
-    if (sg.gs == 32) KVQ_SEG(F, 32);       \
+    if (sg.gs == kKc) KVQ_SEG(F, kKc);     \
+    else if (sg.gs == 32) KVQ_SEG(F, 32);  \
     else if (sg.gs == 128) KVQ_SEG(F, 128); \
     else KVQ_SEG(F, 64);                   \
     break;

@@ -19,8 +19,11 @@ constexpr int kFmtFp16 = 0, kFmtInt2 = 2, kFmtInt4 = 4, kFmtInt8 = 8, kFmtNvfp4 
 
 // Bytes of one 128-slot block (K and V parts together); affine blocks hold one (S, Z) pair per
 // group of gs values (32, 64 or 128) of each token.
+// Group-size code 0 (kKc): K per channel over the block's 128 tokens (512 bytes of per-dim S
+// and Z), V per token in groups of 64.
+constexpr int kKc = 0;
 __host__ __device__ constexpr size_t affine_block_bytes(int nbits, int gs = kGroup) {
-  return 4096u * (size_t)nbits + 1024u * (size_t)(kHeadDim / gs);
+  return gs == kKc ? 4096u * (size_t)nbits + 1536u : 4096u * (size_t)nbits + 1024u * (size_t)(kHeadDim / gs);
 }
 constexpr size_t kNvfp4BlockBytes = 18432;
 constexpr size_t kMxfp4BlockBytes = 17408;
@@ -43,6 +46,9 @@ __host__ __device__ constexpr int decode_ring_depth(size_t bb) { return bb <= 18
 constexpr size_t aff_km(int n) { return 2048u * (size_t)n; }
 constexpr size_t aff_vc(int n, int ng) { return 2048u * (size_t)n + 512u * (size_t)ng; }
 constexpr size_t aff_vm(int n, int ng) { return 4096u * (size_t)n + 512u * (size_t)ng; }
+// Per-channel K blocks: [Kc][Km 512: S of the 128 dims in MFMA operand order, then Z][Vc][Vm 1024]
+constexpr size_t kc_vc(int n) { return 2048u * (size_t)n + 512u; }
+constexpr size_t kc_vm(int n) { return 4096u * (size_t)n + 512u; }
 // Offsets inside an NVFP4 block.
 constexpr size_t kNvKs = 8192, kNvVc = 9216, kNvVs = 17408;
 // Offsets inside an MXFP4 block: Kc as NVFP4's, one E8M0 byte per K lane, V bytes pairing
@@ -70,7 +76,7 @@ struct QuantArgs {
   int64_t arena_bh_stride;        // bytes per (b, h)
   int64_t dst_slot0;
   int fmt;
-  int gs;                         // affine group size (32, 64, 128)
+  int gs;                         // affine group size (32, 64, 128; kKc: K per channel)
   int B, H;
 };
 
@@ -98,7 +104,7 @@ struct DecodeSeg {
   int64_t bh_stride;       // bytes per (b, h)
   int64_t ntok;            // valid slots per (b, h)
   int fmt;                 // block format (kFmt*)
-  int gs;                  // affine group size (32, 64, 128; 64 for the other formats)
+  int gs;                  // affine group size (32, 64, 128, kKc; 64 for the other formats)
   int chunk;               // blocks per unit (fixed units and the cursor's big units)
   int items;               // work items per (b, h)
   int fixed;               // units per item assigned up front

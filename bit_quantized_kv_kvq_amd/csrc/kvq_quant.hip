@@ -146,6 +146,15 @@ __device__ __forceinline__ int k_lane_dim32(int fmt, int g, int f) {
   }
   return 32 * j + 8 * g + e;
 }
+// Dim fed by element e of MFMA k-step j in lane quarter g of the groups-of-64 K lanes: the field
+// f that (j, e) reads, through k_lane_dim.
+__device__ __forceinline__ int k_operand_dim(int fmt, int g, int j, int e) {
+  int f;
+  if (fmt == kFmtInt2) f = 16 * (j >> 1) + 4 * (j & 1) + (e >> 1) + 8 * (e & 1);
+  else if (fmt == kFmtInt4) f = 8 * j + (e >> 1) + 4 * (e & 1);
+  else f = 8 * j + 4 * (e >> 2) + ((e >> 1) & 1) + 2 * (e & 1);
+  return k_lane_dim(fmt, g, f);
+}
 
 __device__ __forceinline__ void v_field(int fmt, int phi, int &k, int &e) {
   if (fmt == kFmtInt2) {
@@ -227,7 +236,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
   constexpr int kWordsPerRow = kRowBytes / 4;
   constexpr int kQmax = (1 << kBits) - 1;
   constexpr size_t kBlockBytes = block_bytes(FMT, GS);
-  constexpr int NG = kHeadDim / GS;                      // affine groups per token
+  constexpr bool kKcK = GS == kKc;                       // K per channel (V in groups of 64)
+  constexpr int NG = kKcK ? 2 : kHeadDim / GS;           // affine groups per token (V's, per channel)
+  constexpr int GSV = kKcK ? kGroup : GS;                 // head_dim group width of per-token groups
 
   // 34.8 KB of staged tokens and 1-3 KB of metadata: four workgroups fit in a CU
   constexpr int kMeta = kMx ? 4 : kNv ? 8 : NG;  // affine: S per group; NVFP4: per 16; MXFP4: per 32
@@ -299,6 +310,85 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
 
   // ---- per-group metadata (none for FP8)
   if constexpr (kF8 || kF16) {
+  } else if constexpr (kKcK && !kNv) {
+    // per-channel K (this kernel's K half): each dim's 128 values of the block form one group
+    // (the block is one whole window; the host quantizes only whole windows)
+    if (kv == 0) {
+      if (tid < kHeadDim) {
+        const int d = tid;
+        half2v mn2 = {(_Float16)INFINITY, (_Float16)INFINITY}, mx2 = {-(_Float16)INFINITY, -(_Float16)INFINITY};
+#pragma unroll 8
+        for (int t = 0; t < kBlock; t += 2) {
+          const half2v x2 = {__builtin_bit_cast(_Float16, xs[t * kRowHalves + d]), __builtin_bit_cast(_Float16, xs[(t + 1) * kRowHalves + d])};
+          mn2 = __builtin_elementwise_min(mn2, x2);
+          mx2 = __builtin_elementwise_max(mx2, x2);
+        }
+        const float mn = fminf((float)mn2.x, (float)mn2.y), mx = fmaxf((float)mx2.x, (float)mx2.y);
+        float S = 0.0f;
+        uint32_t Sb = 0;
+        if (mx > mn) {
+          Sb = f64_to_f16_rne(((double)mx - (double)mn) / (double)kQmax);
+          S = h2f((uint16_t)Sb);
+        }
+        if (!(mx > mn) || S == 0.0f) {
+          S = mn != 0.0f ? fabsf(mn) : 1.0f;
+          Sb = __builtin_bit_cast(uint16_t, (_Float16)S);
+        }
+        double z = rint(-(double)mn / (double)S);
+        z = fmin(fmax(z, -65504.0), 65504.0);
+        const uint32_t Zb = f64_to_f16_rne(z);
+        mS[d][0] = S;
+        mInv[d][0] = 1.0f / S;
+        mZ[d][0] = h2f((uint16_t)Zb);
+      }
+      __syncthreads();
+      // (S, Z) in MFMA operand order: position 32g + 8j + e holds the dim that element feeds
+      if (tid < kHeadDim) {
+        const int pos = tid, d = k_operand_dim(FMT, pos >> 5, (pos >> 3) & 3, pos & 7);
+        uint8_t *m = blkp + aff_km(kBits);
+        *(uint16_t *)(m + 2 * pos) = __builtin_bit_cast(uint16_t, (_Float16)mS[d][0]);
+        *(uint16_t *)(m + 256 + 2 * pos) = __builtin_bit_cast(uint16_t, (_Float16)mZ[d][0]);
+      }
+    } else {
+      for (int idx = tid; idx < kBlock * 2; idx += kThreads) {
+        const int slot = idx >> 1, g = idx & 1;
+        if (slot < lo || slot >= hi) continue;
+        const uint4 *row = (const uint4 *)&xs[slot * kRowHalves + g * kGroup];
+        half2v mn2 = {(_Float16)INFINITY, (_Float16)INFINITY}, mx2 = {-(_Float16)INFINITY, -(_Float16)INFINITY};
+#pragma unroll
+        for (int i = 0; i < kGroup / 8; ++i) {
+          const uint4 v = row[i];
+          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const half2v x2 = __builtin_bit_cast(half2v, w4[k]);
+            mn2 = __builtin_elementwise_min(mn2, x2);
+            mx2 = __builtin_elementwise_max(mx2, x2);
+          }
+        }
+        const float mn = fminf((float)mn2.x, (float)mn2.y), mx = fmaxf((float)mx2.x, (float)mx2.y);
+        float S = 0.0f;
+        uint32_t Sb = 0;
+        if (mx > mn) {
+          Sb = f64_to_f16_rne(((double)mx - (double)mn) / (double)kQmax);
+          S = h2f((uint16_t)Sb);
+        }
+        if (!(mx > mn) || S == 0.0f) {
+          S = mn != 0.0f ? fabsf(mn) : 1.0f;
+          Sb = __builtin_bit_cast(uint16_t, (_Float16)S);
+        }
+        double z = rint(-(double)mn / (double)S);
+        z = fmin(fmax(z, -65504.0), 65504.0);
+        const uint32_t Zb = f64_to_f16_rne(z);
+        mS[slot][g] = S;
+        mInv[slot][g] = 1.0f / S;
+        mZ[slot][g] = h2f((uint16_t)Zb);
+        const int tau = slot >> 4, r = slot & 15, q = r >> 2, i = r & 3;
+        uint8_t *m = blkp + kc_vm(kBits) + (tau * 4 + q) * 32;
+        *(uint16_t *)(m + 8 * g + 2 * i) = (uint16_t)Sb;
+        *(uint16_t *)(m + 16 + 8 * g + 2 * i) = (uint16_t)Zb;
+      }
+    }
   } else if constexpr (!kNv) {
    for (int idx = tid; idx < kBlock * NG; idx += kThreads) {
     const int slot = idx / NG, g = idx % NG;
@@ -437,6 +527,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
     else if constexpr (kNv) return e2m1_code(x, mS[slot][grp]);
     else return affine_code(x, mS[slot][grp], mInv[slot][grp], mZ[slot][grp], kQmax);
   };
+  // K code of dim d of a slot (per-channel K: the dim's group; else the slot's group of d)
+  auto kcode_of = [&](float x, int slot, int d) -> uint32_t {
+    if constexpr (kKcK && !kNv && !kF8) return affine_code(x, mS[d][0], mInv[d][0], mZ[d][0], kQmax);
+    else return code_of(x, slot, d / (kMx ? kMxBlock : kNv ? kNvBlock : GSV));
+  };
   if (kv == 0) {
     // K: [part w][tile u][chunk r][lane][cb bytes]; a word holds F fields of one slot at F
     // consecutive dims, read from LDS 8 values at a time
@@ -462,7 +557,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
         }
       } else if (slot < hi) {
         const int d0 = k_lane_dim(FMT, g, omega * F);   // first of F consecutive dims
-        const int grp = d0 / (kMx ? kMxBlock : kNv ? kNvBlock : GS);
+        const int grp = d0 / (kMx ? kMxBlock : kNv ? kNvBlock : GSV);
         const uint16_t *xr = &xs[slot * kRowHalves + d0];
         if constexpr (F >= 8) {
 #pragma unroll
@@ -470,14 +565,14 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
             float x[8];
             unpack8(*(const uint4 *)(xr + 8 * h8), x);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) word |= code_of(x[k], slot, grp) << ((8 * h8 + k) * kBits);
+            for (int k = 0; k < 8; ++k) word |= kcode_of(x[k], slot, d0 + 8 * h8 + k) << ((8 * h8 + k) * kBits);
           }
         } else {
           const uint2 v = *(const uint2 *)xr;
           const float x[4] = {h2f((uint16_t)(v.x & 0xFFFFu)), h2f((uint16_t)(v.x >> 16)), h2f((uint16_t)(v.y & 0xFFFFu)),
                               h2f((uint16_t)(v.y >> 16))};
 #pragma unroll
-          for (int k = 0; k < 4; ++k) word |= code_of(x[k], slot, grp) << (k * kBits);
+          for (int k = 0; k < 4; ++k) word |= kcode_of(x[k], slot, d0 + k) << (k * kBits);
         }
       }
       *(uint32_t *)(blkp + (size_t)w * 4) = word;
@@ -487,7 +582,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
     // of dim 16 k + c and slot 32 w + 16 (e >> 2) + 4 g + (e & 3).  A task is (part, g, omega,
     // c0 in {0, 8}): the words of lanes 16 g + c0 .. +7, whose field j reads the same slot at
     // the 8 consecutive dims 16 k + c0 .. +7 (one 16-byte LDS read and one metadata lookup).
-    const size_t vc = kMx ? kMxVc : kNv ? kNvVc : kF8 ? kF8Vc : aff_vc(kBits, NG);
+    const size_t vc = kMx ? kMxVc : kNv ? kNvVc : kF8 ? kF8Vc : kKcK ? kc_vc(kBits) : aff_vc(kBits, NG);
     constexpr int kChunks = kBits / 2;              // 16-byte chunks per lane
     constexpr int kLaneWords = 4 * kChunks;
     constexpr int kTasks = 4 * 4 * kLaneWords * 2;
@@ -510,7 +605,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
         any = true;
         if (slot >= hi) continue;                    // cleared: code 0
         const int d0 = 16 * k + c0;
-        const int grp = d0 / (kMx ? kMxBlock : kNv ? kNvBlock : GS);
+        const int grp = d0 / (kMx ? kMxBlock : kNv ? kNvBlock : GSV);
         float x[8];
         unpack8(*(const uint4 *)&xs[slot * kRowHalves + d0], x);
 #pragma unroll
@@ -548,7 +643,8 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t s) {
   dim3 grid((unsigned)nblk, (unsigned)a.H, (unsigned)(a.B * 2));
 #define KVQ_AFFINE_CASE(F)                                                                             \
   case F:                                                                                              \
-    if (a.gs == 32) quantize_kernel<F, 32><<<grid, kThreads, 0, s>>>(a, blk0, nblk);                   \
+    if (a.gs == kKc) quantize_kernel<F, kKc><<<grid, kThreads, 0, s>>>(a, blk0, nblk);                 \
+    else if (a.gs == 32) quantize_kernel<F, 32><<<grid, kThreads, 0, s>>>(a, blk0, nblk);              \
     else if (a.gs == 128) quantize_kernel<F, 128><<<grid, kThreads, 0, s>>>(a, blk0, nblk);            \
     else if (a.gs == 64) quantize_kernel<F, 64><<<grid, kThreads, 0, s>>>(a, blk0, nblk);              \
     else return hipErrorInvalidValue;                                                                  \

@@ -81,6 +81,13 @@ typedef struct {
   int64_t old_after;    /* a chunk of tokens quantized together goes to the old tier when
                            all of them are at least old_after positions behind the length
                            at the end of the append call; 0 disables the old tier */
+  int32_t k_per_channel; /* 1: K is quantized per channel, each dim's values over a window of
+                           128 consecutive tokens forming one affine group (page
+                           "KV缓存量化技术：提升大模型长文本生成效率" §2.1, per-channel grouping);
+                           V stays per token in groups of 64.  Needs an affine format with
+                           group_size 64 (and an affine old format), residual_len a positive
+                           multiple of 128; kvq_flush_residual then flushes only whole windows.
+                           0: per-token groups for K and V. */
 } kvq_config;
 
 /* Bytes of device memory a cache with this configuration needs (0 if cfg is invalid).

@@ -15,7 +15,7 @@ import kvq_synth as syn
 from oracle.cache import LayerCache
 from oracle.attention import decode_layer
 from oracle import layout as olayout
-from oracle.quant import quantize_tokens, affine_params
+from oracle.quant import quantize_tokens, affine_params, k_per_channel
 
 pytestmark = pytest.mark.gpu
 
@@ -40,8 +40,11 @@ def _check_blocks(cache, ora: LayerCache, b, h, tier, region):
     nblk = -(-ntok // 128)
     for blk in sorted({0, nblk // 2, nblk - 1}):
         sl = pos[128 * blk:128 * (blk + 1)]
-        kq, vq = quantize_tokens(K[sl], fmt), quantize_tokens(V[sl], fmt)
-        if fmt == "nvfp4":
+        kq, vq = quantize_tokens(K[sl], fmt, "k"), quantize_tokens(V[sl], fmt, "v")
+        if k_per_channel(fmt):               # one whole 128-token window per block
+            want = olayout.pack_affine_kc_block(affine_params(fmt)[0], {"codes": kq["codes"], "S": kq["S"][0],
+                                                                       "Z": kq["Z"][0]}, vq)
+        elif fmt == "nvfp4":
             want = olayout.pack_nvfp4_block(kq, vq, sl.size)
         elif fmt == "mxfp4":
             want = olayout.pack_mxfp4_block(kq, vq, sl.size)
@@ -131,6 +134,10 @@ def test_fullsize_llama3_70b_gqa8_32k_fp8():
 
 def test_fullsize_long_context_128k_int4_groups_of_32():
     _run(4, "int4g32", steps=1, n_pairs=2)
+
+
+def test_fullsize_long_context_128k_int4_per_channel_k():
+    _run(4, "int4kc", steps=2, n_pairs=2, check_steps=(1, 2))
 
 
 def test_fullsize_long_context_128k_int4_groups_of_128():

@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 import torch
 
+import bit_quantized_kv_kvq_amd as kvq
 from gpu_helpers import Pair, adversarial_tokens, assert_attention_close
 
 pytestmark = pytest.mark.gpu
@@ -177,6 +178,46 @@ def test_debugging_configuration_group32_residual256():
         p.check_bytes(0)
         got, want = p.decode(0, q, 1 / np.sqrt(128))
         assert_attention_close(got, want)
+
+
+KC_FORMATS = ["int2kc", "int4kc", "int8kc"]
+
+
+@pytest.mark.parametrize("R", [128, 256])
+@pytest.mark.parametrize("fmt", KC_FORMATS)
+def test_per_channel_k_bytes_and_decode(fmt, R):
+    """Per-channel K: windows of 128 tokens flushed from a full residual or quantized in bulk;
+    stored bytes and decode (G 1, 4, 8) against the oracle after each append."""
+    rng = np.random.default_rng(R + sum(map(ord, fmt)))
+    B, H = 2, 2
+    p = Pair(1, B, H, 3000, fmt, R)
+    for n in [300, 1, 127, 129, 700, 1]:
+        k = adversarial_tokens(rng, B, H, n)
+        k[..., 7] = np.clip(k[..., 7].astype(np.float32) * 12, -65504, 65504)   # an outlier channel
+        p.append(0, k, adversarial_tokens(rng, B, H, n))
+        p.check_bytes(0)
+        for G in (1, 4, 8):
+            q = (rng.standard_normal((B, H * G, 128)) / np.sqrt(128)).astype(np.float16)
+            got, want = p.decode(0, q, 1 / np.sqrt(128))
+            assert_attention_close(got, want)
+
+
+def test_per_channel_k_tiers_and_partial_flush():
+    """Young INT4 and old INT2 tiers both with per-channel K; an explicit flush of a partial
+    window is refused and changes nothing."""
+    rng = np.random.default_rng(41)
+    B, H, G = 1, 2, 4
+    p = Pair(1, B, H, 4000, "int4kc", 128, "int2kc", 1000)
+    p.append(0, rng.standard_normal((B, H, 2900, 128)).astype(np.float16),
+             rng.standard_normal((B, H, 2900, 128)).astype(np.float16))
+    p.check_bytes(0)
+    assert p.gpu.layout(0, 2)[2] > 0 and p.gpu.seq_len(0)[1] % 128 != 0
+    with pytest.raises(kvq.KvqError):
+        p.gpu.flush(0)
+    p.check_bytes(0)
+    q = (rng.standard_normal((B, H * G, 128)) / np.sqrt(128)).astype(np.float16)
+    got, want = p.decode(0, q, 1.0)
+    assert_attention_close(got, want)
 
 
 def test_group_size_tiers():

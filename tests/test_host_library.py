@@ -29,7 +29,8 @@ def test_library_exports_every_declared_symbol():
 @pytest.mark.parametrize("bad", [
     dict(head_dim=64), dict(fmt="int4", residual_len=100), dict(fmt="nvfp4", group=64),
     dict(fmt="fp8", group=64), dict(fmt="int8", group=0), dict(fmt="fp16", group=16), dict(fmt="mxfp4", group=16),
-    dict(fmt="int4", group=16), dict(fmt="int4", group=256),
+    dict(fmt="int4", group=16), dict(fmt="int4", group=256), dict(fmt="int4kc", residual_len=0),
+    dict(fmt="int4kc", residual_len=64),
     dict(max_tokens=0), dict(residual_len=2048), dict(old_after=-1)])
 def test_config_rejected(bad):
     cfg = kvq.make_config(1, 1, 1, 100, bad.get("fmt", "int4"), bad.get("residual_len", 128),
@@ -45,7 +46,8 @@ def test_config_rejected(bad):
 @pytest.mark.parametrize("fmt,R,old", [("int4", 128, None), ("int2", 32, None), ("nvfp4", 0, None),
                                        ("int4", 128, "int2"), ("int8", 16, None), ("fp8", 128, None),
                                        ("int4", 128, "fp8"), ("fp16", 0, None), ("int4", 128, "fp16"), ("mxfp4", 0, None),
-                                       ("int4g32", 128, None), ("int2g128", 16, None), ("int4g32", 128, "int2g32")])
+                                       ("int4g32", 128, None), ("int2g128", 16, None), ("int4g32", 128, "int2g32"),
+                                       ("int4kc", 128, None), ("int2kc", 256, "int2kc")])
 def test_layout_regions(fmt, R, old):
     cfg = kvq.make_config(3, 2, 4, 5000, fmt, R, old, 1000 if old else 0)
     c = kvq.Cache(cfg, plan_only=True)
