@@ -20,7 +20,8 @@ REGION_RESIDUAL, REGION_YOUNG, REGION_OLD = 0, 1, 2
 
 # every symbol include/kvq.h declares
 EXPORTS = ("kvq_cache_bytes", "kvq_cache_create", "kvq_cache_destroy", "kvq_cache_reset", "kvq_append",
-           "kvq_flush_residual", "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_seq_len", "kvq_layout",
+           "kvq_flush_residual", "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_append_decode_attn",
+           "kvq_seq_len", "kvq_layout",
            "kvq_set_plan_only", "kvq_set_deterministic", "kvq_last_error")
 
 
@@ -63,6 +64,8 @@ def lib() -> ctypes.CDLL:
     L.kvq_decode_workspace_bytes.argtypes = [vp, i32]; L.kvq_decode_workspace_bytes.restype = sz
     L.kvq_decode_attn.argtypes = [vp, i32, vp, i32, ctypes.c_float, vp, i32, vp, sz, vp]
     L.kvq_decode_attn.restype = ctypes.c_int
+    L.kvq_append_decode_attn.argtypes = [vp, i32, vp, vp, i64, vp, i32, ctypes.c_float, vp, i32, vp, sz, vp]
+    L.kvq_append_decode_attn.restype = ctypes.c_int
     L.kvq_seq_len.argtypes = [vp, i32, P(i64), P(i64)]; L.kvq_seq_len.restype = ctypes.c_int
     L.kvq_layout.argtypes = [vp, i32, i32, P(sz), P(sz), P(i64)]; L.kvq_layout.restype = ctypes.c_int
     L.kvq_set_plan_only.argtypes = [vp, i32]; L.kvq_set_plan_only.restype = ctypes.c_int
@@ -183,6 +186,17 @@ class Cache:
         _check(lib().kvq_decode_attn(self.h, layer, q.data_ptr(), q.shape[1], float(softmax_scale), out.data_ptr(),
                                      out_fp32, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                      _stream_ptr(stream)))
+
+    def append_decode(self, layer: int, k, v, q, softmax_scale: float, out, workspace, stream=None):
+        """kvq_append_decode_attn: append k, v (fp16 [B, H, n, 128]) then attend with q."""
+        import torch
+        out_fp32 = 1 if out.dtype == torch.float32 else 0
+        for t in (k, v, q):
+            assert t.is_contiguous() and t.dtype == torch.float16
+        _check(lib().kvq_append_decode_attn(self.h, layer, k.data_ptr(), v.data_ptr(), k.shape[2], q.data_ptr(),
+                                            q.shape[1], float(softmax_scale), out.data_ptr(), out_fp32,
+                                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                            _stream_ptr(stream)))
 
     def seq_len(self, layer: int) -> tuple[int, int]:
         t, r = ctypes.c_int64(), ctypes.c_int64()

@@ -317,6 +317,69 @@ int plan_decode(const kvq_cache *c, int layer, DecodeArgs &a, uint64_t *cursors)
   return (int)(nbh * a.items_total);
 }
 
+int check_decode(const kvq_cache *c, const void *q, int32_t num_q_heads, float softmax_scale, const void *out,
+                 const void *workspace, size_t ws_bytes) {
+  const auto &cfg = c->cfg;
+  if (num_q_heads < 1 || num_q_heads % cfg.num_kv_heads != 0)
+    return fail(KVQ_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads, cfg.num_kv_heads);
+  const int G = num_q_heads / cfg.num_kv_heads;
+  if (G > 16) return fail(KVQ_EINVAL, "query heads per kv head (%d) must be <= 16", G);
+  if (!q || !out || !workspace) return fail(KVQ_EINVAL, "q, out and workspace must be non-NULL");
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return fail(KVQ_EINVAL, "q, out and workspace must be 16-byte aligned");
+  if (!(softmax_scale > 0.0f) || softmax_scale > 3.0e38f) return fail(KVQ_EINVAL, "softmax_scale must be positive and finite");
+  if (ws_bytes < workspace_bound(c, num_q_heads))
+    return fail(KVQ_ENOSPACE, "workspace %zu < required %zu", ws_bytes, workspace_bound(c, num_q_heads));
+  return KVQ_OK;
+}
+
+int check_append(const kvq_cache *c, int32_t layer, const void *k, const void *v, int64_t n_tokens) {
+  if (n_tokens < 0) return fail(KVQ_EINVAL, "n_tokens < 0");
+  if (n_tokens == 0) return KVQ_OK;
+  if (!k || !v) return fail(KVQ_EINVAL, "k or v is NULL");
+  if (!aligned16(k) || !aligned16(v)) return fail(KVQ_EINVAL, "k and v must be 16-byte aligned");
+  const LayerState &st = c->layers[layer];
+  if (st.length + n_tokens > c->cfg.max_tokens)
+    return fail(KVQ_ECAPACITY, "layer %d: %lld + %lld tokens exceeds max_tokens %lld", layer, (long long)st.length,
+                (long long)n_tokens, (long long)c->cfg.max_tokens);
+  return KVQ_OK;
+}
+
+// The decode launch of a checked call.  `pending` (may be null): the residual copy of the same
+// call's append (tokens [src_tok0, +count) of k / v, n_src tokens each), done by the launch itself.
+int run_decode(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_heads, float softmax_scale, void *out,
+               int32_t out_fp32, void *workspace, const Op *pending, const void *k, const void *v, int64_t n_src,
+               void *stream) {
+  const auto &cfg = c->cfg;
+  const int G = num_q_heads / cfg.num_kv_heads;
+  if (c->plan_only) return KVQ_OK;
+  if (c->num_cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      c->num_cus = n;
+    else
+      c->num_cus = 256;
+  }
+  DecodeArgs a{};
+  const int num_wg = plan_decode(c, layer, a, (uint64_t *)workspace + (size_t)cfg.batch * cfg.num_kv_heads);
+  a.q = (const uint16_t *)q;
+  a.out = out;
+  a.out_fp32 = out_fp32 ? 1 : 0;
+  a.counters = (uint64_t *)workspace;
+  a.partials = (float *)((uint8_t *)workspace + counters_bytes(c));
+  a.B = cfg.batch; a.H = cfg.num_kv_heads; a.G = G;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  uint32_t ep = ++g_epoch;
+  if (ep == 0) ep = ++g_epoch;
+  a.epoch = ep;
+  if (pending) {
+    a.pend_k = (const uint16_t *)k; a.pend_v = (const uint16_t *)v;
+    a.pend_src_ntok = n_src; a.pend_src_tok0 = pending->src_tok0;
+    a.pend_count = (int)pending->count; a.pend_slot0 = (int)pending->dst_slot0;
+  }
+  return hip_check(launch_decode(a, num_wg, (hipStream_t)stream), "decode");
+}
+
+
 }  // namespace
 
 // ============================================================================== C ABI
@@ -377,14 +440,9 @@ int kvq_set_deterministic(kvq_cache *c, int32_t on) {
 
 int kvq_append(kvq_cache *c, int32_t layer, const void *k, const void *v, int64_t n_tokens, void *stream) {
   if (int e = check_cache(c, layer)) return e;
-  if (n_tokens < 0) return fail(KVQ_EINVAL, "n_tokens < 0");
+  if (int e = check_append(c, layer, k, v, n_tokens)) return e;
   if (n_tokens == 0) return KVQ_OK;
-  if (!k || !v) return fail(KVQ_EINVAL, "k or v is NULL");
-  if (!aligned16(k) || !aligned16(v)) return fail(KVQ_EINVAL, "k and v must be 16-byte aligned");
   LayerState &st = c->layers[layer];
-  if (st.length + n_tokens > c->cfg.max_tokens)
-    return fail(KVQ_ECAPACITY, "layer %d: %lld + %lld tokens exceeds max_tokens %lld", layer, (long long)st.length,
-                (long long)n_tokens, (long long)c->cfg.max_tokens);
   Plan p = plan_append(c->cfg, st, n_tokens);
   int e = run_plan(c, layer, p, k, v, n_tokens, (hipStream_t)stream);
   if (e == KVQ_OK || e == KVQ_EHIP) st = p.after;
@@ -415,38 +473,36 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t num_q_heads) {
 int kvq_decode_attn(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_heads, float softmax_scale, void *out,
                     int32_t out_fp32, void *workspace, size_t ws_bytes, void *stream) {
   if (int e = check_cache(c, layer)) return e;
-  const auto &cfg = c->cfg;
-  if (num_q_heads < 1 || num_q_heads % cfg.num_kv_heads != 0)
-    return fail(KVQ_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads, cfg.num_kv_heads);
-  const int G = num_q_heads / cfg.num_kv_heads;
-  if (G > 16) return fail(KVQ_EINVAL, "query heads per kv head (%d) must be <= 16", G);
-  if (!q || !out || !workspace) return fail(KVQ_EINVAL, "q, out and workspace must be non-NULL");
-  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return fail(KVQ_EINVAL, "q, out and workspace must be 16-byte aligned");
-  if (!(softmax_scale > 0.0f) || softmax_scale > 3.0e38f) return fail(KVQ_EINVAL, "softmax_scale must be positive and finite");
-  if (ws_bytes < workspace_bound(c, num_q_heads))
-    return fail(KVQ_ENOSPACE, "workspace %zu < required %zu", ws_bytes, workspace_bound(c, num_q_heads));
+  if (int e = check_decode(c, q, num_q_heads, softmax_scale, out, workspace, ws_bytes)) return e;
   if (c->layers[layer].length == 0) return fail(KVQ_ESTATE, "layer %d is empty", layer);
-  if (c->plan_only) return KVQ_OK;
-  if (c->num_cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      c->num_cus = n;
-    else
-      c->num_cus = 256;
+  return run_decode(c, layer, q, num_q_heads, softmax_scale, out, out_fp32, workspace, nullptr, nullptr, nullptr, 0,
+                    stream);
+}
+
+int kvq_append_decode_attn(kvq_cache *c, int32_t layer, const void *k, const void *v, int64_t n_tokens, const void *q,
+                           int32_t num_q_heads, float softmax_scale, void *out, int32_t out_fp32, void *workspace,
+                           size_t ws_bytes, void *stream) {
+  if (int e = check_cache(c, layer)) return e;
+  if (int e = check_append(c, layer, k, v, n_tokens)) return e;
+  if (int e = check_decode(c, q, num_q_heads, softmax_scale, out, workspace, ws_bytes)) return e;
+  LayerState &st = c->layers[layer];
+  if (st.length + n_tokens == 0) return fail(KVQ_ESTATE, "layer %d is empty", layer);
+  Op pending{};
+  bool has_pending = false;
+  if (n_tokens > 0) {
+    Plan p = plan_append(c->cfg, st, n_tokens);
+    // a last copy into the residual moves into the decode launch (nothing else reads the residual)
+    if (!p.ops.empty() && p.ops.back().kind == Op::kResCopy) {
+      pending = p.ops.back();
+      p.ops.pop_back();
+      has_pending = true;
+    }
+    const int e = run_plan(c, layer, p, k, v, n_tokens, (hipStream_t)stream);
+    if (e == KVQ_OK || e == KVQ_EHIP) st = p.after;
+    if (e != KVQ_OK) return e;
   }
-  DecodeArgs a{};
-  const int num_wg = plan_decode(c, layer, a, (uint64_t *)workspace + (size_t)cfg.batch * cfg.num_kv_heads);
-  a.q = (const uint16_t *)q;
-  a.out = out;
-  a.out_fp32 = out_fp32 ? 1 : 0;
-  a.counters = (uint64_t *)workspace;
-  a.partials = (float *)((uint8_t *)workspace + counters_bytes(c));
-  a.B = cfg.batch; a.H = cfg.num_kv_heads; a.G = G;
-  a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  uint32_t ep = ++g_epoch;
-  if (ep == 0) ep = ++g_epoch;
-  a.epoch = ep;
-  return hip_check(launch_decode(a, num_wg, (hipStream_t)stream), "decode");
+  return run_decode(c, layer, q, num_q_heads, softmax_scale, out, out_fp32, workspace, has_pending ? &pending : nullptr,
+                    k, v, n_tokens, stream);
 }
 
 int kvq_seq_len(const kvq_cache *c, int32_t layer, int64_t *total, int64_t *in_residual) {

@@ -1571,6 +1571,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   const bool valid_head = (NSUB == 2 ? (c & 7) : c) < a.G;
   const Item it = decode_item(a, blockIdx.x);
   __shared__ int s_chunk;
+  if (a.pend_count > 0 && it.has_res) {
+    // this call's new tokens go to the residual: copied here, before this workgroup (the only
+    // reader of the residual in the launch) reads it
+    const int b = it.bh / a.H, h = it.bh % a.H;
+    uint16_t *rk = (uint16_t *)(a.res_base + (int64_t)it.bh * a.res_bh_stride);   // K [R][128]
+    uint16_t *rv = rk + (int64_t)a.res_len * kHeadDim;                               // V [R/16][128][16]
+    const int64_t src0 = ((int64_t)(b * a.H + h) * a.pend_src_ntok + a.pend_src_tok0) * kHeadDim;
+    for (int e = threadIdx.x; e < a.pend_count * kHeadDim; e += kThreads) {
+      const int slot = a.pend_slot0 + e / kHeadDim, d = e % kHeadDim;
+      rk[slot * kHeadDim + d] = a.pend_k[src0 + e];
+      rv[((slot / 16) * kHeadDim + d) * 16 + slot % 16] = a.pend_v[src0 + e];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  }
   State st;
 #pragma unroll
   for (int k = 0; k < 8; ++k) st.o[k] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};

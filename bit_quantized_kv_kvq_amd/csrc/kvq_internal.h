@@ -135,6 +135,11 @@ struct DecodeArgs {
   float scale_log2;        // softmax_scale * log2(e)
   uint32_t epoch;          // distinct per call, tags the arrival counters
   int q_lds_off;           // LDS byte offset of the query rows (past the largest block ring)
+  // Tokens of the same call's append that go to the residual (pend_count 0: none): the work
+  // item holding the residual of a (b, h) copies them there before it reads the residual.
+  const uint16_t *pend_k, *pend_v;   // caller input [B][H][pend_src_ntok][128]
+  int64_t pend_src_ntok, pend_src_tok0;
+  int pend_count, pend_slot0;
 };
 
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t s);

@@ -135,6 +135,19 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t num_q_heads);
 int kvq_decode_attn(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_heads, float softmax_scale,
                     void *out, int32_t out_fp32, void *workspace, size_t ws_bytes, void *stream);
 
+/* One decode step of `layer` in one call: exactly kvq_append(c, layer, k, v, n_tokens, stream)
+   followed by kvq_decode_attn(c, layer, q, ...), the step that every generated token makes (it
+   appends its K/V and attends over the whole history: page "NVFP4 KV缓存技术详解" §2.1, the
+   decoding and cache-update phases).  When the new tokens go to the fp16 residual (no flush,
+   or after the flush that a full residual takes first), the decode launch itself writes them
+   there before it reads the residual, so the step costs one launch instead of two.  All
+   arguments of both calls are checked before anything is enqueued; errors as for the two
+   calls (on KVQ_EHIP during the append part, the append state has advanced as kvq_append's
+   would).  n_tokens = 0 is a plain kvq_decode_attn. */
+int kvq_append_decode_attn(kvq_cache *c, int32_t layer, const void *k, const void *v, int64_t n_tokens,
+                           const void *q, int32_t num_q_heads, float softmax_scale, void *out, int32_t out_fp32,
+                           void *workspace, size_t ws_bytes, void *stream);
+
 /* Host counters of a layer: total cached tokens and tokens currently in the residual. */
 int kvq_seq_len(const kvq_cache *c, int32_t layer, int64_t *total, int64_t *in_residual);
 
