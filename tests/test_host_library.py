@@ -132,6 +132,31 @@ def test_errors_leave_state_unchanged():
     assert c.seq_len(0) == (0, 0) and c.layout(0, 1)[2] == 0
 
 
+def test_append_decode_checks_everything_before_enqueue():
+    """kvq_append_decode_attn: any bad argument of either part is refused with the state
+    unchanged; a good call advances the counters as kvq_append would; n = 0 is a decode."""
+    cfg = kvq.make_config(2, 1, 2, 300, "int4", 128)
+    c = kvq.Cache(cfg, plan_only=True)
+    L, P = kvq.lib(), 1 << 40
+    ws = c.workspace_bytes(8)
+    f = L.kvq_append_decode_attn
+    assert f(c.h, 0, P, P, 0, P, 8, 1.0, P, 1, P, ws, None) == kvq.KVQ_ESTATE     # empty, nothing appended
+    assert f(c.h, 0, P, P, 5, 0, 8, 1.0, P, 1, P, ws, None) == kvq.KVQ_EINVAL     # q NULL
+    assert f(c.h, 0, P, P, 5, P, 3, 1.0, P, 1, P, ws, None) == kvq.KVQ_EINVAL     # heads not a multiple
+    assert f(c.h, 0, P, P, 5, P, 8, -1.0, P, 1, P, ws, None) == kvq.KVQ_EINVAL    # scale
+    assert f(c.h, 0, P, P, 5, P, 8, 1.0, P, 1, P, ws - 1, None) == kvq.KVQ_ENOSPACE
+    assert f(c.h, 0, P + 2, P, 5, P, 8, 1.0, P, 1, P, ws, None) == kvq.KVQ_EINVAL  # misaligned k
+    assert f(c.h, 0, P, P, 301, P, 8, 1.0, P, 1, P, ws, None) == kvq.KVQ_ECAPACITY
+    assert f(c.h, 2, P, P, 5, P, 8, 1.0, P, 1, P, ws, None) == kvq.KVQ_EINVAL     # layer
+    assert c.seq_len(0) == (0, 0)
+    assert f(c.h, 0, P, P, 5, P, 8, 1.0, P, 1, P, ws, None) == kvq.KVQ_OK
+    assert c.seq_len(0) == (5, 5)
+    assert f(c.h, 0, P, P, 130, P, 8, 1.0, P, 1, P, ws, None) == kvq.KVQ_OK      # flush + residual
+    assert c.seq_len(0) == (135, 7) and c.layout(0, 1)[2] == 128
+    assert f(c.h, 0, P, P, 0, P, 8, 1.0, P, 1, P, ws, None) == kvq.KVQ_OK
+    assert c.seq_len(0) == (135, 7)
+
+
 def test_create_checks_buffer():
     cfg = kvq.make_config(1, 1, 1, 128, "int4", 128)
     need = kvq.kvq_cache_bytes(cfg)
