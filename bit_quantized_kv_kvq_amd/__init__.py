@@ -21,7 +21,7 @@ REGION_RESIDUAL, REGION_YOUNG, REGION_OLD = 0, 1, 2
 # every symbol include/kvq.h declares
 EXPORTS = ("kvq_cache_bytes", "kvq_cache_create", "kvq_cache_destroy", "kvq_cache_reset", "kvq_append",
            "kvq_flush_residual", "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_append_decode_attn",
-           "kvq_seq_len", "kvq_layout",
+           "kvq_seq_len", "kvq_layout", "kvq_tier_first_block",
            "kvq_set_plan_only", "kvq_set_deterministic", "kvq_last_error")
 
 
@@ -35,7 +35,7 @@ class kvq_config(ctypes.Structure):
     _fields_ = [("num_layers", ctypes.c_int32), ("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("max_tokens", ctypes.c_int64), ("format", ctypes.c_int32),
                 ("group_size", ctypes.c_int32), ("residual_len", ctypes.c_int32), ("old_format", ctypes.c_int32),
-                ("old_after", ctypes.c_int64), ("k_per_channel", ctypes.c_int32)]
+                ("old_after", ctypes.c_int64), ("k_per_channel", ctypes.c_int32), ("demote_young", ctypes.c_int32)]
 
 
 _lib = None
@@ -68,6 +68,7 @@ def lib() -> ctypes.CDLL:
     L.kvq_append_decode_attn.restype = ctypes.c_int
     L.kvq_seq_len.argtypes = [vp, i32, P(i64), P(i64)]; L.kvq_seq_len.restype = ctypes.c_int
     L.kvq_layout.argtypes = [vp, i32, i32, P(sz), P(sz), P(i64)]; L.kvq_layout.restype = ctypes.c_int
+    L.kvq_tier_first_block.argtypes = [vp, i32, i32, P(i64)]; L.kvq_tier_first_block.restype = ctypes.c_int
     L.kvq_set_plan_only.argtypes = [vp, i32]; L.kvq_set_plan_only.restype = ctypes.c_int
     L.kvq_set_deterministic.argtypes = [vp, i32]; L.kvq_set_deterministic.restype = ctypes.c_int
     L.kvq_last_error.argtypes = []; L.kvq_last_error.restype = ctypes.c_char_p
@@ -95,9 +96,10 @@ def parse_format(name: str):
 
 
 def make_config(num_layers, batch, num_kv_heads, max_tokens, fmt="int4", residual_len=128,
-                old_fmt=None, old_after=0, head_dim=128) -> kvq_config:
+                old_fmt=None, old_after=0, head_dim=128, demote=False) -> kvq_config:
     """An affine old tier shares the young tier's group size when the young format is affine
-    (64 otherwise): old_fmt must name that group size."""
+    (64 otherwise): old_fmt must name that group size.  demote: young blocks move to the old
+    tier as they age (demote_young)."""
     code, gs = parse_format(fmt)
     old_code, old_gs = parse_format(old_fmt or fmt)
     if old_fmt and old_code in (2, 4, 8) and old_gs != (gs if code in (2, 4, 8) else 64):
@@ -106,7 +108,7 @@ def make_config(num_layers, batch, num_kv_heads, max_tokens, fmt="int4", residua
     if old_fmt and old_code in (2, 4, 8) and old_fmt.endswith("kc") != kc:
         raise ValueError(f"old tier {old_fmt!r} must quantize K like the young tier ({fmt!r})")
     return kvq_config(num_layers, batch, num_kv_heads, head_dim, max_tokens, code, gs, residual_len,
-                      old_code, old_after, int(kc))
+                      old_code, old_after, int(kc), int(bool(demote)))
 
 
 def kvq_cache_bytes(cfg: kvq_config) -> int:
@@ -208,6 +210,12 @@ class Cache:
         off, nb, tok = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int64()
         _check(lib().kvq_layout(self.h, layer, region, ctypes.byref(off), ctypes.byref(nb), ctypes.byref(tok)))
         return off.value, nb.value, tok.value
+
+    def first_block(self, layer: int, region: int) -> int:
+        """kvq_tier_first_block: the first live block of a region's arena."""
+        b = ctypes.c_int64()
+        _check(lib().kvq_tier_first_block(self.h, layer, region, ctypes.byref(b)))
+        return b.value
 
     def region_tensor(self, layer: int, region: int):
         """uint8 device view [batch, kv_heads, bytes per (b, h)] of a region."""

@@ -55,11 +55,18 @@ int tier_gs(const kvq_config *c, int fmt) {
   return is_affine(c->format) ? c->group_size : kGroup;
 }
 
+// Young slots [slot0, slot0 + count) hold the tokens at stream positions [pos0, pos0 + count).
+struct Run {
+  int64_t slot0, pos0, count;
+};
+
 struct LayerState {
   int64_t length = 0;  // tokens cached
   int64_t res = 0;     // tokens in the residual
   int64_t young = 0;   // slots used in the young arena
   int64_t old = 0;     // slots used in the old arena
+  int64_t young_head = 0;   // young blocks demoted to the old tier (the tier starts after them)
+  std::vector<Run> runs;    // positions of the live young slots (kept only when demoting)
 };
 
 struct Geometry {
@@ -82,6 +89,13 @@ const char *check_config(const kvq_config *c) {
     return "residual_len must be 0 or a multiple of 16 up to 1024";
   if (c->old_after < 0) return "old_after must be >= 0";
   if (c->k_per_channel != 0 && c->k_per_channel != 1) return "k_per_channel must be 0 or 1";
+  if (c->demote_young != 0 && c->demote_young != 1) return "demote_young must be 0 or 1";
+  if (c->demote_young) {
+    if (c->old_after <= 0) return "demote_young needs old_after > 0";
+    if (!is_affine(c->format) || c->group_size != kGroup || c->k_per_channel)
+      return "demote_young needs an affine young format with groups of 64 (per-token K)";
+    if (!is_block_fmt(c->old_format) || c->old_format == kFmtFp16) return "demote_young needs a quantized old_format";
+  }
   if (c->k_per_channel) {
     if (!is_affine(c->format) || c->group_size != kGroup) return "k_per_channel needs an affine format with group_size 64";
     if (c->residual_len == 0 || c->residual_len % kBlock != 0)
@@ -145,8 +159,8 @@ int hip_check(hipError_t e, const char *what) {
 // ---------------------------------------------------------------------------- append plan
 
 struct Op {
-  enum Kind { kResCopy, kQuantInput, kQuantResidual } kind;
-  int64_t src_tok0, count, dst_slot0;
+  enum Kind { kResCopy, kQuantInput, kQuantResidual, kDemote } kind;
+  int64_t src_tok0, count, dst_slot0;   // kDemote: src_tok0 = the young block
   int tier;  // 0 young, 1 old (quantize ops)
 };
 
@@ -160,9 +174,17 @@ int chunk_tier(const kvq_config &cfg, int64_t end, int64_t L1) {
   return (cfg.old_after > 0 && end <= L1 - cfg.old_after) ? 1 : 0;
 }
 
-void add_quant(Plan &p, Op::Kind kind, int64_t src0, int64_t count, int tier) {
+// pos0: stream position of the first token (recorded for young chunks when demoting)
+void add_quant(Plan &p, Op::Kind kind, int64_t src0, int64_t count, int tier, int64_t pos0, bool track) {
   if (count <= 0) return;
   Op op{kind, src0, count, tier ? p.after.old : p.after.young, tier};
+  if (track && tier == 0) {
+    auto &rs = p.after.runs;
+    if (!rs.empty() && rs.back().slot0 + rs.back().count == op.dst_slot0 && rs.back().pos0 + rs.back().count == pos0)
+      rs.back().count += count;
+    else
+      rs.push_back(Run{op.dst_slot0, pos0, count});
+  }
   (tier ? p.after.old : p.after.young) += count;
   // merge with the previous op when it continues the same tier from the same source
   if (!p.ops.empty()) {
@@ -176,22 +198,55 @@ void add_quant(Plan &p, Op::Kind kind, int64_t src0, int64_t count, int tier) {
   p.ops.push_back(op);
 }
 
+// Demotion: after an append or a flush, every full young block whose last token is old_after
+// behind the length moves to the old tier (re-quantized from its decoded values), in order.
+// The ops go before a trailing copy into the residual, which they do not touch.
+void plan_demotions(const kvq_config &cfg, Plan &p) {
+  if (!cfg.demote_young || cfg.old_after <= 0) return;
+  LayerState &a = p.after;
+  std::vector<Op> dem;
+  while ((a.young_head + 1) * kBlock <= a.young) {
+    const int64_t last = (a.young_head + 1) * kBlock - 1;   // young slot of the block's last token
+    int64_t pos = -1;
+    for (const Run &r : a.runs)
+      if (last >= r.slot0 && last < r.slot0 + r.count) pos = r.pos0 + (last - r.slot0);
+    if (pos < 0 || pos + 1 > a.length - cfg.old_after) break;
+    dem.push_back(Op{Op::kDemote, a.young_head, kBlock, a.old, 1});
+    a.old += kBlock;
+    ++a.young_head;
+  }
+  // forget the runs of demoted slots
+  const int64_t live0 = a.young_head * kBlock;
+  std::vector<Run> keep;
+  for (const Run &r : a.runs) {
+    if (r.slot0 + r.count <= live0) continue;
+    const int64_t cut = std::max<int64_t>(0, live0 - r.slot0);
+    keep.push_back(Run{r.slot0 + cut, r.pos0 + cut, r.count - cut});
+  }
+  a.runs.swap(keep);
+  const bool tail_copy = !p.ops.empty() && p.ops.back().kind == Op::kResCopy;
+  p.ops.insert(tail_copy ? p.ops.end() - 1 : p.ops.end(), dem.begin(), dem.end());
+}
+
 Plan plan_append(const kvq_config &cfg, const LayerState &st, int64_t n) {
   Plan p;
   p.after = st;
+  const bool track = cfg.demote_young != 0;
   const int64_t R = cfg.residual_len, L = st.length, L1 = L + n, r = st.res;
   p.after.length = L1;
   if (R == 0) {
     int64_t n_old = 0;
     if (cfg.old_after > 0) n_old = std::min<int64_t>(n, std::max<int64_t>(0, L1 - cfg.old_after - L));
-    add_quant(p, Op::kQuantInput, 0, n_old, 1);
-    add_quant(p, Op::kQuantInput, n_old, n - n_old, 0);
+    add_quant(p, Op::kQuantInput, 0, n_old, 1, L, track);
+    add_quant(p, Op::kQuantInput, n_old, n - n_old, 0, L + n_old, track);
+    plan_demotions(cfg, p);
     return p;
   }
   const int64_t total = r + n;
   if (total <= R) {
     p.ops.push_back(Op{Op::kResCopy, 0, n, r, 0});
     p.after.res = total;
+    plan_demotions(cfg, p);
     return p;
   }
   const int64_t r_final = (total - 1) % R + 1;
@@ -199,13 +254,14 @@ Plan plan_append(const kvq_config &cfg, const LayerState &st, int64_t n) {
   int64_t c0 = 0;
   if (r > 0) {
     p.ops.push_back(Op{Op::kResCopy, 0, R - r, r, 0});            // top the residual up to R
-    add_quant(p, Op::kQuantResidual, 0, R, chunk_tier(cfg, L - r + R, L1));
+    add_quant(p, Op::kQuantResidual, 0, R, chunk_tier(cfg, L - r + R, L1), L - r, track);
     c0 = 1;
   }
   for (int64_t c = c0; c < n_chunks; ++c)                        // chunk c = input [cR - r, cR - r + R)
-    add_quant(p, Op::kQuantInput, c * R - r, R, chunk_tier(cfg, L - r + (c + 1) * R, L1));
+    add_quant(p, Op::kQuantInput, c * R - r, R, chunk_tier(cfg, L - r + (c + 1) * R, L1), L - r + c * R, track);
   p.ops.push_back(Op{Op::kResCopy, n - r_final, r_final, 0, 0});
   p.after.res = r_final;
+  plan_demotions(cfg, p);
   return p;
 }
 
@@ -226,10 +282,16 @@ int run_plan(kvq_cache *c, int layer, const Plan &p, const void *k, const void *
       if (int e = hip_check(launch_residual_copy(a, s), "residual copy")) return e;
     } else {
       QuantArgs a{};
-      a.src_kind = op.kind == Op::kQuantInput ? 0 : 1;
+      a.src_kind = op.kind == Op::kQuantInput ? 0 : op.kind == Op::kQuantResidual ? 1 : 2;
       a.k_src = (const uint16_t *)k; a.v_src = (const uint16_t *)v; a.src_ntok = n;
       a.res_base = c->res(layer); a.res_bh_stride = (int64_t)c->geo.res_bh; a.res_len = cfg.residual_len;
       a.src_tok0 = op.src_tok0; a.count = op.count;
+      if (op.kind == Op::kDemote) {   // one whole young block, decoded and quantized again
+        a.src_arena = c->young(layer);
+        a.src_bh_stride = (int64_t)c->geo.young_bh;
+        a.src_fmt = cfg.format;
+        a.src_tok0 = op.src_tok0 * kBlock;
+      }
       a.arena = op.tier ? c->old(layer) : c->young(layer);
       a.arena_bh_stride = (int64_t)(op.tier ? c->geo.old_bh : c->geo.young_bh);
       a.dst_slot0 = op.dst_slot0;
@@ -273,8 +335,10 @@ int plan_decode(const kvq_cache *c, int layer, DecodeArgs &a, uint64_t *cursors)
   if (st.old > 0)
     tiers[nt++] = {c->old(layer), (int64_t)c->geo.old_bh, st.old, ceil_div(st.old, kBlock), cfg.old_format,
                    tier_gs(&cfg, cfg.old_format)};
-  if (st.young > 0)
-    tiers[nt++] = {c->young(layer), (int64_t)c->geo.young_bh, st.young, ceil_div(st.young, kBlock), cfg.format,
+  const int64_t young_live = st.young - st.young_head * kBlock;
+  if (young_live > 0)
+    tiers[nt++] = {c->young(layer) + (size_t)st.young_head * block_bytes(cfg.format, tier_gs(&cfg, cfg.format)),
+                   (int64_t)c->geo.young_bh, young_live, ceil_div(young_live, kBlock), cfg.format,
                    tier_gs(&cfg, cfg.format)};
   const int cus = c->num_cus > 0 ? c->num_cus : 256;
   const int64_t slots = 2LL * cus;
@@ -458,8 +522,10 @@ int kvq_flush_residual(kvq_cache *c, int32_t layer, void *stream) {
                 (long long)st.res);
   Plan p;
   p.after = st;
-  add_quant(p, Op::kQuantResidual, 0, st.res, chunk_tier(c->cfg, st.length, st.length));
+  add_quant(p, Op::kQuantResidual, 0, st.res, chunk_tier(c->cfg, st.length, st.length), st.length - st.res,
+            c->cfg.demote_young != 0);
   p.after.res = 0;
+  plan_demotions(c->cfg, p);
   int e = run_plan(c, layer, p, nullptr, nullptr, 0, (hipStream_t)stream);
   if (e == KVQ_OK || e == KVQ_EHIP) st = p.after;
   return e;
@@ -505,6 +571,13 @@ int kvq_append_decode_attn(kvq_cache *c, int32_t layer, const void *k, const voi
                     k, v, n_tokens, stream);
 }
 
+int kvq_tier_first_block(const kvq_cache *c, int32_t layer, int32_t region, int64_t *block) {
+  if (int e = check_cache(c, layer)) return e;
+  if (region < 0 || region > 2) return fail(KVQ_EINVAL, "region %d is not 0, 1 or 2", region);
+  if (block) *block = region == 1 ? c->layers[layer].young_head : 0;
+  return KVQ_OK;
+}
+
 int kvq_seq_len(const kvq_cache *c, int32_t layer, int64_t *total, int64_t *in_residual) {
   if (int e = check_cache(c, layer)) return e;
   if (total) *total = c->layers[layer].length;
@@ -520,7 +593,7 @@ int kvq_layout(const kvq_cache *c, int32_t layer, int32_t region, size_t *offset
   int64_t t;
   switch (region) {
     case 0: off = lb + c->geo.off_res; nb = bh * c->geo.res_bh; t = c->layers[layer].res; break;
-    case 1: off = lb + c->geo.off_young; nb = bh * c->geo.young_bh; t = c->layers[layer].young; break;
+    case 1: off = lb + c->geo.off_young; nb = bh * c->geo.young_bh; t = c->layers[layer].young - c->layers[layer].young_head * kBlock; break;
     case 2: off = lb + c->geo.off_old; nb = bh * c->geo.old_bh; t = c->layers[layer].old; break;
     default: return fail(KVQ_EINVAL, "region %d is not 0, 1 or 2", region);
   }

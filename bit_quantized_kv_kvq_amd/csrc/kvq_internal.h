@@ -62,8 +62,12 @@ constexpr size_t kF16Vc = 32768;
 // One quantize launch: tokens [src_tok0, src_tok0 + count) of a source are quantized into
 // slots [dst_slot0, dst_slot0 + count) of a tier arena, for every (batch, kv_head), K and V.
 struct QuantArgs {
-  // source: kind 0 = caller input fp16 [B][H][src_ntok][128]; kind 1 = the layer's residual
+  // source: kind 0 = caller input fp16 [B][H][src_ntok][128]; kind 1 = the layer's residual;
+  // kind 2 = one full block of an affine (groups of 64) tier arena, decoded
   int src_kind;
+  const uint8_t *src_arena;       // kind 2: the source arena; src_tok0 is its slot index
+  int64_t src_bh_stride;          // kind 2: bytes per (b, h)
+  int src_fmt;                    // kind 2: affine format code of the source block
   const uint16_t *k_src, *v_src;  // kind 0
   int64_t src_ntok;               // kind 0: tokens per (b, h) in the input tensor
   const uint8_t *res_base;        // kind 1: residual region of the layer

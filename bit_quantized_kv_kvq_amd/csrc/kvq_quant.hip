@@ -224,6 +224,54 @@ __device__ void store_fp16_block(const uint16_t *xs, uint8_t *blkp, int kv, int 
   }
 }
 
+// Decoded values S (q - Z) of one full affine block (groups of 64, n-bit codes) into the
+// staging rows: block slot s goes to row s - row_off when that row is in [lo, hi).  The
+// product is exact in double; it is clamped to +-65504 and rounded to fp16, ties to even.
+// The words are walked in storage order, each mapped to its slot and dims as the layout
+// above places them (K: a word holds consecutive dims of one slot; V: fields per v_field).
+__device__ void stage_affine_decoded(const uint8_t *yb, int n, int kv, int row_off, int lo, int hi, uint16_t *xs,
+                                     int tid) {
+  const int F = 32 / n, qmax = (1 << n) - 1, nwords = 512 * n;
+  auto dec = [&](const uint8_t *sp, const uint8_t *zp, uint32_t q) -> uint16_t {
+    const double S = (double)h2f(*(const uint16_t *)sp), Z = (double)h2f(*(const uint16_t *)zp);
+    double x = S * ((double)q - Z);
+    x = fmin(fmax(x, -65504.0), 65504.0);
+    return f64_to_f16_rne(x);
+  };
+  if (kv == 0) {
+    const int cb = min(16, 4 * n), K = 4 * n / cb;
+    for (int w = tid; w < nwords; w += kThreads) {
+      const int ci = 4 * w / cb, in_chunk = 4 * w % cb;
+      const int lane = ci & 63, t2 = ci >> 6;
+      const int r = t2 % K, wu = t2 / K;
+      const int slot = 16 * wu + (lane & 15), row = slot - row_off;
+      if (row < lo || row >= hi) continue;
+      const int f0 = (r * cb + in_chunk) / 4 * F;
+      const int d0 = 64 * (f0 >> 4) + 16 * (lane >> 4) + (f0 & 15), grp = d0 >> 6;
+      const uint8_t *m = yb + aff_km(n) + (slot >> 4) * 128 + 2 * (2 * (slot & 15) + grp);
+      const uint32_t word = *(const uint32_t *)(yb + 4 * (size_t)w);
+      for (int k = 0; k < F; ++k) xs[row * kRowHalves + d0 + k] = dec(m, m + 64, (word >> (k * n)) & qmax);
+    }
+  } else {
+    const int chunks = n / 2, fmt = n;
+    for (int w = tid; w < nwords; w += kThreads) {
+      const int lane = (w >> 2) & 63, pc = w >> 8;
+      const int part = pc / chunks, omega = 4 * (pc % chunks) + (w & 3);
+      const int g = lane >> 4, c = lane & 15;
+      const uint32_t word = *(const uint32_t *)(yb + aff_vc(n, 2) + 4 * (size_t)w);
+      for (int j = 0; j < F; ++j) {
+        int k, e;
+        v_field(fmt, omega * F + j, k, e);
+        const int slot = 32 * part + 16 * (e >> 2) + 4 * g + (e & 3), row = slot - row_off;
+        if (row < lo || row >= hi) continue;
+        const int d = 16 * k + c, grp = d >> 6;
+        const uint8_t *m = yb + aff_vm(n, 2) + ((slot >> 4) * 4 + ((slot & 15) >> 2)) * 32 + 8 * grp + 2 * (slot & 3);
+        xs[row * kRowHalves + d] = dec(m, m + 16, (word >> (j * n)) & qmax);
+      }
+    }
+  }
+}
+
 template <int FMT, int GS>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t blk0, int64_t nblk) {
   constexpr bool kMx = FMT == kFmtMxfp4;
@@ -260,7 +308,13 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
   const int64_t tok_off = a.src_tok0 + bstart - a.dst_slot0;   // source index of slot 0
 
   // ---- stage the source tokens of slots [lo, hi) in LDS as fp16 rows
-  if (a.src_kind == 0 || kv == 0) {
+  if (a.src_kind == 2) {
+    // slots [lo, hi) come from one block of the source arena
+    const int64_t s0 = tok_off + lo;
+    const uint8_t *yb = a.src_arena + (int64_t)(b * a.H + h) * a.src_bh_stride +
+                        (s0 / kBlock) * (int64_t)block_bytes(a.src_fmt, kGroup);
+    stage_affine_decoded(yb, a.src_fmt, kv, (int)(tok_off - s0 / kBlock * kBlock), lo, hi, xs, tid);
+  } else if (a.src_kind == 0 || kv == 0) {
     const uint8_t *src;
     int64_t row_stride;
     if (a.src_kind == 0) {

@@ -88,6 +88,17 @@ typedef struct {
                            group_size 64 (and an affine old format), residual_len a positive
                            multiple of 128; kvq_flush_residual then flushes only whole windows.
                            0: per-token groups for K and V. */
+  int32_t demote_young; /* 1: tokens age into the old tier while decoding (page
+                           "KV缓存量化技术：提升大模型长文本生成效率" §4.2, stronger quantization
+                           for early blocks): at the end of every kvq_append and
+                           kvq_flush_residual, while the first live young block is full and its
+                           last token is at least old_after positions behind the length, that
+                           block's 128 tokens are appended to the old tier, quantized in
+                           old_format from the fp16 rounding (to nearest even, saturating at
+                           +-65504) of their decoded young values; the young tier then starts
+                           one block later.  Needs old_after > 0, an affine format with
+                           group_size 64 and per-token K, and a quantized old_format.
+                           0: a stored token keeps its tier. */
 } kvq_config;
 
 /* Bytes of device memory a cache with this configuration needs (0 if cfg is invalid).
@@ -153,9 +164,15 @@ int kvq_seq_len(const kvq_cache *c, int32_t layer, int64_t *total, int64_t *in_r
 
 /* Where a region of a layer lives: region 0 = fp16 residual, 1 = young tier, 2 = old tier.
    *offset: byte offset of the region in dev_buf; *bytes: bytes of the region (all batch
-   entries and kv heads, [batch][kv_head][...]); *tokens: slots in use per (batch, kv_head).
+   entries and kv heads, [batch][kv_head][...]); *tokens: slots in use per (batch, kv_head)
+   (for the young tier: its live slots, from kvq_tier_first_block's block on).
    Any output pointer may be NULL. */
 int kvq_layout(const kvq_cache *c, int32_t layer, int32_t region, size_t *offset, size_t *bytes, int64_t *tokens);
+
+/* First live block of a region's arena: the young tier's blocks before it were moved to the
+   old tier (demote_young); 0 for the other regions and without demotion.  Host-only.
+   Errors: KVQ_EINVAL (handle, layer, region). */
+int kvq_tier_first_block(const kvq_cache *c, int32_t layer, int32_t region, int64_t *block);
 
 /* Plan-only mode (1) updates the host counters exactly as the real calls do but enqueues
    no device work; it lets the bookkeeping run on machines without a GPU.  0 restores

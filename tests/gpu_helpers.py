@@ -34,10 +34,10 @@ def to_dev(a):
 class Pair:
     """A GPU cache and its oracle twin for one layer-set."""
 
-    def __init__(self, layers, B, H, max_tokens, fmt, R, old_fmt=None, old_after=0):
-        self.cfg = kvq.make_config(layers, B, H, max_tokens, fmt, R, old_fmt, old_after)
+    def __init__(self, layers, B, H, max_tokens, fmt, R, old_fmt=None, old_after=0, demote=False):
+        self.cfg = kvq.make_config(layers, B, H, max_tokens, fmt, R, old_fmt, old_after, demote=demote)
         self.gpu = kvq.Cache(self.cfg)
-        self.ora = [LayerCache(fmt, R, old_fmt, old_after) for _ in range(layers)]
+        self.ora = [LayerCache(fmt, R, old_fmt, old_after, demote) for _ in range(layers)]
         self.B, self.H, self.fmt, self.old_fmt, self.R = B, H, fmt, old_fmt or fmt, R
 
     def append(self, layer, k16, v16):
@@ -60,8 +60,11 @@ class Pair:
             dev = self.gpu.region_tensor(layer, region)
             fmt = o.tier_format(tier)
             nblk = -(-ntok // 128)
+            bb = olayout.block_bytes(fmt)
+            fb = self.gpu.first_block(layer, region)        # young blocks before it were demoted
+            assert fb * 128 == (o.sched.young_head if tier == "young" else 0)
             for b, h in pairs:
-                got = dev[b, h, :nblk * olayout.block_bytes(fmt)].cpu().numpy()
+                got = dev[b, h, fb * bb:(fb + nblk) * bb].cpu().numpy()
                 want = o.arena(b, h, tier).ravel()
                 if not np.array_equal(got, want):
                     bad = np.flatnonzero(got != want)

@@ -14,16 +14,17 @@ from oracle import layout as olayout
 pytestmark = pytest.mark.gpu
 
 SIGMA = 1 / np.sqrt(128)
-CASES = [("int4", 128, None, 0), ("nvfp4", 0, None, 0), ("fp8", 16, None, 0), ("int4g32", 256, None, 0),
-         ("int4kc", 128, None, 0), ("int4", 128, "int2", 300), ("mxfp4", 32, None, 0)]
+CASES = [("int4", 128, None, 0, False), ("nvfp4", 0, None, 0, False), ("fp8", 16, None, 0, False),
+         ("int4g32", 256, None, 0, False), ("int4kc", 128, None, 0, False), ("int4", 128, "int2", 300, False),
+         ("mxfp4", 32, None, 0, False), ("int4", 128, "int2", 300, True), ("int8", 0, "nvfp4", 200, True)]
 
 
-@pytest.mark.parametrize("fmt,R,old,old_after", CASES, ids=lambda x: str(x))
-def test_fused_step_matches_separate_calls(fmt, R, old, old_after):
+@pytest.mark.parametrize("fmt,R,old,old_after,demote", CASES, ids=lambda x: str(x))
+def test_fused_step_matches_separate_calls(fmt, R, old, old_after, demote):
     rng = np.random.default_rng(hash((fmt, R)) % 2 ** 32)
     B, H, G = 2, 2, 4
-    fused = Pair(1, B, H, 2000, fmt, R, old, old_after)
-    sep = kvq.Cache(kvq.make_config(1, B, H, 2000, fmt, R, old, old_after))
+    fused = Pair(1, B, H, 2000, fmt, R, old, old_after, demote)
+    sep = kvq.Cache(kvq.make_config(1, B, H, 2000, fmt, R, old, old_after, demote=demote))
     for c in (fused.gpu, sep):
         c.set_deterministic(True)
     k0 = rng.standard_normal((B, H, 300, 128)).astype(np.float16)
@@ -49,7 +50,10 @@ def test_fused_step_matches_separate_calls(fmt, R, old, old_after):
         fused.check_bytes(0)                              # both tiers and the residual against the oracle
         for region, tfmt in ((1, fmt), (2, old or fmt)):     # the twin's written blocks equal the fused cache's
             ntok = fused.gpu.layout(0, region)[2]
-            nb = -(-ntok // 128) * olayout.block_bytes(tfmt)
+            assert fused.gpu.first_block(0, region) == sep.first_block(0, region)
+            nb = (fused.gpu.first_block(0, region) + -(-ntok // 128)) * olayout.block_bytes(tfmt)
             a, b = fused.gpu.region_tensor(0, region), sep.region_tensor(0, region)
             assert torch.equal(a[..., :nb], b[..., :nb]), f"region {region} differs after a step of {n}"
         assert_attention_close(out_f.cpu().numpy().astype(np.float64), decode_layer(fused.ora[0], q, SIGMA))
+    if demote:
+        assert fused.ora[0].sched.young_head > 0, "the steps never demoted a block"

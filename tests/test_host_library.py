@@ -70,10 +70,10 @@ def test_layout_regions(fmt, R, old):
     assert spans[-1][1] <= c.nbytes
 
 
-def _run_schedule(fmt, R, old_after, ops):
-    cfg = kvq.make_config(1, 1, 1, 100000, fmt, R, "int2" if old_after else None, old_after)
+def _run_schedule(fmt, R, old_after, ops, demote=False, old_fmt="int2"):
+    cfg = kvq.make_config(1, 1, 1, 100000, fmt, R, old_fmt if old_after else None, old_after, demote=demote)
     c = kvq.Cache(cfg, plan_only=True)
-    s = Schedule(R, old_after)
+    s = Schedule(R, old_after, demote)
     for op in ops:
         if op == "flush":
             c.flush(0); s.flush()
@@ -81,8 +81,11 @@ def _run_schedule(fmt, R, old_after, ops):
             c.append_plan(0, op); s.append(op)
         total, res = c.seq_len(0)
         assert (total, res) == (s.length, len(s.residual))
-        assert c.layout(0, 1)[2] == len(s.young)
+        assert c.layout(0, 1)[2] == len(s.live_young())
+        assert c.first_block(0, 1) * 128 == s.young_head
         assert c.layout(0, 2)[2] == len(s.old)
+        assert c.first_block(0, 0) == 0 and c.first_block(0, 2) == 0
+    return s
 
 
 @pytest.mark.parametrize("fmt,R,old_after", [("int4", 128, 0), ("int2", 16, 0), ("nvfp4", 0, 0),
@@ -93,6 +96,28 @@ def test_schedule_matches_oracle(fmt, R, old_after):
     ops = [1152, 1, 127, 1, 1, "flush", 3, 128, 129, 1000, "flush", "flush"] + \
           [int(x) if x > 0 else "flush" for x in rng.integers(-3, 300, 40)]
     _run_schedule(fmt, R, old_after, ops)
+
+
+@pytest.mark.parametrize("fmt,R,old_after,old_fmt", [("int4", 128, 300, "int2"), ("int4", 0, 200, "int2"),
+                                                     ("int8", 32, 129, "nvfp4"), ("int2", 16, 1000, "mxfp4"),
+                                                     ("int4", 256, 1, "fp8"), ("int8", 128, 128, "int4")])
+def test_demotion_schedule_matches_oracle(fmt, R, old_after, old_fmt):
+    rng = np.random.default_rng(R + old_after)
+    ops = [1152, 1, 127, 1, 1, "flush", 3, 128, 129, 1000, "flush", "flush"] + [1] * 300 + \
+          [int(x) if x > 0 else "flush" for x in rng.integers(-3, 300, 40)]
+    s = _run_schedule(fmt, R, old_after, ops, demote=True, old_fmt=old_fmt)
+    assert s.young_head > 0 and any(s.old_demoted)
+
+
+@pytest.mark.parametrize("bad", [dict(old_after=0), dict(fmt="nvfp4"), dict(fmt="int4g32", old="int2g32"),
+                                 dict(fmt="int4kc", old="int2kc"), dict(old="fp16"), dict(flag=2)])
+def test_demotion_config_rejected(bad):
+    cfg = kvq.make_config(1, 1, 1, 1000, bad.get("fmt", "int4"), 128, bad.get("old", "int2"),
+                          bad.get("old_after", 100), demote=True)
+    if "flag" in bad:
+        cfg.demote_young = bad["flag"]
+    assert kvq.kvq_cache_bytes(cfg) == 0
+    assert "demote_young" in kvq.lib().kvq_last_error().decode()
 
 
 def test_workload_tiers():
