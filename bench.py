@@ -38,7 +38,11 @@ WORKLOADS = {
     "c4-int4": (4, "int4"), "c4-int2": (4, "int2"), "c5": (5, None),
     "c4-int4g32": (4, "int4g32"), "c4-int4g128": (4, "int4g128"), "c4-int4kc": (4, "int4kc"),
     "c3-mxfp4": (3, "mxfp4"), "c4-mxfp4": (4, "mxfp4"), "c3-fp8": (3, "fp8"), "c4-fp8": (4, "fp8"), "c3-fp16": (3, "fp16"), "c4-fp16": (4, "fp16"),
+    "c5-demote": (5, None),
 }
+# workloads whose young blocks move to the old tier as they age (demote_young), and the
+# timed steps they default to (a block of one (batch, kv_head) ages every 128 one-token steps)
+DEMOTE_STEPS = {"c5-demote": 320}
 
 
 def bytes_per_token(fmt: str) -> float:
@@ -96,14 +100,14 @@ def cpu_baseline(samples, wl, sigma, budget_s: float):
     with threadpool_limits(limits=1):
         for (b, h, kch, vch, q16, got) in samples:
             t0 = time.perf_counter()
-            lc = LayerCache(wl["fmt"], wl["R"], wl["old_fmt"], wl["old_after"])
+            lc = LayerCache(wl["fmt"], wl["R"], wl["old_fmt"], wl["old_after"], wl.get("demote", False))
             for kc, vc in zip(kch, vch):
                 lc.append(kc[None, None], vc[None, None])
             want = decode_layer(lc, q16[None], sigma)[0]
             dt = time.perf_counter() - t0
             t_total += dt
             n_tok = lc.sched.length
-            nq_y, nq_o, nr = len(lc.sched.young), len(lc.sched.old), len(lc.sched.residual)
+            nq_y, nq_o, nr = len(lc.tier_tokens("young")), len(lc.sched.old), len(lc.sched.residual)
             bytes_total += nq_o * bytes_per_token(lc.old_fmt) + nq_y * bytes_per_token(lc.fmt) + nr * 512.0
             worst = max(worst, float(np.abs(got - want).max() / np.abs(want).max()))
             used += 1
@@ -207,7 +211,7 @@ def log(msg: str):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 64; 320 for c5-demote)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c4-int4", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -239,6 +243,9 @@ def main():
     import bit_quantized_kv_kvq_amd as kvq
     import kvq_synth as syn
 
+    demote = args.workload in DEMOTE_STEPS
+    if args.steps is None:
+        args.steps = DEMOTE_STEPS.get(args.workload, 64)
     cid, fmt_over = WORKLOADS[args.workload]
     W = syn.WORKLOADS[cid]
     fmt = fmt_over or W.fmt
@@ -254,7 +261,7 @@ def main():
 
     probe = read_probe_gbs()
 
-    cfg = kvq.make_config(L, B, H, T + n_steps * per_step + 1, fmt, R, W.old_fmt, W.old_after)
+    cfg = kvq.make_config(L, B, H, T + n_steps * per_step + 1, fmt, R, W.old_fmt, W.old_after, demote=demote)
     cache = kvq.Cache(cfg)
     samples_bh = [(b, h) for b in range(B) for h in range(H)][:args.cpu_pairs]
     host_hist = {bh: ([], []) for bh in samples_bh}
@@ -304,9 +311,23 @@ def main():
     # about 3 % of the step time themselves (measured), which the wall clock would then include.
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
-    for e0, e1 in events:
+    # and around each append that demotes a block (demotion workloads), likewise made up front
+    dem_events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(L * (args.steps * per_step // 128 + 2) if demote else 0)]
+    for e0, e1 in events + dem_events:
         e0.record(stream)
         e1.record(stream)
+    dem_used = []
+
+    def demotes(l):
+        """Whether appending this step's tokens to layer l (without a flush) moves a young
+        block to the old tier.  The positions stay in order here (one prefill, then steps),
+        so the first live young block holds positions [old, old + 128)."""
+        if not demote:
+            return False
+        n_old = cache.layout(l, kvq.REGION_OLD)[2]
+        return (cache.layout(l, kvq.REGION_YOUNG)[2] >= 128
+                and n_old + 128 <= cache.seq_len(l)[0] + per_step - W.old_after)
 
     def step(s, ev=None, nbytes=None, timed=None):
         for l in range(L):
@@ -314,9 +335,16 @@ def main():
             # a step whose tokens go straight to the residual is one call and one launch (the
             # copy runs inside the decode launch); a step that quantizes (a full residual, or
             # R = 0) appends first, so that the timed bracket always holds one decode launch
-            quantizes = R == 0 or cache.seq_len(l)[1] + per_step > R
+            quantizes = R == 0 or cache.seq_len(l)[1] + per_step > R or demotes(l)
             if args.separate_append or quantizes:
+                dem = nbytes is not None and demotes(l) and len(dem_used) < len(dem_events)
+                if dem:
+                    fb = cache.first_block(l, kvq.REGION_YOUNG)
+                    dem_events[len(dem_used)][0].record(stream)
                 cache.append(l, knew[s][l], vnew[s][l])
+                if dem:
+                    dem_events[len(dem_used)][1].record(stream)
+                    dem_used.append(cache.first_block(l, kvq.REGION_YOUNG) - fb)
                 if pair is not None:
                     pair[0].record(stream)
                 cache.decode(l, qs[s][l], sigma, outs[l], ws)
@@ -378,7 +406,8 @@ def main():
         "vs_baseline": None,
         "dtype": f"{fmt}-codes/fp16-operands/fp32-accum",
         "data": "synthetic (seeded, drawn on the GPU)",
-        "config": {"workload": W.name if fmt_over is None else W.name.replace(W.fmt, fmt),
+        "config": {"workload": (W.name if fmt_over is None else W.name.replace(W.fmt, fmt))
+                   + (", young blocks demoted as they age" if demote else ""),
                    "layers": L, "batch": B, "q_heads": Hq, "kv_heads": H, "head_dim": 128,
                    "cached_tokens": T, "format": fmt, "old_format": W.old_fmt, "residual": R,
                    "append_per_step": per_step, "parallelism": "none (1 GPU)"},
@@ -395,8 +424,20 @@ def main():
                      "bytes_per_launch": round(float(np.mean(timed_bytes))),
                      "timed_launches": int(dec_ms.size)},
     }
+    if demote:
+        # each demoted block: one young block read and one old block written per (batch, kv_head)
+        blk_bytes = B * H * 128 * (bytes_per_token(fmt) + bytes_per_token(old_fmt))
+        dem_ms = np.array([dem_events[i][0].elapsed_time(dem_events[i][1]) for i in range(len(dem_used))])
+        nblk = int(sum(dem_used))
+        line["config"]["demote_young"] = 1
+        line["demotion"] = {"appends": len(dem_used), "blocks": nblk,
+                            "append_us": round(float(dem_ms.mean()) * 1e3, 2) if dem_used else None,
+                            "bytes_per_block": round(blk_bytes),
+                            "gbs": round(blk_bytes * nblk / (dem_ms.sum() * 1e-3) / 1e9, 1) if nblk else None,
+                            "note": "event brackets around the whole append call that demotes (its residual "
+                                    "copy included)"}
     if not args.no_cpu_baseline:
-        wl = {"fmt": fmt, "R": R, "old_fmt": W.old_fmt, "old_after": W.old_after}
+        wl = {"fmt": fmt, "R": R, "old_fmt": W.old_fmt, "old_after": W.old_after, "demote": demote}
         log("cpu baseline (oracle)")
         base, err = cpu_baseline(samples, wl, sigma, args.cpu_budget)
         line["cpu_baseline"] = base
