@@ -20,8 +20,8 @@ REGION_RESIDUAL, REGION_YOUNG, REGION_OLD = 0, 1, 2
 
 # every symbol include/kvq.h declares
 EXPORTS = ("kvq_cache_bytes", "kvq_cache_create", "kvq_cache_destroy", "kvq_cache_reset", "kvq_append",
-           "kvq_flush_residual", "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_append_decode_attn",
-           "kvq_seq_len", "kvq_layout", "kvq_tier_first_block",
+           "kvq_append_seq", "kvq_flush_residual", "kvq_decode_workspace_bytes", "kvq_decode_attn",
+           "kvq_append_decode_attn", "kvq_seq_len", "kvq_seq_info", "kvq_layout",
            "kvq_set_plan_only", "kvq_set_deterministic", "kvq_last_error")
 
 
@@ -36,6 +36,11 @@ class kvq_config(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("max_tokens", ctypes.c_int64), ("format", ctypes.c_int32),
                 ("group_size", ctypes.c_int32), ("residual_len", ctypes.c_int32), ("old_format", ctypes.c_int32),
                 ("old_after", ctypes.c_int64), ("k_per_channel", ctypes.c_int32), ("demote_young", ctypes.c_int32)]
+
+
+class kvq_seq_info_t(ctypes.Structure):
+    _fields_ = [("length", ctypes.c_int64), ("residual", ctypes.c_int64), ("young_first_block", ctypes.c_int64),
+                ("young_tokens", ctypes.c_int64), ("old_tokens", ctypes.c_int64)]
 
 
 _lib = None
@@ -60,6 +65,7 @@ def lib() -> ctypes.CDLL:
     L.kvq_cache_destroy.argtypes = [vp]; L.kvq_cache_destroy.restype = ctypes.c_int
     L.kvq_cache_reset.argtypes = [vp]; L.kvq_cache_reset.restype = ctypes.c_int
     L.kvq_append.argtypes = [vp, i32, vp, vp, i64, vp]; L.kvq_append.restype = ctypes.c_int
+    L.kvq_append_seq.argtypes = [vp, i32, i32, vp, vp, i64, vp]; L.kvq_append_seq.restype = ctypes.c_int
     L.kvq_flush_residual.argtypes = [vp, i32, vp]; L.kvq_flush_residual.restype = ctypes.c_int
     L.kvq_decode_workspace_bytes.argtypes = [vp, i32]; L.kvq_decode_workspace_bytes.restype = sz
     L.kvq_decode_attn.argtypes = [vp, i32, vp, i32, ctypes.c_float, vp, i32, vp, sz, vp]
@@ -68,7 +74,7 @@ def lib() -> ctypes.CDLL:
     L.kvq_append_decode_attn.restype = ctypes.c_int
     L.kvq_seq_len.argtypes = [vp, i32, P(i64), P(i64)]; L.kvq_seq_len.restype = ctypes.c_int
     L.kvq_layout.argtypes = [vp, i32, i32, P(sz), P(sz), P(i64)]; L.kvq_layout.restype = ctypes.c_int
-    L.kvq_tier_first_block.argtypes = [vp, i32, i32, P(i64)]; L.kvq_tier_first_block.restype = ctypes.c_int
+    L.kvq_seq_info.argtypes = [vp, i32, i32, P(kvq_seq_info_t)]; L.kvq_seq_info.restype = ctypes.c_int
     L.kvq_set_plan_only.argtypes = [vp, i32]; L.kvq_set_plan_only.restype = ctypes.c_int
     L.kvq_set_deterministic.argtypes = [vp, i32]; L.kvq_set_deterministic.restype = ctypes.c_int
     L.kvq_last_error.argtypes = []; L.kvq_last_error.restype = ctypes.c_char_p
@@ -168,6 +174,20 @@ class Cache:
         assert self.plan_only
         _check(lib().kvq_append(self.h, layer, 1 << 40, 1 << 40, n, None))
 
+    def append_seq(self, layer: int, seq: int, k, v, stream=None):
+        """kvq_append_seq: k, v fp16 [kv_heads, n, 128] appended to sequence seq alone."""
+        n = k.shape[-2]
+        if self.plan_only:
+            _check(lib().kvq_append_seq(self.h, layer, seq, 1 << 40, 1 << 40, n, None))
+            return
+        assert k.is_contiguous() and v.is_contiguous()
+        _check(lib().kvq_append_seq(self.h, layer, seq, k.data_ptr(), v.data_ptr(), n, _stream_ptr(stream)))
+
+    def append_seq_plan(self, layer: int, seq: int, n: int):
+        """Bookkeeping-only kvq_append_seq of n tokens (plan-only caches)."""
+        assert self.plan_only
+        _check(lib().kvq_append_seq(self.h, layer, seq, 1 << 40, 1 << 40, n, None))
+
     def flush(self, layer: int, stream=None):
         _check(lib().kvq_flush_residual(self.h, layer, None if self.plan_only else _stream_ptr(stream)))
 
@@ -211,11 +231,16 @@ class Cache:
         _check(lib().kvq_layout(self.h, layer, region, ctypes.byref(off), ctypes.byref(nb), ctypes.byref(tok)))
         return off.value, nb.value, tok.value
 
-    def first_block(self, layer: int, region: int) -> int:
-        """kvq_tier_first_block: the first live block of a region's arena."""
-        b = ctypes.c_int64()
-        _check(lib().kvq_tier_first_block(self.h, layer, region, ctypes.byref(b)))
-        return b.value
+    def seq_info(self, layer: int, seq: int = 0) -> dict:
+        """kvq_seq_info: one sequence's host counters."""
+        i = kvq_seq_info_t()
+        _check(lib().kvq_seq_info(self.h, layer, seq, ctypes.byref(i)))
+        return {f: getattr(i, f) for f, _ in kvq_seq_info_t._fields_}
+
+    def first_block(self, layer: int, region: int, seq: int = 0) -> int:
+        """First live block of a region's arena for one sequence (the young tier's blocks before
+        it were demoted)."""
+        return self.seq_info(layer, seq)["young_first_block"] if region == REGION_YOUNG else 0
 
     def region_tensor(self, layer: int, region: int):
         """uint8 device view [batch, kv_heads, bytes per (b, h)] of a region."""

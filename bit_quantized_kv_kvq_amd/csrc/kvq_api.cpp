@@ -58,6 +58,7 @@ int tier_gs(const kvq_config *c, int fmt) {
 // Young slots [slot0, slot0 + count) hold the tokens at stream positions [pos0, pos0 + count).
 struct Run {
   int64_t slot0, pos0, count;
+  bool operator==(const Run &o) const { return slot0 == o.slot0 && pos0 == o.pos0 && count == o.count; }
 };
 
 struct LayerState {
@@ -67,6 +68,10 @@ struct LayerState {
   int64_t old = 0;     // slots used in the old arena
   int64_t young_head = 0;   // young blocks demoted to the old tier (the tier starts after them)
   std::vector<Run> runs;    // positions of the live young slots (kept only when demoting)
+  bool operator==(const LayerState &o) const {
+    return length == o.length && res == o.res && young == o.young && old == o.old && young_head == o.young_head &&
+           runs == o.runs;
+  }
 };
 
 struct Geometry {
@@ -130,7 +135,8 @@ struct kvq_cache {
   Geometry geo;
   uint8_t *base = nullptr;
   size_t bytes = 0;
-  std::vector<LayerState> layers;
+  std::vector<LayerState> seqs;      // [layer][sequence]: each sequence of the batch has its own schedule
+  std::vector<uint8_t> rag_host;     // host copy of a ragged decode call's tables
   int plan_only = 0;
   int deterministic = 0;   // decode: chunks assigned up front instead of through the cursor
   int num_cus = 0;
@@ -139,6 +145,14 @@ struct kvq_cache {
   uint8_t *res(int l) const { return layer_base(l) + geo.off_res; }
   uint8_t *young(int l) const { return layer_base(l) + geo.off_young; }
   uint8_t *old(int l) const { return layer_base(l) + geo.off_old; }
+  LayerState &st(int l, int b) { return seqs[(size_t)l * cfg.batch + b]; }
+  const LayerState &st(int l, int b) const { return seqs[(size_t)l * cfg.batch + b]; }
+  // every sequence of the layer in the same state (the batched path); else a ragged batch
+  bool uniform(int l) const {
+    for (int b = 1; b < cfg.batch; ++b)
+      if (!(st(l, b) == st(l, 0))) return false;
+    return true;
+  }
 };
 
 namespace {
@@ -265,34 +279,46 @@ Plan plan_append(const kvq_config &cfg, const LayerState &st, int64_t n) {
   return p;
 }
 
-int run_plan(kvq_cache *c, int layer, const Plan &p, const void *k, const void *v, int64_t n, hipStream_t s) {
-  const auto &cfg = c->cfg;
-  // capacity of the tier arenas follows from max_tokens; checked again here
+// capacity of the tier arenas follows from max_tokens; checked again here
+int check_capacity(const kvq_cache *c, const Plan &p) {
   if (p.after.young > c->geo.young_cap_blocks * kBlock || p.after.old > c->geo.old_cap_blocks * kBlock)
     return fail(KVQ_ECAPACITY, "tier arena full (young %lld/%lld, old %lld/%lld slots)", (long long)p.after.young,
                 (long long)(c->geo.young_cap_blocks * kBlock), (long long)p.after.old, (long long)(c->geo.old_cap_blocks * kBlock));
+  return KVQ_OK;
+}
+
+// Enqueue a plan's ops for every sequence (seq < 0: the batch shares the plan; k, v are
+// [B][H][n][128]) or for sequence seq alone (k, v are its [H][n][128]).
+int run_plan(kvq_cache *c, int layer, const Plan &p, const void *k, const void *v, int64_t n, hipStream_t s,
+             int seq = -1) {
+  const auto &cfg = c->cfg;
+  if (int e = check_capacity(c, p)) return e;
   if (c->plan_only) return KVQ_OK;
+  const int B = seq < 0 ? cfg.batch : 1;
+  const size_t b0 = seq < 0 ? 0 : (size_t)seq * cfg.num_kv_heads;   // first (b, h) of the launch
+  uint8_t *res = c->res(layer) + b0 * c->geo.res_bh;
+  uint8_t *young = c->young(layer) + b0 * c->geo.young_bh, *old = c->old(layer) + b0 * c->geo.old_bh;
   for (const Op &op : p.ops) {
     if (op.kind == Op::kResCopy) {
       ResCopyArgs a{};
       a.k_src = (const uint16_t *)k; a.v_src = (const uint16_t *)v; a.src_ntok = n;
       a.src_tok0 = op.src_tok0; a.count = op.count;
-      a.res_base = c->res(layer); a.res_bh_stride = (int64_t)c->geo.res_bh; a.res_len = cfg.residual_len;
-      a.dst_slot0 = op.dst_slot0; a.B = cfg.batch; a.H = cfg.num_kv_heads;
+      a.res_base = res; a.res_bh_stride = (int64_t)c->geo.res_bh; a.res_len = cfg.residual_len;
+      a.dst_slot0 = op.dst_slot0; a.B = B; a.H = cfg.num_kv_heads;
       if (int e = hip_check(launch_residual_copy(a, s), "residual copy")) return e;
     } else {
       QuantArgs a{};
       a.src_kind = op.kind == Op::kQuantInput ? 0 : op.kind == Op::kQuantResidual ? 1 : 2;
       a.k_src = (const uint16_t *)k; a.v_src = (const uint16_t *)v; a.src_ntok = n;
-      a.res_base = c->res(layer); a.res_bh_stride = (int64_t)c->geo.res_bh; a.res_len = cfg.residual_len;
+      a.res_base = res; a.res_bh_stride = (int64_t)c->geo.res_bh; a.res_len = cfg.residual_len;
       a.src_tok0 = op.src_tok0; a.count = op.count;
       if (op.kind == Op::kDemote) {   // one whole young block, decoded and quantized again
-        a.src_arena = c->young(layer);
+        a.src_arena = young;
         a.src_bh_stride = (int64_t)c->geo.young_bh;
         a.src_fmt = cfg.format;
         a.src_tok0 = op.src_tok0 * kBlock;
       }
-      a.arena = op.tier ? c->old(layer) : c->young(layer);
+      a.arena = op.tier ? old : young;
       a.arena_bh_stride = (int64_t)(op.tier ? c->geo.old_bh : c->geo.young_bh);
       a.dst_slot0 = op.dst_slot0;
       a.fmt = op.tier ? cfg.old_format : cfg.format;
@@ -300,7 +326,7 @@ int run_plan(kvq_cache *c, int layer, const Plan &p, const void *k, const void *
       if (a.gs == kKc && (op.dst_slot0 % kBlock != 0 || op.count % kBlock != 0))
         return fail(KVQ_ESTATE, "per-channel K: a quantize of %lld slots at %lld is not whole windows",
                     (long long)op.count, (long long)op.dst_slot0);
-      a.B = cfg.batch; a.H = cfg.num_kv_heads;
+      a.B = B; a.H = cfg.num_kv_heads;
       if (int e = hip_check(launch_quantize(a, s), "quantize")) return e;
     }
   }
@@ -315,70 +341,198 @@ std::atomic<uint32_t> g_epoch{0};
 size_t counters_bytes(const kvq_cache *c) {
   return align_up((size_t)c->cfg.batch * c->cfg.num_kv_heads * (1 + kMaxSegs) * sizeof(uint64_t));
 }
-
-size_t workspace_bound(const kvq_cache *c, int32_t num_q_heads) {
+size_t partials_bytes(const kvq_cache *c, int32_t num_q_heads) {
   const size_t bh = (size_t)c->cfg.batch * c->cfg.num_kv_heads;
-  const size_t G = (size_t)(num_q_heads / c->cfg.num_kv_heads);
-  return counters_bytes(c) + bh * kMaxParts * G * kPartialStride * sizeof(float);
+  return align_up(bh * kMaxParts * (size_t)(num_q_heads / c->cfg.num_kv_heads) * kPartialStride * sizeof(float));
+}
+// ragged calls: one RagSeq per sequence, then one table entry per workgroup
+size_t rag_seq_bytes(const kvq_cache *c) { return align_up((size_t)c->cfg.batch * sizeof(RagSeq)); }
+size_t rag_wg_bytes(const kvq_cache *c) {
+  return align_up((size_t)c->cfg.batch * c->cfg.num_kv_heads * kMaxParts * sizeof(uint32_t));
 }
 
-// Give every tier of the layer work items in proportion to its bytes, so that all work items
-// of the call fill the GPU about once (two workgroups per CU), and cut it into chunks small
-// enough (about 32 per item) that the items of a (b, h) even out their finishing times.
-int plan_decode(const kvq_cache *c, int layer, DecodeArgs &a, uint64_t *cursors) {
+size_t workspace_bound(const kvq_cache *c, int32_t num_q_heads) {
+  return counters_bytes(c) + partials_bytes(c, num_q_heads) + rag_seq_bytes(c) + rag_wg_bytes(c);
+}
+
+// The quantized tiers of one sequence as the decode streams them: old, then young from its
+// first live block.
+struct TierRef {
+  const uint8_t *base;
+  int64_t stride, ntok, nblk;
+  int fmt, gs, slot;   // slot: 0 old, 1 young
+};
+int tiers_of(const kvq_cache *c, int layer, const LayerState &st, TierRef *t) {
   const auto &cfg = c->cfg;
-  const LayerState &st = c->layers[layer];
-  const int64_t nbh = (int64_t)cfg.batch * cfg.num_kv_heads;
-  struct T { const uint8_t *base; int64_t stride, ntok, nblk; int fmt, gs; };
-  T tiers[2];
   int nt = 0;
   if (st.old > 0)
-    tiers[nt++] = {c->old(layer), (int64_t)c->geo.old_bh, st.old, ceil_div(st.old, kBlock), cfg.old_format,
-                   tier_gs(&cfg, cfg.old_format)};
+    t[nt++] = {c->old(layer), (int64_t)c->geo.old_bh, st.old, ceil_div(st.old, kBlock), cfg.old_format,
+               tier_gs(&cfg, cfg.old_format), 0};
   const int64_t young_live = st.young - st.young_head * kBlock;
   if (young_live > 0)
-    tiers[nt++] = {c->young(layer) + (size_t)st.young_head * block_bytes(cfg.format, tier_gs(&cfg, cfg.format)),
-                   (int64_t)c->geo.young_bh, young_live, ceil_div(young_live, kBlock), cfg.format,
-                   tier_gs(&cfg, cfg.format)};
-  const int cus = c->num_cus > 0 ? c->num_cus : 256;
-  const int64_t slots = 2LL * cus;
-  const int64_t target = std::max<int64_t>(1, slots / nbh);       // work items per (b, h)
+    t[nt++] = {c->young(layer) + (size_t)st.young_head * block_bytes(cfg.format, tier_gs(&cfg, cfg.format)),
+               (int64_t)c->geo.young_bh, young_live, ceil_div(young_live, kBlock), cfg.format,
+               tier_gs(&cfg, cfg.format), 1};
+  return nt;
+}
+
+double tier_bytes(const TierRef &t) { return (double)t.nblk * (double)block_bytes(t.fmt, t.gs); }
+
+// Give each tier of a (b, h) work items in proportion to its bytes (`target` items in all),
+// cut into chunks small enough (about 32 per item) that the items of a (b, h) even out their
+// finishing times.  Fills out[i] for tier i (not its cursors); returns the items.
+int split_tiers(const kvq_cache *c, const TierRef *t, int nt, int64_t target, DecodeSeg *out) {
   double bytes = 0;
-  for (int i = 0; i < nt; ++i) bytes += (double)tiers[i].nblk * (double)block_bytes(tiers[i].fmt, tiers[i].gs);
-  a.nseg = 0;
+  for (int i = 0; i < nt; ++i) bytes += tier_bytes(t[i]);
   int parts = 0;
   for (int i = 0; i < nt; ++i) {
-    const T &t = tiers[i];
-    int64_t items = std::max<int64_t>(1, (int64_t)((double)target * t.nblk * block_bytes(t.fmt, t.gs) / bytes + 0.5));
+    int64_t items = std::max<int64_t>(1, (int64_t)((double)target * tier_bytes(t[i]) / bytes + 0.5));
     items = std::min<int64_t>(items, kMaxParts / std::max(1, nt));
     // units of about 1/32 of an item's share, at least four blocks (a unit's cursor fetch
     // has four block times to come back); two fixed units per item, then the cursor's big
     // units, then two single blocks per item for the finish
-    int64_t chunk = std::max<int64_t>(4, ceil_div(t.nblk, items * 32));
+    const int64_t nblk = t[i].nblk;
+    int64_t chunk = std::max<int64_t>(4, ceil_div(nblk, items * 32));
     int64_t fixed = 2, nbig = 0;
-    if (t.nblk >= (fixed + 2) * items * chunk) {
+    if (nblk >= (fixed + 2) * items * chunk) {
       if (c->deterministic)
-        fixed = ceil_div(ceil_div(t.nblk, chunk), items);   // every chunk dealt round-robin up front
+        fixed = ceil_div(ceil_div(nblk, chunk), items);   // every chunk dealt round-robin up front
       else
-        nbig = std::max<int64_t>(0, (t.nblk - fixed * items * chunk - 2 * items) / chunk);
+        nbig = std::max<int64_t>(0, (nblk - fixed * items * chunk - 2 * items) / chunk);
     } else {
       // too little to share out: single blocks, dealt round-robin
       chunk = 1;
-      items = std::min<int64_t>(items, t.nblk);
-      fixed = ceil_div(t.nblk, items);
+      items = std::min<int64_t>(items, nblk);
+      fixed = ceil_div(nblk, items);
     }
-    DecodeSeg &s = a.seg[a.nseg++];
-    s.base = t.base; s.bh_stride = t.stride; s.ntok = t.ntok; s.fmt = t.fmt; s.gs = t.gs;
+    DecodeSeg &s = out[i];
+    s.base = t[i].base; s.bh_stride = t[i].stride; s.ntok = t[i].ntok; s.fmt = t[i].fmt; s.gs = t[i].gs;
     s.chunk = (int)chunk; s.items = (int)items; s.fixed = (int)fixed; s.nbig = (int)nbig; s.part0 = parts;
-    s.cursors = cursors + (size_t)i * nbh;
+    s.cursors = nullptr;
     parts += (int)items;
   }
+  return parts;
+}
+
+int num_cus(kvq_cache *c) {
+  if (c->num_cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      c->num_cus = n;
+    else
+      c->num_cus = 256;
+  }
+  return c->num_cus;
+}
+
+// Every sequence in one state: all work items of the call fill the GPU about once (two
+// workgroups per CU), the same split for every (b, h).
+int plan_decode(kvq_cache *c, int layer, DecodeArgs &a, uint64_t *cursors) {
+  const auto &cfg = c->cfg;
+  const LayerState &st = c->st(layer, 0);
+  const int64_t nbh = (int64_t)cfg.batch * cfg.num_kv_heads;
+  TierRef tiers[kMaxSegs];
+  const int nt = tiers_of(c, layer, st, tiers);
+  const int64_t target = std::max<int64_t>(1, 2LL * num_cus(c) / nbh);       // work items per (b, h)
+  const int parts = split_tiers(c, tiers, nt, target, a.seg);
+  for (int i = 0; i < nt; ++i) a.seg[i].cursors = cursors + (size_t)i * nbh;
+  a.nseg = nt;
   a.items_total = std::max(1, parts);
   a.res_base = c->res(layer);
   a.res_bh_stride = (int64_t)c->geo.res_bh;
   a.res_len = cfg.residual_len;
   a.res_ntok = (int)st.res;
+  a.rag = nullptr;
+  a.rag_wg = nullptr;
   return (int)(nbh * a.items_total);
+}
+
+// A ragged batch: each sequence gets work items in proportion to its own bytes (the call's
+// items still fill the GPU about once) and its own split; the tables go to the workspace
+// (stream-ordered copy) for the kernel.  pend[b]: sequence b's pending residual copy (count 0: none).
+int plan_decode_ragged(kvq_cache *c, int layer, DecodeArgs &a, uint8_t *ws, const Op *pend, hipStream_t stream,
+                       int *num_wg) {
+  const auto &cfg = c->cfg;
+  const int B = cfg.batch, H = cfg.num_kv_heads;
+  const int64_t nbh = (int64_t)B * H;
+  if (B > 65536 || H > 512) return fail(KVQ_EINVAL, "ragged decode supports batch <= 65536 and kv heads <= 512");
+  uint64_t *cursors = (uint64_t *)ws + nbh;
+  // the call's segments: a tier that any sequence has (old first, as for one sequence)
+  std::vector<TierRef> tb((size_t)B * kMaxSegs);
+  std::vector<int> nts(B);
+  std::vector<double> bytes(B, 0.0);
+  bool has[2] = {false, false};
+  double total = 0;
+  for (int b = 0; b < B; ++b) {
+    nts[b] = tiers_of(c, layer, c->st(layer, b), &tb[(size_t)b * kMaxSegs]);
+    for (int i = 0; i < nts[b]; ++i) {
+      has[tb[(size_t)b * kMaxSegs + i].slot] = true;
+      bytes[b] += tier_bytes(tb[(size_t)b * kMaxSegs + i]);
+    }
+    bytes[b] += 512.0 * (double)c->st(layer, b).res;
+    total += bytes[b];
+  }
+  int seg_of[2] = {-1, -1};
+  a.nseg = 0;
+  for (int slot = 0; slot < 2; ++slot) {
+    if (!has[slot]) continue;
+    DecodeSeg &s = a.seg[a.nseg];
+    s = DecodeSeg{};
+    s.base = slot ? c->young(layer) : c->old(layer);
+    s.bh_stride = (int64_t)(slot ? c->geo.young_bh : c->geo.old_bh);
+    s.fmt = slot ? cfg.format : cfg.old_format;
+    s.gs = tier_gs(&cfg, s.fmt);
+    s.cursors = cursors + (size_t)a.nseg * nbh;
+    seg_of[slot] = a.nseg++;
+  }
+  const double slots = 2.0 * num_cus(c);
+  c->rag_host.assign(rag_seq_bytes(c) + rag_wg_bytes(c), 0);
+  RagSeq *rs = (RagSeq *)c->rag_host.data();
+  int maxp = 1;
+  for (int b = 0; b < B; ++b) {
+    RagSeq &r = rs[b];
+    for (int u = 0; u < a.nseg; ++u) {
+      r.seg[u] = a.seg[u];
+      r.seg[u].chunk = 1;
+    }
+    const int64_t target = std::max<int64_t>(1, (int64_t)(slots * bytes[b] / (total * H) + 0.5));
+    DecodeSeg out[kMaxSegs];
+    const int parts = split_tiers(c, &tb[(size_t)b * kMaxSegs], nts[b], target, out);
+    for (int i = 0; i < nts[b]; ++i) {
+      const int u = seg_of[tb[(size_t)b * kMaxSegs + i].slot];
+      out[i].cursors = a.seg[u].cursors;
+      r.seg[u] = out[i];
+    }
+    r.items_total = std::max(1, parts);
+    r.res_ntok = (int)c->st(layer, b).res;
+    if (pend && pend[b].count > 0) {
+      r.pend_src_tok0 = pend[b].src_tok0;
+      r.pend_count = (int)pend[b].count;
+      r.pend_slot0 = (int)pend[b].dst_slot0;
+    }
+    maxp = std::max(maxp, r.items_total);
+  }
+  // part-major, so that the items of a (b, h) are spread over the launch
+  uint32_t *wg = (uint32_t *)(c->rag_host.data() + rag_seq_bytes(c));
+  int n = 0;
+  for (int p = 0; p < maxp; ++p)
+    for (int b = 0; b < B; ++b)
+      if (p < rs[b].items_total)
+        for (int h = 0; h < H; ++h) wg[n++] = (uint32_t)b | ((uint32_t)h << 16) | ((uint32_t)p << 25);
+  uint8_t *dev_tab = ws + counters_bytes(c) + partials_bytes(c, a.G * H);
+  const size_t copy = rag_seq_bytes(c) + (size_t)n * sizeof(uint32_t);
+  if (!c->plan_only)
+    if (int e = hip_check(hipMemcpyAsync(dev_tab, c->rag_host.data(), copy, hipMemcpyHostToDevice, stream), "ragged tables"))
+      return e;
+  a.rag = (const RagSeq *)dev_tab;
+  a.rag_wg = (const uint32_t *)(dev_tab + rag_seq_bytes(c));
+  a.items_total = 1;
+  a.res_base = c->res(layer);
+  a.res_bh_stride = (int64_t)c->geo.res_bh;
+  a.res_len = cfg.residual_len;
+  a.res_ntok = 0;
+  *num_wg = n;
+  return KVQ_OK;
 }
 
 int check_decode(const kvq_cache *c, const void *q, int32_t num_q_heads, float softmax_scale, const void *out,
@@ -396,53 +550,100 @@ int check_decode(const kvq_cache *c, const void *q, int32_t num_q_heads, float s
   return KVQ_OK;
 }
 
-int check_append(const kvq_cache *c, int32_t layer, const void *k, const void *v, int64_t n_tokens) {
+// seq < 0: every sequence appends n_tokens
+int check_append(const kvq_cache *c, int32_t layer, const void *k, const void *v, int64_t n_tokens, int seq = -1) {
   if (n_tokens < 0) return fail(KVQ_EINVAL, "n_tokens < 0");
   if (n_tokens == 0) return KVQ_OK;
   if (!k || !v) return fail(KVQ_EINVAL, "k or v is NULL");
   if (!aligned16(k) || !aligned16(v)) return fail(KVQ_EINVAL, "k and v must be 16-byte aligned");
-  const LayerState &st = c->layers[layer];
-  if (st.length + n_tokens > c->cfg.max_tokens)
-    return fail(KVQ_ECAPACITY, "layer %d: %lld + %lld tokens exceeds max_tokens %lld", layer, (long long)st.length,
-                (long long)n_tokens, (long long)c->cfg.max_tokens);
+  for (int b = seq < 0 ? 0 : seq; b < (seq < 0 ? c->cfg.batch : seq + 1); ++b) {
+    const LayerState &st = c->st(layer, b);
+    if (st.length + n_tokens > c->cfg.max_tokens)
+      return fail(KVQ_ECAPACITY, "layer %d, sequence %d: %lld + %lld tokens exceeds max_tokens %lld", layer, b,
+                  (long long)st.length, (long long)n_tokens, (long long)c->cfg.max_tokens);
+  }
   return KVQ_OK;
 }
 
 // The decode launch of a checked call.  `pending` (may be null): the residual copy of the same
-// call's append (tokens [src_tok0, +count) of k / v, n_src tokens each), done by the launch itself.
+// call's append (tokens [src_tok0, +count) of k / v, n_src tokens each), done by the launch
+// itself; for a ragged batch (`ragged`) one Op per sequence.
 int run_decode(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_heads, float softmax_scale, void *out,
                int32_t out_fp32, void *workspace, const Op *pending, const void *k, const void *v, int64_t n_src,
-               void *stream) {
+               void *stream, bool ragged) {
   const auto &cfg = c->cfg;
   const int G = num_q_heads / cfg.num_kv_heads;
   if (c->plan_only) return KVQ_OK;
-  if (c->num_cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      c->num_cus = n;
-    else
-      c->num_cus = 256;
-  }
   DecodeArgs a{};
-  const int num_wg = plan_decode(c, layer, a, (uint64_t *)workspace + (size_t)cfg.batch * cfg.num_kv_heads);
+  a.B = cfg.batch; a.H = cfg.num_kv_heads; a.G = G;
+  int num_wg = 0;
+  if (ragged) {
+    if (int e = plan_decode_ragged(c, layer, a, (uint8_t *)workspace, pending, (hipStream_t)stream, &num_wg)) return e;
+  } else {
+    num_wg = plan_decode(c, layer, a, (uint64_t *)workspace + (size_t)cfg.batch * cfg.num_kv_heads);
+  }
   a.q = (const uint16_t *)q;
   a.out = out;
   a.out_fp32 = out_fp32 ? 1 : 0;
   a.counters = (uint64_t *)workspace;
   a.partials = (float *)((uint8_t *)workspace + counters_bytes(c));
-  a.B = cfg.batch; a.H = cfg.num_kv_heads; a.G = G;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   uint32_t ep = ++g_epoch;
   if (ep == 0) ep = ++g_epoch;
   a.epoch = ep;
   if (pending) {
     a.pend_k = (const uint16_t *)k; a.pend_v = (const uint16_t *)v;
-    a.pend_src_ntok = n_src; a.pend_src_tok0 = pending->src_tok0;
-    a.pend_count = (int)pending->count; a.pend_slot0 = (int)pending->dst_slot0;
+    a.pend_src_ntok = n_src;
+    if (!ragged) {
+      a.pend_src_tok0 = pending->src_tok0;
+      a.pend_count = (int)pending->count; a.pend_slot0 = (int)pending->dst_slot0;
+    }
   }
   return hip_check(launch_decode(a, num_wg, (hipStream_t)stream), "decode");
 }
 
+// Append n tokens to every sequence of a layer whose sequences differ: one plan per sequence,
+// all checked before anything is enqueued.  pend (may be null): a trailing residual copy of
+// each plan is taken out into pend[b] (count 0: none) instead of being enqueued.
+int append_ragged(kvq_cache *c, int layer, const void *k, const void *v, int64_t n, hipStream_t s, Op *pend) {
+  const int B = c->cfg.batch;
+  std::vector<Plan> plans(B);
+  for (int b = 0; b < B; ++b) {
+    plans[b] = plan_append(c->cfg, c->st(layer, b), n);
+    if (int e = check_capacity(c, plans[b])) return e;
+  }
+  const size_t per_seq = (size_t)c->cfg.num_kv_heads * (size_t)n * kHeadDim;   // fp16 values
+  for (int b = 0; b < B; ++b) {
+    Plan &p = plans[b];
+    if (pend) {
+      pend[b] = Op{Op::kResCopy, 0, 0, 0, 0};
+      if (!p.ops.empty() && p.ops.back().kind == Op::kResCopy) {
+        pend[b] = p.ops.back();
+        p.ops.pop_back();
+      }
+    }
+    const int e = run_plan(c, layer, p, (const uint16_t *)k + b * per_seq, (const uint16_t *)v + b * per_seq, n, s, b);
+    if (e == KVQ_OK || e == KVQ_EHIP) c->st(layer, b) = p.after;
+    if (e != KVQ_OK) return e;
+  }
+  return KVQ_OK;
+}
+
+int check_seq(const kvq_cache *c, int32_t layer, int32_t seq) {
+  if (int e = check_cache(c, layer)) return e;
+  if (seq < 0 || seq >= c->cfg.batch) return fail(KVQ_EINVAL, "sequence %d out of range [0, %d)", seq, c->cfg.batch);
+  return KVQ_OK;
+}
+
+Plan plan_flush(const kvq_cache *c, const LayerState &st) {
+  Plan p;
+  p.after = st;
+  add_quant(p, Op::kQuantResidual, 0, st.res, chunk_tier(c->cfg, st.length, st.length), st.length - st.res,
+            c->cfg.demote_young != 0);
+  p.after.res = 0;
+  plan_demotions(c->cfg, p);
+  return p;
+}
 
 }  // namespace
 
@@ -473,7 +674,7 @@ int kvq_cache_create(const kvq_config *cfg, void *dev_buf, size_t dev_bytes, kvq
   c->geo = geometry(cfg);
   c->base = (uint8_t *)dev_buf;
   c->bytes = dev_bytes;
-  c->layers.assign(cfg->num_layers, LayerState{});
+  c->seqs.assign((size_t)cfg->num_layers * cfg->batch, LayerState{});
   *out = c;
   g_err.clear();
   return KVQ_OK;
@@ -486,7 +687,7 @@ int kvq_cache_destroy(kvq_cache *c) {
 
 int kvq_cache_reset(kvq_cache *c) {
   if (!c) return fail(KVQ_EINVAL, "cache handle is NULL");
-  for (auto &l : c->layers) l = LayerState{};
+  for (auto &l : c->seqs) l = LayerState{};
   return KVQ_OK;
 }
 
@@ -506,29 +707,55 @@ int kvq_append(kvq_cache *c, int32_t layer, const void *k, const void *v, int64_
   if (int e = check_cache(c, layer)) return e;
   if (int e = check_append(c, layer, k, v, n_tokens)) return e;
   if (n_tokens == 0) return KVQ_OK;
-  LayerState &st = c->layers[layer];
-  Plan p = plan_append(c->cfg, st, n_tokens);
+  if (!c->uniform(layer)) return append_ragged(c, layer, k, v, n_tokens, (hipStream_t)stream, nullptr);
+  Plan p = plan_append(c->cfg, c->st(layer, 0), n_tokens);
   int e = run_plan(c, layer, p, k, v, n_tokens, (hipStream_t)stream);
+  if (e == KVQ_OK || e == KVQ_EHIP)
+    for (int b = 0; b < c->cfg.batch; ++b) c->st(layer, b) = p.after;
+  return e;
+}
+
+int kvq_append_seq(kvq_cache *c, int32_t layer, int32_t seq, const void *k, const void *v, int64_t n_tokens,
+                   void *stream) {
+  if (int e = check_seq(c, layer, seq)) return e;
+  if (int e = check_append(c, layer, k, v, n_tokens, seq)) return e;
+  if (n_tokens == 0) return KVQ_OK;
+  LayerState &st = c->st(layer, seq);
+  Plan p = plan_append(c->cfg, st, n_tokens);
+  int e = run_plan(c, layer, p, k, v, n_tokens, (hipStream_t)stream, seq);
   if (e == KVQ_OK || e == KVQ_EHIP) st = p.after;
   return e;
 }
 
 int kvq_flush_residual(kvq_cache *c, int32_t layer, void *stream) {
   if (int e = check_cache(c, layer)) return e;
-  LayerState &st = c->layers[layer];
-  if (st.res == 0) return KVQ_OK;
-  if (c->cfg.k_per_channel && st.res % kBlock != 0)
-    return fail(KVQ_ESTATE, "per-channel K quantizes whole windows of 128 tokens; the residual holds %lld",
-                (long long)st.res);
-  Plan p;
-  p.after = st;
-  add_quant(p, Op::kQuantResidual, 0, st.res, chunk_tier(c->cfg, st.length, st.length), st.length - st.res,
-            c->cfg.demote_young != 0);
-  p.after.res = 0;
-  plan_demotions(c->cfg, p);
-  int e = run_plan(c, layer, p, nullptr, nullptr, 0, (hipStream_t)stream);
-  if (e == KVQ_OK || e == KVQ_EHIP) st = p.after;
-  return e;
+  const int B = c->cfg.batch;
+  for (int b = 0; b < B; ++b) {
+    const int64_t r = c->st(layer, b).res;
+    if (c->cfg.k_per_channel && r % kBlock != 0)
+      return fail(KVQ_ESTATE, "per-channel K quantizes whole windows of 128 tokens; sequence %d's residual holds %lld", b,
+                  (long long)r);
+  }
+  if (c->uniform(layer)) {
+    if (c->st(layer, 0).res == 0) return KVQ_OK;
+    Plan p = plan_flush(c, c->st(layer, 0));
+    int e = run_plan(c, layer, p, nullptr, nullptr, 0, (hipStream_t)stream);
+    if (e == KVQ_OK || e == KVQ_EHIP)
+      for (int b = 0; b < B; ++b) c->st(layer, b) = p.after;
+    return e;
+  }
+  std::vector<Plan> plans(B);
+  for (int b = 0; b < B; ++b) {
+    plans[b] = plan_flush(c, c->st(layer, b));
+    if (int e = check_capacity(c, plans[b])) return e;
+  }
+  for (int b = 0; b < B; ++b) {
+    if (c->st(layer, b).res == 0) continue;
+    int e = run_plan(c, layer, plans[b], nullptr, nullptr, 0, (hipStream_t)stream, b);
+    if (e == KVQ_OK || e == KVQ_EHIP) c->st(layer, b) = plans[b].after;
+    if (e != KVQ_OK) return e;
+  }
+  return KVQ_OK;
 }
 
 size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t num_q_heads) {
@@ -540,9 +767,10 @@ int kvq_decode_attn(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_he
                     int32_t out_fp32, void *workspace, size_t ws_bytes, void *stream) {
   if (int e = check_cache(c, layer)) return e;
   if (int e = check_decode(c, q, num_q_heads, softmax_scale, out, workspace, ws_bytes)) return e;
-  if (c->layers[layer].length == 0) return fail(KVQ_ESTATE, "layer %d is empty", layer);
+  const bool ragged = !c->uniform(layer);
+  if (!ragged && c->st(layer, 0).length == 0) return fail(KVQ_ESTATE, "layer %d is empty", layer);
   return run_decode(c, layer, q, num_q_heads, softmax_scale, out, out_fp32, workspace, nullptr, nullptr, nullptr, 0,
-                    stream);
+                    stream, ragged);
 }
 
 int kvq_append_decode_attn(kvq_cache *c, int32_t layer, const void *k, const void *v, int64_t n_tokens, const void *q,
@@ -551,7 +779,14 @@ int kvq_append_decode_attn(kvq_cache *c, int32_t layer, const void *k, const voi
   if (int e = check_cache(c, layer)) return e;
   if (int e = check_append(c, layer, k, v, n_tokens)) return e;
   if (int e = check_decode(c, q, num_q_heads, softmax_scale, out, workspace, ws_bytes)) return e;
-  LayerState &st = c->layers[layer];
+  if (!c->uniform(layer)) {
+    std::vector<Op> pend(c->cfg.batch, Op{Op::kResCopy, 0, 0, 0, 0});
+    if (n_tokens > 0)
+      if (int e = append_ragged(c, layer, k, v, n_tokens, (hipStream_t)stream, pend.data())) return e;
+    return run_decode(c, layer, q, num_q_heads, softmax_scale, out, out_fp32, workspace, pend.data(), k, v, n_tokens,
+                      stream, true);
+  }
+  LayerState st = c->st(layer, 0);
   if (st.length + n_tokens == 0) return fail(KVQ_ESTATE, "layer %d is empty", layer);
   Op pending{};
   bool has_pending = false;
@@ -564,24 +799,32 @@ int kvq_append_decode_attn(kvq_cache *c, int32_t layer, const void *k, const voi
       has_pending = true;
     }
     const int e = run_plan(c, layer, p, k, v, n_tokens, (hipStream_t)stream);
-    if (e == KVQ_OK || e == KVQ_EHIP) st = p.after;
+    if (e == KVQ_OK || e == KVQ_EHIP)
+      for (int b = 0; b < c->cfg.batch; ++b) c->st(layer, b) = p.after;
     if (e != KVQ_OK) return e;
   }
   return run_decode(c, layer, q, num_q_heads, softmax_scale, out, out_fp32, workspace, has_pending ? &pending : nullptr,
-                    k, v, n_tokens, stream);
+                    k, v, n_tokens, stream, false);
 }
 
-int kvq_tier_first_block(const kvq_cache *c, int32_t layer, int32_t region, int64_t *block) {
-  if (int e = check_cache(c, layer)) return e;
-  if (region < 0 || region > 2) return fail(KVQ_EINVAL, "region %d is not 0, 1 or 2", region);
-  if (block) *block = region == 1 ? c->layers[layer].young_head : 0;
+int kvq_seq_info(const kvq_cache *c, int32_t layer, int32_t seq, kvq_seq_info_t *info) {
+  if (int e = check_seq(c, layer, seq)) return e;
+  if (!info) return fail(KVQ_EINVAL, "info is NULL");
+  const LayerState &st = c->st(layer, seq);
+  info->length = st.length;
+  info->residual = st.res;
+  info->young_first_block = st.young_head;
+  info->young_tokens = st.young - st.young_head * kBlock;
+  info->old_tokens = st.old;
   return KVQ_OK;
 }
 
 int kvq_seq_len(const kvq_cache *c, int32_t layer, int64_t *total, int64_t *in_residual) {
   if (int e = check_cache(c, layer)) return e;
-  if (total) *total = c->layers[layer].length;
-  if (in_residual) *in_residual = c->layers[layer].res;
+  if (!c->uniform(layer))
+    return fail(KVQ_ESTATE, "layer %d: the sequences have different lengths (kvq_seq_info gives each)", layer);
+  if (total) *total = c->st(layer, 0).length;
+  if (in_residual) *in_residual = c->st(layer, 0).res;
   return KVQ_OK;
 }
 
@@ -589,12 +832,13 @@ int kvq_layout(const kvq_cache *c, int32_t layer, int32_t region, size_t *offset
   if (int e = check_cache(c, layer)) return e;
   const size_t bh = (size_t)c->cfg.batch * c->cfg.num_kv_heads;
   const size_t lb = (size_t)layer * c->geo.layer_bytes;
+  const LayerState &st = c->st(layer, 0);
   size_t off, nb;
   int64_t t;
   switch (region) {
-    case 0: off = lb + c->geo.off_res; nb = bh * c->geo.res_bh; t = c->layers[layer].res; break;
-    case 1: off = lb + c->geo.off_young; nb = bh * c->geo.young_bh; t = c->layers[layer].young - c->layers[layer].young_head * kBlock; break;
-    case 2: off = lb + c->geo.off_old; nb = bh * c->geo.old_bh; t = c->layers[layer].old; break;
+    case 0: off = lb + c->geo.off_res; nb = bh * c->geo.res_bh; t = st.res; break;
+    case 1: off = lb + c->geo.off_young; nb = bh * c->geo.young_bh; t = st.young - st.young_head * kBlock; break;
+    case 2: off = lb + c->geo.off_old; nb = bh * c->geo.old_bh; t = st.old; break;
     default: return fail(KVQ_EINVAL, "region %d is not 0, 1 or 2", region);
   }
   if (offset) *offset = off;

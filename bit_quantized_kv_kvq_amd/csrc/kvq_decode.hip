@@ -1300,6 +1300,9 @@ struct Item {
   int bh, part, seg;          // seg = -1: residual only
   int j;                      // index of the item among its segment's items
   bool has_res;
+  // of the item's sequence (the call's values, or its RagSeq in a ragged batch)
+  int items_total, res_ntok, pend_count, pend_slot0;
+  int64_t pend_src_tok0;
 };
 
 // Part p of every (b, h) comes in the p-th run of B*H workgroups, so that each (b, h) has
@@ -1322,6 +1325,42 @@ __device__ __forceinline__ Item decode_item(const DecodeArgs &a, int wg) {
     }
   }
   it.has_res = a.res_ntok > 0 && it.part == it.bh % a.items_total;
+  it.items_total = a.items_total;
+  it.res_ntok = a.res_ntok;
+  it.pend_count = a.pend_count;
+  it.pend_slot0 = a.pend_slot0;
+  it.pend_src_tok0 = a.pend_src_tok0;
+  return it;
+}
+
+// Ragged batch: the workgroup's (b, h, part) from its table entry, the rest from the
+// sequence's RagSeq.  The tables are read through the constant address space (the host writes
+// them before the launch; nothing in it writes them), so that, as for the call's own
+// arguments, their loads are scalar and can be repeated instead of held in registers.
+typedef const __attribute__((address_space(4))) RagSeq ConstRagSeq;
+typedef const __attribute__((address_space(4))) uint32_t ConstU32;
+
+__device__ __forceinline__ Item decode_item_ragged(const DecodeArgs &a, int wg) {
+  const uint32_t e = ((ConstU32 *)a.rag_wg)[wg];
+  const int b = (int)(e & 0xFFFFu), h = (int)((e >> 16) & 0x1FFu);
+  ConstRagSeq &r = ((ConstRagSeq *)a.rag)[b];
+  Item it;
+  it.bh = b * a.H + h;
+  it.part = (int)(e >> 25);
+  it.seg = -1;
+  it.j = 0;
+  for (int s = 0; s < a.nseg; ++s) {
+    if (it.part >= r.seg[s].part0 && it.part < r.seg[s].part0 + r.seg[s].items) {
+      it.seg = s;
+      it.j = it.part - r.seg[s].part0;
+    }
+  }
+  it.items_total = r.items_total;
+  it.res_ntok = r.res_ntok;
+  it.has_res = it.res_ntok > 0 && it.part == it.bh % it.items_total;
+  it.pend_count = r.pend_count;
+  it.pend_slot0 = r.pend_slot0;
+  it.pend_src_tok0 = r.pend_src_tok0;
   return it;
 }
 
@@ -1347,15 +1386,15 @@ __device__ __forceinline__ void residual_part(const DecodeArgs &a, const Item &i
                                               int c, bool valid_head, State &st) {
   const uint16_t *qrow = q_row<NSUB>(qgroup, c, valid_head);
   const uint8_t *res = a.res_base + (int64_t)it.bh * a.res_bh_stride;
-  const int nsteps = (a.res_ntok + 31) / 32;
+  const int nsteps = (it.res_ntok + 31) / 32;
   if constexpr (NSUB == 2) {
     QOp2 q;
     load_q2<kFmtFp16, kGroup>(qrow, valid_head, g, c, q);
-    for (int u = w; u < nsteps; u += kWaves) residual_step2(res, a.res_len, a.res_ntok, u, g, c, q, a.scale_log2, valid_head, st);
+    for (int u = w; u < nsteps; u += kWaves) residual_step2(res, a.res_len, it.res_ntok, u, g, c, q, a.scale_log2, valid_head, st);
   } else {
     QOp q;
     load_q<kFmtFp16, kGroup>(qrow, valid_head, g, q.qb, q.qs);
-    for (int u = w; u < nsteps; u += kWaves) residual_step(res, a.res_len, a.res_ntok, u, g, c, q, a.scale_log2, valid_head, st);
+    for (int u = w; u < nsteps; u += kWaves) residual_step(res, a.res_len, it.res_ntok, u, g, c, q, a.scale_log2, valid_head, st);
   }
 }
 
@@ -1569,17 +1608,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
   const bool valid_head = (NSUB == 2 ? (c & 7) : c) < a.G;
-  const Item it = decode_item(a, blockIdx.x);
+  const Item it = a.rag ? decode_item_ragged(a, blockIdx.x) : decode_item(a, blockIdx.x);
   __shared__ int s_chunk;
-  if (a.pend_count > 0 && it.has_res) {
+  if (it.pend_count > 0 && it.has_res) {
     // this call's new tokens go to the residual: copied here, before this workgroup (the only
     // reader of the residual in the launch) reads it
     const int b = it.bh / a.H, h = it.bh % a.H;
     uint16_t *rk = (uint16_t *)(a.res_base + (int64_t)it.bh * a.res_bh_stride);   // K [R][128]
     uint16_t *rv = rk + (int64_t)a.res_len * kHeadDim;                               // V [R/16][128][16]
-    const int64_t src0 = ((int64_t)(b * a.H + h) * a.pend_src_ntok + a.pend_src_tok0) * kHeadDim;
-    for (int e = threadIdx.x; e < a.pend_count * kHeadDim; e += kThreads) {
-      const int slot = a.pend_slot0 + e / kHeadDim, d = e % kHeadDim;
+    const int64_t src0 = ((int64_t)(b * a.H + h) * a.pend_src_ntok + it.pend_src_tok0) * kHeadDim;
+    for (int e = threadIdx.x; e < it.pend_count * kHeadDim; e += kThreads) {
+      const int slot = it.pend_slot0 + e / kHeadDim, d = e % kHeadDim;
       rk[slot * kHeadDim + d] = a.pend_k[src0 + e];
       rv[((slot / 16) * kHeadDim + d) * 16 + slot % 16] = a.pend_v[src0 + e];
     }
@@ -1608,7 +1647,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
   if (it.seg >= 0) {
-    const DecodeSeg &sg = a.seg[it.seg];
+    const DecodeSeg &sg = a.rag ? (const DecodeSeg &)((ConstRagSeq *)a.rag)[it.bh / a.H].seg[it.seg] : a.seg[it.seg];
 #define KVQ_SEG(F, GS) stream_segment<F, GS, NSUB>(a, sg, it, smem, &s_chunk, w, g, c, valid_head, st)
 #define KVQ_AFFINE_SEG(F)                  \
   case F:                                  \
@@ -1671,12 +1710,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
   if (threadIdx.x == 0) {
     uint64_t *cnt = a.counters + it.bh;
     const uint64_t old = __hip_atomic_fetch_add(cnt, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (int)counter_result(cnt, a.epoch, old) + 1 == a.items_total;
+    s_last = (int)counter_result(cnt, a.epoch, old) + 1 == it.items_total;
   }
   __syncthreads();
   if (!s_last) return;
 
-  const int P = a.items_total;
+  const int P = it.items_total;
   const float *parts = a.partials + (int64_t)it.bh * kMaxParts * G * kPartialStride;
   float *sm_m = (float *)smem;            // [P][G]
   float *sm_w = sm_m + P * G;             // [P][G] weights, after the max is known
@@ -1699,7 +1738,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
       sm_w[p * G + hc] = wt;
       L += wt * sm_l[p * G + hc];
     }
-    sm_inv[hc] = 1.0f / L;
+    sm_inv[hc] = L > 0.0f ? 1.0f / L : 0.0f;   // L = 0 only for an empty sequence of a ragged batch: zeros
   }
   __syncthreads();
   const int b = it.bh / a.H, h = it.bh % a.H;

@@ -121,6 +121,17 @@ constexpr int kMaxSegs = 2;        // old tier, young tier
 constexpr int kMaxParts = 128;     // partial results per (b, h) and call
 constexpr int kPartialStride = 132;  // floats per (part, head): m, l, -, -, o[128]
 
+// One sequence of a ragged batch (sequences at different lengths), as the decode kernel reads
+// it from the workspace: the call's tier segments with this sequence's slots and work split
+// (a tier the sequence does not have: ntok 0, items 0), its residual and its pending copy.
+struct RagSeq {
+  DecodeSeg seg[kMaxSegs];
+  int64_t pend_src_tok0;       // this sequence's tokens of the call's append that go to the residual
+  int32_t items_total;         // work items per (b, h) of this sequence (at least 1)
+  int32_t res_ntok;
+  int32_t pend_count, pend_slot0;
+};
+
 struct DecodeArgs {
   const uint16_t *q;       // [B][Hq][128] fp16
   void *out;               // [B][Hq][128] fp32 or fp16
@@ -144,6 +155,11 @@ struct DecodeArgs {
   const uint16_t *pend_k, *pend_v;   // caller input [B][H][pend_src_ntok][128]
   int64_t pend_src_ntok, pend_src_tok0;
   int pend_count, pend_slot0;
+  // Ragged batch (null: every sequence has the state above): per sequence a RagSeq overrides
+  // the segments' slots and split, the residual and the pending copy; rag_wg[workgroup] packs
+  // (b | h << 16 | part << 25) of its work item.
+  const RagSeq *rag;
+  const uint32_t *rag_wg;
 };
 
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t s);

@@ -117,21 +117,35 @@ int kvq_cache_destroy(kvq_cache *c);
 /* Set every layer's length to 0 (host-only; stored bytes are overwritten by later appends). */
 int kvq_cache_reset(kvq_cache *c);
 
-/* Append n_tokens new tokens to layer `layer`.
+/* Append n_tokens new tokens to every sequence of layer `layer`.
    k, v: fp16 [batch][num_kv_heads][n_tokens][128], contiguous, 16-byte aligned, read on the
    stream.  Tokens are processed in order: with R > 0 a token that arrives while the
    residual holds R tokens first flushes those R tokens into the quantized tier (one chunk),
    then goes to the residual; with R = 0 every token is quantized at once.  Appending n
    tokens stores exactly the bytes of n single-token appends when the old tier is off.
-   n_tokens = 0 is a no-op.  Errors: KVQ_EINVAL, KVQ_ECAPACITY, KVQ_EHIP. */
+   Each sequence of the batch keeps its own schedule (page "KV缓存量化技术：提升大模型长文本
+   生成效率" §2.2 describes it for one sequence): when the sequences are at different points
+   (a ragged batch, see kvq_append_seq), each follows its own, in launches of its own where
+   they differ.  n_tokens = 0 is a no-op.  Errors: KVQ_EINVAL, KVQ_ECAPACITY (checked for
+   every sequence before anything is enqueued), KVQ_EHIP. */
 int kvq_append(kvq_cache *c, int32_t layer, const void *k, const void *v, int64_t n_tokens, void *stream);
 
-/* Quantize the r tokens currently in the residual of `layer` (one chunk) and empty it.
-   No-op when r = 0.  Errors: KVQ_EINVAL, KVQ_EHIP. */
+/* Append n_tokens new tokens to sequence `seq` (0 <= seq < batch) of layer `layer` alone, as
+   kvq_append would for that sequence: k, v are fp16 [num_kv_heads][n_tokens][128].  The
+   sequences of a batch may so hold different numbers of tokens (a ragged batch: prompts of
+   different lengths, sequences that started at different steps); every other call then
+   serves each sequence at its own length.  Errors: KVQ_EINVAL (also seq out of range),
+   KVQ_ECAPACITY, KVQ_EHIP. */
+int kvq_append_seq(kvq_cache *c, int32_t layer, int32_t seq, const void *k, const void *v, int64_t n_tokens,
+                   void *stream);
+
+/* Quantize the r tokens currently in the residual of `layer` (one chunk per sequence) and
+   empty it.  No-op for a sequence with r = 0.  Errors: KVQ_EINVAL, KVQ_ESTATE (per-channel K
+   and a partial window), KVQ_EHIP. */
 int kvq_flush_residual(kvq_cache *c, int32_t layer, void *stream);
 
-/* Workspace bytes kvq_decode_attn needs for num_q_heads query heads at the current lengths
-   (the maximum over layers).  0 if the arguments are invalid. */
+/* Workspace bytes kvq_decode_attn needs for num_q_heads query heads (any lengths, ragged
+   batches included).  0 if the arguments are invalid. */
 size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t num_q_heads);
 
 /* Attention of one query token per (batch, query head) over every token cached in `layer`:
@@ -141,8 +155,11 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t num_q_heads);
    fp16; workspace: at least kvq_decode_workspace_bytes() bytes, 16-byte aligned, scratch
    owned by the caller (its contents on entry do not matter).  The cache is not modified.
    num_q_heads must be a multiple of num_kv_heads with a group of at most 16; softmax_scale
-   must be positive and finite.
-   Errors: KVQ_EINVAL, KVQ_ENOSPACE (workspace), KVQ_ESTATE (layer empty), KVQ_EHIP. */
+   must be positive and finite.  In a ragged batch each sequence attends over its own tokens
+   (a sequence with none gets zeros), and the launch's work is split over the sequences in
+   proportion to their cached bytes; the per-sequence tables are copied into the workspace
+   on the stream (stream-ordered, from host memory).
+   Errors: KVQ_EINVAL, KVQ_ENOSPACE (workspace), KVQ_ESTATE (every sequence empty), KVQ_EHIP. */
 int kvq_decode_attn(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_heads, float softmax_scale,
                     void *out, int32_t out_fp32, void *workspace, size_t ws_bytes, void *stream);
 
@@ -154,25 +171,39 @@ int kvq_decode_attn(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_he
    there before it reads the residual, so the step costs one launch instead of two.  All
    arguments of both calls are checked before anything is enqueued; errors as for the two
    calls (on KVQ_EHIP during the append part, the append state has advanced as kvq_append's
-   would).  n_tokens = 0 is a plain kvq_decode_attn. */
+   would).  n_tokens = 0 is a plain kvq_decode_attn.  In a ragged batch every sequence's
+   residual copy moves into the decode launch likewise (sequences that flush first get their
+   quantize launches before it). */
 int kvq_append_decode_attn(kvq_cache *c, int32_t layer, const void *k, const void *v, int64_t n_tokens,
                            const void *q, int32_t num_q_heads, float softmax_scale, void *out, int32_t out_fp32,
                            void *workspace, size_t ws_bytes, void *stream);
 
-/* Host counters of a layer: total cached tokens and tokens currently in the residual. */
+/* Host counters of a layer whose sequences are all in one state: total cached tokens and
+   tokens currently in the residual.  Errors: KVQ_EINVAL, KVQ_ESTATE (a ragged batch: use
+   kvq_seq_info). */
 int kvq_seq_len(const kvq_cache *c, int32_t layer, int64_t *total, int64_t *in_residual);
+
+/* One sequence's state in a layer (host counters). */
+typedef struct {
+  int64_t length;             /* tokens cached */
+  int64_t residual;           /* of which in the fp16 residual */
+  int64_t young_first_block;  /* first live block of its young arena: the blocks before it were
+                                 moved to the old tier (demote_young); 0 without demotion */
+  int64_t young_tokens;       /* live young slots, from that block on */
+  int64_t old_tokens;         /* old slots */
+} kvq_seq_info_t;
+
+/* State of sequence `seq` of `layer`.  Host-only.  Errors: KVQ_EINVAL (handle, layer, seq,
+   NULL info). */
+int kvq_seq_info(const kvq_cache *c, int32_t layer, int32_t seq, kvq_seq_info_t *info);
 
 /* Where a region of a layer lives: region 0 = fp16 residual, 1 = young tier, 2 = old tier.
    *offset: byte offset of the region in dev_buf; *bytes: bytes of the region (all batch
    entries and kv heads, [batch][kv_head][...]); *tokens: slots in use per (batch, kv_head)
-   (for the young tier: its live slots, from kvq_tier_first_block's block on).
+   of sequence 0 (every sequence's when all are in one state; kvq_seq_info gives each), for
+   the young tier its live slots from the sequence's first live block on.
    Any output pointer may be NULL. */
 int kvq_layout(const kvq_cache *c, int32_t layer, int32_t region, size_t *offset, size_t *bytes, int64_t *tokens);
-
-/* First live block of a region's arena: the young tier's blocks before it were moved to the
-   old tier (demote_young); 0 for the other regions and without demotion.  Host-only.
-   Errors: KVQ_EINVAL (handle, layer, region). */
-int kvq_tier_first_block(const kvq_cache *c, int32_t layer, int32_t region, int64_t *block);
 
 /* Plan-only mode (1) updates the host counters exactly as the real calls do but enqueues
    no device work; it lets the bookkeeping run on machines without a GPU.  0 restores

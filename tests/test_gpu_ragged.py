@@ -1,0 +1,152 @@
+"""GPU: ragged batches (sequences of one batch at different lengths).  Each sequence follows
+its own schedule, so its oracle is the one-sequence cache of its own tokens: after every step
+the stored bytes of each sequence (both tiers from its first live block, and its residual)
+equal that oracle's, and the decode of the whole batch in one launch matches each sequence's
+attention within the tolerance (zeros for an empty sequence).  The fused step on a ragged
+batch is bitwise equal to the separate calls on a twin cache (deterministic split).
+
+Keys are normal, values the adversarial patterns: the ragged bookkeeping is the subject here
+(the quantizers' adversarial keys are covered by the batch tests), and adversarial keys make
+logits of thousands whose near-ties the fp32 logits cannot resolve."""
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_kv_kvq_amd as kvq
+from gpu_helpers import to_dev, adversarial_tokens, assert_attention_close
+from oracle.cache import LayerCache
+from oracle.attention import decode_layer
+from oracle import layout as olayout
+
+pytestmark = pytest.mark.gpu
+
+SIGMA = 1 / np.sqrt(128)
+
+
+def keys(rng, B, H, n):
+    return rng.standard_normal((B, H, n, 128)).astype(np.float16)
+
+
+class Ragged:
+    """One-layer GPU cache of B sequences and one oracle cache per sequence."""
+
+    def __init__(self, B, H, max_tokens, fmt, R, old=None, old_after=0, demote=False):
+        self.cfg = kvq.make_config(1, B, H, max_tokens, fmt, R, old, old_after, demote=demote)
+        self.gpu = kvq.Cache(self.cfg)
+        self.ora = [LayerCache(fmt, R, old, old_after, demote) for _ in range(B)]
+        self.B, self.H, self.R = B, H, R
+
+    def append_seq(self, b, k, v):
+        self.gpu.append_seq(0, b, to_dev(k), to_dev(v))
+        self.ora[b].append(k[None], v[None])
+
+    def oracle_append_all(self, k, v):
+        for b in range(self.B):
+            self.ora[b].append(k[b:b + 1], v[b:b + 1])
+
+    def check_bytes(self):
+        torch.cuda.synchronize()
+        for b in range(self.B):
+            o = self.ora[b]
+            info = self.gpu.seq_info(0, b)
+            assert info["length"] == o.sched.length and info["residual"] == len(o.sched.residual)
+            assert info["young_first_block"] * 128 == o.sched.young_head
+            for region, tier, ntok in ((1, "young", info["young_tokens"]), (2, "old", info["old_tokens"])):
+                assert ntok == len(o.tier_tokens(tier)), (b, tier)
+                if ntok == 0:
+                    continue
+                fmt = o.tier_format(tier)
+                bb = olayout.block_bytes(fmt)
+                fb = info["young_first_block"] if region == 1 else 0
+                dev = self.gpu.region_tensor(0, region)
+                for h in range(self.H):
+                    got = dev[b, h, fb * bb:(fb - (-ntok // 128)) * bb].cpu().numpy()
+                    want = o.arena(0, h, tier).ravel()
+                    assert np.array_equal(got, want), f"sequence {b}, head {h}: {tier} bytes differ"
+            if self.R and o.sched.residual:
+                dev = self.gpu.region_tensor(0, 0)
+                for h in range(self.H):
+                    data, mask = o.residual(0, h)
+                    assert np.array_equal(dev[b, h].cpu().numpy()[mask], data[mask]), f"sequence {b} residual"
+
+    def want(self, q16):
+        out = np.zeros(q16.shape, dtype=np.float64)
+        for b in range(self.B):
+            if self.ora[b].sched.length:
+                out[b] = decode_layer(self.ora[b], q16[b:b + 1], SIGMA)[0]
+        return out
+
+
+CASES = [("int4", 128, None, 0, False, [0, 300, 1000]), ("nvfp4", 0, None, 0, False, [5, 129, 700]),
+         ("int4", 128, "int2", 300, True, [100, 900, 2000]), ("fp8", 16, None, 0, False, [40, 0, 513]),
+         ("int4kc", 128, None, 0, False, [256, 1, 640]), ("mxfp4", 32, "int4", 500, False, [1200, 64, 3])]
+
+
+@pytest.mark.parametrize("fmt,R,old,old_after,demote,lens", CASES, ids=lambda x: str(x))
+def test_ragged_bytes_and_decode(fmt, R, old, old_after, demote, lens):
+    rng = np.random.default_rng(sum(lens))
+    B, H, G = len(lens), 2, 4
+    r = Ragged(B, H, 4000, fmt, R, old, old_after, demote)
+    ws = torch.empty(r.gpu.workspace_bytes(H * G), dtype=torch.uint8, device="cuda")
+    for b, n in enumerate(lens):
+        if n:
+            r.append_seq(b, keys(rng, 1, H, n)[0], adversarial_tokens(rng, 1, H, n)[0])
+    r.check_bytes()
+    steps = [1, 1, 130, "flush", 3, 255, 1] if not fmt.endswith("kc") else [1, 1, 130, 3, 255, 1]
+    for n in [0] + steps:
+        q = (rng.standard_normal((B, H * G, 128)) / np.sqrt(128)).astype(np.float16)
+        out = torch.empty((B, H * G, 128), dtype=torch.float32, device="cuda")
+        if n == "flush":
+            r.gpu.flush(0)
+            for o in r.ora:
+                o.flush()
+            r.gpu.decode(0, to_dev(q), SIGMA, out, ws)
+        else:
+            k = keys(rng, B, H, n) if n else np.zeros((B, H, 0, 128), np.float16)
+            v = adversarial_tokens(rng, B, H, n) if n else np.zeros((B, H, 0, 128), np.float16)
+            if n:
+                r.oracle_append_all(k, v)
+            r.gpu.append_decode(0, to_dev(k), to_dev(v), to_dev(q), SIGMA, out, ws)
+        torch.cuda.synchronize()
+        r.check_bytes()
+        got = out.cpu().numpy().astype(np.float64)
+        want = r.want(q)
+        for b in range(B):
+            if r.ora[b].sched.length == 0:
+                assert np.all(got[b] == 0), f"empty sequence {b} must give zeros"
+            else:
+                assert_attention_close(got[b], want[b])
+    if demote:
+        assert any(o.sched.young_head > 0 for o in r.ora)
+
+
+def test_ragged_fused_step_matches_separate_calls():
+    """Deterministic split: the fused step on a ragged batch (some sequences flushing, the
+    rest copying into the residual inside the decode launch) equals kvq_append followed by
+    kvq_decode_attn on a twin cache, bit for bit; both caches' bytes equal the oracle's."""
+    rng = np.random.default_rng(77)
+    B, H, G = 4, 2, 4
+    pair = [Ragged(B, H, 3000, "int4", 128, "int2", 400) for _ in range(2)]
+    for r in pair:
+        r.gpu.set_deterministic(True)
+    for b, n in enumerate([127, 0, 500, 1000]):
+        if n:
+            k, v = keys(rng, 1, H, n)[0], adversarial_tokens(rng, 1, H, n)[0]
+            for r in pair:
+                r.append_seq(b, k, v)
+    ws = torch.empty(pair[0].gpu.workspace_bytes(H * G), dtype=torch.uint8, device="cuda")
+    for n in [1, 1, 3, 130, 1, 0, 129]:
+        k, v = keys(rng, B, H, n), adversarial_tokens(rng, B, H, n)
+        kd, vd = to_dev(k), to_dev(v)
+        q = to_dev((rng.standard_normal((B, H * G, 128)) / np.sqrt(128)).astype(np.float16))
+        outs = [torch.empty((B, H * G, 128), dtype=torch.float32, device="cuda") for _ in range(2)]
+        pair[0].gpu.append_decode(0, kd, vd, q, SIGMA, outs[0], ws)
+        if n:
+            pair[1].gpu.append(0, kd, vd)
+        pair[1].gpu.decode(0, q, SIGMA, outs[1], ws)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], outs[1]), f"step of {n}: fused and separate outputs differ"
+        for r in pair:
+            if n:
+                r.oracle_append_all(k, v)
+            r.check_bytes()

@@ -120,6 +120,63 @@ def test_demotion_config_rejected(bad):
     assert "demote_young" in kvq.lib().kvq_last_error().decode()
 
 
+@pytest.mark.parametrize("fmt,R,old_after,demote", [("int4", 128, 0, False), ("nvfp4", 0, 70, False),
+                                                   ("int4", 128, 300, True), ("int8", 16, 129, True)])
+def test_ragged_schedules_match_oracle(fmt, R, old_after, demote):
+    """Sequences of one batch appended separately keep one schedule each: every sequence's
+    counters equal those of its own oracle schedule, through per-sequence appends, batch-wide
+    appends and flushes."""
+    B = 3
+    cfg = kvq.make_config(1, B, 2, 100000, fmt, R, "int2" if old_after else None, old_after, demote=demote)
+    c = kvq.Cache(cfg, plan_only=True)
+    s = [Schedule(R, old_after, demote) for _ in range(B)]
+    rng = np.random.default_rng(B + R + old_after)
+
+    def check():
+        for b in range(B):
+            i = c.seq_info(0, b)
+            assert (i["length"], i["residual"]) == (s[b].length, len(s[b].residual))
+            assert i["young_first_block"] * 128 == s[b].young_head
+            assert (i["young_tokens"], i["old_tokens"]) == (len(s[b].live_young()), len(s[b].old))
+
+    for b, n in enumerate([0, 300, 1000]):
+        if n:
+            c.append_seq_plan(0, b, n); s[b].append(n)
+    check()
+    with pytest.raises(kvq.KvqError) as e:
+        c.seq_len(0)
+    assert e.value.code == kvq.KVQ_ESTATE
+    ops = [1, 1, 127, "flush", 3, 1000] + [int(x) if x > 0 else "flush" for x in rng.integers(-2, 200, 30)]
+    for i, op in enumerate(ops):
+        if op == "flush":
+            c.flush(0)
+            for x in s:
+                x.flush()
+        elif i % 3 == 0:
+            b = i % B
+            c.append_seq_plan(0, b, op); s[b].append(op)
+        else:
+            c.append_plan(0, op)
+            for x in s:
+                x.append(op)
+        check()
+
+
+def test_ragged_capacity_checked_for_every_sequence():
+    cfg = kvq.make_config(1, 2, 1, 1000, "int4", 128)
+    c = kvq.Cache(cfg, plan_only=True)
+    c.append_seq_plan(0, 1, 900)
+    with pytest.raises(kvq.KvqError) as e:
+        c.append_plan(0, 101)                      # sequence 1 would exceed max_tokens
+    assert e.value.code == kvq.KVQ_ECAPACITY
+    assert c.seq_info(0, 0)["length"] == 0 and c.seq_info(0, 1)["length"] == 900
+    c.append_plan(0, 100)
+    assert c.seq_info(0, 0)["length"] == 100 and c.seq_info(0, 1)["length"] == 1000
+    for bad in (-1, 2):
+        with pytest.raises(kvq.KvqError):
+            c.append_seq_plan(0, bad, 1)
+
+
 def test_workload_tiers():
     cfg = kvq.make_config(1, 1, 8, 262144 + 16, "int4", 128, "int2", 65536)
     c = kvq.Cache(cfg, plan_only=True)
