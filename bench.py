@@ -38,8 +38,10 @@ WORKLOADS = {
     "c4-int4": (4, "int4"), "c4-int2": (4, "int2"), "c5": (5, None),
     "c4-int4g32": (4, "int4g32"), "c4-int4g128": (4, "int4g128"), "c4-int4kc": (4, "int4kc"),
     "c3-mxfp4": (3, "mxfp4"), "c4-mxfp4": (4, "mxfp4"), "c3-fp8": (3, "fp8"), "c4-fp8": (4, "fp8"), "c3-fp16": (3, "fp16"), "c4-fp16": (4, "fp16"),
-    "c5-demote": (5, None),
+    "c5-demote": (5, None), "c4-ragged": (4, "int4"),
 }
+# ragged workloads: sequence b of the batch holds T (b + 1) / batch of the workload's T tokens
+RAGGED = {"c4-ragged"}
 # workloads whose young blocks move to the old tier as they age (demote_young), and the
 # timed steps they default to (a block of one (batch, kv_head) ages every 128 one-token steps)
 DEMOTE_STEPS = {"c5-demote": 320}
@@ -56,10 +58,17 @@ def bytes_per_token(fmt: str) -> float:
     return {"nvfp4": 18432 / 128, "mxfp4": 17408 / 128, "fp8": 32768 / 128, "fp16": 512.0}[fmt]
 
 
-def decode_bytes(cache, layer: int, fmt: str, old_fmt: str) -> float:
+def decode_bytes(cache, layer: int, fmt: str, old_fmt: str, ragged: bool = False) -> float:
     """Algorithmic cache bytes one decode call reads: every cached token once."""
     import bit_quantized_kv_kvq_amd as kvq
     B, H = cache.cfg.batch, cache.cfg.num_kv_heads
+    if ragged:
+        tot = 0.0
+        for b in range(B):
+            i = cache.seq_info(layer, b)
+            tot += H * (i["old_tokens"] * bytes_per_token(old_fmt) + i["young_tokens"] * bytes_per_token(fmt)
+                        + i["residual"] * 512.0)
+        return tot
     n_res = cache.layout(layer, kvq.REGION_RESIDUAL)[2]
     n_young = cache.layout(layer, kvq.REGION_YOUNG)[2]
     n_old = cache.layout(layer, kvq.REGION_OLD)[2]
@@ -244,6 +253,7 @@ def main():
     import kvq_synth as syn
 
     demote = args.workload in DEMOTE_STEPS
+    ragged = args.workload in RAGGED
     if args.steps is None:
         args.steps = DEMOTE_STEPS.get(args.workload, 64)
     cid, fmt_over = WORKLOADS[args.workload]
@@ -266,8 +276,14 @@ def main():
     samples_bh = [(b, h) for b in range(B) for h in range(H)][:args.cpu_pairs]
     host_hist = {bh: ([], []) for bh in samples_bh}
 
-    # ---- untimed state: bulk prefill of every layer (one append of T tokens); HIP events
-    # around each append give the bulk quantize rate (fp16 read + packed bytes written)
+    # ragged: sequence b keeps the first lens[b] of its T drawn tokens
+    lens = [T * (b + 1) // B for b in range(B)] if ragged else [T] * B
+    if ragged:
+        assert W.old_after == 0 and R > 0, "the ragged step tracker models one tier with a residual"
+
+    # ---- untimed state: bulk prefill of every layer (one append of T tokens, or one per
+    # sequence when ragged); HIP events around each layer's appends give the bulk quantize rate
+    # (fp16 read + packed bytes written)
     t_prefill = time.perf_counter()
     pre_events = []
     for l in range(L):
@@ -275,11 +291,15 @@ def main():
         v = syn.draw_v_dev(cid, l, B, H, T)
         if l == 0:
             for (b, h) in samples_bh:
-                host_hist[(b, h)][0].append(k[b, h].cpu().numpy())
-                host_hist[(b, h)][1].append(v[b, h].cpu().numpy())
+                host_hist[(b, h)][0].append(k[b, h, :lens[b]].cpu().numpy())
+                host_hist[(b, h)][1].append(v[b, h, :lens[b]].cpu().numpy())
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        cache.append(l, k, v)
+        if ragged:
+            for b in range(B):
+                cache.append_seq(l, b, k[b, :, :lens[b]].contiguous(), v[b, :, :lens[b]].contiguous())
+        else:
+            cache.append(l, k, v)
         e1.record(stream)
         pre_events.append((e0, e1))
         del k, v
@@ -289,7 +309,14 @@ def main():
     torch.cuda.synchronize()
     t_prefill = time.perf_counter() - t_prefill
     pre_ms = float(sum(a.elapsed_time(b) for a, b in pre_events))
-    pre_bytes = float(L * B * H * T * 2 * 128 * 2) + sum(decode_bytes(cache, l, fmt, old_fmt) for l in range(L))
+    pre_bytes = float(L * H * sum(lens) * 2 * 128 * 2) + sum(decode_bytes(cache, l, fmt, old_fmt, ragged)
+                                                                for l in range(L))
+    # ragged: per (layer, sequence) quantized tokens and residual fill, tracked here (a ctypes
+    # query per sequence and layer inside the timed loop would cost host time of its own)
+    if ragged:
+        track = [[[cache.seq_info(l, b)["young_tokens"], cache.seq_info(l, b)["residual"]] for b in range(B)]
+                 for l in range(L)]
+        bpt = bytes_per_token(fmt)
 
     # ---- step inputs, resident in HBM before the timed region
     knew = [[syn.draw_k_dev(cid, l, B, H, per_step, W.kdist, syn.STREAM_K_APPEND, s) for l in range(L)]
@@ -335,7 +362,16 @@ def main():
             # a step whose tokens go straight to the residual is one call and one launch (the
             # copy runs inside the decode launch); a step that quantizes (a full residual, or
             # R = 0) appends first, so that the timed bracket always holds one decode launch
-            quantizes = R == 0 or cache.seq_len(l)[1] + per_step > R or demotes(l)
+            if ragged:
+                quantizes = any(t[1] + per_step > R for t in track[l])
+                for t in track[l]:
+                    if t[1] + per_step > R:
+                        t[0] += t[1] + per_step - ((t[1] + per_step - 1) % R + 1)
+                        t[1] = (t[1] + per_step - 1) % R + 1
+                    else:
+                        t[1] += per_step
+            else:
+                quantizes = R == 0 or cache.seq_len(l)[1] + per_step > R or demotes(l)
             if args.separate_append or quantizes:
                 dem = nbytes is not None and demotes(l) and len(dem_used) < len(dem_events)
                 if dem:
@@ -355,7 +391,8 @@ def main():
             if pair is not None:
                 pair[1].record(stream)
             if nbytes is not None:
-                nbytes.append(decode_bytes(cache, l, fmt, old_fmt))
+                nbytes.append(H * sum(t[0] * bpt + t[1] * 512.0 for t in track[l]) if ragged
+                              else decode_bytes(cache, l, fmt, old_fmt))
                 if pair is not None:
                     timed_bytes.append(nbytes[-1])
 
@@ -374,6 +411,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gc.enable()
+    if ragged:   # the tracker agrees with the library's counters
+        for l in range(L):
+            assert sum(H * (t[0] * bpt + t[1] * 512.0) for t in track[l]) == decode_bytes(cache, l, fmt, old_fmt, True)
     log(f"timed {args.steps} steps in {wall:.3f} s")
 
     dec_ms = np.array([a.elapsed_time(b) for a, b in events])
@@ -407,9 +447,10 @@ def main():
         "dtype": f"{fmt}-codes/fp16-operands/fp32-accum",
         "data": "synthetic (seeded, drawn on the GPU)",
         "config": {"workload": (W.name if fmt_over is None else W.name.replace(W.fmt, fmt))
-                   + (", young blocks demoted as they age" if demote else ""),
+                   + (", young blocks demoted as they age" if demote else "")
+                   + (f", ragged: sequence b holds {T}(b+1)/{B} tokens" if ragged else ""),
                    "layers": L, "batch": B, "q_heads": Hq, "kv_heads": H, "head_dim": 128,
-                   "cached_tokens": T, "format": fmt, "old_format": W.old_fmt, "residual": R,
+                   "cached_tokens": lens if ragged else T, "format": fmt, "old_format": W.old_fmt, "residual": R,
                    "append_per_step": per_step, "parallelism": "none (1 GPU)"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_steps_per_s": round(args.steps / wall, 2),

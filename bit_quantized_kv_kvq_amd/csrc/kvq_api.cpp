@@ -11,6 +11,7 @@
 #include "kvq_internal.h"
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -485,7 +486,21 @@ int plan_decode_ragged(kvq_cache *c, int layer, DecodeArgs &a, uint8_t *ws, cons
     s.cursors = cursors + (size_t)a.nseg * nbh;
     seg_of[slot] = a.nseg++;
   }
-  const double slots = 2.0 * num_cus(c);
+  // items per (b, h) of sequence b: ceil(bytes_b / budget), with the smallest per-item budget
+  // whose items still fit the GPU once (so that the most loaded item carries as little as the
+  // slots allow; rounding each share to the nearest count would leave some items ~10 % heavier)
+  const int64_t slots = 2LL * num_cus(c);
+  auto items_for = [&](double budget) {
+    int64_t n = 0;
+    for (int b = 0; b < B; ++b) n += H * std::max<int64_t>(1, (int64_t)std::ceil(bytes[b] / budget));
+    return n;
+  };
+  double lo = total / (double)slots * H, hi = std::max(total, 1.0);   // items_for(hi) = B H
+  if (items_for(lo) <= slots) hi = lo;
+  for (int it = 0; it < 60 && hi > lo * (1 + 1e-9); ++it) {
+    const double mid = 0.5 * (lo + hi);
+    (items_for(mid) <= slots ? hi : lo) = mid;
+  }
   c->rag_host.assign(rag_seq_bytes(c) + rag_wg_bytes(c), 0);
   RagSeq *rs = (RagSeq *)c->rag_host.data();
   int maxp = 1;
@@ -495,7 +510,7 @@ int plan_decode_ragged(kvq_cache *c, int layer, DecodeArgs &a, uint8_t *ws, cons
       r.seg[u] = a.seg[u];
       r.seg[u].chunk = 1;
     }
-    const int64_t target = std::max<int64_t>(1, (int64_t)(slots * bytes[b] / (total * H) + 0.5));
+    const int64_t target = std::max<int64_t>(1, (int64_t)std::ceil(bytes[b] / hi));
     DecodeSeg out[kMaxSegs];
     const int parts = split_tiers(c, &tb[(size_t)b * kMaxSegs], nts[b], target, out);
     for (int i = 0; i < nts[b]; ++i) {
