@@ -47,6 +47,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kNegInf = -INFINITY;
+// Formats whose P operand is p itself (NVFP4, MXFP4, FP8, FP16) keep their reference max until
+// a logit exceeds it by 2^8 in p: the state is rescaled about once per work item instead of at
+// most blocks of a short item, and P <= 256 stays exact in fp16 range (products with V codes
+// at most 65504 * 256 in fp32).  Affine formats fold S into P' = p S, so their slack is 0.
+constexpr float kSlackLog2 = 8.0f;
 
 __device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 __device__ __forceinline__ uint32_t as_u(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
@@ -158,18 +163,40 @@ __device__ __forceinline__ half8_t unpack_fp8(uint32_t w0, uint32_t w1) {
 }
 
 // ---------------------------------------------------------------- cross-quarter reductions
-// Reduce over lanes {c, c+16, c+32, c+48} (the four lane quarters holding one head).
+// Reduce over lanes {c, c+16, c+32, c+48} (the four lane quarters holding one head).  The
+// partner values come from the lane-swap instructions (v_permlane16_swap / v_permlane32_swap:
+// with both operands x, the two results hold x of rows (0, 1) or (2, 3), resp. of halves
+// (lo, hi), on every lane), so no LDS round trip; both results enter in the same order on every
+// lane, so all lanes of a head get the same bits.
+__device__ __forceinline__ void xor16_pair(float x, float &a, float &b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void xor32_pair(float x, float &a, float &b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
 __device__ __forceinline__ float quad_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+  float a, b;
+  xor16_pair(x, a, b);
+  xor32_pair(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
 }
 __device__ __forceinline__ float quad_sum(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+  float a, b;
+  xor16_pair(x, a, b);
+  xor32_pair(a + b, a, b);
+  return a + b;
+}
+// Value of lane c ^ 8 within the lane's row of 16 (DPP row rotation by 8).
+__device__ __forceinline__ float row_xor8(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
 }
 // Over the eight lanes {c, c^8} x quarters that hold one head in the paired-subtile layout.
-__device__ __forceinline__ float head_max2(float x) { return quad_max(fmaxf(x, __shfl_xor(x, 8))); }
-__device__ __forceinline__ float head_sum2(float x) { return quad_sum(x + __shfl_xor(x, 8)); }
+__device__ __forceinline__ float head_max2(float x) { return quad_max(fmaxf(x, row_xor8(x))); }
+__device__ __forceinline__ float head_sum2(float x) { return quad_sum(x + row_xor8(x)); }
 
 // ---------------------------------------------------------------- Q operand per format
 // Dim fed by B element e of k-step j in lane quarter g, and whether the A element it meets
@@ -309,7 +336,8 @@ __device__ __forceinline__ void barrier() {
 
 // ---------------------------------------------------------------- running softmax state
 struct State {
-  float m = kNegInf;   // running max of the unscaled logits of head c, same on the 4 lane quarters
+  float m = kNegInf;   // reference max of the unscaled logits of head c, same on the 4 lane quarters
+  float slack = 0.0f;  // logits up to m + slack keep the reference (p <= 2^kSlackLog2 then)
   float l = 0.0f;      // this lane's share of sum p
   float z[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};   // affine V: this lane's share of
                        // sum P' Z of group G (z[2G]; INT4's x16 positions in z[2G + 1])
@@ -321,11 +349,13 @@ struct State {
 // by 16 (mask bit e) get p / 16.
 __device__ __forceinline__ void softmax_step(State &st, const float (&s)[8], float (&p)[8], bool valid_head,
                                              unsigned scaled_mask, float sl2) {
-  // Fast path: no logit of a valid head exceeds the running max, so the max and every
-  // accumulator stay as they are and no cross-lane reduction is needed.  Otherwise the new
-  // max of each head is reduced over its four lane quarters and the state is rescaled.
+  // Fast path: no logit of a valid head exceeds the reference max by more than the slack, so
+  // the reference and every accumulator stay as they are and no cross-lane reduction is
+  // needed.  Otherwise the new max of each head is reduced over its four lane quarters and the
+  // state is rescaled to it.  (The reference only has to be common to l and o; with a slack,
+  // p may exceed 1 by at most 2^kSlackLog2.)
   const float ml = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-  if (__builtin_amdgcn_ballot_w64(valid_head && ml > st.m) != 0) {
+  if (__builtin_amdgcn_ballot_w64(valid_head && ml > st.m + st.slack) != 0) {
     const float mt = quad_max(ml);
     const float m_new = fmaxf(st.m, mt);
     const float alpha = (m_new == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f((st.m - m_new) * sl2);
@@ -843,7 +873,7 @@ __device__ __forceinline__ void load_q2(const uint16_t *qrow, bool valid, int g,
 __device__ __forceinline__ void softmax_step2(State &st, const float (&s)[4], float (&p)[4], bool valid_head,
                                               unsigned scaled_mask, float sl2) {
   const float ml = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-  if (__builtin_amdgcn_ballot_w64(valid_head && ml > st.m) != 0) {
+  if (__builtin_amdgcn_ballot_w64(valid_head && ml > st.m + st.slack) != 0) {
     const float m_new = fmaxf(st.m, head_max2(ml));
     const float alpha = (m_new == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f((st.m - m_new) * sl2);
     st.l *= alpha;
@@ -1478,6 +1508,10 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
   for (int t = 0; t < nbuf - 1 && !iss_done; ++t) issue_next();
 
   // while the first blocks load: the residual (natural units), the operands
+  constexpr bool kAff = FMT == kFmtInt2 || FMT == kFmtInt4 || FMT == kFmtInt8;
+  // (capped: logits of fp16 operands stay below 2^40 in magnitude, so the cap never binds
+  // where it would let p exceed the bound, and m + slack stays finite)
+  if constexpr (!kAff) st.slack = fminf(kSlackLog2 / a.scale_log2, 1.0e30f);
   barrier();
   if (it.has_res) residual_part<NSUB>(a, it, qlds, w, g, c, valid_head, st);
   asm volatile("" ::: "memory");   // the operands below are not read before the residual is done
@@ -1487,7 +1521,6 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
   if constexpr (NSUB == 2) load_q2<FMT, GS>(qrow, valid_head, g, c, q2);
   else load_q<FMT, GS>(qrow, valid_head, g, q.qb, q.qs);
   // affine logits come out in units of 2^-24 (subnormal code operands)
-  constexpr bool kAff = FMT == kFmtInt2 || FMT == kFmtInt4 || FMT == kFmtInt8;
   const float sl2 = kAff ? a.scale_log2 * kInvSub : a.scale_log2;
   if constexpr (kAff) {
     if (st.m != kNegInf) st.m *= kSub;
