@@ -25,7 +25,8 @@
 //  PV    O^T += V^T P: A = V codes (16 dims x 32 slots), B = P (32 slots x 16 heads); lane
 //        (c, g) feeds dim c of the tile and the 8 slots whose logits it holds, and accumulates
 //        O^T[dims 4g..4g+3][head c].
-// Affine: the MFMA takes the raw codes as fp16 subnormals (c * 2^-24, some scaled by 16).  K:
+// Affine: the MFMA takes the raw codes as fp16 subnormals (c * 2^-24, some scaled by 16 for
+// INT4, by 4 for INT2).  K:
 // logit = S0 (dot0 - Z0 qsum0) + S1 (dot1 - Z1 qsum1) per 64-dim group, in units of 2^-24.  V:
 // the scale S of each (slot, group) is folded into P and the zero point enters as
 // o = 2^24 o - sum_t P'_t Z_t at the end of the work item.
@@ -97,11 +98,18 @@ __device__ __forceinline__ half8_t unpack_int4(uint32_t x) {
   const uint32_t y = x >> 8;
   return h8(x & 0x000F000Fu, x & 0x00F000F0u, y & 0x000F000Fu, y & 0x00F000F0u);
 }
-// INT2 word -> lo = crumbs [0,8,1,9,2,10,3,11], hi = [4,12,5,13,6,14,7,15]
+// INT2 word -> lo = crumbs [c0, c8, 4c1, 4c9, c2, c10, 4c3, 4c11] * 2^-24, hi = the same for
+// crumbs 4..7 / 12..15: the odd crumb of each nibble is masked in place (times 4), as INT4's
+// high nibble is taken times 16, so the scaled elements sit where INT4's do (3 shifts and 8
+// ands per word instead of 7 and 8)
 __device__ __forceinline__ void unpack_int2(uint32_t x, half8_t &lo, half8_t &hi) {
-  lo = h8(x & 0x00030003u, (x >> 2) & 0x00030003u, (x >> 4) & 0x00030003u, (x >> 6) & 0x00030003u);
-  hi = h8((x >> 8) & 0x00030003u, (x >> 10) & 0x00030003u, (x >> 12) & 0x00030003u, (x >> 14) & 0x00030003u);
+  const uint32_t x4 = x >> 4, x8 = x >> 8, x12 = x >> 12;
+  lo = h8(x & 0x00030003u, x & 0x000C000Cu, x4 & 0x00030003u, x4 & 0x000C000Cu);
+  hi = h8(x8 & 0x00030003u, x8 & 0x000C000Cu, x12 & 0x00030003u, x12 & 0x000C000Cu);
 }
+// log2 of the factor that the scaled A elements carry (INT4 16, INT2 4; none for the others)
+template <int FMT>
+constexpr int kSh = FMT == kFmtInt4 ? 4 : FMT == kFmtInt2 ? 2 : 0;
 // INT8 word pair -> [w0.b0, w0.b2, w0.b1, w0.b3, w1.b0, w1.b2, w1.b1, w1.b3]
 __device__ __forceinline__ half8_t unpack_int8(uint32_t w0, uint32_t w1) {
   return h8(w0 & 0x00FF00FFu, (w0 >> 8) & 0x00FF00FFu, w1 & 0x00FF00FFu, (w1 >> 8) & 0x00FF00FFu);
@@ -200,11 +208,11 @@ __device__ __forceinline__ float head_sum2(float x) { return quad_sum(x + row_xo
 
 // ---------------------------------------------------------------- Q operand per format
 // Dim fed by B element e of k-step j in lane quarter g, and whether the A element it meets
-// carries a factor 16 (then B holds q / 16).
+// carries a factor 2^kSh (then B holds q / 2^kSh).
 template <int FMT, int GS>
 __device__ __forceinline__ int q_dim(int g, int j, int e, bool &scaled) {
   const int G = j >> 1, h = j & 1;
-  scaled = FMT == kFmtInt4 && ((e >> 1) & 1) != 0;
+  scaled = kSh<FMT> != 0 && ((e >> 1) & 1) != 0;
   if constexpr (is_affine(FMT) && GS == 32) {
     return 32 * j + 8 * g + e;   // groups of 32: k-step j feeds dims 32j + 8g .. +7 (group j)
   } else if constexpr (FMT == kFmtInt4) {
@@ -267,9 +275,9 @@ __device__ __forceinline__ void load_q(const uint16_t *qrow, bool valid, int g, 
       const int d = q_dim<FMT, GS>(g, j, e, scaled);
       const int li = kLay32 ? 8 * (d >> 5) + (d & 7) : kLay64 ? 16 * (d >> 6) + (d & 15) : d - 32 * g;
       _Float16 v = loc[li];
-      if (scaled) v = v * (_Float16)0.0625f;
+      if (scaled) v = v * (_Float16)(1.0f / (1 << kSh<FMT>));
       qb[j][e] = v;
-      const float eff = scaled ? 16.0f * (float)v : (float)v;    // the q the MFMA effectively uses
+      const float eff = scaled ? (float)(1 << kSh<FMT>) * (float)v : (float)v;    // the q the MFMA effectively uses
       qs[k_group<GS>(j)] += eff;
     }
   }
@@ -340,13 +348,14 @@ struct State {
   float slack = 0.0f;  // logits up to m + slack keep the reference (p <= 2^kSlackLog2 then)
   float l = 0.0f;      // this lane's share of sum p
   float z[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};   // affine V: this lane's share of
-                       // sum P' Z of group G (z[2G]; INT4's x16 positions in z[2G + 1])
+                       // sum P' Z of group G (z[2G]; the scaled positions of INT4 / INT2 in z[2G + 1])
   float4_t o[8];       // O^T[dims 16k + 4g + i][head c]
 };
 
 // Update the running max with 8 unscaled logits (slots (tt, i) = (e >> 2, e & 3)) and return
 // p = exp2(sl2 (s - m)), sl2 = softmax_scale * log2(e) > 0; positions whose A element is scaled
-// by 16 (mask bit e) get p / 16.
+// by 2^SH (mask bit e) get p / 2^SH.
+template <int SH = 0>
 __device__ __forceinline__ void softmax_step(State &st, const float (&s)[8], float (&p)[8], bool valid_head,
                                              unsigned scaled_mask, float sl2) {
   // Fast path: no logit of a valid head exceeds the reference max by more than the slack, so
@@ -367,13 +376,13 @@ __device__ __forceinline__ void softmax_step(State &st, const float (&s)[8], flo
     st.m = m_new;
   }
   const float nm = st.m == kNegInf ? 0.0f : -st.m * sl2;
-  const float nm4 = nm - 4.0f;
+  const float nm4 = nm - (float)SH;
   float ls = 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const bool sc = (scaled_mask >> e) & 1;
     p[e] = __builtin_amdgcn_exp2f(fmaf(s[e], sl2, sc ? nm4 : nm));   // v_exp_f32; results below 2^-126 flush to 0
-    ls = sc ? fmaf(16.0f, p[e], ls) : ls + p[e];
+    ls = sc ? fmaf((float)(1 << SH), p[e], ls) : ls + p[e];
   }
   st.l += ls;
 }
@@ -403,14 +412,14 @@ __device__ __forceinline__ void lds_words(const uint8_t *p, uint32_t (&w)[N]) {
 __device__ __forceinline__ float half_of(uint32_t word, int h) { return h ? hi_f(word) : lo_f(word); }
 
 // Per-channel K: add a Q operand's sum of (qh + ql) Z over its 8 elements into b1 (or b16 for
-// the INT4 elements 2, 3, 6, 7, which meet codes times 16)
-template <bool kInt4>
+// the INT4 / INT2 elements 2, 3, 6, 7, which meet codes times 16 / 4)
+template <bool kScaledOdd>
 __device__ __forceinline__ void kc_zero_point(half8_t qh, half8_t ql, uint4 zv, float &b1, float &b16) {
   const uint4 hw = __builtin_bit_cast(uint4, qh), lw = __builtin_bit_cast(uint4, ql);
   const uint32_t h[4] = {hw.x, hw.y, hw.z, hw.w}, l[4] = {lw.x, lw.y, lw.z, lw.w}, z[4] = {zv.x, zv.y, zv.z, zv.w};
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    float &b = (kInt4 && (k & 1)) ? b16 : b1;
+    float &b = (kScaledOdd && (k & 1)) ? b16 : b1;
     b = __builtin_amdgcn_fdot2(as_h2(h[k]), as_h2(z[k]), b, false);
     b = __builtin_amdgcn_fdot2(as_h2(l[k]), as_h2(z[k]), b, false);
   }
@@ -476,9 +485,9 @@ __device__ __forceinline__ void affine_step(const uint8_t *blk, int w, int g, in
       const half8_t s8 = __builtin_bit_cast(half8_t, sv);
       qkh[j] = qb[j] * s8;
       qkl[j] = __builtin_elementwise_fma(qb[j], s8, -qkh[j]);
-      kc_zero_point<NB == 4>(qkh[j], qkl[j], zv, b1, b16);
+      kc_zero_point<NB == 4 || NB == 2>(qkh[j], qkl[j], zv, b1, b16);
     }
-    bq = quad_sum(fmaf(16.0f, b16, b1)) * kSub;        // in the 2^-24 units of the logits
+    bq = quad_sum(fmaf((float)(NB == 4 ? 16 : 4), b16, b1)) * kSub;   // in the 2^-24 units of the logits
   }
 
   float s[8];
@@ -538,8 +547,9 @@ __device__ __forceinline__ void affine_step(const uint8_t *blk, int w, int g, in
     }
   }
   float p[8];
-  constexpr unsigned kScaled = NB == 4 ? 0xCCu : 0u;   // INT4: positions i = 2, 3 of both tiles
-  softmax_step(st, s, p, valid_head, kScaled, sl2);
+  constexpr int SH = NB == 4 ? 4 : NB == 2 ? 2 : 0;
+  constexpr unsigned kScaled = SH != 0 ? 0xCCu : 0u;   // INT4 / INT2: positions i = 2, 3 of both tiles
+  softmax_step<SH>(st, s, p, valid_head, kScaled, sl2);
 
   // P' = p * S per group (one fp16 rounding), and the zero-point sums sum P' Z
   half8_t pb[NG];
@@ -554,7 +564,7 @@ __device__ __forceinline__ void affine_step(const uint8_t *blk, int w, int g, in
       pw[2 * tt] = a01;
       pw[2 * tt + 1] = a23;
       const half2_t z01 = as_h2(vzw[tt][2 * G]), z23 = as_h2(vzw[tt][2 * G + 1]);
-      if constexpr (NB == 4) {
+      if constexpr (NB == 4 || NB == 2) {
         st.z[2 * G] = __builtin_amdgcn_fdot2(as_h2(a01), z01, st.z[2 * G], false);
         st.z[2 * G + 1] = __builtin_amdgcn_fdot2(as_h2(a23), z23, st.z[2 * G + 1], false);
       } else {
@@ -797,13 +807,13 @@ struct QOp2 {
 };
 
 // Dim (index into the lane's 64 loaded dims) fed by B element e of k-step j, and whether it
-// meets an A element scaled by 16.  Affine formats and FP8: the lane holds dims 64G + 16(2q + gi) + m
+// meets an A element scaled by 2^kSh.  Affine formats and FP8: the lane holds dims 64G + 16(2q + gi) + m
 // at local index 32G + 16gi + m (G, gi in {0,1}); natural formats dims 64q + i at index i.
 // B operand idx feeds k-step j = 2(idx >> 2) + (idx & 1) of lane quarter 2q + gi, gi = (idx >> 1) & 1.
 template <int FMT, int GS>
 __device__ __forceinline__ int q_loc2(int j, int e, bool &scaled) {
   const int G = j >> 2, gi = (j >> 1) & 1, hh = j & 1;
-  scaled = FMT == kFmtInt4 && ((e >> 1) & 1) != 0;
+  scaled = kSh<FMT> != 0 && ((e >> 1) & 1) != 0;
   if constexpr (is_affine(FMT) && GS == 32) {
     return 8 * (2 * (2 * G + hh) + gi) + e;   // groups of 32: dims 32 step + 8(2q + gi) + e
   } else if constexpr (FMT == kFmtInt4) {
@@ -858,9 +868,9 @@ __device__ __forceinline__ void load_q2(const uint16_t *qrow, bool valid, int g,
     for (int e = 0; e < 8; ++e) {
       bool scaled;
       _Float16 v = loc[q_loc2<FMT, GS>(j, e, scaled)];
-      if (scaled) v = v * (_Float16)0.0625f;
+      if (scaled) v = v * (_Float16)(1.0f / (1 << kSh<FMT>));
       q.qb[j][e] = v;
-      const float eff = scaled ? 16.0f * (float)v : (float)v;
+      const float eff = scaled ? (float)(1 << kSh<FMT>) * (float)v : (float)v;
       qs[k_group<GS>(2 * (j >> 2) + (j & 1))] += eff;
     }
   }
@@ -869,7 +879,8 @@ __device__ __forceinline__ void load_q2(const uint16_t *qrow, bool valid, int g,
 }
 
 // Running max / probabilities for 4 logits (slots i of the lane's subtile); scaled_mask bit i
-// marks positions whose V operand carries a factor 16 (p / 16 there).
+// marks positions whose V operand carries a factor 2^SH (p / 2^SH there).
+template <int SH = 0>
 __device__ __forceinline__ void softmax_step2(State &st, const float (&s)[4], float (&p)[4], bool valid_head,
                                               unsigned scaled_mask, float sl2) {
   const float ml = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
@@ -884,19 +895,19 @@ __device__ __forceinline__ void softmax_step2(State &st, const float (&s)[4], fl
     st.m = m_new;
   }
   const float nm = st.m == kNegInf ? 0.0f : -st.m * sl2;
-  const float nm4 = nm - 4.0f;
+  const float nm4 = nm - (float)SH;
   float ls = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const bool sc = (scaled_mask >> i) & 1;
     p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, sc ? nm4 : nm));
-    ls = sc ? fmaf(16.0f, p[i], ls) : ls + p[i];
+    ls = sc ? fmaf((float)(1 << SH), p[i], ls) : ls + p[i];
   }
   st.l += ls;
 }
 
 // V operand of subtile s0 from the lane's words (tokens i = 0..3), raw codes as subnormals
-// (INT4: [c0, c1, 16 c2, 16 c3])
+// (INT4: [c0, c1, 16 c2, 16 c3]; INT2: [c0, c1, 4 c2, 4 c3])
 template <int NB>
 __device__ __forceinline__ half4_t v_operand2(const uint32_t *vw, int k, int s0);
 
@@ -907,9 +918,10 @@ __device__ __forceinline__ half4_t v_operand2<4>(const uint32_t *vw, int k, int 
 }
 template <>
 __device__ __forceinline__ half4_t v_operand2<2>(const uint32_t *vw, int k, int s0) {
-  // word k >> 1 holds tiles 2(k>>1) + a; pairs (crumb s, crumb s+8), s = 4a + 2 s0 + {0, 1}
+  // word k >> 1 holds tiles 2(k>>1) + a; pairs (crumb s, crumb s+8), s = 4a + 2 s0 + {0, 1},
+  // the second pair in place (times 4: slots i = 2, 3 carry P / 4)
   const uint32_t x = vw[k >> 1] >> (2 * (4 * (k & 1) + 2 * s0));
-  return h4(x & 0x00030003u, (x >> 2) & 0x00030003u);
+  return h4(x & 0x00030003u, x & 0x000C000Cu);
 }
 template <>
 __device__ __forceinline__ half4_t v_operand2<8>(const uint32_t *vw, int k, int s0) {
@@ -962,9 +974,9 @@ __device__ __forceinline__ void affine_step2(const uint8_t *blk, int w, int g, i
       const half8_t s8 = __builtin_bit_cast(half8_t, sv);
       qkh[idx] = q.qb[idx] * s8;
       qkl[idx] = __builtin_elementwise_fma(q.qb[idx], s8, -qkh[idx]);
-      kc_zero_point<NB == 4>(qkh[idx], qkl[idx], zv, b1, b16);
+      kc_zero_point<NB == 4 || NB == 2>(qkh[idx], qkl[idx], zv, b1, b16);
     }
-    bq = quad_sum(fmaf(16.0f, b16, b1)) * kSub;
+    bq = quad_sum(fmaf((float)(NB == 4 ? 16 : 4), b16, b1)) * kSub;
   }
 
   // QK^T: lane feeds token (subtile sa, row c) from the lane strings of quarters 2qq + gi:
@@ -1028,8 +1040,9 @@ __device__ __forceinline__ void affine_step2(const uint8_t *blk, int w, int g, i
     s[i] = v;
   }
   float p[4];
-  constexpr unsigned kScaled = NB == 4 ? 0xCu : 0u;   // INT4: positions i = 2, 3
-  softmax_step2(st, s, p, valid_head, kScaled, sl2);
+  constexpr int SH = NB == 4 ? 4 : NB == 2 ? 2 : 0;
+  constexpr unsigned kScaled = SH != 0 ? 0xCu : 0u;   // INT4 / INT2: positions i = 2, 3
+  softmax_step2<SH>(st, s, p, valid_head, kScaled, sl2);
 
   // P' = p * S per group (one fp16 rounding) and the zero-point sums sum P' Z; PV as
   // O^T += V^T P per subtile s0: A = V codes of s0, B = this lane's P' where its column
@@ -1039,7 +1052,7 @@ __device__ __forceinline__ void affine_step2(const uint8_t *blk, int w, int g, i
   for (int G = 0; G < NG; ++G) {
     const uint32_t a01 = pk(p[0] * lo_f(vsw[2 * G]), p[1] * hi_f(vsw[2 * G]));
     const uint32_t a23 = pk(p[2] * lo_f(vsw[2 * G + 1]), p[3] * hi_f(vsw[2 * G + 1]));
-    if constexpr (NB == 4) {
+    if constexpr (NB == 4 || NB == 2) {
       st.z[2 * G] = __builtin_amdgcn_fdot2(as_h2(a01), as_h2(vzw[2 * G]), st.z[2 * G], false);
       st.z[2 * G + 1] = __builtin_amdgcn_fdot2(as_h2(a23), as_h2(vzw[2 * G + 1]), st.z[2 * G + 1], false);
     } else {
@@ -1593,7 +1606,7 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
     float zg[NG];
 #pragma unroll
     for (int G = 0; G < NG; ++G) {
-      const float zl = st.z[2 * G] + 16.0f * st.z[2 * G + 1];
+      const float zl = st.z[2 * G] + (float)(1 << kSh<FMT>) * st.z[2 * G + 1];
       zg[G] = NSUB == 2 ? head_sum2(zl) : quad_sum(zl);
       if (!take) zg[G] = 0.0f;
     }
