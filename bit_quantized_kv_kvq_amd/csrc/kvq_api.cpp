@@ -434,7 +434,13 @@ int plan_decode(kvq_cache *c, int layer, DecodeArgs &a, uint64_t *cursors) {
   const int64_t nbh = (int64_t)cfg.batch * cfg.num_kv_heads;
   TierRef tiers[kMaxSegs];
   const int nt = tiers_of(c, layer, st, tiers);
-  const int64_t target = std::max<int64_t>(1, 2LL * num_cus(c) / nbh);       // work items per (b, h)
+  int fmts[kMaxSegs], gss[kMaxSegs];
+  for (int i = 0; i < nt; ++i) {
+    fmts[i] = tiers[i].fmt;
+    gss[i] = tiers[i].gs;
+  }
+  a.occ = decode_occupancy(fmts, gss, nt, a.G);
+  const int64_t target = std::max<int64_t>(1, (int64_t)a.occ * num_cus(c) / nbh);   // work items per (b, h)
   const int parts = split_tiers(c, tiers, nt, target, a.seg);
   for (int i = 0; i < nt; ++i) a.seg[i].cursors = cursors + (size_t)i * nbh;
   a.nseg = nt;
@@ -489,7 +495,13 @@ int plan_decode_ragged(kvq_cache *c, int layer, DecodeArgs &a, uint8_t *ws, cons
   // items per (b, h) of sequence b: ceil(bytes_b / budget), with the smallest per-item budget
   // whose items still fit the GPU once (so that the most loaded item carries as little as the
   // slots allow; rounding each share to the nearest count would leave some items ~10 % heavier)
-  const int64_t slots = 2LL * num_cus(c);
+  int fmts[kMaxSegs], gss[kMaxSegs];
+  for (int u = 0; u < a.nseg; ++u) {
+    fmts[u] = a.seg[u].fmt;
+    gss[u] = a.seg[u].gs;
+  }
+  a.occ = decode_occupancy(fmts, gss, a.nseg, a.G);
+  const int64_t slots = (int64_t)a.occ * num_cus(c);
   auto items_for = [&](double budget) {
     int64_t n = 0;
     for (int b = 0; b < B; ++b) n += H * std::max<int64_t>(1, (int64_t)std::ceil(bytes[b] / budget));

@@ -1649,8 +1649,12 @@ __device__ __forceinline__ void state_to_lds(State &st, int w, int g, int c, flo
   }
 }
 
-template <int NSUB>
-__global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
+// OCC = workgroups per CU the launch is planned for (the bound on VGPRs follows from it).
+// OCC = 3 holds only the INT2 (groups of 64, per-token K) step: the host launches it only when
+// every tier of the call has that format; its VGPRs then fit three waves per SIMD, which
+// hides more of the step's latency (128K INT2 layer 171 -> 156 us, same box).
+template <int NSUB, int OCC>
+__global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
   const bool valid_head = (NSUB == 2 ? (c & 7) : c) < a.G;
@@ -1702,14 +1706,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(DecodeArgs a) {
     else if (sg.gs == 128) KVQ_SEG(F, 128); \
     else KVQ_SEG(F, 64);                   \
     break;
-    switch (sg.fmt) {
-      KVQ_AFFINE_SEG(kFmtInt2)
-      KVQ_AFFINE_SEG(kFmtInt4)
-      KVQ_AFFINE_SEG(kFmtInt8)
-      case kFmtFp8: KVQ_SEG(kFmtFp8, kGroup); break;
-      case kFmtFp16: KVQ_SEG(kFmtFp16, kGroup); break;
-      case kFmtMxfp4: KVQ_SEG(kFmtMxfp4, kGroup); break;
-      default: KVQ_SEG(kFmtNvfp4, kGroup); break;
+    if constexpr (OCC == 3) {
+      KVQ_SEG(kFmtInt2, 64);
+    } else {
+      switch (sg.fmt) {
+        KVQ_AFFINE_SEG(kFmtInt2)
+        KVQ_AFFINE_SEG(kFmtInt4)
+        KVQ_AFFINE_SEG(kFmtInt8)
+        case kFmtFp8: KVQ_SEG(kFmtFp8, kGroup); break;
+        case kFmtFp16: KVQ_SEG(kFmtFp16, kGroup); break;
+        case kFmtMxfp4: KVQ_SEG(kFmtMxfp4, kGroup); break;
+        default: KVQ_SEG(kFmtNvfp4, kGroup); break;
+      }
     }
 #undef KVQ_AFFINE_SEG
 #undef KVQ_SEG
@@ -1820,12 +1828,21 @@ size_t decode_lds_bytes(const DecodeArgs &a) {
   return std::max(stream, merge);
 }
 
+int decode_occupancy(const int *fmt, const int *gs, int n, int G) {
+  if (n == 0 || G > 8) return 2;
+  for (int i = 0; i < n; ++i)
+    if (fmt[i] != kFmtInt2 || gs[i] != 64) return 2;
+  return 3;
+}
+
 hipError_t launch_decode(const DecodeArgs &a, int num_wg, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)decode_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxDecodeLds);
+    hipError_t e = hipFuncSetAttribute((const void *)decode_kernel<1, 2>, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxDecodeLds);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void *)decode_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxDecodeLds);
+      e = hipFuncSetAttribute((const void *)decode_kernel<2, 2>, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxDecodeLds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void *)decode_kernel<2, 3>, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxDecodeLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -1834,8 +1851,17 @@ hipError_t launch_decode(const DecodeArgs &a, int num_wg, hipStream_t s) {
   const size_t lds = decode_lds_bytes(a);
   if (lds > (size_t)kMaxDecodeLds) return hipErrorInvalidValue;
   // two 16-slot subtiles share the MFMA columns when at most 8 query heads share a kv head
-  if (a.G <= 8) decode_kernel<2><<<(unsigned)num_wg, kThreads, lds, s>>>(b);
-  else decode_kernel<1><<<(unsigned)num_wg, kThreads, lds, s>>>(b);
+  if (a.occ == 3) {
+    // only INT2 tiers with groups of 64 (decode_occupancy), G <= 8
+    if (a.G > 8 || lds * 3 > 160 * 1024) return hipErrorInvalidValue;
+    for (int i = 0; i < a.nseg; ++i)
+      if (a.seg[i].fmt != kFmtInt2 || a.seg[i].gs != 64) return hipErrorInvalidValue;
+    decode_kernel<2, 3><<<(unsigned)num_wg, kThreads, lds, s>>>(b);
+  } else if (a.G <= 8) {
+    decode_kernel<2, 2><<<(unsigned)num_wg, kThreads, lds, s>>>(b);
+  } else {
+    decode_kernel<1, 2><<<(unsigned)num_wg, kThreads, lds, s>>>(b);
+  }
   return hipGetLastError();
 }
 

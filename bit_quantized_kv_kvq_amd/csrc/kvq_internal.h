@@ -160,6 +160,10 @@ struct DecodeArgs {
   // (b | h << 16 | part << 25) of its work item.
   const RagSeq *rag;
   const uint32_t *rag_wg;
+  // Workgroups per CU the call is planned for: 3 when every tier is INT2 with groups of 64
+  // and per-token K and G <= 8 (that kernel instantiation holds only this step and needs at
+  // most 168 VGPRs; its 4-block ring of 10 KB blocks leaves LDS for three), else 2.
+  int occ;
 };
 
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t s);
@@ -169,5 +173,8 @@ size_t decode_lds_bytes(const DecodeArgs &a);
 // Dynamic LDS limit of the decode kernel: the fp16 ring (2 x 64 KB) plus 16 query rows
 constexpr int kMaxDecodeLds = 144 * 1024;
 hipError_t launch_decode(const DecodeArgs &a, int num_wg, hipStream_t s);
+// Workgroups per CU of a decode call whose tiers have formats fmt[0..n) with group-size codes
+// gs[0..n) and G query heads per kv head.
+int decode_occupancy(const int *fmt, const int *gs, int n, int G);
 
 }  // namespace kvq

@@ -79,7 +79,8 @@ class Ragged:
 
 CASES = [("int4", 128, None, 0, False, [0, 300, 1000]), ("nvfp4", 0, None, 0, False, [5, 129, 700]),
          ("int4", 128, "int2", 300, True, [100, 900, 2000]), ("fp8", 16, None, 0, False, [40, 0, 513]),
-         ("int4kc", 128, None, 0, False, [256, 1, 640]), ("mxfp4", 32, "int4", 500, False, [1200, 64, 3])]
+         ("int4kc", 128, None, 0, False, [256, 1, 640]), ("mxfp4", 32, "int4", 500, False, [1200, 64, 3]),
+         ("int2", 128, None, 0, False, [700, 0, 1500])]
 
 
 @pytest.mark.parametrize("fmt,R,old,old_after,demote,lens", CASES, ids=lambda x: str(x))
