@@ -141,18 +141,21 @@ def copy_probe():
 
 
 def read_probe_gbs() -> float:
-    """Achievable HBM read rate: a 4 GiB sum (read-bound), best of 5."""
+    """Achievable HBM read rate of one launch: the library's read probe (a grid-stride stream of
+    16-byte loads) over a 4 GiB buffer, timed with HIP events on its stream, best of 6."""
     import torch
-    x = torch.ones(1 << 31, dtype=torch.float16, device="cuda")
+    import bit_quantized_kv_kvq_amd as kvq
+    x = torch.zeros(1 << 32, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(kvq.read_probe_sink_bytes(), dtype=torch.uint8, device="cuda")
     best = 0.0
     for _ in range(6):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        x.sum(dtype=torch.float32)
+        kvq.read_probe(x, sink)
         e1.record()
         e1.synchronize()
-        best = max(best, x.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
-    del x
+        best = max(best, x.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del x, sink
     torch.cuda.empty_cache()
     return best
 

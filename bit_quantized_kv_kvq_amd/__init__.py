@@ -22,7 +22,8 @@ REGION_RESIDUAL, REGION_YOUNG, REGION_OLD = 0, 1, 2
 EXPORTS = ("kvq_cache_bytes", "kvq_cache_create", "kvq_cache_destroy", "kvq_cache_reset", "kvq_append",
            "kvq_append_seq", "kvq_flush_residual", "kvq_decode_workspace_bytes", "kvq_decode_attn",
            "kvq_append_decode_attn", "kvq_seq_len", "kvq_seq_info", "kvq_layout",
-           "kvq_set_plan_only", "kvq_set_deterministic", "kvq_last_error")
+           "kvq_set_plan_only", "kvq_set_deterministic", "kvq_read_probe_sink_bytes", "kvq_read_probe",
+           "kvq_last_error")
 
 
 class KvqError(RuntimeError):
@@ -77,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.kvq_seq_info.argtypes = [vp, i32, i32, P(kvq_seq_info_t)]; L.kvq_seq_info.restype = ctypes.c_int
     L.kvq_set_plan_only.argtypes = [vp, i32]; L.kvq_set_plan_only.restype = ctypes.c_int
     L.kvq_set_deterministic.argtypes = [vp, i32]; L.kvq_set_deterministic.restype = ctypes.c_int
+    L.kvq_read_probe_sink_bytes.argtypes = []; L.kvq_read_probe_sink_bytes.restype = sz
+    L.kvq_read_probe.argtypes = [vp, sz, vp, sz, vp]; L.kvq_read_probe.restype = ctypes.c_int
     L.kvq_last_error.argtypes = []; L.kvq_last_error.restype = ctypes.c_char_p
     _lib = L
     return L
@@ -85,6 +88,19 @@ def lib() -> ctypes.CDLL:
 def _check(code: int):
     if code != KVQ_OK:
         raise KvqError(code, lib().kvq_last_error().decode())
+
+
+def read_probe_sink_bytes() -> int:
+    return lib().kvq_read_probe_sink_bytes()
+
+
+def read_probe(buf, sink, stream=None):
+    """kvq_read_probe: one kernel reading every byte of the uint8 device tensor `buf` once
+    (measurement aid); `sink` (uint8 device tensor of read_probe_sink_bytes()) receives one
+    uint32 per lane, the XOR of the words it read."""
+    _check(lib().kvq_read_probe(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                                ctypes.c_void_p(sink.data_ptr()), sink.numel() * sink.element_size(),
+                                ctypes.c_void_p(_stream_ptr(stream))))
 
 
 def parse_format(name: str):

@@ -730,6 +730,17 @@ int kvq_set_deterministic(kvq_cache *c, int32_t on) {
   return KVQ_OK;
 }
 
+size_t kvq_read_probe_sink_bytes(void) { return kProbeSinkBytes; }
+
+int kvq_read_probe(const void *buf, size_t bytes, void *sink, size_t sink_bytes, void *stream) {
+  if (!buf || !sink) return fail(KVQ_EINVAL, "buf and sink must be non-NULL");
+  if ((uintptr_t)buf % 16 != 0) return fail(KVQ_EINVAL, "buf must be 16-byte aligned");
+  if ((uintptr_t)sink % 4 != 0) return fail(KVQ_EINVAL, "sink must be 4-byte aligned");
+  if (bytes == 0 || bytes % 16 != 0) return fail(KVQ_EINVAL, "bytes (%zu) must be a positive multiple of 16", bytes);
+  if (sink_bytes < kProbeSinkBytes) return fail(KVQ_EINVAL, "sink holds %zu bytes, needs %zu", sink_bytes, kProbeSinkBytes);
+  return hip_check(launch_read_probe(buf, bytes, (uint32_t *)sink, (hipStream_t)stream), "read probe");
+}
+
 int kvq_append(kvq_cache *c, int32_t layer, const void *k, const void *v, int64_t n_tokens, void *stream) {
   if (int e = check_cache(c, layer)) return e;
   if (int e = check_append(c, layer, k, v, n_tokens)) return e;

@@ -173,6 +173,11 @@ size_t decode_lds_bytes(const DecodeArgs &a);
 // Dynamic LDS limit of the decode kernel: the fp16 ring (2 x 64 KB) plus 16 query rows
 constexpr int kMaxDecodeLds = 144 * 1024;
 hipError_t launch_decode(const DecodeArgs &a, int num_wg, hipStream_t s);
+// Read probe: kProbeBlocks workgroups of kProbeThreads lanes stream the buffer (grid-stride),
+// each lane writes one uint32 to the sink.
+constexpr int kProbeBlocks = 2048, kProbeThreads = 256;
+constexpr size_t kProbeSinkBytes = (size_t)kProbeBlocks * kProbeThreads * sizeof(uint32_t);
+hipError_t launch_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s);
 // Workgroups per CU of a decode call whose tiers have formats fmt[0..n) with group-size codes
 // gs[0..n) and G query heads per kv head.
 int decode_occupancy(const int *fmt, const int *gs, int n, int G);

@@ -219,6 +219,17 @@ int kvq_set_plan_only(kvq_cache *c, int32_t plan_only);
    kvq_decode_attn call.  Errors: KVQ_EINVAL (NULL handle). */
 int kvq_set_deterministic(kvq_cache *c, int32_t on);
 
+/* Measurement aid (not part of the method): the achievable HBM read rate of one launch, the
+   reference the decode call's effective rate is compared with.  kvq_read_probe enqueues one
+   kernel that reads every byte of buf once (grid-stride, 16-byte loads) and writes one uint32
+   per lane to sink: the XOR of the 32-bit words that lane read, so that the XOR of the whole
+   sink equals the XOR of buf.  buf: device address, 16-byte aligned; bytes: a positive
+   multiple of 16; sink: device address, 4-byte aligned, at least kvq_read_probe_sink_bytes()
+   bytes (only that many are written).  Both are owned by the caller.  Errors: KVQ_EINVAL (bad
+   pointer, alignment or size; nothing enqueued), KVQ_EHIP (launch failed). */
+size_t kvq_read_probe_sink_bytes(void);
+int kvq_read_probe(const void *buf, size_t bytes, void *sink, size_t sink_bytes, void *stream);
+
 /* Text describing the last failure on the calling thread ("" if none). */
 const char *kvq_last_error(void);
 

@@ -257,3 +257,28 @@ def test_deterministic_switch():
     c = kvq.Cache(kvq.make_config(1, 1, 1, 1000), plan_only=True)
     c.set_deterministic(True)
     c.set_deterministic(False)
+
+
+@pytest.mark.parametrize("case", ["null_buf", "null_sink", "misaligned", "zero", "not16", "small_sink"])
+def test_read_probe_rejects_bad_arguments(case):
+    """kvq_read_probe checks every argument before enqueueing (no GPU is touched here: the
+    pointers are never dereferenced on these paths)."""
+    L = kvq.lib()
+    need = L.kvq_read_probe_sink_bytes()
+    assert need == 2048 * 256 * 4
+    buf, sink, nbytes, sink_bytes = 1 << 20, 1 << 24, 4096, need
+    if case == "null_buf":
+        buf = 0
+    elif case == "null_sink":
+        sink = 0
+    elif case == "misaligned":
+        buf += 8
+    elif case == "zero":
+        nbytes = 0
+    elif case == "not16":
+        nbytes = 4100
+    else:
+        sink_bytes = need - 4
+    rc = L.kvq_read_probe(ctypes.c_void_p(buf or None), nbytes, ctypes.c_void_p(sink or None), sink_bytes, None)
+    assert rc == kvq.KVQ_EINVAL
+    assert L.kvq_last_error()
