@@ -175,7 +175,7 @@ constexpr int kMaxDecodeLds = 144 * 1024;
 hipError_t launch_decode(const DecodeArgs &a, int num_wg, hipStream_t s);
 // Read probe: kProbeBlocks workgroups of kProbeThreads lanes stream the buffer (grid-stride),
 // each lane writes one uint32 to the sink.
-constexpr int kProbeBlocks = 2048, kProbeThreads = 256;
+constexpr int kProbeBlocks = 8192, kProbeThreads = 256;
 constexpr size_t kProbeSinkBytes = (size_t)kProbeBlocks * kProbeThreads * sizeof(uint32_t);
 hipError_t launch_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s);
 // Workgroups per CU of a decode call whose tiers have formats fmt[0..n) with group-size codes

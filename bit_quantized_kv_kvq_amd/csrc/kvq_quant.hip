@@ -334,7 +334,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
       // unconditional (a branch around each load makes the compiler wait for it at the join);
       // past the staged rows the index repeats the last chunk
       const int c = min(tid + t * kThreads, nchunks - 1);
-      v[t] = *(const uint4 *)(src + (tok_off + lo + c / 16) * row_stride + (c % 16) * 16);
+      // (nontemporal: each source row is read once)
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 w = __builtin_nontemporal_load((const u32x4 *)(src + (tok_off + lo + c / 16) * row_stride + (c % 16) * 16));
+      v[t] = make_uint4(w.x, w.y, w.z, w.w);
     }
     // the loaded registers pass through empty asm statements: the loads stay here, all issued
     // before the first store, rather than being sunk into the stores' branches (a "memory"

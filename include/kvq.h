@@ -221,7 +221,8 @@ int kvq_set_deterministic(kvq_cache *c, int32_t on);
 
 /* Measurement aid (not part of the method): the achievable HBM read rate of one launch, the
    reference the decode call's effective rate is compared with.  kvq_read_probe enqueues one
-   kernel that reads every byte of buf once (grid-stride, 16-byte loads) and writes one uint32
+   kernel that reads every byte of buf once (grid-stride, 16-byte nontemporal loads, eight in
+   flight per lane) and writes one uint32
    per lane to sink: the XOR of the 32-bit words that lane read, so that the XOR of the whole
    sink equals the XOR of buf.  buf: device address, 16-byte aligned; bytes: a positive
    multiple of 16; sink: device address, 4-byte aligned, at least kvq_read_probe_sink_bytes()

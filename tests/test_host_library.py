@@ -265,7 +265,7 @@ def test_read_probe_rejects_bad_arguments(case):
     pointers are never dereferenced on these paths)."""
     L = kvq.lib()
     need = L.kvq_read_probe_sink_bytes()
-    assert need == 2048 * 256 * 4
+    assert need == 8192 * 256 * 4
     buf, sink, nbytes, sink_bytes = 1 << 20, 1 << 24, 4096, need
     if case == "null_buf":
         buf = 0
