@@ -379,15 +379,22 @@ int tiers_of(const kvq_cache *c, int layer, const LayerState &st, TierRef *t) {
 
 double tier_bytes(const TierRef &t) { return (double)t.nblk * (double)block_bytes(t.fmt, t.gs); }
 
-// Give each tier of a (b, h) work items in proportion to its bytes (`target` items in all),
+// Decode time per byte of a tier relative to INT4 on the same kernel: the INT2 step is
+// compute-bound (its unpack, logits and P' per block cost about what INT4's do for 56 % of
+// the bytes): on the 128K shape the same number of blocks took 170.3 us as INT2 against
+// 219.6 us as INT4, 1.39x per byte.  The other formats stream at about INT4's rate per byte.
+double tier_cost(const TierRef &t) { return t.fmt == kFmtInt2 ? 1.4 : 1.0; }
+double tier_work(const TierRef &t) { return tier_bytes(t) * tier_cost(t); }
+
+// Give each tier of a (b, h) work items in proportion to its decode time (`target` items in all),
 // cut into chunks small enough (about 32 per item) that the items of a (b, h) even out their
 // finishing times.  Fills out[i] for tier i (not its cursors); returns the items.
 int split_tiers(const kvq_cache *c, const TierRef *t, int nt, int64_t target, DecodeSeg *out) {
-  double bytes = 0;
-  for (int i = 0; i < nt; ++i) bytes += tier_bytes(t[i]);
+  double work = 0;
+  for (int i = 0; i < nt; ++i) work += tier_work(t[i]);
   int parts = 0;
   for (int i = 0; i < nt; ++i) {
-    int64_t items = std::max<int64_t>(1, (int64_t)((double)target * tier_bytes(t[i]) / bytes + 0.5));
+    int64_t items = std::max<int64_t>(1, (int64_t)((double)target * tier_work(t[i]) / work + 0.5));
     items = std::min<int64_t>(items, kMaxParts / std::max(1, nt));
     // units of about 1/32 of an item's share, at least four blocks (a unit's cursor fetch
     // has four block times to come back); two fixed units per item, then the cursor's big
@@ -467,17 +474,17 @@ int plan_decode_ragged(kvq_cache *c, int layer, DecodeArgs &a, uint8_t *ws, cons
   // the call's segments: a tier that any sequence has (old first, as for one sequence)
   std::vector<TierRef> tb((size_t)B * kMaxSegs);
   std::vector<int> nts(B);
-  std::vector<double> bytes(B, 0.0);
+  std::vector<double> work(B, 0.0);   // decode time of each sequence, in INT4 bytes
   bool has[2] = {false, false};
   double total = 0;
   for (int b = 0; b < B; ++b) {
     nts[b] = tiers_of(c, layer, c->st(layer, b), &tb[(size_t)b * kMaxSegs]);
     for (int i = 0; i < nts[b]; ++i) {
       has[tb[(size_t)b * kMaxSegs + i].slot] = true;
-      bytes[b] += tier_bytes(tb[(size_t)b * kMaxSegs + i]);
+      work[b] += tier_work(tb[(size_t)b * kMaxSegs + i]);
     }
-    bytes[b] += 512.0 * (double)c->st(layer, b).res;
-    total += bytes[b];
+    work[b] += 512.0 * (double)c->st(layer, b).res;
+    total += work[b];
   }
   int seg_of[2] = {-1, -1};
   a.nseg = 0;
@@ -492,7 +499,7 @@ int plan_decode_ragged(kvq_cache *c, int layer, DecodeArgs &a, uint8_t *ws, cons
     s.cursors = cursors + (size_t)a.nseg * nbh;
     seg_of[slot] = a.nseg++;
   }
-  // items per (b, h) of sequence b: ceil(bytes_b / budget), with the smallest per-item budget
+  // items per (b, h) of sequence b: ceil(work_b / budget), with the smallest per-item budget
   // whose items still fit the GPU once (so that the most loaded item carries as little as the
   // slots allow; rounding each share to the nearest count would leave some items ~10 % heavier)
   int fmts[kMaxSegs], gss[kMaxSegs];
@@ -504,7 +511,7 @@ int plan_decode_ragged(kvq_cache *c, int layer, DecodeArgs &a, uint8_t *ws, cons
   const int64_t slots = (int64_t)a.occ * num_cus(c);
   auto items_for = [&](double budget) {
     int64_t n = 0;
-    for (int b = 0; b < B; ++b) n += H * std::max<int64_t>(1, (int64_t)std::ceil(bytes[b] / budget));
+    for (int b = 0; b < B; ++b) n += H * std::max<int64_t>(1, (int64_t)std::ceil(work[b] / budget));
     return n;
   };
   double lo = total / (double)slots * H, hi = std::max(total, 1.0);   // items_for(hi) = B H
@@ -522,7 +529,7 @@ int plan_decode_ragged(kvq_cache *c, int layer, DecodeArgs &a, uint8_t *ws, cons
       r.seg[u] = a.seg[u];
       r.seg[u].chunk = 1;
     }
-    const int64_t target = std::max<int64_t>(1, (int64_t)std::ceil(bytes[b] / hi));
+    const int64_t target = std::max<int64_t>(1, (int64_t)std::ceil(work[b] / hi));
     DecodeSeg out[kMaxSegs];
     const int parts = split_tiers(c, &tb[(size_t)b * kMaxSegs], nts[b], target, out);
     for (int i = 0; i < nts[b]; ++i) {

@@ -202,6 +202,27 @@ __device__ __forceinline__ float quad_sum(float x) {
 __device__ __forceinline__ float row_xor8(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
 }
+// Over all 64 lanes (the final merge, once per (batch, kv_head) and call): DPP rotations by
+// 8, 4, 2 and 1 within each row of 16, then the two lane swaps.  Every lane gets the max; for
+// the sum the lanes of a row add in different orders, and lane 0's value is the one used.
+__device__ __forceinline__ float row_ror(float x, int k) {
+  switch (k) {
+    case 8: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+    case 4: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xF, 0xF, false));
+    case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x122, 0xF, 0xF, false));
+    default: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x121, 0xF, 0xF, false));
+  }
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int k = 8; k >= 1; k >>= 1) x = fmaxf(x, row_ror(x, k));
+  return quad_max(x);
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int k = 8; k >= 1; k >>= 1) x += row_ror(x, k);
+  return quad_sum(x);
+}
 // Over the eight lanes {c, c^8} x quarters that hold one head in the paired-subtile layout.
 __device__ __forceinline__ float head_max2(float x) { return quad_max(fmaxf(x, row_xor8(x))); }
 __device__ __forceinline__ float head_sum2(float x) { return quad_sum(x + row_xor8(x)); }
@@ -1619,6 +1640,24 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
   }
 }
 
+// Sum over the call's P partials of one output (head hc, dim d) weighted by w[p][hc]: NB loads
+// in flight per batch, every batch whole (parts past P re-read the last one and enter with
+// weight 0; partials are finite), the sum in order over p.
+template <int NB>
+__device__ __forceinline__ float merge_parts(const float *parts, const float *w, int P, int G, int hc, int d) {
+  float O = 0.0f;
+  for (int p = 0; p < P; p += NB) {
+    float v[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      v[u] = __hip_atomic_load(parts + (int64_t)(min(p + u, P - 1) * G + hc) * kPartialStride + 4 + d, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int u = 0; u < NB; ++u) O += (p + u < P ? w[(p + u) * G + hc] : 0.0f) * v[u];
+  }
+  return O;
+}
+
 // Per-wave state -> LDS rows for the workgroup merge: m[16], l[16] (log2 units) and
 // o[16][128], heads in natural order.
 template <int NSUB>
@@ -1783,28 +1822,41 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeArgs a) {
     sm_l[idx] = __hip_atomic_load(pp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  if (threadIdx.x < G) {
-    const int hc = threadIdx.x;
-    float M = kNegInf;
-    for (int p = 0; p < P; ++p) M = fmaxf(M, sm_m[p * G + hc]);
-    float L = 0.0f;
-    for (int p = 0; p < P; ++p) {
-      const float mv = sm_m[p * G + hc];
-      const float wt = mv == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
-      sm_w[p * G + hc] = wt;
-      L += wt * sm_l[p * G + hc];
+  // few parts: one thread per head walks them; many (a small batch split into many items):
+  // one wave per head, lane l taking parts l and l + 64 (P <= kMaxParts = 128), the max and
+  // the weighted sum of l reduced across the wave
+  if (P <= 16) {
+    if (threadIdx.x < G) {
+      const int hc = threadIdx.x;
+      float M = kNegInf;
+      for (int p = 0; p < P; ++p) M = fmaxf(M, sm_m[p * G + hc]);
+      float L = 0.0f;
+      for (int p = 0; p < P; ++p) {
+        const float mv = sm_m[p * G + hc];
+        const float wt = mv == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
+        sm_w[p * G + hc] = wt;
+        L += wt * sm_l[p * G + hc];
+      }
+      sm_inv[hc] = L > 0.0f ? 1.0f / L : 0.0f;   // L = 0 only for an empty sequence of a ragged batch: zeros
     }
-    sm_inv[hc] = L > 0.0f ? 1.0f / L : 0.0f;   // L = 0 only for an empty sequence of a ragged batch: zeros
+  } else {
+    for (int hc = w; hc < G; hc += kWaves) {
+      const int p0 = lane, p1 = lane + 64;
+      const float m0 = p0 < P ? sm_m[p0 * G + hc] : kNegInf, m1 = p1 < P ? sm_m[p1 * G + hc] : kNegInf;
+      const float M = wave_max(fmaxf(m0, m1));
+      const float w0 = m0 == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m0 - M);
+      const float w1 = m1 == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m1 - M);
+      if (p0 < P) sm_w[p0 * G + hc] = w0;
+      if (p1 < P) sm_w[p1 * G + hc] = w1;
+      const float L = wave_sum((p0 < P ? w0 * sm_l[p0 * G + hc] : 0.0f) + (p1 < P ? w1 * sm_l[p1 * G + hc] : 0.0f));
+      if (lane == 0) sm_inv[hc] = L > 0.0f ? 1.0f / L : 0.0f;
+    }
   }
   __syncthreads();
   const int b = it.bh / a.H, h = it.bh % a.H;
   for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kThreads) {
     const int hc = idx >> 7, d = idx & 127;
-    float O = 0.0f;
-#pragma unroll 8
-    for (int p = 0; p < P; ++p)
-      O += sm_w[p * G + hc] * __hip_atomic_load(parts + (int64_t)(p * G + hc) * kPartialStride + 4 + d, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
+    const float O = P <= 8 ? merge_parts<8>(parts, sm_w, P, G, hc, d) : merge_parts<16>(parts, sm_w, P, G, hc, d);
     const float r = O * sm_inv[hc];
     const int64_t o = ((int64_t)b * a.H * G + (int64_t)h * G + hc) * kHeadDim + d;
     if (a.out_fp32) ((float *)a.out)[o] = r;
