@@ -307,3 +307,23 @@ def test_decode_is_deterministic():
     q = (rng.standard_normal((2, 8, 128)) / np.sqrt(128)).astype(np.float16)
     outs = [p.decode(0, q, 1.0)[0] for _ in range(3)]
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_decode_rotated_block_order_with_partial_block(fmt):
+    """Each (batch, kv_head) visits its blocks rotated by a hashed offset; with 38 blocks (37
+    full, the last holding 5 slots) the four (b, h) get rotations 0, 25, 6 and 31, which wrap
+    past the partial block, and it must still be the one whose tail slots are masked."""
+    R = 0 if fmt == "nvfp4" else 128
+    rng = np.random.default_rng(zlib.crc32(f"rot/{fmt}".encode()))
+    B, H, G, L = 2, 2, 4, 37 * 128 + 5 + R
+    p = Pair(1, B, H, L + 64, fmt, R)
+    k = rng.standard_normal((B, H, L, 128)).astype(np.float16)
+    k[..., :4] *= 15
+    v = rng.standard_normal((B, H, L, 128)).astype(np.float16)
+    p.append(0, k, v)
+    p.check_bytes(0)
+    q = (rng.standard_normal((B, H * G, 128)) / np.sqrt(128)).astype(np.float16)
+    for sigma in (1 / np.sqrt(128), 1.0):
+        got, want = p.decode(0, q, sigma)
+        assert_attention_close(got, want)
