@@ -433,8 +433,8 @@ int num_cus(kvq_cache *c) {
   return c->num_cus;
 }
 
-// Every sequence in one state: all work items of the call fill the GPU about once (two
-// workgroups per CU), the same split for every (b, h).
+// Every sequence in one state: all work items of the call fill the GPU about once (a.occ
+// workgroups per CU: decode_occupancy), the same split for every (b, h).
 int plan_decode(kvq_cache *c, int layer, DecodeArgs &a, uint64_t *cursors) {
   const auto &cfg = c->cfg;
   const LayerState &st = c->st(layer, 0);
