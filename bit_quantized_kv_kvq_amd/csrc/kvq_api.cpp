@@ -87,6 +87,8 @@ const char *check_config(const kvq_config *c) {
   if (c->num_layers < 1 || c->batch < 1 || c->num_kv_heads < 1) return "num_layers, batch and num_kv_heads must be >= 1";
   if (c->head_dim != kHeadDim) return "head_dim must be 128";
   if (c->max_tokens < 1) return "max_tokens must be >= 1";
+  // the decode cursors count a tier's blocks plus its work items in 20 bits
+  if (c->max_tokens > (int64_t)1 << 26) return "max_tokens must be <= 67,108,864";
   if (!is_block_fmt(c->format)) return "format must be KVQ_FMT_FP16/INT2/INT4/INT8/NVFP4/MXFP4/FP8";
   if (is_affine(c->format) ? (c->group_size != 32 && c->group_size != 64 && c->group_size != 128)
                            : c->group_size != group_of(c->format))
@@ -138,6 +140,17 @@ struct kvq_cache {
   size_t bytes = 0;
   std::vector<LayerState> seqs;      // [layer][sequence]: each sequence of the batch has its own schedule
   std::vector<uint8_t> rag_host;     // host copy of a ragged decode call's tables
+  // Pinned host slots the ragged tables are copied from (so that the stream-ordered copy never
+  // blocks the host), each with an event marking its copy; used round-robin, a slot is
+  // rewritten only after its previous copy has completed.
+  struct PinnedSlot {
+    void *host = nullptr;
+    size_t cap = 0;
+    hipEvent_t ev = nullptr;
+    bool pending = false;
+  };
+  std::vector<PinnedSlot> pinned;
+  size_t pinned_next = 0;
   int plan_only = 0;
   int deterministic = 0;   // decode: chunks assigned up front instead of through the cursor
   int num_cus = 0;
@@ -153,6 +166,15 @@ struct kvq_cache {
     for (int b = 1; b < cfg.batch; ++b)
       if (!(st(l, b) == st(l, 0))) return false;
     return true;
+  }
+  ~kvq_cache() {
+    for (PinnedSlot &p : pinned) {
+      if (p.ev) {
+        if (p.pending) (void)hipEventSynchronize(p.ev);
+        (void)hipEventDestroy(p.ev);
+      }
+      if (p.host) (void)hipHostFree(p.host);
+    }
   }
 };
 
@@ -336,15 +358,23 @@ int run_plan(kvq_cache *c, int layer, const Plan &p, const void *k, const void *
 
 // ---------------------------------------------------------------------------- decode plan
 
-std::atomic<uint32_t> g_epoch{0};
+// Call tags of the decode counters: 44 bits, never 0 (the value the counters hold between calls).
+std::atomic<uint64_t> g_epoch{0};
+uint64_t next_epoch() {
+  for (;;) {
+    const uint64_t e = ++g_epoch & ((1ull << 44) - 1);
+    if (e != 0) return e;
+  }
+}
 
 // Per (b, h): one arrival counter and one chunk cursor per tier.
 size_t counters_bytes(const kvq_cache *c) {
   return align_up((size_t)c->cfg.batch * c->cfg.num_kv_heads * (1 + kMaxSegs) * sizeof(uint64_t));
 }
-size_t partials_bytes(const kvq_cache *c, int32_t num_q_heads) {
+// parts: partial slots per (b, h) (a call uses its most work items of one (b, h))
+size_t partials_bytes(const kvq_cache *c, int32_t num_q_heads, int parts = kMaxParts) {
   const size_t bh = (size_t)c->cfg.batch * c->cfg.num_kv_heads;
-  return align_up(bh * kMaxParts * (size_t)(num_q_heads / c->cfg.num_kv_heads) * kPartialStride * sizeof(float));
+  return align_up(bh * (size_t)parts * (size_t)(num_q_heads / c->cfg.num_kv_heads) * kPartialStride * sizeof(float));
 }
 // ragged calls: one RagSeq per sequence, then one table entry per workgroup
 size_t rag_seq_bytes(const kvq_cache *c) { return align_up((size_t)c->cfg.batch * sizeof(RagSeq)); }
@@ -449,7 +479,7 @@ int plan_decode(kvq_cache *c, int layer, DecodeArgs &a, uint64_t *cursors) {
   a.occ = decode_occupancy(fmts, gss, nt, a.G);
   const int64_t target = std::max<int64_t>(1, (int64_t)a.occ * num_cus(c) / nbh);   // work items per (b, h)
   const int parts = split_tiers(c, tiers, nt, target, a.seg);
-  for (int i = 0; i < nt; ++i) a.seg[i].cursors = cursors + (size_t)i * nbh;
+  for (int i = 0; i < nt; ++i) a.seg[i].cursors = cursors ? cursors + (size_t)i * nbh : nullptr;
   a.nseg = nt;
   a.items_total = std::max(1, parts);
   a.res_base = c->res(layer);
@@ -462,15 +492,15 @@ int plan_decode(kvq_cache *c, int layer, DecodeArgs &a, uint64_t *cursors) {
 }
 
 // A ragged batch: each sequence gets work items in proportion to its own bytes (the call's
-// items still fill the GPU about once) and its own split; the tables go to the workspace
-// (stream-ordered copy) for the kernel.  pend[b]: sequence b's pending residual copy (count 0: none).
-int plan_decode_ragged(kvq_cache *c, int layer, DecodeArgs &a, uint8_t *ws, const Op *pend, hipStream_t stream,
-                       int *num_wg) {
+// items still fill the GPU about once) and its own split.  The tables are built in
+// c->rag_host (host only); *copy_bytes of them go to the workspace before the launch, *maxp
+// is the most work items of one (b, h).  pend[b]: sequence b's pending residual copy (count 0: none).
+int plan_decode_ragged(kvq_cache *c, int layer, DecodeArgs &a, uint64_t *cursors, const Op *pend, int *num_wg,
+                       int *maxp_out, size_t *copy_bytes) {
   const auto &cfg = c->cfg;
   const int B = cfg.batch, H = cfg.num_kv_heads;
   const int64_t nbh = (int64_t)B * H;
   if (B > 65536 || H > 512) return fail(KVQ_EINVAL, "ragged decode supports batch <= 65536 and kv heads <= 512");
-  uint64_t *cursors = (uint64_t *)ws + nbh;
   // the call's segments: a tier that any sequence has (old first, as for one sequence)
   std::vector<TierRef> tb((size_t)B * kMaxSegs);
   std::vector<int> nts(B);
@@ -553,13 +583,8 @@ int plan_decode_ragged(kvq_cache *c, int layer, DecodeArgs &a, uint8_t *ws, cons
     for (int b = 0; b < B; ++b)
       if (p < rs[b].items_total)
         for (int h = 0; h < H; ++h) wg[n++] = (uint32_t)b | ((uint32_t)h << 16) | ((uint32_t)p << 25);
-  uint8_t *dev_tab = ws + counters_bytes(c) + partials_bytes(c, a.G * H);
-  const size_t copy = rag_seq_bytes(c) + (size_t)n * sizeof(uint32_t);
-  if (!c->plan_only)
-    if (int e = hip_check(hipMemcpyAsync(dev_tab, c->rag_host.data(), copy, hipMemcpyHostToDevice, stream), "ragged tables"))
-      return e;
-  a.rag = (const RagSeq *)dev_tab;
-  a.rag_wg = (const uint32_t *)(dev_tab + rag_seq_bytes(c));
+  *copy_bytes = rag_seq_bytes(c) + (size_t)n * sizeof(uint32_t);
+  *maxp_out = maxp;
   a.items_total = 1;
   a.res_base = c->res(layer);
   a.res_bh_stride = (int64_t)c->geo.res_bh;
@@ -569,16 +594,51 @@ int plan_decode_ragged(kvq_cache *c, int layer, DecodeArgs &a, uint8_t *ws, cons
   return KVQ_OK;
 }
 
-int check_decode(const kvq_cache *c, const void *q, int32_t num_q_heads, float softmax_scale, const void *out,
-                 const void *workspace, size_t ws_bytes) {
+// Stream-ordered copy of `bytes` host bytes to device address dst through the cache's pinned
+// slots: the copy is a DMA from pinned memory, so enqueueing it does not wait for the device;
+// the host waits only when every slot's previous copy is still queued.
+int pinned_copy(kvq_cache *c, void *dst, const void *src, size_t bytes, hipStream_t s) {
+  if (c->pinned.empty()) c->pinned.resize((size_t)std::min(256, std::max(8, 2 * c->cfg.num_layers)));
+  auto &p = c->pinned[c->pinned_next];
+  c->pinned_next = (c->pinned_next + 1) % c->pinned.size();
+  if (p.pending) {
+    if (int e = hip_check(hipEventSynchronize(p.ev), "pinned slot")) return e;
+    p.pending = false;
+  }
+  if (p.cap < bytes) {
+    if (p.host) (void)hipHostFree(p.host);
+    p.host = nullptr;
+    p.cap = 0;
+    if (int e = hip_check(hipHostMalloc(&p.host, bytes, hipHostMallocDefault), "pinned slot")) return e;
+    p.cap = bytes;
+  }
+  if (!p.ev)
+    if (int e = hip_check(hipEventCreateWithFlags(&p.ev, hipEventDisableTiming), "pinned slot event")) return e;
+  std::memcpy(p.host, src, bytes);
+  if (int e = hip_check(hipMemcpyAsync(dst, p.host, bytes, hipMemcpyHostToDevice, s), "ragged tables")) return e;
+  if (int e = hip_check(hipEventRecord(p.ev, s), "pinned slot event")) return e;
+  p.pending = true;
+  return KVQ_OK;
+}
+
+// the arguments of a decode call other than the workspace
+int check_decode_args(const kvq_cache *c, const void *q, int32_t num_q_heads, float softmax_scale, const void *out) {
   const auto &cfg = c->cfg;
   if (num_q_heads < 1 || num_q_heads % cfg.num_kv_heads != 0)
     return fail(KVQ_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads, cfg.num_kv_heads);
   const int G = num_q_heads / cfg.num_kv_heads;
   if (G > 16) return fail(KVQ_EINVAL, "query heads per kv head (%d) must be <= 16", G);
-  if (!q || !out || !workspace) return fail(KVQ_EINVAL, "q, out and workspace must be non-NULL");
-  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return fail(KVQ_EINVAL, "q, out and workspace must be 16-byte aligned");
+  if (!q || !out) return fail(KVQ_EINVAL, "q and out must be non-NULL");
+  if (!aligned16(q) || !aligned16(out)) return fail(KVQ_EINVAL, "q and out must be 16-byte aligned");
   if (!(softmax_scale > 0.0f) || softmax_scale > 3.0e38f) return fail(KVQ_EINVAL, "softmax_scale must be positive and finite");
+  return KVQ_OK;
+}
+
+int check_decode(const kvq_cache *c, const void *q, int32_t num_q_heads, float softmax_scale, const void *out,
+                 const void *workspace, size_t ws_bytes) {
+  if (int e = check_decode_args(c, q, num_q_heads, softmax_scale, out)) return e;
+  if (!workspace) return fail(KVQ_EINVAL, "workspace must be non-NULL");
+  if (!aligned16(workspace)) return fail(KVQ_EINVAL, "workspace must be 16-byte aligned");
   if (ws_bytes < workspace_bound(c, num_q_heads))
     return fail(KVQ_ENOSPACE, "workspace %zu < required %zu", ws_bytes, workspace_bound(c, num_q_heads));
   return KVQ_OK;
@@ -602,29 +662,43 @@ int check_append(const kvq_cache *c, int32_t layer, const void *k, const void *v
 // The decode launch of a checked call.  `pending` (may be null): the residual copy of the same
 // call's append (tokens [src_tok0, +count) of k / v, n_src tokens each), done by the launch
 // itself; for a ragged batch (`ragged`) one Op per sequence.
+// Workspace layout of one call: [arrival counters and cursors][partials: part_stride slots per
+// (b, h)][ragged tables].  A call needs counters_bytes + partials_bytes(part_stride) (+ the
+// tables); ws_bytes is checked against that before anything is enqueued.
 int run_decode(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_heads, float softmax_scale, void *out,
-               int32_t out_fp32, void *workspace, const Op *pending, const void *k, const void *v, int64_t n_src,
-               void *stream, bool ragged) {
+               int32_t out_fp32, void *workspace, size_t ws_bytes, const Op *pending, const void *k, const void *v,
+               int64_t n_src, void *stream, bool ragged) {
   const auto &cfg = c->cfg;
   const int G = num_q_heads / cfg.num_kv_heads;
   if (c->plan_only) return KVQ_OK;
   DecodeArgs a{};
   a.B = cfg.batch; a.H = cfg.num_kv_heads; a.G = G;
-  int num_wg = 0;
+  uint64_t *cursors = (uint64_t *)workspace + (size_t)cfg.batch * cfg.num_kv_heads;
+  int num_wg = 0, parts = 1;
+  size_t tab_bytes = 0;
   if (ragged) {
-    if (int e = plan_decode_ragged(c, layer, a, (uint8_t *)workspace, pending, (hipStream_t)stream, &num_wg)) return e;
+    if (int e = plan_decode_ragged(c, layer, a, cursors, pending, &num_wg, &parts, &tab_bytes)) return e;
   } else {
-    num_wg = plan_decode(c, layer, a, (uint64_t *)workspace + (size_t)cfg.batch * cfg.num_kv_heads);
+    num_wg = plan_decode(c, layer, a, cursors);
+    parts = a.items_total;
+  }
+  const size_t part_bytes = partials_bytes(c, num_q_heads, parts);
+  const size_t need = counters_bytes(c) + part_bytes + tab_bytes;
+  if (need > ws_bytes) return fail(KVQ_ENOSPACE, "this call needs %zu bytes of workspace, %zu given", need, ws_bytes);
+  if (ragged) {
+    uint8_t *dev_tab = (uint8_t *)workspace + counters_bytes(c) + part_bytes;
+    if (int e = pinned_copy(c, dev_tab, c->rag_host.data(), tab_bytes, (hipStream_t)stream)) return e;
+    a.rag = (const RagSeq *)dev_tab;
+    a.rag_wg = (const uint32_t *)(dev_tab + rag_seq_bytes(c));
   }
   a.q = (const uint16_t *)q;
   a.out = out;
   a.out_fp32 = out_fp32 ? 1 : 0;
   a.counters = (uint64_t *)workspace;
   a.partials = (float *)((uint8_t *)workspace + counters_bytes(c));
+  a.part_stride = parts;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  uint32_t ep = ++g_epoch;
-  if (ep == 0) ep = ++g_epoch;
-  a.epoch = ep;
+  a.epoch = next_epoch();
   if (pending) {
     a.pend_k = (const uint16_t *)k; a.pend_v = (const uint16_t *)v;
     a.pend_src_ntok = n_src;
@@ -814,8 +888,8 @@ int kvq_decode_attn(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_he
   if (int e = check_decode(c, q, num_q_heads, softmax_scale, out, workspace, ws_bytes)) return e;
   const bool ragged = !c->uniform(layer);
   if (!ragged && c->st(layer, 0).length == 0) return fail(KVQ_ESTATE, "layer %d is empty", layer);
-  return run_decode(c, layer, q, num_q_heads, softmax_scale, out, out_fp32, workspace, nullptr, nullptr, nullptr, 0,
-                    stream, ragged);
+  return run_decode(c, layer, q, num_q_heads, softmax_scale, out, out_fp32, workspace, ws_bytes, nullptr, nullptr,
+                    nullptr, 0, stream, ragged);
 }
 
 int kvq_append_decode_attn(kvq_cache *c, int32_t layer, const void *k, const void *v, int64_t n_tokens, const void *q,
@@ -828,8 +902,8 @@ int kvq_append_decode_attn(kvq_cache *c, int32_t layer, const void *k, const voi
     std::vector<Op> pend(c->cfg.batch, Op{Op::kResCopy, 0, 0, 0, 0});
     if (n_tokens > 0)
       if (int e = append_ragged(c, layer, k, v, n_tokens, (hipStream_t)stream, pend.data())) return e;
-    return run_decode(c, layer, q, num_q_heads, softmax_scale, out, out_fp32, workspace, pend.data(), k, v, n_tokens,
-                      stream, true);
+    return run_decode(c, layer, q, num_q_heads, softmax_scale, out, out_fp32, workspace, ws_bytes, pend.data(), k, v,
+                      n_tokens, stream, true);
   }
   LayerState st = c->st(layer, 0);
   if (st.length + n_tokens == 0) return fail(KVQ_ESTATE, "layer %d is empty", layer);
@@ -848,8 +922,8 @@ int kvq_append_decode_attn(kvq_cache *c, int32_t layer, const void *k, const voi
       for (int b = 0; b < c->cfg.batch; ++b) c->st(layer, b) = p.after;
     if (e != KVQ_OK) return e;
   }
-  return run_decode(c, layer, q, num_q_heads, softmax_scale, out, out_fp32, workspace, has_pending ? &pending : nullptr,
-                    k, v, n_tokens, stream, false);
+  return run_decode(c, layer, q, num_q_heads, softmax_scale, out, out_fp32, workspace, ws_bytes,
+                    has_pending ? &pending : nullptr, k, v, n_tokens, stream, false);
 }
 
 int kvq_seq_info(const kvq_cache *c, int32_t layer, int32_t seq, kvq_seq_info_t *info) {

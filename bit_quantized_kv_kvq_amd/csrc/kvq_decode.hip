@@ -259,11 +259,31 @@ __device__ __forceinline__ constexpr int v_group(int k) { return GS == 32 ? k >>
 template <int GS>
 constexpr int kGroups = GS == kKc ? 2 : kHeadDim / GS;   // per-token groups along head_dim
 
+// INT4 and INT2 meet half of the query row with codes taken times 2^kSh (the masked high
+// fields), so that half enters the MFMA as q / 2^kSh.  Divided as it stands, a query entry
+// below 2^(kSh - 14) would become an fp16 subnormal and lose relative precision (the oracle
+// uses q exactly).  So each head's row is first scaled by a power of two 2^t that puts its
+// largest magnitude M into [2^14, 2^15): every entry >= M 2^-24 then keeps its full fp16
+// precision after the division, and smaller ones are off by at most M 2^-35 (both roundings
+// are exact otherwise: a power-of-two scaling).  The logits come out 2^t larger, which the
+// softmax scale and the max take back (t >= 0 keeps every entry finite).  Per-channel K
+// multiplies q by the block's per-dim S first, where no fixed shift is safe from overflow.
+template <int FMT, int GS>
+constexpr bool kQShift = kSh<FMT> != 0 && GS != kKc;
+// 2^t for a row maximum M (the same on every lane of the head: M is reduced over them)
+__device__ __forceinline__ float q_shift_scale(float M) {
+  if (!(M > 0.0f)) return 1.0f;
+  const int E = (int)((__float_as_uint(M) >> 23) & 0xFFu) - 127;   // M = 2^E (1 + f), normal in fp32
+  const int t = max(0, 14 - E);
+  return __uint_as_float((uint32_t)(127 + t) << 23);
+}
+
 // The 32 dims a lane quarter g feeds: affine formats (groups of 64 or 128) and FP8 dims
 // 16g..16g+15 and 64+16g..64+16g+15 (local index 16G + m); affine groups of 32 dims 32j + 8g
 // .. +7 (local index 8j + m); NVFP4 and fp16 dims 32g..32g+31 (local index dim - 32g).
 template <int FMT, int GS>
-__device__ __forceinline__ void load_q(const uint16_t *qrow, bool valid, int g, half8_t (&qb)[4], float (&qs)[4]) {
+__device__ __forceinline__ void load_q(const uint16_t *qrow, bool valid, int g, half8_t (&qb)[4], float (&qs)[4],
+                                       float &qscale) {
   constexpr bool kLay32 = is_affine(FMT) && GS == 32;
   constexpr bool kLay64 = !kLay32 && (is_affine(FMT) || FMT == kFmtFp8);
   uint4 raw[4];
@@ -286,6 +306,13 @@ __device__ __forceinline__ void load_q(const uint16_t *qrow, bool valid, int g, 
 #pragma unroll
     for (int e = 0; e < 8; ++e) loc[8 * i + e] = valid ? v[e] : (_Float16)0.0f;
   }
+  qscale = 1.0f;
+  if constexpr (kQShift<FMT, GS>) {
+    _Float16 mh = (_Float16)0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) mh = __builtin_fmaxf16(mh, __builtin_fabsf16(loc[i]));
+    qscale = q_shift_scale(quad_max((float)mh));   // the four quarters hold the head's 128 dims
+  }
 #pragma unroll
   for (int G = 0; G < 4; ++G) qs[G] = 0.0f;
 #pragma unroll
@@ -296,7 +323,8 @@ __device__ __forceinline__ void load_q(const uint16_t *qrow, bool valid, int g, 
       const int d = q_dim<FMT, GS>(g, j, e, scaled);
       const int li = kLay32 ? 8 * (d >> 5) + (d & 7) : kLay64 ? 16 * (d >> 6) + (d & 15) : d - 32 * g;
       _Float16 v = loc[li];
-      if (scaled) v = v * (_Float16)(1.0f / (1 << kSh<FMT>));
+      if constexpr (kQShift<FMT, GS>) v = (_Float16)((float)v * (scaled ? qscale * (1.0f / (1 << kSh<FMT>)) : qscale));
+      else if (scaled) v = v * (_Float16)(1.0f / (1 << kSh<FMT>));
       qb[j][e] = v;
       const float eff = scaled ? (float)(1 << kSh<FMT>) * (float)v : (float)v;    // the q the MFMA effectively uses
       qs[k_group<GS>(j)] += eff;
@@ -416,6 +444,7 @@ __device__ __forceinline__ void softmax_step(State &st, const float (&s)[8], flo
 struct QOp {
   half8_t qb[4];
   float qs[4];             // per-group sums of the effective q (zero-point terms)
+  float qscale = 1.0f;     // 2^t the query row was scaled by (kQShift formats; else 1)
 };
 
 // N consecutive 32-bit words from LDS (N = 2, 4 or 8)
@@ -827,6 +856,7 @@ __device__ __forceinline__ void residual_step(const uint8_t *res, int R, int r, 
 struct QOp2 {
   half8_t qb[8];
   float qs[4];
+  float qscale = 1.0f;     // as in QOp
 };
 
 // Dim (index into the lane's 64 loaded dims) fed by B element e of k-step j, and whether it
@@ -884,6 +914,14 @@ __device__ __forceinline__ void load_q2(const uint16_t *qrow, bool valid, int g,
 #pragma unroll
     for (int e = 0; e < 8; ++e) loc[8 * i + e] = active ? v[e] : (_Float16)0.0f;
   }
+  q.qscale = 1.0f;
+  if constexpr (kQShift<FMT, GS>) {
+    // the two active quarters of the lane's column hold the head's two halves (the others zeros)
+    _Float16 mh = (_Float16)0.0f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) mh = __builtin_fmaxf16(mh, __builtin_fabsf16(loc[i]));
+    q.qscale = q_shift_scale(quad_max((float)mh));
+  }
   float qs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -891,7 +929,8 @@ __device__ __forceinline__ void load_q2(const uint16_t *qrow, bool valid, int g,
     for (int e = 0; e < 8; ++e) {
       bool scaled;
       _Float16 v = loc[q_loc2<FMT, GS>(j, e, scaled)];
-      if (scaled) v = v * (_Float16)(1.0f / (1 << kSh<FMT>));
+      if constexpr (kQShift<FMT, GS>) v = (_Float16)((float)v * (scaled ? q.qscale * (1.0f / (1 << kSh<FMT>)) : q.qscale));
+      else if (scaled) v = v * (_Float16)(1.0f / (1 << kSh<FMT>));
       q.qb[j][e] = v;
       const float eff = scaled ? (float)(1 << kSh<FMT>) * (float)v : (float)v;
       qs[k_group<GS>(2 * (j >> 2) + (j & 1))] += eff;
@@ -1325,40 +1364,47 @@ __device__ __forceinline__ void residual_step2(const uint8_t *res, int R, int r,
 }
 
 // ---------------------------------------------------------------- call-tagged counters
-// A counter in the caller's workspace is a 64-bit word (epoch << 32 | count).  A call works
-// only with words tagged with its own epoch; a word still tagged with an older one is
-// replaced, by compare-and-swap, with a fresh count of this call.  Adds that land on an old
-// word are void (their issuer sees the old tag) and are made again.  All accesses are
-// agent-scope atomics, so workgroups on different XCDs see one order of them.
-__device__ __forceinline__ uint32_t tag_of(uint64_t v) { return (uint32_t)(v >> 32); }
+// A counter in the workspace is a 64-bit word (epoch << kCountBits | count): a 44-bit call
+// tag over a 20-bit count (arrivals <= kMaxParts; cursor units <= blocks + items of a tier,
+// which the host keeps below 2^20).  A call works only with words tagged with its own
+// epoch; a word with any other tag is replaced, by compare-and-swap, with a fresh count of
+// this call.  Adds that land on such a word are void (their issuer sees the other tag) and
+// are made again.  The last workgroup of a (batch, kv_head) sets its words back to zero once
+// every other access of the call has completed, so between calls they hold 0 (tag 0, which
+// no call uses); only words the caller wrote since (or a workspace's first use) hold other
+// values, and those are replaced unless their top 44 bits equal the call's epoch.  All
+// accesses are agent-scope atomics, so workgroups on different XCDs see one order of them.
+constexpr int kCountBits = 20;
+constexpr uint64_t kCountMask = (1ull << kCountBits) - 1;
+__device__ __forceinline__ uint64_t tag_of(uint64_t v) { return v >> kCountBits; }
 
 // Tag the word with this call's epoch and a zero count, unless this call has done so already.
-__device__ __forceinline__ void counter_open(uint64_t *w, uint32_t epoch) {
+__device__ __forceinline__ void counter_open(uint64_t *w, uint64_t epoch) {
   uint64_t cur = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   while (tag_of(cur) != epoch)
-    if (__hip_atomic_compare_exchange_strong(w, &cur, (uint64_t)epoch << 32, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+    if (__hip_atomic_compare_exchange_strong(w, &cur, epoch << kCountBits, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT))
       break;
 }
 
-// The count before this call's add, after an add that came back with an older tag: open the
+// The count before this call's add, after an add that came back with another tag: open the
 // word with this add counted (count 0 before it), or add again once another opener has.
 // Each pass either succeeds or finds the word changed by one of the finitely many other
 // accesses of the call.
-__device__ __forceinline__ uint32_t counter_add_slow(uint64_t *w, uint32_t epoch) {
+__device__ __forceinline__ uint32_t counter_add_slow(uint64_t *w, uint64_t epoch) {
   uint64_t cur = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (;;) {
     if (tag_of(cur) == epoch)
-      return (uint32_t)__hip_atomic_fetch_add(w, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (__hip_atomic_compare_exchange_strong(w, &cur, ((uint64_t)epoch << 32) | 1u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+      return (uint32_t)(__hip_atomic_fetch_add(w, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kCountMask);
+    if (__hip_atomic_compare_exchange_strong(w, &cur, (epoch << kCountBits) | 1u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT))
       return 0;
   }
 }
 
 // The count before an add whose returned word is `old`.
-__device__ __forceinline__ uint32_t counter_result(uint64_t *w, uint32_t epoch, uint64_t old) {
-  return tag_of(old) == epoch ? (uint32_t)old : counter_add_slow(w, epoch);
+__device__ __forceinline__ uint32_t counter_result(uint64_t *w, uint64_t epoch, uint64_t old) {
+  return tag_of(old) == epoch ? (uint32_t)(old & kCountMask) : counter_add_slow(w, epoch);
 }
 
 // ---------------------------------------------------------------- the kernel
@@ -1459,7 +1505,7 @@ __device__ __forceinline__ void residual_part(const DecodeArgs &a, const Item &i
     for (int u = w; u < nsteps; u += kWaves) residual_step2(res, a.res_len, it.res_ntok, u, g, c, q, a.scale_log2, valid_head, st);
   } else {
     QOp q;
-    load_q<kFmtFp16, kGroup>(qrow, valid_head, g, q.qb, q.qs);
+    load_q<kFmtFp16, kGroup>(qrow, valid_head, g, q.qb, q.qs, q.qscale);
     for (int u = w; u < nsteps; u += kWaves) residual_step(res, a.res_len, it.res_ntok, u, g, c, q, a.scale_log2, valid_head, st);
   }
 }
@@ -1562,11 +1608,13 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
   QOp q;
   QOp2 q2;
   if constexpr (NSUB == 2) load_q2<FMT, GS>(qrow, valid_head, g, c, q2);
-  else load_q<FMT, GS>(qrow, valid_head, g, q.qb, q.qs);
-  // affine logits come out in units of 2^-24 (subnormal code operands)
-  const float sl2 = kAff ? a.scale_log2 * kInvSub : a.scale_log2;
+  else load_q<FMT, GS>(qrow, valid_head, g, q.qb, q.qs, q.qscale);
+  // affine logits come out in units of 2^-24 (subnormal code operands), times the query row's
+  // power-of-two scale
+  const float qscale = NSUB == 2 ? q2.qscale : q.qscale;
+  const float sl2 = kAff ? a.scale_log2 * (kInvSub / qscale) : a.scale_log2;
   if constexpr (kAff) {
-    if (st.m != kNegInf) st.m *= kSub;
+    if (st.m != kNegInf) st.m *= kSub * qscale;
 #pragma unroll
     for (int k = 0; k < 8; ++k) st.o[k] = st.o[k] * kSub;
   }
@@ -1630,7 +1678,7 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
     // Back to natural units: m * 2^24, and o = 2^24 o - sum P' Z of the group of each dim (for
     // paired subtiles the head's total goes to its subtile-0 column only; the two columns are
     // summed later).
-    if (st.m != kNegInf) st.m *= kInvSub;
+    if (st.m != kNegInf) st.m *= kInvSub / qscale;
     constexpr int NG = kGroups<GS>;
     const bool take = NSUB == 2 ? (c >> 3) == 0 : true;
     float zg[NG];
@@ -1778,7 +1826,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeArgs a) {
   __syncthreads();
 
   const int G = a.G;
-  float *part = a.partials + ((int64_t)it.bh * kMaxParts + it.part) * G * kPartialStride;
+  float *part = a.partials + ((int64_t)it.bh * a.part_stride + it.part) * G * kPartialStride;
   for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kThreads) {
     const int hc = idx >> 7, d = idx & 127;
     float M = kNegInf;
@@ -1818,7 +1866,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeArgs a) {
   if (!s_last) return;
 
   const int P = it.items_total;
-  const float *parts = a.partials + (int64_t)it.bh * kMaxParts * G * kPartialStride;
+  const float *parts = a.partials + (int64_t)it.bh * a.part_stride * G * kPartialStride;
   float *sm_m = (float *)smem;            // [P][G]
   float *sm_w = sm_m + P * G;             // [P][G] weights, after the max is known
   float *sm_l = sm_w + P * G;             // [P][G]
@@ -1868,6 +1916,13 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeArgs a) {
     const int64_t o = ((int64_t)b * a.H * G + (int64_t)h * G + hc) * kHeadDim + d;
     if (a.out_fp32) ((float *)a.out)[o] = r;
     else ((_Float16 *)a.out)[o] = (_Float16)r;
+  }
+  // Every other workgroup of this (b, h) has arrived, each after all its memory operations
+  // completed (its cursor fetch-adds included), so no access of this call to the (b, h)'s
+  // arrival counter or cursors is left: set them back to zero for the next call.
+  if (threadIdx.x < 1 + a.nseg) {
+    uint64_t *wd = threadIdx.x == 0 ? a.counters + it.bh : a.seg[threadIdx.x - 1].cursors + it.bh;
+    __hip_atomic_store(wd, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

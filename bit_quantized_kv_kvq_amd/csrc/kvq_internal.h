@@ -114,7 +114,7 @@ struct DecodeSeg {
   int fixed;               // units per item assigned up front
   int nbig;                // big units the cursor hands out before the single blocks
   int part0;               // index of this segment's first partial among a (b, h)'s partials
-  uint64_t *cursors;       // [B*H] chunk cursors (epoch << 32 | units handed out)
+  uint64_t *cursors;       // [B*H] chunk cursors (epoch << 20 | units handed out)
 };
 
 constexpr int kMaxSegs = 2;        // old tier, young tier
@@ -136,8 +136,9 @@ struct DecodeArgs {
   const uint16_t *q;       // [B][Hq][128] fp16
   void *out;               // [B][Hq][128] fp32 or fp16
   int out_fp32;
-  uint64_t *counters;      // [B*H] arrival counters (epoch << 32 | count)
-  float *partials;         // [B*H][kMaxParts][G][kPartialStride]
+  uint64_t *counters;      // [B*H] arrival counters (epoch << 20 | count)
+  float *partials;         // [B*H][part_stride][G][kPartialStride]
+  int part_stride;         // partial slots per (b, h): the call's most work items of a (b, h) (<= kMaxParts)
   DecodeSeg seg[kMaxSegs];
   int nseg;
   int items_total;         // work items per (b, h), all segments (at least 1)
@@ -148,7 +149,7 @@ struct DecodeArgs {
   int res_ntok;            // r (slots in use)
   int B, H, G;             // Hq = H * G
   float scale_log2;        // softmax_scale * log2(e)
-  uint32_t epoch;          // distinct per call, tags the arrival counters
+  uint64_t epoch;          // distinct per call (44 bits, never 0), tags the arrival counters and cursors
   int q_lds_off;           // LDS byte offset of the query rows (past the largest block ring)
   // Tokens of the same call's append that go to the residual (pend_count 0: none): the work
   // item holding the residual of a (b, h) copies them there before it reads the residual.

@@ -313,15 +313,16 @@ def test_decode_is_deterministic():
 def test_decode_rotated_block_order_with_partial_block(fmt):
     """Each (batch, kv_head) visits its blocks rotated by a hashed offset; with 38 blocks (37
     full, the last holding 5 slots) the four (b, h) get rotations 0, 25, 6 and 31, which wrap
-    past the partial block, and it must still be the one whose tail slots are masked."""
-    R = 0 if fmt == "nvfp4" else 128
+    past the partial block, and it must still be the one whose tail slots are masked.  Every
+    token is quantized (residual 0), so every format has the partial block."""
     rng = np.random.default_rng(zlib.crc32(f"rot/{fmt}".encode()))
-    B, H, G, L = 2, 2, 4, 37 * 128 + 5 + R
-    p = Pair(1, B, H, L + 64, fmt, R)
+    B, H, G, L = 2, 2, 4, 37 * 128 + 5
+    p = Pair(1, B, H, L + 64, fmt, 0)
     k = rng.standard_normal((B, H, L, 128)).astype(np.float16)
     k[..., :4] *= 15
     v = rng.standard_normal((B, H, L, 128)).astype(np.float16)
     p.append(0, k, v)
+    assert p.gpu.layout(0, 1)[2] == L and L % 128 == 5       # 37 full blocks and a partial one
     p.check_bytes(0)
     q = (rng.standard_normal((B, H * G, 128)) / np.sqrt(128)).astype(np.float16)
     for sigma in (1 / np.sqrt(128), 1.0):
