@@ -21,7 +21,7 @@ REGION_RESIDUAL, REGION_YOUNG, REGION_OLD = 0, 1, 2
 # every symbol include/kvq.h declares
 EXPORTS = ("kvq_cache_bytes", "kvq_cache_create", "kvq_cache_destroy", "kvq_cache_reset", "kvq_append",
            "kvq_append_seq", "kvq_flush_residual", "kvq_decode_workspace_bytes", "kvq_decode_attn",
-           "kvq_append_decode_attn", "kvq_seq_len", "kvq_seq_info", "kvq_layout",
+           "kvq_append_decode_attn", "kvq_decode_attn_noalloc", "kvq_seq_len", "kvq_seq_info", "kvq_layout",
            "kvq_set_plan_only", "kvq_set_deterministic", "kvq_read_probe_sink_bytes", "kvq_read_probe",
            "kvq_last_error")
 
@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
     L.kvq_decode_workspace_bytes.argtypes = [vp, i32]; L.kvq_decode_workspace_bytes.restype = sz
     L.kvq_decode_attn.argtypes = [vp, i32, vp, i32, ctypes.c_float, vp, i32, vp, sz, vp]
     L.kvq_decode_attn.restype = ctypes.c_int
+    L.kvq_decode_attn_noalloc.argtypes = [vp, i32, vp, i32, ctypes.c_float, vp, i32, vp]
+    L.kvq_decode_attn_noalloc.restype = ctypes.c_int
     L.kvq_append_decode_attn.argtypes = [vp, i32, vp, vp, i64, vp, i32, ctypes.c_float, vp, i32, vp, sz, vp]
     L.kvq_append_decode_attn.restype = ctypes.c_int
     L.kvq_seq_len.argtypes = [vp, i32, P(i64), P(i64)]; L.kvq_seq_len.restype = ctypes.c_int
@@ -224,6 +226,18 @@ class Cache:
         _check(lib().kvq_decode_attn(self.h, layer, q.data_ptr(), q.shape[1], float(softmax_scale), out.data_ptr(),
                                      out_fp32, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                      _stream_ptr(stream)))
+
+    def decode_noalloc(self, layer: int, q, softmax_scale: float, out, stream=None):
+        """kvq_decode_attn_noalloc: decode with the library's per-GPU scratch as workspace."""
+        import torch
+        out_fp32 = 1 if out.dtype == torch.float32 else 0
+        _check(lib().kvq_decode_attn_noalloc(self.h, layer, q.data_ptr(), q.shape[1], float(softmax_scale),
+                                             out.data_ptr(), out_fp32, _stream_ptr(stream)))
+
+    def decode_noalloc_plan(self, layer: int, num_q_heads: int):
+        """Host-side checks of kvq_decode_attn_noalloc (plan-only caches: nothing is launched)."""
+        assert self.plan_only
+        _check(lib().kvq_decode_attn_noalloc(self.h, layer, 1 << 40, num_q_heads, 0.125, 1 << 40, 1, None))
 
     def append_decode(self, layer: int, k, v, q, softmax_scale: float, out, workspace, stream=None):
         """kvq_append_decode_attn: append k, v (fp16 [B, H, n, 128]) then attend with q."""

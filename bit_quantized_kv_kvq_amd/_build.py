@@ -8,7 +8,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvq.so")
-SOURCES = ["kvq_api.cpp", "kvq_quant.hip", "kvq_decode.hip", "kvq_probe.hip"]
+SOURCES = ["kvq_api.cpp", "kvq_quant.hip", "kvq_decode.hip", "kvq_probe.hip", "kvq_noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -892,6 +892,29 @@ int kvq_decode_attn(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_he
                     nullptr, 0, stream, ragged);
 }
 
+int kvq_decode_attn_noalloc(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_heads, float softmax_scale,
+                            void *out, int32_t out_fp32, void *stream) {
+  if (int e = check_cache(c, layer)) return e;
+  if (int e = check_decode_args(c, q, num_q_heads, softmax_scale, out)) return e;
+  if (!c->uniform(layer))
+    return fail(KVQ_ESTATE, "layer %d: the sequences have different lengths; kvq_decode_attn_noalloc serves "
+                "uniform batches only (kvq_decode_attn serves ragged ones)", layer);
+  if (c->st(layer, 0).length == 0) return fail(KVQ_ESTATE, "layer %d is empty", layer);
+  // the call's workspace (the same split as kvq_decode_attn's) must fit the scratch array
+  DecodeArgs a{};
+  a.B = c->cfg.batch; a.H = c->cfg.num_kv_heads; a.G = num_q_heads / c->cfg.num_kv_heads;
+  plan_decode(c, layer, a, nullptr);
+  const size_t need = counters_bytes(c) + partials_bytes(c, num_q_heads, a.items_total);
+  if (need > kNoAllocScratchBytes)
+    return fail(KVQ_ENOSPACE, "this call needs %zu bytes of workspace; the no-alloc scratch holds %zu", need,
+                kNoAllocScratchBytes);
+  if (c->plan_only) return KVQ_OK;
+  void *ws = nullptr;
+  if (int e = hip_check(noalloc_scratch(&ws, (hipStream_t)stream), "no-alloc scratch")) return e;
+  return run_decode(c, layer, q, num_q_heads, softmax_scale, out, out_fp32, ws, kNoAllocScratchBytes, nullptr, nullptr,
+                    nullptr, 0, stream, false);
+}
+
 int kvq_append_decode_attn(kvq_cache *c, int32_t layer, const void *k, const void *v, int64_t n_tokens, const void *q,
                            int32_t num_q_heads, float softmax_scale, void *out, int32_t out_fp32, void *workspace,
                            size_t ws_bytes, void *stream) {

@@ -167,6 +167,12 @@ struct DecodeArgs {
   int occ;
 };
 
+// Workspace of kvq_decode_attn_noalloc: a device array of this size per GPU (kvq_noalloc.hip).
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+// Device address of the current GPU's scratch array; the first call on a device looks it up
+// and enqueues its clearing on stream s.
+hipError_t noalloc_scratch(void **ptr, hipStream_t s);
+
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t s);
 hipError_t launch_residual_copy(const ResCopyArgs &a, hipStream_t s);
 // LDS bytes one decode workgroup needs for the segments in `a`.

@@ -163,6 +163,23 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t num_q_heads);
 int kvq_decode_attn(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_heads, float softmax_scale,
                     void *out, int32_t out_fp32, void *workspace, size_t ws_bytes, void *stream);
 
+/* kvq_decode_attn for callers that cannot allocate device memory (code under HIP graph
+   capture, tight serving loops, harnesses that forbid allocation): the same attention, the
+   same kernel and the same result, with the workspace taken from a library-owned scratch
+   array instead of an argument.  That array is a file-scope device array of 8 MiB
+   (8,388,608 bytes) per GPU, held until the process ends; its device address on the current
+   GPU is looked up on the first call there, which also enqueues its clearing on `stream`.
+   The call itself allocates nothing (no hipMalloc, hipFree or allocating library routine).
+   Every call on a GPU shares that GPU's array: calls that overlap in time on one GPU (on two
+   streams, or from two threads) race and must not be made.  Uniform batches only (every
+   sequence of the layer at the same length).  Errors: as kvq_decode_attn; KVQ_ENOSPACE when
+   the call's workspace (arrival counters, chunk cursors and split partials: about
+   batch * num_q_heads * 2 KB at most, more exactly kvq_decode_workspace_bytes' counters plus
+   528 bytes per query head and work item) exceeds the 8 MiB; KVQ_ESTATE for a ragged
+   batch or an empty layer; nothing is enqueued on any error but KVQ_EHIP. */
+int kvq_decode_attn_noalloc(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_heads, float softmax_scale,
+                            void *out, int32_t out_fp32, void *stream);
+
 /* One decode step of `layer` in one call: exactly kvq_append(c, layer, k, v, n_tokens, stream)
    followed by kvq_decode_attn(c, layer, q, ...), the step that every generated token makes (it
    appends its K/V and attends over the whole history: page "NVFP4 KV缓存技术详解" §2.1, the

@@ -282,3 +282,27 @@ def test_read_probe_rejects_bad_arguments(case):
     rc = L.kvq_read_probe(ctypes.c_void_p(buf or None), nbytes, ctypes.c_void_p(sink or None), sink_bytes, None)
     assert rc == kvq.KVQ_EINVAL
     assert L.kvq_last_error()
+
+
+def test_noalloc_entry_checks_before_enqueue():
+    """kvq_decode_attn_noalloc (plan-only: nothing is launched): the decode checks, uniform
+    batches only, and a call whose workspace exceeds the 8 MiB scratch is refused."""
+    L, P = kvq.lib(), 1 << 40
+    c = kvq.Cache(kvq.make_config(2, 2, 2, 300, "int4", 128), plan_only=True)
+    f = L.kvq_decode_attn_noalloc
+    assert f(c.h, 0, P, 8, 1.0, P, 1, None) == kvq.KVQ_ESTATE            # empty layer
+    c.append_plan(0, 200)
+    assert f(c.h, 0, P, 3, 1.0, P, 1, None) == kvq.KVQ_EINVAL            # heads not a multiple
+    assert f(c.h, 0, 0, 8, 1.0, P, 1, None) == kvq.KVQ_EINVAL            # q NULL
+    assert f(c.h, 0, P + 2, 8, 1.0, P, 1, None) == kvq.KVQ_EINVAL        # misaligned
+    assert f(c.h, 0, P, 8, 0.0, P, 1, None) == kvq.KVQ_EINVAL            # scale
+    assert f(c.h, 2, P, 8, 1.0, P, 1, None) == kvq.KVQ_EINVAL            # layer
+    assert f(c.h, 0, P, 8, 1.0, P, 1, None) == kvq.KVQ_OK
+    c.append_seq_plan(1, 0, 50)                                           # ragged layer
+    assert f(c.h, 1, P, 8, 1.0, P, 1, None) == kvq.KVQ_ESTATE
+    # 4096 (batch, kv_head) pairs x 16 query heads: one work item each, 34.6 MB of partials
+    big = kvq.Cache(kvq.make_config(1, 512, 8, 300, "int4", 128), plan_only=True)
+    big.append_plan(0, 10)
+    assert f(big.h, 0, P, 8 * 16, 1.0, P, 1, None) == kvq.KVQ_ENOSPACE
+    assert b"no-alloc scratch" in L.kvq_last_error()
+    assert f(big.h, 0, P, 8 * 2, 1.0, P, 1, None) == kvq.KVQ_OK          # 4.3 MB fits
