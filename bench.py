@@ -1,17 +1,22 @@
 """Decode-step benchmark of the quantized KV cache on one MI355X.
 
-A step is, for every layer: append one new token (quantize + pack when the fp16 residual is
-full, else an fp16 copy into the residual) and one fused dequant + decode-attention call over
-the whole cache.  Inputs are seeded synthetic K/V/Q drawn on the GPU before the timed region.
+A step is, for every layer: append the step's new token(s) (quantize + pack when the fp16
+residual is full or the residual length is 0, else an fp16 copy into the residual) and one
+fused dequant + decode-attention call over the whole cache.  Inputs are seeded synthetic K/V/Q
+drawn on the GPU before the timed region.
 
-Default workload: 32 layers, batch 8, 32 query / 8 KV heads, head_dim 128, 131072 cached
+Headline workload: 32 layers, batch 8, 32 query / 8 KV heads, head_dim 128, 131072 cached
 tokens per sequence in INT4 affine (group 64, fp16 S/Z, 128-token fp16 residual), Student-t
-(nu = 4) K and Gaussian V, consecutive decode steps with append and residual flushes.
+(nu = 4) K and Gaussian V, consecutive decode steps with append and residual flushes.  The
+prefill is sized so that the first timed step is the one that flushes the full residual.
 
 Output: one JSON line.  `value` is the effective HBM GB/s of the cache read (codes + scales +
 zero points + fp16 residual) summed over the timed steps, divided by their wall time.
 `roofline` gives the decode-attention call alone, timed with HIP events on the stream it is
-launched on.  `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+launched on.  `cpu_baseline` times the CPU oracle on a bounded sample of the same workload, on
+a pool of host processes.  With no --workload, `per_config` holds the other workloads measured
+in the same run: the 1K single layer (MALL-hot and cold), the Llama-2-shaped MHA step, the
+32K NVFP4 GQA-8 step, the 128K INT2 step and the 256K tier workload with its bulk prefill.
 """
 from __future__ import annotations
 
@@ -31,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 DECODE_SRC = os.path.join(ROOT, "bit_quantized_kv_kvq_amd", "csrc", "kvq_decode.hip")
+POOL_CAP = 16           # host worker processes at most (one GPU's share of a box's cores)
 
 # workload name -> (config id in kvq_synth.WORKLOADS, young format override)
 WORKLOADS = {
@@ -45,6 +51,8 @@ RAGGED = {"c4-ragged"}
 # workloads whose young blocks move to the old tier as they age (demote_young), and the
 # timed steps they default to (a block of one (batch, kv_head) ages every 128 one-token steps)
 DEMOTE_STEPS = {"c5-demote": 320}
+# the other workloads of a default run: (steps, warmup, (batch, kv_head) pairs for the oracle)
+PER_CONFIG = [("c2", 8, 2, 32), ("c3", 8, 2, 12), ("c4-int2", 20, 5, 32), ("c5", 16, 0, 8)]
 
 
 def bytes_per_token(fmt: str) -> float:
@@ -93,40 +101,66 @@ def traffic_from_profiles(workload: str):
     return float(val.group(1))
 
 
-def cpu_baseline(samples, wl, sigma, budget_s: float):
-    """Time the CPU oracle on (layer 0, b, kv_head) samples of the final cache state.
+# ----------------------------------------------------------------------------- CPU oracle pool
 
-    samples: list of (b, h, k chunks, v chunks, q16 [G,128], gpu_out [G,128] fp32); the chunks
-    (fp16 [n_i, 128]) are appended in order, as the GPU cache received them.
-    Returns (baseline dict, max relative error of the GPU output on the samples)."""
+def _worker_ready(_):
+    return os.getpid()
+
+
+def oracle_task(spec):
+    """One (batch, kv_head) pair of layer 0 through the CPU oracle: quantize every token it
+    received (chunks in order, as the GPU cache did) and attend in float64.  Runs in a worker
+    process (one BLAS thread).  Returns (seconds, out [G, 128] float64, algorithmic bytes)."""
     from threadpoolctl import threadpool_limits
     from oracle.cache import LayerCache
     from oracle.attention import decode_layer
-    used = 0
-    t_total = 0.0
-    bytes_total = 0.0
-    worst = 0.0
+    fmt, R, old_fmt, old_after, demote, kch, vch, q16, sigma = spec
     with threadpool_limits(limits=1):
-        for (b, h, kch, vch, q16, got) in samples:
-            t0 = time.perf_counter()
-            lc = LayerCache(wl["fmt"], wl["R"], wl["old_fmt"], wl["old_after"], wl.get("demote", False))
-            for kc, vc in zip(kch, vch):
-                lc.append(kc[None, None], vc[None, None])
-            want = decode_layer(lc, q16[None], sigma)[0]
-            dt = time.perf_counter() - t0
-            t_total += dt
-            n_tok = lc.sched.length
-            nq_y, nq_o, nr = len(lc.tier_tokens("young")), len(lc.sched.old), len(lc.sched.residual)
-            bytes_total += nq_o * bytes_per_token(lc.old_fmt) + nq_y * bytes_per_token(lc.fmt) + nr * 512.0
-            worst = max(worst, float(np.abs(got - want).max() / np.abs(want).max()))
-            used += 1
-            if t_total >= budget_s:
-                break
-    return {"value": bytes_total / t_total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"layer 0, {used} (batch, kv_head) pair(s) x {n_tok} tokens at the final state: "
-                      f"quantize every token + fp64 attention of the {samples[0][4].shape[0]} query heads; "
-                      f"{t_total:.1f} s on 1 host thread"}, worst
+        t0 = time.perf_counter()
+        lc = LayerCache(fmt, R, old_fmt, old_after, demote)
+        for kc, vc in zip(kch, vch):
+            lc.append(kc[None, None], vc[None, None])
+        out = decode_layer(lc, q16[None], sigma)[0]
+        dt = time.perf_counter() - t0
+    nb = (len(lc.sched.old) * bytes_per_token(lc.old_fmt) + len(lc.tier_tokens("young")) * bytes_per_token(lc.fmt)
+          + len(lc.sched.residual) * 512.0)
+    return dt, out, nb
 
+
+def start_pool():
+    """Worker processes for the oracle, all forked here, before this process touches the GPU
+    (torch is not imported yet), so that no worker holds GPU state; they live until the pool
+    is closed.  At most POOL_CAP workers, and no more than the cores this process may run on."""
+    import multiprocessing as mp
+    n = max(1, min(POOL_CAP, len(os.sched_getaffinity(0))))
+    pool = mp.get_context("fork").Pool(n)
+    pids = set(pool.map(_worker_ready, range(4 * n), chunksize=1))
+    return pool, n, len(pids)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def run_oracle(pool, specs, gpu_outs):
+    """Oracle on the sampled pairs in the pool: (wall seconds, summed worker seconds, bytes,
+    max |gpu - oracle| / max |oracle| over the samples)."""
+    t0 = time.perf_counter()
+    res = pool.map(oracle_task, specs, chunksize=1)
+    wall = time.perf_counter() - t0
+    worst = 0.0
+    for (dt, want, nb), got in zip(res, gpu_outs):
+        worst = max(worst, float(np.abs(got - want).max() / np.abs(want).max()))
+    return wall, sum(r[0] for r in res), sum(r[2] for r in res), worst
+
+
+# ----------------------------------------------------------------------------- probes
 
 def copy_probe():
     """A plain copy of a known size (1 GiB), for scaling the HBM byte counters."""
@@ -220,46 +254,22 @@ def log(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 64; 320 for c5-demote)")
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c4-int4", choices=sorted(WORKLOADS))
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
-    ap.add_argument("--cpu-pairs", type=int, default=48, help="(batch, kv_head) pairs of layer 0 kept for the oracle")
-    ap.add_argument("--probe", choices=["copy"], default=None)
-    ap.add_argument("--separate-append", action="store_true",
-                    help="kvq_append then kvq_decode_attn per layer (default: kvq_append_decode_attn)")
-    ap.add_argument("--study", choices=["noise"], default=None,
-                    help="noise: decode error of every format against the fp16 cache vs cached length")
-    ap.add_argument("--study-lengths", default="1024,4096,16384,65536,131072")
-    ap.add_argument("--study-queries", type=int, default=8)
-    args = ap.parse_args()
+# ----------------------------------------------------------------------------- one workload
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this path runs on one GPU; (batch, kv_head) pairs, layers and token splits shard "
-              "without exchange except a final LSE merge, which is not built here. Use --gpus 1.",
-              file=sys.stderr)
-        sys.exit(2)
+def measure(name: str, steps: int, warmup: int, n_pairs: int, separate_append: bool = False):
+    """Prefill, warm up, time `steps` decode steps of workload `name`.
 
+    Returns (result dict, oracle specs of the sampled pairs, GPU fp32 outputs of those pairs).
+    With a residual and one token per step, the prefill holds T - warmup tokens, so that after
+    the warmup the cache holds the workload's T tokens with a full residual and the first timed
+    step is the one that flushes it (reported separately as flush_step_ms)."""
     import torch
-    if args.probe == "copy":
-        copy_probe()
-        return
-    if args.study == "noise":
-        noise_study([int(x) for x in args.study_lengths.split(",")], args.study_queries)
-        return
-
     import bit_quantized_kv_kvq_amd as kvq
     import kvq_synth as syn
 
-    demote = args.workload in DEMOTE_STEPS
-    ragged = args.workload in RAGGED
-    if args.steps is None:
-        args.steps = DEMOTE_STEPS.get(args.workload, 64)
-    cid, fmt_over = WORKLOADS[args.workload]
+    demote = name in DEMOTE_STEPS
+    ragged = name in RAGGED
+    cid, fmt_over = WORKLOADS[name]
     W = syn.WORKLOADS[cid]
     fmt = fmt_over or W.fmt
     old_fmt = W.old_fmt or fmt
@@ -267,31 +277,28 @@ def main():
     G = Hq // H
     sigma = 1.0 / np.sqrt(128.0)
     per_step = max(1, W.append_per_step)
-    n_steps = args.warmup + args.steps
+    n_steps = warmup + steps
     dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    flush_first = R > 0 and per_step == 1 and not ragged and not demote and warmup < R
+    T0 = T - warmup if flush_first else T
 
-    probe = read_probe_gbs()
-
-    cfg = kvq.make_config(L, B, H, T + n_steps * per_step + 1, fmt, R, W.old_fmt, W.old_after, demote=demote)
+    cfg = kvq.make_config(L, B, H, T0 + n_steps * per_step + 1, fmt, R, W.old_fmt, W.old_after, demote=demote)
     cache = kvq.Cache(cfg)
-    samples_bh = [(b, h) for b in range(B) for h in range(H)][:args.cpu_pairs]
+    samples_bh = [(b, h) for b in range(B) for h in range(H)][:n_pairs]
     host_hist = {bh: ([], []) for bh in samples_bh}
-
-    # ragged: sequence b keeps the first lens[b] of its T drawn tokens
-    lens = [T * (b + 1) // B for b in range(B)] if ragged else [T] * B
+    lens = [T0 * (b + 1) // B for b in range(B)] if ragged else [T0] * B
     if ragged:
         assert W.old_after == 0 and R > 0, "the ragged step tracker models one tier with a residual"
 
-    # ---- untimed state: bulk prefill of every layer (one append of T tokens, or one per
+    # ---- untimed state: bulk prefill of every layer (one append of T0 tokens, or one per
     # sequence when ragged); HIP events around each layer's appends give the bulk quantize rate
     # (fp16 read + packed bytes written)
     t_prefill = time.perf_counter()
     pre_events = []
     for l in range(L):
-        k = syn.draw_k_dev(cid, l, B, H, T, W.kdist)
-        v = syn.draw_v_dev(cid, l, B, H, T)
+        k = syn.draw_k_dev(cid, l, B, H, T0, W.kdist)
+        v = syn.draw_v_dev(cid, l, B, H, T0)
         if l == 0:
             for (b, h) in samples_bh:
                 host_hist[(b, h)][0].append(k[b, h, :lens[b]].cpu().numpy())
@@ -306,16 +313,13 @@ def main():
         e1.record(stream)
         pre_events.append((e0, e1))
         del k, v
-        if l % 8 == 7 or l == L - 1:
+        if l % 16 == 15 or l == L - 1:
             torch.cuda.synchronize()
-            log(f"prefill: {l + 1}/{L} layers, {time.perf_counter() - t_prefill:.1f} s")
     torch.cuda.synchronize()
     t_prefill = time.perf_counter() - t_prefill
     pre_ms = float(sum(a.elapsed_time(b) for a, b in pre_events))
     pre_bytes = float(L * H * sum(lens) * 2 * 128 * 2) + sum(decode_bytes(cache, l, fmt, old_fmt, ragged)
                                                                 for l in range(L))
-    # ragged: per (layer, sequence) quantized tokens and residual fill, tracked here (a ctypes
-    # query per sequence and layer inside the timed loop would cost host time of its own)
     if ragged:
         track = [[[cache.seq_info(l, b)["young_tokens"], cache.seq_info(l, b)["residual"]] for b in range(B)]
                  for l in range(L)]
@@ -335,36 +339,33 @@ def main():
     outs = [torch.empty((B, Hq, 128), dtype=torch.float16, device=dev) for _ in range(L)]
     torch.cuda.synchronize()
 
-    # HIP events around one decode launch per timed step (layer s mod L of step s, so that the
-    # sample turns through the layers), created (and each recorded once) before the timed
-    # region so that no event set-up falls inside it.  Events around every launch would cost
-    # about 3 % of the step time themselves (measured), which the wall clock would then include.
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    # and around each append that demotes a block (demotion workloads), likewise made up front
-    dem_events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(L * (args.steps * per_step // 128 + 2) if demote else 0)]
-    for e0, e1 in events + dem_events:
+    # HIP events, all created (and each recorded once) before the timed region: around each
+    # timed step; around one decode launch per timed step (layer s mod L of step s) and around
+    # the separate append of that layer when the step makes one.  Events around every launch
+    # would cost about 3 % of the step time themselves (measured).
+    def mk(n):
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    step_ev, dec_ev, app_ev = mk(steps), mk(steps), mk(steps)
+    dem_ev = mk(L * (steps * per_step // 128 + 2) if demote else 0)
+    for e0, e1 in step_ev + dec_ev + app_ev + dem_ev:
         e0.record(stream)
         e1.record(stream)
-    dem_used = []
+    app_used, dem_used = [], []
 
     def demotes(l):
-        """Whether appending this step's tokens to layer l (without a flush) moves a young
-        block to the old tier.  The positions stay in order here (one prefill, then steps),
-        so the first live young block holds positions [old, old + 128)."""
         if not demote:
             return False
         n_old = cache.layout(l, kvq.REGION_OLD)[2]
         return (cache.layout(l, kvq.REGION_YOUNG)[2] >= 128
                 and n_old + 128 <= cache.seq_len(l)[0] + per_step - W.old_after)
 
-    def step(s, ev=None, nbytes=None, timed=None):
+    timed_bytes = []
+
+    def step(s, i=None, nbytes=None):
+        timed = s % L if i is not None else -1
+        if i is not None:
+            step_ev[i][0].record(stream)
         for l in range(L):
-            pair = ev if ev is not None and l == timed else None
-            # a step whose tokens go straight to the residual is one call and one launch (the
-            # copy runs inside the decode launch); a step that quantizes (a full residual, or
-            # R = 0) appends first, so that the timed bracket always holds one decode launch
             if ragged:
                 quantizes = any(t[1] + per_step > R for t in track[l])
                 for t in track[l]:
@@ -375,55 +376,107 @@ def main():
                         t[1] += per_step
             else:
                 quantizes = R == 0 or cache.seq_len(l)[1] + per_step > R or demotes(l)
-            if args.separate_append or quantizes:
-                dem = nbytes is not None and demotes(l) and len(dem_used) < len(dem_events)
+            # a step whose tokens go straight to the residual is one call and one launch (the
+            # copy runs inside the decode launch); a step that quantizes appends first
+            if separate_append or quantizes:
+                dem = nbytes is not None and demotes(l) and len(dem_used) < len(dem_ev)
                 if dem:
                     fb = cache.first_block(l, kvq.REGION_YOUNG)
-                    dem_events[len(dem_used)][0].record(stream)
+                    dem_ev[len(dem_used)][0].record(stream)
+                if l == timed:
+                    app_ev[i][0].record(stream)
                 cache.append(l, knew[s][l], vnew[s][l])
+                if l == timed:
+                    app_ev[i][1].record(stream)
+                    app_used.append(i)
                 if dem:
-                    dem_events[len(dem_used)][1].record(stream)
+                    dem_ev[len(dem_used)][1].record(stream)
                     dem_used.append(cache.first_block(l, kvq.REGION_YOUNG) - fb)
-                if pair is not None:
-                    pair[0].record(stream)
+                if l == timed:
+                    dec_ev[i][0].record(stream)
                 cache.decode(l, qs[s][l], sigma, outs[l], ws)
             else:
-                if pair is not None:
-                    pair[0].record(stream)
+                if l == timed:
+                    dec_ev[i][0].record(stream)
                 cache.append_decode(l, knew[s][l], vnew[s][l], qs[s][l], sigma, outs[l], ws)
-            if pair is not None:
-                pair[1].record(stream)
+            if l == timed:
+                dec_ev[i][1].record(stream)
             if nbytes is not None:
                 nbytes.append(H * sum(t[0] * bpt + t[1] * 512.0 for t in track[l]) if ragged
                               else decode_bytes(cache, l, fmt, old_fmt))
-                if pair is not None:
+                if l == timed:
                     timed_bytes.append(nbytes[-1])
+        if i is not None:
+            step_ev[i][1].record(stream)
 
-    log("step inputs ready; warmup")
-    for s in range(args.warmup):
+    for s in range(warmup):
         step(s)
     torch.cuda.synchronize()
+    if flush_first:
+        assert cache.seq_len(0) == (T, R), cache.seq_len(0)
 
-    nbytes, timed_bytes = [], []
+    nbytes = []
     gc.collect()
     gc.disable()            # no collector pause inside the timed region
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i, s in enumerate(range(args.warmup, n_steps)):
-        step(s, events[i], nbytes, s % L)
+    for i, s in enumerate(range(warmup, n_steps)):
+        step(s, i, nbytes)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gc.enable()
-    if ragged:   # the tracker agrees with the library's counters
+    if ragged:
         for l in range(L):
             assert sum(H * (t[0] * bpt + t[1] * 512.0) for t in track[l]) == decode_bytes(cache, l, fmt, old_fmt, True)
-    log(f"timed {args.steps} steps in {wall:.3f} s")
 
-    dec_ms = np.array([a.elapsed_time(b) for a, b in events])
-    nbytes = np.array(nbytes)
-    total_bytes = float(nbytes.sum())
-    value = total_bytes / wall / 1e9
+    step_ms = np.array([a.elapsed_time(b) for a, b in step_ev])
+    dec_ms = np.array([a.elapsed_time(b) for a, b in dec_ev])
+    app_ms = np.array([app_ev[i][0].elapsed_time(app_ev[i][1]) for i in app_used])
+    total_bytes = float(np.sum(nbytes))
     achieved = float(np.mean(timed_bytes) / (dec_ms.mean() * 1e-3) / 1e9)
+    res = {
+        "workload": (W.name if fmt_over is None else W.name.replace(W.fmt, fmt))
+                    + (", young blocks demoted as they age" if demote else "")
+                    + (f", ragged: sequence b holds {T0}(b+1)/{B} tokens" if ragged else ""),
+        "layers": L, "batch": B, "q_heads": Hq, "kv_heads": H, "head_dim": 128,
+        "cached_tokens": lens if ragged else T, "format": fmt, "old_format": W.old_fmt, "residual": R,
+        "append_per_step": per_step, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(wall / steps * 1e3, 4),
+        "steps_per_s": round(steps / wall, 2),
+        "gbs": round(total_bytes / wall / 1e9, 1),
+        "pct_hbm_peak": round(100 * total_bytes / wall / 1e9 / HBM_PEAK_GBS, 2),
+        "decode_launch_us": round(float(dec_ms.mean()) * 1e3, 2),
+        "decode_bytes_per_launch": round(float(np.mean(timed_bytes))),
+        "decode_gbs": round(achieved, 1),
+        "decode_frac": round(achieved / HBM_PEAK_GBS, 4),
+        "prefill_s": round(t_prefill, 2),
+        "prefill_quantize_ms": round(pre_ms, 2),
+        "prefill_quantize_gbs": round(pre_bytes / (pre_ms * 1e-3) / 1e9, 1),
+        "step_event_ms_mean": round(float(step_ms.mean()), 4),
+    }
+    if app_used:
+        res["append_us"] = round(float(app_ms.mean()) * 1e3, 2)
+        res["append_note"] = ("HIP events around one layer's kvq_append per timed step (" +
+                              ("quantize of the step's token" if R == 0 else
+                               "flush of the full residual + copy of the new tokens" if per_step > 1 or flush_first
+                               else "residual copy") + ")")
+    if flush_first:
+        res["flush_step_ms"] = round(float(step_ms[0]), 4)
+        res["plain_step_ms_mean"] = round(float(step_ms[1:].mean()), 4) if steps > 1 else None
+        res["flush_note"] = ("timed step 0 appends to a full residual in every layer: each layer's append "
+                             "quantizes the 128 residual tokens into the young tier, then decodes")
+        res["flush_append_us"] = round(float(app_ms[0]) * 1e3, 2) if app_used and app_used[0] == 0 else None
+    if demote:
+        blk_bytes = B * H * 128 * (bytes_per_token(fmt) + bytes_per_token(old_fmt))
+        dm = np.array([dem_ev[i][0].elapsed_time(dem_ev[i][1]) for i in range(len(dem_used))])
+        nblk = int(sum(dem_used))
+        res["demote_young"] = 1
+        res["demotion"] = {"appends": len(dem_used), "blocks": nblk,
+                           "append_us": round(float(dm.mean()) * 1e3, 2) if dem_used else None,
+                           "bytes_per_block": round(blk_bytes),
+                           "gbs": round(blk_bytes * nblk / (dm.sum() * 1e-3) / 1e9, 1) if nblk else None,
+                           "note": "event brackets around the whole append call that demotes (its residual "
+                                   "copy included)"}
 
     # ---- parity on sampled outputs at full size: one more fp32 decode of layer 0
     out32 = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
@@ -431,61 +484,216 @@ def main():
     torch.cuda.synchronize()
     out_h = out32.cpu().numpy().astype(np.float64)
     q_h = qs[n_steps - 1][0].cpu().numpy()
-    samples = []
+    specs, gpu_outs = [], []
     for (b, h) in samples_bh:
-        samples.append((b, h, host_hist[(b, h)][0], host_hist[(b, h)][1], q_h[b, h * G:(h + 1) * G],
-                        out_h[b, h * G:(h + 1) * G]))
+        specs.append((fmt, R, W.old_fmt, W.old_after, demote, host_hist[(b, h)][0], host_hist[(b, h)][1],
+                      q_h[b, h * G:(h + 1) * G], sigma))
+        gpu_outs.append(out_h[b, h * G:(h + 1) * G])
+    res["_pairs_per_step"] = L * B * H
+    del cache, ws, outs, knew, vnew, qs, out32
+    gc.collect()
+    torch.cuda.empty_cache()
+    return res, specs, gpu_outs
+
+
+def measure_c1(n_copies: int = 200, reps: int = 200):
+    """The 1K single-layer workload: decode of the prefilled state (1024 INT4 + 128 fp16 tokens;
+    the step's token is the last residual token), MALL-hot (one cache, repeated) and cold (the
+    same call rotated over n_copies caches, ~1.7 MB each, more than the 256 MiB of MALL), each
+    the mean over `reps` calls between two synchronizations; then the 1-token append timed
+    separately on a full residual (a flush) and on a part-filled one (an fp16 copy)."""
+    import torch
+    import bit_quantized_kv_kvq_amd as kvq
+    import kvq_synth as syn
+    cid = 1
+    W = syn.WORKLOADS[cid]
+    B, Hq, H, T, R = W.batch, W.num_q_heads, W.num_kv_heads, W.prefill, W.residual_len
+    G = Hq // H
+    sigma = 1.0 / np.sqrt(128.0)
+    k = syn.draw_k_dev(cid, 0, B, H, T, W.kdist)
+    v = syn.draw_v_dev(cid, 0, B, H, T)
+    q = syn.draw_q_dev(cid, 0, B, Hq)
+    caches = [kvq.Cache(kvq.make_config(1, B, H, T + 64, W.fmt, R)) for _ in range(n_copies)]
+    for c in caches:
+        c.append(0, k, v)
+    ws = torch.empty(caches[0].workspace_bytes(Hq), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, Hq, 128), dtype=torch.float16, device="cuda")
+    nb = decode_bytes(caches[0], 0, W.fmt, W.fmt)
+    for _ in range(5):
+        caches[0].decode(0, q, sigma, out, ws)
+    torch.cuda.synchronize()
+
+    def timed(seq):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        for c in seq:
+            c.decode(0, q, sigma, out, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / len(seq), e0.elapsed_time(e1) * 1e-3 / len(seq)
+
+    hot_wall, hot_ev = timed([caches[0]] * reps)
+    timed([caches[i % n_copies] for i in range(n_copies)])          # every copy read once first
+    cold_wall, cold_ev = timed([caches[i % n_copies] for i in range(reps)])
+    # the parity sample (fp32 out of the first cache) and the 1-token appends
+    out32 = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")
+    caches[0].decode(0, q, sigma, out32, ws)
+    torch.cuda.synchronize()
+    gpu = out32.cpu().numpy().astype(np.float64)
+    kh, vh, qh = k.cpu().numpy(), v.cpu().numpy(), q.cpu().numpy()
+    specs = [(W.fmt, R, None, 0, False, [kh[0, h]], [vh[0, h]], qh[0, h * G:(h + 1) * G], sigma) for h in range(H)]
+    gpu_outs = [gpu[0, h * G:(h + 1) * G] for h in range(H)]
+    app = []
+    for s in range(9):
+        kn = syn.draw_k_dev(cid, 0, B, H, 1, W.kdist, syn.STREAM_K_APPEND, s)
+        vn = syn.draw_v_dev(cid, 0, B, H, 1, syn.STREAM_V_APPEND, s)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        caches[1].append(0, kn, vn)
+        e1.record()
+        torch.cuda.synchronize()
+        app.append(e0.elapsed_time(e1) * 1e3)
+    res = {
+        "workload": W.name, "layers": 1, "batch": B, "q_heads": Hq, "kv_heads": H, "cached_tokens": T,
+        "format": W.fmt, "residual": R, "decode_bytes_per_launch": round(nb),
+        "hot": {"decode_us": round(hot_ev * 1e6, 2), "wall_us_per_call": round(hot_wall * 1e6, 2),
+                "gbs": round(nb / hot_ev / 1e9, 1), "decode_frac": round(nb / hot_ev / 1e9 / HBM_PEAK_GBS, 5),
+                "steps_per_s": round(1.0 / hot_wall, 1),
+                "note": f"one cache decoded {reps} times back to back (its {nb / 1e6:.2f} MB stay in the MALL)"},
+        "cold": {"decode_us": round(cold_ev * 1e6, 2), "wall_us_per_call": round(cold_wall * 1e6, 2),
+                 "gbs": round(nb / cold_ev / 1e9, 1), "decode_frac": round(nb / cold_ev / 1e9 / HBM_PEAK_GBS, 5),
+                 "steps_per_s": round(1.0 / cold_wall, 1),
+                 "note": f"calls rotated over {n_copies} copies ({n_copies * nb / 1e6:.0f} MB, above the 256 MiB MALL)"},
+        "append_1_flush_us": round(app[0], 2),
+        "append_1_us": round(float(np.mean(app[1:])), 2),
+        "append_note": "HIP events around kvq_append of one token: first on the full residual (quantize of "
+                       "the 128 residual tokens + copy), then 8 more (fp16 copy into the residual)",
+        "_pairs_per_step": B * H,
+    }
+    del caches, ws, out, out32
+    gc.collect()
+    torch.cuda.empty_cache()
+    return res, specs, gpu_outs
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 64; 320 for c5-demote)")
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS),
+                    help="one workload alone (default: the 128K INT4 headline plus every other workload)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-pairs", type=int, default=48, help="(batch, kv_head) pairs of layer 0 for the oracle")
+    ap.add_argument("--probe", choices=["copy"], default=None)
+    ap.add_argument("--separate-append", action="store_true",
+                    help="kvq_append then kvq_decode_attn per layer (default: kvq_append_decode_attn)")
+    ap.add_argument("--study", choices=["noise"], default=None,
+                    help="noise: decode error of every format against the fp16 cache vs cached length")
+    ap.add_argument("--study-lengths", default="1024,4096,16384,65536,131072")
+    ap.add_argument("--study-queries", type=int, default=8)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this path runs on one GPU; (batch, kv_head) pairs, layers and token splits shard "
+              "without exchange except a final LSE merge, which is not built here. Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    want_cpu = not args.no_cpu_baseline and args.probe is None and args.study is None
+    pool = None
+    if want_cpu:
+        pool, n_workers, n_pids = start_pool()      # before anything touches the GPU
+        log(f"oracle pool: {n_workers} worker processes ({n_pids} answered)")
+
+    import torch
+    if args.probe == "copy":
+        copy_probe()
+        return
+    if args.study == "noise":
+        noise_study([int(x) for x in args.study_lengths.split(",")], args.study_queries)
+        return
+
+    name = args.workload or "c4-int4"
+    per_config = args.workload is None
+    if args.steps is None:
+        args.steps = DEMOTE_STEPS.get(name, 64)
+    torch.cuda.set_device(0)
+    probe = read_probe_gbs()
+
+    log(f"{name}: prefill, {args.warmup} warmup + {args.steps} timed steps")
+    head, specs, gouts = measure(name, args.steps, args.warmup, args.cpu_pairs, args.separate_append)
+    head_oracle = run_oracle(pool, specs, gouts) if want_cpu else None
 
     line = {
         "metric": "fused dequant+decode-attn effective GB/s (% HBM peak); decode steps/s",
-        "value": round(value, 1),
+        "value": head["gbs"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": f"{fmt}-codes/fp16-operands/fp32-accum",
+        "dtype": f"{head['format']}-codes/fp16-operands/fp32-accum",
         "data": "synthetic (seeded, drawn on the GPU)",
-        "config": {"workload": (W.name if fmt_over is None else W.name.replace(W.fmt, fmt))
-                   + (", young blocks demoted as they age" if demote else "")
-                   + (f", ragged: sequence b holds {T}(b+1)/{B} tokens" if ragged else ""),
-                   "layers": L, "batch": B, "q_heads": Hq, "kv_heads": H, "head_dim": 128,
-                   "cached_tokens": lens if ragged else T, "format": fmt, "old_format": W.old_fmt, "residual": R,
-                   "append_per_step": per_step, "parallelism": "none (1 GPU)"},
-        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "decode_steps_per_s": round(args.steps / wall, 2),
+        "config": {k: head[k] for k in ("workload", "layers", "batch", "q_heads", "kv_heads", "head_dim",
+                                        "cached_tokens", "format", "old_format", "residual", "append_per_step")}
+                  | {"parallelism": "none (1 GPU)"},
+        "pct_hbm_peak": head["pct_hbm_peak"],
+        "decode_steps_per_s": head["steps_per_s"],
         "read_probe_gbs": round(probe, 1),
-        "prefill_s": round(t_prefill, 2),
-        "prefill_quantize_ms": round(pre_ms, 2),
-        "prefill_quantize_gbs": round(pre_bytes / (pre_ms * 1e-3) / 1e9, 1),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(args.workload),
+        "roofline": {"bound": "hbm", "achieved": head["decode_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": head["decode_frac"], "traffic": traffic_from_profiles(name),
                      "kernel": "decode_kernel (one launch per kvq_append_decode_attn / kvq_decode_attn call)",
-                     "launch_us": round(float(dec_ms.mean()) * 1e3, 2),
-                     "bytes_per_launch": round(float(np.mean(timed_bytes))),
-                     "timed_launches": int(dec_ms.size)},
+                     "launch_us": head["decode_launch_us"], "bytes_per_launch": head["decode_bytes_per_launch"],
+                     "timed_launches": args.steps},
     }
-    if demote:
-        # each demoted block: one young block read and one old block written per (batch, kv_head)
-        blk_bytes = B * H * 128 * (bytes_per_token(fmt) + bytes_per_token(old_fmt))
-        dem_ms = np.array([dem_events[i][0].elapsed_time(dem_events[i][1]) for i in range(len(dem_used))])
-        nblk = int(sum(dem_used))
-        line["config"]["demote_young"] = 1
-        line["demotion"] = {"appends": len(dem_used), "blocks": nblk,
-                            "append_us": round(float(dem_ms.mean()) * 1e3, 2) if dem_used else None,
-                            "bytes_per_block": round(blk_bytes),
-                            "gbs": round(blk_bytes * nblk / (dem_ms.sum() * 1e-3) / 1e9, 1) if nblk else None,
-                            "note": "event brackets around the whole append call that demotes (its residual "
-                                    "copy included)"}
-    if not args.no_cpu_baseline:
-        wl = {"fmt": fmt, "R": R, "old_fmt": W.old_fmt, "old_after": W.old_after, "demote": demote}
-        log("cpu baseline (oracle)")
-        base, err = cpu_baseline(samples, wl, sigma, args.cpu_budget)
-        line["cpu_baseline"] = base
+    for k in ("prefill_s", "prefill_quantize_ms", "prefill_quantize_gbs", "append_us", "append_note", "flush_step_ms",
+              "plain_step_ms_mean", "flush_append_us", "flush_note", "demote_young", "demotion"):
+        if k in head:
+            line[k] = head[k]
+    model = cpu_model()
+    if want_cpu:
+        wall, cpu_s, nb, err = head_oracle
+        n = len(specs)
+        line["cpu_baseline"] = {
+            "value": round(nb / wall / 1e9, 4), "unit": "GB/s", "cores": n_workers, "kind": "oracle",
+            "cpu_model": model,
+            "s_per_step_extrapolated": round(wall / n * head["_pairs_per_step"], 1),
+            "sample": f"layer 0, {n} (batch, kv_head) pairs at the final state, each re-quantizing its "
+                      f"{head['cached_tokens']} + steps tokens and attending in float64, on {n_workers} worker "
+                      f"processes (one BLAS thread each): {wall:.1f} s wall, {cpu_s:.1f} s of worker time; the "
+                      f"full step ({head['_pairs_per_step']} pairs) is extrapolated from that rate"}
         line["sample_parity_max_rel_err"] = float(f"{err:.3e}")
+
+    if per_config:
+        pc = {}
+        jobs = [("c1", None)] + [(w, (st, wu, pairs)) for (w, st, wu, pairs) in PER_CONFIG]
+        for w, spec in jobs:
+            log(f"per-config {w}")
+            if w == "c1":
+                r, sp, go = measure_c1()
+            else:
+                st, wu, pairs = spec
+                r, sp, go = measure(w, st, wu, pairs)
+            if want_cpu:
+                wall, cpu_s, nb, err = run_oracle(pool, sp, go)
+                r["parity_max_rel_err"] = float(f"{err:.3e}")
+                r["parity_pairs"] = len(sp)
+                r["cpu_oracle_s_per_step_extrapolated"] = round(wall / len(sp) * r["_pairs_per_step"], 2)
+                r["cpu_oracle_sample"] = (f"layer 0, {len(sp)} pairs in {wall:.2f} s wall on {n_workers} "
+                                          f"processes; {r['_pairs_per_step']} pairs per step")
+            r.pop("_pairs_per_step", None)
+            pc[w] = r
+        line["per_config"] = pc
+    if pool is not None:
+        pool.close()
+        pool.join()
     print(json.dumps(line), flush=True)
 
 
