@@ -72,6 +72,12 @@ __device__ __forceinline__ half4_t h4(uint32_t a, uint32_t b) { return __builtin
 __device__ __forceinline__ float4_t mfma16(half4_t a, half4_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
+// PV over both 16-slot subtiles of a wave in one 16x16x32 step: k element e of lane quarter g
+// is slot 4g + (e & 3) of subtile e >> 2, so A = (codes of subtile 0, codes of subtile 1) and
+// B = the lane's P where its column's subtile matches (zeros in the other half).
+__device__ __forceinline__ float4_t mfma_pv2(half4_t a0, half4_t a1, half4_t b0, half4_t b1, float4_t c) {
+  return mfma(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7), c);
+}
 
 // fp16 pair (1024 + f_lo, 1024 + f_hi) of the two fields selected by mask, minus 1024 + off:
 // exact (f - off, or 16 f - off for a mask shifted by 4 bits).
@@ -110,6 +116,11 @@ __device__ __forceinline__ void unpack_int2(uint32_t x, half8_t &lo, half8_t &hi
 // log2 of the factor that the scaled A elements carry (INT4 16, INT2 4; none for the others)
 template <int FMT>
 constexpr int kSh = FMT == kFmtInt4 ? 4 : FMT == kFmtInt2 ? 2 : 0;
+// log2 of the factor of K operand element e: (e >> 1) odd: INT4 4, INT2 2; else 0
+template <int FMT, int GS>
+__device__ __forceinline__ constexpr int k_elem_sh(int e) {
+  return ((e >> 1) & 1) ? kSh<FMT> : 0;
+}
 // INT8 word pair -> [w0.b0, w0.b2, w0.b1, w0.b3, w1.b0, w1.b2, w1.b1, w1.b3]
 __device__ __forceinline__ half8_t unpack_int8(uint32_t w0, uint32_t w1) {
   return h8(w0 & 0x00FF00FFu, (w0 >> 8) & 0x00FF00FFu, w1 & 0x00FF00FFu, (w1 >> 8) & 0x00FF00FFu);
@@ -228,12 +239,12 @@ __device__ __forceinline__ float head_max2(float x) { return quad_max(fmaxf(x, r
 __device__ __forceinline__ float head_sum2(float x) { return quad_sum(x + row_xor8(x)); }
 
 // ---------------------------------------------------------------- Q operand per format
-// Dim fed by B element e of k-step j in lane quarter g, and whether the A element it meets
-// carries a factor 2^kSh (then B holds q / 2^kSh).
+// Dim fed by B element e of k-step j in lane quarter g, and the log2 sh of the factor the A
+// element it meets carries (then B holds q / 2^sh).
 template <int FMT, int GS>
-__device__ __forceinline__ int q_dim(int g, int j, int e, bool &scaled) {
+__device__ __forceinline__ int q_dim(int g, int j, int e, int &sh) {
   const int G = j >> 1, h = j & 1;
-  scaled = kSh<FMT> != 0 && ((e >> 1) & 1) != 0;
+  sh = k_elem_sh<FMT, GS>(e);
   if constexpr (is_affine(FMT) && GS == 32) {
     return 32 * j + 8 * g + e;   // groups of 32: k-step j feeds dims 32j + 8g .. +7 (group j)
   } else if constexpr (FMT == kFmtInt4) {
@@ -319,14 +330,14 @@ __device__ __forceinline__ void load_q(const uint16_t *qrow, bool valid, int g, 
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      bool scaled;
-      const int d = q_dim<FMT, GS>(g, j, e, scaled);
+      int sh;
+      const int d = q_dim<FMT, GS>(g, j, e, sh);
       const int li = kLay32 ? 8 * (d >> 5) + (d & 7) : kLay64 ? 16 * (d >> 6) + (d & 15) : d - 32 * g;
       _Float16 v = loc[li];
-      if constexpr (kQShift<FMT, GS>) v = (_Float16)((float)v * (scaled ? qscale * (1.0f / (1 << kSh<FMT>)) : qscale));
-      else if (scaled) v = v * (_Float16)(1.0f / (1 << kSh<FMT>));
+      if constexpr (kQShift<FMT, GS>) v = (_Float16)((float)v * (qscale * (1.0f / (float)(1 << sh))));
+      else if (sh) v = v * (_Float16)(1.0f / (float)(1 << sh));
       qb[j][e] = v;
-      const float eff = scaled ? (float)(1 << kSh<FMT>) * (float)v : (float)v;    // the q the MFMA effectively uses
+      const float eff = (float)(1 << sh) * (float)v;    // the q the MFMA effectively uses
       qs[k_group<GS>(j)] += eff;
     }
   }
@@ -461,7 +472,13 @@ __device__ __forceinline__ void lds_words(const uint8_t *p, uint32_t (&w)[N]) {
     }
   }
 }
-__device__ __forceinline__ float half_of(uint32_t word, int h) { return h ? hi_f(word) : lo_f(word); }
+// fp16 half h of a word as an f32 operand (folds into v_fma_mix as a converted source)
+__device__ __forceinline__ float half_of(uint32_t word, int h) { return (float)as_h2(word)[h]; }
+// fp16 pair (fp16(p0 S.lo), fp16(p1 S.hi)): each product rounded to f32, then to fp16 (written
+// as fused multiply-adds with +0 so that each is one v_fma_mix with the fp16 half as a source)
+__device__ __forceinline__ uint32_t pk_scaled(float p0, float p1, uint32_t s) {
+  return pk(__builtin_fmaf(p0, half_of(s, 0), 0.0f), __builtin_fmaf(p1, half_of(s, 1), 0.0f));
+}
 
 // Per-channel K: add a Q operand's sum of (qh + ql) Z over its 8 elements into b1 (or b16 for
 // the INT4 / INT2 elements 2, 3, 6, 7, which meet codes times 16 / 4)
@@ -591,8 +608,8 @@ __device__ __forceinline__ void affine_step(const uint8_t *blk, int w, int g, in
 #pragma unroll
       for (int G = 0; G < NG; ++G) {
         const int hx = NG * i + G;
-        const float u = fmaf(-half_of(kzw[hx >> 1], hx & 1), q.qs[G], acc[G][i]);
-        v = G == 0 ? half_of(ksw[hx >> 1], hx & 1) * u : fmaf(half_of(ksw[hx >> 1], hx & 1), u, v);
+        const float u = __builtin_fmaf(-half_of(kzw[hx >> 1], hx & 1), q.qs[G], acc[G][i]);
+        v = __builtin_fmaf(half_of(ksw[hx >> 1], hx & 1), u, G == 0 ? 0.0f : v);
       }
       if (TAIL && 16 * tau + 4 * g + i >= nvalid) v = kNegInf;
       s[4 * tt + i] = v;
@@ -612,7 +629,7 @@ __device__ __forceinline__ void affine_step(const uint8_t *blk, int w, int g, in
     for (int tt = 0; tt < 2; ++tt) {
       const float *pp = p + 4 * tt;
       const uint32_t s01 = vsw[tt][2 * G], s23 = vsw[tt][2 * G + 1];
-      const uint32_t a01 = pk(pp[0] * lo_f(s01), pp[1] * hi_f(s01)), a23 = pk(pp[2] * lo_f(s23), pp[3] * hi_f(s23));
+      const uint32_t a01 = pk_scaled(pp[0], pp[1], s01), a23 = pk_scaled(pp[2], pp[3], s23);
       pw[2 * tt] = a01;
       pw[2 * tt + 1] = a23;
       const half2_t z01 = as_h2(vzw[tt][2 * G]), z23 = as_h2(vzw[tt][2 * G + 1]);
@@ -859,14 +876,14 @@ struct QOp2 {
   float qscale = 1.0f;     // as in QOp
 };
 
-// Dim (index into the lane's 64 loaded dims) fed by B element e of k-step j, and whether it
-// meets an A element scaled by 2^kSh.  Affine formats and FP8: the lane holds dims 64G + 16(2q + gi) + m
+// Dim (index into the lane's 64 loaded dims) fed by B element e of k-step j, and the log2 of
+// the factor of the A element it meets.  Affine formats and FP8: the lane holds dims 64G + 16(2q + gi) + m
 // at local index 32G + 16gi + m (G, gi in {0,1}); natural formats dims 64q + i at index i.
 // B operand idx feeds k-step j = 2(idx >> 2) + (idx & 1) of lane quarter 2q + gi, gi = (idx >> 1) & 1.
 template <int FMT, int GS>
-__device__ __forceinline__ int q_loc2(int j, int e, bool &scaled) {
+__device__ __forceinline__ int q_loc2(int j, int e, int &sh) {
   const int G = j >> 2, gi = (j >> 1) & 1, hh = j & 1;
-  scaled = kSh<FMT> != 0 && ((e >> 1) & 1) != 0;
+  sh = k_elem_sh<FMT, GS>(e);
   if constexpr (is_affine(FMT) && GS == 32) {
     return 8 * (2 * (2 * G + hh) + gi) + e;   // groups of 32: dims 32 step + 8(2q + gi) + e
   } else if constexpr (FMT == kFmtInt4) {
@@ -927,12 +944,12 @@ __device__ __forceinline__ void load_q2(const uint16_t *qrow, bool valid, int g,
   for (int j = 0; j < 8; ++j) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      bool scaled;
-      _Float16 v = loc[q_loc2<FMT, GS>(j, e, scaled)];
-      if constexpr (kQShift<FMT, GS>) v = (_Float16)((float)v * (scaled ? q.qscale * (1.0f / (1 << kSh<FMT>)) : q.qscale));
-      else if (scaled) v = v * (_Float16)(1.0f / (1 << kSh<FMT>));
+      int sh;
+      _Float16 v = loc[q_loc2<FMT, GS>(j, e, sh)];
+      if constexpr (kQShift<FMT, GS>) v = (_Float16)((float)v * (q.qscale * (1.0f / (float)(1 << sh))));
+      else if (sh) v = v * (_Float16)(1.0f / (float)(1 << sh));
       q.qb[j][e] = v;
-      const float eff = scaled ? (float)(1 << kSh<FMT>) * (float)v : (float)v;
+      const float eff = (float)(1 << sh) * (float)v;
       qs[k_group<GS>(2 * (j >> 2) + (j & 1))] += eff;
     }
   }
@@ -1095,8 +1112,8 @@ __device__ __forceinline__ void affine_step2(const uint8_t *blk, int w, int g, i
 #pragma unroll
     for (int G = 0; G < NG; ++G) {
       const int hx = NG * i + G;
-      const float u = fmaf(-half_of(kzw[hx >> 1], hx & 1), q.qs[G], acc[G][i]);
-      v = G == 0 ? half_of(ksw[hx >> 1], hx & 1) * u : fmaf(half_of(ksw[hx >> 1], hx & 1), u, v);
+      const float u = __builtin_fmaf(-half_of(kzw[hx >> 1], hx & 1), q.qs[G], acc[G][i]);
+      v = __builtin_fmaf(half_of(ksw[hx >> 1], hx & 1), u, G == 0 ? 0.0f : v);
     }
     if (TAIL && 16 * tau_c + 4 * g + i >= nvalid) v = kNegInf;
     s[i] = v;
@@ -1112,8 +1129,8 @@ __device__ __forceinline__ void affine_step2(const uint8_t *blk, int w, int g, i
   half4_t pa[NG][2];
 #pragma unroll
   for (int G = 0; G < NG; ++G) {
-    const uint32_t a01 = pk(p[0] * lo_f(vsw[2 * G]), p[1] * hi_f(vsw[2 * G]));
-    const uint32_t a23 = pk(p[2] * lo_f(vsw[2 * G + 1]), p[3] * hi_f(vsw[2 * G + 1]));
+    const uint32_t a01 = pk_scaled(p[0], p[1], vsw[2 * G]);
+    const uint32_t a23 = pk_scaled(p[2], p[3], vsw[2 * G + 1]);
     if constexpr (NB == 4 || NB == 2) {
       st.z[2 * G] = __builtin_amdgcn_fdot2(as_h2(a01), as_h2(vzw[2 * G]), st.z[2 * G], false);
       st.z[2 * G + 1] = __builtin_amdgcn_fdot2(as_h2(a23), as_h2(vzw[2 * G + 1]), st.z[2 * G + 1], false);
@@ -1126,8 +1143,8 @@ __device__ __forceinline__ void affine_step2(const uint8_t *blk, int w, int g, i
   }
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    st.o[k] = mfma16(v_operand2<NB>(vw, k, 0), pa[v_group<GS>(k)][0], st.o[k]);
-    st.o[k] = mfma16(v_operand2<NB>(vw, k, 1), pa[v_group<GS>(k)][1], st.o[k]);
+    st.o[k] = mfma_pv2(v_operand2<NB>(vw, k, 0), v_operand2<NB>(vw, k, 1), pa[v_group<GS>(k)][0], pa[v_group<GS>(k)][1],
+                       st.o[k]);
   }
 }
 
@@ -1176,8 +1193,7 @@ __device__ __forceinline__ void nvfp4_step2(const uint8_t *blk, int w, int g, in
     const uint32_t f3 = as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vw[k], 1.0f, 3));
     const half4_t b0 = h4(as_u(as_h2(f0) * as_h2(e4m3_pair(scb.x, false))), as_u(as_h2(f1) * as_h2(e4m3_pair(scb.x, true))));
     const half4_t b1 = h4(as_u(as_h2(f2) * as_h2(e4m3_pair(scb.y, false))), as_u(as_h2(f3) * as_h2(e4m3_pair(scb.y, true))));
-    st.o[k] = mfma16(b0, pa0, st.o[k]);
-    st.o[k] = mfma16(b1, pa1, st.o[k]);
+    st.o[k] = mfma_pv2(b0, b1, pa0, pa1, st.o[k]);
   }
 }
 
@@ -1224,8 +1240,8 @@ __device__ __forceinline__ void fp8_step2(const uint8_t *blk, int w, int g, int 
   const half4_t pa0 = sc == 0 ? h4(p02, p13) : h4(0u, 0u), pa1 = sc == 1 ? h4(p02, p13) : h4(0u, 0u);
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    st.o[k] = mfma16(h4(e4m3_pair(vw[2 * k], false), e4m3_pair(vw[2 * k], true)), pa0, st.o[k]);
-    st.o[k] = mfma16(h4(e4m3_pair(vw[2 * k + 1], false), e4m3_pair(vw[2 * k + 1], true)), pa1, st.o[k]);
+    st.o[k] = mfma_pv2(h4(e4m3_pair(vw[2 * k], false), e4m3_pair(vw[2 * k], true)),
+                       h4(e4m3_pair(vw[2 * k + 1], false), e4m3_pair(vw[2 * k + 1], true)), pa0, pa1, st.o[k]);
   }
 }
 
@@ -1269,10 +1285,8 @@ __device__ __forceinline__ void mxfp4_step2(const uint8_t *blk, int w, int g, in
   for (int m = 0; m < 4; ++m) {
     uint32_t lo[4], hi[4];
     mx_v_tiles(xw[2 * m], xw[2 * m + 1], sw[2 * m], sw[2 * m + 1], lo, hi);
-    st.o[2 * m] = mfma16(h4(lo[0], lo[1]), pa0, st.o[2 * m]);
-    st.o[2 * m] = mfma16(h4(lo[2], lo[3]), pa1, st.o[2 * m]);
-    st.o[2 * m + 1] = mfma16(h4(hi[0], hi[1]), pa0, st.o[2 * m + 1]);
-    st.o[2 * m + 1] = mfma16(h4(hi[2], hi[3]), pa1, st.o[2 * m + 1]);
+    st.o[2 * m] = mfma_pv2(h4(lo[0], lo[1]), h4(lo[2], lo[3]), pa0, pa1, st.o[2 * m]);
+    st.o[2 * m + 1] = mfma_pv2(h4(hi[0], hi[1]), h4(hi[2], hi[3]), pa0, pa1, st.o[2 * m + 1]);
   }
 }
 
@@ -1308,8 +1322,7 @@ __device__ __forceinline__ void fp16_step2(const uint8_t *blk, int w, int g, int
   const half4_t pa0 = sc == 0 ? h4(p01, p23) : h4(0u, 0u), pa1 = sc == 1 ? h4(p01, p23) : h4(0u, 0u);
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    st.o[k] = mfma16(h4(vx[k].x, vx[k].y), pa0, st.o[k]);
-    st.o[k] = mfma16(h4(vx[k].z, vx[k].w), pa1, st.o[k]);
+    st.o[k] = mfma_pv2(h4(vx[k].x, vx[k].y), h4(vx[k].z, vx[k].w), pa0, pa1, st.o[k]);
   }
 }
 
