@@ -281,9 +281,12 @@ def measure(name: str, steps: int, warmup: int, n_pairs: int, separate_append: b
     dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream()
     flush_first = R > 0 and per_step == 1 and not ragged and not demote and warmup < R
+    # NVFP4 without a residual: kvq_append_decode_attn quantizes a one-token step inside the
+    # decode launch (one call and one launch per layer)
+    in_launch = fmt == "nvfp4" and R == 0 and not W.old_after and not demote and per_step == 1
     T0 = T - warmup if flush_first else T
 
-    cfg = kvq.make_config(L, B, H, T0 + n_steps * per_step + 1, fmt, R, W.old_fmt, W.old_after, demote=demote)
+    cfg = kvq.make_config(L, B, H, T0 + n_steps * per_step + 9, fmt, R, W.old_fmt, W.old_after, demote=demote)
     cache = kvq.Cache(cfg)
     samples_bh = [(b, h) for b in range(B) for h in range(H)][:n_pairs]
     host_hist = {bh: ([], []) for bh in samples_bh}
@@ -375,7 +378,7 @@ def measure(name: str, steps: int, warmup: int, n_pairs: int, separate_append: b
                     else:
                         t[1] += per_step
             else:
-                quantizes = R == 0 or cache.seq_len(l)[1] + per_step > R or demotes(l)
+                quantizes = (R == 0 and not in_launch) or (R > 0 and cache.seq_len(l)[1] + per_step > R) or demotes(l)
             # a step whose tokens go straight to the residual is one call and one launch (the
             # copy runs inside the decode launch); a step that quantizes appends first
             if separate_append or quantizes:
@@ -429,6 +432,17 @@ def measure(name: str, steps: int, warmup: int, n_pairs: int, separate_append: b
         for l in range(L):
             assert sum(H * (t[0] * bpt + t[1] * 512.0) for t in track[l]) == decode_bytes(cache, l, fmt, old_fmt, True)
 
+    # the 1-token append as a call of its own, on the last layer after the timed steps (R = 0:
+    # the quantize launch that an in-launch append saves)
+    sep_app = []
+    if in_launch:
+        for s in range(min(8, n_steps)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            cache.append(L - 1, knew[s][L - 1], vnew[s][L - 1])
+            e1.record(stream)
+            sep_app.append((e0, e1))
+        torch.cuda.synchronize()
     step_ms = np.array([a.elapsed_time(b) for a, b in step_ev])
     dec_ms = np.array([a.elapsed_time(b) for a, b in dec_ev])
     app_ms = np.array([app_ev[i][0].elapsed_time(app_ev[i][1]) for i in app_used])
@@ -454,6 +468,12 @@ def measure(name: str, steps: int, warmup: int, n_pairs: int, separate_append: b
         "prefill_quantize_gbs": round(pre_bytes / (pre_ms * 1e-3) / 1e9, 1),
         "step_event_ms_mean": round(float(step_ms.mean()), 4),
     }
+    if in_launch:
+        res["append_in_launch"] = True
+        res["append_1_separate_us"] = round(float(np.mean([a.elapsed_time(b) for a, b in sep_app])) * 1e3, 2)
+        res["append_note"] = ("each step's token is quantized inside the decode launch (kvq_append_decode_attn); "
+                              "append_1_separate_us: HIP events around kvq_append of one token as a call of its own "
+                              "(8 calls on the last layer after the timed steps)")
     if app_used:
         res["append_us"] = round(float(app_ms.mean()) * 1e3, 2)
         res["append_note"] = ("HIP events around one layer's kvq_append per timed step (" +

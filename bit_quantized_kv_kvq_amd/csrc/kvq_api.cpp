@@ -382,8 +382,19 @@ size_t rag_wg_bytes(const kvq_cache *c) {
   return align_up((size_t)c->cfg.batch * c->cfg.num_kv_heads * kMaxParts * sizeof(uint32_t));
 }
 
+// An NVFP4 cache without a residual appends a step's token inside the decode launch
+// (kvq_append_decode_attn): per (b, h) a one-token fp16 residual of 16 slots (K [16][128],
+// V [1][128][16]) holds the token's decoded values.
+constexpr size_t kPqResBytes = 2 * 16 * kHeadDim * sizeof(uint16_t);
+bool fuses_nvfp4_append(const kvq_config &c) {
+  return c.format == kFmtNvfp4 && c.residual_len == 0 && c.old_after == 0 && !c.demote_young;
+}
+size_t pq_bytes(const kvq_cache *c) {
+  return fuses_nvfp4_append(c->cfg) ? align_up((size_t)c->cfg.batch * c->cfg.num_kv_heads * kPqResBytes) : 0;
+}
+
 size_t workspace_bound(const kvq_cache *c, int32_t num_q_heads) {
-  return counters_bytes(c) + partials_bytes(c, num_q_heads) + rag_seq_bytes(c) + rag_wg_bytes(c);
+  return counters_bytes(c) + partials_bytes(c, num_q_heads) + rag_seq_bytes(c) + rag_wg_bytes(c) + pq_bytes(c);
 }
 
 // The quantized tiers of one sequence as the decode streams them: old, then young from its
@@ -465,9 +476,13 @@ int num_cus(kvq_cache *c) {
 
 // Every sequence in one state: all work items of the call fill the GPU about once (a.occ
 // workgroups per CU: decode_occupancy), the same split for every (b, h).
-int plan_decode(kvq_cache *c, int layer, DecodeArgs &a, uint64_t *cursors) {
+// hold_young: young slots at the end of the tier that the launch leaves out of the stream and
+// attends to as residual slots instead (a token it appends itself).
+int plan_decode(kvq_cache *c, int layer, DecodeArgs &a, uint64_t *cursors, int64_t hold_young = 0) {
   const auto &cfg = c->cfg;
-  const LayerState &st = c->st(layer, 0);
+  LayerState st = c->st(layer, 0);
+  st.young -= hold_young;
+  st.res += hold_young;
   const int64_t nbh = (int64_t)cfg.batch * cfg.num_kv_heads;
   TierRef tiers[kMaxSegs];
   const int nt = tiers_of(c, layer, st, tiers);
@@ -665,9 +680,11 @@ int check_append(const kvq_cache *c, int32_t layer, const void *k, const void *v
 // Workspace layout of one call: [arrival counters and cursors][partials: part_stride slots per
 // (b, h)][ragged tables].  A call needs counters_bytes + partials_bytes(part_stride) (+ the
 // tables); ws_bytes is checked against that before anything is enqueued.
+// pq_slot >= 0: the young slot of the token this launch quantizes itself (NVFP4 without a
+// residual; `pending` is then null and k, v hold that one token).
 int run_decode(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_heads, float softmax_scale, void *out,
                int32_t out_fp32, void *workspace, size_t ws_bytes, const Op *pending, const void *k, const void *v,
-               int64_t n_src, void *stream, bool ragged) {
+               int64_t n_src, void *stream, bool ragged, int64_t pq_slot = -1) {
   const auto &cfg = c->cfg;
   const int G = num_q_heads / cfg.num_kv_heads;
   if (c->plan_only) return KVQ_OK;
@@ -679,11 +696,13 @@ int run_decode(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_heads, 
   if (ragged) {
     if (int e = plan_decode_ragged(c, layer, a, cursors, pending, &num_wg, &parts, &tab_bytes)) return e;
   } else {
-    num_wg = plan_decode(c, layer, a, cursors);
+    // a token this launch appends itself is attended to as a one-token residual
+    num_wg = plan_decode(c, layer, a, cursors, pq_slot >= 0 ? 1 : 0);
     parts = a.items_total;
   }
   const size_t part_bytes = partials_bytes(c, num_q_heads, parts);
-  const size_t need = counters_bytes(c) + part_bytes + tab_bytes;
+  const size_t pq_off = workspace_bound(c, num_q_heads) - pq_bytes(c);
+  const size_t need = pq_slot >= 0 ? pq_off + pq_bytes(c) : counters_bytes(c) + part_bytes + tab_bytes;
   if (need > ws_bytes) return fail(KVQ_ENOSPACE, "this call needs %zu bytes of workspace, %zu given", need, ws_bytes);
   if (ragged) {
     uint8_t *dev_tab = (uint8_t *)workspace + counters_bytes(c) + part_bytes;
@@ -697,6 +716,19 @@ int run_decode(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_heads, 
   a.counters = (uint64_t *)workspace;
   a.partials = (float *)((uint8_t *)workspace + counters_bytes(c));
   a.part_stride = parts;
+  if (pq_slot >= 0) {
+    a.pq_nvfp4 = 1;
+    a.pq_arena = c->young(layer);
+    a.pq_bh_stride = (int64_t)c->geo.young_bh;
+    a.pq_slot = pq_slot;
+    a.res_base = (const uint8_t *)workspace + pq_off;
+    a.res_bh_stride = (int64_t)kPqResBytes;
+    a.res_len = 16;
+    a.res_ntok = 1;
+    a.pend_k = (const uint16_t *)k; a.pend_v = (const uint16_t *)v;
+    a.pend_src_ntok = n_src;
+    a.pend_src_tok0 = 0;
+  }
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.epoch = next_epoch();
   if (pending) {
@@ -932,6 +964,16 @@ int kvq_append_decode_attn(kvq_cache *c, int32_t layer, const void *k, const voi
   if (st.length + n_tokens == 0) return fail(KVQ_ESTATE, "layer %d is empty", layer);
   Op pending{};
   bool has_pending = false;
+  if (n_tokens == 1 && fuses_nvfp4_append(c->cfg)) {
+    // NVFP4 without a residual: the decode launch quantizes the step's token itself
+    Plan p = plan_append(c->cfg, st, n_tokens);
+    if (int e = check_capacity(c, p)) return e;
+    if (p.ops.size() != 1 || p.ops[0].kind != Op::kQuantInput || p.ops[0].tier != 0 || p.ops[0].count != 1)
+      return fail(KVQ_ESTATE, "internal: unexpected append plan");
+    for (int b = 0; b < c->cfg.batch; ++b) c->st(layer, b) = p.after;
+    return run_decode(c, layer, q, num_q_heads, softmax_scale, out, out_fp32, workspace, ws_bytes, nullptr, k, v,
+                      n_tokens, stream, false, p.ops[0].dst_slot0);
+  }
   if (n_tokens > 0) {
     Plan p = plan_append(c->cfg, st, n_tokens);
     // a last copy into the residual moves into the decode launch (nothing else reads the residual)

@@ -33,6 +33,7 @@
 // NVFP4: E2M1 codes and E4M3 scales are converted by the hardware to fp16 and multiplied
 // (exact: at most 6 significant bits, magnitude in [2^-10, 2688]).
 #include "kvq_internal.h"
+#include "kvq_fp_codes.h"
 
 #include <algorithm>
 #include <cmath>
@@ -1758,6 +1759,73 @@ __device__ __forceinline__ void state_to_lds(State &st, int w, int g, int c, flo
   }
 }
 
+// The call's new token of (b, h), quantized in this launch (the update phase of page "NVFP4
+// KV缓存技术详解" §2.1: quantize the new token and append it): for each of its 16-value blocks
+// of K and V, s = E4M3_RNE(amax / 6) and E2M1 codes, stored at slot pq_slot of the young arena
+// exactly as the append kernel stores them (a slot that opens a block first clears the block:
+// the slots past a tier's length hold zero bytes).  The decoded values (code * s, exact in
+// fp16) become slot 0 of a one-token fp16 residual (K [16][128], V [1][128][16]) that this
+// workgroup attends to.  Streaming workgroups leave the slot out; the words they read may hold
+// it or not, and its fields meet zero weights.
+__device__ __forceinline__ void nvfp4_append_token(const DecodeArgs &a, int bh) {
+  const int s = (int)(a.pq_slot % kBlock);
+  uint8_t *blkp = a.pq_arena + (int64_t)bh * a.pq_bh_stride + (a.pq_slot / kBlock) * (int64_t)kNvfp4BlockBytes;
+  if (s == 0) {
+    for (int i = threadIdx.x; i < (int)(kNvfp4BlockBytes / 16); i += kThreads) ((uint4 *)blkp)[i] = uint4{0u, 0u, 0u, 0u};
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  }
+  if (threadIdx.x < 16) {
+    const int kv = threadIdx.x >> 3, nb = threadIdx.x & 7;   // tensor, 16-value block
+    const uint16_t *src = (kv ? a.pend_v : a.pend_k) + ((int64_t)bh * a.pend_src_ntok + a.pend_src_tok0) * kHeadDim + 16 * nb;
+    const uint4 x0 = *(const uint4 *)src, x1 = *(const uint4 *)(src + 8);
+    const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    uint32_t amax = 0;                                   // |x| of finite fp16 orders like its bits
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = max(amax, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+    const uint32_t sb = f32_to_e4m3((float)__builtin_bit_cast(_Float16, (uint16_t)amax) / 6.0f);
+    const float sc = e4m3_to_f32(sb);
+    uint32_t cw[2] = {0u, 0u};                           // the 16 codes, element i at nibble i
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float x = (float)__builtin_bit_cast(_Float16, (uint16_t)(i & 1 ? w[i >> 1] >> 16 : w[i >> 1] & 0xFFFFu));
+      cw[i >> 3] |= e2m1_code(x, sc) << (4 * (i & 7));
+    }
+    // decoded values, as the stream decodes them: the hardware E2M1 -> fp16 conversion times
+    // the E4M3 scale in fp16 (exact)
+    const uint32_t s2 = e4m3_pair(sb * 0x0101u, false);
+    const half8_t d0 = unpack_fp4(cw[0], s2, s2, s2, s2), d1 = unpack_fp4(cw[1], s2, s2, s2, s2);
+    const u32x4 d0w = __builtin_bit_cast(u32x4, d0), d1w = __builtin_bit_cast(u32x4, d1);
+    const uint32_t dw[8] = {d0w.x, d0w.y, d0w.z, d0w.w, d1w.x, d1w.y, d1w.z, d1w.w};
+    uint16_t *rk = (uint16_t *)(a.res_base + (int64_t)bh * a.res_bh_stride);   // K [16][128]
+    uint16_t *rv = rk + (int64_t)a.res_len * kHeadDim;                          // V [1][128][16]
+    if (kv == 0) {
+      // K: the 16 dims are fields 16 (nb & 1) .. +15 of the lane string of quarter nb >> 1
+      const int lane = 16 * (nb >> 1) + (s & 15);
+      *(uint2 *)(blkp + ((s >> 4) * 64 + lane) * 16 + 8 * (nb & 1)) = make_uint2(cw[0], cw[1]);
+      blkp[kNvKs + ((s >> 4) * 64 + lane) * 2 + (nb & 1)] = (uint8_t)sb;
+      *(uint4 *)(rk + 16 * nb) = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+      *(uint4 *)(rk + 16 * nb + 8) = make_uint4(dw[4], dw[5], dw[6], dw[7]);
+    } else {
+      // V: dim 16 nb + i is nibble e of word nb % 4 of lane 16 g + i in chunk 2 w + nb / 4
+      const int wp = s >> 5, g = (s >> 2) & 3, tt = (s >> 4) & 1, e = 4 * tt + (s & 3);
+      uint32_t *vw = (uint32_t *)(blkp + kNvVc + ((2 * wp + (nb >> 2)) * 64 + 16 * g) * 16 + (nb & 3) * 4);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t code = (cw[i >> 3] >> (4 * (i & 7))) & 0xFu;
+        vw[4 * i] = (vw[4 * i] & ~(0xFu << (4 * e))) | (code << (4 * e));
+      }
+      blkp[kNvVs + ((4 * wp + g) * 8 + nb) * 8 + 4 * tt + (s & 3)] = (uint8_t)sb;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) rv[(16 * nb + i) * 16] = (uint16_t)(i & 1 ? dw[i >> 1] >> 16 : dw[i >> 1] & 0xFFFFu);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 // OCC = workgroups per CU the launch is planned for (the bound on VGPRs follows from it).
 // OCC = 3 holds only the INT2 (groups of 64, per-token K) step: the host launches it only when
 // every tier of the call has that format; its VGPRs then fit three waves per SIMD, which
@@ -1769,6 +1837,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeArgs a) {
   const bool valid_head = (NSUB == 2 ? (c & 7) : c) < a.G;
   const Item it = a.rag ? decode_item_ragged(a, blockIdx.x) : decode_item(a, blockIdx.x);
   __shared__ int s_chunk;
+  if (a.pq_nvfp4 && it.has_res) nvfp4_append_token(a, it.bh);
   if (it.pend_count > 0 && it.has_res) {
     // this call's new tokens go to the residual: copied here, before this workgroup (the only
     // reader of the residual in the launch) reads it

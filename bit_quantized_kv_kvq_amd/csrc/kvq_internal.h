@@ -156,6 +156,15 @@ struct DecodeArgs {
   const uint16_t *pend_k, *pend_v;   // caller input [B][H][pend_src_ntok][128]
   int64_t pend_src_ntok, pend_src_tok0;
   int pend_count, pend_slot0;
+  // One new token per (b, h) quantized to NVFP4 by the launch itself (pq_nvfp4 = 1): the item
+  // holding the residual of each (b, h) writes the token (pend_k / pend_v, token pend_src_tok0
+  // of pend_src_ntok) into slot pq_slot of the young arena (pq_arena, pq_bh_stride bytes per
+  // (b, h)), then attends to its decoded values as a one-token residual at res_base; the
+  // streamed tier leaves that slot out.
+  int pq_nvfp4;
+  uint8_t *pq_arena;
+  int64_t pq_bh_stride;
+  int64_t pq_slot;
   // Ragged batch (null: every sequence has the state above): per sequence a RagSeq overrides
   // the segments' slots and split, the residual and the pending copy; rag_wg[workgroup] packs
   // (b | h << 16 | part << 25) of its work item.

@@ -17,6 +17,7 @@
 //    error unless it lies on it exactly; it is then rounded to 3 mantissa bits, ties even.
 //  * E2M1: |x| is compared with midpoint*s, both exact in fp32.
 #include "kvq_internal.h"
+#include "kvq_fp_codes.h"
 
 #include <cmath>
 
@@ -62,31 +63,6 @@ __device__ uint16_t f64_to_f16_rne(double v) {
   return sign | (uint16_t)((e + 15) << 10) | (uint16_t)keep;
 }
 
-// Non-negative float -> OCP E4M3 byte, round to nearest even, saturating at 448 (0x7E).
-__device__ uint8_t f32_to_e4m3(float v) {
-  if (v >= 448.0f) return 0x7E;
-  if (v < 0.015625f) return (uint8_t)rintf(v * 512.0f);   // below 2^-6: multiples of 2^-9 (8 -> 0x08)
-  uint32_t bits = __float_as_uint(v);
-  int e = (int)((bits >> 23) & 0xFF) - 127;                // -6..8
-  uint32_t m = bits & 0x7FFFFF;
-  uint32_t keep = m >> 20, rem = m & 0xFFFFF, half = 0x80000;
-  if (rem > half || (rem == half && (keep & 1))) ++keep;
-  if (keep == 8) { keep = 0; ++e; }
-  uint32_t code = ((uint32_t)(e + 7) << 3) | keep;
-  return (uint8_t)(code > 0x7E ? 0x7E : code);
-}
-
-// FP8 cache code of an fp16 value: E4M3 of |x| (round to nearest even, saturating at 448)
-// with the sign bit of x.
-__device__ __forceinline__ uint32_t e4m3_cast(float x) {
-  return (uint32_t)f32_to_e4m3(fabsf(x)) | (signbit(x) ? 0x80u : 0u);
-}
-
-__device__ float e4m3_to_f32(uint32_t b) {
-  uint32_t e = (b >> 3) & 0xF, m = b & 7;
-  float mag = e == 0 ? (float)m * 0.001953125f : ldexpf(1.0f + (float)m * 0.125f, (int)e - 7);
-  return (b & 0x80) ? -mag : mag;
-}
 
 // round-half-even of x/S for fp16-valued x and S > 0 with |x/S| < 2^20; inv ~ 1/S.  k is
 // within one of the answer; the exact remainder r = x - k S decides: |r| > S/2, or |r| = S/2
@@ -106,17 +82,6 @@ __device__ __forceinline__ uint32_t affine_code(float x, float S, float inv, flo
   return (uint32_t)q;
 }
 
-__device__ __forceinline__ uint32_t e2m1_code(float x, float s) {
-  float a = fabsf(x);
-  uint32_t idx = 0;
-  if (s > 0.0f) {
-    const float t0 = 0.25f * s, t1 = 0.75f * s, t2 = 1.25f * s, t3 = 1.75f * s, t4 = 2.5f * s, t5 = 3.5f * s, t6 = 5.0f * s;
-    idx = (a > t0) + (a > t1) + (a > t2) + (a > t3) + (a > t4) + (a > t5) + (a > t6);
-    bool tie = a == t0 || a == t1 || a == t2 || a == t3 || a == t4 || a == t5 || a == t6;
-    if (tie && (idx & 1)) ++idx;   // on midpoint idx: pick the even neighbour
-  }
-  return idx | (signbit(x) ? 8u : 0u);
-}
 
 // Block layout (128 slots, head_dim 128).  K codes: 4 parts w x 2 tiles u x 64 lanes
 // (g = lane >> 4, c = lane & 15) x 4n bytes (NVFP4 16) of slot 32w + 16u + c, stored in
