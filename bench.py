@@ -194,6 +194,30 @@ def read_probe_gbs() -> float:
     return best
 
 
+def same_bytes_probe_us(nbytes: float) -> float:
+    """Event-timed duration of the library's read probe over a buffer of the decode call's
+    algorithmic bytes (median of 24 launches, rotated over copies that together exceed the
+    256 MiB MALL): what one streaming launch of that size reaches on this machine, launch cost
+    included, as the decode launches are timed."""
+    import torch
+    import bit_quantized_kv_kvq_amd as kvq
+    n = max(16, int(nbytes) // 16 * 16)
+    bufs = [torch.zeros(n, dtype=torch.uint8, device="cuda") for _ in range(max(1, -(-600 << 20) // n))]
+    sink = torch.empty(kvq.read_probe_sink_bytes(), dtype=torch.uint8, device="cuda")
+    for b in bufs:
+        kvq.read_probe(b, sink)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(24)]
+    for i, (e0, e1) in enumerate(ev):
+        e0.record()
+        kvq.read_probe(bufs[i % len(bufs)], sink)
+        e1.record()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    del bufs, sink
+    torch.cuda.empty_cache()
+    return ts[len(ts) // 2]
+
+
 NOISE_FORMATS = ("int8", "fp8", "int4g32", "int4", "int4kc", "int4g128", "nvfp4", "mxfp4", "int2g32", "int2kc", "int2")
 
 
@@ -444,6 +468,7 @@ def measure(name: str, steps: int, warmup: int, n_pairs: int, separate_append: b
             sep_app.append((e0, e1))
         torch.cuda.synchronize()
     step_ms = np.array([a.elapsed_time(b) for a, b in step_ev])
+    probe_us = same_bytes_probe_us(float(np.mean(timed_bytes)))
     dec_ms = np.array([a.elapsed_time(b) for a, b in dec_ev])
     app_ms = np.array([app_ev[i][0].elapsed_time(app_ev[i][1]) for i in app_used])
     total_bytes = float(np.sum(nbytes))
@@ -463,6 +488,8 @@ def measure(name: str, steps: int, warmup: int, n_pairs: int, separate_append: b
         "decode_bytes_per_launch": round(float(np.mean(timed_bytes))),
         "decode_gbs": round(achieved, 1),
         "decode_frac": round(achieved / HBM_PEAK_GBS, 4),
+        "read_probe_same_bytes_us": round(probe_us, 2),
+        "decode_vs_read_probe": round(probe_us / (float(dec_ms.mean()) * 1e3), 3),
         "prefill_s": round(t_prefill, 2),
         "prefill_quantize_ms": round(pre_ms, 2),
         "prefill_quantize_gbs": round(pre_bytes / (pre_ms * 1e-3) / 1e9, 1),
@@ -671,7 +698,9 @@ def main():
                      "frac": head["decode_frac"], "traffic": traffic_from_profiles(name),
                      "kernel": "decode_kernel (one launch per kvq_append_decode_attn / kvq_decode_attn call)",
                      "launch_us": head["decode_launch_us"], "bytes_per_launch": head["decode_bytes_per_launch"],
-                     "timed_launches": args.steps},
+                     "timed_launches": args.steps,
+                     "read_probe_same_bytes_us": head["read_probe_same_bytes_us"],
+                     "decode_vs_read_probe": head["decode_vs_read_probe"]},
     }
     for k in ("prefill_s", "prefill_quantize_ms", "prefill_quantize_gbs", "append_us", "append_note", "flush_step_ms",
               "plain_step_ms_mean", "flush_append_us", "flush_note", "demote_young", "demotion"):

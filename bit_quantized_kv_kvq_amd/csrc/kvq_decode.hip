@@ -1709,22 +1709,97 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
   }
 }
 
-// Sum over the call's P partials of one output (head hc, dim d) weighted by w[p][hc]: NB loads
-// in flight per batch, every batch whole (parts past P re-read the last one and enter with
-// weight 0; partials are finite), the sum in order over p.
+// The last workgroup's merge of the P partials of a (b, h) (geometry in MergeGeom): the weights
+// of the parts per head from their (m, l), then out = sum_p w_p o_p / sum_p w_p l_p with NB
+// 16-byte loads in flight per thread.
+struct MergeGeom {
+  int P, G, GO, S, nout;
+  __amdgpu_buffer_rsrc_t prs;
+  float *sm_m, *sm_w, *sm_l, *sm_inv;
+  float4_t *sm_red;
+  int64_t row0;            // output row of head 0 of this (b, h)
+  void *out;
+  int out_fp32;
+};
+
 template <int NB>
-__device__ __forceinline__ float merge_parts(const float *parts, const float *w, int P, int G, int hc, int d) {
-  float O = 0.0f;
-  for (int p = 0; p < P; p += NB) {
-    float v[NB];
+__device__ __forceinline__ void merge_tail(const MergeGeom &m, const float *parts) {
+  const int P = m.P, G = m.G, GO = m.GO, S = m.S;
+  const int w = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63;
+  const int sg0 = S > 1 ? (int)threadIdx.x / GO : 0;
+  const int per = sg0 < S ? (P - sg0 + S - 1) / S : 0;       // parts of this thread
+  auto o_offset = [&](int pp, int uu) { return ((pp * G + (uu >> 5)) * kPartialStride + 4 + 4 * (uu & 31)) * 4; };
+  u32x4 ob[NB];
+  {
+    const int u0 = S > 1 ? (int)threadIdx.x % GO : (int)threadIdx.x;
 #pragma unroll
-    for (int u = 0; u < NB; ++u)
-      v[u] = __hip_atomic_load(parts + (int64_t)(min(p + u, P - 1) * G + hc) * kPartialStride + 4 + d, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-    for (int u = 0; u < NB; ++u) O += (p + u < P ? w[(p + u) * G + hc] : 0.0f) * v[u];
+    for (int jb = 0; jb < NB; ++jb) ob[jb] = __builtin_amdgcn_raw_buffer_load_b128(m.prs, o_offset(sg0 + S * jb, u0), 0, 16);
   }
-  return O;
+  for (int idx = threadIdx.x; idx < P * G; idx += kThreads) {
+    const float *pp = parts + (int64_t)idx * kPartialStride;       // part idx / G, head idx % G
+    m.sm_m[idx] = __hip_atomic_load(pp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    m.sm_l[idx] = __hip_atomic_load(pp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  // few parts: one thread per head walks them; many (a small batch split into many items):
+  // one wave per head, lane l taking parts l and l + 64 (P <= kMaxParts = 128), the max and
+  // the weighted sum of l reduced across the wave
+  if (P <= 16) {
+    if ((int)threadIdx.x < G) {
+      const int hc = threadIdx.x;
+      float M = kNegInf;
+      for (int p = 0; p < P; ++p) M = fmaxf(M, m.sm_m[p * G + hc]);
+      float L = 0.0f;
+      for (int p = 0; p < P; ++p) {
+        const float mv = m.sm_m[p * G + hc];
+        const float wt = mv == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
+        m.sm_w[p * G + hc] = wt;
+        L += wt * m.sm_l[p * G + hc];
+      }
+      m.sm_inv[hc] = L > 0.0f ? 1.0f / L : 0.0f;   // L = 0 only for an empty sequence of a ragged batch: zeros
+    }
+  } else {
+    for (int hc = w; hc < G; hc += kWaves) {
+      const int p0 = lane, p1 = lane + 64;
+      const float m0 = p0 < P ? m.sm_m[p0 * G + hc] : kNegInf, m1 = p1 < P ? m.sm_m[p1 * G + hc] : kNegInf;
+      const float M = wave_max(fmaxf(m0, m1));
+      const float w0 = m0 == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m0 - M);
+      const float w1 = m1 == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m1 - M);
+      if (p0 < P) m.sm_w[p0 * G + hc] = w0;
+      if (p1 < P) m.sm_w[p1 * G + hc] = w1;
+      const float L = wave_sum((p0 < P ? w0 * m.sm_l[p0 * G + hc] : 0.0f) + (p1 < P ? w1 * m.sm_l[p1 * G + hc] : 0.0f));
+      if (lane == 0) m.sm_inv[hc] = L > 0.0f ? 1.0f / L : 0.0f;
+    }
+  }
+  __syncthreads();
+  for (int oi = 0; oi < m.nout; ++oi) {
+    const int u = S > 1 ? (int)threadIdx.x % GO : (int)threadIdx.x + oi * kThreads;
+    const int hc = u >> 5;
+    float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j0 = 0; j0 < per; j0 += NB) {
+      if (j0 > 0 || oi > 0) {
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) ob[jb] = __builtin_amdgcn_raw_buffer_load_b128(m.prs, o_offset(sg0 + S * (j0 + jb), u), 0, 16);
+      }
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb) {
+        const float wt = j0 + jb < per ? m.sm_w[(sg0 + S * (j0 + jb)) * G + hc] : 0.0f;
+        acc += wt * __builtin_bit_cast(float4_t, ob[jb]);
+      }
+    }
+    if (S > 1) {
+      if (sg0 < S) m.sm_red[sg0 * GO + u] = acc;
+      __syncthreads();
+      if (sg0 == 0)
+        for (int s2 = 1; s2 < S; ++s2) acc += m.sm_red[s2 * GO + u];
+    }
+    if (sg0 == 0 && u < GO) {
+      const float4_t r = acc * m.sm_inv[hc];
+      const int64_t o = (m.row0 + hc) * kHeadDim + 4 * (u & 31);
+      if (m.out_fp32) *(float4_t *)((float *)m.out + o) = r;
+      else *(uint2 *)((_Float16 *)m.out + o) = make_uint2(pk(r[0], r[1]), pk(r[2], r[3]));
+    }
+  }
 }
 
 // Per-wave state -> LDS rows for the workgroup merge: m[16], l[16] (log2 units) and
@@ -1953,52 +2028,28 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeArgs a) {
   float *sm_w = sm_m + P * G;             // [P][G] weights, after the max is known
   float *sm_l = sm_w + P * G;             // [P][G]
   float *sm_inv = sm_l + P * G;           // [G]
-  for (int idx = threadIdx.x; idx < P * G; idx += kThreads) {
-    const float *pp = parts + (int64_t)idx * kPartialStride;       // part idx / G, head idx % G
-    sm_m[idx] = __hip_atomic_load(pp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm_l[idx] = __hip_atomic_load(pp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  // few parts: one thread per head walks them; many (a small batch split into many items):
-  // one wave per head, lane l taking parts l and l + 64 (P <= kMaxParts = 128), the max and
-  // the weighted sum of l reduced across the wave
-  if (P <= 16) {
-    if (threadIdx.x < G) {
-      const int hc = threadIdx.x;
-      float M = kNegInf;
-      for (int p = 0; p < P; ++p) M = fmaxf(M, sm_m[p * G + hc]);
-      float L = 0.0f;
-      for (int p = 0; p < P; ++p) {
-        const float mv = sm_m[p * G + hc];
-        const float wt = mv == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
-        sm_w[p * G + hc] = wt;
-        L += wt * sm_l[p * G + hc];
-      }
-      sm_inv[hc] = L > 0.0f ? 1.0f / L : 0.0f;   // L = 0 only for an empty sequence of a ragged batch: zeros
-    }
-  } else {
-    for (int hc = w; hc < G; hc += kWaves) {
-      const int p0 = lane, p1 = lane + 64;
-      const float m0 = p0 < P ? sm_m[p0 * G + hc] : kNegInf, m1 = p1 < P ? sm_m[p1 * G + hc] : kNegInf;
-      const float M = wave_max(fmaxf(m0, m1));
-      const float w0 = m0 == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m0 - M);
-      const float w1 = m1 == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m1 - M);
-      if (p0 < P) sm_w[p0 * G + hc] = w0;
-      if (p1 < P) sm_w[p1 * G + hc] = w1;
-      const float L = wave_sum((p0 < P ? w0 * sm_l[p0 * G + hc] : 0.0f) + (p1 < P ? w1 * sm_l[p1 * G + hc] : 0.0f));
-      if (lane == 0) sm_inv[hc] = L > 0.0f ? 1.0f / L : 0.0f;
-    }
-  }
-  __syncthreads();
+  float4_t *sm_red = (float4_t *)(smem + ((3 * P * G + G) * 4 + 15) / 16 * 16);   // [S][G * 32]
+  // The weighted sum reads o of every (part, head) as 16-byte loads with the agent-scope cache
+  // policy (sc1, as the partials were written: past the writer's XCD L2), through a buffer
+  // descriptor bounded by this (b, h)'s partials (a read past them returns zeros).  Thread t
+  // takes float4 output u of the G * 32 and the parts sg, sg + S, ...: with more than 16 parts
+  // and G < 8, S thread groups share an output (at most 16 parts each where the threads allow),
+  // their sums added in a fixed order, so that deterministic splits stay reproducible.  A
+  // thread's first batch of loads goes out before the (m, l) reads, so that the two latencies
+  // overlap.
+  const int GO = G * 32;
+  const int S = GO >= kThreads ? 1 : max(1, min(kThreads / GO, (P + 15) / 16));
+  const int per = (P + S - 1) / S;                                  // parts per thread, at most
+  const __amdgpu_buffer_rsrc_t prs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)parts, 0, P * G * kPartialStride * 4, 0x00020000);
   const int b = it.bh / a.H, h = it.bh % a.H;
-  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kThreads) {
-    const int hc = idx >> 7, d = idx & 127;
-    const float O = P <= 8 ? merge_parts<8>(parts, sm_w, P, G, hc, d) : merge_parts<16>(parts, sm_w, P, G, hc, d);
-    const float r = O * sm_inv[hc];
-    const int64_t o = ((int64_t)b * a.H * G + (int64_t)h * G + hc) * kHeadDim + d;
-    if (a.out_fp32) ((float *)a.out)[o] = r;
-    else ((_Float16 *)a.out)[o] = (_Float16)r;
-  }
+  const MergeGeom mg{P, G, GO, S, GO > kThreads ? 2 : 1, prs, sm_m, sm_w, sm_l, sm_inv, sm_red,
+                     (int64_t)b * a.H * G + (int64_t)h * G, a.out, a.out_fp32};
+  if (per <= 1) merge_tail<1>(mg, parts);
+  else if (per <= 2) merge_tail<2>(mg, parts);
+  else if (per <= 4) merge_tail<4>(mg, parts);
+  else if (per <= 8) merge_tail<8>(mg, parts);
+  else merge_tail<16>(mg, parts);
   // Every other workgroup of this (b, h) has arrived, each after all its memory operations
   // completed (its cursor fetch-adds included), so no access of this call to the (b, h)'s
   // arrival counter or cursors is left: set them back to zero for the next call.

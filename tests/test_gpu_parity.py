@@ -328,3 +328,23 @@ def test_decode_rotated_block_order_with_partial_block(fmt):
     for sigma in (1 / np.sqrt(128), 1.0):
         got, want = p.decode(0, q, sigma)
         assert_attention_close(got, want)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "nvfp4", "fp16"])
+@pytest.mark.parametrize("G", [2, 3, 6, 12, 16])
+@pytest.mark.parametrize("L", [700, 20000])
+def test_decode_other_group_sizes(fmt, G, L):
+    """Query heads per kv head other than 1, 4 and 8 (the merge splits the G * 32 output
+    columns over thread groups, or gives a thread two of them at G = 16), with few and with
+    many work items per (batch, kv_head): 20000 tokens of 2 kv heads give 128 items each."""
+    rng = np.random.default_rng(zlib.crc32(f"og/{fmt}/{G}/{L}".encode()))
+    B, H = 1, 2
+    R = 0 if fmt == "nvfp4" else 128
+    p = Pair(1, B, H, L + 8, fmt, R)
+    k = rng.standard_normal((B, H, L, 128)).astype(np.float16)
+    k[..., :4] *= 15
+    p.append(0, k, rng.standard_normal((B, H, L, 128)).astype(np.float16))
+    q = (rng.standard_normal((B, H * G, 128)) / np.sqrt(128)).astype(np.float16)
+    for sigma in (1 / np.sqrt(128), 1.0):
+        got, want = p.decode(0, q, sigma)
+        assert_attention_close(got, want)
