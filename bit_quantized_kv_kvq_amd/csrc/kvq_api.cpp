@@ -367,9 +367,9 @@ uint64_t next_epoch() {
   }
 }
 
-// Per (b, h): one arrival counter and one chunk cursor per tier.
+// Per (b, h): one arrival counter and one chunk cursor per tier, each in a line of its own.
 size_t counters_bytes(const kvq_cache *c) {
-  return align_up((size_t)c->cfg.batch * c->cfg.num_kv_heads * (1 + kMaxSegs) * sizeof(uint64_t));
+  return align_up((size_t)c->cfg.batch * c->cfg.num_kv_heads * (1 + kMaxSegs) * kCtrStride * sizeof(uint64_t));
 }
 // parts: partial slots per (b, h) (a call uses its most work items of one (b, h))
 size_t partials_bytes(const kvq_cache *c, int32_t num_q_heads, int parts = kMaxParts) {
@@ -494,7 +494,7 @@ int plan_decode(kvq_cache *c, int layer, DecodeArgs &a, uint64_t *cursors, int64
   a.occ = decode_occupancy(fmts, gss, nt, a.G);
   const int64_t target = std::max<int64_t>(1, (int64_t)a.occ * num_cus(c) / nbh);   // work items per (b, h)
   const int parts = split_tiers(c, tiers, nt, target, a.seg);
-  for (int i = 0; i < nt; ++i) a.seg[i].cursors = cursors ? cursors + (size_t)i * nbh : nullptr;
+  for (int i = 0; i < nt; ++i) a.seg[i].cursors = cursors ? cursors + (size_t)i * nbh * kCtrStride : nullptr;
   a.nseg = nt;
   a.items_total = std::max(1, parts);
   a.res_base = c->res(layer);
@@ -541,7 +541,7 @@ int plan_decode_ragged(kvq_cache *c, int layer, DecodeArgs &a, uint64_t *cursors
     s.bh_stride = (int64_t)(slot ? c->geo.young_bh : c->geo.old_bh);
     s.fmt = slot ? cfg.format : cfg.old_format;
     s.gs = tier_gs(&cfg, s.fmt);
-    s.cursors = cursors + (size_t)a.nseg * nbh;
+    s.cursors = cursors + (size_t)a.nseg * nbh * kCtrStride;
     seg_of[slot] = a.nseg++;
   }
   // items per (b, h) of sequence b: ceil(work_b / budget), with the smallest per-item budget
@@ -690,7 +690,7 @@ int run_decode(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_heads, 
   if (c->plan_only) return KVQ_OK;
   DecodeArgs a{};
   a.B = cfg.batch; a.H = cfg.num_kv_heads; a.G = G;
-  uint64_t *cursors = (uint64_t *)workspace + (size_t)cfg.batch * cfg.num_kv_heads;
+  uint64_t *cursors = (uint64_t *)workspace + (size_t)cfg.batch * cfg.num_kv_heads * kCtrStride;
   int num_wg = 0, parts = 1;
   size_t tab_bytes = 0;
   if (ragged) {

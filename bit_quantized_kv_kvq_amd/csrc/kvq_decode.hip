@@ -1538,7 +1538,7 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
   constexpr int kDmaWaves = kWaves - 1;
   const bool dispatcher = w == kDmaWaves;
   const int mine = dispatcher ? 0 : (ndma - w + kDmaWaves - 1) / kDmaWaves;
-  uint64_t *cursor = sg.cursors + it.bh;
+  uint64_t *cursor = sg.cursors + (int64_t)it.bh * kCtrStride;
   const int K = sg.chunk, items = sg.items, F = sg.fixed, nbig = sg.nbig, j = it.j;
   const int nblk = (int)((sg.ntok + kBlock - 1) / kBlock);
   const int fixed_end = min(F * items * K, nblk);            // blocks of the fixed units
@@ -1935,7 +1935,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeArgs a) {
 
   // part 0 opens the arrival counter early, so that the arrivals find it open (wave 3 loads no
   // blocks, so its wait here holds up nothing else)
-  if (it.part == 0 && w == kWaves - 1 && lane == 0) counter_open(a.counters + it.bh, a.epoch);
+  if (it.part == 0 && w == kWaves - 1 && lane == 0) counter_open(a.counters + (int64_t)it.bh * kCtrStride, a.epoch);
   // residual only (no quantized tier yet)
   if (it.seg < 0 && it.has_res) residual_part<NSUB>(a, it, q_group(a, it.bh), w, g, c, valid_head, st);
   if (it.seg >= 0 && w == kWaves - 1) {
@@ -2015,7 +2015,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint64_t *cnt = a.counters + it.bh;
+    uint64_t *cnt = a.counters + (int64_t)it.bh * kCtrStride;
     const uint64_t old = __hip_atomic_fetch_add(cnt, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (int)counter_result(cnt, a.epoch, old) + 1 == it.items_total;
   }
@@ -2054,7 +2054,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeArgs a) {
   // completed (its cursor fetch-adds included), so no access of this call to the (b, h)'s
   // arrival counter or cursors is left: set them back to zero for the next call.
   if (threadIdx.x < 1 + a.nseg) {
-    uint64_t *wd = threadIdx.x == 0 ? a.counters + it.bh : a.seg[threadIdx.x - 1].cursors + it.bh;
+    uint64_t *wd = (threadIdx.x == 0 ? a.counters : a.seg[threadIdx.x - 1].cursors) + (int64_t)it.bh * kCtrStride;
     __hip_atomic_store(wd, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }

@@ -114,11 +114,16 @@ struct DecodeSeg {
   int fixed;               // units per item assigned up front
   int nbig;                // big units the cursor hands out before the single blocks
   int part0;               // index of this segment's first partial among a (b, h)'s partials
-  uint64_t *cursors;       // [B*H] chunk cursors (epoch << 20 | units handed out)
+  uint64_t *cursors;       // [B*H] chunk cursors (epoch << 20 | units handed out), kCtrStride words apart
 };
 
 constexpr int kMaxSegs = 2;        // old tier, young tier
 constexpr int kMaxParts = 128;     // partial results per (b, h) and call
+// The arrival counter and every chunk cursor of a (b, h) sit in a 128-byte line of their own
+// (word i of an array at i * kCtrStride): the items of one (b, h) fetch-add its cursor for
+// every chunk, and atomics on one line serialize where they are performed, so words of
+// different (b, h) and tiers must not share one.
+constexpr int kCtrStride = 16;
 constexpr int kPartialStride = 132;  // floats per (part, head): m, l, -, -, o[128]
 
 // One sequence of a ragged batch (sequences at different lengths), as the decode kernel reads
@@ -136,7 +141,7 @@ struct DecodeArgs {
   const uint16_t *q;       // [B][Hq][128] fp16
   void *out;               // [B][Hq][128] fp32 or fp16
   int out_fp32;
-  uint64_t *counters;      // [B*H] arrival counters (epoch << 20 | count)
+  uint64_t *counters;      // [B*H] arrival counters (epoch << 20 | count), kCtrStride words apart
   float *partials;         // [B*H][part_stride][G][kPartialStride]
   int part_stride;         // partial slots per (b, h): the call's most work items of a (b, h) (<= kMaxParts)
   DecodeSeg seg[kMaxSegs];
