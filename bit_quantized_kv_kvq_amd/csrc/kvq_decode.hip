@@ -817,16 +817,33 @@ __device__ __forceinline__ void residual_step(const uint8_t *res, int R, int r, 
                                               float sl2, bool valid_head, State &st) {
   const half8_t (&qb)[4] = q.qb;
   const int ntiles = R / 16;
+  // every K and V load of the step goes out first (one wait for memory); a tile past the
+  // residual reads the last tile instead and is masked below
+  uint4 kx[2][4];
+  uint2 vx[8][2];
+  const uint8_t *vres = res + (int64_t)R * 256;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int tau = min(2 * u + tt, ntiles - 1);
+    const uint4 *row = (const uint4 *)(res + (16 * tau + c) * 256 + 64 * g);   // dims 32g .. 32g+31
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kx[tt][j] = row[j];
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int tau = min(2 * u + tt, ntiles - 1);
+      vx[k][tt] = *(const uint2 *)(vres + ((tau * kHeadDim + 16 * k + c) * 16 + 4 * g) * 2);
+    }
   float s[8];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
     const int tau = 2 * u + tt;
     float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
     if (tau < ntiles) {
-      const int t = 16 * tau + c;
-      const uint4 *row = (const uint4 *)(res + t * 256 + 64 * g);   // dims 32g .. 32g+31
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc = mfma(__builtin_bit_cast(half8_t, row[j]), qb[j], acc);
+      for (int j = 0; j < 4; ++j) acc = mfma(__builtin_bit_cast(half8_t, kx[tt][j]), qb[j], acc);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -837,16 +854,14 @@ __device__ __forceinline__ void residual_step(const uint8_t *res, int R, int r, 
   float p[8];
   softmax_step(st, s, p, valid_head, 0u, sl2);
   const half8_t pb = h8(pk(p[0], p[1]), pk(p[2], p[3]), pk(p[4], p[5]), pk(p[6], p[7]));
-  const uint8_t *vres = res + (int64_t)R * 256;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const int d = 16 * k + c;
     uint32_t v[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int tau = 2 * u + tt;
       if (tau < ntiles) {
-        const uint2 x = *(const uint2 *)(vres + ((tau * kHeadDim + d) * 16 + 4 * g) * 2);
+        const uint2 x = vx[k][tt];
         v[2 * tt] = x.x;
         v[2 * tt + 1] = x.y;
         // slots past r may hold stale bits (even NaN): zero them
@@ -1327,7 +1342,8 @@ __device__ __forceinline__ void fp16_step2(const uint8_t *blk, int w, int g, int
   }
 }
 
-// fp16 residual, slots 32u .. 32u+31, paired subtiles (direct global loads).
+// fp16 residual, slots 32u .. 32u+31, paired subtiles (direct global loads).  The V loads go
+// out with the K loads, before the logits, so that the step waits for memory once.
 __device__ __forceinline__ void residual_step2(const uint8_t *res, int R, int r, int u, int g, int c, const QOp2 &q,
                                                float sl2, bool valid_head, State &st) {
   const int ntiles = R / 16;
@@ -1337,12 +1353,21 @@ __device__ __forceinline__ void residual_step2(const uint8_t *res, int R, int r,
   // the other subtile's columns through 0 * NaN, so such rows are fed as zeros.
   const bool arow = tau_a < ntiles && 16 * tau_a + c < r;
   const uint4 *row = (const uint4 *)(res + (arow ? 16 * tau_a + c : 0) * 256 + 128 * qq);   // dims 64qq .. 64qq+63
+  uint4 kx[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) kx[j] = row[j];
+  const uint8_t *vres = res + (int64_t)R * 256;
+  uint2 vx[8][2];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int s0 = 0; s0 < 2; ++s0) {
+      const int tau = min(2 * u + s0, ntiles - 1);   // (a tile past the residual is zeroed below)
+      vx[k][s0] = *(const uint2 *)(vres + ((tau * kHeadDim + 16 * k + c) * 16 + 4 * g) * 2);
+    }
   float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint4 x = row[j];
-    acc = mfma(arow ? __builtin_bit_cast(half8_t, x) : h8(0u, 0u, 0u, 0u), q.qb[j], acc);
-  }
+  for (int j = 0; j < 8; ++j) acc = mfma(arow ? __builtin_bit_cast(half8_t, kx[j]) : h8(0u, 0u, 0u, 0u), q.qb[j], acc);
   float s[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1353,18 +1378,15 @@ __device__ __forceinline__ void residual_step2(const uint8_t *res, int R, int r,
   softmax_step2(st, s, p, valid_head, 0u, sl2);
   const uint32_t p01 = pk(p[0], p[1]), p23 = pk(p[2], p[3]);
   const half4_t pa0 = sc == 0 ? h4(p01, p23) : h4(0u, 0u), pa1 = sc == 1 ? h4(p01, p23) : h4(0u, 0u);
-  const uint8_t *vres = res + (int64_t)R * 256;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const int d = 16 * k + c;
 #pragma unroll
     for (int s0 = 0; s0 < 2; ++s0) {
       const int tau = 2 * u + s0;
       uint32_t v0 = 0u, v1 = 0u;
       if (tau < ntiles) {
-        const uint2 x = *(const uint2 *)(vres + ((tau * kHeadDim + d) * 16 + 4 * g) * 2);
-        v0 = x.x;
-        v1 = x.y;
+        v0 = vx[k][s0].x;
+        v1 = vx[k][s0].y;
         // slots past r may hold stale bits (even NaN): zero them
         const int t0 = 16 * tau + 4 * g;
         if (t0 + 0 >= r) v0 &= 0xFFFF0000u;
