@@ -403,9 +403,11 @@ def measure(name: str, steps: int, warmup: int, n_pairs: int, separate_append: b
                         t[1] += per_step
             else:
                 quantizes = (R == 0 and not in_launch) or (R > 0 and cache.seq_len(l)[1] + per_step > R) or demotes(l)
-            # a step whose tokens go straight to the residual is one call and one launch (the
-            # copy runs inside the decode launch); a step that quantizes appends first
-            if separate_append or quantizes:
+            # one kvq_append_decode_attn call per layer: its decode launch copies the tokens
+            # that go to the residual itself, after the quantize launch of a step that flushes.
+            # The layer whose launches are event-timed in a flushing step (and a demoting one)
+            # makes the two calls separately, so that the append and the decode are timed apart.
+            if separate_append or (quantizes and (l == timed or demotes(l))):
                 dem = nbytes is not None and demotes(l) and len(dem_used) < len(dem_ev)
                 if dem:
                     fb = cache.first_block(l, kvq.REGION_YOUNG)

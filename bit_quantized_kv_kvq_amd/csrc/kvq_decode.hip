@@ -34,6 +34,7 @@
 // (exact: at most 6 significant bits, magnitude in [2^-10, 2688]).
 #include "kvq_internal.h"
 #include "kvq_fp_codes.h"
+#include "kvq_rescopy.h"
 
 #include <algorithm>
 #include <cmath>
@@ -1938,15 +1939,9 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeArgs a) {
   if (it.pend_count > 0 && it.has_res) {
     // this call's new tokens go to the residual: copied here, before this workgroup (the only
     // reader of the residual in the launch) reads it
-    const int b = it.bh / a.H, h = it.bh % a.H;
-    uint16_t *rk = (uint16_t *)(a.res_base + (int64_t)it.bh * a.res_bh_stride);   // K [R][128]
-    uint16_t *rv = rk + (int64_t)a.res_len * kHeadDim;                               // V [R/16][128][16]
-    const int64_t src0 = ((int64_t)(b * a.H + h) * a.pend_src_ntok + it.pend_src_tok0) * kHeadDim;
-    for (int e = threadIdx.x; e < it.pend_count * kHeadDim; e += kThreads) {
-      const int slot = it.pend_slot0 + e / kHeadDim, d = e % kHeadDim;
-      rk[slot * kHeadDim + d] = a.pend_k[src0 + e];
-      rv[((slot / 16) * kHeadDim + d) * 16 + slot % 16] = a.pend_v[src0 + e];
-    }
+    const int64_t src0 = ((int64_t)it.bh * a.pend_src_ntok + it.pend_src_tok0) * kHeadDim;
+    residual_store(a.pend_k + src0, a.pend_v + src0, it.pend_count, it.pend_slot0,
+                   (uint8_t *)(a.res_base + (int64_t)it.bh * a.res_bh_stride), a.res_len, threadIdx.x, kThreads);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");

@@ -18,6 +18,7 @@
 //  * E2M1: |x| is compared with midpoint*s, both exact in fp32.
 #include "kvq_internal.h"
 #include "kvq_fp_codes.h"
+#include "kvq_rescopy.h"
 
 #include <cmath>
 
@@ -644,15 +645,15 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
   }
 }
 
-__global__ __launch_bounds__(128) void residual_copy_kernel(ResCopyArgs a) {
-  const int64_t i = blockIdx.x;                 // token of this copy
-  const int h = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
-  const int64_t tok = a.src_tok0 + i, slot = a.dst_slot0 + i;
-  const int64_t src = ((int64_t)(b * a.H + h) * a.src_ntok + tok) * kHeadDim + d;
-  uint8_t *res = a.res_base + (int64_t)(b * a.H + h) * a.res_bh_stride;
-  ((uint16_t *)res)[slot * kHeadDim + d] = a.k_src[src];
-  uint16_t *rv = (uint16_t *)(res + (int64_t)a.res_len * 256);
-  rv[((slot / 16) * kHeadDim + d) * 16 + slot % 16] = a.v_src[src];
+// Workgroup (x, h, b) copies tokens [64 x, 64 x + 64) of the copy for (b, h).
+constexpr int kCopyTokens = 64;
+__global__ __launch_bounds__(256) void residual_copy_kernel(ResCopyArgs a) {
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t i0 = (int64_t)blockIdx.x * kCopyTokens;
+  const int n = (int)min<int64_t>(kCopyTokens, a.count - i0);
+  const int64_t src = ((int64_t)(b * a.H + h) * a.src_ntok + a.src_tok0 + i0) * kHeadDim;
+  residual_store(a.k_src + src, a.v_src + src, n, (int)(a.dst_slot0 + i0),
+                 a.res_base + (int64_t)(b * a.H + h) * a.res_bh_stride, a.res_len, threadIdx.x, 256);
 }
 
 }  // namespace
@@ -687,8 +688,8 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t s) {
 
 hipError_t launch_residual_copy(const ResCopyArgs &a, hipStream_t s) {
   if (a.count <= 0) return hipSuccess;
-  dim3 grid((unsigned)a.count, (unsigned)a.H, (unsigned)a.B);
-  residual_copy_kernel<<<grid, kHeadDim, 0, s>>>(a);
+  dim3 grid((unsigned)((a.count + kCopyTokens - 1) / kCopyTokens), (unsigned)a.H, (unsigned)a.B);
+  residual_copy_kernel<<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

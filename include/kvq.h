@@ -183,14 +183,17 @@ int kvq_decode_attn_noalloc(kvq_cache *c, int32_t layer, const void *q, int32_t 
 /* One decode step of `layer` in one call: exactly kvq_append(c, layer, k, v, n_tokens, stream)
    followed by kvq_decode_attn(c, layer, q, ...), the step that every generated token makes (it
    appends its K/V and attends over the whole history: page "NVFP4 KV缓存技术详解" §2.1, the
-   decoding and cache-update phases).  When the new tokens go to the fp16 residual (no flush,
-   or after the flush that a full residual takes first), the decode launch itself writes them
-   there before it reads the residual, so the step costs one launch instead of two.  All
+   decoding and cache-update phases).  When at most 64 new tokens go to the fp16 residual
+   (no flush, or after the flush that a full residual takes first), the decode launch itself
+   writes them there before it reads the residual, so the step costs one launch instead of
+   two (more tokens are copied by the append's own copy launch, which spreads them over more
+   workgroups than the one that reads the residual).  NVFP4 without a residual quantizes a
+   one-token step inside the decode launch.  All
    arguments of both calls are checked before anything is enqueued; errors as for the two
    calls (on KVQ_EHIP during the append part, the append state has advanced as kvq_append's
    would).  n_tokens = 0 is a plain kvq_decode_attn.  In a ragged batch every sequence's
-   residual copy moves into the decode launch likewise (sequences that flush first get their
-   quantize launches before it). */
+   residual copy of at most 64 tokens moves into the decode launch likewise (sequences that
+   flush first get their quantize launches before it). */
 int kvq_append_decode_attn(kvq_cache *c, int32_t layer, const void *k, const void *v, int64_t n_tokens,
                            const void *q, int32_t num_q_heads, float softmax_scale, void *out, int32_t out_fp32,
                            void *workspace, size_t ws_bytes, void *stream);
