@@ -603,16 +603,19 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
   } else {
     // V: [part w][chunk r][lane][16 bytes]; lane (g, c) word omega holds fields phi = omega F + j
     // of dim 16 k + c and slot 32 w + 16 (e >> 2) + 4 g + (e & 3).  A task is (part, g, omega,
-    // c0 in {0, 8}): the words of lanes 16 g + c0 .. +7, whose field j reads the same slot at
-    // the 8 consecutive dims 16 k + c0 .. +7 (one 16-byte LDS read and one metadata lookup).
+    // c0): the words of lanes 16 g + c0 .. + NL - 1, whose field j reads the same slot at the NL
+    // consecutive dims 16 k + c0 .. (one LDS read and one metadata lookup).  NL = 8, or 4 where
+    // 8 would leave threads idle (INT2: 128 tasks of 8 lanes for 256 threads).
     const size_t vc = kMx ? kMxVc : kNv ? kNvVc : kF8 ? kF8Vc : kKcK ? kc_vc(kBits) : aff_vc(kBits, NG);
     constexpr int kChunks = kBits / 2;              // 16-byte chunks per lane
     constexpr int kLaneWords = 4 * kChunks;
-    constexpr int kTasks = 4 * 4 * kLaneWords * 2;
+    constexpr int NL = 4 * 4 * kLaneWords * 2 >= kThreads ? 8 : 4;
+    constexpr int kSplit = 16 / NL;
+    constexpr int kTasks = 4 * 4 * kLaneWords * kSplit;
     for (int task = tid; task < kTasks; task += kThreads) {
-      const int c0 = 8 * (task & 1), omega = (task >> 1) % kLaneWords, g = ((task >> 1) / kLaneWords) & 3;
-      const int part = (task >> 1) / kLaneWords >> 2;
-      uint32_t words[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      const int c0 = NL * (task % kSplit), omega = (task / kSplit) % kLaneWords, g = ((task / kSplit) / kLaneWords) & 3;
+      const int part = (task / kSplit) / kLaneWords >> 2;
+      uint32_t words[NL] = {};
       uint32_t keep = 0;                            // field bits of slots before lo (kept as stored)
       bool any = false;
 #pragma unroll
@@ -630,13 +633,19 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
         const int d0 = 16 * k + c0;
         const int grp = d0 / (kMx ? kMxBlock : kNv ? kNvBlock : GSV);
         float x[8];
-        unpack8(*(const uint4 *)&xs[slot * kRowHalves + d0], x);
+        if constexpr (NL == 8) {
+          unpack8(*(const uint4 *)&xs[slot * kRowHalves + d0], x);
+        } else {
+          const uint2 u = *(const uint2 *)&xs[slot * kRowHalves + d0];
+          x[0] = h2f((uint16_t)(u.x & 0xFFFFu)); x[1] = h2f((uint16_t)(u.x >> 16));
+          x[2] = h2f((uint16_t)(u.y & 0xFFFFu)); x[3] = h2f((uint16_t)(u.y >> 16));
+        }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) words[i] |= code_of(x[i], slot, grp) << (j * kBits);
+        for (int i = 0; i < NL; ++i) words[i] |= code_of(x[i], slot, grp) << (j * kBits);
       }
       if (!any) continue;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < NL; ++i) {
         const int lane = 16 * g + c0 + i;
         uint32_t *dst = (uint32_t *)(blkp + vc + ((size_t)(part * kChunks + omega / 4) * 64 + lane) * 16 + (omega % 4) * 4);
         *dst = keep ? (*dst & keep) | words[i] : words[i];

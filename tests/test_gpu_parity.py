@@ -30,6 +30,45 @@ def test_append_bytes_exact(fmt, R):
         p.check_bytes(0)
 
 
+def tie_tokens(rng, B, H, n, qmax, gs):
+    """fp16 [B, H, n, 128] whose affine groups of gs dims are built so that x / S is exactly a
+    half-integer for most values while 1 / S is not a binary fraction: S = m 2^e (m odd, at
+    most 7, so that qmax S is exact), one value at -j S and one at (qmax - j) S fix the group's
+    range to qmax S (so S and Z = j come out exactly), the others at (c - j + 1/2) S."""
+    ms = [3] if qmax == 255 else [3, 5, 7]
+    x = np.empty((B, H, n, 128), np.float64)
+    for b in range(B):
+        for h in range(H):
+            for t in range(n):
+                for g0 in range(0, 128, gs):
+                    S = float(rng.choice(ms)) * 2.0 ** int(rng.integers(-10, 1))
+                    j = int(rng.integers(0, qmax + 1))
+                    c = rng.integers(0, qmax, gs)
+                    v = (c - j + 0.5) * S
+                    pos = rng.permutation(gs)[:2]
+                    v[pos[0]], v[pos[1]] = -j * S, (qmax - j) * S
+                    x[b, h, t, g0:g0 + gs] = v
+    y = x.astype(np.float16)
+    assert np.array_equal(y.astype(np.float64), x)
+    return y
+
+
+@pytest.mark.parametrize("fmt", ["int2", "int4", "int8", "int2g32", "int4g32", "int4g128", "int8g128"])
+@pytest.mark.parametrize("R", [0, 128])
+def test_append_bytes_exact_rounding_ties(fmt, R):
+    """Affine codes where x / S is exactly halfway between two codes for most values and S is
+    not a power of two: the round-half-even decision of the quantizer, from input and from the
+    residual's flush."""
+    gs = int(fmt.split("g")[1]) if "g" in fmt else 64
+    qmax = (1 << int(fmt[3])) - 1
+    rng = np.random.default_rng(zlib.crc32(f"ties/{fmt}/{R}".encode()))
+    B, H = 1, 2
+    p = Pair(1, B, H, 800, fmt, R)
+    for n in [300, 1, 129, 200]:
+        p.append(0, tie_tokens(rng, B, H, n, qmax, gs), tie_tokens(rng, B, H, n, qmax, gs))
+        p.check_bytes(0)
+
+
 def test_tiers_bytes_exact():
     rng = np.random.default_rng(77)
     B, H = 1, 2
