@@ -83,6 +83,13 @@ __device__ __forceinline__ uint32_t affine_code(float x, float S, float inv, flo
   return (uint32_t)q;
 }
 
+// Raise the block's eps (float bits in *eps, non-negative) to the bound of a group whose values
+// lie in [mn, mx] and whose 1 / S is inv: max |x / S| 2^-20, eight times the largest error of
+// x * inv against x / S in the group (two roundings, each within |x / S| 2^-24).
+__device__ __forceinline__ void note_eps(uint32_t *eps, float mn, float mx, float inv) {
+  atomicMax(eps, __float_as_uint(fmaxf(fabsf(mn), fabsf(mx)) * inv * 0x1p-20f));
+}
+
 
 // Block layout (128 slots, head_dim 128).  K codes: 4 parts w x 2 tiles u x 64 lanes
 // (g = lane >> 4, c = lane & 15) x 4n bytes (NVFP4 16) of slot 32w + 16u + c, stored in
@@ -261,8 +268,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
   __shared__ float mS[kBlock][kMeta];
   __shared__ float mInv[kBlock][kAffMeta];
   __shared__ float mZ[kBlock][kAffMeta];
+  // largest eps_g of the block's affine groups (float bits; see the codes below)
+  __shared__ uint32_t s_eps;
 
   const int tid = threadIdx.x;
+  if (tid == 0) s_eps = 0u;
   const int64_t blk = blk0 + blockIdx.x;
   const int h = blockIdx.y, b = blockIdx.z >> 1, kv = blockIdx.z & 1;
   const int64_t bstart = blk * kBlock;
@@ -363,6 +373,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
         mS[d][0] = S;
         mInv[d][0] = 1.0f / S;
         mZ[d][0] = h2f((uint16_t)Zb);
+        note_eps(&s_eps, mn, mx, mInv[d][0]);
       }
       __syncthreads();
       // (S, Z) in MFMA operand order: position 32g + 8j + e holds the dim that element feeds
@@ -406,6 +417,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
         mS[slot][g] = S;
         mInv[slot][g] = 1.0f / S;
         mZ[slot][g] = h2f((uint16_t)Zb);
+        note_eps(&s_eps, mn, mx, mInv[slot][g]);
         const int tau = slot >> 4, r = slot & 15, q = r >> 2, i = r & 3;
         uint8_t *m = blkp + kc_vm(kBits) + (tau * 4 + q) * 32;
         *(uint16_t *)(m + 8 * g + 2 * i) = (uint16_t)Sb;
@@ -448,6 +460,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
       mS[slot][g] = S;
       mInv[slot][g] = 1.0f / S;
       mZ[slot][g] = h2f((uint16_t)Zb);
+      note_eps(&s_eps, mn, mx, mInv[slot][g]);
       write = true;
     } else if (slot >= hi && slot < zhi) {
       write = true;                            // cleared slot: S = Z = +0
@@ -545,6 +558,20 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
 
   // ---- codes
   constexpr int F = 32 / kBits;                     // fields per word
+  // Affine codes, fast: t = x * inv with inv = RN(1 / S) lies within eps_g = A_g 2^-20 of x / S
+  // for every x of group g (A_g = max(|min|, |max|) / S >= |x / S|; the two roundings cost at
+  // most |x / S| 2^-23), so rint(t) is RNE(x / S) unless x / S is within eps_g of a
+  // half-integer.  Where |t - rint(t)| reaches 0.5 - eps (eps: the block's largest eps_g) the
+  // code is decided by the exact remainder instead (div_rne): a branch that the wave takes
+  // only when one of its lanes meets such a value (about 3e-4 of normally distributed inputs,
+  // nearly all of them exact ties).
+  const float thr = 0.5f - __uint_as_float(s_eps);
+  auto fast_code = [&](float x, float S_of, float inv, float Z) -> uint32_t {
+    const float t = x * inv;
+    float k = rintf(t);
+    if (__builtin_expect(fabsf(t - k) >= thr, 0)) k = div_rne(x, S_of, inv);
+    return (uint32_t)__builtin_amdgcn_fmed3f(k + Z, 0.0f, (float)kQmax);
+  };
   auto code_of = [&](float x, int slot, int grp) -> uint32_t {
     if constexpr (kF8) return e4m3_cast(x);
     else if constexpr (kNv) return e2m1_code(x, mS[slot][grp]);
@@ -576,8 +603,31 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
 #pragma unroll
         for (int k = 0; k < F; ++k) {
           const int d = k_lane_dim32(FMT, g, omega * F + k);
-          word |= code_of(h2f(xs[slot * kRowHalves + d]), slot, d >> 5) << (k * kBits);
+          word |= fast_code(h2f(xs[slot * kRowHalves + d]), mS[slot][d >> 5], mInv[slot][d >> 5], mZ[slot][d >> 5])
+                  << (k * kBits);
         }
+      } else if (kAffine && !kKcK && slot < hi) {
+        // one group for the word's F consecutive dims
+        const int d0 = k_lane_dim(FMT, g, omega * F);
+        const int grp = d0 / GSV;
+        const uint16_t *xr = &xs[slot * kRowHalves + d0];
+        const float Sg = mS[slot][grp], inv = mInv[slot][grp], Z = mZ[slot][grp];
+        float x[F];
+        if constexpr (F >= 8) {
+#pragma unroll
+          for (int h8 = 0; h8 < F / 8; ++h8) {
+            float x8[8];
+            unpack8(*(const uint4 *)(xr + 8 * h8), x8);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) x[8 * h8 + k] = x8[k];
+          }
+        } else {
+          const uint2 v = *(const uint2 *)xr;
+          x[0] = h2f((uint16_t)(v.x & 0xFFFFu)); x[1] = h2f((uint16_t)(v.x >> 16));
+          x[2] = h2f((uint16_t)(v.y & 0xFFFFu)); x[3] = h2f((uint16_t)(v.y >> 16));
+        }
+#pragma unroll
+        for (int k = 0; k < F; ++k) word |= fast_code(x[k], Sg, inv, Z) << (k * kBits);
       } else if (slot < hi) {
         const int d0 = k_lane_dim(FMT, g, omega * F);   // first of F consecutive dims
         const int grp = d0 / (kMx ? kMxBlock : kNv ? kNvBlock : GSV);
@@ -609,7 +659,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
     const size_t vc = kMx ? kMxVc : kNv ? kNvVc : kF8 ? kF8Vc : kKcK ? kc_vc(kBits) : aff_vc(kBits, NG);
     constexpr int kChunks = kBits / 2;              // 16-byte chunks per lane
     constexpr int kLaneWords = 4 * kChunks;
-    constexpr int NL = 4 * 4 * kLaneWords * 2 >= kThreads ? 8 : 4;
+    constexpr int NL = 4 * 4 * kLaneWords * 2 >= kThreads ? 8 : 4 * 4 * kLaneWords * 4 >= kThreads ? 4 : 2;
     constexpr int kSplit = 16 / NL;
     constexpr int kTasks = 4 * 4 * kLaneWords * kSplit;
     for (int task = tid; task < kTasks; task += kThreads) {
@@ -635,13 +685,22 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
         float x[8];
         if constexpr (NL == 8) {
           unpack8(*(const uint4 *)&xs[slot * kRowHalves + d0], x);
-        } else {
+        } else if constexpr (NL == 4) {
           const uint2 u = *(const uint2 *)&xs[slot * kRowHalves + d0];
           x[0] = h2f((uint16_t)(u.x & 0xFFFFu)); x[1] = h2f((uint16_t)(u.x >> 16));
           x[2] = h2f((uint16_t)(u.y & 0xFFFFu)); x[3] = h2f((uint16_t)(u.y >> 16));
+        } else {
+          const uint32_t u = *(const uint32_t *)&xs[slot * kRowHalves + d0];
+          x[0] = h2f((uint16_t)(u & 0xFFFFu)); x[1] = h2f((uint16_t)(u >> 16));
         }
+        if constexpr (kAffine) {
+          const float Sg = mS[slot][grp], inv = mInv[slot][grp], Z = mZ[slot][grp];
 #pragma unroll
-        for (int i = 0; i < NL; ++i) words[i] |= code_of(x[i], slot, grp) << (j * kBits);
+          for (int i = 0; i < NL; ++i) words[i] |= fast_code(x[i], Sg, inv, Z) << (j * kBits);
+        } else {
+#pragma unroll
+          for (int i = 0; i < NL; ++i) words[i] |= code_of(x[i], slot, grp) << (j * kBits);
+        }
       }
       if (!any) continue;
 #pragma unroll
