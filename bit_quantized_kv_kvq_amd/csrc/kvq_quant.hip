@@ -31,6 +31,7 @@ constexpr int kRowHalves = 136;  // LDS row stride (halves) of the staged fp16 t
 __device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 // the 8 fp16 values of a 16-byte LDS read, as floats
@@ -84,10 +85,11 @@ __device__ __forceinline__ uint32_t affine_code(float x, float S, float inv, flo
 }
 
 // Raise the block's eps (float bits in *eps, non-negative) to the bound of a group whose values
-// lie in [mn, mx] and whose 1 / S is inv: max |x / S| 2^-20, eight times the largest error of
-// x * inv against x / S in the group (two roundings, each within |x / S| 2^-24).
-__device__ __forceinline__ void note_eps(uint32_t *eps, float mn, float mx, float inv) {
-  atomicMax(eps, __float_as_uint(fmaxf(fabsf(mn), fabsf(mx)) * inv * 0x1p-20f));
+// lie in [mn, mx], whose 1 / S is inv and whose zero point is Z: (max |x / S| + |Z|) 2^-20,
+// eight times the largest error of RN(x * inv + Z) against x / S + Z in the group (the
+// rounding of inv and that of the fused multiply-add, each within (|x / S| + |Z|) 2^-24).
+__device__ __forceinline__ void note_eps(uint32_t *eps, float mn, float mx, float inv, float Z) {
+  atomicMax(eps, __float_as_uint((fmaxf(fabsf(mn), fabsf(mx)) * inv + fabsf(Z)) * 0x1p-20f));
 }
 
 
@@ -373,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
         mS[d][0] = S;
         mInv[d][0] = 1.0f / S;
         mZ[d][0] = h2f((uint16_t)Zb);
-        note_eps(&s_eps, mn, mx, mInv[d][0]);
+        note_eps(&s_eps, mn, mx, mInv[d][0], mZ[d][0]);
       }
       __syncthreads();
       // (S, Z) in MFMA operand order: position 32g + 8j + e holds the dim that element feeds
@@ -417,7 +419,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
         mS[slot][g] = S;
         mInv[slot][g] = 1.0f / S;
         mZ[slot][g] = h2f((uint16_t)Zb);
-        note_eps(&s_eps, mn, mx, mInv[slot][g]);
+        note_eps(&s_eps, mn, mx, mInv[slot][g], mZ[slot][g]);
         const int tau = slot >> 4, r = slot & 15, q = r >> 2, i = r & 3;
         uint8_t *m = blkp + kc_vm(kBits) + (tau * 4 + q) * 32;
         *(uint16_t *)(m + 8 * g + 2 * i) = (uint16_t)Sb;
@@ -460,7 +462,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
       mS[slot][g] = S;
       mInv[slot][g] = 1.0f / S;
       mZ[slot][g] = h2f((uint16_t)Zb);
-      note_eps(&s_eps, mn, mx, mInv[slot][g]);
+      note_eps(&s_eps, mn, mx, mInv[slot][g], mZ[slot][g]);
       write = true;
     } else if (slot >= hi && slot < zhi) {
       write = true;                            // cleared slot: S = Z = +0
@@ -558,19 +560,19 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
 
   // ---- codes
   constexpr int F = 32 / kBits;                     // fields per word
-  // Affine codes, fast: t = x * inv with inv = RN(1 / S) lies within eps_g = A_g 2^-20 of x / S
-  // for every x of group g (A_g = max(|min|, |max|) / S >= |x / S|; the two roundings cost at
-  // most |x / S| 2^-23), so rint(t) is RNE(x / S) unless x / S is within eps_g of a
+  // Affine codes, fast: t = RN(x * inv + Z) (one fused multiply-add of the fp16 x, with
+  // inv = RN(1 / S)) lies within eps_g of x / S + Z for every x of group g (note_eps), so
+  // rint(t) is RNE(x / S) + Z (Z is an integer) unless x / S is within eps_g of a
   // half-integer.  Where |t - rint(t)| reaches 0.5 - eps (eps: the block's largest eps_g) the
   // code is decided by the exact remainder instead (div_rne): a branch that the wave takes
   // only when one of its lanes meets such a value (about 3e-4 of normally distributed inputs,
   // nearly all of them exact ties).
   const float thr = 0.5f - __uint_as_float(s_eps);
-  auto fast_code = [&](float x, float S_of, float inv, float Z) -> uint32_t {
-    const float t = x * inv;
+  auto fast_code = [&](_Float16 xh, float S_of, float inv, float Z) -> uint32_t {
+    const float t = __builtin_fmaf((float)xh, inv, Z);
     float k = rintf(t);
-    if (__builtin_expect(fabsf(t - k) >= thr, 0)) k = div_rne(x, S_of, inv);
-    return (uint32_t)__builtin_amdgcn_fmed3f(k + Z, 0.0f, (float)kQmax);
+    if (__builtin_expect(fabsf(t - k) >= thr, 0)) k = div_rne((float)xh, S_of, inv) + Z;
+    return (uint32_t)__builtin_amdgcn_fmed3f(k, 0.0f, (float)kQmax);
   };
   auto code_of = [&](float x, int slot, int grp) -> uint32_t {
     if constexpr (kF8) return e4m3_cast(x);
@@ -603,8 +605,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
 #pragma unroll
         for (int k = 0; k < F; ++k) {
           const int d = k_lane_dim32(FMT, g, omega * F + k);
-          word |= fast_code(h2f(xs[slot * kRowHalves + d]), mS[slot][d >> 5], mInv[slot][d >> 5], mZ[slot][d >> 5])
-                  << (k * kBits);
+          word |= fast_code(__builtin_bit_cast(_Float16, xs[slot * kRowHalves + d]), mS[slot][d >> 5], mInv[slot][d >> 5],
+                            mZ[slot][d >> 5]) << (k * kBits);
         }
       } else if (kAffine && !kKcK && slot < hi) {
         // one group for the word's F consecutive dims
@@ -612,19 +614,18 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
         const int grp = d0 / GSV;
         const uint16_t *xr = &xs[slot * kRowHalves + d0];
         const float Sg = mS[slot][grp], inv = mInv[slot][grp], Z = mZ[slot][grp];
-        float x[F];
+        _Float16 x[F];
         if constexpr (F >= 8) {
 #pragma unroll
           for (int h8 = 0; h8 < F / 8; ++h8) {
-            float x8[8];
-            unpack8(*(const uint4 *)(xr + 8 * h8), x8);
+            const half8v x8 = __builtin_bit_cast(half8v, *(const uint4 *)(xr + 8 * h8));
 #pragma unroll
             for (int k = 0; k < 8; ++k) x[8 * h8 + k] = x8[k];
           }
         } else {
-          const uint2 v = *(const uint2 *)xr;
-          x[0] = h2f((uint16_t)(v.x & 0xFFFFu)); x[1] = h2f((uint16_t)(v.x >> 16));
-          x[2] = h2f((uint16_t)(v.y & 0xFFFFu)); x[3] = h2f((uint16_t)(v.y >> 16));
+          const half8v x8 = __builtin_bit_cast(half8v, make_uint4((*(const uint2 *)xr).x, (*(const uint2 *)xr).y, 0u, 0u));
+#pragma unroll
+          for (int k = 0; k < 4; ++k) x[k] = x8[k];
         }
 #pragma unroll
         for (int k = 0; k < F; ++k) word |= fast_code(x[k], Sg, inv, Z) << (k * kBits);
@@ -682,22 +683,23 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
         if (slot >= hi) continue;                    // cleared: code 0
         const int d0 = 16 * k + c0;
         const int grp = d0 / (kMx ? kMxBlock : kNv ? kNvBlock : GSV);
-        float x[8];
+        uint4 raw = make_uint4(0u, 0u, 0u, 0u);
         if constexpr (NL == 8) {
-          unpack8(*(const uint4 *)&xs[slot * kRowHalves + d0], x);
+          raw = *(const uint4 *)&xs[slot * kRowHalves + d0];
         } else if constexpr (NL == 4) {
           const uint2 u = *(const uint2 *)&xs[slot * kRowHalves + d0];
-          x[0] = h2f((uint16_t)(u.x & 0xFFFFu)); x[1] = h2f((uint16_t)(u.x >> 16));
-          x[2] = h2f((uint16_t)(u.y & 0xFFFFu)); x[3] = h2f((uint16_t)(u.y >> 16));
+          raw.x = u.x; raw.y = u.y;
         } else {
-          const uint32_t u = *(const uint32_t *)&xs[slot * kRowHalves + d0];
-          x[0] = h2f((uint16_t)(u & 0xFFFFu)); x[1] = h2f((uint16_t)(u >> 16));
+          raw.x = *(const uint32_t *)&xs[slot * kRowHalves + d0];
         }
         if constexpr (kAffine) {
+          const half8v xh = __builtin_bit_cast(half8v, raw);
           const float Sg = mS[slot][grp], inv = mInv[slot][grp], Z = mZ[slot][grp];
 #pragma unroll
-          for (int i = 0; i < NL; ++i) words[i] |= fast_code(x[i], Sg, inv, Z) << (j * kBits);
+          for (int i = 0; i < NL; ++i) words[i] |= fast_code(xh[i], Sg, inv, Z) << (j * kBits);
         } else {
+          float x[8];
+          unpack8(raw, x);
 #pragma unroll
           for (int i = 0; i < NL; ++i) words[i] |= code_of(x[i], slot, grp) << (j * kBits);
         }
