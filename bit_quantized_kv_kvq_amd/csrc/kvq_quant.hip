@@ -84,6 +84,35 @@ __device__ __forceinline__ uint32_t affine_code(float x, float S, float inv, flo
   return (uint32_t)q;
 }
 
+// Bits of S = RN16((mx - mn) / qmax), mx > mn: in fp32 where that provably gives the same
+// fp16 value, else in fp64.  The difference is used only when exact (its TwoSum error is 0);
+// r = d * RN(1/qmax) is then within 2 fp32 ulps of d / qmax, so rounding r to fp16 (to
+// nearest, ties to even) matches unless r lies within a few ulps of a midpoint between fp16
+// values (low 13 mantissa bits near 0x1000) or outside the normal fp16 range.
+__device__ __forceinline__ uint32_t scale_bits(float mn, float mx, int qmax) {
+  const float d = mx - mn;
+  const float bb = d - mx;
+  const float err = (mx - (d - bb)) + (-mn - bb);
+  const float r = d * (1.0f / (float)qmax);
+  const uint32_t m13 = __float_as_uint(r) & 0x1FFFu;
+  if (err == 0.0f && r >= 0x1p-14f && r < 65504.0f && (m13 < 0x1000u - 8u || m13 > 0x1000u + 8u))
+    return __builtin_bit_cast(uint16_t, (_Float16)r);
+  return f64_to_f16_rne(((double)mx - (double)mn) / (double)qmax);
+}
+
+// Bits of Z = RN16(clamp(RNE(-mn / S), +-65504)) for fp16 values mn and S > 0, a zero always
+// +0: by the exact remainder in fp32 (div_rne) where |mn / S| < 2^19, else in fp64.
+__device__ __forceinline__ uint32_t zero_bits(float mn, float S) {
+  const float inv = 1.0f / S;
+  if (fabsf(mn) * inv < 0x1p19f) {
+    const float z = fminf(fmaxf(div_rne(-mn, S, inv), -65504.0f), 65504.0f) + 0.0f;   // -0 + 0 = +0
+    return __builtin_bit_cast(uint16_t, (_Float16)z);
+  }
+  double z = rint(-(double)mn / (double)S);
+  z = fmin(fmax(z, -65504.0), 65504.0);
+  return f64_to_f16_rne(z);
+}
+
 // Raise the block's eps (float bits in *eps, non-negative) to the bound of a group whose values
 // lie in [mn, mx], whose 1 / S is inv and whose zero point is Z: (max |x / S| + |Z|) 2^-20,
 // eight times the largest error of RN(x * inv + Z) against x / S + Z in the group (the
@@ -362,16 +391,14 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
         float S = 0.0f;
         uint32_t Sb = 0;
         if (mx > mn) {
-          Sb = f64_to_f16_rne(((double)mx - (double)mn) / (double)kQmax);
+          Sb = scale_bits(mn, mx, kQmax);
           S = h2f((uint16_t)Sb);
         }
         if (!(mx > mn) || S == 0.0f) {
           S = mn != 0.0f ? fabsf(mn) : 1.0f;
           Sb = __builtin_bit_cast(uint16_t, (_Float16)S);
         }
-        double z = rint(-(double)mn / (double)S);
-        z = fmin(fmax(z, -65504.0), 65504.0);
-        const uint32_t Zb = f64_to_f16_rne(z);
+        const uint32_t Zb = zero_bits(mn, S);
         mS[d][0] = S;
         mInv[d][0] = 1.0f / S;
         mZ[d][0] = h2f((uint16_t)Zb);
@@ -406,16 +433,14 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
         float S = 0.0f;
         uint32_t Sb = 0;
         if (mx > mn) {
-          Sb = f64_to_f16_rne(((double)mx - (double)mn) / (double)kQmax);
+          Sb = scale_bits(mn, mx, kQmax);
           S = h2f((uint16_t)Sb);
         }
         if (!(mx > mn) || S == 0.0f) {
           S = mn != 0.0f ? fabsf(mn) : 1.0f;
           Sb = __builtin_bit_cast(uint16_t, (_Float16)S);
         }
-        double z = rint(-(double)mn / (double)S);
-        z = fmin(fmax(z, -65504.0), 65504.0);
-        const uint32_t Zb = f64_to_f16_rne(z);
+        const uint32_t Zb = zero_bits(mn, S);
         mS[slot][g] = S;
         mInv[slot][g] = 1.0f / S;
         mZ[slot][g] = h2f((uint16_t)Zb);
@@ -449,16 +474,14 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
       const float mn = fminf((float)mn2.x, (float)mn2.y), mx = fmaxf((float)mx2.x, (float)mx2.y);
       float S = 0.0f;
       if (mx > mn) {
-        Sb = f64_to_f16_rne(((double)mx - (double)mn) / (double)kQmax);
+        Sb = scale_bits(mn, mx, kQmax);
         S = h2f((uint16_t)Sb);
       }
       if (!(mx > mn) || S == 0.0f) {          // degenerate group: S = |min|, or 1 when min is 0
         S = mn != 0.0f ? fabsf(mn) : 1.0f;
         Sb = __builtin_bit_cast(uint16_t, (_Float16)S);
       }
-      double z = rint(-(double)mn / (double)S);
-      z = fmin(fmax(z, -65504.0), 65504.0);
-      Zb = f64_to_f16_rne(z);
+      Zb = zero_bits(mn, S);
       mS[slot][g] = S;
       mInv[slot][g] = 1.0f / S;
       mZ[slot][g] = h2f((uint16_t)Zb);
