@@ -335,6 +335,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
     // that their latencies overlap
     const int nchunks = (hi - lo) * 16;
     constexpr int kPer = kBlock * 16 / kThreads;
+    // rows of 256 bytes: chunk c of the staged rows lies c * 16 bytes past the first row
+    // (a uniform 64-bit base and a 32-bit per-lane offset)
+    const uint8_t *row0 = src + (tok_off + lo) * row_stride;
     uint4 v[kPer];
 #pragma unroll
     for (int t = 0; t < kPer; ++t) {
@@ -343,7 +346,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
       const int c = min(tid + t * kThreads, nchunks - 1);
       // (nontemporal: each source row is read once)
       typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-      const u32x4 w = __builtin_nontemporal_load((const u32x4 *)(src + (tok_off + lo + c / 16) * row_stride + (c % 16) * 16));
+      const u32x4 w = __builtin_nontemporal_load((const u32x4 *)(row0 + (uint32_t)c * 16u));
       v[t] = make_uint4(w.x, w.y, w.z, w.w);
     }
     // the loaded registers pass through empty asm statements: the loads stay here, all issued
