@@ -20,10 +20,18 @@
  *
  * Conventions for every call:
  *  - Device pointers are HIP device addresses owned by the caller.  The library never
- *    allocates or frees device memory and never synchronizes the host with the device.
+ *    allocates or frees device memory and never synchronizes the host with the device, with
+ *    one exception: a ragged-batch decode call waits when every pinned host slot of its
+ *    cache still has a table copy queued (max(8, 2 * num_layers) slots, at most 256).
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is
  *    enqueued on it in call order; calls on one cache must be serialized on one stream.
- *  - Host bookkeeping (lengths) advances when a call enqueues its work.
+ *  - Host bookkeeping (lengths) advances when a call enqueues its work, so a call's device
+ *    work is fixed when it is enqueued.  Under HIP graph capture, a captured decode call
+ *    (uniform batch) replays the same attention over the same tokens each time: its counters
+ *    and cursors in the workspace are back at zero when each launch ends, and no call records
+ *    a memset.  Replaying a captured append writes the same slots again without advancing
+ *    the lengths, and a ragged decode call's table copy reads a pinned slot that later calls
+ *    reuse, so neither is meant to be captured.
  *  - Return value: KVQ_OK (0) or a negative kvq_status.  Every argument and capacity check
  *    happens before anything is enqueued; on any error except KVQ_EHIP nothing is enqueued
  *    and the cache state is unchanged.  KVQ_EHIP means a kernel launch failed; the
@@ -101,8 +109,14 @@ typedef struct {
                            0: a stored token keeps its tier. */
 } kvq_config;
 
-/* Bytes of device memory a cache with this configuration needs (0 if cfg is invalid).
-   Host-only. */
+/* Bytes of device memory a cache with this configuration needs (0 if cfg is invalid):
+   per layer the fp16 residual (R slots of K and V), the young tier arena and the old tier
+   arena of every (batch, kv_head), each region 256-byte aligned.  A tier arena holds
+   ceil(slots / 128) blocks of its format's size (144 bytes per token for INT4 and NVFP4, 80
+   for INT2, 272 for INT8, 136 for MXFP4, 256 for FP8, 512 for FP16, per kv head; page "KV
+   Cache量化实战：Model Optimizer为大模型长上下文省下50%显存", section on why long context runs
+   out of memory first, gives the size as 2 * layers * kv heads * head_dim * tokens * bytes
+   per value, which these sizes follow plus their scales).  Host-only. */
 size_t kvq_cache_bytes(const kvq_config *cfg);
 
 /* Create a cache over caller-owned device memory dev_buf of dev_bytes bytes (256-byte
@@ -140,7 +154,9 @@ int kvq_append_seq(kvq_cache *c, int32_t layer, int32_t seq, const void *k, cons
                    void *stream);
 
 /* Quantize the r tokens currently in the residual of `layer` (one chunk per sequence) and
-   empty it.  No-op for a sequence with r = 0.  Errors: KVQ_EINVAL, KVQ_ESTATE (per-channel K
+   empty it (page "KV缓存量化技术：提升大模型长文本生成效率" §2.2: the residual's tokens are
+   quantized, merged into the quantized cache and the residual cleared; here that happens on
+   demand as well as when a full residual meets a new token).  No-op for a sequence with r = 0.  Errors: KVQ_EINVAL, KVQ_ESTATE (per-channel K
    and a partial window), KVQ_EHIP. */
 int kvq_flush_residual(kvq_cache *c, int32_t layer, void *stream);
 
@@ -150,7 +166,12 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t num_q_heads);
 
 /* Attention of one query token per (batch, query head) over every token cached in `layer`:
    out[b][h] = softmax(softmax_scale * q[b][h] . K_hat^T) . V_hat with query head h reading kv
-   head h / (num_q_heads / num_kv_heads).
+   head h / (num_q_heads / num_kv_heads).  The decoding step of page "NVFP4 KV缓存技术详解"
+   §2.1 (each new token attends over the whole cached history), reading the low-precision
+   cache itself rather than a dequantized copy (page "KV Cache量化实战：Model Optimizer为大模型
+   长上下文省下50%显存", questions section: the engine must actually read the low-precision
+   cache for the savings to hold); K_hat, V_hat are the decoded values of each format (affine:
+   S*(q-Z), page "KV缓存量化技术：提升大模型长文本生成效率" §2.1) and the residual's fp16 values.
    q: fp16 [batch][num_q_heads][128]; out: [batch][num_q_heads][128] fp32 if out_fp32 else
    fp16; workspace: at least kvq_decode_workspace_bytes() bytes, 16-byte aligned, scratch
    owned by the caller (its contents on entry do not matter).  The cache is not modified.
@@ -158,7 +179,7 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t num_q_heads);
    must be positive and finite.  In a ragged batch each sequence attends over its own tokens
    (a sequence with none gets zeros), and the launch's work is split over the sequences in
    proportion to their cached bytes; the per-sequence tables are copied into the workspace
-   on the stream (stream-ordered, from host memory).
+   on the stream (stream-ordered, from pinned host memory).
    Errors: KVQ_EINVAL, KVQ_ENOSPACE (workspace), KVQ_ESTATE (every sequence empty), KVQ_EHIP. */
 int kvq_decode_attn(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_heads, float softmax_scale,
                     void *out, int32_t out_fp32, void *workspace, size_t ws_bytes, void *stream);
@@ -218,6 +239,10 @@ typedef struct {
 int kvq_seq_info(const kvq_cache *c, int32_t layer, int32_t seq, kvq_seq_info_t *info);
 
 /* Where a region of a layer lives: region 0 = fp16 residual, 1 = young tier, 2 = old tier.
+   The byte layout inside a region is this library's own (the pages give none): 128-slot blocks
+   per (batch, kv_head) in the lane order the decode kernel reads, the residual as K rows then
+   V in 16-slot tiles; the oracle's layout module writes the same bytes from its own
+   specification.
    *offset: byte offset of the region in dev_buf; *bytes: bytes of the region (all batch
    entries and kv heads, [batch][kv_head][...]); *tokens: slots in use per (batch, kv_head)
    of sequence 0 (every sequence's when all are in one state; kvq_seq_info gives each), for

@@ -7,7 +7,8 @@ batch is bitwise equal to the separate calls on a twin cache (deterministic spli
 
 Keys are normal, values the adversarial patterns: the ragged bookkeeping is the subject here
 (the quantizers' adversarial keys are covered by the batch tests), and adversarial keys make
-logits of thousands whose near-ties the fp32 logits cannot resolve."""
+logits of thousands whose near-ties the fp32 logits cannot resolve (that regime is checked
+against its fp32 error bound in test_gpu_numeric_regimes.py)."""
 import numpy as np
 import pytest
 import torch
