@@ -82,6 +82,8 @@ struct QuantArgs {
   int fmt;
   int gs;                         // affine group size (32, 64, 128; kKc: K per channel)
   int B, H;
+  int nsplit;                     // workgroups per block (1, or 4: one per 32-slot part; set by
+                                  // launch_quantize)
 };
 
 // Copy of caller tokens [src_tok0, src_tok0 + count) into residual slots [dst_slot0, ...).

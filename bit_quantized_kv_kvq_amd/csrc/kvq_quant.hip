@@ -304,18 +304,27 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
 
   const int tid = threadIdx.x;
   if (tid == 0) s_eps = 0u;
-  const int64_t blk = blk0 + blockIdx.x;
+  // a.nsplit workgroups per block, workgroup `sub` taking the slots [ps, pe) of one or more
+  // whole 32-slot parts: every code word and every (S, Z) belongs to one part, so the
+  // workgroups of a block write disjoint words
+  const int nsplit = a.nsplit, sub = (int)(blockIdx.x % (unsigned)nsplit);
+  const int64_t blk = blk0 + blockIdx.x / (unsigned)nsplit;
+  const int ps = sub * (kBlock / nsplit), pe = ps + kBlock / nsplit;
   const int h = blockIdx.y, b = blockIdx.z >> 1, kv = blockIdx.z & 1;
   const int64_t bstart = blk * kBlock;
-  const int lo = (int)(max(a.dst_slot0, bstart) - bstart);
-  const int hi = (int)(min(a.dst_slot0 + a.count, bstart + kBlock) - bstart);
-  const bool last = blockIdx.x == nblk - 1;
-  const int zhi = last ? kBlock : hi;             // slots [hi, zhi) are cleared
+  const int lo = max((int)(max(a.dst_slot0, bstart) - bstart), ps);
+  const int hi_blk = (int)(min(a.dst_slot0 + a.count, bstart + kBlock) - bstart);
+  const int hi = max(lo, min(hi_blk, pe));
+  const bool last = blk == blk0 + nblk - 1;
+  const int zhi = max(hi, min(last ? kBlock : hi_blk, pe));   // slots [hi, zhi) are cleared
+  if (lo >= zhi) return;                          // a part before this append's first slot
   uint8_t *blkp = a.arena + (int64_t)(b * a.H + h) * a.arena_bh_stride + blk * (int64_t)kBlockBytes;
   const int64_t tok_off = a.src_tok0 + bstart - a.dst_slot0;   // source index of slot 0
 
-  // ---- stage the source tokens of slots [lo, hi) in LDS as fp16 rows
-  if (a.src_kind == 2) {
+  // ---- stage the source tokens of slots [lo, hi) in LDS as fp16 rows (none when this
+  // workgroup's parts only clear slots past the append)
+  if (hi == lo) {
+  } else if (a.src_kind == 2) {
     // slots [lo, hi) come from one block of the source arena
     const int64_t s0 = tok_off + lo;
     const uint8_t *yb = a.src_arena + (int64_t)(b * a.H + h) * a.src_bh_stride +
@@ -360,13 +369,30 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
       if (c < nchunks) *(uint4 *)&xs[(lo + c / 16) * kRowHalves + (c % 16) * 8] = v[t];
     }
   } else {
-    // residual V: [R/16][128][16] fp16
+    // residual V: [R/16][128][16] fp16, 16 slots of one dim together.  Runs of 8 residual
+    // slots starting at a multiple of 8 come as one 16-byte load per dim (scattered into 8 LDS
+    // rows); the slots before the first and after the last such run one value at a time.
     const uint16_t *src = (const uint16_t *)(a.res_base + (int64_t)(b * a.H + h) * a.res_bh_stride + (int64_t)a.res_len * 256);
-    const int nel = (hi - lo) * kHeadDim;
-    for (int e = tid; e < nel; e += kThreads) {
-      const int row = lo + e / kHeadDim, d = e % kHeadDim;
-      const int64_t t = tok_off + row;
-      xs[row * kRowHalves + d] = src[((t / 16) * kHeadDim + d) * 16 + t % 16];
+    const int t_lo = (int)(tok_off + lo), t_hi = (int)(tok_off + hi);   // residual slots of rows [lo, hi)
+    const int r0 = (t_lo + 7) & ~7, r1 = t_hi & ~7;
+    const int nrun = r1 > r0 ? (r1 - r0) >> 3 : 0;
+    const int head = nrun ? r0 - t_lo : t_hi - t_lo;                  // loose slots before the runs
+    for (int e = tid; e < nrun * kHeadDim; e += kThreads) {
+      const int t0 = r0 + 8 * (e >> 7), d = e & 127;
+      const uint4 x = *(const uint4 *)(src + ((t0 >> 4) * kHeadDim + d) * 16 + (t0 & 15));
+      uint16_t *dst = &xs[(t0 - (int)tok_off) * kRowHalves + d];
+      const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dst[(2 * i) * kRowHalves] = (uint16_t)(w4[i] & 0xFFFFu);
+        dst[(2 * i + 1) * kRowHalves] = (uint16_t)(w4[i] >> 16);
+      }
+    }
+    const int nloose = head + (nrun ? t_hi - r1 : 0);
+    for (int e = tid; e < nloose * kHeadDim; e += kThreads) {
+      const int i = e >> 7, d = e & 127;
+      const int t = i < head ? t_lo + i : r1 + (i - head);
+      xs[(t - (int)tok_off) * kRowHalves + d] = src[((t >> 4) * kHeadDim + d) * 16 + (t & 15)];
     }
   }
   __syncthreads();
@@ -617,7 +643,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
     constexpr int kLaneBytes = 4 * kBits;
     constexpr int kCb = kLaneBytes < 16 ? kLaneBytes : 16;
     constexpr int kK = kLaneBytes / kCb;
-    for (int w = tid; w < kWords; w += kThreads) {
+    const int wend = (sub + 1) * (kWords / nsplit);   // the words of this workgroup's parts
+    for (int w = sub * (kWords / nsplit) + tid; w < wend; w += kThreads) {
       const int ci = (4 * w) / kCb, in_chunk = (4 * w) % kCb;
       const int lane = ci & 63, t2 = ci >> 6;
       const int r = t2 % kK, wu = t2 / kK;
@@ -689,7 +716,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
     constexpr int NL = 4 * 4 * kLaneWords * 2 >= kThreads ? 8 : 4 * 4 * kLaneWords * 4 >= kThreads ? 4 : 2;
     constexpr int kSplit = 16 / NL;
     constexpr int kTasks = 4 * 4 * kLaneWords * kSplit;
-    for (int task = tid; task < kTasks; task += kThreads) {
+    const int tend = (sub + 1) * (kTasks / nsplit);   // tasks are part-major: this workgroup's parts
+    for (int task = sub * (kTasks / nsplit) + tid; task < tend; task += kThreads) {
       const int c0 = NL * (task % kSplit), omega = (task / kSplit) % kLaneWords, g = ((task / kSplit) / kLaneWords) & 3;
       const int part = (task / kSplit) / kLaneWords >> 2;
       uint32_t words[NL] = {};
@@ -754,12 +782,29 @@ __global__ __launch_bounds__(256) void residual_copy_kernel(ResCopyArgs a) {
 
 }  // namespace
 
-hipError_t launch_quantize(const QuantArgs &a, hipStream_t s) {
-  if (a.count <= 0) return hipSuccess;
-  const int64_t blk0 = a.dst_slot0 / kBlock;
-  const int64_t blk1 = (a.dst_slot0 + a.count - 1) / kBlock;
+// Compute units of the current device (256 if the query fails), looked up once per device.
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cus[dev];
+}
+
+hipError_t launch_quantize(const QuantArgs &in, hipStream_t s) {
+  if (in.count <= 0) return hipSuccess;
+  const int64_t blk0 = in.dst_slot0 / kBlock;
+  const int64_t blk1 = (in.dst_slot0 + in.count - 1) / kBlock;
   const int64_t nblk = blk1 - blk0 + 1;
-  dim3 grid((unsigned)nblk, (unsigned)a.H, (unsigned)(a.B * 2));
+  // A launch of few blocks (a residual flush: one or two blocks per (b, h)) leaves most CUs
+  // idle with one workgroup per block: affine formats with per-token groups then take one
+  // workgroup per 32-slot part.
+  QuantArgs a = in;
+  a.nsplit = is_affine(a.fmt) && a.gs != kKc && nblk * a.H * a.B * 2 < 2 * device_cus() ? 4 : 1;
+  dim3 grid((unsigned)(nblk * a.nsplit), (unsigned)a.H, (unsigned)(a.B * 2));
 #define KVQ_AFFINE_CASE(F)                                                                             \
   case F:                                                                                              \
     if (a.gs == kKc) quantize_kernel<F, kKc><<<grid, kThreads, 0, s>>>(a, blk0, nblk);                 \
