@@ -321,7 +321,25 @@ int run_plan(kvq_cache *c, int layer, const Plan &p, const void *k, const void *
   const size_t b0 = seq < 0 ? 0 : (size_t)seq * cfg.num_kv_heads;   // first (b, h) of the launch
   uint8_t *res = c->res(layer) + b0 * c->geo.res_bh;
   uint8_t *young = c->young(layer) + b0 * c->geo.young_bh, *old = c->old(layer) + b0 * c->geo.old_bh;
-  for (const Op &op : p.ops) {
+  // A flush of the whole residual whose plan ends with the copy that refills the residual from
+  // slot 0: the flush's launch does the copy (each workgroup refills the slots it read; the ops
+  // between the two read the caller's tokens or the young arena, never the residual).
+  const int nops = (int)p.ops.size();
+  int fuse_q = -1;
+  if (nops >= 2 && p.ops.back().kind == Op::kResCopy && p.ops.back().dst_slot0 == 0 && p.ops.back().count > 0 &&
+      p.ops.back().count <= cfg.residual_len) {
+    for (int i = nops - 2; i >= 0; --i) {
+      const Op &o = p.ops[i];
+      if (o.kind == Op::kQuantResidual) {
+        if (o.src_tok0 == 0 && o.count == cfg.residual_len) fuse_q = i;
+        break;
+      }
+      if (o.kind == Op::kResCopy) break;
+    }
+  }
+  for (int i = 0; i < nops; ++i) {
+    const Op &op = p.ops[i];
+    if (fuse_q >= 0 && i == nops - 1) break;   // done by the flush
     if (op.kind == Op::kResCopy) {
       ResCopyArgs a{};
       a.k_src = (const uint16_t *)k; a.v_src = (const uint16_t *)v; a.src_ntok = n;
@@ -350,6 +368,10 @@ int run_plan(kvq_cache *c, int layer, const Plan &p, const void *k, const void *
         return fail(KVQ_ESTATE, "per-channel K: a quantize of %lld slots at %lld is not whole windows",
                     (long long)op.count, (long long)op.dst_slot0);
       a.B = B; a.H = cfg.num_kv_heads;
+      if (i == fuse_q) {
+        a.cp_count = (int)p.ops.back().count;
+        a.cp_src_tok0 = p.ops.back().src_tok0;
+      }
       if (int e = hip_check(launch_quantize(a, s), "quantize")) return e;
     }
   }

@@ -70,7 +70,7 @@ struct QuantArgs {
   int src_fmt;                    // kind 2: affine format code of the source block
   const uint16_t *k_src, *v_src;  // kind 0
   int64_t src_ntok;               // kind 0: tokens per (b, h) in the input tensor
-  const uint8_t *res_base;        // kind 1: residual region of the layer
+  uint8_t *res_base;              // kind 1: residual region of the layer (written by cp_count)
   int64_t res_bh_stride;          // kind 1: bytes per (b, h) residual
   int res_len;                    // kind 1: R
   int64_t src_tok0;
@@ -84,6 +84,11 @@ struct QuantArgs {
   int B, H;
   int nsplit;                     // workgroups per block (1, or 4: one per 32-slot part; set by
                                   // launch_quantize)
+  // kind 1 over the whole residual (src_tok0 0, count R): after reading its residual slots a
+  // workgroup writes caller tokens [cp_src_tok0, cp_src_tok0 + cp_count) of k_src / v_src
+  // ([B][H][src_ntok][128]) into residual slots [0, cp_count); cp_count 0: no copy
+  int cp_count;
+  int64_t cp_src_tok0;
 };
 
 // Copy of caller tokens [src_tok0, src_tok0 + count) into residual slots [dst_slot0, ...).

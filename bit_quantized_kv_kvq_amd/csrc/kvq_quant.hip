@@ -396,6 +396,18 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
     }
   }
   __syncthreads();
+  // A flush followed by the refill of the residual it read: each workgroup refills the residual
+  // slots it staged (the slots of different workgroups are disjoint, and this one's reads are
+  // complete at the barrier above).
+  if (a.cp_count > 0 && hi > lo) {
+    const int t_lo = (int)(tok_off + lo), t_hi = min((int)(tok_off + hi), a.cp_count);
+    if (t_hi > t_lo) {
+      const uint16_t *src = (kv ? a.v_src : a.k_src) + ((int64_t)(b * a.H + h) * a.src_ntok + a.cp_src_tok0 + t_lo) * kHeadDim;
+      uint8_t *res = a.res_base + (int64_t)(b * a.H + h) * a.res_bh_stride;
+      if (kv == 0) residual_store_k(src, t_hi - t_lo, t_lo, res, tid, kThreads);
+      else residual_store_v(src, t_hi - t_lo, t_lo, res, a.res_len, tid, kThreads);
+    }
+  }
   if constexpr (kF16) {
     store_fp16_block(xs, blkp, kv, lo, hi, zhi, tid);
     return;

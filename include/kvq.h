@@ -140,8 +140,10 @@ int kvq_cache_reset(kvq_cache *c);
    Each sequence of the batch keeps its own schedule (page "KV缓存量化技术：提升大模型长文本
    生成效率" §2.2 describes it for one sequence): when the sequences are at different points
    (a ragged batch, see kvq_append_seq), each follows its own, in launches of its own where
-   they differ.  n_tokens = 0 is a no-op.  Errors: KVQ_EINVAL, KVQ_ECAPACITY (checked for
-   every sequence before anything is enqueued), KVQ_EHIP. */
+   they differ.  An append that flushes a full residual and then refills it is one launch: the
+   flush's workgroups write the new tokens into the residual slots they have just read.
+   n_tokens = 0 is a no-op.  Errors: KVQ_EINVAL, KVQ_ECAPACITY (checked for every sequence
+   before anything is enqueued), KVQ_EHIP. */
 int kvq_append(kvq_cache *c, int32_t layer, const void *k, const void *v, int64_t n_tokens, void *stream);
 
 /* Append n_tokens new tokens to sequence `seq` (0 <= seq < batch) of layer `layer` alone, as
@@ -207,8 +209,9 @@ int kvq_decode_attn_noalloc(kvq_cache *c, int32_t layer, const void *q, int32_t 
    decoding and cache-update phases).  When at most 64 new tokens go to the fp16 residual
    (no flush, or after the flush that a full residual takes first), the decode launch itself
    writes them there before it reads the residual, so the step costs one launch instead of
-   two (more tokens are copied by the append's own copy launch, which spreads them over more
-   workgroups than the one that reads the residual).  NVFP4 without a residual quantizes a
+   two (more tokens are written by the append's own launches, which spread them over more
+   workgroups than the one that reads the residual: by the flush launch when the step
+   flushes, else by a copy launch).  NVFP4 without a residual quantizes a
    one-token step inside the decode launch.  All
    arguments of both calls are checked before anything is enqueued; errors as for the two
    calls (on KVQ_EHIP during the append part, the append state has advanced as kvq_append's
