@@ -414,7 +414,11 @@ struct State {
   float z[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};   // affine V: this lane's share of
                        // sum P' Z of group G (z[2G]; the scaled positions of INT4 / INT2 in z[2G + 1])
   float4_t o[8];       // O^T[dims 16k + 4g + i][head c]
+  float nm = 0.0f;     // -m sl2 (0 while m = -inf): the exponent offset of softmax_step2, set with
+                       // m and the scale sl2 in use (set_nm)
+  uint64_t vmask = 0;  // lanes of the wave whose head is valid (wave-uniform)
 };
+__device__ __forceinline__ void set_nm(State &st, float sl2) { st.nm = st.m == kNegInf ? 0.0f : -st.m * sl2; }
 
 // Update the running max with 8 unscaled logits (slots (tt, i) = (e >> 2, e & 3)) and return
 // p = exp2(sl2 (s - m)), sl2 = softmax_scale * log2(e) > 0; positions whose A element is scaled
@@ -980,7 +984,8 @@ template <int SH = 0>
 __device__ __forceinline__ void softmax_step2(State &st, const float (&s)[4], float (&p)[4], bool valid_head,
                                               unsigned scaled_mask, float sl2) {
   const float ml = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-  if (__builtin_amdgcn_ballot_w64(valid_head && ml > st.m + st.slack) != 0) {
+  // (the compare's lane mask as it is, masked by the valid heads')
+  if ((__builtin_amdgcn_ballot_w64(ml > st.m + st.slack) & st.vmask) != 0) {
     const float m_new = fmaxf(st.m, head_max2(ml));
     const float alpha = (m_new == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f((st.m - m_new) * sl2);
     st.l *= alpha;
@@ -989,15 +994,17 @@ __device__ __forceinline__ void softmax_step2(State &st, const float (&s)[4], fl
 #pragma unroll
     for (int k = 0; k < 8; ++k) st.o[k] *= alpha;
     st.m = m_new;
+    set_nm(st, sl2);
   }
-  const float nm = st.m == kNegInf ? 0.0f : -st.m * sl2;
+  const float nm = st.nm;
   const float nm4 = nm - (float)SH;
   float ls = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const bool sc = (scaled_mask >> i) & 1;
     p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, sc ? nm4 : nm));
-    ls = sc ? fmaf((float)(1 << SH), p[i], ls) : ls + p[i];
+    if (i == 0) ls = sc ? (float)(1 << SH) * p[i] : p[i];
+    else ls = sc ? fmaf((float)(1 << SH), p[i], ls) : ls + p[i];
   }
   st.l += ls;
 }
@@ -1015,9 +1022,11 @@ __device__ __forceinline__ half4_t v_operand2<4>(const uint32_t *vw, int k, int 
 template <>
 __device__ __forceinline__ half4_t v_operand2<2>(const uint32_t *vw, int k, int s0) {
   // word k >> 1 holds tiles 2(k>>1) + a; pairs (crumb s, crumb s+8), s = 4a + 2 s0 + {0, 1},
-  // the second pair in place (times 4: slots i = 2, 3 carry P / 4)
-  const uint32_t x = vw[k >> 1] >> (2 * (4 * (k & 1) + 2 * s0));
-  return h4(x & 0x00030003u, x & 0x000C000Cu);
+  // the second pair in place (times 4: slots i = 2, 3 carry P / 4).  The word is shifted by 8
+  // for a = 1 only: subtile 1's crumbs are masked in place, times 16, so that the columns of
+  // subtile 1 accumulate 16 times their sums (taken out at the end of the tier, exactly).
+  const uint32_t x = (k & 1) ? vw[k >> 1] >> 8 : vw[k >> 1];
+  return s0 ? h4(x & 0x00300030u, x & 0x00C000C0u) : h4(x & 0x00030003u, x & 0x000C000Cu);
 }
 template <>
 __device__ __forceinline__ half4_t v_operand2<8>(const uint32_t *vw, int k, int s0) {
@@ -1539,6 +1548,7 @@ __device__ __forceinline__ void residual_part(const DecodeArgs &a, const Item &i
   if constexpr (NSUB == 2) {
     QOp2 q;
     load_q2<kFmtFp16, kGroup>(qrow, valid_head, g, c, q);
+    set_nm(st, a.scale_log2);
     for (int u = w; u < nsteps; u += kWaves) residual_step2(res, a.res_len, it.res_ntok, u, g, c, q, a.scale_log2, valid_head, st);
   } else {
     QOp q;
@@ -1650,11 +1660,16 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
   // power-of-two scale
   const float qscale = NSUB == 2 ? q2.qscale : q.qscale;
   const float sl2 = kAff ? a.scale_log2 * (kInvSub / qscale) : a.scale_log2;
+  // INT2 in paired subtiles: the columns of subtile 1 accumulate 16 times their PV sums
+  // (v_operand2<2>); the factor is exact and taken out with the units below
+  constexpr bool kO16 = FMT == kFmtInt2 && NSUB == 2;
+  const float ofac = kO16 && (c >> 3) ? 16.0f : 1.0f;
   if constexpr (kAff) {
     if (st.m != kNegInf) st.m *= kSub * qscale;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) st.o[k] = st.o[k] * kSub;
+    for (int k = 0; k < 8; ++k) st.o[k] = st.o[k] * (kSub * ofac);
   }
+  if constexpr (NSUB == 2) set_nm(st, sl2);
   int buf = 0;
   for (int p = 0; p < iss_end; ++p) {
     if (!dispatcher) {
@@ -1726,7 +1741,7 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
       if (!take) zg[G] = 0.0f;
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) st.o[k] = st.o[k] * kInvSub - zg[v_group<GS>(k)];
+    for (int k = 0; k < 8; ++k) st.o[k] = st.o[k] * (kInvSub / ofac) - zg[v_group<GS>(k)];
 #pragma unroll
     for (int i = 0; i < 8; ++i) st.z[i] = 0.0f;
   }
@@ -1949,6 +1964,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeArgs a) {
   State st;
 #pragma unroll
   for (int k = 0; k < 8; ++k) st.o[k] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  st.vmask = __builtin_amdgcn_ballot_w64(valid_head);
 
   // part 0 opens the arrival counter early, so that the arrivals find it open (wave 3 loads no
   // blocks, so its wait here holds up nothing else)
