@@ -1841,7 +1841,10 @@ __device__ __forceinline__ void merge_tail(const MergeGeom &m, const float *part
 }
 
 // Per-wave state -> LDS rows for the workgroup merge: m[16], l[16] (log2 units) and
-// o[16][128], heads in natural order.
+// o[16][kWoStride], heads in natural order.  The rows are 128 dims plus 16 floats of padding:
+// the 8 (or 16) lanes of one quarter write 16 bytes of 8 different rows at once, which with
+// 512-byte rows all fell on the same LDS banks.
+constexpr int kWoStride = kHeadDim + 16;
 template <int NSUB>
 __device__ __forceinline__ void state_to_lds(State &st, int w, int g, int c, float sl2, float *wm, float *wl, float *wo) {
   if constexpr (NSUB == 1) {
@@ -1851,7 +1854,7 @@ __device__ __forceinline__ void state_to_lds(State &st, int w, int g, int c, flo
       wl[w * 16 + c] = l;
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) *(float4_t *)(wo + ((w * 16 + c) * kHeadDim + 16 * k + 4 * g)) = st.o[k];
+    for (int k = 0; k < 8; ++k) *(float4_t *)(wo + ((w * 16 + c) * kWoStride + 16 * k + 4 * g)) = st.o[k];
   } else {
     // lane (c, g): column (subtile c >> 3, head c & 7), accumulator rows dims 16k + 4g + i;
     // the subtile-1 column of a head is lane c ^ 8
@@ -1867,7 +1870,7 @@ __device__ __forceinline__ void state_to_lds(State &st, int w, int g, int c, flo
       o[1] += __shfl_xor(o[1], 8);
       o[2] += __shfl_xor(o[2], 8);
       o[3] += __shfl_xor(o[3], 8);
-      if (c < 8) *(float4_t *)(wo + ((w * 16 + c) * kHeadDim + 16 * k + 4 * g)) = o;
+      if (c < 8) *(float4_t *)(wo + ((w * 16 + c) * kWoStride + 16 * k + 4 * g)) = o;
     }
   }
 }
@@ -2011,7 +2014,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeArgs a) {
   // ---- merge the four waves in LDS: per wave m[16], l[16], o[16][128] (m in log2 units)
   float *wm = (float *)smem;                       // [4][16]
   float *wl = wm + kWaves * 16;                    // [4][16]
-  float *wo = wl + kWaves * 16;                    // [4][16][128]
+  float *wo = wl + kWaves * 16;                    // [4][16][kWoStride]
   state_to_lds<NSUB>(st, w, g, c, a.scale_log2, wm, wl, wo);
   __syncthreads();
 
@@ -2027,7 +2030,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeArgs a) {
     for (int v = 0; v < kWaves; ++v) {
       const float mv = wm[v * 16 + hc];
       const float wt = mv == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
-      O += wt * wo[(v * 16 + hc) * kHeadDim + d];
+      O += wt * wo[(v * 16 + hc) * kWoStride + d];
       L += wt * wl[v * 16 + hc];
     }
     // Partials are written with agent-scope stores, which go past this XCD's L2, so the
@@ -2106,7 +2109,7 @@ static size_t decode_ring_bytes(const DecodeArgs &a) {
 
 size_t decode_lds_bytes(const DecodeArgs &a) {
   const size_t stream = decode_ring_bytes(a) + (size_t)a.G * kHeadDim * 2;
-  const size_t merge = (size_t)kWaves * (16 + 16 + 16 * kHeadDim) * sizeof(float);
+  const size_t merge = (size_t)kWaves * (16 + 16 + 16 * kWoStride) * sizeof(float);
   return std::max(stream, merge);
 }
 
