@@ -42,16 +42,18 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
 
 // E2M1 code (sign bit 8, magnitude index 0..7 on {0, 0.5, 1, 1.5, 2, 3, 4, 6}) of x under
 // scale s: nearest magnitude of |x| / s clipped to 6, ties to the even index; s = 0 gives a
-// signed zero.
+// signed zero.  The index counts the decision points that |x| has passed: the midpoints m_j s
+// between magnitudes j and j + 1, passed when |x| > m_j s for even j and when |x| >= m_j s for
+// odd j (a value on a midpoint then lands on the even neighbour).  The points passed form a
+// prefix, so three comparisons (a binary search over 1.75, then 0.75 or 3.5, then one of 0.25,
+// 1.25, 2.5, 5) find the count; each m_j s is exact in fp32 (3 significant bits times the 4 of
+// an E4M3 or power-of-two scale), so every comparison is exact.
 __device__ __forceinline__ uint32_t e2m1_code(float x, float s) {
-  float a = fabsf(x);
-  uint32_t idx = 0;
-  if (s > 0.0f) {
-    const float t0 = 0.25f * s, t1 = 0.75f * s, t2 = 1.25f * s, t3 = 1.75f * s, t4 = 2.5f * s, t5 = 3.5f * s, t6 = 5.0f * s;
-    idx = (a > t0) + (a > t1) + (a > t2) + (a > t3) + (a > t4) + (a > t5) + (a > t6);
-    bool tie = a == t0 || a == t1 || a == t2 || a == t3 || a == t4 || a == t5 || a == t6;
-    if (tie && (idx & 1)) ++idx;   // on midpoint idx: pick the even neighbour
-  }
+  const float a = fabsf(x);
+  const bool c1 = a >= 1.75f * s;
+  const bool c2 = a >= (c1 ? 3.5f : 0.75f) * s;
+  const bool c3 = a > (c1 ? (c2 ? 5.0f : 2.5f) : (c2 ? 1.25f : 0.25f)) * s;
+  const uint32_t idx = s > 0.0f ? 4u * c1 + 2u * c2 + (uint32_t)c3 : 0u;
   return idx | (signbit(x) ? 8u : 0u);
 }
 
