@@ -327,7 +327,7 @@ int run_plan(kvq_cache *c, int layer, const Plan &p, const void *k, const void *
   const int nops = (int)p.ops.size();
   int fuse_q = -1;
   if (nops >= 2 && p.ops.back().kind == Op::kResCopy && p.ops.back().dst_slot0 == 0 && p.ops.back().count > 0 &&
-      p.ops.back().count <= cfg.residual_len) {
+      p.ops.back().count <= cfg.residual_len && p.ops.back().src_tok0 + p.ops.back().count == n) {
     for (int i = nops - 2; i >= 0; --i) {
       const Op &o = p.ops[i];
       if (o.kind == Op::kQuantResidual) {
@@ -368,10 +368,7 @@ int run_plan(kvq_cache *c, int layer, const Plan &p, const void *k, const void *
         return fail(KVQ_ESTATE, "per-channel K: a quantize of %lld slots at %lld is not whole windows",
                     (long long)op.count, (long long)op.dst_slot0);
       a.B = B; a.H = cfg.num_kv_heads;
-      if (i == fuse_q) {
-        a.cp_count = (int)p.ops.back().count;
-        a.cp_src_tok0 = p.ops.back().src_tok0;
-      }
+      if (i == fuse_q) a.cp_count = (int)p.ops.back().count;   // the last cp_count of the n tokens
       if (int e = hip_check(launch_quantize(a, s), "quantize")) return e;
     }
   }

@@ -85,10 +85,9 @@ struct QuantArgs {
   int nsplit;                     // workgroups per block (1, or 4: one per 32-slot part; set by
                                   // launch_quantize)
   // kind 1 over the whole residual (src_tok0 0, count R): after reading its residual slots a
-  // workgroup writes caller tokens [cp_src_tok0, cp_src_tok0 + cp_count) of k_src / v_src
-  // ([B][H][src_ntok][128]) into residual slots [0, cp_count); cp_count 0: no copy
+  // workgroup writes the caller's last cp_count tokens of k_src / v_src ([B][H][src_ntok][128])
+  // into residual slots [0, cp_count); cp_count 0: no copy
   int cp_count;
-  int64_t cp_src_tok0;
 };
 
 // Copy of caller tokens [src_tok0, src_tok0 + count) into residual slots [dst_slot0, ...).

@@ -276,7 +276,9 @@ __device__ void stage_affine_decoded(const uint8_t *yb, int n, int kv, int row_o
   }
 }
 
-template <int FMT, int GS>
+// REFILL: the launch also refills the residual it flushes (cp_count > 0); a separate
+// instantiation, so that the other launches (the bulk prefill among them) keep their registers.
+template <int FMT, int GS, bool REFILL>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t blk0, int64_t nblk) {
   constexpr bool kMx = FMT == kFmtMxfp4;
   constexpr bool kNv = FMT == kFmtNvfp4 || kMx;          // E2M1 codes (NVFP4 or MXFP4 scales)
@@ -397,15 +399,18 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
   }
   __syncthreads();
   // A flush followed by the refill of the residual it read: each workgroup refills the residual
-  // slots it staged (the slots of different workgroups are disjoint, and this one's reads are
-  // complete at the barrier above).
-  if (a.cp_count > 0 && hi > lo) {
-    const int t_lo = (int)(tok_off + lo), t_hi = min((int)(tok_off + hi), a.cp_count);
-    if (t_hi > t_lo) {
-      const uint16_t *src = (kv ? a.v_src : a.k_src) + ((int64_t)(b * a.H + h) * a.src_ntok + a.cp_src_tok0 + t_lo) * kHeadDim;
-      uint8_t *res = a.res_base + (int64_t)(b * a.H + h) * a.res_bh_stride;
-      if (kv == 0) residual_store_k(src, t_hi - t_lo, t_lo, res, tid, kThreads);
-      else residual_store_v(src, t_hi - t_lo, t_lo, res, a.res_len, tid, kThreads);
+  // slots it staged with the caller's last cp_count tokens (the slots of different workgroups are
+  // disjoint, and this one's reads completed before the barrier above); the stores go out here,
+  // ahead of the codes, so that they complete while the codes are computed.
+  if constexpr (REFILL) {
+    if (a.cp_count > 0 && hi > lo) {
+      const int t_lo = (int)(tok_off + lo), t_hi = min((int)(tok_off + hi), a.cp_count);
+      if (t_hi > t_lo) {
+        const uint16_t *src = (kv ? a.v_src : a.k_src) + ((int64_t)(b * a.H + h) * a.src_ntok + a.src_ntok - a.cp_count + t_lo) * kHeadDim;
+        uint8_t *res = a.res_base + (int64_t)(b * a.H + h) * a.res_bh_stride;
+        if (kv == 0) residual_store_k(src, t_hi - t_lo, t_lo, res, tid, kThreads);
+        else residual_store_v(src, t_hi - t_lo, t_lo, res, a.res_len, tid, kThreads);
+      }
     }
   }
   if constexpr (kF16) {
@@ -806,6 +811,12 @@ int device_cus() {
   return cus[dev];
 }
 
+template <int F, int GS>
+void launch_quantize_as(const QuantArgs &a, dim3 grid, int64_t blk0, int64_t nblk, hipStream_t s) {
+  if (a.cp_count > 0) quantize_kernel<F, GS, true><<<grid, kThreads, 0, s>>>(a, blk0, nblk);
+  else quantize_kernel<F, GS, false><<<grid, kThreads, 0, s>>>(a, blk0, nblk);
+}
+
 hipError_t launch_quantize(const QuantArgs &in, hipStream_t s) {
   if (in.count <= 0) return hipSuccess;
   const int64_t blk0 = in.dst_slot0 / kBlock;
@@ -817,22 +828,22 @@ hipError_t launch_quantize(const QuantArgs &in, hipStream_t s) {
   QuantArgs a = in;
   a.nsplit = is_affine(a.fmt) && a.gs != kKc && nblk * a.H * a.B * 2 < 2 * device_cus() ? 4 : 1;
   dim3 grid((unsigned)(nblk * a.nsplit), (unsigned)a.H, (unsigned)(a.B * 2));
-#define KVQ_AFFINE_CASE(F)                                                                             \
-  case F:                                                                                              \
-    if (a.gs == kKc) quantize_kernel<F, kKc><<<grid, kThreads, 0, s>>>(a, blk0, nblk);                 \
-    else if (a.gs == 32) quantize_kernel<F, 32><<<grid, kThreads, 0, s>>>(a, blk0, nblk);              \
-    else if (a.gs == 128) quantize_kernel<F, 128><<<grid, kThreads, 0, s>>>(a, blk0, nblk);            \
-    else if (a.gs == 64) quantize_kernel<F, 64><<<grid, kThreads, 0, s>>>(a, blk0, nblk);              \
-    else return hipErrorInvalidValue;                                                                  \
+#define KVQ_AFFINE_CASE(F)                                                     \
+  case F:                                                                      \
+    if (a.gs == kKc) launch_quantize_as<F, kKc>(a, grid, blk0, nblk, s);       \
+    else if (a.gs == 32) launch_quantize_as<F, 32>(a, grid, blk0, nblk, s);    \
+    else if (a.gs == 128) launch_quantize_as<F, 128>(a, grid, blk0, nblk, s);  \
+    else if (a.gs == 64) launch_quantize_as<F, 64>(a, grid, blk0, nblk, s);    \
+    else return hipErrorInvalidValue;                                          \
     break;
   switch (a.fmt) {
     KVQ_AFFINE_CASE(kFmtInt2)
     KVQ_AFFINE_CASE(kFmtInt4)
     KVQ_AFFINE_CASE(kFmtInt8)
-    case kFmtNvfp4: quantize_kernel<kFmtNvfp4, 64><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
-    case kFmtFp8: quantize_kernel<kFmtFp8, 64><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
-    case kFmtMxfp4: quantize_kernel<kFmtMxfp4, 64><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
-    case kFmtFp16: quantize_kernel<kFmtFp16, 64><<<grid, kThreads, 0, s>>>(a, blk0, nblk); break;
+    case kFmtNvfp4: launch_quantize_as<kFmtNvfp4, 64>(a, grid, blk0, nblk, s); break;
+    case kFmtFp8: launch_quantize_as<kFmtFp8, 64>(a, grid, blk0, nblk, s); break;
+    case kFmtMxfp4: launch_quantize_as<kFmtMxfp4, 64>(a, grid, blk0, nblk, s); break;
+    case kFmtFp16: launch_quantize_as<kFmtFp16, 64>(a, grid, blk0, nblk, s); break;
     default: return hipErrorInvalidValue;
   }
 #undef KVQ_AFFINE_CASE
