@@ -350,20 +350,23 @@ __device__ __forceinline__ void load_q(const uint16_t *qrow, bool valid, int g, 
 }
 
 // ---------------------------------------------------------------- LDS DMA
-// 16 bytes per lane from global `src` to LDS address lds + 16 * lane (wave-uniform lds).
-// M0 is saved and restored around the load so the compiler's use of it is undisturbed.
-// The cache bytes are read once per call: the load carries the nontemporal policy (nt), with
-// which a plain read stream of 4 GiB ran at 6.4-6.5 TB/s against 5.6-6.0 TB/s without.
-__device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
+// 16 bytes per lane from global sbase + voff (wave-uniform 64-bit base in scalar registers,
+// per-lane 32-bit offset) to LDS address lds + 16 * lane (wave-uniform lds).  With the base in
+// scalar registers the per-block address arithmetic is scalar work, not three vector
+// instructions per load.  M0 is saved and restored around the load so the compiler's use of
+// it is undisturbed.  The cache bytes are read once per call: the load carries the
+// nontemporal policy (nt), with which a plain read stream of 4 GiB ran at 6.4-6.5 TB/s against
+// 5.6-6.0 TB/s without.
+__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t lds) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off nt\n\t"
+      "global_load_lds_dwordx4 %1, %2 nt\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(src), "s"(lds)
+      : "v"(voff), "s"(sbase), "s"(lds)
       : "memory");
 }
 
@@ -1578,7 +1581,8 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
   const bool dyn = fixed_end < nblk;                          // a cursor hands out the rest
   // item 0 opens the cursor early, so that the other items' first fetch-adds find it open
   if (dyn && j == 0 && dispatcher && lane == 0) counter_open(cursor, a.epoch);
-  const uint8_t *gbh = sg.base + (int64_t)it.bh * sg.bh_stride + lane * 16;
+  const uint8_t *gbh = sg.base + (int64_t)it.bh * sg.bh_stride;   // wave-uniform; lanes add 16 * lane
+  const uint32_t lane_off = (uint32_t)lane * 16u;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   const int nbuf = decode_ring_depth(bb);
   const uint16_t *qlds = (const uint16_t *)(smem + a.q_lds_off);   // the group's query rows
@@ -1626,13 +1630,13 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
     const int phys = blk_idx + rot < nblk ? blk_idx + rot : blk_idx + rot - nblk;
     const int slot = iss_end % nbuf;
     if (!dispatcher) {
-      const uint8_t *src = gbh + (int64_t)phys * bb;
-      const uint32_t dst = lds0 + (uint32_t)(slot * bb);
+      const uint8_t *src = gbh + (int64_t)phys * bb;   // uniform
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(slot * bb));   // M0 takes a scalar
       for (int jj = w; jj < ndma; jj += kDmaWaves) {
         if (kTailLanes != 0 && jj == ndma - 1) {
-          if (lane < kTailLanes) dma16(src + jj * 1024, __builtin_amdgcn_readfirstlane(dst + jj * 1024));
+          if (lane < kTailLanes) dma16(src + jj * 1024, lane_off, dst + jj * 1024);
         } else {
-          dma16(src + jj * 1024, __builtin_amdgcn_readfirstlane(dst + jj * 1024));
+          dma16(src + jj * 1024, lane_off, dst + jj * 1024);
         }
       }
     }
