@@ -1674,8 +1674,11 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
     for (int k = 0; k < 8; ++k) st.o[k] = st.o[k] * (kSub * ofac);
   }
   if constexpr (NSUB == 2) set_nm(st, sl2);
-  int buf = 0;
-  for (int p = 0; p < iss_end; ++p) {
+  // One block of the ring: wait for it, issue the next, compute on it.  For INT2 in paired
+  // subtiles (the whole ring within 64 KB) the loop is unrolled over the ring, so that each
+  // slot's LDS offset is a constant folded into the reads' immediate offsets instead of a vector
+  // add per address per block.
+  auto one_block = [&](int p, int buf) __attribute__((always_inline)) {
     if (!dispatcher) {
       // blocks issued after this one may stay in flight
       wait_vmcnt(__builtin_amdgcn_readfirstlane(mine * (iss_end - p - 1)));
@@ -1691,7 +1694,6 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
     const bool full = !((tailmask >> buf) & 1u);
     if (!iss_done) issue_next();
     const uint8_t *blk = smem + buf * bb;
-    buf = buf + 1 == nbuf ? 0 : buf + 1;
     const int nv = full ? kBlock : tail_valid;
     if constexpr (NSUB == 2) {
       if constexpr (FMT == kFmtNvfp4) {
@@ -1727,6 +1729,25 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
         if (full) affine_step<FMT, GS, false>(blk, w, g, c, q, sl2, valid_head, nv, st);
         else affine_step<FMT, GS, true>(blk, w, g, c, q, sl2, valid_head, nv, st);
       }
+    }
+  };
+  constexpr bool kUnrollRing = FMT == kFmtInt2 && GS == 64 && NSUB == 2 &&
+                               decode_ring_depth(block_bytes(FMT, GS)) * block_bytes(FMT, GS) <= 65536;
+  if constexpr (kUnrollRing) {
+    constexpr int kRing = decode_ring_depth(block_bytes(FMT, GS));
+    static_assert(kRing == 4, "the unrolled ring has four slots");
+    // (iss_end grows as blocks are issued inside one_block: each test sees the current count)
+    for (int p = 0; p < iss_end; p += kRing) {
+      one_block(p, 0);
+      if (p + 1 < iss_end) one_block(p + 1, 1);
+      if (p + 2 < iss_end) one_block(p + 2, 2);
+      if (p + 3 < iss_end) one_block(p + 3, 3);
+    }
+  } else {
+    int buf = 0;
+    for (int p = 0; p < iss_end; ++p) {
+      one_block(p, buf);
+      buf = buf + 1 == nbuf ? 0 : buf + 1;
     }
   }
   barrier();   // every wave is done with the ring before it is reused
