@@ -115,12 +115,28 @@ __device__ __forceinline__ void unpack_int2(uint32_t x, half8_t &lo, half8_t &hi
   lo = h8(x & 0x00030003u, x & 0x000C000Cu, x4 & 0x00030003u, x4 & 0x000C000Cu);
   hi = h8(x8 & 0x00030003u, x8 & 0x000C000Cu, x12 & 0x00030003u, x12 & 0x000C000Cu);
 }
+// INT2 K word with per-token groups -> the same crumbs in the same order as unpack_int2, with
+// the three crumbs in bits 0..5 of each half masked in place (times 1, 4, 16), the next three
+// after one shift by 6, the last two after a shift by 12 (2 shifts and 8 ands per word):
+// lo = [c0, c8, 4c1, 4c9, 16c2, 16c10, c3, c11], hi = [4c4, 4c12, 16c5, 16c13, c6, c14, 4c7, 4c15]
+// (factors at most 16 apart within one MFMA operand, as INT4's)
+__device__ __forceinline__ void unpack_int2_k(uint32_t x, half8_t &lo, half8_t &hi) {
+  const uint32_t x6 = x >> 6, x12 = x >> 12;
+  lo = h8(x & 0x00030003u, x & 0x000C000Cu, x & 0x00300030u, x6 & 0x00030003u);
+  hi = h8(x6 & 0x000C000Cu, x6 & 0x00300030u, x12 & 0x00030003u, x12 & 0x000C000Cu);
+}
 // log2 of the factor that the scaled A elements carry (INT4 16, INT2 4; none for the others)
 template <int FMT>
 constexpr int kSh = FMT == kFmtInt4 ? 4 : FMT == kFmtInt2 ? 2 : 0;
-// log2 of the factor of K operand element e: (e >> 1) odd: INT4 4, INT2 2; else 0
+// log2 of the factor of K operand element e of the word's first (hh = 0) or second (hh = 1)
+// operand: INT2 with per-token groups as unpack_int2_k; otherwise (e >> 1) odd: INT4 4, INT2
+// 2, else 0
 template <int FMT, int GS>
-__device__ __forceinline__ constexpr int k_elem_sh(int e) {
+__device__ __forceinline__ constexpr int k_elem_sh(int hh, int e) {
+  if constexpr (FMT == kFmtInt2 && GS != kKc) {
+    constexpr int lo_sh[4] = {0, 2, 4, 0}, hi_sh[4] = {2, 4, 0, 2};
+    return hh ? hi_sh[e >> 1] : lo_sh[e >> 1];
+  }
   return ((e >> 1) & 1) ? kSh<FMT> : 0;
 }
 // INT8 word pair -> [w0.b0, w0.b2, w0.b1, w0.b3, w1.b0, w1.b2, w1.b1, w1.b3]
@@ -246,7 +262,7 @@ __device__ __forceinline__ float head_sum2(float x) { return quad_sum(x + row_xo
 template <int FMT, int GS>
 __device__ __forceinline__ int q_dim(int g, int j, int e, int &sh) {
   const int G = j >> 1, h = j & 1;
-  sh = k_elem_sh<FMT, GS>(e);
+  sh = k_elem_sh<FMT, GS>(h, e);
   if constexpr (is_affine(FMT) && GS == 32) {
     return 32 * j + 8 * g + e;   // groups of 32: k-step j feeds dims 32j + 8g .. +7 (group j)
   } else if constexpr (FMT == kFmtInt4) {
@@ -580,8 +596,13 @@ __device__ __forceinline__ void affine_step(const uint8_t *blk, int w, int g, in
       op[0] = unpack_int4(x.x); op[1] = unpack_int4(x.y); op[2] = unpack_int4(x.z); op[3] = unpack_int4(x.w);
     } else if constexpr (NB == 2) {
       const uint2 x = *(const uint2 *)row;
-      unpack_int2(x.x, op[0], op[1]);
-      unpack_int2(x.y, op[2], op[3]);
+      if constexpr (kKcK) {
+        unpack_int2(x.x, op[0], op[1]);
+        unpack_int2(x.y, op[2], op[3]);
+      } else {
+        unpack_int2_k(x.x, op[0], op[1]);
+        unpack_int2_k(x.y, op[2], op[3]);
+      }
     } else {
       const uint4 x = *(const uint4 *)row, y = *(const uint4 *)(row + 1024);
       op[0] = unpack_int8(x.x, x.y); op[1] = unpack_int8(x.z, x.w);
@@ -907,7 +928,7 @@ struct QOp2 {
 template <int FMT, int GS>
 __device__ __forceinline__ int q_loc2(int j, int e, int &sh) {
   const int G = j >> 2, gi = (j >> 1) & 1, hh = j & 1;
-  sh = k_elem_sh<FMT, GS>(e);
+  sh = k_elem_sh<FMT, GS>(hh, e);
   if constexpr (is_affine(FMT) && GS == 32) {
     return 8 * (2 * (2 * G + hh) + gi) + e;   // groups of 32: dims 32 step + 8(2q + gi) + e
   } else if constexpr (FMT == kFmtInt4) {
@@ -1102,8 +1123,13 @@ __device__ __forceinline__ void affine_step2(const uint8_t *blk, int w, int g, i
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
       const uint2 x = *(const uint2 *)(blk + (tau_a * 64 + 16 * (2 * qq + gi) + c) * 8);
-      unpack_int2(x.x, op[gi][0], op[gi][1]);
-      unpack_int2(x.y, op[gi][2], op[gi][3]);
+      if constexpr (kKcK) {
+        unpack_int2(x.x, op[gi][0], op[gi][1]);
+        unpack_int2(x.y, op[gi][2], op[gi][3]);
+      } else {
+        unpack_int2_k(x.x, op[gi][0], op[gi][1]);
+        unpack_int2_k(x.y, op[gi][2], op[gi][3]);
+      }
     }
   } else {
     // chunk r of (tile, lane') at ((tile * 2 + r) * 64 + lane') * 16
