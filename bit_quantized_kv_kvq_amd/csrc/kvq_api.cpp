@@ -511,11 +511,24 @@ int plan_decode(kvq_cache *c, int layer, DecodeArgs &a, uint64_t *cursors, int64
     gss[i] = tiers[i].gs;
   }
   a.occ = decode_occupancy(fmts, gss, nt, a.G);
-  const int64_t target = std::max<int64_t>(1, (int64_t)a.occ * num_cus(c) / nbh);   // work items per (b, h)
-  const int parts = split_tiers(c, tiers, nt, target, a.seg);
+  const int64_t target = std::min<int64_t>(std::max<int64_t>(1, (int64_t)a.occ * num_cus(c) / nbh), kMaxParts - 1);
+  // A residual that alone is at least one work item's share of the (b, h)'s work gets an item of
+  // its own, which streams no blocks: riding on a block item it made that item finish last (its
+  // fp16 slots cost about 1.5x a quantized byte; on the 1K batch-4 shape, 4 items per (b, h) of 2
+  // blocks each, the residual's item took 13 us against 7 us for the others).
+  double blk_work = 0.0;
+  for (int i = 0; i < nt; ++i) blk_work += tier_work(tiers[i]);
+  const double res_work = (double)st.res * 512.0 * 1.5;
+  bool own_res = nt > 0 && target >= 2 && st.res > 0 && res_work * (double)target >= blk_work;
+  int parts = split_tiers(c, tiers, nt, own_res ? target - 1 : target, a.seg);
+  if (own_res && parts + 1 > kMaxParts) {   // (rounding gave the tiers every partial slot)
+    own_res = false;
+    parts = split_tiers(c, tiers, nt, target, a.seg);
+  }
   for (int i = 0; i < nt; ++i) a.seg[i].cursors = cursors ? cursors + (size_t)i * nbh * kCtrStride : nullptr;
   a.nseg = nt;
-  a.items_total = std::max(1, parts);
+  a.items_total = std::max(1, parts + (own_res ? 1 : 0));
+  a.res_item = own_res ? parts : -1;
   a.res_base = c->res(layer);
   a.res_bh_stride = (int64_t)c->geo.res_bh;
   a.res_len = cfg.residual_len;
@@ -709,6 +722,7 @@ int run_decode(kvq_cache *c, int32_t layer, const void *q, int32_t num_q_heads, 
   if (c->plan_only) return KVQ_OK;
   DecodeArgs a{};
   a.B = cfg.batch; a.H = cfg.num_kv_heads; a.G = G;
+  a.res_item = -1;
   uint64_t *cursors = (uint64_t *)workspace + (size_t)cfg.batch * cfg.num_kv_heads * kCtrStride;
   int num_wg = 0, parts = 1;
   size_t tab_bytes = 0;
@@ -960,6 +974,7 @@ int kvq_decode_attn_noalloc(kvq_cache *c, int32_t layer, const void *q, int32_t 
   // the call's workspace (the same split as kvq_decode_attn's) must fit the scratch array
   DecodeArgs a{};
   a.B = c->cfg.batch; a.H = c->cfg.num_kv_heads; a.G = num_q_heads / c->cfg.num_kv_heads;
+  a.res_item = -1;
   plan_decode(c, layer, a, nullptr);
   const size_t need = counters_bytes(c) + partials_bytes(c, num_q_heads, a.items_total);
   if (need > kNoAllocScratchBytes)

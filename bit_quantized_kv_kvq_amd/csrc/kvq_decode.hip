@@ -1511,7 +1511,7 @@ __device__ __forceinline__ Item decode_item(const DecodeArgs &a, int wg) {
       it.j = it.part - sg.part0;
     }
   }
-  it.has_res = a.res_ntok > 0 && it.part == it.bh % a.items_total;
+  it.has_res = a.res_ntok > 0 && it.part == (a.res_item >= 0 ? a.res_item : it.bh % a.items_total);
   it.items_total = a.items_total;
   it.res_ntok = a.res_ntok;
   it.pend_count = a.pend_count;

@@ -153,7 +153,9 @@ struct DecodeArgs {
   DecodeSeg seg[kMaxSegs];
   int nseg;
   int items_total;         // work items per (b, h), all segments (at least 1)
-  // fp16 residual, handled by the last work item of each (b, h)
+  int res_item;            // >= 0: work item res_item of every (b, h) holds the residual alone (it
+                           // streams no blocks); -1: item (b h-index) % items_total holds it as well
+  // fp16 residual, handled by one work item of each (b, h)
   const uint8_t *res_base;
   int64_t res_bh_stride;
   int res_len;             // R (slots allocated)
