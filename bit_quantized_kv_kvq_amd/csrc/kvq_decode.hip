@@ -1830,24 +1830,10 @@ __device__ __forceinline__ void merge_tail(const MergeGeom &m, const float *part
     m.sm_l[idx] = __hip_atomic_load(pp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  // few parts: one thread per head walks them; many (a small batch split into many items):
   // one wave per head, lane l taking parts l and l + 64 (P <= kMaxParts = 128), the max and
-  // the weighted sum of l reduced across the wave
-  if (P <= 16) {
-    if ((int)threadIdx.x < G) {
-      const int hc = threadIdx.x;
-      float M = kNegInf;
-      for (int p = 0; p < P; ++p) M = fmaxf(M, m.sm_m[p * G + hc]);
-      float L = 0.0f;
-      for (int p = 0; p < P; ++p) {
-        const float mv = m.sm_m[p * G + hc];
-        const float wt = mv == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
-        m.sm_w[p * G + hc] = wt;
-        L += wt * m.sm_l[p * G + hc];
-      }
-      m.sm_inv[hc] = L > 0.0f ? 1.0f / L : 0.0f;   // L = 0 only for an empty sequence of a ragged batch: zeros
-    }
-  } else {
+  // the weighted sum of l reduced across the wave (a single thread walking the parts of a head
+  // one LDS read after another took about a microsecond of the merge for 12 parts)
+  {
     for (int hc = w; hc < G; hc += kWaves) {
       const int p0 = lane, p1 = lane + 64;
       const float m0 = p0 < P ? m.sm_m[p0 * G + hc] : kNegInf, m1 = p1 < P ? m.sm_m[p1 * G + hc] : kNegInf;
