@@ -61,8 +61,6 @@ __device__ __forceinline__ uint32_t as_u(half2_t h) { return __builtin_bit_cast(
 __device__ __forceinline__ half8_t h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   return __builtin_bit_cast(half8_t, u32x4{a, b, c, d});
 }
-__device__ __forceinline__ float lo_f(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFF)); }
-__device__ __forceinline__ float hi_f(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16)); }
 __device__ __forceinline__ uint32_t pk(float a, float b) { return as_u(half2_t{(_Float16)a, (_Float16)b}); }
 
 __device__ __forceinline__ float4_t mfma(half8_t a, half8_t b, float4_t c) {
@@ -83,19 +81,6 @@ __device__ __forceinline__ float4_t mfma_pv2(half4_t a0, half4_t a1, half4_t b0,
 
 // fp16 pair (1024 + f_lo, 1024 + f_hi) of the two fields selected by mask, minus 1024 + off:
 // exact (f - off, or 16 f - off for a mask shifted by 4 bits).
-// (x & mask) | magic in one v_and_or_b32; gfx950 VOP3 reads at most one scalar operand, so the
-// magic constant lives in a VGPR.
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic_v) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(magic_v));
-  return r;
-}
-template <int OFF = 0>
-__device__ __forceinline__ uint32_t field_pair(uint32_t x, uint32_t mask) {
-  constexpr _Float16 k = (_Float16)(1024.0f + OFF);
-  return as_u(as_h2(and_or(x, mask, 0x64006400u)) - half2_t{k, k});
-}
-
 // ---------------------------------------------------------------- operand unpack per format
 // Affine codes enter the MFMA as fp16 subnormals: the 16-bit halves of (x & mask) are the raw
 // codes c, i.e. the values c * 2^-24 (16 c * 2^-24 for a mask shifted by 4 bits), which the
@@ -384,6 +369,58 @@ __device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t
       : "=&s"(saved)
       : "v"(voff), "s"(sbase), "s"(lds)
       : "memory");
+}
+
+// N (1..4) chunk loads of one wave as dma16, chunk t from sbase + t * STRIDE to LDS lds + t *
+// STRIDE, with M0 saved once and restored once around all of them
+template <int N, int STRIDE>
+__device__ __forceinline__ void dma16_run(const uint8_t *sbase, uint32_t voff, uint32_t lds) {
+  static_assert(N >= 1 && N <= 4, "one to four chunks");
+  const uint8_t *s1 = sbase + STRIDE, *s2 = sbase + 2 * STRIDE, *s3 = sbase + 3 * STRIDE;
+  const uint32_t l1 = lds + STRIDE, l2 = lds + 2 * STRIDE, l3 = lds + 3 * STRIDE;
+  uint32_t saved;
+  if constexpr (N == 1) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(lds)
+        : "memory");
+  } else if constexpr (N == 2) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt\n\t"
+        "s_mov_b32 m0, %5\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %4 nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(lds), "s"(s1), "s"(l1)
+        : "memory");
+  } else if constexpr (N == 3) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt\n\t"
+        "s_mov_b32 m0, %5\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %4 nt\n\t"
+        "s_mov_b32 m0, %7\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %6 nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(lds), "s"(s1), "s"(l1), "s"(s2), "s"(l2)
+        : "memory");
+  } else {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt\n\t"
+        "s_mov_b32 m0, %5\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %4 nt\n\t"
+        "s_mov_b32 m0, %7\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %6 nt\n\t"
+        "s_mov_b32 m0, %9\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %8 nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(lds), "s"(s1), "s"(l1), "s"(s2), "s"(l2), "s"(s3), "s"(l3)
+        : "memory");
+  }
+}
+
+// vmcnt(N) for a count known at compile time
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_c() {
+  static_assert(N >= 0 && N <= 63, "the vmcnt field holds 0..63");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 __device__ __forceinline__ void wait_vmcnt(int n) {
@@ -1005,8 +1042,8 @@ __device__ __forceinline__ void load_q2(const uint16_t *qrow, bool valid, int g,
 // Running max / probabilities for 4 logits (slots i of the lane's subtile); scaled_mask bit i
 // marks positions whose V operand carries a factor 2^SH (p / 2^SH there).
 template <int SH = 0>
-__device__ __forceinline__ void softmax_step2(State &st, const float (&s)[4], float (&p)[4], bool valid_head,
-                                              unsigned scaled_mask, float sl2) {
+__device__ __forceinline__ void softmax_step2(State &st, const float (&s)[4], float (&p)[4], unsigned scaled_mask,
+                                              float sl2) {
   const float ml = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
   // (the compare's lane mask as it is, masked by the valid heads')
   if ((__builtin_amdgcn_ballot_w64(ml > st.m + st.slack) & st.vmask) != 0) {
@@ -1060,7 +1097,7 @@ __device__ __forceinline__ half4_t v_operand2<8>(const uint32_t *vw, int k, int 
 
 template <int NB, int GS, bool TAIL>
 __device__ __forceinline__ void affine_step2(const uint8_t *blk, int w, int g, int c, const QOp2 &q, float sl2,
-                                             bool valid_head, int nvalid, State &st) {
+                                             int nvalid, State &st) {
   constexpr bool kKcK = GS == kKc;
   constexpr int NG = kGroups<GS>;
   constexpr int kKm = 2048 * NB;
@@ -1176,7 +1213,7 @@ __device__ __forceinline__ void affine_step2(const uint8_t *blk, int w, int g, i
   float p[4];
   constexpr int SH = NB == 4 ? 4 : NB == 2 ? 2 : 0;
   constexpr unsigned kScaled = SH != 0 ? 0xCu : 0u;   // INT4 / INT2: positions i = 2, 3
-  softmax_step2<SH>(st, s, p, valid_head, kScaled, sl2);
+  softmax_step2<SH>(st, s, p, kScaled, sl2);
 
   // P' = p * S per group (one fp16 rounding) and the zero-point sums sum P' Z; PV as
   // O^T += V^T P per subtile s0: A = V codes of s0, B = this lane's P' where its column
@@ -1205,7 +1242,7 @@ __device__ __forceinline__ void affine_step2(const uint8_t *blk, int w, int g, i
 
 template <bool TAIL>
 __device__ __forceinline__ void nvfp4_step2(const uint8_t *blk, int w, int g, int c, const QOp2 &q, float sl2,
-                                            bool valid_head, int nvalid, State &st) {
+                                            int nvalid, State &st) {
   const int lane = 16 * g + c;
   const int qq = g & 1, sa = g >> 1, sc = c >> 3;
   const int tau_a = 2 * w + sa, tau_c = 2 * w + sc;
@@ -1236,7 +1273,7 @@ __device__ __forceinline__ void nvfp4_step2(const uint8_t *blk, int w, int g, in
     s[i] = v;
   }
   float p[4];
-  softmax_step2(st, s, p, valid_head, 0u, sl2);
+  softmax_step2(st, s, p, 0u, sl2);
   const uint32_t p01 = pk(p[0], p[1]), p23 = pk(p[2], p[3]);
   const half4_t pa0 = sc == 0 ? h4(p01, p23) : h4(0u, 0u), pa1 = sc == 1 ? h4(p01, p23) : h4(0u, 0u);
 #pragma unroll
@@ -1254,7 +1291,7 @@ __device__ __forceinline__ void nvfp4_step2(const uint8_t *blk, int w, int g, in
 
 template <bool TAIL>
 __device__ __forceinline__ void fp8_step2(const uint8_t *blk, int w, int g, int c, const QOp2 &q, float sl2,
-                                          bool valid_head, int nvalid, State &st) {
+                                          int nvalid, State &st) {
   const int lane = 16 * g + c;
   const int qq = g & 1, sa = g >> 1, sc = c >> 3;
   const int tau_a = 2 * w + sa, tau_c = 2 * w + sc;
@@ -1289,7 +1326,7 @@ __device__ __forceinline__ void fp8_step2(const uint8_t *blk, int w, int g, int 
     s[i] = v;
   }
   float p[4];
-  softmax_step2(st, s, p, valid_head, 0u, sl2);
+  softmax_step2(st, s, p, 0u, sl2);
   // word 2k + s0 holds slots 4 s0 + (0, 2, 1, 3) of dim 16k + c in byte order
   const uint32_t p02 = pk(p[0], p[2]), p13 = pk(p[1], p[3]);
   const half4_t pa0 = sc == 0 ? h4(p02, p13) : h4(0u, 0u), pa1 = sc == 1 ? h4(p02, p13) : h4(0u, 0u);
@@ -1302,7 +1339,7 @@ __device__ __forceinline__ void fp8_step2(const uint8_t *blk, int w, int g, int 
 
 template <bool TAIL>
 __device__ __forceinline__ void mxfp4_step2(const uint8_t *blk, int w, int g, int c, const QOp2 &q, float sl2,
-                                            bool valid_head, int nvalid, State &st) {
+                                            int nvalid, State &st) {
   const int lane = 16 * g + c;
   const int qq = g & 1, sa = g >> 1, sc = c >> 3;
   const int tau_a = 2 * w + sa, tau_c = 2 * w + sc;
@@ -1331,7 +1368,7 @@ __device__ __forceinline__ void mxfp4_step2(const uint8_t *blk, int w, int g, in
     s[i] = v;
   }
   float p[4];
-  softmax_step2(st, s, p, valid_head, 0u, sl2);
+  softmax_step2(st, s, p, 0u, sl2);
   const uint32_t p01 = pk(p[0], p[1]), p23 = pk(p[2], p[3]);
   const half4_t pa0 = sc == 0 ? h4(p01, p23) : h4(0u, 0u), pa1 = sc == 1 ? h4(p01, p23) : h4(0u, 0u);
   const uint32_t xw[8] = {vx0.x, vx0.y, vx0.z, vx0.w, vx1.x, vx1.y, vx1.z, vx1.w};
@@ -1347,7 +1384,7 @@ __device__ __forceinline__ void mxfp4_step2(const uint8_t *blk, int w, int g, in
 
 template <bool TAIL>
 __device__ __forceinline__ void fp16_step2(const uint8_t *blk, int w, int g, int c, const QOp2 &q, float sl2,
-                                           bool valid_head, int nvalid, State &st) {
+                                           int nvalid, State &st) {
   const int lane = 16 * g + c;
   const int qq = g & 1, sa = g >> 1, sc = c >> 3;
   const int tau_a = 2 * w + sa, tau_c = 2 * w + sc;
@@ -1372,7 +1409,7 @@ __device__ __forceinline__ void fp16_step2(const uint8_t *blk, int w, int g, int
     s[i] = v;
   }
   float p[4];
-  softmax_step2(st, s, p, valid_head, 0u, sl2);
+  softmax_step2(st, s, p, 0u, sl2);
   const uint32_t p01 = pk(p[0], p[1]), p23 = pk(p[2], p[3]);
   const half4_t pa0 = sc == 0 ? h4(p01, p23) : h4(0u, 0u), pa1 = sc == 1 ? h4(p01, p23) : h4(0u, 0u);
 #pragma unroll
@@ -1384,7 +1421,7 @@ __device__ __forceinline__ void fp16_step2(const uint8_t *blk, int w, int g, int
 // fp16 residual, slots 32u .. 32u+31, paired subtiles (direct global loads).  The V loads go
 // out with the K loads, before the logits, so that the step waits for memory once.
 __device__ __forceinline__ void residual_step2(const uint8_t *res, int R, int r, int u, int g, int c, const QOp2 &q,
-                                               float sl2, bool valid_head, State &st) {
+                                               float sl2, State &st) {
   const int ntiles = R / 16;
   const int qq = g & 1, sa = g >> 1, sc = c >> 3;
   const int tau_a = 2 * u + sa, tau_c = 2 * u + sc;
@@ -1414,7 +1451,7 @@ __device__ __forceinline__ void residual_step2(const uint8_t *res, int R, int r,
     s[i] = (tau_c < ntiles && slot < r) ? acc[i] : kNegInf;
   }
   float p[4];
-  softmax_step2(st, s, p, valid_head, 0u, sl2);
+  softmax_step2(st, s, p, 0u, sl2);
   const uint32_t p01 = pk(p[0], p[1]), p23 = pk(p[2], p[3]);
   const half4_t pa0 = sc == 0 ? h4(p01, p23) : h4(0u, 0u), pa1 = sc == 1 ? h4(p01, p23) : h4(0u, 0u);
 #pragma unroll
@@ -1578,7 +1615,7 @@ __device__ __forceinline__ void residual_part(const DecodeArgs &a, const Item &i
     QOp2 q;
     load_q2<kFmtFp16, kGroup>(qrow, valid_head, g, c, q);
     set_nm(st, a.scale_log2);
-    for (int u = w; u < nsteps; u += kWaves) residual_step2(res, a.res_len, it.res_ntok, u, g, c, q, a.scale_log2, valid_head, st);
+    for (int u = w; u < nsteps; u += kWaves) residual_step2(res, a.res_len, it.res_ntok, u, g, c, q, a.scale_log2, st);
   } else {
     QOp q;
     load_q<kFmtFp16, kGroup>(qrow, valid_head, g, q.qb, q.qs, q.qscale);
@@ -1590,16 +1627,20 @@ template <int FMT, int GS, int NSUB>
 __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const DecodeSeg &sg, const Item &it, uint8_t *smem, int *s_chunk, int w,
                                int g, int c, bool valid_head, State &st) {
   const int lane = 16 * g + c;
-  const int bb = (int)block_bytes(FMT, GS);
+  constexpr int kBB = (int)block_bytes(FMT, GS);
+  const int bb = kBB;
   // 1 KB per wave instruction; a block that ends on a partial KB (per-channel K blocks end on
   // half a KB) gets a last instruction with only the lanes of its remaining bytes active
   constexpr int kTailLanes = (int)(block_bytes(FMT, GS) % 1024) / 16;
-  const int ndma = (bb + 1023) / 1024;
+  constexpr int kNdma = (kBB + 1023) / 1024;
   // Waves 0..2 load the blocks; wave 3 loads none and hands out the chunks, so that waiting
   // for its cursor atomic never waits for block loads (vmcnt counts both).
   constexpr int kDmaWaves = kWaves - 1;
   const bool dispatcher = w == kDmaWaves;
-  const int mine = dispatcher ? 0 : (ndma - w + kDmaWaves - 1) / kDmaWaves;
+  // wave w < kDmaWaves loads chunks jj = w, w + kDmaWaves, ... below kNdma: kMineHi of them
+  // for the first kNdma % kDmaWaves waves, kMineLo for the others
+  constexpr int kMineHi = (kNdma + kDmaWaves - 1) / kDmaWaves, kMineLo = kNdma / kDmaWaves;
+  const int mine = dispatcher ? 0 : (kNdma - w + kDmaWaves - 1) / kDmaWaves;
   uint64_t *cursor = sg.cursors + (int64_t)it.bh * kCtrStride;
   const int K = sg.chunk, items = sg.items, F = sg.fixed, nbig = sg.nbig, j = it.j;
   const int nblk = (int)((sg.ntok + kBlock - 1) / kBlock);
@@ -1610,7 +1651,11 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
   const uint8_t *gbh = sg.base + (int64_t)it.bh * sg.bh_stride;   // wave-uniform; lanes add 16 * lane
   const uint32_t lane_off = (uint32_t)lane * 16u;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  const int nbuf = decode_ring_depth(bb);
+  constexpr int kNbuf = decode_ring_depth(block_bytes(FMT, GS));
+  const int nbuf = kNbuf;
+  // INT2 in paired subtiles (the whole ring within 64 KB): the block loop is unrolled over the
+  // ring, the chunk loads of a block are unrolled and the steady-state wait is a constant
+  constexpr bool kUnrollRing = FMT == kFmtInt2 && GS == 64 && NSUB == 2 && kNbuf * kBB <= 65536;
   const uint16_t *qlds = (const uint16_t *)(smem + a.q_lds_off);   // the group's query rows
 
   const int tail_valid = (int)(sg.ntok - (int64_t)(nblk - 1) * kBlock);   // slots in the last block
@@ -1654,16 +1699,24 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
     }
     const int blk_idx = u_start + u_off;
     const int phys = blk_idx + rot < nblk ? blk_idx + rot : blk_idx + rot - nblk;
-    const int slot = iss_end % nbuf;
+    const int slot = (int)((uint32_t)iss_end % (uint32_t)kNbuf);
     if (!dispatcher) {
       const uint8_t *src = gbh + (int64_t)phys * bb;   // uniform
       const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(slot * bb));   // M0 takes a scalar
-      for (int jj = w; jj < ndma; jj += kDmaWaves) {
-        if (kTailLanes != 0 && jj == ndma - 1) {
+      auto load_chunk = [&](int jj) __attribute__((always_inline)) {
+        if (kTailLanes != 0 && jj == kNdma - 1) {
           if (lane < kTailLanes) dma16(src + jj * 1024, lane_off, dst + jj * 1024);
         } else {
           dma16(src + jj * 1024, lane_off, dst + jj * 1024);
         }
+      };
+      if constexpr (kUnrollRing) {
+        // the wave's chunks w, w + kDmaWaves, ... in one statement (whole chunks: no tail lanes)
+        static_assert(kTailLanes == 0 && kMineHi <= 4, "whole chunks, four per wave at most");
+        if (mine == kMineHi) dma16_run<kMineHi, kDmaWaves * 1024>(src + w * 1024, lane_off, dst + w * 1024);
+        else dma16_run<kMineLo, kDmaWaves * 1024>(src + w * 1024, lane_off, dst + w * 1024);
+      } else {
+        for (int jj = w; jj < kNdma; jj += kDmaWaves) load_chunk(jj);
       }
     }
     const bool part = phys == nblk - 1 && tail_valid < kBlock;
@@ -1706,8 +1759,15 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
   // add per address per block.
   auto one_block = [&](int p, int buf) __attribute__((always_inline)) {
     if (!dispatcher) {
-      // blocks issued after this one may stay in flight
-      wait_vmcnt(__builtin_amdgcn_readfirstlane(mine * (iss_end - p - 1)));
+      // blocks issued after this one may stay in flight: with the ring full ahead (the steady
+      // state) that count is one of two constants
+      const int ahead = iss_end - p - 1;
+      if (kUnrollRing && ahead == kNbuf - 2) {
+        if (mine == kMineHi) wait_vmcnt_c<kMineHi * (kNbuf - 2)>();
+        else wait_vmcnt_c<kMineLo * (kNbuf - 2)>();   // (mine is kMineLo)
+      } else {
+        wait_vmcnt(__builtin_amdgcn_readfirstlane(mine * ahead));
+      }
     } else if (dyn && !iss_done && u_off == u_len && u_idx + 1 >= F) {
       // the issue side enters a cursor unit now: publish the one fetched a unit ago
       if (lane == 0) {
@@ -1723,20 +1783,20 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
     const int nv = full ? kBlock : tail_valid;
     if constexpr (NSUB == 2) {
       if constexpr (FMT == kFmtNvfp4) {
-        if (full) nvfp4_step2<false>(blk, w, g, c, q2, sl2, valid_head, nv, st);
-        else nvfp4_step2<true>(blk, w, g, c, q2, sl2, valid_head, nv, st);
+        if (full) nvfp4_step2<false>(blk, w, g, c, q2, sl2, nv, st);
+        else nvfp4_step2<true>(blk, w, g, c, q2, sl2, nv, st);
       } else if constexpr (FMT == kFmtFp8) {
-        if (full) fp8_step2<false>(blk, w, g, c, q2, sl2, valid_head, nv, st);
-        else fp8_step2<true>(blk, w, g, c, q2, sl2, valid_head, nv, st);
+        if (full) fp8_step2<false>(blk, w, g, c, q2, sl2, nv, st);
+        else fp8_step2<true>(blk, w, g, c, q2, sl2, nv, st);
       } else if constexpr (FMT == kFmtFp16) {
-        if (full) fp16_step2<false>(blk, w, g, c, q2, sl2, valid_head, nv, st);
-        else fp16_step2<true>(blk, w, g, c, q2, sl2, valid_head, nv, st);
+        if (full) fp16_step2<false>(blk, w, g, c, q2, sl2, nv, st);
+        else fp16_step2<true>(blk, w, g, c, q2, sl2, nv, st);
       } else if constexpr (FMT == kFmtMxfp4) {
-        if (full) mxfp4_step2<false>(blk, w, g, c, q2, sl2, valid_head, nv, st);
-        else mxfp4_step2<true>(blk, w, g, c, q2, sl2, valid_head, nv, st);
+        if (full) mxfp4_step2<false>(blk, w, g, c, q2, sl2, nv, st);
+        else mxfp4_step2<true>(blk, w, g, c, q2, sl2, nv, st);
       } else {
-        if (full) affine_step2<FMT, GS, false>(blk, w, g, c, q2, sl2, valid_head, nv, st);
-        else affine_step2<FMT, GS, true>(blk, w, g, c, q2, sl2, valid_head, nv, st);
+        if (full) affine_step2<FMT, GS, false>(blk, w, g, c, q2, sl2, nv, st);
+        else affine_step2<FMT, GS, true>(blk, w, g, c, q2, sl2, nv, st);
       }
     } else {
       if constexpr (FMT == kFmtNvfp4) {
@@ -1757,8 +1817,6 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
       }
     }
   };
-  constexpr bool kUnrollRing = FMT == kFmtInt2 && GS == 64 && NSUB == 2 &&
-                               decode_ring_depth(block_bytes(FMT, GS)) * block_bytes(FMT, GS) <= 65536;
   if constexpr (kUnrollRing) {
     constexpr int kRing = decode_ring_depth(block_bytes(FMT, GS));
     static_assert(kRing == 4, "the unrolled ring has four slots");
@@ -2126,7 +2184,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeArgs a) {
   // Every other workgroup of this (b, h) has arrived, each after all its memory operations
   // completed (its cursor fetch-adds included), so no access of this call to the (b, h)'s
   // arrival counter or cursors is left: set them back to zero for the next call.
-  if (threadIdx.x < 1 + a.nseg) {
+  if ((int)threadIdx.x < 1 + a.nseg) {
     uint64_t *wd = (threadIdx.x == 0 ? a.counters : a.seg[threadIdx.x - 1].cursors) + (int64_t)it.bh * kCtrStride;
     __hip_atomic_store(wd, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }

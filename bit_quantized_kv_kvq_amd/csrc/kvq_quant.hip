@@ -701,7 +701,6 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
         for (int k = 0; k < F; ++k) word |= fast_code(x[k], Sg, inv, Z) << (k * kBits);
       } else if (slot < hi) {
         const int d0 = k_lane_dim(FMT, g, omega * F);   // first of F consecutive dims
-        const int grp = d0 / (kMx ? kMxBlock : kNv ? kNvBlock : GSV);
         const uint16_t *xr = &xs[slot * kRowHalves + d0];
         if constexpr (F >= 8) {
 #pragma unroll
