@@ -416,6 +416,17 @@ __device__ __forceinline__ void dma16_run(const uint8_t *sbase, uint32_t voff, u
   }
 }
 
+// N (1..8) chunk loads as dma16_run, in statements of four
+template <int N, int STRIDE>
+__device__ __forceinline__ void dma16_runs(const uint8_t *sbase, uint32_t voff, uint32_t lds) {
+  if constexpr (N <= 4) {
+    dma16_run<N, STRIDE>(sbase, voff, lds);
+  } else {
+    dma16_run<4, STRIDE>(sbase, voff, lds);
+    dma16_run<N - 4, STRIDE>(sbase + 4 * STRIDE, voff, lds + 4 * STRIDE);
+  }
+}
+
 // vmcnt(N) for a count known at compile time
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_c() {
@@ -1656,6 +1667,9 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
   // INT2 in paired subtiles (the whole ring within 64 KB): the block loop is unrolled over the
   // ring, the chunk loads of a block are unrolled and the steady-state wait is a constant
   constexpr bool kUnrollRing = FMT == kFmtInt2 && GS == 64 && NSUB == 2 && kNbuf * kBB <= 65536;
+  // Blocks of whole chunks, at most six per wave: a wave's chunk loads are issued in one or two
+  // statements and the steady-state wait is a constant
+  constexpr bool kBatchIssue = kTailLanes == 0 && kMineHi <= 6;
   const uint16_t *qlds = (const uint16_t *)(smem + a.q_lds_off);   // the group's query rows
 
   const int tail_valid = (int)(sg.ntok - (int64_t)(nblk - 1) * kBlock);   // slots in the last block
@@ -1710,11 +1724,10 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
           dma16(src + jj * 1024, lane_off, dst + jj * 1024);
         }
       };
-      if constexpr (kUnrollRing) {
-        // the wave's chunks w, w + kDmaWaves, ... in one statement (whole chunks: no tail lanes)
-        static_assert(kTailLanes == 0 && kMineHi <= 4, "whole chunks, four per wave at most");
-        if (mine == kMineHi) dma16_run<kMineHi, kDmaWaves * 1024>(src + w * 1024, lane_off, dst + w * 1024);
-        else dma16_run<kMineLo, kDmaWaves * 1024>(src + w * 1024, lane_off, dst + w * 1024);
+      if constexpr (kBatchIssue) {
+        // the wave's chunks w, w + kDmaWaves, ...
+        if (mine == kMineHi) dma16_runs<kMineHi, kDmaWaves * 1024>(src + w * 1024, lane_off, dst + w * 1024);
+        else dma16_runs<kMineLo, kDmaWaves * 1024>(src + w * 1024, lane_off, dst + w * 1024);
       } else {
         for (int jj = w; jj < kNdma; jj += kDmaWaves) load_chunk(jj);
       }
@@ -1762,7 +1775,7 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
       // blocks issued after this one may stay in flight: with the ring full ahead (the steady
       // state) that count is one of two constants
       const int ahead = iss_end - p - 1;
-      if (kUnrollRing && ahead == kNbuf - 2) {
+      if (kBatchIssue && ahead == kNbuf - 2) {
         if (mine == kMineHi) wait_vmcnt_c<kMineHi * (kNbuf - 2)>();
         else wait_vmcnt_c<kMineLo * (kNbuf - 2)>();   // (mine is kMineLo)
       } else {
