@@ -21,6 +21,7 @@
 #include "kvq_rescopy.h"
 
 #include <cmath>
+#include <type_traits>
 
 namespace kvq {
 namespace {
@@ -725,62 +726,76 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs a, int64_t
     // of dim 16 k + c and slot 32 w + 16 (e >> 2) + 4 g + (e & 3).  A task is (part, g, omega,
     // c0): the words of lanes 16 g + c0 .. + NL - 1, whose field j reads the same slot at the NL
     // consecutive dims 16 k + c0 .. (one LDS read and one metadata lookup).  NL = 8, or 4 where
-    // 8 would leave threads idle (INT2: 128 tasks of 8 lanes for 256 threads).
+    // 8 would leave threads idle (INT2: 128 tasks of 8 lanes for 256 threads); a workgroup of a
+    // split block (one 32-slot part: a quarter of the tasks) gives each task kLaneWords / 4
+    // lanes, so that it has one task per thread (INT4: 64 tasks of 8 lanes would leave three
+    // waves idle; 2 lanes for INT4, 1 for INT2, 4 for INT8).
     const size_t vc = kMx ? kMxVc : kNv ? kNvVc : kF8 ? kF8Vc : kKcK ? kc_vc(kBits) : aff_vc(kBits, NG);
     constexpr int kChunks = kBits / 2;              // 16-byte chunks per lane
     constexpr int kLaneWords = 4 * kChunks;
-    constexpr int NL = 4 * 4 * kLaneWords * 2 >= kThreads ? 8 : 4 * 4 * kLaneWords * 4 >= kThreads ? 4 : 2;
-    constexpr int kSplit = 16 / NL;
-    constexpr int kTasks = 4 * 4 * kLaneWords * kSplit;
-    const int tend = (sub + 1) * (kTasks / nsplit);   // tasks are part-major: this workgroup's parts
-    for (int task = sub * (kTasks / nsplit) + tid; task < tend; task += kThreads) {
-      const int c0 = NL * (task % kSplit), omega = (task / kSplit) % kLaneWords, g = ((task / kSplit) / kLaneWords) & 3;
-      const int part = (task / kSplit) / kLaneWords >> 2;
-      uint32_t words[NL] = {};
-      uint32_t keep = 0;                            // field bits of slots before lo (kept as stored)
-      bool any = false;
-#pragma unroll
-      for (int j = 0; j < F; ++j) {
-        int k, e;
-        v_field(FMT, omega * F + j, k, e);
-        const int slot = 32 * part + 16 * (e >> 2) + 4 * g + (e & 3);
-        if (slot < lo) {
-          keep |= (uint32_t)kQmax << (j * kBits);
-          continue;
+    constexpr int kNL = 4 * 4 * kLaneWords * 2 >= kThreads ? 8 : 4 * 4 * kLaneWords * 4 >= kThreads ? 4 : 2;
+    auto v_codes = [&](auto nl) __attribute__((always_inline)) {
+      constexpr int NL = decltype(nl)::value;
+      constexpr int kSplit = 16 / NL;
+      constexpr int kTasks = 4 * 4 * kLaneWords * kSplit;
+      const int tend = (sub + 1) * (kTasks / nsplit);   // tasks are part-major: this workgroup's parts
+      for (int task = sub * (kTasks / nsplit) + tid; task < tend; task += kThreads) {
+        const int c0 = NL * (task % kSplit), omega = (task / kSplit) % kLaneWords, g = ((task / kSplit) / kLaneWords) & 3;
+        const int part = (task / kSplit) / kLaneWords >> 2;
+        uint32_t words[NL] = {};
+        uint32_t keep = 0;                            // field bits of slots before lo (kept as stored)
+        bool any = false;
+  #pragma unroll
+        for (int j = 0; j < F; ++j) {
+          int k, e;
+          v_field(FMT, omega * F + j, k, e);
+          const int slot = 32 * part + 16 * (e >> 2) + 4 * g + (e & 3);
+          if (slot < lo) {
+            keep |= (uint32_t)kQmax << (j * kBits);
+            continue;
+          }
+          if (slot >= zhi) continue;
+          any = true;
+          if (slot >= hi) continue;                    // cleared: code 0
+          const int d0 = 16 * k + c0;
+          const int grp = d0 / (kMx ? kMxBlock : kNv ? kNvBlock : GSV);
+          uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+          if constexpr (NL == 8) {
+            raw = *(const uint4 *)&xs[slot * kRowHalves + d0];
+          } else if constexpr (NL == 4) {
+            const uint2 u = *(const uint2 *)&xs[slot * kRowHalves + d0];
+            raw.x = u.x; raw.y = u.y;
+          } else if constexpr (NL == 1) {
+            raw.x = xs[slot * kRowHalves + d0];
+          } else {
+            raw.x = *(const uint32_t *)&xs[slot * kRowHalves + d0];
+          }
+          if constexpr (kAffine) {
+            const half8v xh = __builtin_bit_cast(half8v, raw);
+            const float Sg = mS[slot][grp], inv = mInv[slot][grp], Z = mZ[slot][grp];
+  #pragma unroll
+            for (int i = 0; i < NL; ++i) words[i] |= fast_code(xh[i], Sg, inv, Z) << (j * kBits);
+          } else {
+            float x[8];
+            unpack8(raw, x);
+  #pragma unroll
+            for (int i = 0; i < NL; ++i) words[i] |= code_of(x[i], slot, grp) << (j * kBits);
+          }
         }
-        if (slot >= zhi) continue;
-        any = true;
-        if (slot >= hi) continue;                    // cleared: code 0
-        const int d0 = 16 * k + c0;
-        const int grp = d0 / (kMx ? kMxBlock : kNv ? kNvBlock : GSV);
-        uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-        if constexpr (NL == 8) {
-          raw = *(const uint4 *)&xs[slot * kRowHalves + d0];
-        } else if constexpr (NL == 4) {
-          const uint2 u = *(const uint2 *)&xs[slot * kRowHalves + d0];
-          raw.x = u.x; raw.y = u.y;
-        } else {
-          raw.x = *(const uint32_t *)&xs[slot * kRowHalves + d0];
-        }
-        if constexpr (kAffine) {
-          const half8v xh = __builtin_bit_cast(half8v, raw);
-          const float Sg = mS[slot][grp], inv = mInv[slot][grp], Z = mZ[slot][grp];
-#pragma unroll
-          for (int i = 0; i < NL; ++i) words[i] |= fast_code(xh[i], Sg, inv, Z) << (j * kBits);
-        } else {
-          float x[8];
-          unpack8(raw, x);
-#pragma unroll
-          for (int i = 0; i < NL; ++i) words[i] |= code_of(x[i], slot, grp) << (j * kBits);
+        if (!any) continue;
+  #pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          const int lane = 16 * g + c0 + i;
+          uint32_t *dst = (uint32_t *)(blkp + vc + ((size_t)(part * kChunks + omega / 4) * 64 + lane) * 16 + (omega % 4) * 4);
+          *dst = keep ? (*dst & keep) | words[i] : words[i];
         }
       }
-      if (!any) continue;
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const int lane = 16 * g + c0 + i;
-        uint32_t *dst = (uint32_t *)(blkp + vc + ((size_t)(part * kChunks + omega / 4) * 64 + lane) * 16 + (omega % 4) * 4);
-        *dst = keep ? (*dst & keep) | words[i] : words[i];
-      }
+    };
+    if constexpr (kAffine && !kKcK) {
+      if (nsplit > 1) v_codes(std::integral_constant<int, (kLaneWords >= 4 ? kLaneWords / 4 : 1)>{});
+      else v_codes(std::integral_constant<int, kNL>{});
+    } else {
+      v_codes(std::integral_constant<int, kNL>{});
     }
   }
 }
