@@ -1665,7 +1665,7 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
   constexpr int kNbuf = decode_ring_depth(block_bytes(FMT, GS));
   const int nbuf = kNbuf;
   // INT2 in paired subtiles (the whole ring within 64 KB): the block loop is unrolled over the
-  // ring, the chunk loads of a block are unrolled and the steady-state wait is a constant
+  // ring slots (below)
   constexpr bool kUnrollRing = FMT == kFmtInt2 && GS == 64 && NSUB == 2 && kNbuf * kBB <= 65536;
   // Blocks of whole chunks, at most six per wave: a wave's chunk loads are issued in one or two
   // statements and the steady-state wait is a constant
@@ -1717,19 +1717,18 @@ __device__ __forceinline__ void stream_segment(const DecodeArgs &a, const Decode
     if (!dispatcher) {
       const uint8_t *src = gbh + (int64_t)phys * bb;   // uniform
       const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(slot * bb));   // M0 takes a scalar
-      auto load_chunk = [&](int jj) __attribute__((always_inline)) {
-        if (kTailLanes != 0 && jj == kNdma - 1) {
-          if (lane < kTailLanes) dma16(src + jj * 1024, lane_off, dst + jj * 1024);
-        } else {
-          dma16(src + jj * 1024, lane_off, dst + jj * 1024);
-        }
-      };
       if constexpr (kBatchIssue) {
         // the wave's chunks w, w + kDmaWaves, ...
         if (mine == kMineHi) dma16_runs<kMineHi, kDmaWaves * 1024>(src + w * 1024, lane_off, dst + w * 1024);
         else dma16_runs<kMineLo, kDmaWaves * 1024>(src + w * 1024, lane_off, dst + w * 1024);
       } else {
-        for (int jj = w; jj < kNdma; jj += kDmaWaves) load_chunk(jj);
+        for (int jj = w; jj < kNdma; jj += kDmaWaves) {
+          if (kTailLanes != 0 && jj == kNdma - 1) {
+            if (lane < kTailLanes) dma16(src + jj * 1024, lane_off, dst + jj * 1024);
+          } else {
+            dma16(src + jj * 1024, lane_off, dst + jj * 1024);
+          }
+        }
       }
     }
     const bool part = phys == nblk - 1 && tail_valid < kBlock;
