@@ -528,6 +528,12 @@ def measure(name: str, steps: int, warmup: int, n_pairs: int, separate_append: b
                               ("quantize of the step's token" if R == 0 else
                                "flush of the full residual + copy of the new tokens" if per_step > 1 or flush_first
                                else "residual copy") + ")")
+    if app_used and R > 0 and per_step >= R:
+        # every step's append flushes the full residual: its quantize rate, as the prefill's
+        qbytes = B * H * R * (512 + bytes_per_token(fmt))
+        res["append_quantize_gbs"] = round(qbytes / (float(app_ms.mean()) * 1e-3) / 1e9, 1)
+        res["append_quantize_note"] = ("fp16 read + packed bytes written of the flushed residual over append_us "
+                                       "(the same launch also copies the step's tokens into the residual)")
     if flush_first:
         res["flush_step_ms"] = round(float(step_ms[flush_k]), 4)
         res["plain_step_ms_mean"] = round(float(np.delete(step_ms, flush_k).mean()), 4) if steps > 1 else None
@@ -724,7 +730,8 @@ def main():
                      "read_probe_same_bytes_us": head["read_probe_same_bytes_us"],
                      "decode_vs_read_probe": head["decode_vs_read_probe"]},
     }
-    for k in ("prefill_s", "prefill_quantize_ms", "prefill_quantize_gbs", "append_us", "append_note", "flush_step_ms",
+    for k in ("prefill_s", "prefill_quantize_ms", "prefill_quantize_gbs", "append_us", "append_note",
+              "append_quantize_gbs", "append_quantize_note", "flush_step_ms",
               "plain_step_ms_mean", "flush_append_us", "flush_note", "demote_young", "demotion"):
         if k in head:
             line[k] = head[k]
