@@ -458,7 +458,9 @@ int split_tiers(const kvq_cache *c, const TierRef *t, int nt, int64_t target, De
     items = std::min<int64_t>(items, kMaxParts / std::max(1, nt));
     // units of about 1/32 of an item's share, at least four blocks (a unit's cursor fetch
     // has four block times to come back); two fixed units per item, then the cursor's big
-    // units, then two single blocks per item for the finish
+    // units, then six single blocks per item for the finish (an item that takes the last big
+    // unit as the others take single blocks finishes up to a unit later: with two singles per
+    // item the items of one (b, h) ended 3-4 us apart on the 32K and 128K shapes)
     const int64_t nblk = t[i].nblk;
     int64_t chunk = std::max<int64_t>(4, ceil_div(nblk, items * 32));
     int64_t fixed = 2, nbig = 0;
@@ -466,7 +468,7 @@ int split_tiers(const kvq_cache *c, const TierRef *t, int nt, int64_t target, De
       if (c->deterministic)
         fixed = ceil_div(ceil_div(nblk, chunk), items);   // every chunk dealt round-robin up front
       else
-        nbig = std::max<int64_t>(0, (nblk - fixed * items * chunk - 2 * items) / chunk);
+        nbig = std::max<int64_t>(0, (nblk - fixed * items * chunk - 6 * items) / chunk);
     } else {
       // too little to share out: single blocks, dealt round-robin
       chunk = 1;
