@@ -457,12 +457,15 @@ int split_tiers(const kvq_cache *c, const TierRef *t, int nt, int64_t target, De
     int64_t items = std::max<int64_t>(1, (int64_t)((double)target * tier_work(t[i]) / work + 0.5));
     items = std::min<int64_t>(items, kMaxParts / std::max(1, nt));
     // units of about 1/32 of an item's share, at least four blocks (a unit's cursor fetch
-    // has four block times to come back); two fixed units per item, then the cursor's big
-    // units, then six single blocks per item for the finish (an item that takes the last big
-    // unit as the others take single blocks finishes up to a unit later: with two singles per
-    // item the items of one (b, h) ended 3-4 us apart on the 32K and 128K shapes)
+    // has four block times to come back), at least eight where the tier has at most 16 items
+    // per (b, h) (half the cursor fetches: 128K INT4 187.0 -> 185.7 us, 32K NVFP4 59.4 ->
+    // 59.0 us; the 256K tiers, with more items per (b, h), lost 1 % with eight); two fixed
+    // units per item, then the cursor's big units, then six single blocks per item for the
+    // finish (an item that takes the last big unit as the others take single blocks finishes
+    // up to a unit later: with two singles per item the items of one (b, h) ended 3-4 us apart
+    // on the 32K and 128K shapes)
     const int64_t nblk = t[i].nblk;
-    int64_t chunk = std::max<int64_t>(4, ceil_div(nblk, items * 32));
+    int64_t chunk = std::max<int64_t>(items <= 16 ? 8 : 4, ceil_div(nblk, items * 32));
     int64_t fixed = 2, nbig = 0;
     if (nblk >= (fixed + 2) * items * chunk) {
       if (c->deterministic)
